@@ -1,0 +1,160 @@
+"""Pins for the block-attention oracle: brute force with explicit masks, a
+library routine (torch CPU float64 scaled-dot-product attention), closed forms
+and invariances."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+
+def _case(seed, B=3, k=4, Hq=4, Hkv=2, D=8, ctx=(0, 5, 19), dtype="f32", **kw):
+    return synth.attention_case(seed, dtype=dtype, B=B, k=k, n_q_heads=Hq, n_kv_heads=Hkv,
+                                head_dim=D, ctx_lens=list(ctx), **kw)
+
+
+def _run(c, fn=oracle.block_attention, scale=None):
+    return fn(c.q, c.k_blk, c.v_blk, c.cache_k, c.cache_v, c.block_table, c.ctx_lens, c.dtype,
+              scale=scale)
+
+
+@pytest.mark.parametrize("seed,ctx", [(1, (0, 5, 19)), (2, (8, 1, 33)), (3, (16, 16, 0))])
+def test_gather_form_equals_explicit_mask_brute_force(seed, ctx):
+    c = _case(seed, ctx=ctx)
+    o1, l1 = _run(c)
+    o2, l2 = _run(c, oracle.block_attention_masked)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-12)
+
+
+def test_bf16_gather_equals_brute_force():
+    c = _case(4, B=2, k=8, Hq=4, Hkv=2, D=16, ctx=(7, 40), dtype="bf16", q_scale=3.0)
+    o1, l1 = _run(c)
+    o2, l2 = _run(c, oracle.block_attention_masked)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-12)
+
+
+def test_matches_torch_sdpa_float64_with_bool_mask():
+    """Library routine: torch CPU float64 SDPA over each request's keys with
+    an explicit bool mask (all True: the block is non-causal)."""
+    c = _case(5, B=2, k=4, Hq=6, Hkv=2, D=16, ctx=(9, 23))
+    out, lse = _run(c)
+    q = oracle.widen(c.q, "f32")
+    for b in range(c.B):
+        C = int(c.ctx_lens[b])
+        keys = np.concatenate([oracle.gather_paged(oracle.widen(c.cache_k, "f32"),
+                                                   c.block_table[b], C),
+                               oracle.widen(c.k_blk, "f32")[b]])
+        vals = np.concatenate([oracle.gather_paged(oracle.widen(c.cache_v, "f32"),
+                                                   c.block_table[b], C),
+                               oracle.widen(c.v_blk, "f32")[b]])
+        G = c.n_q_heads // c.n_kv_heads
+        for h in range(c.n_q_heads):
+            qt = torch.from_numpy(q[b, :, h, :])[None, None]
+            kt = torch.from_numpy(keys[:, h // G, :])[None, None]
+            vt = torch.from_numpy(vals[:, h // G, :])[None, None]
+            mask = torch.ones(c.k, C + c.k, dtype=torch.bool)
+            ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask)
+            np.testing.assert_allclose(out[b, :, h, :], ref[0, 0].numpy(), atol=1e-12)
+
+
+def test_closed_form_single_key_returns_value():
+    """C = 0 and k = 1: the only visible key is the query's own, so o = v."""
+    c = _case(6, B=2, k=1, ctx=(0, 0))
+    out, lse = _run(c)
+    v = oracle.widen(c.v_blk, "f32")
+    G = c.n_q_heads // c.n_kv_heads
+    for h in range(c.n_q_heads):
+        np.testing.assert_allclose(out[:, 0, h], v[:, 0, h // G], atol=1e-15)
+
+
+def test_closed_form_zero_query_is_mean_of_values():
+    c = _case(7, ctx=(3, 0, 21))
+    c.q[:] = 0
+    out, lse = _run(c)
+    v = oracle.widen(c.v_blk, "f32"); cv = oracle.widen(c.cache_v, "f32")
+    G = c.n_q_heads // c.n_kv_heads
+    for b in range(c.B):
+        C = int(c.ctx_lens[b])
+        vals = np.concatenate([oracle.gather_paged(cv, c.block_table[b], C), v[b]])
+        for h in range(c.n_q_heads):
+            np.testing.assert_allclose(out[b, :, h], np.broadcast_to(vals[:, h // G].mean(0),
+                                                                     (c.k, c.head_dim)),
+                                       atol=1e-14)
+            np.testing.assert_allclose(lse[b, h], np.log(C + c.k), atol=1e-14)
+
+
+def test_identical_keys_give_mean_of_values():
+    c = _case(8, ctx=(5, 12, 2))
+    c.cache_k[:] = c.cache_k[0, 0, :, :][None, None]
+    c.k_blk[:] = c.cache_k[0, 0][None, None]
+    out, _ = _run(c)
+    v = oracle.widen(c.v_blk, "f32"); cv = oracle.widen(c.cache_v, "f32")
+    G = c.n_q_heads // c.n_kv_heads
+    for b in range(c.B):
+        vals = np.concatenate([oracle.gather_paged(cv, c.block_table[b], int(c.ctx_lens[b])),
+                               v[b]])
+        for h in range(c.n_q_heads):
+            np.testing.assert_allclose(out[b, :, h], np.broadcast_to(vals[:, h // G].mean(0),
+                                                                     (c.k, c.head_dim)),
+                                       atol=1e-12)
+
+
+def test_invariant_to_physical_page_order():
+    a = _case(9, ctx=(40, 17, 33), shuffle=False)
+    b = _case(9, ctx=(40, 17, 33), shuffle=True)
+    # same logical contents, different physical placement
+    for bb in range(a.B):
+        for lp in range(a.block_table.shape[1]):
+            pa, pb = a.block_table[bb, lp], b.block_table[bb, lp]
+            if pa >= 0:
+                b.cache_k[pb] = a.cache_k[pa]
+                b.cache_v[pb] = a.cache_v[pa]
+    oa, la = _run(a)
+    ob, lb = _run(b)
+    np.testing.assert_allclose(oa, ob, atol=1e-14)
+    np.testing.assert_allclose(la, lb, atol=1e-14)
+
+
+def test_scale_argument():
+    c = _case(10)
+    o1, l1 = _run(c, scale=0.25)
+    o2, l2 = _run(c, oracle.block_attention_masked, scale=0.25)
+    np.testing.assert_allclose(o1, o2, atol=1e-12)
+    o3, _ = _run(c, scale=0.0)
+    o4, _ = _run(c)
+    np.testing.assert_allclose(o3, o4, atol=0)
+
+
+def test_packed_training_mask_equals_dense_sequence_mask():
+    """[DFlash overview] 随机锚点采样: blocks packed into one training sequence
+    see the injected context of target positions before their anchor, all of
+    their own positions, and nothing of the other blocks.  Written here as one
+    dense mask over [context positions ; all block positions]."""
+    seq, k, Hq, Hkv, D = 96, 4, 2, 1, 8
+    c, P = synth.packed_attention_case(77, dtype="f32", seq_len=seq, k=k, n_q_heads=Hq,
+                                       n_kv_heads=Hkv, head_dim=D, max_anchors=9,
+                                       prompt_range=(20, 30))
+    nb = c.B
+    out, _ = _run(c)
+    q = oracle.widen(c.q, "f32"); kb = oracle.widen(c.k_blk, "f32"); vb = oracle.widen(c.v_blk, "f32")
+    ck = oracle.gather_paged(oracle.widen(c.cache_k, "f32"), c.block_table[0], seq)
+    cv = oracle.gather_paged(oracle.widen(c.cache_v, "f32"), c.block_table[0], seq)
+    keys = np.concatenate([ck, kb.reshape(nb * k, Hkv, D)])
+    vals = np.concatenate([cv, vb.reshape(nb * k, Hkv, D)])
+    mask = np.zeros((nb * k, seq + nb * k), dtype=bool)
+    for i, a in enumerate(c.ctx_lens):
+        mask[i * k:(i + 1) * k, :a] = True                               # context before anchor
+        mask[i * k:(i + 1) * k, seq + i * k: seq + (i + 1) * k] = True    # own block
+    for h in range(Hq):
+        qq = torch.from_numpy(q[:, :, h, :].reshape(nb * k, D))[None, None]
+        kk = torch.from_numpy(keys[:, 0, :])[None, None]
+        vv = torch.from_numpy(vals[:, 0, :])[None, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qq, kk, vv, attn_mask=torch.from_numpy(mask)[None, None])
+        np.testing.assert_allclose(out[:, :, h, :].reshape(nb * k, D), ref[0, 0].numpy(),
+                                   atol=1e-12)
+    # anchors are disjoint blocks in the loss region
+    a = np.sort(c.ctx_lens)
+    assert (np.diff(a) >= k).all() and a[0] >= P and a[-1] + k <= seq
