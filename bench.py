@@ -1,0 +1,302 @@
+#!/usr/bin/env python3
+"""Throughput of the DFlash draft-and-verify step on one MI355X.
+
+One step = ctx-KV materialisation of the rows committed by the previous
+verify (B requests x k rows, all five captured hiddens fused, K/V for every
+draft layer written to the paged caches) + block attention for each draft
+layer + greedy verification over the full vocabulary (target argmax, fused
+draft argmax, acceptance, bonus).  Workload: the Llama-3.1-8B-shaped decode
+step -- d_model 4096, 5 captured hiddens, 5 draft layers with 32 Q / 8 KV
+heads of 128, block k = 16, ctx 8192 per request, vocab 128256, batch 64,
+random weights ~N(0, 0.02), logits ~N(0, 3), caches ~N(0, 1), all bf16 and
+resident in HBM before timing starts.
+
+Prints one JSON line (rank 0) with blocks/s, the roofline of the dominant
+kernel (block attention) measured live with HIP events, and the CPU oracle
+timed on a bounded sample of the same step.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+BF16_PEAK = 2.5e15         # dense bf16 MFMA flop/s
+METRIC = "draft-step blocks/sec (inject+block attn+verify); % HBM / MFMA peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--batch", type=int, default=64)
+    ap.add_argument("--ctx", type=int, default=8192)
+    ap.add_argument("--block", type=int, default=16)
+    ap.add_argument("--vocab", type=int, default=128256)
+    ap.add_argument("--layers", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=3, help="requests in the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--breakdown", action="store_true", help="per-part timings to stderr")
+    return ap.parse_args()
+
+
+class Step:
+    """Device-resident inputs, outputs and workspaces of one draft step."""
+
+    def __init__(self, B, C, k, V, Ld, d=4096, m=5, Hq=32, Hkv=8, D=128, seed=0):
+        import torch
+        import block_diffusion_draft_ctx_amd as dfl
+        self.dfl = dfl
+        self.B, self.C, self.k, self.V, self.Ld = B, C, k, V, Ld
+        self.d, self.m, self.Hq, self.Hkv, self.D = d, m, Hq, Hkv, D
+        dev = torch.device("cuda:0")
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        bf = torch.bfloat16
+
+        def randn(*shape, std=1.0):
+            return (torch.randn(*shape, generator=g, device=dev, dtype=torch.float32) * std).to(bf)
+
+        T = B * k
+        self.T = T
+        self.hiddens = [randn(T, d) for _ in range(m)]
+        self.W_f = randn(d, m * d, std=0.02)
+        self.b_f = randn(d, std=0.02)
+        self.W_K = [randn(Hkv * D, d, std=0.02) for _ in range(Ld)]
+        self.W_V = [randn(Hkv * D, d, std=0.02) for _ in range(Ld)]
+        # pages for positions [0, C + k) of every request, physically shuffled
+        self.max_pages = (C + k + 15) // 16
+        num_pages = B * self.max_pages
+        perm = torch.randperm(num_pages, generator=g, device=dev).to(torch.int32)
+        self.block_table = perm.view(B, self.max_pages).contiguous()
+        self.num_pages = num_pages
+        self.cache_k = [randn(num_pages, 16, Hkv, D) for _ in range(Ld)]
+        self.cache_v = [randn(num_pages, 16, Hkv, D) for _ in range(Ld)]
+        self.q = [randn(B, k, Hq, D) for _ in range(Ld)]
+        self.k_blk = [randn(B, k, Hkv, D) for _ in range(Ld)]
+        self.v_blk = [randn(B, k, Hkv, D) for _ in range(Ld)]
+        self.attn_out = [torch.empty(B, k, Hq, D, dtype=bf, device=dev) for _ in range(Ld)]
+        self.ctx_lens = torch.full((B,), C, dtype=torch.int32, device=dev)
+        # the rows committed last round sit right after the visible context
+        self.seq_start = torch.full((B,), C, dtype=torch.int32, device=dev)
+        self.commit = torch.full((B,), k, dtype=torch.int32, device=dev)
+        self.target_logits = randn(B, k, V, std=3.0)
+        self.draft_logits = randn(B, k - 1, V, std=3.0)
+        self.draft_tokens = torch.empty(B, k - 1, dtype=torch.int32, device=dev)
+        self.prefix = torch.full((B,), C, dtype=torch.int32, device=dev)
+        L = dfl.lib()
+        self.ws_mat = torch.empty(max(256, L.dflash_materialize_workspace_size(
+            T, m, d, Ld, Hkv, D, dfl.BF16)), dtype=torch.uint8, device=dev)
+        self.ws_att = torch.empty(max(256, L.dflash_attention_workspace_size(
+            B, k, Hq, Hkv, D, self.max_pages, dfl.BF16)), dtype=torch.uint8, device=dev)
+        self.ws_ver = torch.empty(max(256, L.dflash_verify_workspace_size(B, k - 1, V)),
+                                  dtype=torch.uint8, device=dev)
+        self.ver_out = {n: torch.empty(B, dtype=torch.int32, device=dev)
+                        for n in ("accept_len", "bonus", "commit_lens", "new_seq_lens")}
+        self.ver_out["target_predict"] = torch.empty(B, k, dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+
+    def materialize(self):
+        self.dfl.materialize_ctx_kv(self.hiddens, self.W_f, self.b_f, self.W_K, self.W_V,
+                                    self.cache_k, self.cache_v, self.block_table, self.k,
+                                    self.seq_start, self.commit, workspace=self.ws_mat)
+
+    def attention(self, l):
+        self.dfl.block_attention(self.q[l], self.k_blk[l], self.v_blk[l], self.cache_k[l],
+                                 self.cache_v[l], self.block_table, self.ctx_lens,
+                                 out=self.attn_out[l], workspace=self.ws_att)
+
+    def verify(self):
+        self.dfl.verify_greedy(self.target_logits, draft_tokens=self.draft_tokens,
+                               draft_logits=self.draft_logits, prefix_lens=self.prefix,
+                               out=self.ver_out, workspace=self.ws_ver)
+
+    # algorithmic work per launch
+    def attn_bytes(self):
+        B, C, k, Hq, Hkv, D = self.B, self.C, self.k, self.Hq, self.Hkv, self.D
+        return B * C * Hkv * D * 2 * 2 + B * k * (2 * Hq + 2 * Hkv) * D * 2
+
+    def attn_flops(self):
+        return 4.0 * self.B * self.k * self.Hq * self.D * (self.C + self.k)
+
+    def verify_bytes(self):
+        return self.B * (2 * self.k - 1) * self.V * 2
+
+    def mat_flops(self):
+        return 2.0 * self.T * (self.m * self.d ** 2 + 2 * self.Ld * self.Hkv * self.D * self.d)
+
+    def mat_bytes(self):
+        d, m, T = self.d, self.m, self.T
+        w = 2 * (m * d * d + d + 2 * self.Ld * self.Hkv * self.D * d)
+        return T * m * d * 2 + w + T * 2 * self.Ld * self.Hkv * self.D * 2
+
+
+def time_steps(st, steps, warmup):
+    """Run warmup steps, then time `steps` whole steps; HIP events on the
+    launch stream bracket every attention call inside the timed region."""
+    import torch
+    for _ in range(warmup):
+        st.materialize()
+        for l in range(st.Ld):
+            st.attention(l)
+        st.verify()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps * st.Ld)]
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    i = 0
+    for _ in range(steps):
+        st.materialize()
+        for l in range(st.Ld):
+            ev[i][0].record()
+            st.attention(l)
+            ev[i][1].record()
+            i += 1
+        st.verify()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(stop)
+    attn_ms = [a.elapsed_time(b) for a, b in ev]
+    return total_ms / steps, sum(attn_ms) / len(attn_ms), wall
+
+
+def time_part(fn, reps):
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def cpu_baseline(st, n_req):
+    """The oracle, as it stands, on n_req requests of the same step: their
+    materialisation rows, their block attention for every layer, and their
+    greedy verification.  Returns blocks/s on the host and the thread count."""
+    import numpy as np
+    import torch
+    import oracle
+
+    def host(t):
+        t = t.detach().cpu().contiguous()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16)
+        return t.numpy()
+
+    k, C = st.k, st.C
+    rows = slice(0, n_req * k)
+    hid = [host(h[rows]) for h in st.hiddens]
+    Wf, bf = host(st.W_f), host(st.b_f)
+    WK = [host(w) for w in st.W_K]
+    WV = [host(w) for w in st.W_V]
+    bt = host(st.block_table[:n_req])
+    pages = np.unique(bt[bt >= 0])
+    remap = np.full(st.num_pages, -1, dtype=np.int64)
+    remap[pages] = np.arange(len(pages))
+    bt_c = np.where(bt >= 0, remap[np.maximum(bt, 0)], -1).astype(np.int32)
+    idx = torch.from_numpy(pages).to(st.block_table.device)
+    ck = [host(c.index_select(0, idx)) for c in st.cache_k]
+    cv = [host(c.index_select(0, idx)) for c in st.cache_v]
+    q = [host(x[:n_req]) for x in st.q]
+    kb = [host(x[:n_req]) for x in st.k_blk]
+    vb = [host(x[:n_req]) for x in st.v_blk]
+    tl = host(st.target_logits[:n_req])
+    dl = host(st.draft_logits[:n_req])
+    ctx = np.full(n_req, C, dtype=np.int32)
+    t0 = time.perf_counter()
+    res = oracle.materialize(hid, Wf, bf, WK, WV, st.Hkv, st.D, "bf16")
+    for l in range(st.Ld):
+        kc = oracle.widen(ck[l], "bf16")
+        oracle.paged_write(kc, res["K"][l], bt_c, k, np.full(n_req, C), np.full(n_req, k))
+        oracle.block_attention(q[l], kb[l], vb[l], ck[l], cv[l], bt_c, ctx, "bf16")
+    oracle.verify_greedy(tl, "bf16", draft_logits=dl, prefix_lens=np.full(n_req, C))
+    dt = time.perf_counter() - t0
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return n_req / dt, dt, cores
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build "
+              "targets a single MI355X: the step is data parallel by request and needs no "
+              "collective).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    st = Step(args.batch, args.ctx, args.block, args.vocab, args.layers)
+    print(f"[bench] inputs ready: B={st.B} ctx={st.C} k={st.k} V={st.V} layers={st.Ld}",
+          file=sys.stderr, flush=True)
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+    ms, attn_ms, wall = time_steps(st, args.steps, args.warmup)
+    print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+    value = st.B / (ms * 1e-3)
+    ab = st.attn_bytes()
+    achieved = ab / (attn_ms * 1e-3)
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "blocks/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": (f"Llama-3.1-8B-shaped DFlash decode step: batch {st.B}, ctx "
+                                f"{st.C}, block {st.k}, {st.Ld} draft layers (32 Q / 8 KV heads "
+                                f"x 128), d_model 4096 with 5 captured hiddens, greedy verify "
+                                f"over vocab {st.V} with fused draft argmax"),
+                   "batch": st.B, "ctx": st.C, "block": st.k, "draft_layers": st.Ld,
+                   "vocab": st.V, "d_model": st.d, "committed_rows": st.T},
+        "roofline": {"kernel": "block_attention (per layer)", "bound": "hbm",
+                     "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
+                     "traffic": None, "algorithmic_bytes": ab,
+                     "avg_launch_us": round(attn_ms * 1e3, 2)},
+    }
+    if args.breakdown:
+        tm = time_part(st.materialize, 10)
+        tv = time_part(st.verify, 10)
+        br = {"materialize_us": round(tm * 1e3, 1),
+              "materialize_mfma_frac": round(st.mat_flops() / (tm * 1e-3) / BF16_PEAK, 4),
+              "attention_us_per_layer": round(attn_ms * 1e3, 1),
+              "attention_hbm_frac": round(achieved / HBM_PEAK, 4),
+              "verify_us": round(tv * 1e3, 1),
+              "verify_hbm_frac": round(st.verify_bytes() / (tv * 1e-3) / HBM_PEAK, 4)}
+        out["breakdown"] = br
+        print(f"[bench] breakdown {json.dumps(br)}", file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        v, dt, cores = cpu_baseline(st, args.cpu_sample)
+        out["cpu_baseline"] = {
+            "value": round(v, 3), "unit": "blocks/s", "cores": cores, "kind": "oracle",
+            "sample": (f"{args.cpu_sample} of the {st.B} requests of the same step: their "
+                       f"{args.cpu_sample * st.k} committed rows materialised, their block "
+                       f"attention for all {st.Ld} layers at ctx {st.C}, their greedy verify "
+                       f"({st.k} target + {st.k - 1} draft rows each); {dt:.1f} s of CPU work")}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,358 @@
+"""Python binding of the DFlash step library (libdflash.so, C ABI in include/dflash.h).
+
+Argument marshalling only: tensors are PyTorch device tensors (PyTorch is
+used for device memory and streams); every step of the computation runs in
+the HIP kernels behind the C ABI.  There is no fallback: if the library is
+missing this module raises on first use.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdflash.so")
+
+OK, E_ARG, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+
+EXPORTS = (
+    "dflash_status_string", "dflash_version",
+    "dflash_materialize_workspace_size", "dflash_materialize_ctx_kv",
+    "dflash_attention_workspace_size", "dflash_block_attention",
+    "dflash_verify_workspace_size", "dflash_verify_greedy", "dflash_verify_sample",
+    "dflash_gate_workspace_size", "dflash_gate",
+)
+
+
+class KVLayer(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("num_pages", ctypes.c_int32), ("page_size", ctypes.c_int32)]
+
+
+class DFlashError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+P = ctypes.c_void_p
+I32 = ctypes.c_int
+I64 = ctypes.c_int64
+SZ = ctypes.c_size_t
+F = ctypes.c_float
+PP = ctypes.POINTER(ctypes.c_void_p)
+
+
+def _declare(lib):
+    lib.dflash_status_string.restype = ctypes.c_char_p
+    lib.dflash_status_string.argtypes = [I32]
+    lib.dflash_version.restype = I32
+    lib.dflash_version.argtypes = []
+    lib.dflash_materialize_workspace_size.restype = SZ
+    lib.dflash_materialize_workspace_size.argtypes = [I64, I32, I32, I32, I32, I32, I32]
+    lib.dflash_materialize_ctx_kv.restype = I32
+    lib.dflash_materialize_ctx_kv.argtypes = [
+        I64, I32, I32, PP, P, P, I32, I32, I32, PP, PP, ctypes.POINTER(KVLayer), P, I32, I32,
+        P, P, P, I32, P, SZ, P]
+    lib.dflash_attention_workspace_size.restype = SZ
+    lib.dflash_attention_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, I32]
+    lib.dflash_block_attention.restype = I32
+    lib.dflash_block_attention.argtypes = [
+        I32, I32, I32, I32, I32, P, P, P, P, P, I32, I32, P, I32, P, F, P, P, I32, I32, P, SZ, P]
+    lib.dflash_verify_workspace_size.restype = SZ
+    lib.dflash_verify_workspace_size.argtypes = [I32, I32, I32]
+    lib.dflash_verify_greedy.restype = I32
+    lib.dflash_verify_greedy.argtypes = [
+        I32, I32, I32, P, I64, P, I64, P, P, P, P, P, P, P, P, I32, P, SZ, P]
+    lib.dflash_verify_sample.restype = I32
+    lib.dflash_verify_sample.argtypes = [
+        I32, I32, I32, P, I64, P, I64, P, P, P, P, F, P, P, P, P, P, P, P, P, I32, P, SZ, P]
+    lib.dflash_gate_workspace_size.restype = SZ
+    lib.dflash_gate_workspace_size.argtypes = [I32, I32, I32]
+    lib.dflash_gate.restype = I32
+    lib.dflash_gate.argtypes = [I32, I32, I32, P, I64, P, P, F, F, P, P, P, P, I32, P, SZ, P]
+
+
+def lib():
+    """The loaded C library (loads on first use; raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m block_diffusion_draft_ctx_amd.build` first")
+        handle = ctypes.CDLL(LIB_PATH)
+        _declare(handle)
+        _lib = handle
+    return _lib
+
+
+def status_string(s: int) -> str:
+    return lib().dflash_status_string(s).decode()
+
+
+def _check(s: int, what: str):
+    if s != OK:
+        raise DFlashError(s, f"{what}: {status_string(s)}")
+
+
+# ----------------------------------------------------------------------------
+# tensor marshalling
+# ----------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _i32(t, name):
+    torch = _torch()
+    if t is None:
+        return None
+    _dev(t, name)
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+    return t
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _workspace(nbytes, device, ws):
+    torch = _torch()
+    if nbytes == 0:
+        return None, 0
+    if ws is not None and ws.numel() * ws.element_size() >= nbytes:
+        return ws, ws.numel() * ws.element_size()
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return buf, nbytes
+
+
+def _pp(ptrs):
+    arr = (ctypes.c_void_p * len(ptrs))(*ptrs)
+    return ctypes.cast(arr, PP), arr
+
+
+# ----------------------------------------------------------------------------
+# entry points
+# ----------------------------------------------------------------------------
+
+def materialize_ctx_kv(hiddens: Sequence, W_f, b_f, W_K: Sequence, W_V: Sequence,
+                       cache_k: Sequence, cache_v: Sequence, block_table, rows_per_seq: int,
+                       seq_start_pos, commit_lens=None, h_ctx_out=None, workspace=None,
+                       stream=None):
+    """dflash_materialize_ctx_kv.  hiddens: m tensors [T, d]; W_f [d, m*d];
+    b_f [d] or None; W_K/W_V: per-layer [Hkv*D, d]; cache_k/cache_v: per-layer
+    [num_pages, 16, Hkv, D]; block_table [n_seq, max_pages] int32."""
+    L = lib()
+    m = len(hiddens)
+    T, d = hiddens[0].shape
+    for i, h in enumerate(hiddens):
+        _dev(h, f"hiddens[{i}]")
+    dt = _dtype_code(hiddens[0])
+    n_layers = len(W_K)
+    _, _, Hkv, D = cache_k[0].shape
+    _i32(block_table, "block_table")
+    _i32(seq_start_pos, "seq_start_pos")
+    _i32(commit_lens, "commit_lens")
+    caches = (KVLayer * n_layers)(*[KVLayer(_ptr(_dev(k, "cache_k")), _ptr(_dev(v, "cache_v")),
+                                            k.shape[0], k.shape[1])
+                                    for k, v in zip(cache_k, cache_v)])
+    need = L.dflash_materialize_workspace_size(T, m, d, n_layers, Hkv, D, dt)
+    ws, nws = _workspace(need, hiddens[0].device, workspace)
+    hp, _h = _pp([_ptr(h) for h in hiddens])
+    kp, _k = _pp([_ptr(_dev(w, "W_K")) for w in W_K])
+    vp, _v = _pp([_ptr(_dev(w, "W_V")) for w in W_V])
+    s = L.dflash_materialize_ctx_kv(
+        T, m, d, hp, _ptr(_dev(W_f, "W_f")), _ptr(b_f), n_layers, Hkv, D, kp, vp, caches,
+        _ptr(block_table), block_table.shape[1], rows_per_seq, _ptr(seq_start_pos),
+        _ptr(commit_lens), _ptr(h_ctx_out), dt, _ptr(ws), nws, _stream(stream))
+    _check(s, "dflash_materialize_ctx_kv")
+    return h_ctx_out
+
+
+def block_attention(q, k_blk, v_blk, cache_k, cache_v, block_table, ctx_lens, scale=0.0,
+                    out=None, lse=None, workspace=None, stream=None, out_dtype=None):
+    """dflash_block_attention.  q [B,k,Hq,D]; k_blk/v_blk [B,k,Hkv,D]; caches
+    [num_pages,16,Hkv,D]; block_table [B,max_pages]; ctx_lens [B].  The output
+    takes the dtype of ``out`` (or ``out_dtype``, default: q's dtype).  Returns
+    (out, lse) where lse is the tensor given (or None)."""
+    torch = _torch()
+    L = lib()
+    B, k, Hq, D = q.shape
+    Hkv = k_blk.shape[2]
+    dt = _dtype_code(q)
+    for n, t in (("q", q), ("k_blk", k_blk), ("v_blk", v_blk), ("cache_k", cache_k),
+                 ("cache_v", cache_v)):
+        _dev(t, n)
+    _i32(block_table, "block_table")
+    _i32(ctx_lens, "ctx_lens")
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    _dev(out, "out")
+    odt = _dtype_code(out)
+    need = L.dflash_attention_workspace_size(B, k, Hq, Hkv, D, block_table.shape[1], dt)
+    ws, nws = _workspace(need, q.device, workspace)
+    s = L.dflash_block_attention(
+        B, k, Hq, Hkv, D, _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(cache_k), _ptr(cache_v),
+        cache_k.shape[0], cache_k.shape[1], _ptr(block_table), block_table.shape[1],
+        _ptr(ctx_lens), float(scale), _ptr(out), _ptr(lse), dt, odt, _ptr(ws), nws,
+        _stream(stream))
+    _check(s, "dflash_block_attention")
+    return out, lse
+
+
+def _logit_rows(t, name):
+    """Row stride (elements) of a [B, R, V] logits view whose rows are evenly
+    spaced (contiguous, or a slice of a wider row buffer)."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    B, R, V = t.shape
+    if t.stride(2) != 1 or (B > 1 and t.stride(0) != R * t.stride(1)) or t.stride(1) < V:
+        raise ValueError(f"{name}: rows must be evenly spaced with unit element stride")
+    return t.stride(1)
+
+
+def _row_stride(t):
+    return _logit_rows(t, "logits")
+
+
+def verify_greedy(target_logits, draft_tokens=None, draft_logits=None, chain_lens=None,
+                  prefix_lens=None, want_target_predict=True, out=None, workspace=None,
+                  stream=None):
+    """dflash_verify_greedy.  target_logits [B, L+1, V]; draft_logits [B, L, V]
+    or None (then draft_tokens [B, L] int32 is the input).  Returns a dict of
+    device tensors: accept_len, bonus, commit_lens, new_seq_lens (if
+    prefix_lens), target_predict (if wanted), draft_tokens."""
+    torch = _torch()
+    L_ = lib()
+    _logit_rows(target_logits, "target_logits")
+    B, Lp1, V = target_logits.shape
+    L = Lp1 - 1
+    dt = _dtype_code(target_logits)
+    dev = target_logits.device
+    o = dict(out or {})
+    if draft_logits is not None:
+        _logit_rows(draft_logits, "draft_logits")
+        if draft_tokens is None:
+            draft_tokens = torch.empty((B, L), dtype=torch.int32, device=dev)
+    _i32(draft_tokens, "draft_tokens")
+    _i32(chain_lens, "chain_lens")
+    _i32(prefix_lens, "prefix_lens")
+    for name in ("accept_len", "bonus", "commit_lens"):
+        o.setdefault(name, torch.empty(B, dtype=torch.int32, device=dev))
+    if prefix_lens is not None:
+        o.setdefault("new_seq_lens", torch.empty(B, dtype=torch.int32, device=dev))
+    if want_target_predict:
+        o.setdefault("target_predict", torch.empty((B, L + 1), dtype=torch.int32, device=dev))
+    need = L_.dflash_verify_workspace_size(B, L, V)
+    ws, nws = _workspace(need, dev, workspace)
+    s = L_.dflash_verify_greedy(
+        B, L, V, _ptr(target_logits), _row_stride(target_logits), _ptr(draft_logits),
+        _row_stride(draft_logits) if draft_logits is not None else 0, _ptr(draft_tokens),
+        _ptr(chain_lens), _ptr(o.get("target_predict")), _ptr(o["accept_len"]), _ptr(o["bonus"]),
+        _ptr(o["commit_lens"]), _ptr(prefix_lens), _ptr(o.get("new_seq_lens")), dt, _ptr(ws),
+        nws, _stream(stream))
+    _check(s, "dflash_verify_greedy")
+    o["draft_tokens"] = draft_tokens
+    return o
+
+
+def verify_sample(target_logits, draft_logits, draft_tokens, u_accept, u_bonus, temperature=1.0,
+                  chain_lens=None, prefix_lens=None, audit=True, out=None, workspace=None,
+                  stream=None):
+    """dflash_verify_sample.  Returns a dict with accept_len, bonus,
+    commit_lens, new_seq_lens (if prefix_lens) and, with ``audit``, ratio
+    [B, L], beta [B] and cdf_gap [B]."""
+    torch = _torch()
+    L_ = lib()
+    _logit_rows(target_logits, "target_logits")
+    B, Lp1, V = target_logits.shape
+    L = Lp1 - 1
+    dt = _dtype_code(target_logits)
+    dev = target_logits.device
+    if draft_logits is not None:
+        _logit_rows(draft_logits, "draft_logits")
+    _i32(draft_tokens, "draft_tokens")
+    _i32(chain_lens, "chain_lens")
+    _i32(prefix_lens, "prefix_lens")
+    for n, t in (("u_accept", u_accept), ("u_bonus", u_bonus)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{n} must be float32")
+        if t is not None:
+            _dev(t, n)
+    o = dict(out or {})
+    for name in ("accept_len", "bonus", "commit_lens"):
+        o.setdefault(name, torch.empty(B, dtype=torch.int32, device=dev))
+    if prefix_lens is not None:
+        o.setdefault("new_seq_lens", torch.empty(B, dtype=torch.int32, device=dev))
+    if audit:
+        o.setdefault("ratio", torch.empty((B, L), dtype=torch.float32, device=dev))
+        o.setdefault("beta", torch.empty(B, dtype=torch.float32, device=dev))
+        o.setdefault("cdf_gap", torch.empty(B, dtype=torch.float32, device=dev))
+    need = L_.dflash_verify_workspace_size(B, L, V)
+    ws, nws = _workspace(need, dev, workspace)
+    s = L_.dflash_verify_sample(
+        B, L, V, _ptr(target_logits), _row_stride(target_logits), _ptr(draft_logits),
+        _row_stride(draft_logits) if draft_logits is not None else 0, _ptr(draft_tokens),
+        _ptr(chain_lens), _ptr(u_accept), _ptr(u_bonus), float(temperature),
+        _ptr(o["accept_len"]), _ptr(o["bonus"]), _ptr(o["commit_lens"]), _ptr(prefix_lens),
+        _ptr(o.get("new_seq_lens")), _ptr(o.get("ratio")), _ptr(o.get("beta")),
+        _ptr(o.get("cdf_gap")), dt, _ptr(ws), nws, _stream(stream))
+    _check(s, "dflash_verify_sample")
+    return o
+
+
+def gate(draft_logits, draft_tokens, temperature=1.0, g=-0.5, valid_lens=None, row_stats=True,
+         out=None, workspace=None, stream=None):
+    """dflash_gate.  Returns a dict with c [B], go [B] and, with row_stats,
+    row_max and row_lse [B, n]."""
+    torch = _torch()
+    L_ = lib()
+    _logit_rows(draft_logits, "draft_logits")
+    B, n, V = draft_logits.shape
+    dt = _dtype_code(draft_logits)
+    dev = draft_logits.device
+    _i32(draft_tokens, "draft_tokens")
+    _i32(valid_lens, "valid_lens")
+    o = dict(out or {})
+    o.setdefault("c", torch.empty(B, dtype=torch.float32, device=dev))
+    o.setdefault("go", torch.empty(B, dtype=torch.int32, device=dev))
+    if row_stats:
+        o.setdefault("row_max", torch.empty((B, n), dtype=torch.float32, device=dev))
+        o.setdefault("row_lse", torch.empty((B, n), dtype=torch.float32, device=dev))
+    need = L_.dflash_gate_workspace_size(B, n, V)
+    ws, nws = _workspace(need, dev, workspace)
+    s = L_.dflash_gate(B, n, V, _ptr(draft_logits), _row_stride(draft_logits), _ptr(draft_tokens),
+                       _ptr(valid_lens), float(temperature), float(g), _ptr(o["c"]), _ptr(o["go"]),
+                       _ptr(o.get("row_max")), _ptr(o.get("row_lse")), dt, _ptr(ws), nws,
+                       _stream(stream))
+    _check(s, "dflash_gate")
+    return o

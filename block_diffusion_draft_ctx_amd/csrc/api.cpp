@@ -1,0 +1,236 @@
+// C ABI of the DFlash step: argument validation, workspace sizing, dispatch.
+// Every host-visible argument error is reported before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/dflash.h"
+#include "launch.h"
+
+using namespace dflash;
+
+namespace {
+
+constexpr int kMaxL = 64;
+constexpr size_t kWsAlign = 256;
+
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool bad_dtype(dflash_dtype d) { return d != DFLASH_F32 && d != DFLASH_BF16; }
+
+dflash_status check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return DFLASH_OK;
+  if (!ws || have < need) return DFLASH_E_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % kWsAlign) return DFLASH_E_WORKSPACE;
+  return DFLASH_OK;
+}
+
+dflash_status hip_status(hipError_t e) { return e == hipSuccess ? DFLASH_OK : DFLASH_E_HIP; }
+
+// Shared checks of the verify entry points.
+dflash_status check_verify_common(int B, int L, int V, const void* tl, int64_t ts,
+                                  const void* dl, int64_t ds, bool need_dl) {
+  if (B < 0 || L < 0 || V < 1) return DFLASH_E_ARG;
+  if (L > kMaxL) return DFLASH_E_UNSUPPORTED;
+  if (B == 0) return DFLASH_OK;
+  if (!tl || ts < V) return DFLASH_E_ARG;
+  if ((need_dl && !dl) || (dl && ds < V)) return DFLASH_E_ARG;
+  return DFLASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dflash_status_string(dflash_status s) {
+  switch (s) {
+    case DFLASH_OK: return "DFLASH_OK";
+    case DFLASH_E_ARG: return "DFLASH_E_ARG: invalid argument";
+    case DFLASH_E_UNSUPPORTED: return "DFLASH_E_UNSUPPORTED: shape or dtype not implemented";
+    case DFLASH_E_WORKSPACE: return "DFLASH_E_WORKSPACE: workspace missing, too small or misaligned";
+    case DFLASH_E_HIP: return "DFLASH_E_HIP: kernel launch failed";
+  }
+  return "DFLASH_E_UNKNOWN";
+}
+
+int dflash_version(void) { return 100; }
+
+// ------------------------------------------------------------ materialise
+size_t dflash_materialize_workspace_size(int64_t T, int m, int d_model, int n_layers,
+                                         int n_kv_heads, int head_dim, dflash_dtype dtype) {
+  if (T <= 0 || m <= 0 || d_model <= 0 || n_layers <= 0 || n_kv_heads <= 0 || head_dim <= 0)
+    return 0;
+  return materialize_ws_bytes(T, m, d_model, n_layers, n_kv_heads, head_dim, dtype == DFLASH_BF16);
+}
+
+dflash_status dflash_materialize_ctx_kv(
+    int64_t T, int m, int d_model, const void* const* hiddens, const void* W_f, const void* b_f,
+    int n_layers, int n_kv_heads, int head_dim, const void* const* W_K, const void* const* W_V,
+    const dflash_kv_layer* caches, const int32_t* block_table, int max_pages_per_seq,
+    int rows_per_seq, const int32_t* seq_start_pos, const int32_t* commit_lens, void* h_ctx_out,
+    dflash_dtype dtype, void* ws, size_t ws_bytes, dflash_stream_t stream) {
+  if (bad_dtype(dtype)) return DFLASH_E_ARG;
+  if (T < 0 || m < 1 || d_model < 1 || n_layers < 1 || n_kv_heads < 1 || head_dim < 1)
+    return DFLASH_E_ARG;
+  if (m > 8 || n_layers > kMaxLayers) return DFLASH_E_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return DFLASH_E_UNSUPPORTED;
+  if (T == 0) return DFLASH_OK;
+  if (T > INT32_MAX || (int64_t)m * d_model > INT32_MAX) return DFLASH_E_UNSUPPORTED;
+  if (rows_per_seq < 1 || T % rows_per_seq != 0 || max_pages_per_seq < 1) return DFLASH_E_ARG;
+  if (!hiddens || !W_f || !W_K || !W_V || !caches || !block_table || !seq_start_pos)
+    return DFLASH_E_ARG;
+  const bool bf16 = dtype == DFLASH_BF16;
+  const int HD = n_kv_heads * head_dim;
+  if (bf16 && (d_model % 128 != 0 || HD % 128 != 0)) return DFLASH_E_UNSUPPORTED;
+  MatArgs a{};
+  a.T = T; a.m = m; a.d = d_model;
+  for (int s = 0; s < m; ++s) {
+    if (!hiddens[s]) return DFLASH_E_ARG;
+    if (bf16 && !al16(hiddens[s])) return DFLASH_E_UNSUPPORTED;
+    a.hiddens[s] = hiddens[s];
+  }
+  if (bf16 && (!al16(W_f) || (h_ctx_out && !al16(h_ctx_out)))) return DFLASH_E_UNSUPPORTED;
+  a.W_f = W_f; a.b_f = b_f;
+  a.n_layers = n_layers; a.Hkv = n_kv_heads; a.D = head_dim;
+  for (int l = 0; l < n_layers; ++l) {
+    if (!W_K[l] || !W_V[l] || !caches[l].k || !caches[l].v) return DFLASH_E_ARG;
+    if (caches[l].page_size != 16) return DFLASH_E_UNSUPPORTED;
+    if (caches[l].num_pages < 1) return DFLASH_E_ARG;
+    if (bf16 && (!al16(W_K[l]) || !al16(W_V[l]))) return DFLASH_E_UNSUPPORTED;
+    a.W_K[l] = W_K[l]; a.W_V[l] = W_V[l];
+    a.cache_k[l] = caches[l].k; a.cache_v[l] = caches[l].v;
+    a.num_pages[l] = caches[l].num_pages;
+  }
+  a.block_table = block_table; a.max_pages = max_pages_per_seq;
+  a.rows_per_seq = rows_per_seq; a.seq_start = seq_start_pos; a.commit_lens = commit_lens;
+  a.h_out = h_ctx_out;
+  const size_t need = materialize_ws_bytes(T, m, d_model, n_layers, n_kv_heads, head_dim, bf16);
+  if (dflash_status s = check_ws(ws, ws_bytes, need)) return s;
+  return hip_status(launch_materialize(bf16, a, ws, ws_bytes, static_cast<hipStream_t>(stream)));
+}
+
+// --------------------------------------------------------------- attention
+size_t dflash_attention_workspace_size(int B, int k, int n_q_heads, int n_kv_heads, int head_dim,
+                                       int max_pages_per_seq, dflash_dtype dtype) {
+  if (B <= 0 || k <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 ||
+      max_pages_per_seq <= 0 || n_q_heads % n_kv_heads)
+    return 0;
+  if (dtype != DFLASH_BF16) return 0;
+  return attention_ws_bytes(B, k, n_q_heads, n_kv_heads, head_dim, max_pages_per_seq, true);
+}
+
+dflash_status dflash_block_attention(int B, int k, int n_q_heads, int n_kv_heads, int head_dim,
+                                     const void* q, const void* k_blk, const void* v_blk,
+                                     const void* cache_k, const void* cache_v, int num_pages,
+                                     int page_size, const int32_t* block_table,
+                                     int max_pages_per_seq, const int32_t* ctx_lens, float scale,
+                                     void* out, float* lse_out, dflash_dtype dtype,
+                                     dflash_dtype out_dtype, void* ws, size_t ws_bytes,
+                                     dflash_stream_t stream) {
+  if (bad_dtype(dtype) || bad_dtype(out_dtype)) return DFLASH_E_ARG;
+  if (dtype == DFLASH_F32 && out_dtype != DFLASH_F32) return DFLASH_E_UNSUPPORTED;
+  if (B < 0 || k < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1) return DFLASH_E_ARG;
+  if (n_q_heads % n_kv_heads) return DFLASH_E_ARG;
+  if (head_dim != 64 && head_dim != 128) return DFLASH_E_UNSUPPORTED;
+  if (k > 64 || (n_q_heads / n_kv_heads) * k > 256) return DFLASH_E_UNSUPPORTED;
+  if (page_size != 16) return DFLASH_E_UNSUPPORTED;
+  if (!(scale >= 0.f)) return DFLASH_E_ARG;
+  if (B == 0) return DFLASH_OK;
+  if (num_pages < 1 || max_pages_per_seq < 1) return DFLASH_E_ARG;
+  if (!q || !k_blk || !v_blk || !cache_k || !cache_v || !block_table || !ctx_lens || !out)
+    return DFLASH_E_ARG;
+  const bool bf16 = dtype == DFLASH_BF16;
+  if (bf16 && !(al16(q) && al16(k_blk) && al16(v_blk) && al16(cache_k) && al16(cache_v) && al16(out)))
+    return DFLASH_E_UNSUPPORTED;
+  const size_t need = bf16 ? attention_ws_bytes(B, k, n_q_heads, n_kv_heads, head_dim,
+                                                max_pages_per_seq, true)
+                           : 0;
+  if (dflash_status s = check_ws(ws, ws_bytes, need)) return s;
+  AttnArgs a{B, k, n_q_heads, n_kv_heads, head_dim, q, k_blk, v_blk, cache_k, cache_v, num_pages,
+             block_table, max_pages_per_seq, ctx_lens, scale, out, lse_out,
+             out_dtype == DFLASH_F32};
+  return hip_status(launch_attention(bf16, a, ws, static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------------------------ verify
+size_t dflash_verify_workspace_size(int B, int L, int V) {
+  if (B <= 0 || L < 0 || L > kMaxL || V < 1) return 0;
+  const size_t a = greedy_ws_bytes(B, L, V), b = sample_ws_bytes(B, L, V);
+  return a > b ? a : b;
+}
+
+dflash_status dflash_verify_greedy(int B, int L, int V, const void* target_logits,
+                                   int64_t t_row_stride, const void* draft_logits,
+                                   int64_t d_row_stride, int32_t* draft_tokens,
+                                   const int32_t* chain_lens, int32_t* target_predict,
+                                   int32_t* accept_len, int32_t* bonus, int32_t* commit_lens,
+                                   const int32_t* prefix_lens, int32_t* new_seq_lens,
+                                   dflash_dtype dtype, void* ws, size_t ws_bytes,
+                                   dflash_stream_t stream) {
+  if (bad_dtype(dtype)) return DFLASH_E_ARG;
+  if (dflash_status s = check_verify_common(B, L, V, target_logits, t_row_stride, draft_logits,
+                                            d_row_stride, false))
+    return s;
+  if (B == 0) return DFLASH_OK;
+  if ((L > 0 && !draft_tokens) || !accept_len || !bonus || !commit_lens) return DFLASH_E_ARG;
+  if ((prefix_lens == nullptr) != (new_seq_lens == nullptr)) return DFLASH_E_ARG;
+  if (dflash_status s = check_ws(ws, ws_bytes, greedy_ws_bytes(B, L, V))) return s;
+  return hip_status(launch_verify_greedy(dtype == DFLASH_BF16, B, L, V, target_logits,
+                                         t_row_stride, draft_logits, d_row_stride, draft_tokens,
+                                         chain_lens, target_predict, accept_len, bonus,
+                                         commit_lens, prefix_lens, new_seq_lens, ws,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+dflash_status dflash_verify_sample(int B, int L, int V, const void* target_logits,
+                                   int64_t t_row_stride, const void* draft_logits,
+                                   int64_t d_row_stride, const int32_t* draft_tokens,
+                                   const int32_t* chain_lens, const float* u_accept,
+                                   const float* u_bonus, float temperature, int32_t* accept_len,
+                                   int32_t* bonus, int32_t* commit_lens,
+                                   const int32_t* prefix_lens, int32_t* new_seq_lens,
+                                   float* ratio_out, float* beta_out, float* u_cdf_gap_out,
+                                   dflash_dtype dtype, void* ws, size_t ws_bytes,
+                                   dflash_stream_t stream) {
+  if (bad_dtype(dtype)) return DFLASH_E_ARG;
+  if (!(temperature > 0.f) || temperature == __builtin_huge_valf()) return DFLASH_E_ARG;
+  if (dflash_status s = check_verify_common(B, L, V, target_logits, t_row_stride, draft_logits,
+                                            d_row_stride, L > 0))
+    return s;
+  if (B == 0) return DFLASH_OK;
+  if ((L > 0 && (!draft_tokens || !u_accept)) || !u_bonus || !accept_len || !bonus ||
+      !commit_lens)
+    return DFLASH_E_ARG;
+  if ((prefix_lens == nullptr) != (new_seq_lens == nullptr)) return DFLASH_E_ARG;
+  if (dflash_status s = check_ws(ws, ws_bytes, sample_ws_bytes(B, L, V))) return s;
+  return hip_status(launch_verify_sample(
+      dtype == DFLASH_BF16, B, L, V, target_logits, t_row_stride,
+      draft_logits ? draft_logits : target_logits, draft_logits ? d_row_stride : t_row_stride,
+      draft_tokens, chain_lens, u_accept, u_bonus, temperature, accept_len, bonus, commit_lens,
+      prefix_lens, new_seq_lens, ratio_out, beta_out, u_cdf_gap_out, ws,
+      static_cast<hipStream_t>(stream)));
+}
+
+// -------------------------------------------------------------------- gate
+size_t dflash_gate_workspace_size(int B, int n, int V) {
+  if (B <= 0 || n < 1 || n > kMaxL || V < 1) return 0;
+  return gate_ws_bytes(B, n, V);
+}
+
+dflash_status dflash_gate(int B, int n, int V, const void* draft_logits, int64_t row_stride,
+                          const int32_t* draft_tokens, const int32_t* valid_lens,
+                          float temperature, float g, float* c_out, int32_t* go_out,
+                          float* row_max_out, float* row_lse_out, dflash_dtype dtype, void* ws,
+                          size_t ws_bytes, dflash_stream_t stream) {
+  if (bad_dtype(dtype)) return DFLASH_E_ARG;
+  if (B < 0 || n < 1 || V < 1) return DFLASH_E_ARG;
+  if (n > kMaxL) return DFLASH_E_UNSUPPORTED;
+  if (!(temperature > 0.f) || temperature == __builtin_huge_valf() || g != g) return DFLASH_E_ARG;
+  if (B == 0) return DFLASH_OK;
+  if (!draft_logits || row_stride < V || !draft_tokens || !c_out || !go_out) return DFLASH_E_ARG;
+  if (dflash_status s = check_ws(ws, ws_bytes, gate_ws_bytes(B, n, V))) return s;
+  return hip_status(launch_gate(dtype == DFLASH_BF16, B, n, V, draft_logits, row_stride,
+                                draft_tokens, valid_lens, temperature, g, c_out, go_out,
+                                row_max_out, row_lse_out, ws, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

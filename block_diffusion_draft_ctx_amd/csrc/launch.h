@@ -1,0 +1,97 @@
+// Internal launch interface between the C-ABI layer (api.cpp) and the kernel
+// translation units.  Arguments here are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dflash {
+
+// ---------------------------------------------------------------- vocab pass
+// Chunking of a vocabulary row: every row is cut into n_chunks pieces of
+// `chunk` elements (a multiple of 8) and one workgroup reduces one piece.
+struct VocabPlan {
+  int chunk;
+  int n_chunks;
+};
+VocabPlan plan_vocab(int64_t n_rows, int V);
+
+struct RowSet {
+  const void* base;     // first row
+  int64_t stride;       // elements between rows
+  int rows_per_req;     // rows of request b are b*rows_per_req + i
+  int extra;            // row i is read iff i < n_b + extra
+};
+
+size_t greedy_ws_bytes(int B, int L, int V);
+size_t sample_ws_bytes(int B, int L, int V);
+size_t gate_ws_bytes(int B, int n, int V);
+
+hipError_t launch_verify_greedy(bool bf16, int B, int L, int V, const void* tl, int64_t ts,
+                                const void* dl, int64_t ds, int32_t* draft_tokens,
+                                const int32_t* chain_lens, int32_t* target_predict,
+                                int32_t* accept_len, int32_t* bonus, int32_t* commit_lens,
+                                const int32_t* prefix_lens, int32_t* new_seq_lens, void* ws,
+                                hipStream_t st);
+
+hipError_t launch_verify_sample(bool bf16, int B, int L, int V, const void* tl, int64_t ts,
+                                const void* dl, int64_t ds, const int32_t* draft_tokens,
+                                const int32_t* chain_lens, const float* u_accept,
+                                const float* u_bonus, float temperature, int32_t* accept_len,
+                                int32_t* bonus, int32_t* commit_lens, const int32_t* prefix_lens,
+                                int32_t* new_seq_lens, float* ratio_out, float* beta_out,
+                                float* gap_out, void* ws, hipStream_t st);
+
+hipError_t launch_gate(bool bf16, int B, int n, int V, const void* dl, int64_t rs,
+                       const int32_t* tokens, const int32_t* valid_lens, float temperature,
+                       float g, float* c_out, int32_t* go_out, float* row_max, float* row_lse,
+                       void* ws, hipStream_t st);
+
+// ----------------------------------------------------------------- attention
+struct AttnArgs {
+  int B, k, Hq, Hkv, D;
+  const void* q;
+  const void* k_blk;
+  const void* v_blk;
+  const void* cache_k;
+  const void* cache_v;
+  int num_pages;
+  const int32_t* block_table;
+  int max_pages;
+  const int32_t* ctx_lens;
+  float scale;
+  void* out;
+  float* lse;
+  bool out_f32;  // bf16 inputs with an fp32 output
+};
+int attention_splits(int B, int Hkv, int k, int max_pages);
+size_t attention_ws_bytes(int B, int k, int Hq, int Hkv, int D, int max_pages, bool bf16);
+hipError_t launch_attention(bool bf16, const AttnArgs& a, void* ws, hipStream_t st);
+
+// ----------------------------------------------------------- materialisation
+struct MatArgs {
+  int64_t T;
+  int m, d;
+  const void* hiddens[8];
+  const void* W_f;
+  const void* b_f;
+  int n_layers, Hkv, D;
+  const void* W_K[64];
+  const void* W_V[64];
+  void* cache_k[64];
+  void* cache_v[64];
+  int num_pages[64];
+  const int32_t* block_table;
+  int max_pages;
+  int rows_per_seq;
+  const int32_t* seq_start;
+  const int32_t* commit_lens;
+  void* h_out;
+};
+constexpr int kMaxLayers = 64;
+size_t materialize_ws_bytes(int64_t T, int m, int d, int n_layers, int Hkv, int D, bool bf16);
+hipError_t launch_materialize(bool bf16, const MatArgs& a, void* ws, size_t ws_bytes,
+                              hipStream_t st);
+
+}  // namespace dflash

@@ -1,0 +1,708 @@
+// Vocabulary-wide verification and the DLoop gate.
+//
+// Greedy acceptance: [SGLang DFlash], section 3 (target prediction = row
+// argmax; leading matches; bonus = prediction at accept_len).
+// Rejection sampling: [Spec tutorial], section 3 (accept with min(1, p/q);
+// residual max(0, p - q) renormalised) and section 4 (first rejection ends the
+// chain); all-accepted bonus from the next target row ([DFlash overview],
+// pseudocode); chains of several stages ([DLoop], "验证与无损性").
+// Gate: [DLoop], "机制一：置信度门控" (c = sum of drafted-token log-probs,
+// continue iff c >= g).
+//
+// Design.  Every logit row is read once, coalesced, by workgroups that each
+// reduce one chunk of the row (16-byte loads, 4 in flight per lane).  A chunk
+// reduces to (max, lowest argmax) for greedy, or to (m, s) with
+// m = max(z), s = sum 2^(z - m), z = logit * log2(e) / T for the softmax
+// normalisers.  Small per-request kernels merge the chunk partials in a fixed
+// order (deterministic), run the sequential acceptance scan, and -- for a
+// rejection or the all-accepted bonus -- re-read the one chosen row pair
+// (cache-resident) to build the inverse CDF: per-chunk weight sums, then a
+// chunk-local scan inside the selected chunk.
+#include <climits>
+
+#include "common.h"
+#include "launch.h"
+
+namespace dflash {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxChunks = 64;
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct ReqInfo {
+  int row;    // bonus row index within the request (= accept_len)
+  int mode;   // 0: residual of a rejected row, 1: bonus from p of the row
+  int acc;    // accept_len
+  int err;    // in-band error
+  float Mt, St, Md, Sd;  // base-2 normalisers of the chosen rows
+};
+
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int chain_of(const int32_t* lens, int b, int L, bool* bad) {
+  if (!lens) { if (bad) *bad = false; return L; }
+  int v = lens[b];
+  bool b_ = (v < 0 || v > L);
+  if (bad) *bad = b_;
+  return b_ ? L : v;
+}
+
+// Map a flat row index of the launch to (set, b, i, row pointer).
+template <typename T>
+__device__ __forceinline__ bool locate_row(const RowSet& s0, const RowSet& s1, int B, int L,
+                                           const int32_t* lens, int r, const T** row) {
+  const int rows0 = B * s0.rows_per_req;
+  const RowSet& s = (r < rows0) ? s0 : s1;
+  const int rl = (r < rows0) ? r : r - rows0;
+  const int b = rl / s.rows_per_req;
+  const int i = rl - b * s.rows_per_req;
+  const int nb = chain_of(lens, b, L, nullptr);
+  if (i >= nb + s.extra) return false;
+  *row = static_cast<const T*>(s.base) + (int64_t)rl * s.stride;
+  return true;
+}
+
+// ---------------------------------------------------------------- argmax pass
+__device__ __forceinline__ void am_update(const float (&v)[8], int x, float& best, int& bi) {
+  float m8 = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])),
+                   fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+  if (m8 > best) {
+    best = m8;
+#pragma unroll
+    for (int j = 7; j >= 0; --j)
+      if (v[j] == m8) bi = x + j;  // the loop runs downward, so the lowest j wins
+  }
+}
+__device__ __forceinline__ void am_merge(float& best, int& bi, float ob, int oi) {
+  if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_row_argmax(RowSet s0, RowSet s1, int B, int L,
+                                                         int V, const int32_t* __restrict__ lens,
+                                                         int chunk, int n_chunks,
+                                                         float* __restrict__ pmax,
+                                                         int* __restrict__ pidx) {
+  const int c = blockIdx.x % n_chunks;
+  const int r = blockIdx.x / n_chunks;
+  const T* row;
+  if (!locate_row<T>(s0, s1, B, L, lens, r, &row)) return;
+  const int x0 = c * chunk;
+  const int x1 = min(V, x0 + chunk);
+  float best = neg_inf();
+  int bi = INT_MAX;
+  if (VEC) {
+    const int nvec = (x1 - x0) >> 3;
+    int v = threadIdx.x;
+    for (; v + 3 * kThreads < nvec; v += 4 * kThreads) {
+      float a[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) load8(row + x0 + (v + u * kThreads) * 8, a[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) am_update(a[u], x0 + (v + u * kThreads) * 8, best, bi);
+    }
+    for (; v < nvec; v += kThreads) {
+      float a[8];
+      load8(row + x0 + v * 8, a);
+      am_update(a, x0 + v * 8, best, bi);
+    }
+    for (int x = x0 + nvec * 8 + threadIdx.x; x < x1; x += kThreads) {
+      float e = load1(row + x);
+      if (e > best) { best = e; bi = x; }
+    }
+  } else {
+    for (int x = x0 + threadIdx.x; x < x1; x += kThreads) {
+      float e = load1(row + x);
+      if (e > best) { best = e; bi = x; }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float ob = __shfl_xor(best, o, 64);
+    int oi = __shfl_xor(bi, o, 64);
+    am_merge(best, bi, ob, oi);
+  }
+  __shared__ float sb[kThreads / 64];
+  __shared__ int si[kThreads / 64];
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { sb[w] = best; si[w] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < kThreads / 64; ++k) am_merge(sb[0], si[0], sb[k], si[k]);
+    pmax[blockIdx.x] = sb[0];
+    pidx[blockIdx.x] = si[0];
+  }
+}
+
+__device__ int reduce_argmax_row(const float* pmax, const int* pidx, int row, int nc) {
+  float best = neg_inf();
+  int bi = INT_MAX;
+  for (int c = 0; c < nc; ++c) am_merge(best, bi, pmax[row * nc + c], pidx[row * nc + c]);
+  return bi == INT_MAX ? 0 : bi;  // an all -inf row: every entry ties, the first wins
+}
+
+__global__ __launch_bounds__(128) void k_greedy_finalize(
+    int B, int L, int V, int nc, const float* __restrict__ pmax, const int* __restrict__ pidx,
+    int have_dl, int32_t* __restrict__ draft_tokens, const int32_t* __restrict__ lens,
+    int32_t* __restrict__ target_predict, int32_t* __restrict__ accept_len,
+    int32_t* __restrict__ bonus, int32_t* __restrict__ commit,
+    const int32_t* __restrict__ prefix, int32_t* __restrict__ new_seq) {
+  const int b = blockIdx.x;
+  const int t = threadIdx.x;
+  __shared__ int tp[65];
+  __shared__ int dt[64];
+  bool bad;
+  const int nb = chain_of(lens, b, L, &bad);
+  if (t <= L) {
+    int v = -1;
+    if (t <= nb) v = reduce_argmax_row(pmax, pidx, b * (L + 1) + t, nc);
+    tp[t] = v;
+    if (target_predict) target_predict[b * (L + 1) + t] = v;
+  }
+  if (t < L) {
+    int v = -1;
+    if (have_dl) {
+      if (t < nb) {
+        v = reduce_argmax_row(pmax, pidx, B * (L + 1) + b * L + t, nc);
+        draft_tokens[b * L + t] = v;
+      }
+    } else {
+      v = draft_tokens[b * L + t];
+    }
+    dt[t] = v;
+  }
+  __syncthreads();
+  if (t == 0) {
+    bool err = bad;
+    for (int i = 0; i < nb; ++i) err |= (dt[i] < 0 || dt[i] >= V);
+    int a = -1, bo = -1;
+    if (!err) {
+      a = 0;
+      while (a < nb && dt[a] == tp[a]) ++a;
+      bo = tp[a];
+    }
+    const int cm = err ? 0 : a + 1;
+    accept_len[b] = a;
+    bonus[b] = bo;
+    commit[b] = cm;
+    if (new_seq) new_seq[b] = prefix[b] + cm;
+  }
+}
+
+// ------------------------------------------------------------ softmax pass
+__device__ __forceinline__ void lse_update(const float (&v)[8], float a, float& m, float& s) {
+  float xm = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])),
+                   fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+  float gm = xm * a;
+  if (gm > m) {
+    s *= fexp2(m - gm);
+    m = gm;
+  }
+  if (m != neg_inf()) {
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc += fexp2(fmaf(v[j], a, -m));
+    s += acc;
+  }
+}
+__device__ __forceinline__ void lse_update1(float v, float a, float& m, float& s) {
+  float z = v * a;
+  if (z > m) { s *= fexp2(m - z); m = z; }
+  if (m != neg_inf()) s += fexp2(z - m);
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_row_lse(RowSet s0, RowSet s1, int B, int L, int V,
+                                                      const int32_t* __restrict__ lens, float a,
+                                                      int chunk, int n_chunks,
+                                                      float2* __restrict__ part) {
+  const int c = blockIdx.x % n_chunks;
+  const int r = blockIdx.x / n_chunks;
+  const T* row;
+  if (!locate_row<T>(s0, s1, B, L, lens, r, &row)) return;
+  const int x0 = c * chunk;
+  const int x1 = min(V, x0 + chunk);
+  float m = neg_inf(), s = 0.f;
+  if (VEC) {
+    const int nvec = (x1 - x0) >> 3;
+    int v = threadIdx.x;
+    for (; v + 3 * kThreads < nvec; v += 4 * kThreads) {
+      float e[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) load8(row + x0 + (v + u * kThreads) * 8, e[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) lse_update(e[u], a, m, s);
+    }
+    for (; v < nvec; v += kThreads) {
+      float e[8];
+      load8(row + x0 + v * 8, e);
+      lse_update(e, a, m, s);
+    }
+    for (int x = x0 + nvec * 8 + threadIdx.x; x < x1; x += kThreads) lse_update1(load1(row + x), a, m, s);
+  } else {
+    for (int x = x0 + threadIdx.x; x < x1; x += kThreads) lse_update1(load1(row + x), a, m, s);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float om = __shfl_xor(m, o, 64);
+    float os = __shfl_xor(s, o, 64);
+    lse2_merge(m, s, om, os);
+  }
+  __shared__ float sm[kThreads / 64], ss[kThreads / 64];
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { sm[w] = m; ss[w] = s; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float mm = sm[0], s2 = ss[0];
+    for (int k = 1; k < kThreads / 64; ++k) lse2_merge(mm, s2, sm[k], ss[k]);
+    part[blockIdx.x] = make_float2(mm, s2);
+  }
+}
+
+__device__ void reduce_lse_row(const float2* part, int row, int nc, float& m, float& s) {
+  m = neg_inf();
+  s = 0.f;
+  for (int c = 0; c < nc; ++c) {
+    float2 p = part[row * nc + c];
+    lse2_merge(m, s, p.x, p.y);
+  }
+}
+
+// --------------------------------------------------------- sampled verify
+template <typename T>
+__global__ __launch_bounds__(128) void k_sample_accept(
+    int B, int L, int V, int nc, const float2* __restrict__ part, const T* __restrict__ tl,
+    int64_t ts, const T* __restrict__ dl, int64_t ds, const int32_t* __restrict__ toks,
+    const int32_t* __restrict__ lens, const float* __restrict__ u, float a,
+    float* __restrict__ ratio_out, ReqInfo* __restrict__ info) {
+  const int b = blockIdx.x;
+  const int t = threadIdx.x;
+  __shared__ float Mt[65], St[65], Md[64], Sd[64], rat[64];
+  __shared__ int okx[64];
+  bool bad;
+  const int nb = chain_of(lens, b, L, &bad);
+  if (t <= nb) reduce_lse_row(part, b * (L + 1) + t, nc, Mt[t], St[t]);
+  if (t < nb) {
+    reduce_lse_row(part, B * (L + 1) + b * L + t, nc, Md[t], Sd[t]);
+    const int x = toks[b * L + t];
+    float r = __builtin_nanf("");
+    okx[t] = (x >= 0 && x < V);
+    if (okx[t]) {
+      const float tx = load1(tl + (int64_t)(b * (L + 1) + t) * ts + x);
+      const float dx = load1(dl + (int64_t)(b * L + t) * ds + x);
+      const float e = fmaf(tx, a, -Mt[t]) - fmaf(dx, a, -Md[t]);
+      r = exp2f(e) * (Sd[t] / St[t]);
+    }
+    rat[t] = r;
+    if (ratio_out) ratio_out[b * L + t] = r;
+  } else if (t < L && ratio_out) {
+    ratio_out[b * L + t] = __builtin_nanf("");
+  }
+  __syncthreads();
+  if (t == 0) {
+    ReqInfo I;
+    bool err = bad;
+    for (int i = 0; i < nb; ++i) err |= !okx[i];
+    I.err = err;
+    I.acc = -1; I.row = 0; I.mode = 1;
+    I.Mt = I.St = I.Md = I.Sd = 0.f;
+    if (!err) {
+      int j = nb;
+      for (int i = 0; i < nb; ++i)
+        if (!(u[b * L + i] < rat[i])) { j = i; break; }
+      I.acc = j;
+      I.row = j;
+      I.mode = (j < nb) ? 0 : 1;
+      I.Mt = Mt[j];
+      I.St = St[j];
+      if (j < nb) { I.Md = Md[j]; I.Sd = Sd[j]; }
+    }
+    info[b] = I;
+  }
+}
+
+// Weight of token x in the bonus draw: residual max(0, p - q) (kind 0) or the
+// unnormalised target exponential 2^(z - Mt) (kind 1).
+template <typename T>
+struct BonusRow {
+  const T* tr;
+  const T* dr;
+  float a, Mt, invSt, Md, invSd;
+  __device__ __forceinline__ float et(float tv) const { return fexp2(fmaf(tv, a, -Mt)); }
+  __device__ __forceinline__ float res(float tv, float dv) const {
+    float p = et(tv) * invSt;
+    float q = fexp2(fmaf(dv, a, -Md)) * invSd;
+    return fmaxf(0.f, p - q);
+  }
+};
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_bonus_partial(
+    int B, int L, int V, int chunk, int nc, const T* __restrict__ tl, int64_t ts,
+    const T* __restrict__ dl, int64_t ds, float a, const ReqInfo* __restrict__ info,
+    float4* __restrict__ rpart) {
+  const int c = blockIdx.x % nc;
+  const int b = blockIdx.x / nc;
+  const ReqInfo I = info[b];
+  if (I.err) return;
+  BonusRow<T> R{tl + (int64_t)(b * (L + 1) + I.row) * ts,
+                I.mode == 0 ? dl + (int64_t)(b * L + I.row) * ds : nullptr,
+                a, I.Mt, 1.f / I.St, I.Md, I.mode == 0 ? 1.f / I.Sd : 0.f};
+  const int x0 = c * chunk;
+  const int x1 = min(V, x0 + chunk);
+  float ar = 0.f, amin = 0.f, ap = 0.f;
+  auto one = [&](float tv, float dv) {
+    float e = R.et(tv);
+    ap += e;
+    if (I.mode == 0) {
+      float p = e * R.invSt;
+      float q = fexp2(fmaf(dv, R.a, -R.Md)) * R.invSd;
+      ar += fmaxf(0.f, p - q);
+      amin += fminf(p, q);
+    }
+  };
+  if (VEC) {
+    const int nvec = (x1 - x0) >> 3;
+    for (int v = threadIdx.x; v < nvec; v += kThreads) {
+      float tv[8], dv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      load8(R.tr + x0 + v * 8, tv);
+      if (I.mode == 0) load8(R.dr + x0 + v * 8, dv);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) one(tv[j], dv[j]);
+    }
+    for (int x = x0 + nvec * 8 + threadIdx.x; x < x1; x += kThreads)
+      one(load1(R.tr + x), I.mode == 0 ? load1(R.dr + x) : 0.f);
+  } else {
+    for (int x = x0 + threadIdx.x; x < x1; x += kThreads)
+      one(load1(R.tr + x), I.mode == 0 ? load1(R.dr + x) : 0.f);
+  }
+  ar = wave_sum(ar);
+  amin = wave_sum(amin);
+  ap = wave_sum(ap);
+  __shared__ float s[3][kThreads / 64];
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { s[0][w] = ar; s[1][w] = amin; s[2][w] = ap; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < kThreads / 64; ++k) { o.x += s[0][k]; o.y += s[1][k]; o.z += s[2][k]; }
+    rpart[blockIdx.x] = o;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_bonus_select(
+    int B, int L, int V, int chunk, int nc, const T* __restrict__ tl, int64_t ts,
+    const T* __restrict__ dl, int64_t ds, float a, const ReqInfo* __restrict__ info,
+    const float4* __restrict__ rpart, const float* __restrict__ u2,
+    int32_t* __restrict__ accept_len, int32_t* __restrict__ bonus, int32_t* __restrict__ commit,
+    const int32_t* __restrict__ prefix, int32_t* __restrict__ new_seq,
+    float* __restrict__ beta_out, float* __restrict__ gap_out) {
+  const int b = blockIdx.x;
+  const int t = threadIdx.x;
+  const ReqInfo I = info[b];
+  if (I.err) {
+    if (t == 0) {
+      accept_len[b] = -1; bonus[b] = -1; commit[b] = 0;
+      if (new_seq) new_seq[b] = prefix[b];
+      if (beta_out) beta_out[b] = __builtin_nanf("");
+      if (gap_out) gap_out[b] = __builtin_nanf("");
+    }
+    return;
+  }
+  __shared__ int sh_kind, sh_cc, sh_x;
+  __shared__ float sh_base, sh_thr, sh_Z;
+  __shared__ float sh_loc[kThreads];
+  __shared__ float sh_gap;
+  __shared__ int sh_last;
+  if (t == 0) {
+    float Rs = 0.f, Ps = 0.f, Ms = 0.f;
+    for (int c = 0; c < nc; ++c) { float4 p = rpart[b * nc + c]; Rs += p.x; Ms += p.y; Ps += p.z; }
+    const int kind = (I.mode == 0 && Rs > 0.f) ? 0 : 1;
+    const float Z = kind == 0 ? Rs : Ps;
+    const float thr = u2[b] * Z;
+    float pre = 0.f;
+    int cc = -1;
+    float base = 0.f;
+    for (int c = 0; c < nc; ++c) {
+      float4 p = rpart[b * nc + c];
+      float w = kind == 0 ? p.x : p.z;
+      if (pre + w > thr) { cc = c; base = pre; break; }
+      pre += w;
+    }
+    if (cc < 0) {  // rounding left u'*Z at the very end: the last chunk with mass
+      pre = 0.f;
+      for (int c = 0; c < nc; ++c) {
+        float4 p = rpart[b * nc + c];
+        float w = kind == 0 ? p.x : p.z;
+        if (w > 0.f) { cc = c; base = pre; }
+        pre += w;
+      }
+    }
+    if (cc < 0) cc = 0;  // no chunk has mass (only with invalid logits)
+    sh_kind = kind; sh_cc = cc; sh_base = base; sh_thr = thr; sh_Z = Z;
+    sh_x = INT_MAX; sh_last = -1; sh_gap = 0.f;
+    if (beta_out) beta_out[b] = (I.mode == 0) ? Ms : __builtin_nanf("");
+  }
+  __syncthreads();
+  BonusRow<T> R{tl + (int64_t)(b * (L + 1) + I.row) * ts,
+                I.mode == 0 ? dl + (int64_t)(b * L + I.row) * ds : nullptr,
+                a, I.Mt, 1.f / I.St, I.Md, I.mode == 0 ? 1.f / I.Sd : 0.f};
+  const int kind = sh_kind;
+  auto wt = [&](int x) -> float {
+    float tv = load1(R.tr + x);
+    return kind == 0 ? R.res(tv, load1(R.dr + x)) : R.et(tv);
+  };
+  const int x0 = sh_cc * chunk;
+  const int x1 = min(V, x0 + chunk);
+  const int seg = (x1 - x0 + kThreads - 1) / kThreads;
+  const int xs = min(x1, x0 + t * seg);
+  const int xe = min(x1, xs + seg);
+  float loc = 0.f;
+  int lastpos = -1;
+  for (int x = xs; x < xe; ++x) {
+    float w = wt(x);
+    loc += w;
+    if (w > 0.f) lastpos = x;
+  }
+  sh_loc[t] = loc;
+  if (lastpos >= 0) atomicMax(&sh_last, lastpos);
+  __syncthreads();
+  if (t == 0) {  // exclusive prefix over the segment sums, in segment order
+    float acc = 0.f;
+    for (int k = 0; k < kThreads; ++k) { float v = sh_loc[k]; sh_loc[k] = acc; acc += v; }
+  }
+  __syncthreads();
+  const float thr = sh_thr;
+  const float base = sh_base + sh_loc[t];
+  if (base <= thr && base + loc > thr) {
+    float acc = base;
+    int found = -1;
+    float lo = 0.f, hi = 0.f;
+    for (int x = xs; x < xe; ++x) {
+      float w = wt(x);
+      if (acc + w > thr) { found = x; lo = acc; hi = acc + w; break; }
+      acc += w;
+    }
+    if (found < 0 && lastpos >= 0) { found = lastpos; lo = hi = thr; }
+    if (found >= 0) {
+      int prev = atomicMin(&sh_x, found);
+      if (found < prev) sh_gap = fminf(thr - lo, hi - thr) / sh_Z;
+    }
+  }
+  __syncthreads();
+  if (t == 0) {
+    int x = sh_x;
+    float gap = sh_gap;
+    if (x == INT_MAX) { x = sh_last >= 0 ? sh_last : x0; gap = 0.f; }
+    accept_len[b] = I.acc;
+    bonus[b] = x;
+    commit[b] = I.acc + 1;
+    if (new_seq) new_seq[b] = prefix[b] + I.acc + 1;
+    if (gap_out) gap_out[b] = gap;
+  }
+}
+
+// ------------------------------------------------------------------- gate
+__global__ __launch_bounds__(64) void k_gate_finalize(
+    int B, int n, int V, int nc, const float2* __restrict__ part, const void* __restrict__ dl,
+    int64_t rs, int bf16, const int32_t* __restrict__ toks, const int32_t* __restrict__ valid,
+    int rows_all, float a, float g, float* __restrict__ c_out, int32_t* __restrict__ go_out,
+    float* __restrict__ row_max, float* __restrict__ row_lse) {
+  const int b = blockIdx.x;
+  const int t = threadIdx.x;
+  __shared__ float term[64];
+  bool bad;
+  const int nv = chain_of(valid, b, n, &bad);
+  const int nread = rows_all ? n : nv;
+  float tm = 0.f;
+  if (t < n) {
+    if (t < nread) {
+      float M, S;
+      reduce_lse_row(part, b * n + t, nc, M, S);
+      const float l2 = M + log2f(S);
+      if (row_max) row_max[b * n + t] = M * kLn2;
+      if (row_lse) row_lse[b * n + t] = l2 * kLn2;
+      if (t < nv) {
+        const int x = toks[b * n + t];
+        if (x < 0 || x >= V) {
+          tm = __builtin_nanf("");
+        } else {
+          const int64_t off = (int64_t)(b * n + t) * rs + x;
+          const float dx = bf16 ? bf16_to_f32(static_cast<const uint16_t*>(dl)[off])
+                                : static_cast<const float*>(dl)[off];
+          tm = (dx * a - l2) * kLn2;
+        }
+      }
+    }
+    term[t] = tm;
+  }
+  __syncthreads();
+  if (t == 0) {
+    float c = 0.f;
+    for (int i = 0; i < nv; ++i) c += term[i];
+    if (bad) c = __builtin_nanf("");
+    c_out[b] = c;
+    go_out[b] = (c >= g) ? 1 : 0;
+  }
+}
+
+bool aligned16(const void* p, int64_t stride, int esize) {
+  return (reinterpret_cast<uintptr_t>(p) % 16 == 0) && ((stride * esize) % 16 == 0);
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+template <typename T, bool VEC>
+void launch_argmax(RowSet s0, RowSet s1, int B, int L, int V, const int32_t* lens, VocabPlan pl,
+                   int64_t rows, float* pmax, int* pidx, hipStream_t st) {
+  hipLaunchKernelGGL((k_row_argmax<T, VEC>), dim3((unsigned)(rows * pl.n_chunks)), dim3(kThreads),
+                     0, st, s0, s1, B, L, V, lens, pl.chunk, pl.n_chunks, pmax, pidx);
+}
+template <typename T, bool VEC>
+void launch_lse(RowSet s0, RowSet s1, int B, int L, int V, const int32_t* lens, float a,
+                VocabPlan pl, int64_t rows, float2* part, hipStream_t st) {
+  hipLaunchKernelGGL((k_row_lse<T, VEC>), dim3((unsigned)(rows * pl.n_chunks)), dim3(kThreads),
+                     0, st, s0, s1, B, L, V, lens, a, pl.chunk, pl.n_chunks, part);
+}
+
+template <typename T, bool VEC>
+void sample_impl(int B, int L, int V, const void* tl, int64_t ts, const void* dl, int64_t ds,
+                 const int32_t* toks, const int32_t* lens, const float* u, const float* u2,
+                 float temperature, int32_t* acc, int32_t* bonus, int32_t* commit,
+                 const int32_t* prefix, int32_t* new_seq, float* ratio_out, float* beta_out,
+                 float* gap_out, void* ws, hipStream_t st) {
+  const int64_t rows = (int64_t)B * (2 * L + 1);
+  const VocabPlan pl = plan_vocab(rows, V);
+  const VocabPlan pr = plan_vocab(2 * (int64_t)B, V);
+  char* w = static_cast<char*>(ws);
+  float2* part = reinterpret_cast<float2*>(w);
+  w += align256(sizeof(float2) * rows * pl.n_chunks);
+  ReqInfo* info = reinterpret_cast<ReqInfo*>(w);
+  w += align256(sizeof(ReqInfo) * B);
+  float4* rpart = reinterpret_cast<float4*>(w);
+  const float a = kLog2e / temperature;
+  RowSet s0{tl, ts, L + 1, 1}, s1{dl, ds, L, 0};
+  launch_lse<T, VEC>(s0, s1, B, L, V, lens, a, pl, rows, part, st);
+  hipLaunchKernelGGL((k_sample_accept<T>), dim3(B), dim3(128), 0, st, B, L, V, pl.n_chunks, part,
+                     static_cast<const T*>(tl), ts, static_cast<const T*>(dl), ds, toks, lens, u,
+                     a, ratio_out, info);
+  hipLaunchKernelGGL((k_bonus_partial<T, VEC>), dim3(B * pr.n_chunks), dim3(kThreads), 0, st, B,
+                     L, V, pr.chunk, pr.n_chunks, static_cast<const T*>(tl), ts,
+                     static_cast<const T*>(dl), ds, a, info, rpart);
+  hipLaunchKernelGGL((k_bonus_select<T>), dim3(B), dim3(kThreads), 0, st, B, L, V, pr.chunk,
+                     pr.n_chunks, static_cast<const T*>(tl), ts, static_cast<const T*>(dl), ds,
+                     a, info, rpart, u2, acc, bonus, commit, prefix, new_seq, beta_out, gap_out);
+}
+
+}  // namespace
+
+VocabPlan plan_vocab(int64_t n_rows, int V) {
+  // About 4096 workgroups per launch, chunks of at least 2048 elements, at
+  // most kMaxChunks chunks per row; chunk boundaries are multiples of 8 so
+  // that 16-byte loads stay aligned.
+  const int64_t rows = n_rows > 0 ? n_rows : 1;
+  const int64_t want = std::max<int64_t>(1, cdiv(4096, rows));
+  int64_t chunk = std::max<int64_t>(cdiv(V, want), 2048);
+  chunk = cdiv(chunk, 8) * 8;
+  int64_t n = cdiv(V, chunk);
+  if (n > kMaxChunks) {
+    chunk = cdiv(cdiv(V, kMaxChunks), 8) * 8;
+    n = cdiv(V, chunk);
+  }
+  return VocabPlan{(int)chunk, (int)std::max<int64_t>(n, 1)};
+}
+
+size_t greedy_ws_bytes(int B, int L, int V) {
+  const int64_t rows = (int64_t)B * (2 * L + 1);
+  const VocabPlan pl = plan_vocab(rows, V);
+  return align256(sizeof(float) * rows * pl.n_chunks) + align256(sizeof(int) * rows * pl.n_chunks);
+}
+
+size_t sample_ws_bytes(int B, int L, int V) {
+  const int64_t rows = (int64_t)B * (2 * L + 1);
+  const VocabPlan pl = plan_vocab(rows, V);
+  const VocabPlan pr = plan_vocab(2 * (int64_t)B, V);
+  return align256(sizeof(float2) * rows * pl.n_chunks) + align256(sizeof(ReqInfo) * B) +
+         align256(sizeof(float4) * B * pr.n_chunks);
+}
+
+size_t gate_ws_bytes(int B, int n, int V) {
+  const int64_t rows = (int64_t)B * n;
+  const VocabPlan pl = plan_vocab(rows, V);
+  return align256(sizeof(float2) * rows * pl.n_chunks);
+}
+
+hipError_t launch_verify_greedy(bool bf16, int B, int L, int V, const void* tl, int64_t ts,
+                                const void* dl, int64_t ds, int32_t* draft_tokens,
+                                const int32_t* lens, int32_t* target_predict, int32_t* accept_len,
+                                int32_t* bonus, int32_t* commit, const int32_t* prefix,
+                                int32_t* new_seq, void* ws, hipStream_t st) {
+  const int64_t rows = (int64_t)B * ((L + 1) + (dl ? L : 0));
+  const VocabPlan pl = plan_vocab((int64_t)B * (2 * L + 1), V);
+  float* pmax = static_cast<float*>(ws);
+  int* pidx = reinterpret_cast<int*>(static_cast<char*>(ws) +
+                                     align256(sizeof(float) * (int64_t)B * (2 * L + 1) * pl.n_chunks));
+  const int es = bf16 ? 2 : 4;
+  const bool vec = aligned16(tl, ts, es) && (!dl || aligned16(dl, ds, es));
+  RowSet s0{tl, ts, L + 1, 1}, s1{dl, ds, dl ? L : 0, 0};
+  if (bf16) {
+    if (vec) launch_argmax<uint16_t, true>(s0, s1, B, L, V, lens, pl, rows, pmax, pidx, st);
+    else launch_argmax<uint16_t, false>(s0, s1, B, L, V, lens, pl, rows, pmax, pidx, st);
+  } else {
+    if (vec) launch_argmax<float, true>(s0, s1, B, L, V, lens, pl, rows, pmax, pidx, st);
+    else launch_argmax<float, false>(s0, s1, B, L, V, lens, pl, rows, pmax, pidx, st);
+  }
+  hipLaunchKernelGGL(k_greedy_finalize, dim3(B), dim3(128), 0, st, B, L, V, pl.n_chunks, pmax,
+                     pidx, dl ? 1 : 0, draft_tokens, lens, target_predict, accept_len, bonus,
+                     commit, prefix, new_seq);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify_sample(bool bf16, int B, int L, int V, const void* tl, int64_t ts,
+                                const void* dl, int64_t ds, const int32_t* toks,
+                                const int32_t* lens, const float* u, const float* u2,
+                                float temperature, int32_t* acc, int32_t* bonus, int32_t* commit,
+                                const int32_t* prefix, int32_t* new_seq, float* ratio_out,
+                                float* beta_out, float* gap_out, void* ws, hipStream_t st) {
+  const int es = bf16 ? 2 : 4;
+  const bool vec = aligned16(tl, ts, es) && aligned16(dl, ds, es);
+  if (bf16) {
+    if (vec) sample_impl<uint16_t, true>(B, L, V, tl, ts, dl, ds, toks, lens, u, u2, temperature, acc, bonus, commit, prefix, new_seq, ratio_out, beta_out, gap_out, ws, st);
+    else sample_impl<uint16_t, false>(B, L, V, tl, ts, dl, ds, toks, lens, u, u2, temperature, acc, bonus, commit, prefix, new_seq, ratio_out, beta_out, gap_out, ws, st);
+  } else {
+    if (vec) sample_impl<float, true>(B, L, V, tl, ts, dl, ds, toks, lens, u, u2, temperature, acc, bonus, commit, prefix, new_seq, ratio_out, beta_out, gap_out, ws, st);
+    else sample_impl<float, false>(B, L, V, tl, ts, dl, ds, toks, lens, u, u2, temperature, acc, bonus, commit, prefix, new_seq, ratio_out, beta_out, gap_out, ws, st);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gate(bool bf16, int B, int n, int V, const void* dl, int64_t rs,
+                       const int32_t* toks, const int32_t* valid, float temperature, float g,
+                       float* c_out, int32_t* go_out, float* row_max, float* row_lse, void* ws,
+                       hipStream_t st) {
+  const int64_t rows = (int64_t)B * n;
+  const VocabPlan pl = plan_vocab(rows, V);
+  float2* part = static_cast<float2*>(ws);
+  const float a = kLog2e / temperature;
+  const bool rows_all = (row_max != nullptr) || (row_lse != nullptr);
+  const int32_t* lens = rows_all ? nullptr : valid;
+  RowSet s0{dl, rs, n, 0}, s1{dl, rs, 0, 0};
+  const int es = bf16 ? 2 : 4;
+  const bool vec = aligned16(dl, rs, es);
+  if (bf16) {
+    if (vec) launch_lse<uint16_t, true>(s0, s1, B, n, V, lens, a, pl, rows, part, st);
+    else launch_lse<uint16_t, false>(s0, s1, B, n, V, lens, a, pl, rows, part, st);
+  } else {
+    if (vec) launch_lse<float, true>(s0, s1, B, n, V, lens, a, pl, rows, part, st);
+    else launch_lse<float, false>(s0, s1, B, n, V, lens, a, pl, rows, part, st);
+  }
+  hipLaunchKernelGGL(k_gate_finalize, dim3(B), dim3(64), 0, st, B, n, V, pl.n_chunks, part, dl, rs,
+                     bf16 ? 1 : 0, toks, valid, rows_all ? 1 : 0, a, g, c_out, go_out, row_max,
+                     row_lse);
+  return hipGetLastError();
+}
+
+}  // namespace dflash

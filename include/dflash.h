@@ -1,0 +1,280 @@
+/*
+ * dflash.h -- C ABI of the DFlash draft-and-verify step on AMD MI355X (gfx950).
+ *
+ * Five operations, each the hot path of one part of the step:
+ *   dflash_materialize_ctx_kv  target-context KV injection
+ *   dflash_block_attention     non-causal block attention over [ctx; block]
+ *   dflash_verify_greedy       greedy acceptance over the full vocabulary
+ *   dflash_verify_sample       lossless rejection sampling over the full vocabulary
+ *   dflash_gate                DLoop block-confidence gate
+ *
+ * Pages these follow (cited by short title):
+ *   [DFlash overview]  "DFlash 块扩散解码：以并行扩散替代自回归草稿，实现无损 6 倍推理加速"
+ *                      pinghaoyang.com.cn/aigc/posts/dflash/
+ *   [SGLang DFlash]    "详解SGlang 最新DFlash投机解码算法的工程实现、overlap策略和改进点"
+ *                      www.10100.com/article/149138197
+ *   [Spec tutorial]    "让大模型快 8 倍：从投机解码到 DDTree 的完整原理"
+ *                      liyongzhi.xyz/posts/2026/04/speculative-decoding/
+ *   [DLoop]            "DLoop 完全拆解：让一次验证覆盖多个草稿阶段的循环投机解码"
+ *                      pinghaoyang.com.cn/aigc/posts/dloop-looped-speculative-decoding/
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Ownership   Every tensor pointer is a device pointer owned by the caller,
+ *             except where a parameter is documented as a host array.  The
+ *             library never allocates, frees or keeps a pointer after the
+ *             call returns.  Scratch memory comes from the caller's workspace
+ *             `ws` of at least the size reported by the matching
+ *             dflash_*_workspace_size() query (ws may be NULL when that size
+ *             is 0).  The workspace must be 256-byte aligned and must not be
+ *             shared by calls that may run concurrently.
+ * Async       Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *             stream) and the call returns without waiting.  No entry point
+ *             synchronises or copies to the host.
+ * Layout      Row-major and contiguous unless a stride is given.  Strides
+ *             are in elements.
+ * Dtypes      DFLASH_BF16: bf16 storage for hiddens, weights, logits, Q/K/V
+ *             and caches; all accumulation, softmax, ratio and CDF arithmetic
+ *             is fp32.  DFLASH_F32: fp32 storage and arithmetic throughout.
+ * Paged cache One tensor each for K and V, shape [num_pages, page_size,
+ *             n_kv_heads, head_dim]; page_size must be 16.  A block table
+ *             [n_seq, max_pages_per_seq] of int32 maps a request's logical
+ *             page (position / 16) to a physical page; -1 = unmapped.
+ * Errors      A call returns DFLASH_OK or an error code.  Every argument error
+ *             that the host can see is reported before anything is enqueued,
+ *             and then nothing is enqueued.  DFLASH_E_HIP reports a failed
+ *             launch.  Errors in device-resident data (a token id outside
+ *             [0, V), a chain length outside [0, L], a page-table entry
+ *             outside [0, num_pages)) are reported in band, as described at
+ *             each entry point.  No exception crosses the ABI; the library
+ *             never prints.
+ * Threads     The library holds no mutable global state; calls from several
+ *             host threads are safe.
+ */
+#ifndef DFLASH_H_
+#define DFLASH_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DFLASH_OK = 0,
+  DFLASH_E_ARG = 1,          /* a NULL pointer, a negative or inconsistent size */
+  DFLASH_E_UNSUPPORTED = 2,  /* a valid request outside what is implemented (e.g. head_dim) */
+  DFLASH_E_WORKSPACE = 3,    /* ws too small or misaligned */
+  DFLASH_E_HIP = 4           /* a HIP launch failed */
+} dflash_status;
+
+typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
+
+/* One draft layer's paged KV cache (device pointers). */
+typedef struct {
+  void* k;           /* [num_pages, page_size, n_kv_heads, head_dim] */
+  void* v;           /* same shape as k */
+  int32_t num_pages;
+  int32_t page_size; /* must be 16 */
+} dflash_kv_layer;
+
+typedef void* dflash_stream_t; /* a hipStream_t */
+
+/* Human-readable name of a status code (static storage). */
+const char* dflash_status_string(dflash_status s);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int dflash_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Target-context KV injection.
+ *
+ * [DFlash overview], section "KV 注入", steps 2-3: the m captured target
+ * hidden states are concatenated along features and fused,
+ *     h_ctx = [h_1; ...; h_m] W_f^T + b_f            (W_f: [d, m*d], b_f: [d])
+ * and every draft layer l projects h_ctx into its own cache,
+ *     K^(l) = h_ctx W_K^(l)^T,  V^(l) = h_ctx W_V^(l)^T  (W: [Hkv*D, d]).
+ * [SGLang DFlash], section 4.1: only the committed rows of each request are
+ * written, at the physical slots of their logical positions.
+ *
+ * T            rows to materialise (T = n_seq * rows_per_seq; T = 0 is a no-op)
+ * m, d_model   number of captured hiddens and their width
+ * hiddens      HOST array of m device pointers, each [T, d_model]; they are
+ *              read as one virtual [T, m*d_model] matrix, hidden 0 first
+ * W_f, b_f     [d_model, m*d_model] and [d_model] (b_f may be NULL: no bias)
+ * n_layers, n_kv_heads, head_dim   draft layers and their KV geometry
+ * W_K, W_V     HOST arrays of n_layers device pointers, each [Hkv*D, d_model]
+ * caches       HOST array of n_layers dflash_kv_layer
+ * block_table  [n_seq, max_pages_per_seq] int32
+ * rows_per_seq row r belongs to request s = r / rows_per_seq and sits at
+ *              logical position seq_start_pos[s] + r % rows_per_seq
+ * commit_lens  [n_seq] int32 or NULL; when given, only rows with
+ *              r % rows_per_seq < commit_lens[s] are written (the prefix-valid
+ *              write of the SGLang page)
+ * h_ctx_out    [T, d_model] in the storage dtype, or NULL
+ * Rows whose page-table entry is outside [0, num_pages) are not written.
+ * h_ctx is rounded to the storage dtype before the K/V projections; cache
+ * entries are rounded to the storage dtype (bf16: round to nearest even).
+ * Shape limits: bf16 needs d_model % 128 == 0, (n_kv_heads*head_dim) % 128
+ * == 0 and 16-byte aligned tensors; m <= 8; n_layers <= 64; head_dim in
+ * {64, 128}.
+ * ------------------------------------------------------------------------- */
+size_t dflash_materialize_workspace_size(int64_t T, int m, int d_model, int n_layers,
+                                         int n_kv_heads, int head_dim, dflash_dtype dtype);
+
+dflash_status dflash_materialize_ctx_kv(
+    int64_t T, int m, int d_model, const void* const* hiddens,
+    const void* W_f, const void* b_f,
+    int n_layers, int n_kv_heads, int head_dim,
+    const void* const* W_K, const void* const* W_V,
+    const dflash_kv_layer* caches,
+    const int32_t* block_table, int max_pages_per_seq,
+    int rows_per_seq, const int32_t* seq_start_pos, const int32_t* commit_lens,
+    void* h_ctx_out,
+    dflash_dtype dtype, void* ws, size_t ws_bytes, dflash_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Non-causal block attention.
+ *
+ * [DFlash overview], section "KV 注入" (the Attention formula) and section
+ * "块扩散": each of the k positions of a request's block attends, with no
+ * causal mask, to [K_ctx; K_blk] and [V_ctx; V_blk]; section "随机锚点采样":
+ * in packed training each block sees the injected context of positions before
+ * its anchor and only its own block (map each block to one request whose
+ * block-table row lists the sequence's pages and whose ctx_len is its anchor).
+ *
+ * For request b, q-head h (kv-head h / (Hq/Hkv)), block position i:
+ *   keys   = cache K at logical positions [0, ctx_lens[b]) ++ k_blk[b, 0:k]
+ *   out    = softmax(scale * q . keys) @ values,  lse = natural log-sum-exp
+ *
+ * q            [B, k, Hq, D]      k_blk, v_blk  [B, k, Hkv, D]
+ * cache_k/v    [num_pages, 16, Hkv, D]
+ * block_table  [B, max_pages_per_seq] int32;  ctx_lens [B] int32 (0 allowed)
+ * scale        softmax scale; 0 means 1/sqrt(D)
+ * out          [B, k, Hq, D] in out_dtype (DFLASH_BF16 needs bf16 inputs;
+ *              DFLASH_F32 keeps the fp32 result unrounded);
+ * lse_out      [B, Hq, k] fp32 or NULL
+ * In band: if ctx_lens[b] is negative or exceeds max_pages_per_seq*16, or a
+ * page entry it needs is outside [0, num_pages), request b's outputs are NaN.
+ * Shape limits: head_dim in {64, 128}; Hq % Hkv == 0; 1 <= k <= 64;
+ * (Hq/Hkv)*k <= 256; bf16 tensors 16-byte aligned.  The fp32 path needs no
+ * workspace.
+ * ------------------------------------------------------------------------- */
+size_t dflash_attention_workspace_size(int B, int k, int n_q_heads, int n_kv_heads,
+                                       int head_dim, int max_pages_per_seq, dflash_dtype dtype);
+
+dflash_status dflash_block_attention(
+    int B, int k, int n_q_heads, int n_kv_heads, int head_dim,
+    const void* q, const void* k_blk, const void* v_blk,
+    const void* cache_k, const void* cache_v, int num_pages, int page_size,
+    const int32_t* block_table, int max_pages_per_seq, const int32_t* ctx_lens,
+    float scale, void* out, float* lse_out,
+    dflash_dtype dtype, dflash_dtype out_dtype, void* ws, size_t ws_bytes,
+    dflash_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Greedy verification.
+ *
+ * [SGLang DFlash], section 3: the target's prediction at row i is the argmax
+ * of its logits; draft i is accepted while it equals the target prediction at
+ * row i (leading run of matches); bonus = target prediction at row
+ * accept_len; commit = accept_len + 1; new_seq_len = prefix_len + commit.
+ * Argmax ties go to the lowest token id.
+ *
+ * target_logits  rows b*(L+1)+i, i = 0..L, each of V elements, t_row_stride
+ *                elements apart
+ * draft_logits   rows b*L+i (d_row_stride apart) or NULL.  When given, the
+ *                drafts are their argmax and are written to draft_tokens
+ *                (rows i < chain length); when NULL, draft_tokens is input.
+ * draft_tokens   [B, L] int32
+ * chain_lens     [B] int32 in [0, L], or NULL (= L): rows past the chain are
+ *                not read
+ * target_predict [B, L+1] int32 or NULL; -1 past the chain
+ * accept_len, bonus, commit_lens  [B] int32 outputs
+ * prefix_lens, new_seq_lens       [B] int32, both NULL or both given
+ * In band: a chain length outside [0, L] or a draft token outside [0, V)
+ * within the chain gives accept_len = bonus = -1, commit = 0,
+ * new_seq_len = prefix_len.
+ * Limits: 0 <= L <= 64; V >= 1.
+ * ------------------------------------------------------------------------- */
+size_t dflash_verify_workspace_size(int B, int L, int V);
+
+dflash_status dflash_verify_greedy(
+    int B, int L, int V,
+    const void* target_logits, int64_t t_row_stride,
+    const void* draft_logits, int64_t d_row_stride,
+    int32_t* draft_tokens, const int32_t* chain_lens,
+    int32_t* target_predict, int32_t* accept_len, int32_t* bonus, int32_t* commit_lens,
+    const int32_t* prefix_lens, int32_t* new_seq_lens,
+    dflash_dtype dtype, void* ws, size_t ws_bytes, dflash_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Lossless rejection-sampling verification.
+ *
+ * [Spec tutorial], section 3: with p = softmax(target/T) and q =
+ * softmax(draft/T) at a row, draft x is kept with probability min(1, p(x)/q(x));
+ * at the first rejection the bonus is drawn from max(0, p - q) / (1 - beta),
+ * beta = sum min(p, q); section 4: later drafts are discarded.  [DFlash
+ * overview], pseudocode: if all drafts are kept the bonus is drawn from p of
+ * the row after the last draft.  [DLoop], "验证与无损性": several stages are
+ * verified as one chain of chain_lens[b] drafts.
+ *
+ * Randomness is supplied: row i is accepted iff u_accept[b,i] < p(x)/q(x);
+ * the bonus is the smallest token x whose cumulative weight (ascending token
+ * id) exceeds u_bonus[b] times the total weight, where the weight is the
+ * residual max(0, p-q) (or p when that residual sums to 0) at a rejection and
+ * p of row chain_len when all drafts are kept.
+ *
+ * target_logits [B, L+1, V] rows (t_row_stride apart); draft_logits [B, L, V]
+ * rows (d_row_stride apart); draft_tokens [B, L]; chain_lens [B] or NULL;
+ * u_accept [B, L] and u_bonus [B] in [0, 1); temperature > 0.
+ * Outputs accept_len, bonus, commit_lens [B]; new_seq_lens as for greedy.
+ * Audit outputs (each may be NULL):
+ *   ratio_out [B, L]  p/q of every draft within the chain (NaN past it)
+ *   beta_out  [B]     sum min(p, q) of the rejected row (NaN if none)
+ *   u_cdf_gap_out [B] distance of u'*Z to the nearer CDF boundary of the
+ *                     chosen token, divided by the total weight Z
+ * In band: as for greedy.
+ * Limits: 0 <= L <= 64; V >= 1.
+ * ------------------------------------------------------------------------- */
+dflash_status dflash_verify_sample(
+    int B, int L, int V,
+    const void* target_logits, int64_t t_row_stride,
+    const void* draft_logits, int64_t d_row_stride,
+    const int32_t* draft_tokens, const int32_t* chain_lens,
+    const float* u_accept, const float* u_bonus, float temperature,
+    int32_t* accept_len, int32_t* bonus, int32_t* commit_lens,
+    const int32_t* prefix_lens, int32_t* new_seq_lens,
+    float* ratio_out, float* beta_out, float* u_cdf_gap_out,
+    dflash_dtype dtype, void* ws, size_t ws_bytes, dflash_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * DLoop confidence gate.
+ *
+ * [DLoop], "机制一：置信度门控": c = sum over the stage's drafted tokens of
+ * the drafter's log-probability of that token; drafting continues iff c >= g.
+ *   c[b]  = sum_{i < n_b} ( x_i-th logit / T - logsumexp(row / T) )
+ *   go[b] = c[b] >= g
+ * draft_logits [B, n, V] rows (row_stride apart); draft_tokens [B, n];
+ * valid_lens [B] in [0, n] or NULL (= n); temperature > 0.
+ * c_out [B] fp32, go_out [B] int32 (1/0); row_max_out, row_lse_out [B, n]
+ * fp32 (max and logsumexp of row / T) or NULL.
+ * In band: a token outside [0, V) or a valid length outside [0, n] gives
+ * c = NaN and go = 0.
+ * Limits: 1 <= n <= 64.
+ * ------------------------------------------------------------------------- */
+size_t dflash_gate_workspace_size(int B, int n, int V);
+
+dflash_status dflash_gate(
+    int B, int n, int V, const void* draft_logits, int64_t row_stride,
+    const int32_t* draft_tokens, const int32_t* valid_lens,
+    float temperature, float g, float* c_out, int32_t* go_out,
+    float* row_max_out, float* row_lse_out,
+    dflash_dtype dtype, void* ws, size_t ws_bytes, dflash_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH_H_ */

@@ -1,0 +1,58 @@
+"""Helpers of the GPU parity tests: move seeded inputs to the device and
+compare against the oracle with the tolerances of the acceptance bar."""
+import os
+import sys
+
+import numpy as np
+
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+def device():
+    import torch
+    import block_diffusion_draft_ctx_amd as dfl
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need a GPU")
+    dfl.lib()  # raises if the HIP library is missing: no fallback path exists
+    return torch.device("cuda:0")
+
+
+def up(a, kind):
+    import torch
+    dev = device()
+    a = np.ascontiguousarray(a)
+    if kind == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    if kind == "f32":
+        return torch.from_numpy(a.astype(np.float32)).to(dev)
+    if kind == "i32":
+        return torch.from_numpy(a.astype(np.int32)).to(dev)
+    raise ValueError(kind)
+
+
+def down(t):
+    """Device tensor -> numpy float64 (or int64 for integer tensors)."""
+    import torch
+    if t.dtype in (torch.int32, torch.int64):
+        return t.cpu().numpy().astype(np.int64)
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def bits(t):
+    """Raw storage bits of a bf16 / fp32 device tensor as unsigned ints."""
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.view(torch.int32).cpu().numpy().view(np.uint32)
+
+
+def rel_err(gpu, ref):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = np.sqrt(np.mean(ref ** 2))
+    return float(np.abs(gpu - ref).max() / rms)
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()

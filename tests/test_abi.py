@@ -1,0 +1,172 @@
+"""Boundary tests that need no GPU: the library loads, exports every symbol
+the header declares, sizes workspaces, and rejects bad arguments before it
+touches the device (fake pointers are only passed where validation must
+fail first; the calls that would get past validation are never made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_diffusion_draft_ctx_amd as dfl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dflash.h")
+
+# Calls with fake addresses are kept off machines with a GPU driver, where a
+# validation bug would turn into a device access.
+no_gpu = pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="fake-pointer tests run on CPU hosts")
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced
+WS = 0x100000   # 256-byte aligned
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dfl.LIB_PATH):
+        from block_diffusion_draft_ctx_amd import build
+        build.build()
+    return dfl.lib()
+
+
+def test_header_lists_the_exports():
+    assert declared_functions() == sorted(dfl.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(lib):
+    for s in range(5):
+        assert dfl.status_string(s).startswith("DFLASH_")
+    assert "UNKNOWN" in dfl.status_string(99)
+    assert lib.dflash_version() >= 100
+
+
+def test_workspace_queries(lib):
+    # greedy/sample partials grow with rows; degenerate sizes need nothing
+    a = lib.dflash_verify_workspace_size(64, 15, 128256)
+    b = lib.dflash_verify_workspace_size(1, 15, 128256)
+    assert a > b > 0 and a % 256 == 0
+    assert lib.dflash_verify_workspace_size(0, 15, 100) == 0
+    assert lib.dflash_verify_workspace_size(4, 65, 100) == 0
+    assert lib.dflash_gate_workspace_size(16, 8, 151936) > 0
+    # attention: large batches need no split, small ones do
+    assert lib.dflash_attention_workspace_size(256, 16, 32, 8, 128, 512, dfl.BF16) == 0
+    assert lib.dflash_attention_workspace_size(1, 16, 32, 8, 128, 512, dfl.BF16) > 0
+    assert lib.dflash_attention_workspace_size(1, 16, 32, 8, 128, 512, dfl.F32) == 0
+    # materialise: h_ctx staging, plus split-K partials for few rows
+    big = lib.dflash_materialize_workspace_size(131072, 5, 4096, 5, 8, 128, dfl.BF16)
+    assert big >= 131072 * 4096 * 2
+    small = lib.dflash_materialize_workspace_size(16, 5, 4096, 5, 8, 128, dfl.BF16)
+    assert small > 16 * 4096 * 2
+
+
+@no_gpu
+def test_zero_batch_is_a_noop(lib):
+    assert lib.dflash_verify_greedy(0, 15, 100, None, 100, None, 0, None, None, None, None, None,
+                                    None, None, None, dfl.BF16, None, 0, None) == dfl.OK
+    assert lib.dflash_block_attention(0, 16, 32, 8, 128, None, None, None, None, None, 1, 16,
+                                      None, 1, None, 0.0, None, None, dfl.BF16, dfl.BF16, None, 0,
+                                      None) == dfl.OK
+    assert lib.dflash_gate(0, 8, 100, None, 100, None, None, 1.0, -0.5, None, None, None, None,
+                           dfl.BF16, None, 0, None) == dfl.OK
+    assert lib.dflash_verify_sample(0, 8, 100, None, 100, None, 100, None, None, None, None, 1.0,
+                                    None, None, None, None, None, None, None, None, dfl.BF16,
+                                    None, 0, None) == dfl.OK
+
+
+def _greedy(lib, **kw):
+    a = dict(B=2, L=3, V=100, tl=FAKE, ts=100, dl=None, ds=0, dt=FAKE, cl=None, tp=None,
+             acc=FAKE, bo=FAKE, cm=FAKE, pre=None, new=None, dtype=dfl.BF16, ws=WS, nws=1 << 20)
+    a.update(kw)
+    return lib.dflash_verify_greedy(a["B"], a["L"], a["V"], a["tl"], a["ts"], a["dl"], a["ds"],
+                                    a["dt"], a["cl"], a["tp"], a["acc"], a["bo"], a["cm"],
+                                    a["pre"], a["new"], a["dtype"], a["ws"], a["nws"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), dfl.E_ARG), (dict(V=0), dfl.E_ARG), (dict(L=65), dfl.E_UNSUPPORTED),
+    (dict(tl=None), dfl.E_ARG), (dict(ts=99), dfl.E_ARG), (dict(dl=FAKE, ds=10), dfl.E_ARG),
+    (dict(acc=None), dfl.E_ARG), (dict(dt=None), dfl.E_ARG), (dict(pre=FAKE), dfl.E_ARG),
+    (dict(ws=None), dfl.E_WORKSPACE), (dict(nws=16), dfl.E_WORKSPACE),
+    (dict(ws=WS + 8), dfl.E_WORKSPACE), (dict(dtype=7), dfl.E_ARG),
+])
+def test_greedy_argument_errors(lib, kw, code):
+    assert _greedy(lib, **kw) == code
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=0.0), dfl.E_ARG), (dict(T=float("nan")), dfl.E_ARG), (dict(dl=None), dfl.E_ARG),
+    (dict(u=None), dfl.E_ARG), (dict(u2=None), dfl.E_ARG), (dict(nws=0), dfl.E_WORKSPACE),
+])
+def test_sample_argument_errors(lib, kw, code):
+    a = dict(T=1.0, dl=FAKE, u=FAKE, u2=FAKE, nws=1 << 24)
+    a.update(kw)
+    s = lib.dflash_verify_sample(2, 3, 100, FAKE, 100, a["dl"], 100, FAKE, None, a["u"], a["u2"],
+                                 a["T"], FAKE, FAKE, FAKE, None, None, None, None, None,
+                                 dfl.BF16, WS, a["nws"], None)
+    assert s == code
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=0), dfl.E_ARG), (dict(n=65), dfl.E_UNSUPPORTED), (dict(T=-1.0), dfl.E_ARG),
+    (dict(g=float("nan")), dfl.E_ARG), (dict(rs=5), dfl.E_ARG), (dict(c=None), dfl.E_ARG),
+    (dict(nws=0), dfl.E_WORKSPACE),
+])
+def test_gate_argument_errors(lib, kw, code):
+    a = dict(n=8, T=1.0, g=-0.5, rs=100, c=FAKE, nws=1 << 20)
+    a.update(kw)
+    s = lib.dflash_gate(2, a["n"], 100, FAKE, a["rs"], FAKE, None, a["T"], a["g"], a["c"], FAKE,
+                        None, None, dfl.BF16, WS, a["nws"], None)
+    assert s == code
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=96), dfl.E_UNSUPPORTED), (dict(Hq=30), dfl.E_ARG), (dict(k=65), dfl.E_UNSUPPORTED),
+    (dict(Hq=64, Hkv=2, k=16), dfl.E_UNSUPPORTED), (dict(ps=32), dfl.E_UNSUPPORTED),
+    (dict(scale=-1.0), dfl.E_ARG), (dict(q=None), dfl.E_ARG), (dict(q=FAKE + 2), dfl.E_UNSUPPORTED),
+    (dict(np_=0), dfl.E_ARG), (dict(nws=0, B=1), dfl.E_WORKSPACE),
+    (dict(dt=dfl.F32, odt=dfl.BF16), dfl.E_UNSUPPORTED), (dict(odt=5), dfl.E_ARG),
+])
+def test_attention_argument_errors(lib, kw, code):
+    a = dict(B=4, k=16, Hq=32, Hkv=8, D=128, q=FAKE, ps=16, scale=0.0, np_=10, nws=1 << 26,
+             dt=dfl.BF16, odt=dfl.BF16)
+    a.update(kw)
+    s = lib.dflash_block_attention(a["B"], a["k"], a["Hq"], a["Hkv"], a["D"], a["q"], FAKE, FAKE,
+                                   FAKE, FAKE, a["np_"], a["ps"], FAKE, 64, FAKE, a["scale"], FAKE,
+                                   None, a["dt"], a["odt"], WS, a["nws"], None)
+    assert s == code
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(m=9), dfl.E_UNSUPPORTED), (dict(D=80), dfl.E_UNSUPPORTED), (dict(d=200), dfl.E_UNSUPPORTED),
+    (dict(rps=5), dfl.E_ARG), (dict(T=-2), dfl.E_ARG), (dict(page=32), dfl.E_UNSUPPORTED),
+    (dict(hid0=None), dfl.E_ARG), (dict(wf=None), dfl.E_ARG), (dict(nws=0), dfl.E_WORKSPACE),
+])
+def test_materialize_argument_errors(lib, kw, code):
+    a = dict(T=32, m=2, d=256, D=128, rps=16, page=16, hid0=FAKE, wf=FAKE, nws=1 << 26)
+    a.update(kw)
+    m = a["m"]
+    hid = (ctypes.c_void_p * max(m, 1))(*([a["hid0"]] + [FAKE] * (m - 1)))
+    wk = (ctypes.c_void_p * 1)(FAKE)
+    wv = (ctypes.c_void_p * 1)(FAKE)
+    caches = (dfl.KVLayer * 1)(dfl.KVLayer(FAKE, FAKE, 8, a["page"]))
+    s = lib.dflash_materialize_ctx_kv(a["T"], m, a["d"], ctypes.cast(hid, dfl.PP), a["wf"], None,
+                                      1, 1, a["D"], ctypes.cast(wk, dfl.PP), ctypes.cast(wv, dfl.PP),
+                                      caches, FAKE, 4, a["rps"], FAKE, None, None, dfl.BF16, WS,
+                                      a["nws"], None)
+    assert s == code

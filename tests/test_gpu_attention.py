@@ -1,0 +1,174 @@
+"""GPU parity: block attention through the C ABI against the CPU oracle.
+
+Tolerance: max-abs / RMS <= 2e-2 (bf16 inputs) or 1e-4 (fp32), for the
+output and the log-sum-exp.  The bar applies to the computed output: the
+kernels are run with an fp32 output, and with a bf16 output whose elements
+may in addition differ by the storage rounding, half a bf16 unit in the last
+place (at most 2^-8 of the value)."""
+import numpy as np
+import pytest
+
+import block_diffusion_draft_ctx_amd as dfl
+import oracle
+import synth
+from tests.gpu_util import TOL, bits, down, log, rel_err, up
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(c, lse=True, out_dtype=None):
+    import torch
+    kind = c.dtype
+    q = up(c.q, kind)
+    lse_t = torch.empty((c.B, c.n_q_heads, c.k), dtype=torch.float32, device=q.device) if lse else None
+    od = {"f32": torch.float32, "bf16": torch.bfloat16, None: None}[out_dtype]
+    out, lse_t = dfl.block_attention(q, up(c.k_blk, kind), up(c.v_blk, kind), up(c.cache_k, kind),
+                                     up(c.cache_v, kind), up(c.block_table, "i32"),
+                                     up(c.ctx_lens, "i32"), lse=lse_t, out_dtype=od)
+    return out, lse_t
+
+
+def _check(c, out, lse, sel=None):
+    """Compare (optionally only the requests in sel) with the oracle."""
+    import torch
+    if sel is not None:
+        c = _subset(c, sel)
+        out = out[sel]
+        lse = lse[sel] if lse is not None else None
+    o_ref, l_ref = oracle.block_attention(c.q, c.k_blk, c.v_blk, c.cache_k, c.cache_v,
+                                          c.block_table, c.ctx_lens, c.dtype)
+    rms = np.sqrt(np.mean(o_ref ** 2))
+    diff = np.abs(down(out) - o_ref)
+    if out.dtype == torch.bfloat16:
+        diff = np.maximum(diff - 2.0 ** -8 * np.abs(o_ref), 0.0)   # storage rounding
+    e = float(diff.max() / rms)
+    el = rel_err(down(lse), l_ref) if lse is not None else 0.0
+    log(f"  out({out.dtype}) err {e:.2e}, lse err {el:.2e}")
+    assert e <= TOL[c.dtype]
+    assert el <= TOL[c.dtype]
+
+
+def _subset(c, sel):
+    """The listed requests with a compacted cache holding only their pages
+    (same logical contents), so the oracle widens little memory."""
+    sel = list(sel)
+    pages = sorted({int(p) for b in sel for p in c.block_table[b] if p >= 0})
+    remap = {p: i for i, p in enumerate(pages)}
+    bt = np.full((len(sel), c.block_table.shape[1]), -1, dtype=np.int32)
+    for i, b in enumerate(sel):
+        for j, p in enumerate(c.block_table[b]):
+            if p >= 0:
+                bt[i, j] = remap[int(p)]
+    idx = np.array(pages, dtype=np.int64)
+    return synth.AttentionCase(c.dtype, len(sel), c.k, c.n_q_heads, c.n_kv_heads, c.head_dim,
+                               c.q[sel], c.k_blk[sel], c.v_blk[sel], c.cache_k[idx],
+                               c.cache_v[idx], bt, c.ctx_lens[sel])
+
+
+@pytest.mark.parametrize("dtype,B,k,Hq,Hkv,D,ctx,qs,seed", [
+    ("f32", 1, 8, 4, 2, 64, [64], 1.0, 1301),              # tiny fp32 workload
+    ("f32", 1, 8, 4, 2, 64, [64], 10.0, 1302),             # peaked attention
+    ("f32", 3, 4, 6, 2, 128, [0, 17, 40], 1.0, 1303),
+    ("bf16", 3, 16, 32, 8, 128, [0, 45, 1000], 1.0, 2301),  # GQA 4, several tiles, ragged
+    ("bf16", 2, 16, 32, 8, 128, [1024, 777], 4.0, 2302),
+    ("bf16", 2, 8, 16, 4, 64, [33, 300], 1.0, 2303),        # D = 64, 2 waves
+    ("bf16", 2, 1, 8, 8, 128, [0, 5], 1.0, 2304),           # k = 1, G = 1
+    ("bf16", 2, 16, 64, 8, 128, [100, 513], 1.0, 2305),     # G = 8: 8 waves
+    ("bf16", 1, 64, 16, 4, 64, [95], 1.0, 2306),            # k = 64, 16 waves
+    ("bf16", 2, 5, 12, 3, 128, [31, 32], 2.0, 2307),        # rows not a multiple of 16
+])
+def test_attention_parity(dtype, B, k, Hq, Hkv, D, ctx, qs, seed):
+    log(f"attention dtype={dtype} B={B} k={k} Hq={Hq} Hkv={Hkv} D={D} ctx={ctx} seed={seed}")
+    c = synth.attention_case(seed, dtype=dtype, B=B, k=k, n_q_heads=Hq, n_kv_heads=Hkv,
+                             head_dim=D, ctx_lens=ctx, q_scale=qs)
+    for od in (["f32"] if dtype == "f32" else ["f32", "bf16"]):
+        out, lse = _run(c, out_dtype=od)
+        _check(c, out, lse)
+
+
+@pytest.mark.parametrize("B,C,seed", [(1, 8192, 2311), (8, 4096, 2312), (1, 1024, 2313)])
+def test_attention_split_context(B, C, seed):
+    """Few requests: the context is split across workgroups and merged by LSE."""
+    log(f"attention split B={B} C={C}")
+    assert dfl.lib().dflash_attention_workspace_size(B, 16, 32, 8, 128, (C + 15) // 16, dfl.BF16) > 0
+    c = synth.attention_case(seed, dtype="bf16", B=B, k=16, n_q_heads=32, n_kv_heads=8,
+                             head_dim=128, ctx_lens=[C - 3 * b for b in range(B)])
+    for od in ("f32", "bf16"):
+        out, lse = _run(c, out_dtype=od)
+        _check(c, out, lse)
+
+
+def test_attention_llama_decode_full_size_sampled():
+    """The timed launch: Llama-3.1-8B-shaped decode, B = 64, ctx 8192, k = 16,
+    32 Q / 8 KV heads, D = 128.  Sampled requests are checked against the
+    oracle; every output must be finite."""
+    B, C = 64, 8192
+    log(f"attention full size B={B} C={C}")
+    c = synth.attention_case(2320, dtype="bf16", B=B, k=16, n_q_heads=32, n_kv_heads=8,
+                             head_dim=128, ctx_lens=[C] * B)
+    out, lse = _run(c)
+    assert np.isfinite(down(out)).all()
+    _check(c, out, lse, sel=[0, 21, 63])
+
+
+def test_attention_ragged_contexts():
+    rng = np.random.default_rng(5)
+    ctx = rng.integers(1024, 8193, size=12)
+    c = synth.attention_case(2321, dtype="bf16", B=12, k=16, n_q_heads=32, n_kv_heads=8,
+                             head_dim=128, ctx_lens=ctx)
+    out, lse = _run(c)
+    _check(c, out, lse, sel=[0, 5, 11])
+
+
+def test_attention_packed_training_mask_sampled():
+    """Packed training blocks: every block's table lists the same sequence's
+    pages, ctx = anchor; checked on sampled blocks."""
+    c, P = synth.packed_attention_case(2330, dtype="bf16", seq_len=8192, k=16, n_q_heads=32,
+                                       n_kv_heads=8, head_dim=128, max_anchors=512)
+    log(f"packed: {c.B} blocks, prompt {P}")
+    sel = [0, c.B // 3, c.B // 2, c.B - 1]
+    for od in ("f32", "bf16"):
+        out, lse = _run(c, out_dtype=od)
+        assert np.isfinite(down(out)).all()
+        _check(c, out, lse, sel=sel)
+
+
+def test_attention_determinism_and_page_order_invariance():
+    """Two runs are bitwise equal; moving the same logical pages to other
+    physical pages changes nothing."""
+    a = synth.attention_case(2340, dtype="bf16", B=4, k=16, n_q_heads=32, n_kv_heads=8,
+                             head_dim=128, ctx_lens=[300, 2000, 17, 900], shuffle=False)
+    b = synth.attention_case(2340, dtype="bf16", B=4, k=16, n_q_heads=32, n_kv_heads=8,
+                             head_dim=128, ctx_lens=[300, 2000, 17, 900], shuffle=True)
+    for bb in range(4):
+        for lp in range(a.block_table.shape[1]):
+            pa, pb = a.block_table[bb, lp], b.block_table[bb, lp]
+            if pa >= 0:
+                b.cache_k[pb] = a.cache_k[pa]
+                b.cache_v[pb] = a.cache_v[pa]
+    o1, l1 = _run(a)
+    o2, l2 = _run(a)
+    o3, l3 = _run(b)
+    np.testing.assert_array_equal(bits(o1), bits(o2))
+    np.testing.assert_array_equal(bits(o1), bits(o3))
+    np.testing.assert_array_equal(bits(l1), bits(l3))
+
+
+def test_attention_in_band_errors():
+    """A ctx length beyond the table's capacity or an out-of-range page entry
+    poisons only that request's outputs (NaN)."""
+    c = synth.attention_case(2350, dtype="bf16", B=3, k=16, n_q_heads=32, n_kv_heads=8,
+                             head_dim=128, ctx_lens=[40, 40, 40])
+    ctx = c.ctx_lens.copy()
+    ctx[0] = c.block_table.shape[1] * 16 + 1
+    bt = c.block_table.copy()
+    bt[2, 1] = c.cache_k.shape[0] + 5
+    import torch
+    kind = "bf16"
+    lse = torch.empty((3, 32, 16), dtype=torch.float32, device="cuda:0")
+    out, lse = dfl.block_attention(up(c.q, kind), up(c.k_blk, kind), up(c.v_blk, kind),
+                                   up(c.cache_k, kind), up(c.cache_v, kind), up(bt, "i32"),
+                                   up(ctx, "i32"), lse=lse)
+    o = down(out)
+    assert np.isnan(o[0]).all() and np.isnan(o[2]).all() and np.isfinite(o[1]).all()
+    assert np.isnan(down(lse)[0]).all() and np.isfinite(down(lse)[1]).all()

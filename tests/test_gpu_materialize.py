@@ -1,0 +1,128 @@
+"""GPU parity: target-context KV materialisation through the C ABI against
+the CPU oracle.  Cache slots that are written must match within max-abs / RMS
+<= 2e-2 (bf16) or 1e-4 (fp32); every other slot must keep its sentinel bits."""
+import numpy as np
+import pytest
+
+import block_diffusion_draft_ctx_amd as dfl
+import oracle
+import synth
+from tests.gpu_util import TOL, bits, down, log, rel_err, up
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(c, want_h=True):
+    import torch
+    kind = c.dtype
+    ck = [up(x, kind) for x in c.cache_k]
+    cv = [up(x, kind) for x in c.cache_v]
+    hid = [up(h, kind) for h in c.hiddens]
+    h_out = None
+    if want_h:
+        h_out = torch.empty((c.T, c.d_model), dtype=hid[0].dtype, device=hid[0].device)
+    dfl.materialize_ctx_kv(hid, up(c.W_f, kind), None if c.b_f is None else up(c.b_f, kind),
+                           [up(w, kind) for w in c.W_K], [up(w, kind) for w in c.W_V], ck, cv,
+                           up(c.block_table, "i32"), c.rows_per_seq, up(c.seq_start_pos, "i32"),
+                           None if c.commit_lens is None else up(c.commit_lens, "i32"),
+                           h_ctx_out=h_out)
+    return ck, cv, h_out
+
+
+def _check(c, ck, cv, h_out, rows=None):
+    """Compare written slots (all rows, or the listed rows) with the oracle and
+    the untouched slots with the sentinel."""
+    T = c.T
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    ref = oracle.materialize([h[rows] for h in c.hiddens], c.W_f, c.b_f, c.W_K, c.W_V,
+                             c.n_kv_heads, c.head_dim, c.dtype)
+    if h_out is not None:
+        e = rel_err(down(h_out)[rows], ref["h_ctx"])
+        log(f"  h_ctx err {e:.2e}")
+        assert e <= TOL[c.dtype]
+    sentinel = c.cache_k[0].reshape(-1).view(np.uint16 if c.dtype == "bf16" else np.uint32)[0]
+    for l in range(c.n_layers):
+        for name, gpu, rv in (("K", ck[l], ref["K"][l]), ("V", cv[l], ref["V"][l])):
+            g = down(gpu)
+            gb = bits(gpu)
+            written = np.zeros(gpu.shape[:2], dtype=bool)
+            got, want = [], []
+            for i, r in enumerate(rows):
+                s, j = divmod(int(r), c.rows_per_seq)
+                if c.commit_lens is not None and j >= c.commit_lens[s]:
+                    continue
+                pos = int(c.seq_start_pos[s]) + j
+                page = int(c.block_table[s, pos // 16])
+                if page < 0 or page >= c.num_pages:
+                    continue
+                written[page, pos % 16] = True
+                got.append(g[page, pos % 16])
+                want.append(rv[i])
+            if got:
+                e = rel_err(np.array(got), np.array(want))
+                assert e <= TOL[c.dtype], f"layer {l} {name}: err {e}"
+            if len(rows) == T:   # every row checked: untouched slots keep the sentinel
+                untouched = gb[~written]
+                assert (untouched == sentinel).all(), f"layer {l} {name}: stray writes"
+        log(f"  layer {l} ok")
+
+
+@pytest.mark.parametrize("dtype,m,d,Ld,Hkv,D,n_seq,rps,start,commit,seed", [
+    ("f32", 5, 256, 1, 2, 64, 1, 64, [0], None, 1401),          # tiny fp32: 64-position prefill
+    ("f32", 5, 256, 1, 2, 64, 1, 8, [64], "random", 1402),      # then an 8-row decode commit
+    ("f32", 3, 96, 2, 1, 64, 3, 5, [0, 14, 30], [5, 2, 0], 1403),
+    ("bf16", 5, 256, 2, 2, 64, 3, 16, None, "random", 2401),
+    ("bf16", 2, 384, 3, 1, 128, 2, 40, [3, 0], [40, 17], 2402),  # rows straddle pages
+    ("bf16", 5, 4096, 5, 8, 128, 8, 16, None, "random", 2403),   # Llama-shaped decode, B = 8
+])
+def test_materialize_parity(dtype, m, d, Ld, Hkv, D, n_seq, rps, start, commit, seed):
+    log(f"materialise dtype={dtype} m={m} d={d} layers={Ld} Hkv={Hkv} D={D} rows={n_seq}x{rps}")
+    c = synth.materialize_case(seed, dtype=dtype, m=m, d_model=d, n_layers=Ld, n_kv_heads=Hkv,
+                               head_dim=D, n_seq=n_seq, rows_per_seq=rps, start_pos=start,
+                               commit=commit)
+    ck, cv, h = _run(c)
+    _check(c, ck, cv, h)
+
+
+def test_materialize_decode_launch_config_sampled():
+    """The timed launch: 64 requests x 16 committed-row candidates (T = 1024)
+    of the Llama-3.1-8B-shaped draft (d 4096, 5 hiddens, 5 layers, 8 KV heads
+    x 128); sampled rows against the oracle."""
+    c = synth.materialize_case(2410, dtype="bf16", m=5, d_model=4096, n_layers=5, n_kv_heads=8,
+                               head_dim=128, n_seq=64, rows_per_seq=16, commit="random")
+    ck, cv, h = _run(c)
+    rows = np.random.default_rng(0).choice(c.T, size=48, replace=False)
+    _check(c, ck, cv, h, rows=np.sort(rows))
+
+
+def test_materialize_prefill_shape_sampled():
+    """Prefill-shaped materialisation (whole sequences, 16-token pages, every
+    row committed) at T = 8192; sampled rows against the oracle."""
+    c = synth.materialize_case(2420, dtype="bf16", m=5, d_model=4096, n_layers=5, n_kv_heads=8,
+                               head_dim=128, n_seq=2, rows_per_seq=4096, start_pos=[0, 0])
+    ck, cv, h = _run(c, want_h=False)
+    rows = np.sort(np.random.default_rng(1).choice(c.T, size=32, replace=False))
+    _check(c, ck, cv, None, rows=rows)
+
+
+def test_materialize_unmapped_and_out_of_range_pages_are_skipped():
+    c = synth.materialize_case(2430, dtype="bf16", m=2, d_model=256, n_layers=1, n_kv_heads=2,
+                               head_dim=64, n_seq=2, rows_per_seq=32, start_pos=[0, 0])
+    c.block_table[0, 1] = -1
+    c.block_table[1, 0] = 10_000
+    ck, cv, h = _run(c)
+    _check(c, ck, cv, h, rows=list(range(0, 16)) + list(range(48, 64)))
+    # rows 16..31 of seq 0 (unmapped) and 0..15 of seq 1 (out of range): nothing written anywhere
+    gb = bits(ck[0])
+    sentinel = c.cache_k[0].reshape(-1)[0]
+    written = 32  # 16 rows of seq 0 + 16 rows of seq 1
+    assert (gb != sentinel).reshape(gb.shape[0], 16, -1).any(-1).sum() == written
+
+
+def test_materialize_is_deterministic():
+    c = synth.materialize_case(2440, dtype="bf16", m=5, d_model=512, n_layers=2, n_kv_heads=4,
+                               head_dim=128, n_seq=4, rows_per_seq=16)
+    a = _run(c)
+    b = _run(c)
+    for x, y in zip(a[0] + a[1] + [a[2]], b[0] + b[1] + [b[2]]):
+        np.testing.assert_array_equal(bits(x), bits(y))
