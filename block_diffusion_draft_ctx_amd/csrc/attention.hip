@@ -31,7 +31,19 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kKT = 32;  // keys per tile
+// Tuning knobs (compile-time): keys per tile, workgroups the split count
+// aims for, and whether context K/V loads carry the non-temporal hint.
+#ifndef DFLASH_ATTN_KT
+#define DFLASH_ATTN_KT 64
+#endif
+#ifndef DFLASH_ATTN_TARGET_WGS
+#define DFLASH_ATTN_TARGET_WGS 512
+#endif
+#ifndef DFLASH_ATTN_NT
+#define DFLASH_ATTN_NT 1
+#endif
+constexpr int kKT = DFLASH_ATTN_KT;  // keys per tile
+constexpr int kMaxSplitPages = 1024; // pages one split may span (16384 keys)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -55,17 +67,41 @@ struct AttnP {
   int S;        // ctx splits
 };
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnP p) {
+// Transposing LDS read (gfx950): within each 16-lane group, output lane j
+// receives element (j % 4) of the 8 bytes addressed by source lane
+// 4*r + j/4, for r = 0..3.  With source lane 4r+q pointing at row key_r,
+// columns c0+4q..c0+4q+3 of a row-major [key][d] tile, lane j gets
+// (row key_0..key_3, column c0 + j): four keys of one column, which is the
+// MFMA operand layout along the key (contraction) axis.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// One workgroup = (request, kv-head, ctx split); 2*NQ wavefronts arranged as
+// NQ query slices of 32 rows x 2 key halves.  Per 64-key tile, wave
+// (wq, wk) computes S^T for keys [32wk, 32wk+32) against its 32 query rows
+// and accumulates O^T over the same keys (MFMA 32x32x16 bf16), with its own
+// online-softmax state; the two key halves are merged once at the end.
+template <int D, int NQ>
+__global__ __launch_bounds__(NQ * 128) __attribute__((amdgpu_waves_per_eu(2)))
+void k_attn_bf16(AttnP p) {
+  constexpr int NW = 2 * NQ;
   constexpr int NT = NW * 64;
   constexpr int CPR = D / 8;             // 16-byte chunks per key row
-  constexpr int NCH = kKT * CPR;         // chunks per tile
+  constexpr int NCH = kKT * CPR;         // chunks per tile (each of K and V)
   constexpr int CPT = (NCH + NT - 1) / NT;
-  constexpr int KS = D + 8;              // LDS row stride of K (elements)
-  constexpr int VS = kKT + 8;            // LDS row stride of V^T
-  constexpr int NB = D / 16;
-  __shared__ __align__(16) uint16_t Ks[kKT * KS];
-  __shared__ __align__(16) uint16_t Vt[D * VS];
+  constexpr int KS = D + 8;              // LDS row stride of the K and V tiles (elements)
+  constexpr int NMB = D / 32;            // 32-row blocks of O^T
+  static_assert(kKT == 64, "the 2x2 wave layout assumes 64-key tiles");
+  __shared__ __align__(16) uint16_t smem[2 * kKT * KS];
+  uint16_t* Ks = smem;
+  uint16_t* Vs = smem + kKT * KS;
+  __shared__ int pages[kMaxSplitPages];
 
   const int split = blockIdx.x % p.S;
   const int g = (blockIdx.x / p.S) % p.Hkv;
@@ -75,20 +111,21 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnP p) {
   const int Mq = G * k;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int c16 = lane & 15;   // column (query) of B/C; row of A
-  const int grp = lane >> 4;
-  const int qrow = w * 16 + c16;
+  const int wq = w >> 1, wk = w & 1;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int qrow = 32 * wq + l32;
   const bool qvalid = qrow < Mq;
   const int hg = qvalid ? qrow / k : 0;
   const int pos = qvalid ? qrow - hg * k : 0;
   const int h = g * G + hg;
 
-  bf16x8 qf[D / 32];
+  // B operand of S^T = K . Q^T: lane (q, hh) holds Q[q][16s + 8hh .. +8]
+  bf16x8 qf[D / 16];
   {
-    const uint16_t* qp = p.q + (((int64_t)b * k + pos) * p.Hq + h) * D + 8 * grp;
+    const uint16_t* qp = p.q + (((int64_t)b * k + pos) * p.Hq + h) * D + 8 * hh;
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-      uint4 v = qvalid ? *reinterpret_cast<const uint4*>(qp + 32 * s) : make_uint4(0, 0, 0, 0);
+    for (int s = 0; s < D / 16; ++s) {
+      uint4 v = qvalid ? *reinterpret_cast<const uint4*>(qp + 16 * s) : make_uint4(0, 0, 0, 0);
       qf[s] = as_bf16x8(v);
     }
   }
@@ -101,42 +138,61 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnP p) {
   const int tps = (nt + p.S - 1) / p.S;
   const int t0 = split * tps;
   const int t1 = min(nt, t0 + tps);
-  const int32_t* btr = p.bt + (int64_t)b * p.max_pages;
 
-  uint4 kr[CPT], vr[CPT];
+  // Physical pages of this split's context keys, staged in LDS once so that
+  // no tile waits on a dependent page-table load.
+  const int pg0 = t0 * (kKT / 16);
+  const int pg1 = min((t1 * kKT + 15) >> 4, (C + 15) >> 4);
+  {
+    const int32_t* btr = p.bt + (int64_t)b * p.max_pages;
+    bool bad = false;
+    for (int i = pg0 + (int)threadIdx.x; i < pg1; i += NT) {
+      int pg = btr[i];
+      if (pg < 0 || pg >= p.num_pages) { bad = true; pg = 0; }
+      pages[i - pg0] = pg;
+    }
+    poison |= __syncthreads_or(bad) != 0;
+  }
+
+  // Branch-free tile fetch: every chunk issues the same two 16-byte loads
+  // (context slot, block key, or -- past the last key -- a clamped block key
+  // whose score is masked), so no load waits on another.
+  u32x4 kr[CPT], vr[CPT];
   auto fetch = [&](int tile) __attribute__((always_inline)) {
+    const int pbase = (tile - t0) * (kKT / 16);
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int e = threadIdx.x + c * NT;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (e < NCH) {
-        const int key = e / CPR;
-        const int dc = e - key * CPR;
-        const int kp = tile * kKT + key;
-        if (kp < C) {
-          const int page = btr[kp >> 4];
-          if (page < 0 || page >= p.num_pages) {
-            poison = true;
-          } else {
-            const int64_t off = (((int64_t)page * 16 + (kp & 15)) * p.Hkv + g) * D + dc * 8;
-            kv = ld_stream16(p.ck + off);
-            vv = ld_stream16(p.cv + off);
-          }
-        } else if (kp < total) {
-          const int64_t off = (((int64_t)b * k + (kp - C)) * p.Hkv + g) * D + dc * 8;
-          kv = *reinterpret_cast<const uint4*>(p.kb + off);
-          vv = *reinterpret_cast<const uint4*>(p.vb + off);
-        }
-      }
-      kr[c] = kv;
-      vr[c] = vv;
+      const int e = min((int)threadIdx.x + c * NT, NCH - 1);
+      const int key = e / CPR;
+      const int dc = e - key * CPR;
+      const int kp = tile * kKT + key;
+      const int page = pages[pbase + (key >> 4)];
+      const int64_t off_c = (((int64_t)page * 16 + (kp & 15)) * p.Hkv + g) * D + dc * 8;
+      const int jb = min(max(kp - C, 0), k - 1);
+      const int64_t off_b = (((int64_t)b * k + jb) * p.Hkv + g) * D + dc * 8;
+      const bool in_ctx = kp < C;
+      const uint16_t* pk = in_ctx ? p.ck + off_c : p.kb + off_b;
+      const uint16_t* pv = in_ctx ? p.cv + off_c : p.vb + off_b;
+#if DFLASH_ATTN_NT
+      kr[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pk));
+      vr[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pv));
+#else
+      kr[c] = *reinterpret_cast<const u32x4*>(pk);
+      vr[c] = *reinterpret_cast<const u32x4*>(pv);
+#endif
     }
   };
 
   float m = neg_inf(), l = 0.f;
-  f32x4 acc[NB];
+  f32x16 acc[NMB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[mb][j] = 0.f;
+
+  // Transposing-read source lane (4r + q) within a 16-lane group
+  const int tr_r = (lane & 15) >> 2, tr_q = lane & 3;
+  const int grp16 = lane >> 4;             // 16-lane group: d offset 16*(grp16&1), key half hh
 
   if (t0 < t1) fetch(t0);
   for (int tile = t0; tile < t1; ++tile) {
@@ -144,122 +200,151 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnP p) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int e = threadIdx.x + c * NT;
-      if (e < NCH) {
+      if (NCH % NT == 0 || e < NCH) {
         const int key = e / CPR;
         const int dc = e - key * CPR;
-        *reinterpret_cast<uint4*>(Ks + key * KS + dc * 8) = kr[c];
-        const uint32_t vw[4] = {vr[c].x, vr[c].y, vr[c].z, vr[c].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          Vt[(dc * 8 + 2 * j) * VS + key] = (uint16_t)(vw[j] & 0xffffu);
-          Vt[(dc * 8 + 2 * j + 1) * VS + key] = (uint16_t)(vw[j] >> 16);
-        }
+        *reinterpret_cast<u32x4*>(Ks + key * KS + dc * 8) = kr[c];
+        *reinterpret_cast<u32x4*>(Vs + key * KS + dc * 8) = vr[c];
       }
     }
     __syncthreads();
     if (tile + 1 < t1) fetch(tile + 1);
 
-    // S^T = K . Q^T for 32 keys (two 16-key blocks)
-    f32x4 sacc[2];
+    // S^T[32 keys x 32 q] for this wave's key half
+    f32x16 sacc;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      sacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
+    const uint16_t* krow = Ks + (32 * wk + l32) * KS + 8 * hh;
 #pragma unroll
-      for (int s = 0; s < D / 32; ++s) {
-        const uint4 a = *reinterpret_cast<const uint4*>(Ks + (16 * mb + c16) * KS + 32 * s + 8 * grp);
-        sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), qf[s], sacc[mb], 0, 0, 0);
-      }
+    for (int s = 0; s < D / 16; ++s) {
+      const uint4 a = *reinterpret_cast<const uint4*>(krow + 16 * s);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[s], sacc, 0, 0, 0);
     }
-    // scores of query c16 for keys tile*32 + 16*mb + 4*grp + r
-    float sv[8];
+    // sacc[j]: key 32wk + 8*(j/4) + 4*hh + j%4 of the tile, query l32
+    float sv[16];
     float tmax = neg_inf();
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kk = tile * kKT + 16 * mb + 4 * grp + r;
-        const float v = (kk < total) ? sacc[mb][r] * p.sl2 : neg_inf();
-        sv[mb * 4 + r] = v;
-        tmax = fmaxf(tmax, v);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    for (int j = 0; j < 16; ++j) {
+      const int kk = tile * kKT + 32 * wk + 8 * (j >> 2) + 4 * hh + (j & 3);
+      const float v = (kk < total) ? sacc[j] * p.sl2 : neg_inf();
+      sv[j] = v;
+      tmax = fmaxf(tmax, v);
+    }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const float mn = fmaxf(m, tmax);
-    const float alpha = exp2f(m - mn);
-    float ps[8];
+    const float mref = (mn == neg_inf()) ? 0.f : mn;   // a key half with no key yet
+    const float alpha = exp2f(m - mref);
     float rs = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      ps[j] = exp2f(sv[j] - mn);
-      rs += ps[j];
+    for (int j = 0; j < 16; ++j) {
+      sv[j] = exp2f(sv[j] - mref);
+      rs += sv[j];
     }
-    rs += __shfl_xor(rs, 16, 64);
     rs += __shfl_xor(rs, 32, 64);
     l = l * alpha + rs;
     m = mn;
-    const uint4 pw = make_uint4(pack_bf16x2(ps[0], ps[1]), pack_bf16x2(ps[2], ps[3]),
-                                pack_bf16x2(ps[4], ps[5]), pack_bf16x2(ps[6], ps[7]));
-    const bf16x8 pb = as_bf16x8(pw);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      acc[nb] *= alpha;
-      const uint16_t* vrow = Vt + (16 * nb + c16) * VS + 4 * grp;
-      const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-      const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-      const bf16x8 a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, acc[nb], 0, 0, 0);
+    for (int mb = 0; mb < NMB; ++mb) acc[mb] *= alpha;
+    // O^T[d x 32 q] += V^T . P^T over this wave's 32 keys, 16 per MFMA.  In
+    // both operands contraction index 8*hh + e is key 16*kk2 + 8*(e/4) +
+    // 4*hh + e%4 (the order the S^T accumulators already hold).
+#pragma unroll
+    for (int kk2 = 0; kk2 < 2; ++kk2) {
+      const float* ps = sv + 8 * kk2;
+      const bf16x8 pb = as_bf16x8(make_uint4(pack_bf16x2(ps[0], ps[1]), pack_bf16x2(ps[2], ps[3]),
+                                             pack_bf16x2(ps[4], ps[5]), pack_bf16x2(ps[6], ps[7])));
+      const uint16_t* v0 = Vs + (32 * wk + 16 * kk2 + 4 * (grp16 >> 1) + tr_r) * KS +
+                           16 * (grp16 & 1) + 4 * tr_q;
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        const uint2 lo = lds_read_tr16(v0 + 32 * mb);
+        const uint2 hi = lds_read_tr16(v0 + 8 * KS + 32 * mb);
+        const bf16x8 a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[mb], 0, 0, 0);
+      }
     }
   }
 
+  // Merge the two key halves: wave (wq, 1) hands its state to wave (wq, 0)
+  // through LDS, one query slice at a time.
+  float* xo = reinterpret_cast<float*>(smem);          // [64 lanes][D/2] partial O
+  float* xm = xo + 64 * (D / 2);                        // [32] m, [32] l
+  for (int sl = 0; sl < NQ; ++sl) {
+    __syncthreads();
+    if (wq == sl && wk == 1) {
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) xo[(mb * 16 + j) * 64 + lane] = acc[mb][j];
+      if (hh == 0) { xm[l32] = m; xm[32 + l32] = l; }
+    }
+    __syncthreads();
+    if (wq == sl && wk == 0) {
+      const float m1 = xm[l32], l1 = xm[32 + l32];
+      const float M = fmaxf(m, m1);
+      const float Mr = (M == neg_inf()) ? 0.f : M;
+      const float w0 = exp2f(m - Mr), w1 = exp2f(m1 - Mr);
+      l = l * w0 + l1 * w1;
+      m = M;
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[mb][j] = acc[mb][j] * w0 + xo[(mb * 16 + j) * 64 + lane] * w1;
+    }
+  }
+  if (wk != 0 || !qvalid) return;
+
+  // lane (q, hh) holds O^T[d][q] for d = 32mb + 8*(j/4) + 4*hh + j%4
   if (p.S == 1) {
-    if (qvalid) {
-      const float inv = poison ? __builtin_nanf("") : 1.f / l;
-      const int64_t o0 = (((int64_t)b * k + pos) * p.Hq + h) * D + 4 * grp;
-      if (p.out_f32) {
-        float* op = static_cast<float*>(p.out) + o0;
+    const float inv = poison ? __builtin_nanf("") : 1.f / l;
+    const int64_t o0 = (((int64_t)b * k + pos) * p.Hq + h) * D + 4 * hh;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          *reinterpret_cast<float4*>(op + 16 * nb) =
-              make_float4(acc[nb][0] * inv, acc[nb][1] * inv, acc[nb][2] * inv, acc[nb][3] * inv);
-      } else {
-        uint16_t* op = static_cast<uint16_t*>(p.out) + o0;
+    for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
+      for (int jq = 0; jq < 4; ++jq) {
+        const int d0 = 32 * mb + 8 * jq;
+        if (p.out_f32) {
+          *reinterpret_cast<float4*>(static_cast<float*>(p.out) + o0 + d0) =
+              make_float4(acc[mb][4 * jq] * inv, acc[mb][4 * jq + 1] * inv,
+                          acc[mb][4 * jq + 2] * inv, acc[mb][4 * jq + 3] * inv);
+        } else {
           uint2 o;
-          o.x = pack_bf16x2(acc[nb][0] * inv, acc[nb][1] * inv);
-          o.y = pack_bf16x2(acc[nb][2] * inv, acc[nb][3] * inv);
-          *reinterpret_cast<uint2*>(op + 16 * nb) = o;
+          o.x = pack_bf16x2(acc[mb][4 * jq] * inv, acc[mb][4 * jq + 1] * inv);
+          o.y = pack_bf16x2(acc[mb][4 * jq + 2] * inv, acc[mb][4 * jq + 3] * inv);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o0 + d0) = o;
         }
       }
-      if (p.lse && grp == 0)
-        p.lse[((int64_t)b * p.Hq + h) * k + pos] = poison ? __builtin_nanf("") : (m + log2f(l)) * kLn2;
-    }
+    if (p.lse && hh == 0)
+      p.lse[((int64_t)b * p.Hq + h) * k + pos] = poison ? __builtin_nanf("") : (m + log2f(l)) * kLn2;
   } else {
     const int64_t rowi = (((int64_t)b * p.Hkv + g) * p.S + split) * Mq + qrow;
-    if (qvalid) {
-      float* op = p.po + rowi * D + 4 * grp;
+    float* op = p.po + rowi * D + 4 * hh;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        *reinterpret_cast<float4*>(op + 16 * nb) = make_float4(acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3]);
-      if (grp == 0) p.pml[rowi] = make_float2(m, poison ? __builtin_nanf("") : l);
-    }
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq)
+        *reinterpret_cast<float4*>(op + 32 * mb + 8 * jq) =
+            make_float4(acc[mb][4 * jq], acc[mb][4 * jq + 1], acc[mb][4 * jq + 2], acc[mb][4 * jq + 3]);
+    if (hh == 0) p.pml[rowi] = make_float2(m, poison ? __builtin_nanf("") : l);
   }
 }
 
 template <typename OutT>
-__global__ __launch_bounds__(256) void k_attn_combine(int B, int k, int Hq, int Hkv, int D, int S,
+__global__ __launch_bounds__(128) void k_attn_combine(int B, int k, int Hq, int Hkv, int D, int S,
                                                      const float* __restrict__ po,
                                                      const float2* __restrict__ pml,
                                                      OutT* __restrict__ out, float* __restrict__ lse) {
-  const int bg = blockIdx.x;
-  const int b = bg / Hkv, g = bg - b * Hkv;
+  // one workgroup per (request, kv-head, query row); lanes over head_dim
   const int G = Hq / Hkv;
   const int Mq = G * k;
-  for (int e = threadIdx.x; e < Mq * D; e += blockDim.x) {
-    const int qrow = e / D, d = e - qrow * D;
-    const int64_t base = (int64_t)bg * S * Mq + qrow;
-    float M = neg_inf();
-    for (int s = 0; s < S; ++s) M = fmaxf(M, pml[base + (int64_t)s * Mq].x);
+  const int qrow = blockIdx.x % Mq;
+  const int bg = blockIdx.x / Mq;
+  const int b = bg / Hkv, g = bg - b * Hkv;
+  const int64_t base = (int64_t)bg * S * Mq + qrow;
+  float M = neg_inf();
+  for (int s = 0; s < S; ++s) M = fmaxf(M, pml[base + (int64_t)s * Mq].x);
+  const int hg = qrow / k, pos = qrow - hg * k, h = g * G + hg;
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
     float Ls = 0.f, O = 0.f;
     for (int s = 0; s < S; ++s) {
       const float2 ml = pml[base + (int64_t)s * Mq];
@@ -268,7 +353,6 @@ __global__ __launch_bounds__(256) void k_attn_combine(int B, int k, int Hq, int 
       Ls += ml.y * wgt;
       O += po[(base + (int64_t)s * Mq) * D + d] * wgt;
     }
-    const int hg = qrow / k, pos = qrow - hg * k, h = g * G + hg;
     const float v = O / Ls;
     const int64_t oi = (((int64_t)b * k + pos) * Hq + h) * D + d;
     if constexpr (sizeof(OutT) == 2) out[oi] = f32_to_bf16(v);
@@ -353,32 +437,34 @@ __global__ __launch_bounds__(64) void k_attn_f32(int B, int k, int Hq, int Hkv, 
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-template <int D, int NW>
+template <int D, int NQ>
 void launch_bf16(const AttnArgs& a, AttnP p, hipStream_t st) {
-  hipLaunchKernelGGL((k_attn_bf16<D, NW>), dim3((unsigned)(a.B * a.Hkv * p.S)), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((k_attn_bf16<D, NQ>), dim3((unsigned)(a.B * a.Hkv * p.S)), dim3(NQ * 128), 0,
                      st, p);
 }
 
 template <int D>
 void dispatch_nw(const AttnArgs& a, AttnP p, hipStream_t st) {
-  const int nw = (a.Hq / a.Hkv * a.k + 15) / 16;
-  if (nw <= 1) launch_bf16<D, 1>(a, p, st);
-  else if (nw <= 2) launch_bf16<D, 2>(a, p, st);
-  else if (nw <= 4) launch_bf16<D, 4>(a, p, st);
-  else if (nw <= 8) launch_bf16<D, 8>(a, p, st);
-  else launch_bf16<D, 16>(a, p, st);
+  const int nq = (a.Hq / a.Hkv * a.k + 31) / 32;   // 32-row query slices
+  if (nq <= 1) launch_bf16<D, 1>(a, p, st);
+  else if (nq <= 2) launch_bf16<D, 2>(a, p, st);
+  else if (nq <= 4) launch_bf16<D, 4>(a, p, st);
+  else launch_bf16<D, 8>(a, p, st);
 }
 
 }  // namespace
 
 int attention_splits(int B, int Hkv, int k, int max_pages) {
-  // Enough workgroups to keep every CU streaming (about 1024), but no split
-  // shorter than 4 key tiles.
+  // About two workgroups per CU so every CU keeps several tiles in flight,
+  // but no split shorter than 4 key tiles; a split never spans more pages
+  // than its LDS page list holds.
   const int64_t groups = (int64_t)B * Hkv;
   const int64_t tiles = ((int64_t)max_pages * 16 + k + kKT - 1) / kKT;
-  int64_t s = (1024 + groups - 1) / std::max<int64_t>(groups, 1);
+  int64_t s = (DFLASH_ATTN_TARGET_WGS + groups - 1) / std::max<int64_t>(groups, 1);
   s = std::min<int64_t>(s, std::max<int64_t>(1, tiles / 4));
   s = std::min<int64_t>(s, 64);
+  const int64_t tiles_cap = kMaxSplitPages * 16 / kKT;
+  s = std::max<int64_t>(s, (tiles + tiles_cap - 1) / tiles_cap);
   return (int)std::max<int64_t>(s, 1);
 }
 
@@ -405,11 +491,12 @@ hipError_t launch_attention(bool bf16, const AttnArgs& a, void* ws, hipStream_t 
     if (a.D == 64) dispatch_nw<64>(a, p, st);
     else dispatch_nw<128>(a, p, st);
     if (S > 1) {
+      const unsigned rows = (unsigned)(a.B * a.Hkv * (a.Hq / a.Hkv) * a.k);
       if (a.out_f32)
-        hipLaunchKernelGGL((k_attn_combine<float>), dim3(a.B * a.Hkv), dim3(256), 0, st, a.B, a.k,
+        hipLaunchKernelGGL((k_attn_combine<float>), dim3(rows), dim3(128), 0, st, a.B, a.k,
                            a.Hq, a.Hkv, a.D, S, po, pml, static_cast<float*>(a.out), a.lse);
       else
-        hipLaunchKernelGGL((k_attn_combine<uint16_t>), dim3(a.B * a.Hkv), dim3(256), 0, st, a.B,
+        hipLaunchKernelGGL((k_attn_combine<uint16_t>), dim3(rows), dim3(128), 0, st, a.B,
                            a.k, a.Hq, a.Hkv, a.D, S, po, pml, static_cast<uint16_t*>(a.out), a.lse);
     }
   } else {
