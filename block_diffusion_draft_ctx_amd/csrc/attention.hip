@@ -95,12 +95,16 @@ void k_attn_bf16(AttnP p) {
   constexpr int CPR = D / 8;             // 16-byte chunks per key row
   constexpr int NCH = kKT * CPR;         // chunks per tile (each of K and V)
   constexpr int CPT = (NCH + NT - 1) / NT;
-  constexpr int KS = D + 8;              // LDS row stride of the K and V tiles (elements)
+  // LDS row strides (elements): K rows are read 16 B per lane down a column
+  // (a stride of 4 banks mod 64 keeps 16 lanes conflict-free); V rows are
+  // read by the transposing read, four rows x 32 B per half-wave, which is
+  // conflict-free with a stride of 16 banks mod 64.
+  constexpr int KS = D + 8;
+  constexpr int VS = D + 32;
   constexpr int NMB = D / 32;            // 32-row blocks of O^T
   static_assert(kKT == 64, "the 2x2 wave layout assumes 64-key tiles");
-  __shared__ __align__(16) uint16_t smem[2 * kKT * KS];
-  uint16_t* Ks = smem;
-  uint16_t* Vs = smem + kKT * KS;
+  constexpr int STAGE = kKT * KS + kKT * VS;   // one K tile + one V tile
+  __shared__ __align__(16) uint16_t smem[2 * STAGE];   // two stages
   __shared__ int pages[kMaxSplitPages];
 
   const int split = blockIdx.x % p.S;
@@ -154,35 +158,61 @@ void k_attn_bf16(AttnP p) {
     poison |= __syncthreads_or(bad) != 0;
   }
 
+  // Per-thread chunk geometry is fixed for the whole loop: chunk c of every
+  // tile is key kc[c] of the tile, 16-byte column dcc[c].
+  int kc[CPT];
+  int64_t coff[CPT];   // offset of (slot kc%16, head g, column) inside a page
+  int64_t boff[CPT];   // offset of (head g, column) inside a block row
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int e = min((int)threadIdx.x + c * NT, NCH - 1);
+    kc[c] = e / CPR;
+    const int dc = e - kc[c] * CPR;
+    coff[c] = ((int64_t)(kc[c] & 15) * p.Hkv + g) * D + dc * 8;
+    boff[c] = (int64_t)g * D + dc * 8;
+  }
+  const int64_t page_elems = (int64_t)16 * p.Hkv * D;
+  const uint16_t* kblk = p.kb + (int64_t)b * k * p.Hkv * D;
+  const uint16_t* vblk = p.vb + (int64_t)b * k * p.Hkv * D;
+
   // Branch-free tile fetch: every chunk issues the same two 16-byte loads
   // (context slot, block key, or -- past the last key -- a clamped block key
   // whose score is masked), so no load waits on another.
   u32x4 kr[CPT], vr[CPT];
   auto fetch = [&](int tile) __attribute__((always_inline)) {
     const int pbase = (tile - t0) * (kKT / 16);
+    if (tile * kKT + kKT <= C) {     // the whole tile is context (uniform)
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int e = min((int)threadIdx.x + c * NT, NCH - 1);
-      const int key = e / CPR;
-      const int dc = e - key * CPR;
-      const int kp = tile * kKT + key;
-      const int page = pages[pbase + (key >> 4)];
-      const int64_t off_c = (((int64_t)page * 16 + (kp & 15)) * p.Hkv + g) * D + dc * 8;
-      const int jb = min(max(kp - C, 0), k - 1);
-      const int64_t off_b = (((int64_t)b * k + jb) * p.Hkv + g) * D + dc * 8;
-      const bool in_ctx = kp < C;
-      const uint16_t* pk = in_ctx ? p.ck + off_c : p.kb + off_b;
-      const uint16_t* pv = in_ctx ? p.cv + off_c : p.vb + off_b;
+      for (int c = 0; c < CPT; ++c) {
+        const int64_t off = (int64_t)pages[pbase + (kc[c] >> 4)] * page_elems + coff[c];
 #if DFLASH_ATTN_NT
-      kr[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pk));
-      vr[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pv));
+        kr[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.ck + off));
+        vr[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.cv + off));
 #else
-      kr[c] = *reinterpret_cast<const u32x4*>(pk);
-      vr[c] = *reinterpret_cast<const u32x4*>(pv);
+        kr[c] = *reinterpret_cast<const u32x4*>(p.ck + off);
+        vr[c] = *reinterpret_cast<const u32x4*>(p.cv + off);
 #endif
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int kp = tile * kKT + kc[c];
+        const int64_t off_c = (int64_t)pages[pbase + (kc[c] >> 4)] * page_elems + coff[c];
+        const int64_t off_b = (int64_t)min(max(kp - C, 0), k - 1) * p.Hkv * D + boff[c];
+        const bool in_ctx = kp < C;
+        const uint16_t* pk = in_ctx ? p.ck + off_c : kblk + off_b;
+        const uint16_t* pv = in_ctx ? p.cv + off_c : vblk + off_b;
+        kr[c] = *reinterpret_cast<const u32x4*>(pk);
+        vr[c] = *reinterpret_cast<const u32x4*>(pv);
+      }
     }
   };
 
+  // Online softmax in the exp2 domain with a lazily moved reference: m only
+  // moves when a score exceeds it by more than 2^kLazy, so the accumulator
+  // rescale is skipped on almost every tile (terms stay below 2^kLazy, safe
+  // in fp32 and bf16); the result is exactly normalised by l at the end.
+  constexpr float kLazy = 8.f;
   float m = neg_inf(), l = 0.f;
   f32x16 acc[NMB];
 #pragma unroll
@@ -194,22 +224,32 @@ void k_attn_bf16(AttnP p) {
   const int tr_r = (lane & 15) >> 2, tr_q = lane & 3;
   const int grp16 = lane >> 4;             // 16-lane group: d offset 16*(grp16&1), key half hh
 
-  if (t0 < t1) fetch(t0);
-  for (int tile = t0; tile < t1; ++tile) {
-    __syncthreads();  // the previous tile's LDS reads are done
+  auto stage = [&](uint16_t* Kd) __attribute__((always_inline)) {
+    uint16_t* Vd = Kd + kKT * KS;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int e = threadIdx.x + c * NT;
       if (NCH % NT == 0 || e < NCH) {
-        const int key = e / CPR;
-        const int dc = e - key * CPR;
-        *reinterpret_cast<u32x4*>(Ks + key * KS + dc * 8) = kr[c];
-        *reinterpret_cast<u32x4*>(Vs + key * KS + dc * 8) = vr[c];
+        const int dc = e - kc[c] * CPR;
+        *reinterpret_cast<u32x4*>(Kd + kc[c] * KS + dc * 8) = kr[c];
+        *reinterpret_cast<u32x4*>(Vd + kc[c] * VS + dc * 8) = vr[c];
       }
     }
-    __syncthreads();
-    if (tile + 1 < t1) fetch(tile + 1);
+  };
 
+  // Pipeline, one barrier per tile: compute tile t from one LDS stage while
+  // tile t+1 (fetched one step earlier) waits in registers; then stage it
+  // into the other LDS stage and fetch tile t+2.
+  if (t0 < t1) {
+    fetch(t0);
+    stage(smem);
+    if (t0 + 1 < t1) fetch(t0 + 1);
+  }
+  __syncthreads();
+  for (int tile = t0; tile < t1; ++tile) {
+    const int cur = (tile - t0) & 1;
+    const uint16_t* Ks = smem + cur * STAGE;
+    const uint16_t* Vs = Ks + kKT * KS;
     // S^T[32 keys x 32 q] for this wave's key half
     f32x16 sacc;
 #pragma unroll
@@ -223,28 +263,38 @@ void k_attn_bf16(AttnP p) {
     // sacc[j]: key 32wk + 8*(j/4) + 4*hh + j%4 of the tile, query l32
     float sv[16];
     float tmax = neg_inf();
+    if (tile * kKT + kKT <= total) {   // no masked key in this tile (uniform)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int kk = tile * kKT + 32 * wk + 8 * (j >> 2) + 4 * hh + (j & 3);
-      const float v = (kk < total) ? sacc[j] * p.sl2 : neg_inf();
-      sv[j] = v;
-      tmax = fmaxf(tmax, v);
+      for (int j = 0; j < 16; ++j) {
+        sv[j] = sacc[j] * p.sl2;
+        tmax = fmaxf(tmax, sv[j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int kk = tile * kKT + 32 * wk + 8 * (j >> 2) + 4 * hh + (j & 3);
+        sv[j] = (kk < total) ? sacc[j] * p.sl2 : neg_inf();
+        tmax = fmaxf(tmax, sv[j]);
+      }
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float mn = fmaxf(m, tmax);
-    const float mref = (mn == neg_inf()) ? 0.f : mn;   // a key half with no key yet
-    const float alpha = exp2f(m - mref);
+    if (__any(tmax > m + kLazy)) {     // move the reference (rare after the first tile)
+      const float mn = (tmax > m + kLazy) ? tmax : m;
+      const float alpha = (mn == neg_inf()) ? 1.f : __builtin_amdgcn_exp2f(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) acc[mb] *= alpha;
+      m = mn;
+    }
+    const float mref = (m == neg_inf()) ? 0.f : m;   // a key half with no key yet
     float rs = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      sv[j] = exp2f(sv[j] - mref);
+      sv[j] = __builtin_amdgcn_exp2f(sv[j] - mref);
       rs += sv[j];
     }
     rs += __shfl_xor(rs, 32, 64);
-    l = l * alpha + rs;
-    m = mn;
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) acc[mb] *= alpha;
+    l += rs;
     // O^T[d x 32 q] += V^T . P^T over this wave's 32 keys, 16 per MFMA.  In
     // both operands contraction index 8*hh + e is key 16*kk2 + 8*(e/4) +
     // 4*hh + e%4 (the order the S^T accumulators already hold).
@@ -253,16 +303,21 @@ void k_attn_bf16(AttnP p) {
       const float* ps = sv + 8 * kk2;
       const bf16x8 pb = as_bf16x8(make_uint4(pack_bf16x2(ps[0], ps[1]), pack_bf16x2(ps[2], ps[3]),
                                              pack_bf16x2(ps[4], ps[5]), pack_bf16x2(ps[6], ps[7])));
-      const uint16_t* v0 = Vs + (32 * wk + 16 * kk2 + 4 * (grp16 >> 1) + tr_r) * KS +
+      const uint16_t* v0 = Vs + (32 * wk + 16 * kk2 + 4 * (grp16 >> 1) + tr_r) * VS +
                            16 * (grp16 & 1) + 4 * tr_q;
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) {
         const uint2 lo = lds_read_tr16(v0 + 32 * mb);
-        const uint2 hi = lds_read_tr16(v0 + 8 * KS + 32 * mb);
+        const uint2 hi = lds_read_tr16(v0 + 8 * VS + 32 * mb);
         const bf16x8 a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
         acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[mb], 0, 0, 0);
       }
     }
+    if (tile + 1 < t1) {
+      stage(smem + (cur ^ 1) * STAGE);
+      if (tile + 2 < t1) fetch(tile + 2);
+    }
+    __syncthreads();
   }
 
   // Merge the two key halves: wave (wq, 1) hands its state to wave (wq, 0)
@@ -270,7 +325,7 @@ void k_attn_bf16(AttnP p) {
   float* xo = reinterpret_cast<float*>(smem);          // [64 lanes][D/2] partial O
   float* xm = xo + 64 * (D / 2);                        // [32] m, [32] l
   for (int sl = 0; sl < NQ; ++sl) {
-    __syncthreads();
+    if (sl) __syncthreads();
     if (wq == sl && wk == 1) {
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
