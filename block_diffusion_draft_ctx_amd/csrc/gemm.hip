@@ -32,7 +32,16 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kML = 16;  // layers a single launch can address
-constexpr int BM = 128, BN = 128, BK = 64, LS = BK + 8;
+constexpr int BK = 64;   // granularity of split-K chunks (a multiple of the pipeline step)
+
+// Tuning knobs: the block-tile height used below 256 x 256 (128 or 256, with
+// 128 columns), and the workgroup count split-K aims for.
+#ifndef DFLASH_GEMM_SMALL_BM
+#define DFLASH_GEMM_SMALL_BM 128
+#endif
+#ifndef DFLASH_GEMM_WGS
+#define DFLASH_GEMM_WGS 512
+#endif
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -110,22 +119,54 @@ __device__ __forceinline__ void emit(const GemmP& p, int row, int col, float v, 
   }
 }
 
-template <int EPI>
+// bf16 MFMA GEMM, C[M x N] = A[M x K] . B[N x K]^T, one BM x BN tile per
+// workgroup of four wavefronts (2 x 2, each BM/2 x BN/2 built from MFMA
+// 32x32x16 blocks).  Operands stream into LDS with direct global->LDS loads
+// (no staging registers, no LDS store instructions) through NSTG stages of
+// 32 contraction columns: step k is computed while steps k+1..k+NSTG-1 are in
+// flight.  Each 64-byte LDS row holds its four 16-byte chunks in XOR-swizzled
+// order (chunk c of row r at slot c ^ ((r/4) mod 4)), which keeps the MFMA
+// operand reads free of bank conflicts.
+constexpr int KB = 32;          // contraction columns per pipeline step
+constexpr int NSTG = 4;         // pipeline stages
+constexpr int ROWB = KB * 2;    // bytes per operand row per stage
+
+#define GPTR(p) ((const void __attribute__((address_space(1)))*)(p))
+#define LPTR(p) ((void __attribute__((address_space(3)))*)(p))
+
+template <int BM_, int BN_>
+constexpr size_t gemm_lds_bytes() {
+  return std::max<size_t>((size_t)NSTG * (BM_ + BN_) * ROWB, (size_t)BM_ * (BN_ + 8) * 2);
+}
+
+template <int BM_, int BN_, int EPI>
 __global__ __launch_bounds__(256) void k_gemm_bf16(GemmP p) {
-  __shared__ __align__(16) uint16_t As[BM * LS];
-  __shared__ __align__(16) uint16_t Bs[BN * LS];
+  constexpr int MI = BM_ / 64, NJ = BN_ / 64;     // 32x32 blocks per wave (rows, cols)
+  constexpr int STG = (BM_ + BN_) * ROWB;         // bytes per stage
+  constexpr int AI = BM_ / 16 / 4, BI = BN_ / 16 / 4;   // DMA instructions per wave per step
+  constexpr int DMA_PER_STEP = AI + BI;
+  extern __shared__ __align__(16) uint16_t lds[];
+  uint8_t* lb = reinterpret_cast<uint8_t*>(lds);
   const int tid = threadIdx.x;
-  const int n_nt = p.N / BN;
+  const int n_nt = p.N / BN_;
   const int tiles = (int)gridDim.x;
   int id = blockIdx.x;
   // Consecutive workgroups land on different XCDs; renumber so that each XCD
-  // owns a contiguous run of tiles (neighbouring tiles share A rows in L2).
+  // owns a contiguous run of tiles, then walk the tiles in groups of GM
+  // row-tiles so that the B columns of a group stay in that XCD's L2.
   if ((tiles & 7) == 0) id = (id & 7) * (tiles >> 3) + (id >> 3);
-  const int mt = id / n_nt, nt = id - mt * n_nt;
-  const int m0 = mt * BM, n0 = nt * BN;
+  constexpr int GM = 8;
+  const int n_mt = (p.M + BM_ - 1) / BM_;
+  const int group = id / (GM * n_nt);
+  const int first_m = group * GM;
+  const int gsz = min(GM, n_mt - first_m);
+  const int mt = first_m + (id % (GM * n_nt)) % gsz;
+  const int nt = (id % (GM * n_nt)) / gsz;
+  const int m0 = mt * BM_, n0 = nt * BN_;
   const int split = blockIdx.y;
   const int kbeg = split * p.kchunk;
   const int kend = min(p.K, kbeg + p.kchunk);
+  const int nk = (kend - kbeg) / KB;
 
   const uint16_t* bbase;
   int64_t ldb;
@@ -140,85 +181,155 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmP p) {
     ldb = p.ldb;
   }
 
-  u32x4 ar[4], br[4];
-  auto gload = [&](int k0) __attribute__((always_inline)) {
-    const int src = k0 / p.a_seg;
-    const int kc = k0 - src * p.a_seg;
-    const uint16_t* asrc = static_cast<const uint16_t*>(pick(p.a, src));
+  const int lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+  // DMA geometry: one instruction fills 16 rows x 64 B; lane L writes slot
+  // L%4 of row L/4, which holds logical chunk (L%4) ^ ((row/4) mod 4).
+  const int drow = lane >> 2;
+  int64_t aoff[AI], boff[BI];
+  int achk[AI], bchk[BI];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int e = tid + 256 * c;
-      const int row = e >> 3;
-      const int cc = (e & 7) * 8;
-      const int gr = m0 + row;
-      ar[c] = gr < p.M ? *reinterpret_cast<const u32x4*>(asrc + (int64_t)gr * p.a_seg + kc + cc)
-                       : u32x4{0u, 0u, 0u, 0u};
-      br[c] = *reinterpret_cast<const u32x4*>(bbase + (int64_t)row * ldb + k0 + cc);
-    }
+  for (int i = 0; i < AI; ++i) {
+    const int row = (w * AI + i) * 16 + drow;
+    achk[i] = 8 * ((lane & 3) ^ ((row >> 2) & 3));
+    aoff[i] = (int64_t)min(m0 + row, p.M - 1) * p.a_seg;   // rows past M load a valid row
+  }
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    const int row = (w * BI + i) * 16 + drow;
+    bchk[i] = 8 * ((lane & 3) ^ ((row >> 2) & 3));
+    boff[i] = (int64_t)row * ldb;
+  }
+  auto issue = [&](int st, int k0) __attribute__((always_inline)) {
+    uint8_t* base = lb + st * STG;
+    const int src = k0 / p.a_seg;
+    const uint16_t* asrc = static_cast<const uint16_t*>(pick(p.a, src)) + (k0 - src * p.a_seg);
+#pragma unroll
+    for (int i = 0; i < AI; ++i)
+      __builtin_amdgcn_global_load_lds(GPTR(asrc + aoff[i] + achk[i]),
+                                       LPTR(base + (w * AI + i) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < BI; ++i)
+      __builtin_amdgcn_global_load_lds(GPTR(bbase + boff[i] + k0 + bchk[i]),
+                                       LPTR(base + BM_ * ROWB + (w * BI + i) * 1024), 16, 0, 0);
   };
 
-  const int lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int r32 = lane & 31, hh = lane >> 5;
-  f32x16 acc[2][2];
+  f32x16 acc[MI][NJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-  if (kbeg < kend) gload(kbeg);
-  for (int k0 = kbeg; k0 < kend; k0 += BK) {
-    __syncthreads();
+  // operand read offsets within a stage (row, swizzled chunk), per sub-step
+  int aro[MI][2], bro[NJ][2];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int e = tid + 256 * c;
-      const int row = e >> 3;
-      const int cc = (e & 7) * 8;
-      *reinterpret_cast<u32x4*>(As + row * LS + cc) = ar[c];
-      *reinterpret_cast<u32x4*>(Bs + row * LS + cc) = br[c];
-    }
-    __syncthreads();
-    if (k0 + BK < kend) gload(k0 + BK);
+  for (int i = 0; i < MI; ++i) {
+    const int row = BM_ / 2 * wm + 32 * i + r32;
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      bf16x8 a[2], b[2];
+    for (int ss = 0; ss < 2; ++ss) aro[i][ss] = row * ROWB + 16 * ((2 * ss + hh) ^ ((row >> 2) & 3));
+  }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                              As + (64 * wm + 32 * i + r32) * LS + 16 * s + 8 * hh));
+  for (int j = 0; j < NJ; ++j) {
+    const int row = BN_ / 2 * wn + 32 * j + r32;
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                              Bs + (64 * wn + 32 * j + r32) * LS + 16 * s + 8 * hh));
+    for (int ss = 0; ss < 2; ++ss)
+      bro[j][ss] = BM_ * ROWB + row * ROWB + 16 * ((2 * ss + hh) ^ ((row >> 2) & 3));
+  }
+
+  for (int s = 0; s < NSTG - 1 && s < nk; ++s) issue(s, kbeg + s * KB);
+  for (int kt = 0; kt < nk; ++kt) {
+    // wait for this step's DMA (later steps may stay in flight), then make
+    // every wave's part visible
+    const int ahead = min(NSTG - 2, nk - 1 - kt);
+    if (ahead >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DMA_PER_STEP) : "memory");
+    else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_PER_STEP) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + NSTG - 1 < nk) issue((kt + NSTG - 1) % NSTG, kbeg + (kt + NSTG - 1) * KB);
+    const uint8_t* sb = lb + (kt % NSTG) * STG;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+    for (int ss = 0; ss < 2; ++ss) {
+      bf16x8 a[MI], b[NJ];
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+      for (int i = 0; i < MI; ++i)
+        a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sb + aro[i][ss]));
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        b[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sb + bro[j][ss]));
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
   }
+  __syncthreads();   // every wave is done with the stages before they are reused
 
   // C layout of the 32x32 MFMA: lane holds column (lane % 32); accumulator q
   // holds row 8*(q/4) + 4*(lane/32) + q%4.
+  if (EPI == EPI_PARTIAL) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int row = m0 + 64 * wm + 32 * i + 8 * (q >> 2) + 4 * hh + (q & 3);
-      if (row >= p.M) continue;
-      int64_t slot = -1;
-      if (EPI == EPI_PAGED) slot = row_slot(p, row, (n0 + 64 * wn) / (2 * p.HD));
+      for (int q = 0; q < 16; ++q) {
+        const int row = m0 + BM_ / 2 * wm + 32 * i + 8 * (q >> 2) + 4 * hh + (q & 3);
+        if (row >= p.M) continue;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = n0 + 64 * wn + 32 * j + r32;
-        const float v = acc[i][j][q];
-        if (EPI == EPI_PARTIAL)
-          p.part[((int64_t)split * p.M + row) * p.N + col] = v;
-        else
-          emit<uint16_t, EPI>(p, row, col, v, slot);
+        for (int j = 0; j < NJ; ++j)
+          p.part[((int64_t)split * p.M + row) * p.N + n0 + BN_ / 2 * wn + 32 * j + r32] = acc[i][j][q];
       }
+    return;
+  }
+  // Final epilogue: bias, bf16 rounding, then the tile goes through LDS so
+  // that every output row leaves as contiguous 16-byte stores (a row of a
+  // column tile is contiguous in h_ctx and in one layer's K or V cache slot).
+  constexpr int OS = BN_ + 8;   // LDS row stride of the output tile
+  uint16_t* ot = lds;           // [BM][OS] bf16 (reuses the operand stages)
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int cl = BN_ / 2 * wn + 32 * j + r32;
+    const float bias = (EPI == EPI_DENSE && p.bias)
+                           ? bf16_to_f32(static_cast<const uint16_t*>(p.bias)[n0 + cl]) : 0.f;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int rl = BM_ / 2 * wm + 32 * i + 8 * (q >> 2) + 4 * hh + (q & 3);
+        ot[rl * OS + cl] = f32_to_bf16(acc[i][j][q] + bias);
+      }
+  }
+  __syncthreads();
+  uint16_t* dst_base;
+  int64_t row_stride;
+  int hd0 = 0, layer = 0;
+  if (EPI == EPI_DENSE) {
+    dst_base = static_cast<uint16_t*>(p.out) + n0;
+    row_stride = p.N;
+  } else {
+    layer = n0 / (2 * p.HD);
+    const int kv = (n0 / p.HD) & 1;
+    hd0 = n0 - (n0 / p.HD) * p.HD;
+    dst_base = static_cast<uint16_t*>(kv ? pick(p.cv, layer) : pick(p.ck, layer)) + hd0;
+    row_stride = p.HD;
+  }
+  constexpr int CPRW = BN_ / 8;            // 16-byte chunks per output row
+  for (int e = tid; e < BM_ * CPRW; e += 256) {
+    const int rl = e / CPRW, c = e - rl * CPRW;
+    const int row = m0 + rl;
+    if (row >= p.M) continue;
+    int64_t dst;
+    if (EPI == EPI_DENSE) {
+      dst = (int64_t)row * row_stride;
+    } else {
+      const int64_t slot = row_slot(p, row, layer);
+      if (slot < 0) continue;
+      dst = slot * row_stride;
     }
+    *reinterpret_cast<u32x4*>(dst_base + dst + 8 * c) =
+        *reinterpret_cast<const u32x4*>(ot + rl * OS + 8 * c);
   }
 }
 
@@ -312,17 +423,41 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmP p) {
 }
 
 struct Plan {
+  int bm, bn;          // block tile (bf16)
   int ksplit, kchunk;
 };
 
 Plan plan_gemm(int64_t M, int64_t N, int64_t K, bool bf16) {
-  const int bk = bf16 ? BK : 16;
-  const int64_t tiles = bf16 ? cdiv(M, BM) * (N / BN) : cdiv(M, 64) * cdiv(N, 64);
+  if (!bf16) {
+    const int64_t tiles = cdiv(M, 64) * cdiv(N, 64);
+    int64_t ks = 1;
+    if (tiles < 512) ks = std::min<int64_t>(cdiv(1024, tiles), std::max<int64_t>(1, K / 64));
+    int64_t kchunk = cdiv(cdiv(K, ks), 16) * 16;
+    return Plan{64, 64, (int)cdiv(K, kchunk), (int)kchunk};
+  }
+  // 256 x 256 tiles when they alone give every CU a workgroup; else the
+  // smaller tile, and split the contraction until about DFLASH_GEMM_WGS
+  // workgroups exist.
+  int bm = 256, bn = 256;
+  if (N % 256 != 0 || cdiv(M, 256) * (N / 256) < 256) {
+    bm = DFLASH_GEMM_SMALL_BM;
+    bn = 128;
+  }
+  const int64_t tiles = cdiv(M, bm) * (N / bn);
   int64_t ks = 1;
-  if (tiles < 512) ks = std::min<int64_t>(cdiv(1024, tiles), std::max<int64_t>(1, K / (4 * bk)));
-  int64_t kchunk = cdiv(cdiv(K, ks), bk) * bk;
+  if (tiles < DFLASH_GEMM_WGS)
+    ks = std::min<int64_t>(cdiv(DFLASH_GEMM_WGS, tiles), std::max<int64_t>(1, K / (4 * BK)));
+  const int64_t kchunk = cdiv(cdiv(K, ks), BK) * BK;
   ks = cdiv(K, kchunk);
-  return Plan{(int)ks, (int)kchunk};
+  return Plan{bm, bn, (int)ks, (int)kchunk};
+}
+
+template <int BM_, int BN_>
+void launch_bf16_gemm(GemmP p, int epi, dim3 grid, hipStream_t st) {
+  const size_t lds = gemm_lds_bytes<BM_, BN_>();
+  if (epi == EPI_DENSE) hipLaunchKernelGGL((k_gemm_bf16<BM_, BN_, EPI_DENSE>), grid, dim3(256), lds, st, p);
+  else if (epi == EPI_PAGED) hipLaunchKernelGGL((k_gemm_bf16<BM_, BN_, EPI_PAGED>), grid, dim3(256), lds, st, p);
+  else hipLaunchKernelGGL((k_gemm_bf16<BM_, BN_, EPI_PARTIAL>), grid, dim3(256), lds, st, p);
 }
 
 void run_gemm(bool bf16, GemmP p, int epi_final, hipStream_t st) {
@@ -330,14 +465,13 @@ void run_gemm(bool bf16, GemmP p, int epi_final, hipStream_t st) {
   p.ksplit = pl.ksplit;
   p.kchunk = pl.kchunk;
   const int epi = pl.ksplit > 1 ? EPI_PARTIAL : epi_final;
-  dim3 grid;
-  if (bf16) grid = dim3((unsigned)(cdiv(p.M, BM) * (p.N / BN)), (unsigned)pl.ksplit);
-  else grid = dim3((unsigned)(cdiv(p.M, 64) * cdiv(p.N, 64)), (unsigned)pl.ksplit);
   if (bf16) {
-    if (epi == EPI_DENSE) hipLaunchKernelGGL(k_gemm_bf16<EPI_DENSE>, grid, dim3(256), 0, st, p);
-    else if (epi == EPI_PAGED) hipLaunchKernelGGL(k_gemm_bf16<EPI_PAGED>, grid, dim3(256), 0, st, p);
-    else hipLaunchKernelGGL(k_gemm_bf16<EPI_PARTIAL>, grid, dim3(256), 0, st, p);
+    const dim3 grid((unsigned)(cdiv(p.M, pl.bm) * (p.N / pl.bn)), (unsigned)pl.ksplit);
+    if (pl.bm == 256 && pl.bn == 256) launch_bf16_gemm<256, 256>(p, epi, grid, st);
+    else if (pl.bm == 256) launch_bf16_gemm<256, 128>(p, epi, grid, st);
+    else launch_bf16_gemm<128, 128>(p, epi, grid, st);
   } else {
+    const dim3 grid((unsigned)(cdiv(p.M, 64) * cdiv(p.N, 64)), (unsigned)pl.ksplit);
     if (epi == EPI_DENSE) hipLaunchKernelGGL(k_gemm_f32<EPI_DENSE>, grid, dim3(256), 0, st, p);
     else if (epi == EPI_PAGED) hipLaunchKernelGGL(k_gemm_f32<EPI_PAGED>, grid, dim3(256), 0, st, p);
     else hipLaunchKernelGGL(k_gemm_f32<EPI_PARTIAL>, grid, dim3(256), 0, st, p);
