@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--vocab", type=int, default=128256)
     ap.add_argument("--layers", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=3, help="requests in the oracle sample")
+    ap.add_argument("--cpu-sample", type=int, default=32, help="requests in the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--breakdown", action="store_true", help="per-part timings to stderr")

@@ -6,20 +6,26 @@
 // request go into its paged draft KV cache.
 //
 // Design.  Both products are "NT" GEMMs (every operand row is contiguous
-// along the contraction), run on the gfx950 MFMA 32x32x16 bf16 instruction
-// with 128x128x64 workgroup tiles (four wavefronts, 64x64 each).
+// along the contraction), run on the gfx950 MFMA 32x32x16 bf16 instruction.
+//  * Tiles: 256 x 256 with eight wavefronts (2 x 4, two per SIMD, each
+//    128 x 64) when there are enough of them to fill the chip, else
+//    128 x 128 with four; operands stream straight from global memory into
+//    LDS (no staging registers) through a software pipeline of 64-column
+//    steps, 2 or 3 stages deep.
 //  * GEMM 1 reads A as a virtual concatenation: the contraction index picks
 //    one of the m hidden-state buffers, so the [T, m*d] matrix never exists.
 //  * GEMM 2 fuses all layers' K and V projections horizontally: output column
 //    n belongs to layer n / (2*Hkv*D), to K or V by (n / (Hkv*D)) mod 2, and
-//    a 128-wide column tile never straddles two weight matrices.
+//    a column tile never straddles two weight matrices.
 //  * The GEMM 2 epilogue turns each output row into its physical cache slot
 //    (request, logical position, block table) and drops rows past the
 //    request's committed length, so K/V go straight from accumulators to the
-//    paged cache.
+//    paged cache, as whole 16-byte row pieces staged through LDS.
 //  * When rows are few (decode), the contraction is split across workgroups
 //    (fp32 partials in the workspace, then a reduction kernel that applies
 //    the same epilogue) so that enough workgroups stream the weights.
+//  * Tile order is XCD-aware: each XCD owns a contiguous run of tiles,
+//    walked in groups of 8 row tiles so their B columns stay in its L2.
 #include <algorithm>
 
 #include "common.h"
@@ -41,6 +47,41 @@ constexpr int BK = 64;   // granularity of split-K chunks (a multiple of the pip
 #endif
 #ifndef DFLASH_GEMM_WGS
 #define DFLASH_GEMM_WGS 512
+#endif
+// Pipeline shape (contraction columns per step, stages) for the 256 x 256
+// tile and for the smaller tiles.
+#ifndef DFLASH_GEMM_KB_BIG
+#define DFLASH_GEMM_KB_BIG 64
+#endif
+#ifndef DFLASH_GEMM_NSTG_BIG
+#define DFLASH_GEMM_NSTG_BIG 2
+#endif
+#ifndef DFLASH_GEMM_KB_SMALL
+#define DFLASH_GEMM_KB_SMALL 64
+#endif
+#ifndef DFLASH_GEMM_NSTG_SMALL
+#define DFLASH_GEMM_NSTG_SMALL 3
+#endif
+// Wavefront columns of the 256 x 256 and 128 x 128 tiles (two rows of
+// wavefronts): 2 gives four wavefronts (one per SIMD), 4 gives eight.
+#ifndef DFLASH_GEMM_BIG_WN
+#define DFLASH_GEMM_BIG_WN 4
+#endif
+#ifndef DFLASH_GEMM_SMALL_WN
+#define DFLASH_GEMM_SMALL_WN 2
+#endif
+// Fewest 256 x 256 tiles (before split-K) for which that tile is used.
+#ifndef DFLASH_GEMM_BIG_MIN_TILES
+#define DFLASH_GEMM_BIG_MIN_TILES 256
+#endif
+// Rotation of each tile's contraction start, in elements per workgroup
+// (0: every tile starts at the beginning of its range).
+#ifndef DFLASH_GEMM_ROT
+#define DFLASH_GEMM_ROT 0
+#endif
+// With two stages, the DMA of a step is issued during this many sub-steps.
+#ifndef DFLASH_GEMM_SPREAD2
+#define DFLASH_GEMM_SPREAD2 1
 #endif
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -120,31 +161,56 @@ __device__ __forceinline__ void emit(const GemmP& p, int row, int col, float v, 
 }
 
 // bf16 MFMA GEMM, C[M x N] = A[M x K] . B[N x K]^T, one BM x BN tile per
-// workgroup of four wavefronts (2 x 2, each BM/2 x BN/2 built from MFMA
+// workgroup of WM x WN wavefronts (each BM/WM x BN/WN, built from MFMA
 // 32x32x16 blocks).  Operands stream into LDS with direct global->LDS loads
 // (no staging registers, no LDS store instructions) through NSTG stages of
-// 32 contraction columns: step k is computed while steps k+1..k+NSTG-1 are in
-// flight.  Each 64-byte LDS row holds its four 16-byte chunks in XOR-swizzled
-// order (chunk c of row r at slot c ^ ((r/4) mod 4)), which keeps the MFMA
-// operand reads free of bank conflicts.
-constexpr int KB = 32;          // contraction columns per pipeline step
-constexpr int NSTG = 4;         // pipeline stages
-constexpr int ROWB = KB * 2;    // bytes per operand row per stage
-
-#define GPTR(p) ((const void __attribute__((address_space(1)))*)(p))
+// KB contraction columns: step k is computed while steps k+1..k+NSTG-1 are
+// in flight.  An operand row of a stage is KB*2 bytes made of 16-byte chunks
+// stored in XOR-swizzled order (chunk c of row r at slot c ^ swz(r), with
+// swz cycling once per 256 bytes of LDS), which keeps the MFMA operand reads
+// free of bank conflicts.
 #define LPTR(p) ((void __attribute__((address_space(3)))*)(p))
 
-template <int BM_, int BN_>
+template <int BM_, int BN_, int KB_, int NSTG_>
 constexpr size_t gemm_lds_bytes() {
-  return std::max<size_t>((size_t)NSTG * (BM_ + BN_) * ROWB, (size_t)BM_ * (BN_ + 8) * 2);
+  return std::max<size_t>((size_t)NSTG_ * (BM_ + BN_) * KB_ * 2, (size_t)BM_ * (BN_ + 8) * 2);
 }
 
-template <int BM_, int BN_, int EPI>
-__global__ __launch_bounds__(256) void k_gemm_bf16(GemmP p) {
-  constexpr int MI = BM_ / 64, NJ = BN_ / 64;     // 32x32 blocks per wave (rows, cols)
+// Wait for all LDS and scalar-memory operations, as an instruction the
+// compiler's wait-count tracking sees (inline assembly it does not): once no
+// scalar load is pending, it can wait for individual LDS reads by count.
+__device__ __forceinline__ void lgkm_drain() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// One direct global->LDS load of 16 bytes per lane: lane L's bytes land at
+// LDS address lds_addr + 16*L.  Written as inline assembly on purpose: the
+// compiler's wait-count tracking treats its own LDS-DMA instruction as an
+// LDS event of another kind and would then drain the LDS counter before
+// every MFMA.  The kernel waits for these loads itself (vmcnt + barrier).
+// M0 must settle for one cycle before the load reads it.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gptr), "s"(lds_addr) : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int BM_, int BN_, int WM_, int WN_, int KB_, int NSTG_, int EPI>
+__global__ __launch_bounds__(64 * WM_ * WN_) void k_gemm_bf16(GemmP p) {
+  constexpr int NW = WM_ * WN_, NT = 64 * NW;     // wavefronts (WM x WN grid), threads
+  constexpr int MI = BM_ / (32 * WM_), NJ = BN_ / (32 * WN_);   // 32x32 blocks per wave
+  constexpr int ROWB = KB_ * 2;                   // bytes per operand row per stage
+  constexpr int CH = KB_ / 8;                     // 16-byte chunks per row
+  constexpr int RP256 = 256 / ROWB;               // rows per 256 bytes of LDS
+  constexpr int RPI = 64 / CH;                    // rows one DMA instruction fills
   constexpr int STG = (BM_ + BN_) * ROWB;         // bytes per stage
-  constexpr int AI = BM_ / 16 / 4, BI = BN_ / 16 / 4;   // DMA instructions per wave per step
+  constexpr int AI = BM_ / RPI / NW, BI = BN_ / RPI / NW;   // DMA instructions per wave per step
+  static_assert(AI * RPI * NW == BM_ && BI * RPI * NW == BN_, "DMA rows per wave");
   constexpr int DMA_PER_STEP = AI + BI;
+  static_assert(NSTG_ >= 2 && NSTG_ <= 4 && (NSTG_ - 2) * DMA_PER_STEP <= 63, "vmcnt range");
+  static_assert(BK % KB_ == 0 && (KB_ == 32 || KB_ == 64), "pipeline step");
   extern __shared__ __align__(16) uint16_t lds[];
   uint8_t* lb = reinterpret_cast<uint8_t*>(lds);
   const int tid = threadIdx.x;
@@ -166,7 +232,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmP p) {
   const int split = blockIdx.y;
   const int kbeg = split * p.kchunk;
   const int kend = min(p.K, kbeg + p.kchunk);
-  const int nk = (kend - kbeg) / KB;
+  const int nk = (kend - kbeg) / KB_;
 
   const uint16_t* bbase;
   int64_t ldb;
@@ -181,36 +247,73 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmP p) {
     ldb = p.ldb;
   }
 
-  const int lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
-  // DMA geometry: one instruction fills 16 rows x 64 B; lane L writes slot
-  // L%4 of row L/4, which holds logical chunk (L%4) ^ ((row/4) mod 4).
-  const int drow = lane >> 2;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w / WN_, wn = w % WN_;
+  // DMA geometry: one instruction fills RPI rows; lane L writes slot L%CH of
+  // row L/CH, which holds logical chunk (L%CH) ^ swz(row).
+  auto swz = [](int row) __attribute__((always_inline)) { return (row / RP256) % CH; };
+  const int drow = lane / CH;
   int64_t aoff[AI], boff[BI];
   int achk[AI], bchk[BI];
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
-    const int row = (w * AI + i) * 16 + drow;
-    achk[i] = 8 * ((lane & 3) ^ ((row >> 2) & 3));
+    const int row = (w * AI + i) * RPI + drow;
+    achk[i] = 8 * ((lane % CH) ^ swz(row));
     aoff[i] = (int64_t)min(m0 + row, p.M - 1) * p.a_seg;   // rows past M load a valid row
   }
 #pragma unroll
   for (int i = 0; i < BI; ++i) {
-    const int row = (w * BI + i) * 16 + drow;
-    bchk[i] = 8 * ((lane & 3) ^ ((row >> 2) & 3));
+    const int row = (w * BI + i) * RPI + drow;
+    bchk[i] = 8 * ((lane % CH) ^ swz(row));
     boff[i] = (int64_t)row * ldb;
   }
-  auto issue = [&](int st, int k0) __attribute__((always_inline)) {
-    uint8_t* base = lb + st * STG;
-    const int src = k0 / p.a_seg;
-    const uint16_t* asrc = static_cast<const uint16_t*>(pick(p.a, src)) + (k0 - src * p.a_seg);
+  // Steps are issued strictly in order; the issue position advances by KB
+  // contraction columns and moves to the next A source at a segment end.
+  // The contraction range of a tile may start at a rotated offset and wrap
+  // around (summation order only), so that workgroups running side by side
+  // read different address ranges at the same time.
+  int rot = 0;
+  if (DFLASH_GEMM_ROT > 0) {
+    rot = (int)(((int64_t)(blockIdx.x >> 3) * DFLASH_GEMM_ROT) % (kend - kbeg));
+    rot -= rot % KB_;
+  }
+  int is_k, is_src, is_off;
+  const uint16_t* acur;
+  auto set_pos = [&](int k) __attribute__((always_inline)) {
+    is_k = k;
+    is_src = k / p.a_seg;
+    is_off = k - is_src * p.a_seg;
+    acur = static_cast<const uint16_t*>(pick(p.a, is_src)) + is_off;
+  };
+  set_pos(kbeg + rot);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)LPTR(lb);
+  // DMA instruction q (< AI + BI) of the step at the issue position into
+  // stage st; the last one moves the position to the next step.
+  auto dma_one = [&](int st, int q) __attribute__((always_inline)) {
+    const uint32_t base = lds0 + st * STG;
+    if (q < AI) {
+      dma16(acur + aoff[q] + achk[q], base + (w * AI + q) * 1024);
+    } else {
+      const int i = q - AI;
+      dma16(bbase + boff[i] + is_k + bchk[i], base + BM_ * ROWB + (w * BI + i) * 1024);
+    }
+    if (q == AI + BI - 1) {
+      is_k += KB_;
+      is_off += KB_;
+      acur += KB_;
+      if (DFLASH_GEMM_ROT > 0 && is_k == kend) {
+        set_pos(kbeg);
+        lgkm_drain();   // the pointer may come from a scalar load
+      } else if (is_off == p.a_seg) {
+        is_off = 0;
+        ++is_src;
+        acur = static_cast<const uint16_t*>(pick(p.a, is_src));
+        lgkm_drain();   // the pointer may come from a scalar load
+      }
+    }
+  };
+  auto issue = [&](int st) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < AI; ++i)
-      __builtin_amdgcn_global_load_lds(GPTR(asrc + aoff[i] + achk[i]),
-                                       LPTR(base + (w * AI + i) * 1024), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < BI; ++i)
-      __builtin_amdgcn_global_load_lds(GPTR(bbase + boff[i] + k0 + bchk[i]),
-                                       LPTR(base + BM_ * ROWB + (w * BI + i) * 1024), 16, 0, 0);
+    for (int q = 0; q < AI + BI; ++q) dma_one(st, q);
   };
 
   const int r32 = lane & 31, hh = lane >> 5;
@@ -223,49 +326,115 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmP p) {
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
   // operand read offsets within a stage (row, swizzled chunk), per sub-step
-  int aro[MI][2], bro[NJ][2];
+  constexpr int SS = KB_ / 16;
+  int aro[MI][SS], bro[NJ][SS];
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
-    const int row = BM_ / 2 * wm + 32 * i + r32;
+    const int row = BM_ / WM_ * wm + 32 * i + r32;
 #pragma unroll
-    for (int ss = 0; ss < 2; ++ss) aro[i][ss] = row * ROWB + 16 * ((2 * ss + hh) ^ ((row >> 2) & 3));
+    for (int ss = 0; ss < SS; ++ss) aro[i][ss] = row * ROWB + 16 * ((2 * ss + hh) ^ swz(row));
   }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int row = BN_ / 2 * wn + 32 * j + r32;
+    const int row = BN_ / WN_ * wn + 32 * j + r32;
 #pragma unroll
-    for (int ss = 0; ss < 2; ++ss)
-      bro[j][ss] = BM_ * ROWB + row * ROWB + 16 * ((2 * ss + hh) ^ ((row >> 2) & 3));
+    for (int ss = 0; ss < SS; ++ss)
+      bro[j][ss] = BM_ * ROWB + row * ROWB + 16 * ((2 * ss + hh) ^ swz(row));
   }
 
-  for (int s = 0; s < NSTG - 1 && s < nk; ++s) issue(s, kbeg + s * KB);
-  for (int kt = 0; kt < nk; ++kt) {
-    // wait for this step's DMA (later steps may stay in flight), then make
-    // every wave's part visible
-    const int ahead = min(NSTG - 2, nk - 1 - kt);
-    if (ahead >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DMA_PER_STEP) : "memory");
-    else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_PER_STEP) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // Software pipeline over steps of KB contraction columns, SS sub-steps of
+  // 16 each.
+  //  * Operand fragments of sub-step s+1 are read from LDS while the MFMAs of
+  //    sub-step s run.
+  //  * At the start of the last sub-step of step k every wave waits for its
+  //    DMA of step k+1, finishes its reads of stage k and meets the others
+  //    at a barrier; it then reads the first fragments of step k+1.
+  //  * The DMA of step k+NSTG-1 goes into the stage of step k-1 (free since
+  //    that barrier), one instruction every few MFMAs of the sub-steps before
+  //    the last, so the matrix pipe keeps running while the loads issue.
+  bf16x8 fa[2][MI], fb[2][NJ];
+  // fragment f of sub-step ss: A blocks first (f < MI), then B blocks
+  auto read_one = [&](int set, const uint8_t* sb, int ss, int f) __attribute__((always_inline)) {
+    if (f < MI)
+      fa[set][f] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sb + aro[f][ss]));
+    else
+      fb[set][f - MI] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sb + bro[f - MI][ss]));
+  };
+  // wait until at most `ahead` steps of DMA are outstanding (ahead < NSTG - 1)
+  auto wait_steps = [&](int ahead) __attribute__((always_inline)) {
+    if (NSTG_ >= 4 && ahead >= 2) wait_vmcnt<(NSTG_ >= 4 ? 2 * DMA_PER_STEP : 0)>();
+    else if (NSTG_ >= 3 && ahead == 1) wait_vmcnt<DMA_PER_STEP>();
+    else wait_vmcnt<0>();
+  };
+  constexpr int MF = MI * NJ;              // MFMAs per sub-step
+  constexpr int NF = MI + NJ;              // operand fragments per sub-step
+  // MFMA slots that carry DMA issue: all sub-steps before the last, or only
+  // the first ones (with two stages the loads need the rest of the step to
+  // land)
+  constexpr int SPREAD = NSTG_ == 2 ? (SS - 1 < DFLASH_GEMM_SPREAD2 ? SS - 1 : DFLASH_GEMM_SPREAD2) : SS - 1;
+  constexpr int SLOTS = SPREAD * MF;
+  static_assert(DMA_PER_STEP <= SLOTS, "DMA issue slots");
+
+  for (int s = 0; s < NSTG_ - 1 && s < nk; ++s) issue(s);
+  if (nk > 0) {
+    wait_steps(min(NSTG_ - 2, nk - 1));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (kt + NSTG - 1 < nk) issue((kt + NSTG - 1) % NSTG, kbeg + (kt + NSTG - 1) * KB);
-    const uint8_t* sb = lb + (kt % NSTG) * STG;
 #pragma unroll
-    for (int ss = 0; ss < 2; ++ss) {
-      bf16x8 a[MI], b[NJ];
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-        a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sb + aro[i][ss]));
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        b[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sb + bro[j][ss]));
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
+    for (int f = 0; f < NF; ++f) read_one(0, lb, 0, f);
   }
+  lgkm_drain();
+  // mode 0: issue the DMA of step kt+NSTG-1; 1: nothing left to issue;
+  // 2: the final step (no hand-over to a next step)
+  auto step = [&](int kt, int mode) __attribute__((always_inline)) {
+    const uint8_t* sb = lb + (kt % NSTG_) * STG;
+    const int dst = (kt + NSTG_ - 1) % NSTG_;
+#pragma unroll
+    for (int ss = 0; ss < SS; ++ss) {
+      const int c = ss & 1;
+      // fragments for the next sub-step: this stage, or the next stage once
+      // every wave has its DMA and is done with this stage
+      const uint8_t* rsb = sb;
+      int rss = ss + 1;
+      const bool rd = ss + 1 < SS || mode != 2;
+      if (ss + 1 == SS && mode != 2) {
+        wait_steps(min(NSTG_ - 2, nk - 2 - kt));
+        lgkm_drain();   // own reads of this stage are done
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        rsb = lb + ((kt + 1) % NSTG_) * STG;
+        rss = 0;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < MF; ++t) {
+        const int i = t / NJ, j = t % NJ;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][i], fb[c][j], acc[i][j], 0, 0, 0);
+        // fragment t rides on MFMA t; any beyond the last MFMA follow it
+        if (rd) {
+#pragma unroll
+          for (int f = 0; f < NF; ++f)
+            if (f == t || (t == MF - 1 && f > t)) read_one(c ^ 1, rsb, rss, f);
+        }
+        if (mode == 0 && ss < SPREAD) {
+          const int slot = ss * MF + t;
+#pragma unroll
+          for (int q = 0; q < DMA_PER_STEP; ++q)
+            if (q * SLOTS / DMA_PER_STEP == slot) {
+              __builtin_amdgcn_sched_barrier(0);
+              dma_one(dst, q);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  const int n_issue = max(0, nk - (NSTG_ - 1));   // steps that still issue a DMA
+  int kt = 0;
+  for (; kt < n_issue; ++kt) step(kt, 0);
+  for (; kt < nk - 1; ++kt) step(kt, 1);
+  if (nk > 0) step(nk - 1, 2);
+  wait_vmcnt<0>();
   __syncthreads();   // every wave is done with the stages before they are reused
 
   // C layout of the 32x32 MFMA: lane holds column (lane % 32); accumulator q
@@ -275,11 +444,11 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmP p) {
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int row = m0 + BM_ / 2 * wm + 32 * i + 8 * (q >> 2) + 4 * hh + (q & 3);
+        const int row = m0 + BM_ / WM_ * wm + 32 * i + 8 * (q >> 2) + 4 * hh + (q & 3);
         if (row >= p.M) continue;
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-          p.part[((int64_t)split * p.M + row) * p.N + n0 + BN_ / 2 * wn + 32 * j + r32] = acc[i][j][q];
+          p.part[((int64_t)split * p.M + row) * p.N + n0 + BN_ / WN_ * wn + 32 * j + r32] = acc[i][j][q];
       }
     return;
   }
@@ -290,14 +459,14 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmP p) {
   uint16_t* ot = lds;           // [BM][OS] bf16 (reuses the operand stages)
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int cl = BN_ / 2 * wn + 32 * j + r32;
+    const int cl = BN_ / WN_ * wn + 32 * j + r32;
     const float bias = (EPI == EPI_DENSE && p.bias)
                            ? bf16_to_f32(static_cast<const uint16_t*>(p.bias)[n0 + cl]) : 0.f;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int rl = BM_ / 2 * wm + 32 * i + 8 * (q >> 2) + 4 * hh + (q & 3);
+        const int rl = BM_ / WM_ * wm + 32 * i + 8 * (q >> 2) + 4 * hh + (q & 3);
         ot[rl * OS + cl] = f32_to_bf16(acc[i][j][q] + bias);
       }
   }
@@ -316,7 +485,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmP p) {
     row_stride = p.HD;
   }
   constexpr int CPRW = BN_ / 8;            // 16-byte chunks per output row
-  for (int e = tid; e < BM_ * CPRW; e += 256) {
+  for (int e = tid; e < BM_ * CPRW; e += NT) {
     const int rl = e / CPRW, c = e - rl * CPRW;
     const int row = m0 + rl;
     if (row >= p.M) continue;
@@ -439,7 +608,7 @@ Plan plan_gemm(int64_t M, int64_t N, int64_t K, bool bf16) {
   // smaller tile, and split the contraction until about DFLASH_GEMM_WGS
   // workgroups exist.
   int bm = 256, bn = 256;
-  if (N % 256 != 0 || cdiv(M, 256) * (N / 256) < 256) {
+  if (N % 256 != 0 || cdiv(M, 256) * (N / 256) < DFLASH_GEMM_BIG_MIN_TILES) {
     bm = DFLASH_GEMM_SMALL_BM;
     bn = 128;
   }
@@ -452,12 +621,13 @@ Plan plan_gemm(int64_t M, int64_t N, int64_t K, bool bf16) {
   return Plan{bm, bn, (int)ks, (int)kchunk};
 }
 
-template <int BM_, int BN_>
+template <int BM_, int BN_, int WM_, int WN_, int KB_, int NSTG_>
 void launch_bf16_gemm(GemmP p, int epi, dim3 grid, hipStream_t st) {
-  const size_t lds = gemm_lds_bytes<BM_, BN_>();
-  if (epi == EPI_DENSE) hipLaunchKernelGGL((k_gemm_bf16<BM_, BN_, EPI_DENSE>), grid, dim3(256), lds, st, p);
-  else if (epi == EPI_PAGED) hipLaunchKernelGGL((k_gemm_bf16<BM_, BN_, EPI_PAGED>), grid, dim3(256), lds, st, p);
-  else hipLaunchKernelGGL((k_gemm_bf16<BM_, BN_, EPI_PARTIAL>), grid, dim3(256), lds, st, p);
+  const size_t lds = gemm_lds_bytes<BM_, BN_, KB_, NSTG_>();
+  const dim3 block(64 * WM_ * WN_);
+  if (epi == EPI_DENSE) hipLaunchKernelGGL((k_gemm_bf16<BM_, BN_, WM_, WN_, KB_, NSTG_, EPI_DENSE>), grid, block, lds, st, p);
+  else if (epi == EPI_PAGED) hipLaunchKernelGGL((k_gemm_bf16<BM_, BN_, WM_, WN_, KB_, NSTG_, EPI_PAGED>), grid, block, lds, st, p);
+  else hipLaunchKernelGGL((k_gemm_bf16<BM_, BN_, WM_, WN_, KB_, NSTG_, EPI_PARTIAL>), grid, block, lds, st, p);
 }
 
 void run_gemm(bool bf16, GemmP p, int epi_final, hipStream_t st) {
@@ -467,9 +637,12 @@ void run_gemm(bool bf16, GemmP p, int epi_final, hipStream_t st) {
   const int epi = pl.ksplit > 1 ? EPI_PARTIAL : epi_final;
   if (bf16) {
     const dim3 grid((unsigned)(cdiv(p.M, pl.bm) * (p.N / pl.bn)), (unsigned)pl.ksplit);
-    if (pl.bm == 256 && pl.bn == 256) launch_bf16_gemm<256, 256>(p, epi, grid, st);
-    else if (pl.bm == 256) launch_bf16_gemm<256, 128>(p, epi, grid, st);
-    else launch_bf16_gemm<128, 128>(p, epi, grid, st);
+    if (pl.bm == 256 && pl.bn == 256)
+      launch_bf16_gemm<256, 256, 2, DFLASH_GEMM_BIG_WN, DFLASH_GEMM_KB_BIG, DFLASH_GEMM_NSTG_BIG>(p, epi, grid, st);
+    else if (pl.bm == 256)
+      launch_bf16_gemm<256, 128, 2, 2, DFLASH_GEMM_KB_SMALL, DFLASH_GEMM_NSTG_SMALL>(p, epi, grid, st);
+    else
+      launch_bf16_gemm<128, 128, 2, DFLASH_GEMM_SMALL_WN, DFLASH_GEMM_KB_SMALL, DFLASH_GEMM_NSTG_SMALL>(p, epi, grid, st);
   } else {
     const dim3 grid((unsigned)(cdiv(p.M, 64) * cdiv(p.N, 64)), (unsigned)pl.ksplit);
     if (epi == EPI_DENSE) hipLaunchKernelGGL(k_gemm_f32<EPI_DENSE>, grid, dim3(256), 0, st, p);
