@@ -18,6 +18,7 @@ timed on a bounded sample of the same step.
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -25,8 +26,39 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+# The attention kernel's measured HBM traffic (two rocprofv3 counter passes,
+# scaled by a copy kernel of known size) is recorded with a hash of the
+# sources it was measured on; it is reported only while they still match.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_b64_ctx8192_hbm_traffic.md")
+ATTN_SOURCES = [os.path.join(ROOT, "block_diffusion_draft_ctx_amd", "csrc", f)
+                for f in ("attention.hip", "common.h")]
 BF16_PEAK = 2.5e15         # dense bf16 MFMA flop/s
 METRIC = "draft-step blocks/sec (inject+block attn+verify); % HBM / MFMA peak"
+
+
+def source_hash(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """Bytes per attention launch from the committed counter summary, or None
+    when the summary is missing or the kernel sources changed since."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    vals = dict(re.findall(r"^\s*(\w+) = (\S+)\s*$", text, re.M))
+    if vals.get("attention_sources_sha256") != source_hash(ATTN_SOURCES):
+        return None
+    try:
+        return float(vals["attention_traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -44,6 +76,13 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--breakdown", action="store_true", help="per-part timings to stderr")
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "sample-gate", "prefill", "packed"],
+                    help="decode: the greedy decode step (default); sample-gate: Qwen3-4B-shaped "
+                         "stochastic chain verify with DLoop gates; prefill: 4 x 32768-row "
+                         "ctx-KV materialisation; packed: training-style packed block mask")
+    ap.add_argument("--sigma", type=float, default=1.0, help="sample-gate: draft = target + N(0, sigma)")
+    ap.add_argument("--stages", type=int, default=4, help="sample-gate: DLoop stages of 8")
     return ap.parse_args()
 
 
@@ -234,17 +273,213 @@ def cpu_baseline(st, n_req):
     return n_req / dt, dt, cores
 
 
+def _events_ms(fn, steps, warmup):
+    """Average milliseconds of fn() over `steps` calls after `warmup`, from HIP
+    events recorded on the stream the library launches on."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def _base_line(args, metric, value, unit, ms, workload, higher=True, **cfg):
+    return {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": higher,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": dict(workload=workload, **cfg)}
+
+
+def bench_sample_gate(args):
+    """Qwen3-4B-shaped stochastic verify with DLoop gating: batch 16, vocab
+    151936, S stages of 8 drafts chained into one verify of 8S candidates
+    (+ bonus).  One step = S gates (one per stage's draft rows) + one sampled
+    chain verify; every request verifies the whole chain (the longest case)."""
+    import torch
+    import block_diffusion_draft_ctx_amd as dfl
+    B, V, kk, S = 16, 151936, 8, args.stages
+    L = kk * S
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(3000 + S)
+    tl32 = torch.randn(B, L + 1, V, generator=g, device=dev) * 3.0
+    dl32 = tl32[:, :L] + torch.randn(B, L, V, generator=g, device=dev) * args.sigma
+    gumbel = -torch.log(-torch.log(torch.rand(B, L, V, generator=g, device=dev).clamp_min(1e-20)))
+    drafts = torch.argmax(dl32 + gumbel, dim=-1).to(torch.int32)
+    del gumbel
+    tl = tl32.to(torch.bfloat16)
+    dl = dl32.to(torch.bfloat16)
+    del tl32, dl32
+    # each stage's draft rows as the draft model emits them (one tensor per
+    # stage, gated on its own); the chain verify reads all stages as one
+    dstage = [dl[:, s_ * kk:(s_ + 1) * kk].contiguous() for s_ in range(S)]
+    tstage = [drafts[:, s_ * kk:(s_ + 1) * kk].contiguous() for s_ in range(S)]
+    u = (torch.randint(0, 1 << 24, (B, L), generator=g, device=dev).float() * 2.0 ** -24)
+    u2 = (torch.randint(0, 1 << 24, (B,), generator=g, device=dev).float() * 2.0 ** -24)
+    ws = torch.empty(max(256, dfl.lib().dflash_verify_workspace_size(B, L, V)), dtype=torch.uint8,
+                     device=dev)
+    wsg = torch.empty(max(256, dfl.lib().dflash_gate_workspace_size(B, kk, V)), dtype=torch.uint8,
+                      device=dev)
+    out = {}
+    gouts = [{} for _ in range(S)]
+
+    def gates():
+        for s_ in range(S):
+            gouts[s_] = dfl.gate(dstage[s_], tstage[s_], g=-0.5, row_stats=False,
+                                 out=gouts[s_] or None, workspace=wsg)
+
+    def verify():
+        out.update(dfl.verify_sample(tl, dl, drafts, u, u2, audit=False, out=out or None,
+                                     workspace=ws))
+
+    def step():
+        gates()
+        verify()
+
+    ms = _events_ms(step, args.steps, args.warmup)
+    vms = _events_ms(verify, args.steps, args.warmup)
+    gms = _events_ms(gates, args.steps, args.warmup) / S
+    vbytes = B * (2 * L + 1) * V * 2
+    gbytes = B * kk * V * 2
+    line = _base_line(args, "Qwen3-4B-shaped stochastic chain verify + DLoop gates, blocks/sec",
+                      round(B / (ms * 1e-3), 1), "blocks/s", ms,
+                      f"stochastic verify of a {S}-stage DLoop chain ({L} drafts + bonus) over vocab "
+                      f"{V}, batch {B}, draft = target + N(0, {args.sigma}), T = 1, plus {S} gates "
+                      f"(c >= -0.5) on the stages' draft rows", batch=B, vocab=V, stages=S,
+                      chain=L, sigma=args.sigma)
+    line["roofline"] = {"kernel": "verify_sample (all its launches)", "bound": "hbm",
+                        "achieved": round(vbytes / (vms * 1e-3) / 1e9, 1), "peak": HBM_PEAK / 1e9,
+                        "unit": "GB/s", "frac": round(vbytes / (vms * 1e-3) / HBM_PEAK, 4),
+                        "traffic": None, "algorithmic_bytes": vbytes,
+                        "avg_launch_us": round(vms * 1e3, 2)}
+    line["gate"] = {"avg_us": round(gms * 1e3, 2), "algorithmic_bytes": gbytes,
+                    "hbm_frac": round(gbytes / (gms * 1e-3) / HBM_PEAK, 4),
+                    "go_fraction": round(float(torch.cat([o["go"] for o in gouts]).float().mean()), 4)}
+    line["accept_len_mean"] = round(float(out["accept_len"].float().mean()), 3)
+    return line
+
+
+def bench_prefill(args):
+    """Prefill ctx-KV materialisation: 4 sequences x 32768 positions, five
+    captured hiddens fused by W_f [4096, 20480] + b_f, then K and V for five
+    draft layers (8 KV heads x 128) into 16-token paged caches."""
+    import torch
+    import block_diffusion_draft_ctx_amd as dfl
+    n_seq, rps, d, m, Ld, Hkv, D = 4, 32768, 4096, 5, 5, 8, 128
+    T = n_seq * rps
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(4000)
+    bf = torch.bfloat16
+
+    def randn(*shape, std=1.0):
+        return (torch.randn(*shape, generator=g, device=dev) * std).to(bf)
+
+    hid = [randn(T, d) for _ in range(m)]
+    Wf, bfv = randn(d, m * d, std=0.02), randn(d, std=0.02)
+    WK = [randn(Hkv * D, d, std=0.02) for _ in range(Ld)]
+    WV = [randn(Hkv * D, d, std=0.02) for _ in range(Ld)]
+    maxp = rps // 16
+    npg = n_seq * maxp
+    bt = torch.randperm(npg, generator=g, device=dev).to(torch.int32).view(n_seq, maxp).contiguous()
+    ck = [torch.empty(npg, 16, Hkv, D, dtype=bf, device=dev) for _ in range(Ld)]
+    cv = [torch.empty(npg, 16, Hkv, D, dtype=bf, device=dev) for _ in range(Ld)]
+    start = torch.zeros(n_seq, dtype=torch.int32, device=dev)
+    ws = torch.empty(dfl.lib().dflash_materialize_workspace_size(T, m, d, Ld, Hkv, D, dfl.BF16),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        dfl.materialize_ctx_kv(hid, Wf, bfv, WK, WV, ck, cv, bt, rps, start, None, workspace=ws)
+
+    ms = _events_ms(step, args.steps, args.warmup)
+    flops = 2.0 * T * (m * d * d + 2 * Ld * Hkv * D * d)
+    line = _base_line(args, "prefill ctx-KV materialisation, rows/sec", round(T / (ms * 1e-3), 1),
+                      "rows/s", ms, f"prefill ctx-KV materialisation: {n_seq} x {rps} rows, 5 "
+                      f"hiddens of 4096 fused by W_f [4096, 20480] + b_f, K and V of {Ld} draft "
+                      f"layers (8 KV heads x 128) written to 16-token paged caches", rows=T,
+                      d_model=d, draft_layers=Ld)
+    line["roofline"] = {"kernel": "materialize (both GEMMs)", "bound": "mfma",
+                        "achieved": round(flops / (ms * 1e-3) / 1e12, 1), "peak": BF16_PEAK / 1e12,
+                        "unit": "TFLOP/s", "frac": round(flops / (ms * 1e-3) / BF16_PEAK, 4),
+                        "traffic": None, "algorithmic_flops": flops,
+                        "avg_launch_us": round(ms * 1e3, 2)}
+    return line
+
+
+def bench_packed(args):
+    """Training-style packed block mask, forward only: one 8192-token
+    sequence, up to 512 non-overlapping anchors in the loss region, block 16;
+    each block attends to the target positions before its anchor and to its
+    own block (32 Q / 8 KV heads x 128, one layer)."""
+    import numpy as np
+    import torch
+    import block_diffusion_draft_ctx_amd as dfl
+    import synth
+    seq, kk, Hq, Hkv, D = 8192, 16, 32, 8, 128
+    rng = synth.make_rng(5000)
+    anchors, P = synth.packed_anchors(rng, seq, kk, 512)
+    nb = len(anchors)
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(5000)
+    bf = torch.bfloat16
+    npg = seq // 16
+    perm = torch.randperm(npg, generator=g, device=dev).to(torch.int32)
+    bt = perm.view(1, npg).repeat(nb, 1).contiguous()
+    ck = torch.randn(npg, 16, Hkv, D, generator=g, device=dev).to(bf)
+    cv = torch.randn(npg, 16, Hkv, D, generator=g, device=dev).to(bf)
+    q = torch.randn(nb, kk, Hq, D, generator=g, device=dev).to(bf)
+    kb = torch.randn(nb, kk, Hkv, D, generator=g, device=dev).to(bf)
+    vb = torch.randn(nb, kk, Hkv, D, generator=g, device=dev).to(bf)
+    ctx = torch.from_numpy(anchors.astype(np.int32)).to(dev)
+    out = torch.empty(nb, kk, Hq, D, dtype=bf, device=dev)
+    ws = torch.empty(max(256, dfl.lib().dflash_attention_workspace_size(nb, kk, Hq, Hkv, D, npg,
+                                                                        dfl.BF16)),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        dfl.block_attention(q, kb, vb, ck, cv, bt, ctx, out=out, workspace=ws)
+
+    ms = _events_ms(step, args.steps, args.warmup)
+    keys = int(anchors.astype(np.int64).sum()) + nb * kk
+    flops = 4.0 * kk * Hq * D * keys
+    stream = float(anchors.astype(np.int64).sum()) * Hkv * D * 2 * 2
+    line = _base_line(args, "packed block-mask attention, blocks/sec", round(nb / (ms * 1e-3), 1),
+                      "blocks/s", ms, f"training-style packed block mask, forward: sequence {seq}, "
+                      f"prompt {P}, {nb} anchors, block {kk}, 32 Q / 8 KV heads x 128, one layer",
+                      blocks=nb, seq_len=seq, prompt=P, mean_anchor=round(float(anchors.mean()), 1))
+    line["roofline"] = {"kernel": "block_attention (packed)", "bound": "mfma",
+                        "achieved": round(flops / (ms * 1e-3) / 1e12, 1), "peak": BF16_PEAK / 1e12,
+                        "unit": "TFLOP/s", "frac": round(flops / (ms * 1e-3) / BF16_PEAK, 4),
+                        "traffic": None, "algorithmic_flops": flops,
+                        "avg_launch_us": round(ms * 1e3, 2),
+                        "ctx_stream_GBps": round(stream / (ms * 1e-3) / 1e9, 1)}
+    return line
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build "
-              "targets a single MI355X: the step is data parallel by request and needs no "
-              "collective).", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the step is "
+              "data parallel by request (no collective), so one GPU's throughput at its share "
+              "of the batch is the figure.", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.workload != "decode":
+        fn = {"sample-gate": bench_sample_gate, "prefill": bench_prefill,
+              "packed": bench_packed}[args.workload]
+        print(json.dumps(fn(args)), flush=True)
+        return
     st = Step(args.batch, args.ctx, args.block, args.vocab, args.layers)
     print(f"[bench] inputs ready: B={st.B} ctx={st.C} k={st.k} V={st.V} layers={st.Ld}",
           file=sys.stderr, flush=True)
@@ -273,7 +508,7 @@ def main():
         "roofline": {"kernel": "block_attention (per layer)", "bound": "hbm",
                      "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
-                     "traffic": None, "algorithmic_bytes": ab,
+                     "traffic": recorded_traffic(), "algorithmic_bytes": ab,
                      "avg_launch_us": round(attn_ms * 1e3, 2)},
     }
     if args.breakdown:

@@ -8,18 +8,20 @@
 //
 // bf16 design (gfx950, wave64).  One workgroup owns one (request, kv-head,
 // ctx-split).  Its G*k query rows (the G q-heads that share the kv-head, times
-// the k block positions) are split into 16-row slices, one per wavefront, so
-// every K/V byte streamed from HBM is used by all G q-heads.  Keys are
-// processed 32 at a time: the tile's K rows and V rows are fetched with
-// 16-byte loads (the next tile's loads are issued before the current tile is
-// computed), K is stored row-major and V transposed in LDS, and each
-// wavefront runs
-//   S^T[32 keys x 16 q] = K . Q^T        2 x (D/32) MFMA 16x16x32 bf16
-//   online softmax per query column      (4-lane shuffles, exp2 domain)
-//   O^T[D x 16 q]      += V^T . P^T      (D/16) MFMA 16x16x32 bf16
+// the k block positions) are cut into 32-row slices; every slice gets two
+// wavefronts, one per half of each 64-key tile, so every K/V byte streamed
+// from HBM is used by all G q-heads.  The split's physical pages are staged in
+// LDS once; tile t+1's K and V rows are fetched with 16-byte loads while tile
+// t is computed, then stored to the other LDS stage (one barrier per tile).
+// Each wavefront runs, on its 32 keys and 32 query rows,
+//   S^T[32 keys x 32 q] = K . Q^T        D/16 MFMA 32x32x16 bf16
+//   online softmax per query column      (exp2 domain, lazily moved max)
+//   O^T[D x 32 q]      += V^T . P^T      2 * D/32 MFMA 32x32x16 bf16, V read
+//                                        from LDS with the transposing read
 // so that a lane's accumulators all belong to one query and rescale with one
-// factor.  Small batches split the context across workgroups and a second
-// kernel merges the splits by their log-sum-exp.
+// factor; the two key halves merge through LDS at the end.  Small batches
+// split the context across workgroups and a second kernel merges the splits
+// by their log-sum-exp.
 #include <cmath>
 
 #include "common.h"

@@ -301,17 +301,20 @@ __global__ __launch_bounds__(128) void k_sample_accept(
     ratio_out[b * L + t] = __builtin_nanf("");
   }
   __syncthreads();
+  // the first wavefront holds every link (chain <= 64): the first rejected
+  // link by a ballot
+  const bool in_chain = t < nb;
+  const bool rej = in_chain && !(u[b * L + t] < rat[min(t, 63)]);
+  const uint64_t rejm = __ballot(rej);
+  const uint64_t badm = __ballot(in_chain && !okx[min(t, 63)]);
   if (t == 0) {
     ReqInfo I;
-    bool err = bad;
-    for (int i = 0; i < nb; ++i) err |= !okx[i];
+    const bool err = bad || badm != 0;
     I.err = err;
     I.acc = -1; I.row = 0; I.mode = 1;
     I.Mt = I.St = I.Md = I.Sd = 0.f;
     if (!err) {
-      int j = nb;
-      for (int i = 0; i < nb; ++i)
-        if (!(u[b * L + i] < rat[i])) { j = i; break; }
+      const int j = rejm ? __ffsll((unsigned long long)rejm) - 1 : nb;
       I.acc = j;
       I.row = j;
       I.mode = (j < nb) ? 0 : 1;
@@ -414,37 +417,39 @@ __global__ __launch_bounds__(kThreads) void k_bonus_select(
   }
   __shared__ int sh_kind, sh_cc, sh_x;
   __shared__ float sh_base, sh_thr, sh_Z;
-  __shared__ float sh_loc[kThreads];
+  __shared__ float sh_loc[kThreads / 64];
   __shared__ float sh_gap;
   __shared__ int sh_last;
-  if (t == 0) {
-    float Rs = 0.f, Ps = 0.f, Ms = 0.f;
-    for (int c = 0; c < nc; ++c) { float4 p = rpart[b * nc + c]; Rs += p.x; Ms += p.y; Ps += p.z; }
+  // Chunk selection by the first wavefront, lane c holding chunk c (at most
+  // 64 chunks): totals by butterfly sums, the running weight by a shuffle
+  // scan in chunk order, the chunk by a ballot.
+  if (t < 64) {
+    const float4 pc = (t < nc) ? rpart[b * nc + t] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float Rs = wave_sum(pc.x), Ms = wave_sum(pc.y), Ps = wave_sum(pc.z);
     const int kind = (I.mode == 0 && Rs > 0.f) ? 0 : 1;
     const float Z = kind == 0 ? Rs : Ps;
     const float thr = u2[b] * Z;
-    float pre = 0.f;
-    int cc = -1;
-    float base = 0.f;
-    for (int c = 0; c < nc; ++c) {
-      float4 p = rpart[b * nc + c];
-      float w = kind == 0 ? p.x : p.z;
-      if (pre + w > thr) { cc = c; base = pre; break; }
-      pre += w;
+    const float w = kind == 0 ? pc.x : pc.z;
+    float incl = w;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float v = __shfl_up(incl, o, 64);
+      if (t >= o) incl += v;
     }
-    if (cc < 0) {  // rounding left u'*Z at the very end: the last chunk with mass
-      pre = 0.f;
-      for (int c = 0; c < nc; ++c) {
-        float4 p = rpart[b * nc + c];
-        float w = kind == 0 ? p.x : p.z;
-        if (w > 0.f) { cc = c; base = pre; }
-        pre += w;
-      }
+    const uint64_t over = __ballot(t < nc && incl > thr);
+    int cc;
+    if (over) {
+      cc = __ffsll((unsigned long long)over) - 1;
+    } else {  // rounding left u'*Z at the very end: the last chunk with mass
+      const uint64_t pos = __ballot(t < nc && w > 0.f);
+      cc = pos ? 63 - __clzll((long long)pos) : 0;   // no mass at all only with invalid logits
     }
-    if (cc < 0) cc = 0;  // no chunk has mass (only with invalid logits)
-    sh_kind = kind; sh_cc = cc; sh_base = base; sh_thr = thr; sh_Z = Z;
-    sh_x = INT_MAX; sh_last = -1; sh_gap = 0.f;
-    if (beta_out) beta_out[b] = (I.mode == 0) ? Ms : __builtin_nanf("");
+    const float base = __shfl(incl - w, cc, 64);
+    if (t == 0) {
+      sh_kind = kind; sh_cc = cc; sh_base = base; sh_thr = thr; sh_Z = Z;
+      sh_x = INT_MAX; sh_last = -1; sh_gap = 0.f;
+      if (beta_out) beta_out[b] = (I.mode == 0) ? Ms : __builtin_nanf("");
+    }
   }
   __syncthreads();
   BonusRow<T> R{tl + (int64_t)(b * (L + 1) + I.row) * ts,
@@ -467,16 +472,21 @@ __global__ __launch_bounds__(kThreads) void k_bonus_select(
     loc += w;
     if (w > 0.f) lastpos = x;
   }
-  sh_loc[t] = loc;
   if (lastpos >= 0) atomicMax(&sh_last, lastpos);
-  __syncthreads();
-  if (t == 0) {  // exclusive prefix over the segment sums, in segment order
-    float acc = 0.f;
-    for (int k = 0; k < kThreads; ++k) { float v = sh_loc[k]; sh_loc[k] = acc; acc += v; }
+  // exclusive prefix of the segment sums in segment order: shuffle scan in
+  // each wavefront, then the wavefront totals
+  float incl = loc;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float v = __shfl_up(incl, o, 64);
+    if ((t & 63) >= o) incl += v;
   }
+  if ((t & 63) == 63) sh_loc[t >> 6] = incl;
   __syncthreads();
+  float wpre = 0.f;
+  for (int k = 0; k < (t >> 6); ++k) wpre += sh_loc[k];
   const float thr = sh_thr;
-  const float base = sh_base + sh_loc[t];
+  const float base = sh_base + wpre + (incl - loc);
   if (base <= thr && base + loc > thr) {
     float acc = base;
     int found = -1;
@@ -506,46 +516,53 @@ __global__ __launch_bounds__(kThreads) void k_bonus_select(
 }
 
 // ------------------------------------------------------------------- gate
-__global__ __launch_bounds__(64) void k_gate_finalize(
+// One workgroup per request: each wavefront merges the chunk partials of
+// one row at a time (lane c holds chunk c, at most 64 chunks) by butterfly
+// max and sum, then the request's terms are summed by the first wavefront.
+__global__ __launch_bounds__(256) void k_gate_finalize(
     int B, int n, int V, int nc, const float2* __restrict__ part, const void* __restrict__ dl,
     int64_t rs, int bf16, const int32_t* __restrict__ toks, const int32_t* __restrict__ valid,
     int rows_all, float a, float g, float* __restrict__ c_out, int32_t* __restrict__ go_out,
     float* __restrict__ row_max, float* __restrict__ row_lse) {
   const int b = blockIdx.x;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   __shared__ float term[64];
   bool bad;
   const int nv = chain_of(valid, b, n, &bad);
   const int nread = rows_all ? n : nv;
-  float tm = 0.f;
-  if (t < n) {
-    if (t < nread) {
-      float M, S;
-      reduce_lse_row(part, b * n + t, nc, M, S);
+  for (int i = w; i < n; i += 4) {
+    float tm = 0.f;
+    if (i < nread) {
+      const float2 pc = lane < nc ? part[(int64_t)(b * n + i) * nc + lane] : make_float2(neg_inf(), 0.f);
+      const float M = wave_max(pc.x);
+      const float S = wave_sum((M == neg_inf() || pc.x == neg_inf()) ? 0.f : pc.y * exp2f(pc.x - M));
       const float l2 = M + log2f(S);
-      if (row_max) row_max[b * n + t] = M * kLn2;
-      if (row_lse) row_lse[b * n + t] = l2 * kLn2;
-      if (t < nv) {
-        const int x = toks[b * n + t];
-        if (x < 0 || x >= V) {
-          tm = __builtin_nanf("");
-        } else {
-          const int64_t off = (int64_t)(b * n + t) * rs + x;
-          const float dx = bf16 ? bf16_to_f32(static_cast<const uint16_t*>(dl)[off])
-                                : static_cast<const float*>(dl)[off];
-          tm = (dx * a - l2) * kLn2;
+      if (lane == 0) {
+        if (row_max) row_max[b * n + i] = M * kLn2;
+        if (row_lse) row_lse[b * n + i] = l2 * kLn2;
+        if (i < nv) {
+          const int x = toks[b * n + i];
+          if (x < 0 || x >= V) {
+            tm = __builtin_nanf("");
+          } else {
+            const int64_t off = (int64_t)(b * n + i) * rs + x;
+            const float dx = bf16 ? bf16_to_f32(static_cast<const uint16_t*>(dl)[off])
+                                  : static_cast<const float*>(dl)[off];
+            tm = (dx * a - l2) * kLn2;
+          }
         }
       }
     }
-    term[t] = tm;
+    if (lane == 0) term[i] = tm;
   }
   __syncthreads();
-  if (t == 0) {
-    float c = 0.f;
-    for (int i = 0; i < nv; ++i) c += term[i];
-    if (bad) c = __builtin_nanf("");
-    c_out[b] = c;
-    go_out[b] = (c >= g) ? 1 : 0;
+  if (w == 0) {
+    float c = wave_sum(lane < nv ? term[lane] : 0.f);
+    if (lane == 0) {
+      if (bad) c = __builtin_nanf("");
+      c_out[b] = c;
+      go_out[b] = (c >= g) ? 1 : 0;
+    }
   }
 }
 
@@ -699,7 +716,7 @@ hipError_t launch_gate(bool bf16, int B, int n, int V, const void* dl, int64_t r
     if (vec) launch_lse<float, true>(s0, s1, B, n, V, lens, a, pl, rows, part, st);
     else launch_lse<float, false>(s0, s1, B, n, V, lens, a, pl, rows, part, st);
   }
-  hipLaunchKernelGGL(k_gate_finalize, dim3(B), dim3(64), 0, st, B, n, V, pl.n_chunks, part, dl, rs,
+  hipLaunchKernelGGL(k_gate_finalize, dim3(B), dim3(256), 0, st, B, n, V, pl.n_chunks, part, dl, rs,
                      bf16 ? 1 : 0, toks, valid, rows_all ? 1 : 0, a, g, c_out, go_out, row_max,
                      row_lse);
   return hipGetLastError();

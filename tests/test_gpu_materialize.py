@@ -126,3 +126,51 @@ def test_materialize_is_deterministic():
     b = _run(c)
     for x, y in zip(a[0] + a[1] + [a[2]], b[0] + b[1] + [b[2]]):
         np.testing.assert_array_equal(bits(x), bits(y))
+
+
+def test_materialize_prefill_full_size_sampled():
+    """The prefill launch at full size: 4 sequences x 32768 rows (T = 131072),
+    five hiddens of 4096, W_f [4096, 20480] + b_f, five draft layers of 8 KV
+    heads x 128, 16-token pages in shuffled order, every row committed.  The
+    inputs are seeded normals drawn on the device by torch (too large to draw
+    on the host); the sampled rows and the weights are copied back bit for bit
+    for the oracle, and those rows' cache slots are compared."""
+    import torch
+    n_seq, rps, d, m, Ld, Hkv, D = 4, 32768, 4096, 5, 5, 8, 128
+    T = n_seq * rps
+    log(f"materialise full prefill T={T}")
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(2450)
+    bf = torch.bfloat16
+
+    def randn(*shape, std=1.0):
+        return (torch.randn(*shape, generator=g, device=dev) * std).to(bf)
+
+    hid = [randn(T, d) for _ in range(m)]
+    Wf, bfv = randn(d, m * d, std=0.02), randn(d, std=0.02)
+    WK = [randn(Hkv * D, d, std=0.02) for _ in range(Ld)]
+    WV = [randn(Hkv * D, d, std=0.02) for _ in range(Ld)]
+    maxp = rps // 16
+    bt = torch.randperm(n_seq * maxp, generator=g, device=dev).to(torch.int32).view(n_seq, maxp)
+    ck = [torch.zeros(n_seq * maxp, 16, Hkv, D, dtype=bf, device=dev) for _ in range(Ld)]
+    cv = [torch.zeros(n_seq * maxp, 16, Hkv, D, dtype=bf, device=dev) for _ in range(Ld)]
+    start = torch.zeros(n_seq, dtype=torch.int32, device=dev)
+    dfl.materialize_ctx_kv(hid, Wf, bfv, WK, WV, ck, cv, bt.contiguous(), rps, start, None)
+    torch.cuda.synchronize()
+    # sampled rows: each sequence's first and last row, a page boundary, random rows
+    rng = np.random.default_rng(2450)
+    rows = sorted({0, rps - 1, rps, 2 * rps + 15, 2 * rps + 16, T - 1,
+                   *rng.choice(T, size=18, replace=False).tolist()})
+    ridx = torch.tensor(rows, dtype=torch.int64, device=dev)
+    ref = oracle.materialize([bits(h.index_select(0, ridx)) for h in hid], bits(Wf), bits(bfv),
+                             [bits(w) for w in WK], [bits(w) for w in WV], Hkv, D, "bf16")
+    btn = bt.cpu().numpy()
+    slots = torch.tensor([int(btn[r // rps, (r % rps) // 16]) * 16 + r % 16 for r in rows],
+                         dtype=torch.int64, device=dev)
+    for l in range(Ld):
+        for name, cache, rv in (("K", ck[l], ref["K"][l]), ("V", cv[l], ref["V"][l])):
+            got = down(cache.view(-1, Hkv, D).index_select(0, slots))
+            e = rel_err(got, rv)
+            assert e <= TOL["bf16"], (l, name, e)
+    log(f"  {len(rows)} rows x {Ld} layers x K/V within {TOL['bf16']}")
