@@ -28,6 +28,15 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxChunks = 64;
+// Tuning knobs: workgroups a vocabulary pass aims for, and 16-byte loads in
+// flight per lane in the row passes.
+#ifndef DFLASH_VOCAB_WGS
+#define DFLASH_VOCAB_WGS 2048
+#endif
+#ifndef DFLASH_VOCAB_INFLIGHT
+#define DFLASH_VOCAB_INFLIGHT 8
+#endif
+constexpr int kNF = DFLASH_VOCAB_INFLIGHT;
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -94,19 +103,25 @@ __global__ __launch_bounds__(kThreads) void k_row_argmax(RowSet s0, RowSet s1, i
   float best = neg_inf();
   int bi = INT_MAX;
   if (VEC) {
+    // full rounds of kNF 16-byte loads in flight per lane, then one last
+    // round whose loads are issued together at clamped (always valid)
+    // indices, the values past the end being dropped
     const int nvec = (x1 - x0) >> 3;
     int v = threadIdx.x;
-    for (; v + 3 * kThreads < nvec; v += 4 * kThreads) {
-      float a[4][8];
+    for (; v + (kNF - 1) * kThreads < nvec; v += kNF * kThreads) {
+      float a[kNF][8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) load8(row + x0 + (v + u * kThreads) * 8, a[u]);
+      for (int u = 0; u < kNF; ++u) load8(row + x0 + (v + u * kThreads) * 8, a[u]);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) am_update(a[u], x0 + (v + u * kThreads) * 8, best, bi);
+      for (int u = 0; u < kNF; ++u) am_update(a[u], x0 + (v + u * kThreads) * 8, best, bi);
     }
-    for (; v < nvec; v += kThreads) {
-      float a[8];
-      load8(row + x0 + v * 8, a);
-      am_update(a, x0 + v * 8, best, bi);
+    if (v < nvec) {
+      float a[kNF][8];
+#pragma unroll
+      for (int u = 0; u < kNF; ++u) load8(row + x0 + min(v + u * kThreads, nvec - 1) * 8, a[u]);
+#pragma unroll
+      for (int u = 0; u < kNF; ++u)
+        if (v + u * kThreads < nvec) am_update(a[u], x0 + (v + u * kThreads) * 8, best, bi);
     }
     for (int x = x0 + nvec * 8 + threadIdx.x; x < x1; x += kThreads) {
       float e = load1(row + x);
@@ -226,19 +241,25 @@ __global__ __launch_bounds__(kThreads) void k_row_lse(RowSet s0, RowSet s1, int 
   const int x1 = min(V, x0 + chunk);
   float m = neg_inf(), s = 0.f;
   if (VEC) {
+    // full rounds of kNF 16-byte loads in flight per lane, then one last
+    // round whose loads are issued together at clamped (always valid)
+    // indices, the values past the end being dropped
     const int nvec = (x1 - x0) >> 3;
     int v = threadIdx.x;
-    for (; v + 3 * kThreads < nvec; v += 4 * kThreads) {
-      float e[4][8];
+    for (; v + (kNF - 1) * kThreads < nvec; v += kNF * kThreads) {
+      float e[kNF][8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) load8(row + x0 + (v + u * kThreads) * 8, e[u]);
+      for (int u = 0; u < kNF; ++u) load8(row + x0 + (v + u * kThreads) * 8, e[u]);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) lse_update(e[u], a, m, s);
+      for (int u = 0; u < kNF; ++u) lse_update(e[u], a, m, s);
     }
-    for (; v < nvec; v += kThreads) {
-      float e[8];
-      load8(row + x0 + v * 8, e);
-      lse_update(e, a, m, s);
+    if (v < nvec) {
+      float e[kNF][8];
+#pragma unroll
+      for (int u = 0; u < kNF; ++u) load8(row + x0 + min(v + u * kThreads, nvec - 1) * 8, e[u]);
+#pragma unroll
+      for (int u = 0; u < kNF; ++u)
+        if (v + u * kThreads < nvec) lse_update(e[u], a, m, s);
     }
     for (int x = x0 + nvec * 8 + threadIdx.x; x < x1; x += kThreads) lse_update1(load1(row + x), a, m, s);
   } else {
@@ -261,26 +282,36 @@ __global__ __launch_bounds__(kThreads) void k_row_lse(RowSet s0, RowSet s1, int 
   }
 }
 
+// Merge a row's chunk partials in chunk order; up to eight are loaded
+// together (indices clamped to valid ones) before they are merged.
 __device__ void reduce_lse_row(const float2* part, int row, int nc, float& m, float& s) {
   m = neg_inf();
   s = 0.f;
-  for (int c = 0; c < nc; ++c) {
-    float2 p = part[row * nc + c];
-    lse2_merge(m, s, p.x, p.y);
+  for (int c0 = 0; c0 < nc; c0 += 8) {
+    float2 p[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = part[row * nc + min(c0 + j, nc - 1)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c0 + j < nc) lse2_merge(m, s, p[j].x, p[j].y);
   }
 }
 
 // --------------------------------------------------------- sampled verify
+// The acceptance scan of request b, run by a whole workgroup (at least 128
+// threads; thread t < 64 owns chain link t): merge each row's chunk partials
+// into its base-2 normalisers, form p/q at the drafted token, and find the
+// first rejected link by a ballot.  Every thread gets the request's ReqInfo.
 template <typename T>
-__global__ __launch_bounds__(128) void k_sample_accept(
-    int B, int L, int V, int nc, const float2* __restrict__ part, const T* __restrict__ tl,
-    int64_t ts, const T* __restrict__ dl, int64_t ds, const int32_t* __restrict__ toks,
-    const int32_t* __restrict__ lens, const float* __restrict__ u, float a,
-    float* __restrict__ ratio_out, ReqInfo* __restrict__ info) {
-  const int b = blockIdx.x;
+__device__ ReqInfo accept_scan(int b, int B, int L, int V, int nc, const float2* __restrict__ part,
+                               const T* __restrict__ tl, int64_t ts, const T* __restrict__ dl,
+                               int64_t ds, const int32_t* __restrict__ toks,
+                               const int32_t* __restrict__ lens, const float* __restrict__ u,
+                               float a, float* __restrict__ ratio_out) {
   const int t = threadIdx.x;
   __shared__ float Mt[65], St[65], Md[64], Sd[64], rat[64];
   __shared__ int okx[64];
+  __shared__ ReqInfo sI;
   bool bad;
   const int nb = chain_of(lens, b, L, &bad);
   if (t <= nb) reduce_lse_row(part, b * (L + 1) + t, nc, Mt[t], St[t]);
@@ -322,8 +353,10 @@ __global__ __launch_bounds__(128) void k_sample_accept(
       I.St = St[j];
       if (j < nb) { I.Md = Md[j]; I.Sd = Sd[j]; }
     }
-    info[b] = I;
+    sI = I;
   }
+  __syncthreads();
+  return sI;
 }
 
 // Weight of token x in the bonus draw: residual max(0, p - q) (kind 0) or the
@@ -341,15 +374,12 @@ struct BonusRow {
   }
 };
 
+// Chunk c's residual weights max(0, p - q) (mode 0), min(p, q) and target
+// weights of request b's chosen row pair, summed into rpart.
 template <typename T, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_bonus_partial(
-    int B, int L, int V, int chunk, int nc, const T* __restrict__ tl, int64_t ts,
-    const T* __restrict__ dl, int64_t ds, float a, const ReqInfo* __restrict__ info,
-    float4* __restrict__ rpart) {
-  const int c = blockIdx.x % nc;
-  const int b = blockIdx.x / nc;
-  const ReqInfo I = info[b];
-  if (I.err) return;
+__device__ void bonus_chunk_sum(int c, int chunk, int V, const T* __restrict__ tl, int64_t ts,
+                                const T* __restrict__ dl, int64_t ds, float a, int b, int L,
+                                const ReqInfo I, float4* __restrict__ rpart) {
   BonusRow<T> R{tl + (int64_t)(b * (L + 1) + I.row) * ts,
                 I.mode == 0 ? dl + (int64_t)(b * L + I.row) * ds : nullptr,
                 a, I.Mt, 1.f / I.St, I.Md, I.mode == 0 ? 1.f / I.Sd : 0.f};
@@ -368,12 +398,23 @@ __global__ __launch_bounds__(kThreads) void k_bonus_partial(
   };
   if (VEC) {
     const int nvec = (x1 - x0) >> 3;
-    for (int v = threadIdx.x; v < nvec; v += kThreads) {
-      float tv[8], dv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      load8(R.tr + x0 + v * 8, tv);
-      if (I.mode == 0) load8(R.dr + x0 + v * 8, dv);
+    for (int v = threadIdx.x; v < nvec; v += 2 * kThreads) {
+      // two loads per operand row in flight; the second index is clamped
+      // (always valid) and its values dropped past the end
+      float tv[2][8], dv[2][8] = {};
+      const int v1 = min(v + kThreads, nvec - 1);
+      load8(R.tr + x0 + v * 8, tv[0]);
+      load8(R.tr + x0 + v1 * 8, tv[1]);
+      if (I.mode == 0) {
+        load8(R.dr + x0 + v * 8, dv[0]);
+        load8(R.dr + x0 + v1 * 8, dv[1]);
+      }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) one(tv[j], dv[j]);
+      for (int j = 0; j < 8; ++j) one(tv[0][j], dv[0][j]);
+      if (v + kThreads < nvec) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) one(tv[1][j], dv[1][j]);
+      }
     }
     for (int x = x0 + nvec * 8 + threadIdx.x; x < x1; x += kThreads)
       one(load1(R.tr + x), I.mode == 0 ? load1(R.dr + x) : 0.f);
@@ -393,19 +434,21 @@ __global__ __launch_bounds__(kThreads) void k_bonus_partial(
     for (int k = 0; k < kThreads / 64; ++k) { o.x += s[0][k]; o.y += s[1][k]; o.z += s[2][k]; }
     rpart[blockIdx.x] = o;
   }
+  __syncthreads();
 }
 
+// Bonus draw of request b by one workgroup, once every chunk's residual (or
+// target) weight sum of the chosen row pair is in rpart: pick the chunk that
+// holds u' * (total weight), then scan inside it.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_bonus_select(
-    int B, int L, int V, int chunk, int nc, const T* __restrict__ tl, int64_t ts,
-    const T* __restrict__ dl, int64_t ds, float a, const ReqInfo* __restrict__ info,
+__device__ void select_bonus(
+    int b, int L, int V, int chunk, int nc, const T* __restrict__ tl, int64_t ts,
+    const T* __restrict__ dl, int64_t ds, float a, const ReqInfo I,
     const float4* __restrict__ rpart, const float* __restrict__ u2,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ bonus, int32_t* __restrict__ commit,
     const int32_t* __restrict__ prefix, int32_t* __restrict__ new_seq,
     float* __restrict__ beta_out, float* __restrict__ gap_out) {
-  const int b = blockIdx.x;
   const int t = threadIdx.x;
-  const ReqInfo I = info[b];
   if (I.err) {
     if (t == 0) {
       accept_len[b] = -1; bonus[b] = -1; commit[b] = 0;
@@ -465,12 +508,41 @@ __global__ __launch_bounds__(kThreads) void k_bonus_select(
   const int seg = (x1 - x0 + kThreads - 1) / kThreads;
   const int xs = min(x1, x0 + t * seg);
   const int xe = min(x1, xs + seg);
+  // the thread's segment: up to kSeg weights loaded together and kept in
+  // registers (longer segments, for very large vocabularies, are streamed)
+  constexpr int kSeg = 16;
+  const bool inreg = seg <= kSeg;
+  float wv[kSeg];
   float loc = 0.f;
   int lastpos = -1;
-  for (int x = xs; x < xe; ++x) {
-    float w = wt(x);
-    loc += w;
-    if (w > 0.f) lastpos = x;
+  if (inreg) {
+    // loads at clamped (always valid) positions, issued together; weights
+    // past the segment end are dropped
+    const int xl = max(xe - 1, x0);
+    float tv[kSeg];
+#pragma unroll
+    for (int i = 0; i < kSeg; ++i) tv[i] = load1(R.tr + min(xs + i, xl));
+    if (kind == 0) {
+      float dv[kSeg];
+#pragma unroll
+      for (int i = 0; i < kSeg; ++i) dv[i] = load1(R.dr + min(xs + i, xl));
+#pragma unroll
+      for (int i = 0; i < kSeg; ++i) wv[i] = (xs + i < xe) ? R.res(tv[i], dv[i]) : 0.f;
+    } else {
+#pragma unroll
+      for (int i = 0; i < kSeg; ++i) wv[i] = (xs + i < xe) ? R.et(tv[i]) : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < kSeg; ++i) {
+      loc += wv[i];
+      if (wv[i] > 0.f) lastpos = xs + i;
+    }
+  } else {
+    for (int x = xs; x < xe; ++x) {
+      float w = wt(x);
+      loc += w;
+      if (w > 0.f) lastpos = x;
+    }
   }
   if (lastpos >= 0) atomicMax(&sh_last, lastpos);
   // exclusive prefix of the segment sums in segment order: shuffle scan in
@@ -491,10 +563,20 @@ __global__ __launch_bounds__(kThreads) void k_bonus_select(
     float acc = base;
     int found = -1;
     float lo = 0.f, hi = 0.f;
-    for (int x = xs; x < xe; ++x) {
-      float w = wt(x);
-      if (acc + w > thr) { found = x; lo = acc; hi = acc + w; break; }
-      acc += w;
+    if (inreg) {
+#pragma unroll
+      for (int i = 0; i < kSeg; ++i) {
+        if (found < 0 && xs + i < xe) {
+          if (acc + wv[i] > thr) { found = xs + i; lo = acc; hi = acc + wv[i]; }
+          else acc += wv[i];
+        }
+      }
+    } else {
+      for (int x = xs; x < xe; ++x) {
+        float w = wt(x);
+        if (acc + w > thr) { found = x; lo = acc; hi = acc + w; break; }
+        acc += w;
+      }
     }
     if (found < 0 && lastpos >= 0) { found = lastpos; lo = hi = thr; }
     if (found >= 0) {
@@ -513,6 +595,36 @@ __global__ __launch_bounds__(kThreads) void k_bonus_select(
     if (new_seq) new_seq[b] = prefix[b] + I.acc + 1;
     if (gap_out) gap_out[b] = gap;
   }
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_bonus_partial(
+    int B, int L, int V, int chunk, int nc, const T* __restrict__ tl, int64_t ts,
+    const T* __restrict__ dl, int64_t ds, float a, int row_nc, const float2* __restrict__ part,
+    const int32_t* __restrict__ toks, const int32_t* __restrict__ lens,
+    const float* __restrict__ u, float* __restrict__ ratio_out, ReqInfo* __restrict__ info,
+    float4* __restrict__ rpart) {
+  const int c = blockIdx.x % nc;
+  const int b = blockIdx.x / nc;
+  // every chunk's workgroup runs the (cheap) acceptance scan itself; chunk 0
+  // publishes it for the selection kernel
+  const ReqInfo I = accept_scan<T>(b, B, L, V, row_nc, part, tl, ts, dl, ds, toks, lens, u, a,
+                                   c == 0 ? ratio_out : nullptr);
+  if (c == 0 && threadIdx.x == 0) info[b] = I;
+  if (!I.err) bonus_chunk_sum<T, VEC>(c, chunk, V, tl, ts, dl, ds, a, b, L, I, rpart);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_bonus_select(
+    int L, int V, int chunk, int nc, const T* __restrict__ tl, int64_t ts,
+    const T* __restrict__ dl, int64_t ds, float a, const ReqInfo* __restrict__ info,
+    const float4* __restrict__ rpart, const float* __restrict__ u2,
+    int32_t* __restrict__ accept_len, int32_t* __restrict__ bonus, int32_t* __restrict__ commit,
+    const int32_t* __restrict__ prefix, int32_t* __restrict__ new_seq,
+    float* __restrict__ beta_out, float* __restrict__ gap_out) {
+  const int b = blockIdx.x;
+  select_bonus<T>(b, L, V, chunk, nc, tl, ts, dl, ds, a, info[b], rpart, u2, accept_len, bonus,
+                  commit, prefix, new_seq, beta_out, gap_out);
 }
 
 // ------------------------------------------------------------------- gate
@@ -603,25 +715,23 @@ void sample_impl(int B, int L, int V, const void* tl, int64_t ts, const void* dl
   const float a = kLog2e / temperature;
   RowSet s0{tl, ts, L + 1, 1}, s1{dl, ds, L, 0};
   launch_lse<T, VEC>(s0, s1, B, L, V, lens, a, pl, rows, part, st);
-  hipLaunchKernelGGL((k_sample_accept<T>), dim3(B), dim3(128), 0, st, B, L, V, pl.n_chunks, part,
-                     static_cast<const T*>(tl), ts, static_cast<const T*>(dl), ds, toks, lens, u,
-                     a, ratio_out, info);
   hipLaunchKernelGGL((k_bonus_partial<T, VEC>), dim3(B * pr.n_chunks), dim3(kThreads), 0, st, B,
                      L, V, pr.chunk, pr.n_chunks, static_cast<const T*>(tl), ts,
-                     static_cast<const T*>(dl), ds, a, info, rpart);
-  hipLaunchKernelGGL((k_bonus_select<T>), dim3(B), dim3(kThreads), 0, st, B, L, V, pr.chunk,
-                     pr.n_chunks, static_cast<const T*>(tl), ts, static_cast<const T*>(dl), ds,
-                     a, info, rpart, u2, acc, bonus, commit, prefix, new_seq, beta_out, gap_out);
+                     static_cast<const T*>(dl), ds, a, pl.n_chunks, part, toks, lens, u, ratio_out,
+                     info, rpart);
+  hipLaunchKernelGGL((k_bonus_select<T>), dim3(B), dim3(kThreads), 0, st, L, V, pr.chunk,
+                     pr.n_chunks, static_cast<const T*>(tl), ts, static_cast<const T*>(dl), ds, a,
+                     info, rpart, u2, acc, bonus, commit, prefix, new_seq, beta_out, gap_out);
 }
 
 }  // namespace
 
 VocabPlan plan_vocab(int64_t n_rows, int V) {
-  // About 4096 workgroups per launch, chunks of at least 2048 elements, at
+  // About DFLASH_VOCAB_WGS workgroups per launch, chunks of at least 2048 elements, at
   // most kMaxChunks chunks per row; chunk boundaries are multiples of 8 so
   // that 16-byte loads stay aligned.
   const int64_t rows = n_rows > 0 ? n_rows : 1;
-  const int64_t want = std::max<int64_t>(1, cdiv(4096, rows));
+  const int64_t want = std::max<int64_t>(1, cdiv(DFLASH_VOCAB_WGS, rows));
   int64_t chunk = std::max<int64_t>(cdiv(V, want), 2048);
   chunk = cdiv(chunk, 8) * 8;
   int64_t n = cdiv(V, chunk);
