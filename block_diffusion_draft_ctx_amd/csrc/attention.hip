@@ -181,18 +181,18 @@ void k_attn_bf16(AttnP p) {
   // (context slot, block key, or -- past the last key -- a clamped block key
   // whose score is masked), so no load waits on another.
   u32x4 kr[CPT], vr[CPT];
-  auto fetch = [&](int tile) __attribute__((always_inline)) {
+  auto fetch = [&](int tile, u32x4 (&kr_)[CPT], u32x4 (&vr_)[CPT]) __attribute__((always_inline)) {
     const int pbase = (tile - t0) * (kKT / 16);
     if (tile * kKT + kKT <= C) {     // the whole tile is context (uniform)
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         const int64_t off = (int64_t)pages[pbase + (kc[c] >> 4)] * page_elems + coff[c];
 #if DFLASH_ATTN_NT
-        kr[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.ck + off));
-        vr[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.cv + off));
+        kr_[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.ck + off));
+        vr_[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.cv + off));
 #else
-        kr[c] = *reinterpret_cast<const u32x4*>(p.ck + off);
-        vr[c] = *reinterpret_cast<const u32x4*>(p.cv + off);
+        kr_[c] = *reinterpret_cast<const u32x4*>(p.ck + off);
+        vr_[c] = *reinterpret_cast<const u32x4*>(p.cv + off);
 #endif
       }
     } else {
@@ -204,8 +204,8 @@ void k_attn_bf16(AttnP p) {
         const bool in_ctx = kp < C;
         const uint16_t* pk = in_ctx ? p.ck + off_c : kblk + off_b;
         const uint16_t* pv = in_ctx ? p.cv + off_c : vblk + off_b;
-        kr[c] = *reinterpret_cast<const u32x4*>(pk);
-        vr[c] = *reinterpret_cast<const u32x4*>(pv);
+        kr_[c] = *reinterpret_cast<const u32x4*>(pk);
+        vr_[c] = *reinterpret_cast<const u32x4*>(pv);
       }
     }
   };
@@ -226,31 +226,22 @@ void k_attn_bf16(AttnP p) {
   const int tr_r = (lane & 15) >> 2, tr_q = lane & 3;
   const int grp16 = lane >> 4;             // 16-lane group: d offset 16*(grp16&1), key half hh
 
-  auto stage = [&](uint16_t* Kd) __attribute__((always_inline)) {
+  auto stage = [&](uint16_t* Kd, const u32x4 (&kr_)[CPT], const u32x4 (&vr_)[CPT]) __attribute__((always_inline)) {
     uint16_t* Vd = Kd + kKT * KS;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int e = threadIdx.x + c * NT;
       if (NCH % NT == 0 || e < NCH) {
         const int dc = e - kc[c] * CPR;
-        *reinterpret_cast<u32x4*>(Kd + kc[c] * KS + dc * 8) = kr[c];
-        *reinterpret_cast<u32x4*>(Vd + kc[c] * VS + dc * 8) = vr[c];
+        *reinterpret_cast<u32x4*>(Kd + kc[c] * KS + dc * 8) = kr_[c];
+        *reinterpret_cast<u32x4*>(Vd + kc[c] * VS + dc * 8) = vr_[c];
       }
     }
   };
 
-  // Pipeline, one barrier per tile: compute tile t from one LDS stage while
-  // tile t+1 (fetched one step earlier) waits in registers; then stage it
-  // into the other LDS stage and fetch tile t+2.
-  if (t0 < t1) {
-    fetch(t0);
-    stage(smem);
-    if (t0 + 1 < t1) fetch(t0 + 1);
-  }
-  __syncthreads();
-  for (int tile = t0; tile < t1; ++tile) {
-    const int cur = (tile - t0) & 1;
-    const uint16_t* Ks = smem + cur * STAGE;
+  // One 64-key tile from the LDS stage at Ks: scores, online softmax, and the
+  // P.V accumulation for this wave's query slice and key half.
+  auto compute = [&](const uint16_t* Ks, int tile) __attribute__((always_inline)) {
     const uint16_t* Vs = Ks + kKT * KS;
     // S^T[32 keys x 32 q] for this wave's key half
     f32x16 sacc;
@@ -315,13 +306,26 @@ void k_attn_bf16(AttnP p) {
         acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[mb], 0, 0, 0);
       }
     }
+  };
+
+  // Pipeline, one barrier per tile: compute tile t from one LDS stage while
+  // tile t+1 (fetched one step earlier) waits in registers; then stage it
+  // into the other LDS stage and fetch tile t+2.
+  if (t0 < t1) {
+    fetch(t0, kr, vr);
+    stage(smem, kr, vr);
+    if (t0 + 1 < t1) fetch(t0 + 1, kr, vr);
+  }
+  __syncthreads();
+  for (int tile = t0; tile < t1; ++tile) {
+    const int cur = (tile - t0) & 1;
+    compute(smem + cur * STAGE, tile);
     if (tile + 1 < t1) {
-      stage(smem + (cur ^ 1) * STAGE);
-      if (tile + 2 < t1) fetch(tile + 2);
+      stage(smem + (cur ^ 1) * STAGE, kr, vr);
+      if (tile + 2 < t1) fetch(tile + 2, kr, vr);
     }
     __syncthreads();
   }
-
   // Merge the two key halves: wave (wq, 1) hands its state to wave (wq, 0)
   // through LDS, one query slice at a time.
   float* xo = reinterpret_cast<float*>(smem);          // [64 lanes][D/2] partial O
