@@ -432,7 +432,7 @@ def bench_packed(args):
     bf = torch.bfloat16
     npg = seq // 16
     perm = torch.randperm(npg, generator=g, device=dev).to(torch.int32)
-    bt = perm.view(1, npg).repeat(nb, 1).contiguous()
+    bt = perm.view(1, npg).contiguous()   # one shared row: every block reads the sequence
     ck = torch.randn(npg, 16, Hkv, D, generator=g, device=dev).to(bf)
     cv = torch.randn(npg, 16, Hkv, D, generator=g, device=dev).to(bf)
     q = torch.randn(nb, kk, Hq, D, generator=g, device=dev).to(bf)

@@ -62,7 +62,8 @@ def _declare(lib):
     lib.dflash_attention_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, I32]
     lib.dflash_block_attention.restype = I32
     lib.dflash_block_attention.argtypes = [
-        I32, I32, I32, I32, I32, P, P, P, P, P, I32, I32, P, I32, P, F, P, P, I32, I32, P, SZ, P]
+        I32, I32, I32, I32, I32, P, P, P, P, P, I32, I32, P, I32, I32, P, F, P, P, I32, I32, P, SZ,
+        P]
     lib.dflash_verify_workspace_size.restype = SZ
     lib.dflash_verify_workspace_size.argtypes = [I32, I32, I32]
     lib.dflash_verify_greedy.restype = I32
@@ -201,7 +202,8 @@ def materialize_ctx_kv(hiddens: Sequence, W_f, b_f, W_K: Sequence, W_V: Sequence
 def block_attention(q, k_blk, v_blk, cache_k, cache_v, block_table, ctx_lens, scale=0.0,
                     out=None, lse=None, workspace=None, stream=None, out_dtype=None):
     """dflash_block_attention.  q [B,k,Hq,D]; k_blk/v_blk [B,k,Hkv,D]; caches
-    [num_pages,16,Hkv,D]; block_table [B,max_pages]; ctx_lens [B].  The output
+    [num_pages,16,Hkv,D]; block_table [B,max_pages], or [1,max_pages] when
+    every request reads the same (packed) sequence; ctx_lens [B].  The output
     takes the dtype of ``out`` (or ``out_dtype``, default: q's dtype).  Returns
     (out, lse) where lse is the tensor given (or None)."""
     torch = _torch()
@@ -223,7 +225,8 @@ def block_attention(q, k_blk, v_blk, cache_k, cache_v, block_table, ctx_lens, sc
     s = L.dflash_block_attention(
         B, k, Hq, Hkv, D, _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(cache_k), _ptr(cache_v),
         cache_k.shape[0], cache_k.shape[1], _ptr(block_table), block_table.shape[1],
-        _ptr(ctx_lens), float(scale), _ptr(out), _ptr(lse), dt, odt, _ptr(ws), nws,
+        block_table.shape[0], _ptr(ctx_lens), float(scale), _ptr(out), _ptr(lse), dt, odt,
+        _ptr(ws), nws,
         _stream(stream))
     _check(s, "dflash_block_attention")
     return out, lse

@@ -59,6 +59,7 @@ struct AttnP {
   int num_pages;
   const int32_t* bt;
   int max_pages;
+  int bt_stride;  // elements between block-table rows (0: every request reads row 0)
   const int32_t* ctx;
   float sl2;  // softmax scale * log2(e)
   void* out;  // bf16 or fp32 (out_f32)
@@ -150,7 +151,7 @@ void k_attn_bf16(AttnP p) {
   const int pg0 = t0 * (kKT / 16);
   const int pg1 = min((t1 * kKT + 15) >> 4, (C + 15) >> 4);
   {
-    const int32_t* btr = p.bt + (int64_t)b * p.max_pages;
+    const int32_t* btr = p.bt + (int64_t)b * p.bt_stride;
     bool bad = false;
     for (int i = pg0 + (int)threadIdx.x; i < pg1; i += NT) {
       int pg = btr[i];
@@ -430,7 +431,7 @@ template <int D>
 __global__ __launch_bounds__(64) void k_attn_f32(int B, int k, int Hq, int Hkv, const float* q,
                                                  const float* kb, const float* vb,
                                                  const float* ck, const float* cv, int num_pages,
-                                                 const int32_t* bt, int max_pages,
+                                                 const int32_t* bt, int max_pages, int bt_stride,
                                                  const int32_t* ctx, float sl2, float* out,
                                                  float* lse, int S, float* po, float2* pml) {
   const int i = blockIdx.x % k;
@@ -452,7 +453,7 @@ __global__ __launch_bounds__(64) void k_attn_f32(int B, int k, int Hq, int Hkv, 
     const float* kr;
     const float* vr;
     if (j < C) {
-      const int page = bt[(int64_t)b * max_pages + (j >> 4)];
+      const int page = bt[(int64_t)b * bt_stride + (j >> 4)];
       if (page < 0 || page >= num_pages) { poison = true; continue; }
       const int64_t off = (((int64_t)page * 16 + (j & 15)) * Hkv + g) * D;
       kr = ck + off; vr = cv + off;
@@ -548,7 +549,8 @@ hipError_t launch_attention(bool bf16, const AttnArgs& a, void* ws, hipStream_t 
             static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_blk),
             static_cast<const uint16_t*>(a.v_blk), static_cast<const uint16_t*>(a.cache_k),
             static_cast<const uint16_t*>(a.cache_v), a.num_pages, a.block_table, a.max_pages,
-            a.ctx_lens, scale * kLog2e, a.out, a.out_f32 ? 1 : 0, a.lse, po, pml, S};
+            a.shared_table ? 0 : a.max_pages, a.ctx_lens, scale * kLog2e, a.out,
+            a.out_f32 ? 1 : 0, a.lse, po, pml, S};
     if (a.D == 64) dispatch_nw<64>(a, p, st);
     else dispatch_nw<128>(a, p, st);
     if (S > 1) {
@@ -568,15 +570,15 @@ hipError_t launch_attention(bool bf16, const AttnArgs& a, void* ws, hipStream_t 
                          static_cast<const float*>(a.q), static_cast<const float*>(a.k_blk),
                          static_cast<const float*>(a.v_blk), static_cast<const float*>(a.cache_k),
                          static_cast<const float*>(a.cache_v), a.num_pages, a.block_table,
-                         a.max_pages, a.ctx_lens, scale * kLog2e, static_cast<float*>(a.out), a.lse,
-                         1, nullptr, nullptr);
+                         a.max_pages, a.shared_table ? 0 : a.max_pages, a.ctx_lens,
+                         scale * kLog2e, static_cast<float*>(a.out), a.lse, 1, nullptr, nullptr);
     else
       hipLaunchKernelGGL((k_attn_f32<128>), dim3(grid), dim3(64), 0, st, a.B, a.k, a.Hq, a.Hkv,
                          static_cast<const float*>(a.q), static_cast<const float*>(a.k_blk),
                          static_cast<const float*>(a.v_blk), static_cast<const float*>(a.cache_k),
                          static_cast<const float*>(a.cache_v), a.num_pages, a.block_table,
-                         a.max_pages, a.ctx_lens, scale * kLog2e, static_cast<float*>(a.out), a.lse,
-                         1, nullptr, nullptr);
+                         a.max_pages, a.shared_table ? 0 : a.max_pages, a.ctx_lens,
+                         scale * kLog2e, static_cast<float*>(a.out), a.lse, 1, nullptr, nullptr);
   }
   return hipGetLastError();
 }

@@ -59,6 +59,7 @@ struct AttnArgs {
   int num_pages;
   const int32_t* block_table;
   int max_pages;
+  bool shared_table;  // every request reads block-table row 0
   const int32_t* ctx_lens;
   float scale;
   void* out;

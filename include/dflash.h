@@ -142,7 +142,8 @@ dflash_status dflash_materialize_ctx_kv(
  * causal mask, to [K_ctx; K_blk] and [V_ctx; V_blk]; section "随机锚点采样":
  * in packed training each block sees the injected context of positions before
  * its anchor and only its own block (map each block to one request whose
- * block-table row lists the sequence's pages and whose ctx_len is its anchor).
+ * ctx_len is its anchor, all requests reading the one sequence's block-table
+ * row: table_rows = 1).
  *
  * For request b, q-head h (kv-head h / (Hq/Hkv)), block position i:
  *   keys   = cache K at logical positions [0, ctx_lens[b]) ++ k_blk[b, 0:k]
@@ -150,7 +151,9 @@ dflash_status dflash_materialize_ctx_kv(
  *
  * q            [B, k, Hq, D]      k_blk, v_blk  [B, k, Hkv, D]
  * cache_k/v    [num_pages, 16, Hkv, D]
- * block_table  [B, max_pages_per_seq] int32;  ctx_lens [B] int32 (0 allowed)
+ * block_table  [table_rows, max_pages_per_seq] int32;  ctx_lens [B] int32 (0 allowed)
+ * table_rows   B (request b reads row b) or 1 (every request reads row 0:
+ *              the blocks of one packed sequence)
  * scale        softmax scale; 0 means 1/sqrt(D)
  * out          [B, k, Hq, D] in out_dtype (DFLASH_BF16 needs bf16 inputs;
  *              DFLASH_F32 keeps the fp32 result unrounded);
@@ -168,8 +171,8 @@ dflash_status dflash_block_attention(
     int B, int k, int n_q_heads, int n_kv_heads, int head_dim,
     const void* q, const void* k_blk, const void* v_blk,
     const void* cache_k, const void* cache_v, int num_pages, int page_size,
-    const int32_t* block_table, int max_pages_per_seq, const int32_t* ctx_lens,
-    float scale, void* out, float* lse_out,
+    const int32_t* block_table, int max_pages_per_seq, int table_rows,
+    const int32_t* ctx_lens, float scale, void* out, float* lse_out,
     dflash_dtype dtype, dflash_dtype out_dtype, void* ws, size_t ws_bytes,
     dflash_stream_t stream);
 

@@ -172,3 +172,70 @@ def test_attention_in_band_errors():
     o = down(out)
     assert np.isnan(o[0]).all() and np.isnan(o[2]).all() and np.isfinite(o[1]).all()
     assert np.isnan(down(lse)[0]).all() and np.isfinite(down(lse)[1]).all()
+
+
+def _run_shared(c, out_dtype=None):
+    """The same case through a one-row block table (every request reads row 0)."""
+    import torch
+    kind = c.dtype
+    assert (c.block_table == c.block_table[:1]).all()
+    q = up(c.q, kind)
+    lse = torch.empty((c.B, c.n_q_heads, c.k), dtype=torch.float32, device=q.device)
+    od = {"f32": torch.float32, "bf16": torch.bfloat16, None: None}[out_dtype]
+    return dfl.block_attention(q, up(c.k_blk, kind), up(c.v_blk, kind), up(c.cache_k, kind),
+                               up(c.cache_v, kind), up(c.block_table[:1], "i32"),
+                               up(c.ctx_lens, "i32"), lse=lse, out_dtype=od)
+
+
+def _shared_case(seed, B, ctx, Hq=32, Hkv=8, D=128, k=16):
+    """A case whose block-table rows all list the same sequence's pages."""
+    c = synth.attention_case(seed, dtype="bf16", B=B, k=k, n_q_heads=Hq, n_kv_heads=Hkv,
+                             head_dim=D, ctx_lens=[max(ctx)] * B)
+    c.block_table[:] = c.block_table[:1]
+    c.ctx_lens[:] = np.asarray(ctx, dtype=np.int32)
+    return c
+
+
+@pytest.mark.parametrize("B,ctx,Hq,Hkv,D,seed", [
+    (5, [100, 37, 0, 260, 64], 32, 8, 128, 2360),       # unsorted, ragged, a zero context
+    (4, [1000, 1003, 17, 500], 32, 8, 128, 2361),
+    (3, [64, 65, 130], 16, 4, 64, 2362),                 # D = 64
+    (2, [300, 301], 64, 8, 128, 2363),                   # G = 8
+])
+def test_attention_shared_table(B, ctx, Hq, Hkv, D, seed):
+    """One block-table row shared by every request (table_rows = 1): each
+    request must match the oracle on its own context length."""
+    log(f"attention shared table B={B} ctx={ctx} Hq={Hq} Hkv={Hkv} D={D}")
+    c = _shared_case(seed, B, ctx, Hq, Hkv, D)
+    for od in ("f32", "bf16"):
+        out, lse = _run_shared(c, out_dtype=od)
+        _check(c, out, lse)
+
+
+def test_attention_packed_training_mask_shared_table_sampled():
+    """The packed training sequence through one shared table row (blocks in
+    anchor order); sampled blocks at both ends and in the middle."""
+    c, P = synth.packed_attention_case(2330, dtype="bf16", seq_len=8192, k=16, n_q_heads=32,
+                                       n_kv_heads=8, head_dim=128, max_anchors=512)
+    log(f"packed shared table: {c.B} blocks, prompt {P}")
+    sel = [0, 1, c.B // 2 - 1, c.B // 2, c.B - 2, c.B - 1]
+    out, lse = _run_shared(c, out_dtype="f32")
+    assert np.isfinite(down(out)).all()
+    _check(c, out, lse, sel=sel)
+
+
+def test_attention_shared_table_bad_page_poisons_only_its_readers():
+    """A bad entry in the shared row poisons the requests whose context
+    reaches it and no other."""
+    c = _shared_case(2364, 4, [40, 200, 20, 200])
+    bt = c.block_table[:1].copy()
+    bt[0, 5] = c.cache_k.shape[0] + 3          # positions 80..95: read by requests 1 and 3
+    import torch
+    lse = torch.empty((4, 32, 16), dtype=torch.float32, device="cuda:0")
+    out, lse = dfl.block_attention(up(c.q, "bf16"), up(c.k_blk, "bf16"), up(c.v_blk, "bf16"),
+                                   up(c.cache_k, "bf16"), up(c.cache_v, "bf16"), up(bt, "i32"),
+                                   up(c.ctx_lens, "i32"), lse=lse, out_dtype=torch.float32)
+    o = down(out)
+    assert np.isnan(o[1]).all() and np.isnan(o[3]).all()
+    assert np.isfinite(o[0]).all() and np.isfinite(o[2]).all()
+    _check(c, out, lse, sel=[0, 2])
