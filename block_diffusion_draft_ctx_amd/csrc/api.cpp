@@ -95,7 +95,8 @@ dflash_status dflash_materialize_ctx_kv(
     if (!W_K[l] || !W_V[l] || !caches[l].k || !caches[l].v) return DFLASH_E_ARG;
     if (caches[l].page_size != 16) return DFLASH_E_UNSUPPORTED;
     if (caches[l].num_pages < 1) return DFLASH_E_ARG;
-    if (bf16 && (!al16(W_K[l]) || !al16(W_V[l]))) return DFLASH_E_UNSUPPORTED;
+    if (bf16 && (!al16(W_K[l]) || !al16(W_V[l]) || !al16(caches[l].k) || !al16(caches[l].v)))
+      return DFLASH_E_UNSUPPORTED;
     a.W_K[l] = W_K[l]; a.W_V[l] = W_V[l];
     a.cache_k[l] = caches[l].k; a.cache_v[l] = caches[l].v;
     a.num_pages[l] = caches[l].num_pages;

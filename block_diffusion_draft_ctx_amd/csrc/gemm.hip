@@ -576,10 +576,50 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmP p) {
   }
 }
 
-// Sum the split-K partials in split order, then the final epilogue.
+// Sum the split-K partials in split order, then the final epilogue.  With
+// bf16 storage and N a multiple of 8, a thread takes 8 consecutive columns of
+// one row: vector loads of the partials, one cache-slot lookup, one 16-byte
+// store (8 columns never straddle a layer or K/V block: HD is a multiple of
+// 128).
 template <typename T, int EPI>
 __global__ __launch_bounds__(256) void k_splitk_reduce(GemmP p) {
   const int64_t total = (int64_t)p.M * p.N;
+  if (sizeof(T) == 2 && p.N % 8 == 0) {
+    const int n8 = p.N / 8;
+    const int64_t total8 = (int64_t)p.M * n8;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total8; e += (int64_t)gridDim.x * 256) {
+      const int row = (int)(e / n8);
+      const int col = (int)(e - (int64_t)row * n8) * 8;
+      const int64_t base = (int64_t)row * p.N + col;
+      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < p.ksplit; ++s) {
+        const f32x4v* src = reinterpret_cast<const f32x4v*>(p.part + (int64_t)s * total + base);
+        const f32x4v lo = src[0], hi = src[1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { v[j] += lo[j]; v[4 + j] += hi[j]; }
+      }
+      uint16_t* dst;
+      if (EPI == EPI_DENSE) {
+        if (p.bias) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] += bf16_to_f32(static_cast<const uint16_t*>(p.bias)[col + j]);
+        }
+        dst = static_cast<uint16_t*>(p.out) + base;
+      } else {
+        const int l = col / (2 * p.HD);
+        const int64_t slot = row_slot(p, row, l);
+        if (slot < 0) continue;
+        const int kv = (col / p.HD) & 1;
+        const int hd = col - (col / p.HD) * p.HD;
+        dst = static_cast<uint16_t*>(kv ? pick(p.cv, l) : pick(p.ck, l)) + slot * p.HD + hd;
+      }
+      u32x4 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
+      *reinterpret_cast<u32x4*>(dst) = o;
+    }
+    return;
+  }
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
     const int row = (int)(e / p.N);
     const int col = (int)(e - (int64_t)row * p.N);
@@ -604,18 +644,22 @@ Plan plan_gemm(int64_t M, int64_t N, int64_t K, bool bf16) {
     int64_t kchunk = cdiv(cdiv(K, ks), 16) * 16;
     return Plan{64, 64, (int)cdiv(K, kchunk), (int)kchunk};
   }
-  // 256 x 256 tiles when they alone give every CU a workgroup; else the
-  // smaller tile, and split the contraction until about DFLASH_GEMM_WGS
-  // workgroups exist.
-  int bm = 256, bn = 256;
-  if (N % 256 != 0 || cdiv(M, 256) * (N / 256) < DFLASH_GEMM_BIG_MIN_TILES) {
-    bm = DFLASH_GEMM_SMALL_BM;
-    bn = 128;
-  }
+  // 256 x 256 tiles (one workgroup per CU) when they alone give every CU a
+  // workgroup, or when splitting the contraction over the CUs keeps every
+  // split at least 4096 columns long; else 128-row tiles, the contraction
+  // split until about DFLASH_GEMM_WGS workgroups exist.  (Per CU the operand
+  // feed from L2 bounds a tile's rate, and a 256 x 256 tile does twice the
+  // work per byte of a 128 x 128 one; short splits lose to their partials.)
+  const int64_t t256 = N % 256 == 0 ? cdiv(M, 256) * (N / 256) : 0;
+  const bool big = t256 > 0 && (t256 >= DFLASH_GEMM_BIG_MIN_TILES ||
+                                K / cdiv(DFLASH_GEMM_BIG_MIN_TILES, t256) >= 4096);
+  const int bm = big ? 256 : DFLASH_GEMM_SMALL_BM;
+  const int bn = big ? 256 : 128;
+  const int64_t target = big ? DFLASH_GEMM_BIG_MIN_TILES : DFLASH_GEMM_WGS;
   const int64_t tiles = cdiv(M, bm) * (N / bn);
   int64_t ks = 1;
-  if (tiles < DFLASH_GEMM_WGS)
-    ks = std::min<int64_t>(cdiv(DFLASH_GEMM_WGS, tiles), std::max<int64_t>(1, K / (4 * BK)));
+  if (tiles < target)
+    ks = std::min<int64_t>(cdiv(target, tiles), std::max<int64_t>(1, K / (4 * BK)));
   const int64_t kchunk = cdiv(cdiv(K, ks), BK) * BK;
   ks = cdiv(K, kchunk);
   return Plan{bm, bn, (int)ks, (int)kchunk};

@@ -157,15 +157,16 @@ def test_attention_argument_errors(lib, kw, code):
     (dict(m=9), dfl.E_UNSUPPORTED), (dict(D=80), dfl.E_UNSUPPORTED), (dict(d=200), dfl.E_UNSUPPORTED),
     (dict(rps=5), dfl.E_ARG), (dict(T=-2), dfl.E_ARG), (dict(page=32), dfl.E_UNSUPPORTED),
     (dict(hid0=None), dfl.E_ARG), (dict(wf=None), dfl.E_ARG), (dict(nws=0), dfl.E_WORKSPACE),
+    (dict(ck=FAKE + 2), dfl.E_UNSUPPORTED),    # bf16 caches take 16-byte stores
 ])
 def test_materialize_argument_errors(lib, kw, code):
-    a = dict(T=32, m=2, d=256, D=128, rps=16, page=16, hid0=FAKE, wf=FAKE, nws=1 << 26)
+    a = dict(T=32, m=2, d=256, D=128, rps=16, page=16, hid0=FAKE, wf=FAKE, nws=1 << 26, ck=FAKE)
     a.update(kw)
     m = a["m"]
     hid = (ctypes.c_void_p * max(m, 1))(*([a["hid0"]] + [FAKE] * (m - 1)))
     wk = (ctypes.c_void_p * 1)(FAKE)
     wv = (ctypes.c_void_p * 1)(FAKE)
-    caches = (dfl.KVLayer * 1)(dfl.KVLayer(FAKE, FAKE, 8, a["page"]))
+    caches = (dfl.KVLayer * 1)(dfl.KVLayer(a["ck"], FAKE, 8, a["page"]))
     s = lib.dflash_materialize_ctx_kv(a["T"], m, a["d"], ctypes.cast(hid, dfl.PP), a["wf"], None,
                                       1, 1, a["D"], ctypes.cast(wk, dfl.PP), ctypes.cast(wv, dfl.PP),
                                       caches, FAKE, 4, a["rps"], FAKE, None, None, dfl.BF16, WS,
