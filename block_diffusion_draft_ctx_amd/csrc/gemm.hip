@@ -70,9 +70,13 @@ constexpr int BK = 64;   // granularity of split-K chunks (a multiple of the pip
 #ifndef DFLASH_GEMM_SMALL_WN
 #define DFLASH_GEMM_SMALL_WN 2
 #endif
-// Fewest 256 x 256 tiles (before split-K) for which that tile is used.
+// Workgroups a 256 x 256 split-K aims for (one per CU), and the fewest
+// 256 x 256 tiles that are used without a split.
 #ifndef DFLASH_GEMM_BIG_MIN_TILES
 #define DFLASH_GEMM_BIG_MIN_TILES 256
+#endif
+#ifndef DFLASH_GEMM_BIG_UNSPLIT_MIN
+#define DFLASH_GEMM_BIG_UNSPLIT_MIN 128
 #endif
 // Rotation of each tile's contraction start, in elements per workgroup
 // (0: every tile starts at the beginning of its range).
@@ -644,22 +648,28 @@ Plan plan_gemm(int64_t M, int64_t N, int64_t K, bool bf16) {
     int64_t kchunk = cdiv(cdiv(K, ks), 16) * 16;
     return Plan{64, 64, (int)cdiv(K, kchunk), (int)kchunk};
   }
-  // 256 x 256 tiles (one workgroup per CU) when they alone give every CU a
-  // workgroup, or when splitting the contraction over the CUs keeps every
-  // split at least 4096 columns long; else 128-row tiles, the contraction
-  // split until about DFLASH_GEMM_WGS workgroups exist.  (Per CU the operand
-  // feed from L2 bounds a tile's rate, and a 256 x 256 tile does twice the
-  // work per byte of a 128 x 128 one; short splits lose to their partials.)
+  // Per CU the operand feed from L2 bounds a tile's rate, and a 256 x 256
+  // tile does twice the work per byte of a 128 x 128 one, so 256 x 256 is
+  // preferred:
+  //  * split over the contraction to one workgroup per CU when every split
+  //    stays at least 4096 columns long (shorter splits lose to their
+  //    partials), or whole when the tiles alone fill the CUs;
+  //  * unsplit when at least DFLASH_GEMM_BIG_UNSPLIT_MIN tiles exist;
+  //  * else 128-row tiles, the contraction split until about
+  //    DFLASH_GEMM_WGS workgroups exist.
+  constexpr int64_t kCUs = DFLASH_GEMM_BIG_MIN_TILES;
   const int64_t t256 = N % 256 == 0 ? cdiv(M, 256) * (N / 256) : 0;
-  const bool big = t256 > 0 && (t256 >= DFLASH_GEMM_BIG_MIN_TILES ||
-                                K / cdiv(DFLASH_GEMM_BIG_MIN_TILES, t256) >= 4096);
-  const int bm = big ? 256 : DFLASH_GEMM_SMALL_BM;
-  const int bn = big ? 256 : 128;
-  const int64_t target = big ? DFLASH_GEMM_BIG_MIN_TILES : DFLASH_GEMM_WGS;
+  const bool split_ok = t256 > 0 && K / cdiv(kCUs, t256) >= 4096;
+  if (split_ok || t256 >= DFLASH_GEMM_BIG_UNSPLIT_MIN) {
+    const int64_t ks0 = split_ok ? cdiv(kCUs, t256) : 1;
+    const int64_t kchunk = cdiv(cdiv(K, ks0), BK) * BK;
+    return Plan{256, 256, (int)cdiv(K, kchunk), (int)kchunk};
+  }
+  const int bm = DFLASH_GEMM_SMALL_BM, bn = 128;
   const int64_t tiles = cdiv(M, bm) * (N / bn);
   int64_t ks = 1;
-  if (tiles < target)
-    ks = std::min<int64_t>(cdiv(target, tiles), std::max<int64_t>(1, K / (4 * BK)));
+  if (tiles < DFLASH_GEMM_WGS)
+    ks = std::min<int64_t>(cdiv(DFLASH_GEMM_WGS, tiles), std::max<int64_t>(1, K / (4 * BK)));
   const int64_t kchunk = cdiv(cdiv(K, ks), BK) * BK;
   ks = cdiv(K, kchunk);
   return Plan{bm, bn, (int)ks, (int)kchunk};
