@@ -67,6 +67,9 @@ constexpr int BK = 64;   // granularity of split-K chunks (a multiple of the pip
 #ifndef DFLASH_GEMM_BIG_WN
 #define DFLASH_GEMM_BIG_WN 4
 #endif
+#ifndef DFLASH_GEMM_BIG_WM
+#define DFLASH_GEMM_BIG_WM 2
+#endif
 #ifndef DFLASH_GEMM_SMALL_WN
 #define DFLASH_GEMM_SMALL_WN 2
 #endif
@@ -692,7 +695,7 @@ void run_gemm(bool bf16, GemmP p, int epi_final, hipStream_t st) {
   if (bf16) {
     const dim3 grid((unsigned)(cdiv(p.M, pl.bm) * (p.N / pl.bn)), (unsigned)pl.ksplit);
     if (pl.bm == 256 && pl.bn == 256)
-      launch_bf16_gemm<256, 256, 2, DFLASH_GEMM_BIG_WN, DFLASH_GEMM_KB_BIG, DFLASH_GEMM_NSTG_BIG>(p, epi, grid, st);
+      launch_bf16_gemm<256, 256, DFLASH_GEMM_BIG_WM, DFLASH_GEMM_BIG_WN, DFLASH_GEMM_KB_BIG, DFLASH_GEMM_NSTG_BIG>(p, epi, grid, st);
     else if (pl.bm == 256)
       launch_bf16_gemm<256, 128, 2, 2, DFLASH_GEMM_KB_SMALL, DFLASH_GEMM_NSTG_SMALL>(p, epi, grid, st);
     else
