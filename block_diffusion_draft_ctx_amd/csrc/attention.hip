@@ -22,6 +22,7 @@
 // factor; the two key halves merge through LDS at the end.  Small batches
 // split the context across workgroups and a second kernel merges the splits
 // by their log-sum-exp.
+#include <climits>
 #include <cmath>
 
 #include "common.h"
@@ -40,6 +41,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #endif
 #ifndef DFLASH_ATTN_TARGET_WGS
 #define DFLASH_ATTN_TARGET_WGS 512
+#endif
+#ifndef DFLASH_ATTN_PAIR
+#define DFLASH_ATTN_PAIR 1     // two requests per workgroup on a shared table row
 #endif
 #ifndef DFLASH_ATTN_NT
 #define DFLASH_ATTN_NT 1
@@ -65,9 +69,10 @@ struct AttnP {
   void* out;  // bf16 or fp32 (out_f32)
   int out_f32;
   float* lse;
-  float* po;    // split partials: O [B*Hkv*S*Mq, D] fp32
-  float2* pml;  // split partials: (m, l) [B*Hkv*S*Mq]
+  float* po;    // split partials: O [B*Hkv*S*G*k, D] fp32, one row set per request
+  float2* pml;  // split partials: (m, l) [B*Hkv*S*G*k]
   int S;        // ctx splits
+  int RC;       // query-row chunks per (request, kv-head): more rows than one workgroup holds
 };
 
 // Transposing LDS read (gfx950): within each 16-lane group, output lane j
@@ -85,12 +90,19 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// One workgroup = (request, kv-head, ctx split); 2*NQ wavefronts arranged as
-// NQ query slices of 32 rows x 2 key halves.  Per 64-key tile, wave
+// One workgroup = (request, kv-head, query-row chunk, ctx split); 2*NQ
+// wavefronts arranged as NQ query slices of 32 rows x 2 key halves (a
+// request with more than 32*NQ rows per kv-head takes several chunks).
+// With NB = 2 (requests reading
+// one shared block-table row: packed training blocks) a workgroup owns two
+// consecutive requests of one kv-head: it streams the context once, up to
+// the longer of their ctx lengths, then both blocks' own keys, and every
+// query row masks the keys its request does not see; it also keeps two key
+// tiles in flight instead of one.  Per 64-key tile, wave
 // (wq, wk) computes S^T for keys [32wk, 32wk+32) against its 32 query rows
 // and accumulates O^T over the same keys (MFMA 32x32x16 bf16), with its own
 // online-softmax state; the two key halves are merged once at the end.
-template <int D, int NQ>
+template <int D, int NQ, int NB>
 __global__ __launch_bounds__(NQ * 128) __attribute__((amdgpu_waves_per_eu(2)))
 void k_attn_bf16(AttnP p) {
   constexpr int NW = 2 * NQ;
@@ -111,19 +123,25 @@ void k_attn_bf16(AttnP p) {
   __shared__ int pages[kMaxSplitPages];
 
   const int split = blockIdx.x % p.S;
-  const int g = (blockIdx.x / p.S) % p.Hkv;
-  const int b = blockIdx.x / (p.S * p.Hkv);
+  const int rc = (blockIdx.x / p.S) % p.RC;           // 32*NQ-row chunk of the query rows
+  const int g = (blockIdx.x / (p.S * p.RC)) % p.Hkv;
+  const int b0 = (blockIdx.x / (p.S * p.RC * p.Hkv)) * NB;   // first request of the workgroup
+  const int nbv = min(NB, p.B - b0);                   // requests it owns
   const int G = p.Hq / p.Hkv;
   const int k = p.k;
-  const int Mq = G * k;
+  const int GK = G * k;                                // query rows per request
+  const int Mq = GK * nbv;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int wq = w >> 1, wk = w & 1;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int qrow = 32 * wq + l32;
+  const int qrow = 32 * NQ * rc + 32 * wq + l32;
   const bool qvalid = qrow < Mq;
-  const int hg = qvalid ? qrow / k : 0;
-  const int pos = qvalid ? qrow - hg * k : 0;
+  const int jb = (NB == 1 || !qvalid) ? 0 : qrow / GK;   // request of this row within the group
+  const int b = b0 + jb;
+  const int rr = qrow - jb * GK;
+  const int hg = qvalid ? rr / k : 0;
+  const int pos = qvalid ? rr - hg * k : 0;
   const int h = g * G + hg;
 
   // B operand of S^T = K . Q^T: lane (q, hh) holds Q[q][16s + 8hh .. +8]
@@ -137,10 +155,26 @@ void k_attn_bf16(AttnP p) {
     }
   }
 
-  int C = p.ctx[b];
-  bool poison = (C < 0 || C > p.max_pages * 16);
-  if (poison) C = 0;
-  const int total = C + k;
+  // Context lengths: this row's request (Crow), and the longest / shortest
+  // of the workgroup's requests (C / Cmin); the key list is the context up
+  // to C followed by the nbv blocks' own keys.
+  int Crow = p.ctx[b];
+  bool poison = (Crow < 0 || Crow > p.max_pages * 16);
+  if (poison) Crow = 0;
+  int C = Crow, Cmin = Crow;
+  if (NB > 1) {
+    C = 0;
+    Cmin = INT_MAX;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      if (j < nbv) {
+        int cj = p.ctx[b0 + j];
+        if (cj < 0 || cj > p.max_pages * 16) cj = 0;
+        C = max(C, cj);
+        Cmin = min(Cmin, cj);
+      }
+  }
+  const int total = C + k * nbv;
   const int nt = (total + kKT - 1) / kKT;
   const int tps = (nt + p.S - 1) / p.S;
   const int t0 = split * tps;
@@ -150,7 +184,7 @@ void k_attn_bf16(AttnP p) {
   // no tile waits on a dependent page-table load.
   const int pg0 = t0 * (kKT / 16);
   const int pg1 = min((t1 * kKT + 15) >> 4, (C + 15) >> 4);
-  {
+  if (NB == 1) {
     const int32_t* btr = p.bt + (int64_t)b * p.bt_stride;
     bool bad = false;
     for (int i = pg0 + (int)threadIdx.x; i < pg1; i += NT) {
@@ -159,6 +193,19 @@ void k_attn_bf16(AttnP p) {
       pages[i - pg0] = pg;
     }
     poison |= __syncthreads_or(bad) != 0;
+  } else {
+    // a bad entry poisons only the rows whose context reaches it
+    __shared__ int first_bad;
+    if (threadIdx.x == 0) first_bad = INT_MAX;
+    __syncthreads();
+    const int32_t* btr = p.bt + (int64_t)b0 * p.bt_stride;
+    for (int i = pg0 + (int)threadIdx.x; i < pg1; i += NT) {
+      int pg = btr[i];
+      if (pg < 0 || pg >= p.num_pages) { atomicMin(&first_bad, i); pg = 0; }
+      pages[i - pg0] = pg;
+    }
+    __syncthreads();
+    poison |= (first_bad != INT_MAX && Crow > first_bad * 16);
   }
 
   // Per-thread chunk geometry is fixed for the whole loop: chunk c of every
@@ -175,8 +222,9 @@ void k_attn_bf16(AttnP p) {
     boff[c] = (int64_t)g * D + dc * 8;
   }
   const int64_t page_elems = (int64_t)16 * p.Hkv * D;
-  const uint16_t* kblk = p.kb + (int64_t)b * k * p.Hkv * D;
-  const uint16_t* vblk = p.vb + (int64_t)b * k * p.Hkv * D;
+  // the group's block keys are consecutive rows of k_blk / v_blk
+  const uint16_t* kblk = p.kb + (int64_t)b0 * k * p.Hkv * D;
+  const uint16_t* vblk = p.vb + (int64_t)b0 * k * p.Hkv * D;
 
   // Branch-free tile fetch: every chunk issues the same two 16-byte loads
   // (context slot, block key, or -- past the last key -- a clamped block key
@@ -201,7 +249,7 @@ void k_attn_bf16(AttnP p) {
       for (int c = 0; c < CPT; ++c) {
         const int kp = tile * kKT + kc[c];
         const int64_t off_c = (int64_t)pages[pbase + (kc[c] >> 4)] * page_elems + coff[c];
-        const int64_t off_b = (int64_t)min(max(kp - C, 0), k - 1) * p.Hkv * D + boff[c];
+        const int64_t off_b = (int64_t)min(max(kp - C, 0), k * nbv - 1) * p.Hkv * D + boff[c];
         const bool in_ctx = kp < C;
         const uint16_t* pk = in_ctx ? p.ck + off_c : kblk + off_b;
         const uint16_t* pv = in_ctx ? p.cv + off_c : vblk + off_b;
@@ -257,7 +305,7 @@ void k_attn_bf16(AttnP p) {
     // sacc[j]: key 32wk + 8*(j/4) + 4*hh + j%4 of the tile, query l32
     float sv[16];
     float tmax = neg_inf();
-    if (tile * kKT + kKT <= total) {   // no masked key in this tile (uniform)
+    if (tile * kKT + kKT <= (NB == 1 ? total : Cmin)) {   // no masked key (uniform)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         sv[j] = sacc[j] * p.sl2;
@@ -267,7 +315,9 @@ void k_attn_bf16(AttnP p) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int kk = tile * kKT + 32 * wk + 8 * (j >> 2) + 4 * hh + (j & 3);
-        sv[j] = (kk < total) ? sacc[j] * p.sl2 : neg_inf();
+        bool vis = kk < total;
+        if (NB > 1) vis = kk < C ? kk < Crow : (vis && (kk - C) / k == jb);
+        sv[j] = vis ? sacc[j] * p.sl2 : neg_inf();
         tmax = fmaxf(tmax, sv[j]);
       }
     }
@@ -311,21 +361,50 @@ void k_attn_bf16(AttnP p) {
 
   // Pipeline, one barrier per tile: compute tile t from one LDS stage while
   // tile t+1 (fetched one step earlier) waits in registers; then stage it
-  // into the other LDS stage and fetch tile t+2.
-  if (t0 < t1) {
-    fetch(t0, kr, vr);
-    stage(smem, kr, vr);
-    if (t0 + 1 < t1) fetch(t0 + 1, kr, vr);
-  }
-  __syncthreads();
-  for (int tile = t0; tile < t1; ++tile) {
-    const int cur = (tile - t0) & 1;
-    compute(smem + cur * STAGE, tile);
-    if (tile + 1 < t1) {
-      stage(smem + (cur ^ 1) * STAGE, kr, vr);
-      if (tile + 2 < t1) fetch(tile + 2, kr, vr);
+  // into the other LDS stage and fetch tile t+2.  With NB = 2 a second
+  // register set keeps tile t+2 in flight as well (tile t+3 is fetched).
+  if (NB == 1) {
+    if (t0 < t1) {
+      fetch(t0, kr, vr);
+      stage(smem, kr, vr);
+      if (t0 + 1 < t1) fetch(t0 + 1, kr, vr);
     }
     __syncthreads();
+    for (int tile = t0; tile < t1; ++tile) {
+      const int cur = (tile - t0) & 1;
+      compute(smem + cur * STAGE, tile);
+      if (tile + 1 < t1) {
+        stage(smem + (cur ^ 1) * STAGE, kr, vr);
+        if (tile + 2 < t1) fetch(tile + 2, kr, vr);
+      }
+      __syncthreads();
+    }
+  } else {
+    u32x4 kr2[CPT], vr2[CPT];
+    if (t0 < t1) {
+      fetch(t0, kr, vr);
+      stage(smem, kr, vr);
+      if (t0 + 1 < t1) fetch(t0 + 1, kr, vr);
+      if (t0 + 2 < t1) fetch(t0 + 2, kr2, vr2);
+    }
+    __syncthreads();
+    // two tiles per trip so each register set has a fixed role: tile t
+    // (even offset) sits in LDS stage 0, t+1 in stage 1
+    for (int tile = t0; tile < t1; tile += 2) {
+      compute(smem, tile);
+      if (tile + 1 < t1) {
+        stage(smem + STAGE, kr, vr);
+        if (tile + 3 < t1) fetch(tile + 3, kr, vr);
+      }
+      __syncthreads();
+      if (tile + 1 >= t1) break;
+      compute(smem + STAGE, tile + 1);
+      if (tile + 2 < t1) {
+        stage(smem, kr2, vr2);
+        if (tile + 4 < t1) fetch(tile + 4, kr2, vr2);
+      }
+      __syncthreads();
+    }
   }
   // Merge the two key halves: wave (wq, 1) hands its state to wave (wq, 0)
   // through LDS, one query slice at a time.
@@ -379,7 +458,7 @@ void k_attn_bf16(AttnP p) {
     if (p.lse && hh == 0)
       p.lse[((int64_t)b * p.Hq + h) * k + pos] = poison ? __builtin_nanf("") : (m + log2f(l)) * kLn2;
   } else {
-    const int64_t rowi = (((int64_t)b * p.Hkv + g) * p.S + split) * Mq + qrow;
+    const int64_t rowi = (((int64_t)b * p.Hkv + g) * p.S + split) * GK + rr;
     float* op = p.po + rowi * D + 4 * hh;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
@@ -499,19 +578,32 @@ __global__ __launch_bounds__(64) void k_attn_f32(int B, int k, int Hq, int Hkv, 
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-template <int D, int NQ>
+template <int D, int NQ, int NB>
 void launch_bf16(const AttnArgs& a, AttnP p, hipStream_t st) {
-  hipLaunchKernelGGL((k_attn_bf16<D, NQ>), dim3((unsigned)(a.B * a.Hkv * p.S)), dim3(NQ * 128), 0,
-                     st, p);
+  const int groups = (a.B + NB - 1) / NB;
+  hipLaunchKernelGGL((k_attn_bf16<D, NQ, NB>), dim3((unsigned)(groups * a.Hkv * p.RC * p.S)),
+                     dim3(NQ * 128), 0, st, p);
 }
 
 template <int D>
 void dispatch_nw(const AttnArgs& a, AttnP p, hipStream_t st) {
-  const int nq = (a.Hq / a.Hkv * a.k + 31) / 32;   // 32-row query slices
-  if (nq <= 1) launch_bf16<D, 1>(a, p, st);
-  else if (nq <= 2) launch_bf16<D, 2>(a, p, st);
-  else if (nq <= 4) launch_bf16<D, 4>(a, p, st);
-  else launch_bf16<D, 8>(a, p, st);
+  const int rows = a.Hq / a.Hkv * a.k;            // query rows per request and kv-head
+  // Requests on one shared table row go two to a workgroup when the pair's
+  // rows fit four 32-row slices: the shared context is then read once per pair.
+  if (DFLASH_ATTN_PAIR && a.shared_table && a.B > 1 && 2 * rows <= 128) {
+    if (2 * rows <= 64) launch_bf16<D, 2, 2>(a, p, st);
+    else launch_bf16<D, 4, 2>(a, p, st);
+    return;
+  }
+  // Otherwise one request per workgroup, at most 128 query rows each (more
+  // rows take several workgroups, each reading the context from L2).
+  const int nq = (rows + 31) / 32;                 // 32-row query slices
+  if (nq <= 1) launch_bf16<D, 1, 1>(a, p, st);
+  else if (nq <= 2) launch_bf16<D, 2, 1>(a, p, st);
+  else {
+    p.RC = (nq + 3) / 4;
+    launch_bf16<D, 4, 1>(a, p, st);
+  }
 }
 
 }  // namespace
@@ -521,7 +613,9 @@ int attention_splits(int B, int Hkv, int k, int max_pages) {
   // but no split shorter than 4 key tiles; a split never spans more pages
   // than its LDS page list holds.
   const int64_t groups = (int64_t)B * Hkv;
-  const int64_t tiles = ((int64_t)max_pages * 16 + k + kKT - 1) / kKT;
+  // (sized for the longest key list of either workgroup shape: a pair of
+  // requests on one shared table row adds 2k block keys)
+  const int64_t tiles = ((int64_t)max_pages * 16 + 2 * k + kKT - 1) / kKT;
   int64_t s = (DFLASH_ATTN_TARGET_WGS + groups - 1) / std::max<int64_t>(groups, 1);
   s = std::min<int64_t>(s, std::max<int64_t>(1, tiles / 4));
   s = std::min<int64_t>(s, 64);
@@ -550,7 +644,7 @@ hipError_t launch_attention(bool bf16, const AttnArgs& a, void* ws, hipStream_t 
             static_cast<const uint16_t*>(a.v_blk), static_cast<const uint16_t*>(a.cache_k),
             static_cast<const uint16_t*>(a.cache_v), a.num_pages, a.block_table, a.max_pages,
             a.shared_table ? 0 : a.max_pages, a.ctx_lens, scale * kLog2e, a.out,
-            a.out_f32 ? 1 : 0, a.lse, po, pml, S};
+            a.out_f32 ? 1 : 0, a.lse, po, pml, S, 1};
     if (a.D == 64) dispatch_nw<64>(a, p, st);
     else dispatch_nw<128>(a, p, st);
     if (S > 1) {

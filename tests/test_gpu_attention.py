@@ -74,7 +74,8 @@ def _subset(c, sel):
     ("bf16", 2, 8, 16, 4, 64, [33, 300], 1.0, 2303),        # D = 64, 2 waves
     ("bf16", 2, 1, 8, 8, 128, [0, 5], 1.0, 2304),           # k = 1, G = 1
     ("bf16", 2, 16, 64, 8, 128, [100, 513], 1.0, 2305),     # G = 8: 8 waves
-    ("bf16", 1, 64, 16, 4, 64, [95], 1.0, 2306),            # k = 64, 16 waves
+    ("bf16", 1, 64, 16, 4, 64, [95], 1.0, 2306),            # k = 64: two 128-row chunks
+    ("bf16", 2, 16, 40, 4, 128, [70, 300], 1.0, 2308),      # 160 rows: a partial second chunk
     ("bf16", 2, 5, 12, 3, 128, [31, 32], 2.0, 2307),        # rows not a multiple of 16
 ])
 def test_attention_parity(dtype, B, k, Hq, Hkv, D, ctx, qs, seed):
@@ -200,7 +201,9 @@ def _shared_case(seed, B, ctx, Hq=32, Hkv=8, D=128, k=16):
     (5, [100, 37, 0, 260, 64], 32, 8, 128, 2360),       # unsorted, ragged, a zero context
     (4, [1000, 1003, 17, 500], 32, 8, 128, 2361),
     (3, [64, 65, 130], 16, 4, 64, 2362),                 # D = 64
-    (2, [300, 301], 64, 8, 128, 2363),                   # G = 8
+    (2, [300, 301], 64, 8, 128, 2363),                   # G = 8: too many rows to pair
+    (2, [8000, 5003], 32, 8, 128, 2365),                 # one pair, context split across workgroups
+    (3, [4100, 0, 3000], 32, 8, 128, 2366),              # split, and a last request without a partner
 ])
 def test_attention_shared_table(B, ctx, Hq, Hkv, D, seed):
     """One block-table row shared by every request (table_rows = 1): each
