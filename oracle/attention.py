@@ -16,6 +16,13 @@ For request b, q-head h, block position i, with G = Hq / Hkv and g = h // G:
     s      = scale * keys @ q[b, i, h],   scale = 1/sqrt(D) unless given
     o      = softmax(s) @ values,         lse = log(sum(exp(s)))
 
+Causal variant (``causal=True``), following [DFlash overview, section
+"块扩散的双向注意力问题"] (the JetSpec change): inside the block, position i
+sees only the block positions 0..i; the injected context stays fully visible.
+The block-causal mask of [Spec tutorial, section 5.3] (a block sees every
+earlier block and all of itself) is the default mode applied to a context that
+holds the earlier blocks.
+
 Readings (also in the design doc): GQA groups are contiguous (q-head h reads kv-head
 h // G); the visible context of a request is its logical positions [0, C_b),
 strictly before the anchor; C_b = 0 is allowed; Q and K arrive already
@@ -37,8 +44,10 @@ def _softmax_rows(s):
 
 
 def block_attention(q, k_blk, v_blk, cache_k, cache_v, block_table, ctx_lens, dtype,
-                    scale=None):
-    """Per-request gather form.  Returns (out [B, k, Hq, D], lse [B, Hq, k])."""
+                    scale=None, causal=False):
+    """Per-request gather form.  Returns (out [B, k, Hq, D], lse [B, Hq, k]).
+    With ``causal`` the score of block key j for block position i is removed
+    when j > i."""
     q, kb, vb = widen(q, dtype), widen(k_blk, dtype), widen(v_blk, dtype)
     ck, cv = widen(cache_k, dtype), widen(cache_v, dtype)
     B, k, Hq, D = q.shape
@@ -57,6 +66,8 @@ def block_attention(q, k_blk, v_blk, cache_k, cache_v, block_table, ctx_lens, dt
         for h in range(Hq):
             g = h // G
             s = scale * (q[b, :, h, :] @ keys[:, g, :].T)               # [k, C+k]
+            if causal:
+                s[:, C:] = np.where(np.tril(np.ones((k, k), dtype=bool)), s[:, C:], -np.inf)
             p, l = _softmax_rows(s)
             out[b, :, h, :] = p @ vals[:, g, :]
             lse[b, h, :] = l
@@ -64,13 +75,14 @@ def block_attention(q, k_blk, v_blk, cache_k, cache_v, block_table, ctx_lens, dt
 
 
 def block_attention_masked(q, k_blk, v_blk, cache_k, cache_v, block_table, ctx_lens, dtype,
-                           scale=None):
+                           scale=None, causal=False):
     """Brute force with an explicit boolean mask over *every* key that exists:
     all physical cache slots followed by every request's block keys.  A query
     of request b may see slot (page, j) iff that slot holds one of b's logical
-    positions < C_b, and may see block key (b', i') iff b' == b.  Exponentials
-    of masked scores are dropped explicitly.  Same outputs as
-    ``block_attention``; used to pin it."""
+    positions < C_b, and may see block key (b', i') iff b' == b (and, with
+    ``causal``, i' <= its own block position).  Exponentials of masked scores
+    are dropped explicitly.  Same outputs as ``block_attention``; used to pin
+    it."""
     q, kb, vb = widen(q, dtype), widen(k_blk, dtype), widen(v_blk, dtype)
     ck, cv = widen(cache_k, dtype), widen(cache_v, dtype)
     B, k, Hq, D = q.shape
@@ -92,9 +104,12 @@ def block_attention_masked(q, k_blk, v_blk, cache_k, cache_v, block_table, ctx_l
         for h in range(Hq):
             g = h // G
             for i in range(k):
+                vis = mask[b].copy()
+                if causal:
+                    vis[n_slots + b * k + i + 1: n_slots + (b + 1) * k] = False
                 s = scale * (keys[:, g, :] @ q[b, i, h, :])
-                m = s[mask[b]].max()
-                e = np.where(mask[b], np.exp(s - m), 0.0)
+                m = s[vis].max()
+                e = np.where(vis, np.exp(s - m), 0.0)
                 out[b, i, h] = (e @ vals[:, g, :]) / e.sum()
                 lse[b, h, i] = m + np.log(e.sum())
     return out, lse

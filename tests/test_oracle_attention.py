@@ -158,3 +158,66 @@ def test_packed_training_mask_equals_dense_sequence_mask():
     # anchors are disjoint blocks in the loss region
     a = np.sort(c.ctx_lens)
     assert (np.diff(a) >= k).all() and a[0] >= P and a[-1] + k <= seq
+
+
+# --- causal block (block position i sees block positions 0..i) -------------
+
+@pytest.mark.parametrize("seed,ctx", [(21, (0, 5, 19)), (22, (8, 1, 33)), (23, (16, 0, 3))])
+def test_causal_gather_form_equals_explicit_mask_brute_force(seed, ctx):
+    c = _case(seed, ctx=ctx)
+    o1, l1 = _run_causal(c)
+    o2, l2 = _run_causal(c, oracle.block_attention_masked)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-12)
+
+
+def _run_causal(c, fn=oracle.block_attention):
+    return fn(c.q, c.k_blk, c.v_blk, c.cache_k, c.cache_v, c.block_table, c.ctx_lens, c.dtype,
+              causal=True)
+
+
+def test_causal_matches_torch_sdpa_float64():
+    """Library routine: torch CPU float64 SDPA -- is_causal=True over the block
+    alone when C = 0, and an explicit [context | lower-triangular] bool mask
+    when C > 0."""
+    c = _case(24, B=2, k=6, Hq=4, Hkv=2, D=16, ctx=(0, 13))
+    out, lse = _run_causal(c)
+    q = oracle.widen(c.q, "f32")
+    G = c.n_q_heads // c.n_kv_heads
+    for b in range(c.B):
+        C = int(c.ctx_lens[b])
+        keys = np.concatenate([oracle.gather_paged(oracle.widen(c.cache_k, "f32"),
+                                                   c.block_table[b], C),
+                               oracle.widen(c.k_blk, "f32")[b]])
+        vals = np.concatenate([oracle.gather_paged(oracle.widen(c.cache_v, "f32"),
+                                                   c.block_table[b], C),
+                               oracle.widen(c.v_blk, "f32")[b]])
+        for h in range(c.n_q_heads):
+            qt = torch.from_numpy(q[b, :, h, :])[None, None]
+            kt = torch.from_numpy(keys[:, h // G, :])[None, None]
+            vt = torch.from_numpy(vals[:, h // G, :])[None, None]
+            if C == 0:
+                ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+            else:
+                mask = torch.cat([torch.ones(c.k, C, dtype=torch.bool),
+                                  torch.tril(torch.ones(c.k, c.k, dtype=torch.bool))], dim=1)
+                ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask)
+            np.testing.assert_allclose(out[b, :, h, :], ref[0, 0].numpy(), atol=1e-12)
+
+
+def test_causal_closed_forms():
+    """With no context, block position 0 sees only its own key: o = v_blk[0]
+    exactly.  The last block position sees the whole block, so its row equals
+    the bidirectional result; with k = 1 the two modes coincide."""
+    c = _case(25, B=2, k=5, Hq=4, Hkv=2, D=8, ctx=(0, 0))
+    out, _ = _run_causal(c)
+    vb = oracle.widen(c.v_blk, "f32")
+    for h in range(c.n_q_heads):
+        np.testing.assert_array_equal(out[:, 0, h, :], vb[:, 0, h // 2, :])
+    c = _case(26, B=3, k=5, Hq=4, Hkv=2, D=8, ctx=(0, 7, 21))
+    oc, lc = _run_causal(c)
+    ob, lb = _run(c)
+    np.testing.assert_allclose(oc[:, -1], ob[:, -1], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lc[:, :, -1], lb[:, :, -1], rtol=0, atol=1e-12)
+    c = _case(27, B=2, k=1, Hq=2, Hkv=1, D=8, ctx=(3, 9))
+    np.testing.assert_allclose(_run_causal(c)[0], _run(c)[0], rtol=0, atol=1e-12)
