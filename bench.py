@@ -83,16 +83,20 @@ def parse():
                          "ctx-KV materialisation; packed: training-style packed block mask")
     ap.add_argument("--sigma", type=float, default=1.0, help="sample-gate: draft = target + N(0, sigma)")
     ap.add_argument("--stages", type=int, default=4, help="sample-gate: DLoop stages of 8")
+    ap.add_argument("--causal", action="store_true",
+                    help="decode and packed: causal mask inside the block (position i sees "
+                         "block keys 0..i) instead of the bidirectional one")
     return ap.parse_args()
 
 
 class Step:
     """Device-resident inputs, outputs and workspaces of one draft step."""
 
-    def __init__(self, B, C, k, V, Ld, d=4096, m=5, Hq=32, Hkv=8, D=128, seed=0):
+    def __init__(self, B, C, k, V, Ld, d=4096, m=5, Hq=32, Hkv=8, D=128, seed=0, causal=False):
         import torch
         import block_diffusion_draft_ctx_amd as dfl
         self.dfl = dfl
+        self.causal = causal
         self.B, self.C, self.k, self.V, self.Ld = B, C, k, V, Ld
         self.d, self.m, self.Hq, self.Hkv, self.D = d, m, Hq, Hkv, D
         dev = torch.device("cuda:0")
@@ -150,7 +154,7 @@ class Step:
     def attention(self, l):
         self.dfl.block_attention(self.q[l], self.k_blk[l], self.v_blk[l], self.cache_k[l],
                                  self.cache_v[l], self.block_table, self.ctx_lens,
-                                 out=self.attn_out[l], workspace=self.ws_att)
+                                 out=self.attn_out[l], workspace=self.ws_att, causal=self.causal)
 
     def verify(self):
         self.dfl.verify_greedy(self.target_logits, draft_tokens=self.draft_tokens,
@@ -163,7 +167,8 @@ class Step:
         return B * C * Hkv * D * 2 * 2 + B * k * (2 * Hq + 2 * Hkv) * D * 2
 
     def attn_flops(self):
-        return 4.0 * self.B * self.k * self.Hq * self.D * (self.C + self.k)
+        blk = (self.k + 1) / 2 if self.causal else self.k   # block keys a query row sees, on average
+        return 4.0 * self.B * self.k * self.Hq * self.D * (self.C + blk)
 
     def verify_bytes(self):
         return self.B * (2 * self.k - 1) * self.V * 2
@@ -263,7 +268,8 @@ def cpu_baseline(st, n_req):
     for l in range(st.Ld):
         kc = oracle.widen(ck[l], "bf16")
         oracle.paged_write(kc, res["K"][l], bt_c, k, np.full(n_req, C), np.full(n_req, k))
-        oracle.block_attention(q[l], kb[l], vb[l], ck[l], cv[l], bt_c, ctx, "bf16")
+        oracle.block_attention(q[l], kb[l], vb[l], ck[l], cv[l], bt_c, ctx, "bf16",
+                               causal=st.causal)
     oracle.verify_greedy(tl, "bf16", draft_logits=dl, prefix_lens=np.full(n_req, C))
     dt = time.perf_counter() - t0
     try:
@@ -413,6 +419,10 @@ def bench_prefill(args):
     return line
 
 
+def _mask_name(args):
+    return "causal" if args.causal else "bidirectional"
+
+
 def bench_packed(args):
     """Training-style packed block mask, forward only: one 8192-token
     sequence, up to 512 non-overlapping anchors in the loss region, block 16;
@@ -445,16 +455,21 @@ def bench_packed(args):
                      dtype=torch.uint8, device=dev)
 
     def step():
-        dfl.block_attention(q, kb, vb, ck, cv, bt, ctx, out=out, workspace=ws)
+        dfl.block_attention(q, kb, vb, ck, cv, bt, ctx, out=out, workspace=ws, causal=args.causal)
 
     ms = _events_ms(step, args.steps, args.warmup)
-    keys = int(anchors.astype(np.int64).sum()) + nb * kk
-    flops = 4.0 * kk * Hq * D * keys
+    # keys seen summed over query rows: kk rows per block see its context and
+    # kk block keys (or, causal, 1..kk of them)
+    row_keys = kk * int(anchors.astype(np.int64).sum()) + nb * (kk * (kk + 1) // 2 if args.causal
+                                                                 else kk * kk)
+    flops = 4.0 * Hq * D * row_keys
     stream = float(anchors.astype(np.int64).sum()) * Hkv * D * 2 * 2
     line = _base_line(args, "packed block-mask attention, blocks/sec", round(nb / (ms * 1e-3), 1),
                       "blocks/s", ms, f"training-style packed block mask, forward: sequence {seq}, "
-                      f"prompt {P}, {nb} anchors, block {kk}, 32 Q / 8 KV heads x 128, one layer",
-                      blocks=nb, seq_len=seq, prompt=P, mean_anchor=round(float(anchors.mean()), 1))
+                      f"prompt {P}, {nb} anchors, block {kk} ({_mask_name(args)} inside the "
+                      f"block), 32 Q / 8 KV heads x 128, one layer",
+                      blocks=nb, seq_len=seq, prompt=P, mean_anchor=round(float(anchors.mean()), 1),
+                      block_mask=_mask_name(args))
     line["roofline"] = {"kernel": "block_attention (packed)", "bound": "mfma",
                         "achieved": round(flops / (ms * 1e-3) / 1e12, 1), "peak": BF16_PEAK / 1e12,
                         "unit": "TFLOP/s", "frac": round(flops / (ms * 1e-3) / BF16_PEAK, 4),
@@ -480,7 +495,7 @@ def main():
               "packed": bench_packed}[args.workload]
         print(json.dumps(fn(args)), flush=True)
         return
-    st = Step(args.batch, args.ctx, args.block, args.vocab, args.layers)
+    st = Step(args.batch, args.ctx, args.block, args.vocab, args.layers, causal=args.causal)
     print(f"[bench] inputs ready: B={st.B} ctx={st.C} k={st.k} V={st.V} layers={st.Ld}",
           file=sys.stderr, flush=True)
     if args.copy_calibration:
@@ -500,11 +515,13 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": (f"Llama-3.1-8B-shaped DFlash decode step: batch {st.B}, ctx "
-                                f"{st.C}, block {st.k}, {st.Ld} draft layers (32 Q / 8 KV heads "
-                                f"x 128), d_model 4096 with 5 captured hiddens, greedy verify "
-                                f"over vocab {st.V} with fused draft argmax"),
+                                f"{st.C}, block {st.k} ({_mask_name(args)} inside the block), "
+                                f"{st.Ld} draft layers (32 Q / 8 KV heads x 128), d_model 4096 "
+                                f"with 5 captured hiddens, greedy verify over vocab {st.V} with "
+                                f"fused draft argmax"),
                    "batch": st.B, "ctx": st.C, "block": st.k, "draft_layers": st.Ld,
-                   "vocab": st.V, "d_model": st.d, "committed_rows": st.T},
+                   "vocab": st.V, "d_model": st.d, "committed_rows": st.T,
+                   "block_mask": _mask_name(args)},
         "roofline": {"kernel": "block_attention (per layer)", "bound": "hbm",
                      "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),

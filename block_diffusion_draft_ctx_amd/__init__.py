@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libdflash.so")
 
 OK, E_ARG, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
+MASK_BIDIRECTIONAL, MASK_CAUSAL = 0, 1
 
 EXPORTS = (
     "dflash_status_string", "dflash_version",
@@ -62,8 +63,8 @@ def _declare(lib):
     lib.dflash_attention_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, I32]
     lib.dflash_block_attention.restype = I32
     lib.dflash_block_attention.argtypes = [
-        I32, I32, I32, I32, I32, P, P, P, P, P, I32, I32, P, I32, I32, P, F, P, P, I32, I32, P, SZ,
-        P]
+        I32, I32, I32, I32, I32, P, P, P, P, P, I32, I32, P, I32, I32, P, F, I32, P, P, I32, I32, P,
+        SZ, P]
     lib.dflash_verify_workspace_size.restype = SZ
     lib.dflash_verify_workspace_size.argtypes = [I32, I32, I32]
     lib.dflash_verify_greedy.restype = I32
@@ -200,12 +201,15 @@ def materialize_ctx_kv(hiddens: Sequence, W_f, b_f, W_K: Sequence, W_V: Sequence
 
 
 def block_attention(q, k_blk, v_blk, cache_k, cache_v, block_table, ctx_lens, scale=0.0,
-                    out=None, lse=None, workspace=None, stream=None, out_dtype=None):
+                    out=None, lse=None, workspace=None, stream=None, out_dtype=None,
+                    causal=False):
     """dflash_block_attention.  q [B,k,Hq,D]; k_blk/v_blk [B,k,Hkv,D]; caches
     [num_pages,16,Hkv,D]; block_table [B,max_pages], or [1,max_pages] when
-    every request reads the same (packed) sequence; ctx_lens [B].  The output
-    takes the dtype of ``out`` (or ``out_dtype``, default: q's dtype).  Returns
-    (out, lse) where lse is the tensor given (or None)."""
+    every request reads the same (packed) sequence; ctx_lens [B].  ``causal``
+    lets block position i see block keys 0..i only (the context stays
+    visible).  The output takes the dtype of ``out`` (or ``out_dtype``,
+    default: q's dtype).  Returns (out, lse) where lse is the tensor given (or
+    None)."""
     torch = _torch()
     L = lib()
     B, k, Hq, D = q.shape
@@ -225,7 +229,8 @@ def block_attention(q, k_blk, v_blk, cache_k, cache_v, block_table, ctx_lens, sc
     s = L.dflash_block_attention(
         B, k, Hq, Hkv, D, _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(cache_k), _ptr(cache_v),
         cache_k.shape[0], cache_k.shape[1], _ptr(block_table), block_table.shape[1],
-        block_table.shape[0], _ptr(ctx_lens), float(scale), _ptr(out), _ptr(lse), dt, odt,
+        block_table.shape[0], _ptr(ctx_lens), float(scale), MASK_CAUSAL if causal else MASK_BIDIRECTIONAL,
+        _ptr(out), _ptr(lse), dt, odt,
         _ptr(ws), nws,
         _stream(stream))
     _check(s, "dflash_block_attention")

@@ -125,7 +125,8 @@ dflash_status dflash_block_attention(int B, int k, int n_q_heads, int n_kv_heads
                                      int page_size, const int32_t* block_table,
                                      int max_pages_per_seq, int table_rows,
                                      const int32_t* ctx_lens, float scale,
-                                     void* out, float* lse_out, dflash_dtype dtype,
+                                     dflash_block_mask block_mask, void* out, float* lse_out,
+                                     dflash_dtype dtype,
                                      dflash_dtype out_dtype, void* ws, size_t ws_bytes,
                                      dflash_stream_t stream) {
   if (bad_dtype(dtype) || bad_dtype(out_dtype)) return DFLASH_E_ARG;
@@ -136,6 +137,7 @@ dflash_status dflash_block_attention(int B, int k, int n_q_heads, int n_kv_heads
   if (k > 64 || (n_q_heads / n_kv_heads) * k > 256) return DFLASH_E_UNSUPPORTED;
   if (page_size != 16) return DFLASH_E_UNSUPPORTED;
   if (!(scale >= 0.f)) return DFLASH_E_ARG;
+  if (block_mask != DFLASH_MASK_BIDIRECTIONAL && block_mask != DFLASH_MASK_CAUSAL) return DFLASH_E_ARG;
   if (B == 0) return DFLASH_OK;
   if (num_pages < 1 || max_pages_per_seq < 1) return DFLASH_E_ARG;
   if (table_rows != B && table_rows != 1) return DFLASH_E_ARG;
@@ -149,8 +151,8 @@ dflash_status dflash_block_attention(int B, int k, int n_q_heads, int n_kv_heads
                            : 0;
   if (dflash_status s = check_ws(ws, ws_bytes, need)) return s;
   AttnArgs a{B, k, n_q_heads, n_kv_heads, head_dim, q, k_blk, v_blk, cache_k, cache_v, num_pages,
-             block_table, max_pages_per_seq, table_rows == 1, ctx_lens, scale, out,
-             lse_out, out_dtype == DFLASH_F32};
+             block_table, max_pages_per_seq, table_rows == 1, ctx_lens, scale,
+             block_mask == DFLASH_MASK_CAUSAL, out, lse_out, out_dtype == DFLASH_F32};
   return hip_status(launch_attention(bf16, a, ws, static_cast<hipStream_t>(stream)));
 }
 

@@ -73,6 +73,7 @@ struct AttnP {
   float2* pml;  // split partials: (m, l) [B*Hkv*S*G*k]
   int S;        // ctx splits
   int RC;       // query-row chunks per (request, kv-head): more rows than one workgroup holds
+  int causal;   // block position i sees block keys 0..i only
 };
 
 // Transposing LDS read (gfx950): within each 16-lane group, output lane j
@@ -305,7 +306,9 @@ void k_attn_bf16(AttnP p) {
     // sacc[j]: key 32wk + 8*(j/4) + 4*hh + j%4 of the tile, query l32
     float sv[16];
     float tmax = neg_inf();
-    if (tile * kKT + kKT <= (NB == 1 ? total : Cmin)) {   // no masked key (uniform)
+    // no masked key in the tile (uniform): all context, or -- without the
+    // causal mask -- all keys of a single request's list
+    if (tile * kKT + kKT <= (NB == 1 && !p.causal ? total : Cmin)) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         sv[j] = sacc[j] * p.sl2;
@@ -317,6 +320,7 @@ void k_attn_bf16(AttnP p) {
         const int kk = tile * kKT + 32 * wk + 8 * (j >> 2) + 4 * hh + (j & 3);
         bool vis = kk < total;
         if (NB > 1) vis = kk < C ? kk < Crow : (vis && (kk - C) / k == jb);
+        if (p.causal && kk >= C) vis = vis && (kk - C) % k <= pos;
         sv[j] = vis ? sacc[j] * p.sl2 : neg_inf();
         tmax = fmaxf(tmax, sv[j]);
       }
@@ -511,8 +515,9 @@ __global__ __launch_bounds__(64) void k_attn_f32(int B, int k, int Hq, int Hkv, 
                                                  const float* kb, const float* vb,
                                                  const float* ck, const float* cv, int num_pages,
                                                  const int32_t* bt, int max_pages, int bt_stride,
-                                                 const int32_t* ctx, float sl2, float* out,
-                                                 float* lse, int S, float* po, float2* pml) {
+                                                 const int32_t* ctx, float sl2, int causal,
+                                                 float* out, float* lse, int S, float* po,
+                                                 float2* pml) {
   const int i = blockIdx.x % k;
   const int h = (blockIdx.x / k) % Hq;
   const int b = blockIdx.x / (k * Hq);
@@ -525,7 +530,7 @@ __global__ __launch_bounds__(64) void k_attn_f32(int B, int k, int Hq, int Hkv, 
   int C = ctx[b];
   bool poison = (C < 0 || C > max_pages * 16);
   if (poison) C = 0;
-  const int total = C + k;
+  const int total = C + (causal ? i + 1 : k);   // causal: block keys 0..i
   float m = neg_inf(), l = 0.f, o[D];
   for (int d = 0; d < D; ++d) o[d] = 0.f;
   for (int j = t; j < total; j += 64) {
@@ -644,7 +649,7 @@ hipError_t launch_attention(bool bf16, const AttnArgs& a, void* ws, hipStream_t 
             static_cast<const uint16_t*>(a.v_blk), static_cast<const uint16_t*>(a.cache_k),
             static_cast<const uint16_t*>(a.cache_v), a.num_pages, a.block_table, a.max_pages,
             a.shared_table ? 0 : a.max_pages, a.ctx_lens, scale * kLog2e, a.out,
-            a.out_f32 ? 1 : 0, a.lse, po, pml, S, 1};
+            a.out_f32 ? 1 : 0, a.lse, po, pml, S, 1, a.causal ? 1 : 0};
     if (a.D == 64) dispatch_nw<64>(a, p, st);
     else dispatch_nw<128>(a, p, st);
     if (S > 1) {
@@ -665,14 +670,16 @@ hipError_t launch_attention(bool bf16, const AttnArgs& a, void* ws, hipStream_t 
                          static_cast<const float*>(a.v_blk), static_cast<const float*>(a.cache_k),
                          static_cast<const float*>(a.cache_v), a.num_pages, a.block_table,
                          a.max_pages, a.shared_table ? 0 : a.max_pages, a.ctx_lens,
-                         scale * kLog2e, static_cast<float*>(a.out), a.lse, 1, nullptr, nullptr);
+                         scale * kLog2e, a.causal ? 1 : 0, static_cast<float*>(a.out), a.lse, 1,
+                         nullptr, nullptr);
     else
       hipLaunchKernelGGL((k_attn_f32<128>), dim3(grid), dim3(64), 0, st, a.B, a.k, a.Hq, a.Hkv,
                          static_cast<const float*>(a.q), static_cast<const float*>(a.k_blk),
                          static_cast<const float*>(a.v_blk), static_cast<const float*>(a.cache_k),
                          static_cast<const float*>(a.cache_v), a.num_pages, a.block_table,
                          a.max_pages, a.shared_table ? 0 : a.max_pages, a.ctx_lens,
-                         scale * kLog2e, static_cast<float*>(a.out), a.lse, 1, nullptr, nullptr);
+                         scale * kLog2e, a.causal ? 1 : 0, static_cast<float*>(a.out), a.lse, 1,
+                         nullptr, nullptr);
   }
   return hipGetLastError();
 }

@@ -62,6 +62,7 @@ struct AttnArgs {
   bool shared_table;  // every request reads block-table row 0
   const int32_t* ctx_lens;
   float scale;
+  bool causal;        // block position i sees block keys 0..i only
   void* out;
   float* lse;
   bool out_f32;  // bf16 inputs with an fp32 output

@@ -71,6 +71,9 @@ typedef enum {
 
 typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
 
+/* What a block position sees of its own block (dflash_block_attention). */
+typedef enum { DFLASH_MASK_BIDIRECTIONAL = 0, DFLASH_MASK_CAUSAL = 1 } dflash_block_mask;
+
 /* One draft layer's paged KV cache (device pointers). */
 typedef struct {
   void* k;           /* [num_pages, page_size, n_kv_heads, head_dim] */
@@ -149,6 +152,15 @@ dflash_status dflash_materialize_ctx_kv(
  *   keys   = cache K at logical positions [0, ctx_lens[b]) ++ k_blk[b, 0:k]
  *   out    = softmax(scale * q . keys) @ values,  lse = natural log-sum-exp
  *
+ * block_mask selects what a block position sees of its own block:
+ *   DFLASH_MASK_BIDIRECTIONAL  all k block keys (DFlash, as above);
+ *   DFLASH_MASK_CAUSAL         block keys 0..i only ([DFlash overview], section
+ *                              "块扩散的双向注意力问题": the JetSpec change);
+ * the context part is fully visible in both modes.  The block-causal mask of
+ * [Spec tutorial], section 5.3 (a block sees every earlier block and all of
+ * itself) is the bidirectional mode over a context that holds the earlier
+ * blocks.  Any other value is DFLASH_E_ARG.
+ *
  * q            [B, k, Hq, D]      k_blk, v_blk  [B, k, Hkv, D]
  * cache_k/v    [num_pages, 16, Hkv, D]
  * block_table  [table_rows, max_pages_per_seq] int32;  ctx_lens [B] int32 (0 allowed)
@@ -172,8 +184,8 @@ dflash_status dflash_block_attention(
     const void* q, const void* k_blk, const void* v_blk,
     const void* cache_k, const void* cache_v, int num_pages, int page_size,
     const int32_t* block_table, int max_pages_per_seq, int table_rows,
-    const int32_t* ctx_lens, float scale, void* out, float* lse_out,
-    dflash_dtype dtype, dflash_dtype out_dtype, void* ws, size_t ws_bytes,
+    const int32_t* ctx_lens, float scale, dflash_block_mask block_mask, void* out,
+    float* lse_out, dflash_dtype dtype, dflash_dtype out_dtype, void* ws, size_t ws_bytes,
     dflash_stream_t stream);
 
 /* ---------------------------------------------------------------------------

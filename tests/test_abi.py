@@ -75,8 +75,8 @@ def test_zero_batch_is_a_noop(lib):
     assert lib.dflash_verify_greedy(0, 15, 100, None, 100, None, 0, None, None, None, None, None,
                                     None, None, None, dfl.BF16, None, 0, None) == dfl.OK
     assert lib.dflash_block_attention(0, 16, 32, 8, 128, None, None, None, None, None, 1, 16,
-                                      None, 1, 0, None, 0.0, None, None, dfl.BF16, dfl.BF16, None,
-                                      0, None) == dfl.OK
+                                      None, 1, 0, None, 0.0, dfl.MASK_BIDIRECTIONAL, None, None,
+                                      dfl.BF16, dfl.BF16, None, 0, None) == dfl.OK
     assert lib.dflash_gate(0, 8, 100, None, 100, None, None, 1.0, -0.5, None, None, None, None,
                            dfl.BF16, None, 0, None) == dfl.OK
     assert lib.dflash_verify_sample(0, 8, 100, None, 100, None, 100, None, None, None, None, 1.0,
@@ -141,14 +141,16 @@ def test_gate_argument_errors(lib, kw, code):
     (dict(np_=0), dfl.E_ARG), (dict(nws=0, B=1, rows=1), dfl.E_WORKSPACE),
     (dict(dt=dfl.F32, odt=dfl.BF16), dfl.E_UNSUPPORTED), (dict(odt=5), dfl.E_ARG),
     (dict(rows=2), dfl.E_ARG), (dict(rows=0), dfl.E_ARG), (dict(rows=5), dfl.E_ARG),
+    (dict(mask=2), dfl.E_ARG), (dict(mask=-1), dfl.E_ARG),
 ])
 def test_attention_argument_errors(lib, kw, code):
     a = dict(B=4, k=16, Hq=32, Hkv=8, D=128, q=FAKE, ps=16, scale=0.0, np_=10, nws=1 << 26,
-             dt=dfl.BF16, odt=dfl.BF16, rows=4)
+             dt=dfl.BF16, odt=dfl.BF16, rows=4, mask=dfl.MASK_CAUSAL)
     a.update(kw)
     s = lib.dflash_block_attention(a["B"], a["k"], a["Hq"], a["Hkv"], a["D"], a["q"], FAKE, FAKE,
                                    FAKE, FAKE, a["np_"], a["ps"], FAKE, 64, a["rows"], FAKE,
-                                   a["scale"], FAKE, None, a["dt"], a["odt"], WS, a["nws"], None)
+                                   a["scale"], a["mask"], FAKE, None, a["dt"], a["odt"], WS,
+                                   a["nws"], None)
     assert s == code
 
 

@@ -16,7 +16,7 @@ from tests.gpu_util import TOL, bits, down, log, rel_err, up
 pytestmark = pytest.mark.gpu
 
 
-def _run(c, lse=True, out_dtype=None):
+def _run(c, lse=True, out_dtype=None, causal=False):
     import torch
     kind = c.dtype
     q = up(c.q, kind)
@@ -24,11 +24,11 @@ def _run(c, lse=True, out_dtype=None):
     od = {"f32": torch.float32, "bf16": torch.bfloat16, None: None}[out_dtype]
     out, lse_t = dfl.block_attention(q, up(c.k_blk, kind), up(c.v_blk, kind), up(c.cache_k, kind),
                                      up(c.cache_v, kind), up(c.block_table, "i32"),
-                                     up(c.ctx_lens, "i32"), lse=lse_t, out_dtype=od)
+                                     up(c.ctx_lens, "i32"), lse=lse_t, out_dtype=od, causal=causal)
     return out, lse_t
 
 
-def _check(c, out, lse, sel=None):
+def _check(c, out, lse, sel=None, causal=False):
     """Compare (optionally only the requests in sel) with the oracle."""
     import torch
     if sel is not None:
@@ -36,7 +36,7 @@ def _check(c, out, lse, sel=None):
         out = out[sel]
         lse = lse[sel] if lse is not None else None
     o_ref, l_ref = oracle.block_attention(c.q, c.k_blk, c.v_blk, c.cache_k, c.cache_v,
-                                          c.block_table, c.ctx_lens, c.dtype)
+                                          c.block_table, c.ctx_lens, c.dtype, causal=causal)
     rms = np.sqrt(np.mean(o_ref ** 2))
     diff = np.abs(down(out) - o_ref)
     if out.dtype == torch.bfloat16:
@@ -175,7 +175,7 @@ def test_attention_in_band_errors():
     assert np.isnan(down(lse)[0]).all() and np.isfinite(down(lse)[1]).all()
 
 
-def _run_shared(c, out_dtype=None):
+def _run_shared(c, out_dtype=None, causal=False):
     """The same case through a one-row block table (every request reads row 0)."""
     import torch
     kind = c.dtype
@@ -185,7 +185,7 @@ def _run_shared(c, out_dtype=None):
     od = {"f32": torch.float32, "bf16": torch.bfloat16, None: None}[out_dtype]
     return dfl.block_attention(q, up(c.k_blk, kind), up(c.v_blk, kind), up(c.cache_k, kind),
                                up(c.cache_v, kind), up(c.block_table[:1], "i32"),
-                               up(c.ctx_lens, "i32"), lse=lse, out_dtype=od)
+                               up(c.ctx_lens, "i32"), lse=lse, out_dtype=od, causal=causal)
 
 
 def _shared_case(seed, B, ctx, Hq=32, Hkv=8, D=128, k=16):
@@ -242,3 +242,68 @@ def test_attention_shared_table_bad_page_poisons_only_its_readers():
     assert np.isnan(o[1]).all() and np.isnan(o[3]).all()
     assert np.isfinite(o[0]).all() and np.isfinite(o[2]).all()
     _check(c, out, lse, sel=[0, 2])
+
+
+# --- causal block mask: block position i sees block keys 0..i ---------------
+
+@pytest.mark.parametrize("dtype,B,k,Hq,Hkv,D,ctx,seed", [
+    ("f32", 1, 8, 4, 2, 64, [64], 1401),
+    ("f32", 3, 4, 6, 2, 128, [0, 17, 40], 1402),
+    ("bf16", 3, 16, 32, 8, 128, [0, 45, 1000], 2401),     # several tiles, ragged, no context
+    ("bf16", 2, 8, 16, 4, 64, [33, 300], 2402),           # D = 64
+    ("bf16", 1, 64, 16, 4, 64, [95], 2403),               # k = 64: block spans two key tiles
+    ("bf16", 2, 5, 12, 3, 128, [31, 32], 2404),           # rows not a multiple of 16
+    ("bf16", 2, 16, 64, 8, 128, [100, 513], 2405),        # G = 8
+])
+def test_attention_causal_parity(dtype, B, k, Hq, Hkv, D, ctx, seed):
+    log(f"attention causal dtype={dtype} B={B} k={k} Hq={Hq} Hkv={Hkv} D={D} ctx={ctx}")
+    c = synth.attention_case(seed, dtype=dtype, B=B, k=k, n_q_heads=Hq, n_kv_heads=Hkv,
+                             head_dim=D, ctx_lens=ctx)
+    for od in (["f32"] if dtype == "f32" else ["f32", "bf16"]):
+        out, lse = _run(c, out_dtype=od, causal=True)
+        _check(c, out, lse, causal=True)
+
+
+def test_attention_causal_split_context():
+    """One request: the context is split across workgroups; the masked block
+    keys sit in the last split only."""
+    c = synth.attention_case(2410, dtype="bf16", B=1, k=16, n_q_heads=32, n_kv_heads=8,
+                             head_dim=128, ctx_lens=[6000])
+    out, lse = _run(c, out_dtype="f32", causal=True)
+    _check(c, out, lse, causal=True)
+
+
+def test_attention_causal_shared_table_pairs():
+    """Causal blocks on one shared table row (two requests per workgroup)."""
+    c = _shared_case(2411, 5, [100, 37, 0, 260, 64])
+    for od in ("f32", "bf16"):
+        out, lse = _run_shared(c, out_dtype=od, causal=True)
+        _check(c, out, lse, causal=True)
+
+
+def test_attention_causal_packed_training_sampled():
+    """Packed training with the causal-within-block mask (one shared row)."""
+    c, P = synth.packed_attention_case(2330, dtype="bf16", seq_len=8192, k=16, n_q_heads=32,
+                                       n_kv_heads=8, head_dim=128, max_anchors=512)
+    log(f"packed causal: {c.B} blocks")
+    out, lse = _run_shared(c, out_dtype="f32", causal=True)
+    assert np.isfinite(down(out)).all()
+    _check(c, out, lse, sel=[0, c.B // 2, c.B - 1], causal=True)
+
+
+def test_attention_causal_first_position_and_last_row():
+    """Closed forms through the kernel: with no context, block position 0
+    returns v_blk[0] (fp32 path exactly up to the division by l = 1); the
+    last block position equals the bidirectional result (to 1e-5 of its size)."""
+    c = synth.attention_case(2412, dtype="f32", B=2, k=6, n_q_heads=4, n_kv_heads=2,
+                             head_dim=64, ctx_lens=[0, 0])
+    out, _ = _run(c, causal=True)
+    o = down(out)
+    for h in range(4):
+        np.testing.assert_allclose(o[:, 0, h], c.v_blk[:, 0, h // 2], rtol=0, atol=1e-6)
+    c = synth.attention_case(2413, dtype="bf16", B=2, k=16, n_q_heads=32, n_kv_heads=8,
+                             head_dim=128, ctx_lens=[300, 1000])
+    oc, lc = _run(c, out_dtype="f32", causal=True)
+    ob, lb = _run(c, out_dtype="f32")
+    e = float(np.abs(down(oc)[:, -1] - down(ob)[:, -1]).max())
+    assert e <= 1e-5 * float(np.abs(down(ob)[:, -1]).max()), e
