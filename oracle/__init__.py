@@ -28,14 +28,15 @@ identities, brute force with explicit masks, library routines on special
 cases, a chi-square test of losslessness).  No function is "parity unpinned".
 """
 from .numerics import widen, round_to_bf16, round_to_f32
-from .materialize import fuse_hiddens, project_kv, materialize, paged_write, gather_paged
+from .materialize import (fuse_hiddens, project_kv, materialize, paged_write, gather_paged,
+                          k_norm, rope_half_split, row_positions)
 from .attention import block_attention, block_attention_masked
 from .verify import (verify_greedy, verify_sample, gate, row_log_softmax, GreedyResult,
                      SampleResult, GateResult)
 
 __all__ = [
     "widen", "round_to_bf16", "round_to_f32", "fuse_hiddens", "project_kv", "materialize",
-    "paged_write", "gather_paged", "block_attention", "block_attention_masked",
+    "paged_write", "gather_paged", "k_norm", "rope_half_split", "row_positions", "block_attention", "block_attention_masked",
     "verify_greedy", "verify_sample", "gate", "row_log_softmax", "GreedyResult",
     "SampleResult", "GateResult",
 ]

@@ -17,9 +17,23 @@ Readings where the pages are silent (listed in the design doc as well):
 * h_ctx is rounded to the storage type before the K/V projections (the point
   where a kernel hands it from one GEMM to the next), and K/V are rounded to
   the storage type when written;
-* no normalisation, K-norm or RoPE is applied (the page's formula has none);
+* no normalisation of h_ctx (the page's formula has none);
 * the per-layer context transform named in section 4.1 has no body on the
   page and is taken as the identity.
+
+Optional K epilogue ([SGLang DFlash, section 4.1]: kv_proj_only, then
+apply_k_norm, then apply_k_rope(positions, k), then the prefix-valid write).
+The page names the two steps without their bodies; the readings are:
+* k_norm: RMSNorm of each head's K over head_dim with the layer's weight w
+  [D]:  k / sqrt(mean(k^2) + eps) * w;
+* rope: the rotary position embedding, half-split layout -- dims i and
+  i + D/2 (i < D/2) form a pair rotated by the angle pos * theta^(-2i/D):
+  (x, y) -> (x cos a - y sin a, y cos a + x sin a);
+* pos is the row's logical position (seq_start_pos[s] + r mod rows_per_seq,
+  the position that also chooses its cache slot);
+* the epilogue acts on the stored K projection (rounded to the storage type,
+  as the projection hands it over) and its result is rounded once when
+  stored; V is untouched.
 """
 import numpy as np
 
@@ -43,16 +57,53 @@ def project_kv(h_ctx, W, n_kv_heads, head_dim):
     return out.reshape(h_ctx.shape[0], n_kv_heads, head_dim)
 
 
-def materialize(hiddens, W_f, b_f, W_K, W_V, n_kv_heads, head_dim, dtype):
+def k_norm(K, weight, eps):
+    """Per-head RMSNorm over head_dim: K [T, Hkv, D] float64, weight [D]."""
+    ms = np.mean(K * K, axis=-1, keepdims=True)
+    return K / np.sqrt(ms + eps) * weight
+
+
+def rope_half_split(K, positions, theta):
+    """Rotary embedding of K [T, Hkv, D] at positions [T] (float64): dims i
+    and i + D/2 rotate by positions * theta^(-2i/D)."""
+    D = K.shape[-1]
+    half = D // 2
+    inv_freq = theta ** (-2.0 * np.arange(half) / D)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * inv_freq[None, :]   # [T, D/2]
+    c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    x, y = K[..., :half], K[..., half:]
+    return np.concatenate([x * c - y * s, y * c + x * s], axis=-1)
+
+
+def row_positions(T, rows_per_seq, seq_start_pos):
+    """Logical position of every row: seq_start_pos[r // rows_per_seq] + r mod rows_per_seq."""
+    r = np.arange(T)
+    return np.asarray(seq_start_pos, dtype=np.int64)[r // rows_per_seq] + r % rows_per_seq
+
+
+def materialize(hiddens, W_f, b_f, W_K, W_V, n_kv_heads, head_dim, dtype, k_norm_weight=None,
+                k_norm_eps=1e-6, rope_theta=0.0, rows_per_seq=None, seq_start_pos=None):
     """Full chain on stored inputs.  Returns dict with the stored-precision
     h_ctx [T, d] and per-layer K, V [T, Hkv, D] (float64 arrays whose values
-    lie on the storage grid)."""
+    lie on the storage grid).  With k_norm_weight (per layer [D]) and/or
+    rope_theta > 0, K goes through the epilogue (norm, then rotary embedding
+    at each row's logical position, which needs rows_per_seq and
+    seq_start_pos) before it is stored."""
     hid = [widen(h, dtype) for h in hiddens]
     Wf = widen(W_f, dtype)
     bf = None if b_f is None else widen(b_f, dtype)
     h = round_to(fuse_hiddens(hid, Wf, bf), dtype)
     K = [round_to(project_kv(h, widen(w, dtype), n_kv_heads, head_dim), dtype) for w in W_K]
     V = [round_to(project_kv(h, widen(w, dtype), n_kv_heads, head_dim), dtype) for w in W_V]
+    if k_norm_weight is not None or rope_theta > 0:
+        pos = row_positions(h.shape[0], rows_per_seq, seq_start_pos) if rope_theta > 0 else None
+        for l in range(len(K)):
+            k = K[l]
+            if k_norm_weight is not None:
+                k = k_norm(k, widen(k_norm_weight[l], dtype), k_norm_eps)
+            if rope_theta > 0:
+                k = rope_half_split(k, pos, rope_theta)
+            K[l] = round_to(k, dtype)
     return {"h_ctx": h, "K": K, "V": V}
 
 

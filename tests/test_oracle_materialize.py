@@ -111,3 +111,78 @@ def test_unmapped_page_is_skipped():
     cache = oracle.widen(c.cache_k[0], "f32")
     w = oracle.paged_write(cache, res["K"][0], bt, 20, c.seq_start_pos, None)
     assert w.sum() == 16
+
+
+# --- K epilogue: per-head RMSNorm, then the rotary embedding ----------------
+
+def test_k_epilogue_hand_example():
+    """One head, D = 4, k = (3, 4, 0, 0), w = (1, 2, 3, 4), eps = 0, position
+    1, theta = 10000.  By hand: mean(k^2) = 25/4, so the norm divides by 2.5
+    and scales by w: (1.2, 3.2, 0, 0).  Pairs are (0, 2) at frequency
+    10000^0 = 1 and (1, 3) at 10000^(-1/2) = 0.01; at position 1 the angles are
+    1 and 0.01 rad, and (x, 0) rotates to (x cos a, x sin a)."""
+    import math
+    k = np.array([[[3.0, 4.0, 0.0, 0.0]]])
+    out = oracle.rope_half_split(oracle.k_norm(k, np.array([1.0, 2.0, 3.0, 4.0]), 0.0),
+                                 np.array([1]), 10000.0)
+    want = [1.2 * math.cos(1.0), 3.2 * math.cos(0.01), 1.2 * math.sin(1.0), 3.2 * math.sin(0.01)]
+    np.testing.assert_allclose(out[0, 0], want, rtol=0, atol=1e-15)
+
+
+def test_k_norm_unit_weight_gives_unit_rms():
+    """With w = 1 and eps = 0 every head has mean square exactly 1; eps > 0
+    gives ms / (ms + eps)."""
+    rng = np.random.default_rng(40)
+    K = rng.standard_normal((7, 3, 16)) * rng.uniform(0.1, 10, (7, 3, 1))
+    out = oracle.k_norm(K, np.ones(16), 0.0)
+    np.testing.assert_allclose(np.mean(out ** 2, axis=-1), 1.0, rtol=0, atol=1e-14)
+    ms = np.mean(K ** 2, axis=-1)
+    out = oracle.k_norm(K, np.ones(16), 0.5)
+    np.testing.assert_allclose(np.mean(out ** 2, axis=-1), ms / (ms + 0.5), rtol=1e-13)
+
+
+def test_rope_identity_at_zero_norm_preserving_and_relative():
+    """Position 0 is the identity; every (i, i + D/2) pair keeps its length;
+    the dot product of two rotated vectors depends only on the difference
+    of their positions (shifting both positions by s changes nothing)."""
+    rng = np.random.default_rng(41)
+    D = 32
+    q = rng.standard_normal((1, 1, D))
+    k = rng.standard_normal((1, 1, D))
+    np.testing.assert_array_equal(oracle.rope_half_split(k, np.array([0]), 1e4), k)
+    r = oracle.rope_half_split(k, np.array([777]), 1e4)
+    np.testing.assert_allclose(r[..., :D // 2] ** 2 + r[..., D // 2:] ** 2,
+                               k[..., :D // 2] ** 2 + k[..., D // 2:] ** 2, rtol=1e-13)
+    for m, n, sft in [(5, 2, 11), (100, 3000, 257), (0, 31, 1000)]:
+        a = np.sum(oracle.rope_half_split(q, np.array([m]), 1e4) *
+                   oracle.rope_half_split(k, np.array([n]), 1e4))
+        b = np.sum(oracle.rope_half_split(q, np.array([m + sft]), 1e4) *
+                   oracle.rope_half_split(k, np.array([n + sft]), 1e4))
+        assert abs(a - b) < 1e-11 * max(1.0, abs(a))
+
+
+def test_k_epilogue_in_the_chain():
+    """In materialize: the epilogue changes K only (V and h_ctx as without
+    it), acts at each row's logical position, and theta = 0 with no weight
+    is the plain chain."""
+    rng = np.random.default_rng(42)
+    T, d, m, Hkv, D = 8, 16, 2, 2, 8
+    hs = [rng.standard_normal((T, d)).astype(np.float32) for _ in range(m)]
+    Wf = (rng.standard_normal((d, m * d)) * 0.2).astype(np.float32)
+    WK = [(rng.standard_normal((Hkv * D, d)) * 0.2).astype(np.float32)]
+    WV = [(rng.standard_normal((Hkv * D, d)) * 0.2).astype(np.float32)]
+    w = [rng.uniform(0.5, 1.5, D).astype(np.float32)]
+    plain = oracle.materialize(hs, Wf, None, WK, WV, Hkv, D, "f32")
+    same = oracle.materialize(hs, Wf, None, WK, WV, Hkv, D, "f32", rope_theta=0.0,
+                              rows_per_seq=4, seq_start_pos=[0, 0])
+    np.testing.assert_array_equal(plain["K"][0], same["K"][0])
+    epi = oracle.materialize(hs, Wf, None, WK, WV, Hkv, D, "f32", k_norm_weight=w,
+                             k_norm_eps=1e-6, rope_theta=1e4, rows_per_seq=4,
+                             seq_start_pos=[10, 500])
+    np.testing.assert_array_equal(plain["V"][0], epi["V"][0])
+    np.testing.assert_array_equal(plain["h_ctx"], epi["h_ctx"])
+    pos = np.array([10, 11, 12, 13, 500, 501, 502, 503])
+    np.testing.assert_array_equal(oracle.row_positions(T, 4, [10, 500]), pos)
+    want = oracle.round_to_f32(oracle.rope_half_split(
+        oracle.k_norm(plain["K"][0], w[0].astype(np.float64), 1e-6), pos, 1e4))
+    np.testing.assert_array_equal(epi["K"][0], want)
