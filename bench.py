@@ -83,6 +83,9 @@ def parse():
                          "ctx-KV materialisation; packed: training-style packed block mask")
     ap.add_argument("--sigma", type=float, default=1.0, help="sample-gate: draft = target + N(0, sigma)")
     ap.add_argument("--stages", type=int, default=4, help="sample-gate: DLoop stages of 8")
+    ap.add_argument("--k-epilogue", action="store_true",
+                    help="decode and prefill: K goes through the per-head RMSNorm and the rotary "
+                         "embedding (base 1e6) before it is stored")
     ap.add_argument("--causal", action="store_true",
                     help="decode and packed: causal mask inside the block (position i sees "
                          "block keys 0..i) instead of the bidirectional one")
@@ -92,7 +95,8 @@ def parse():
 class Step:
     """Device-resident inputs, outputs and workspaces of one draft step."""
 
-    def __init__(self, B, C, k, V, Ld, d=4096, m=5, Hq=32, Hkv=8, D=128, seed=0, causal=False):
+    def __init__(self, B, C, k, V, Ld, d=4096, m=5, Hq=32, Hkv=8, D=128, seed=0, causal=False,
+                 k_epilogue=False):
         import torch
         import block_diffusion_draft_ctx_amd as dfl
         self.dfl = dfl
@@ -114,6 +118,12 @@ class Step:
         self.b_f = randn(d, std=0.02)
         self.W_K = [randn(Hkv * D, d, std=0.02) for _ in range(Ld)]
         self.W_V = [randn(Hkv * D, d, std=0.02) for _ in range(Ld)]
+        # K epilogue: per-layer norm weights around 1, rotary base 1e6
+        self.k_epi = {}
+        if k_epilogue:
+            self.k_epi = dict(k_norm_weight=[(torch.rand(D, generator=g, device=dev) + 0.5).to(bf)
+                                             for _ in range(Ld)],
+                              k_norm_eps=1e-6, rope_theta=1e6)
         # pages for positions [0, C + k) of every request, physically shuffled
         self.max_pages = (C + k + 15) // 16
         num_pages = B * self.max_pages
@@ -149,7 +159,8 @@ class Step:
     def materialize(self):
         self.dfl.materialize_ctx_kv(self.hiddens, self.W_f, self.b_f, self.W_K, self.W_V,
                                     self.cache_k, self.cache_v, self.block_table, self.k,
-                                    self.seq_start, self.commit, workspace=self.ws_mat)
+                                    self.seq_start, self.commit, workspace=self.ws_mat,
+                                    **self.k_epi)
 
     def attention(self, l):
         self.dfl.block_attention(self.q[l], self.k_blk[l], self.v_blk[l], self.cache_k[l],
@@ -264,7 +275,12 @@ def cpu_baseline(st, n_req):
     dl = host(st.draft_logits[:n_req])
     ctx = np.full(n_req, C, dtype=np.int32)
     t0 = time.perf_counter()
-    res = oracle.materialize(hid, Wf, bf, WK, WV, st.Hkv, st.D, "bf16")
+    epi = {}
+    if st.k_epi:
+        epi = dict(k_norm_weight=[host(w) for w in st.k_epi["k_norm_weight"]],
+                   k_norm_eps=st.k_epi["k_norm_eps"], rope_theta=st.k_epi["rope_theta"],
+                   rows_per_seq=k, seq_start_pos=np.full(n_req, C))
+    res = oracle.materialize(hid, Wf, bf, WK, WV, st.Hkv, st.D, "bf16", **epi)
     for l in range(st.Ld):
         kc = oracle.widen(ck[l], "bf16")
         oracle.paged_write(kc, res["K"][l], bt_c, k, np.full(n_req, C), np.full(n_req, k))
@@ -400,17 +416,23 @@ def bench_prefill(args):
     start = torch.zeros(n_seq, dtype=torch.int32, device=dev)
     ws = torch.empty(dfl.lib().dflash_materialize_workspace_size(T, m, d, Ld, Hkv, D, dfl.BF16),
                      dtype=torch.uint8, device=dev)
+    epi = {}
+    if args.k_epilogue:
+        epi = dict(k_norm_weight=[(torch.rand(D, generator=g, device=dev) + 0.5).to(bf)
+                                  for _ in range(Ld)], k_norm_eps=1e-6, rope_theta=1e6)
 
     def step():
-        dfl.materialize_ctx_kv(hid, Wf, bfv, WK, WV, ck, cv, bt, rps, start, None, workspace=ws)
+        dfl.materialize_ctx_kv(hid, Wf, bfv, WK, WV, ck, cv, bt, rps, start, None, workspace=ws,
+                               **epi)
 
     ms = _events_ms(step, args.steps, args.warmup)
     flops = 2.0 * T * (m * d * d + 2 * Ld * Hkv * D * d)
     line = _base_line(args, "prefill ctx-KV materialisation, rows/sec", round(T / (ms * 1e-3), 1),
                       "rows/s", ms, f"prefill ctx-KV materialisation: {n_seq} x {rps} rows, 5 "
                       f"hiddens of 4096 fused by W_f [4096, 20480] + b_f, K and V of {Ld} draft "
-                      f"layers (8 KV heads x 128) written to 16-token paged caches", rows=T,
-                      d_model=d, draft_layers=Ld)
+                      f"layers (8 KV heads x 128) written to 16-token paged caches, K epilogue: "
+                      f"{_epi_name(args)}", rows=T, d_model=d, draft_layers=Ld,
+                      k_epilogue=_epi_name(args))
     line["roofline"] = {"kernel": "materialize (both GEMMs)", "bound": "mfma",
                         "achieved": round(flops / (ms * 1e-3) / 1e12, 1), "peak": BF16_PEAK / 1e12,
                         "unit": "TFLOP/s", "frac": round(flops / (ms * 1e-3) / BF16_PEAK, 4),
@@ -421,6 +443,10 @@ def bench_prefill(args):
 
 def _mask_name(args):
     return "causal" if args.causal else "bidirectional"
+
+
+def _epi_name(args):
+    return "k_norm + rope (base 1e6)" if args.k_epilogue else "none"
 
 
 def bench_packed(args):
@@ -495,7 +521,8 @@ def main():
               "packed": bench_packed}[args.workload]
         print(json.dumps(fn(args)), flush=True)
         return
-    st = Step(args.batch, args.ctx, args.block, args.vocab, args.layers, causal=args.causal)
+    st = Step(args.batch, args.ctx, args.block, args.vocab, args.layers, causal=args.causal,
+              k_epilogue=args.k_epilogue)
     print(f"[bench] inputs ready: B={st.B} ctx={st.C} k={st.k} V={st.V} layers={st.Ld}",
           file=sys.stderr, flush=True)
     if args.copy_calibration:
@@ -521,7 +548,7 @@ def main():
                                 f"fused draft argmax"),
                    "batch": st.B, "ctx": st.C, "block": st.k, "draft_layers": st.Ld,
                    "vocab": st.V, "d_model": st.d, "committed_rows": st.T,
-                   "block_mask": _mask_name(args)},
+                   "block_mask": _mask_name(args), "k_epilogue": _epi_name(args)},
         "roofline": {"kernel": "block_attention (per layer)", "bound": "hbm",
                      "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),

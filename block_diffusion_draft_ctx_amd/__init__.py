@@ -32,6 +32,11 @@ class KVLayer(ctypes.Structure):
                 ("num_pages", ctypes.c_int32), ("page_size", ctypes.c_int32)]
 
 
+class KEpilogue(ctypes.Structure):
+    _fields_ = [("k_norm_weight", ctypes.POINTER(ctypes.c_void_p)), ("k_norm_eps", ctypes.c_float),
+                ("rope_theta", ctypes.c_float)]
+
+
 class DFlashError(RuntimeError):
     def __init__(self, status, msg):
         super().__init__(msg)
@@ -58,7 +63,7 @@ def _declare(lib):
     lib.dflash_materialize_ctx_kv.restype = I32
     lib.dflash_materialize_ctx_kv.argtypes = [
         I64, I32, I32, PP, P, P, I32, I32, I32, PP, PP, ctypes.POINTER(KVLayer), P, I32, I32,
-        P, P, P, I32, P, SZ, P]
+        P, P, ctypes.POINTER(KEpilogue), P, I32, P, SZ, P]
     lib.dflash_attention_workspace_size.restype = SZ
     lib.dflash_attention_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, I32]
     lib.dflash_block_attention.restype = I32
@@ -169,10 +174,13 @@ def _pp(ptrs):
 def materialize_ctx_kv(hiddens: Sequence, W_f, b_f, W_K: Sequence, W_V: Sequence,
                        cache_k: Sequence, cache_v: Sequence, block_table, rows_per_seq: int,
                        seq_start_pos, commit_lens=None, h_ctx_out=None, workspace=None,
-                       stream=None):
+                       stream=None, k_norm_weight: Optional[Sequence] = None,
+                       k_norm_eps: float = 1e-6, rope_theta: float = 0.0):
     """dflash_materialize_ctx_kv.  hiddens: m tensors [T, d]; W_f [d, m*d];
     b_f [d] or None; W_K/W_V: per-layer [Hkv*D, d]; cache_k/cache_v: per-layer
-    [num_pages, 16, Hkv, D]; block_table [n_seq, max_pages] int32."""
+    [num_pages, 16, Hkv, D]; block_table [n_seq, max_pages] int32.  K
+    epilogue: k_norm_weight (per-layer [D] tensors, or None) and rope_theta
+    (0: none)."""
     L = lib()
     m = len(hiddens)
     T, d = hiddens[0].shape
@@ -192,10 +200,23 @@ def materialize_ctx_kv(hiddens: Sequence, W_f, b_f, W_K: Sequence, W_V: Sequence
     hp, _h = _pp([_ptr(h) for h in hiddens])
     kp, _k = _pp([_ptr(_dev(w, "W_K")) for w in W_K])
     vp, _v = _pp([_ptr(_dev(w, "W_V")) for w in W_V])
+    epi, _w = None, None
+    if k_norm_weight is not None or rope_theta:
+        if k_norm_weight is not None:
+            if len(k_norm_weight) != n_layers:
+                raise ValueError("k_norm_weight needs one tensor per layer")
+            for w in k_norm_weight:
+                _dev(w, "k_norm_weight")
+                if _dtype_code(w) != dt or w.numel() != D:
+                    raise ValueError("k_norm_weight tensors are [head_dim] in the storage dtype")
+            wp, _w = _pp([_ptr(w) for w in k_norm_weight])
+        else:
+            wp = None
+        epi = ctypes.pointer(KEpilogue(wp, float(k_norm_eps), float(rope_theta)))
     s = L.dflash_materialize_ctx_kv(
         T, m, d, hp, _ptr(_dev(W_f, "W_f")), _ptr(b_f), n_layers, Hkv, D, kp, vp, caches,
         _ptr(block_table), block_table.shape[1], rows_per_seq, _ptr(seq_start_pos),
-        _ptr(commit_lens), _ptr(h_ctx_out), dt, _ptr(ws), nws, _stream(stream))
+        _ptr(commit_lens), epi, _ptr(h_ctx_out), dt, _ptr(ws), nws, _stream(stream))
     _check(s, "dflash_materialize_ctx_kv")
     return h_ctx_out
 

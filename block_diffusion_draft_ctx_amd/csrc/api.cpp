@@ -2,6 +2,7 @@
 // Every host-visible argument error is reported before anything is enqueued.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 
 #include "../../include/dflash.h"
@@ -66,7 +67,8 @@ dflash_status dflash_materialize_ctx_kv(
     int64_t T, int m, int d_model, const void* const* hiddens, const void* W_f, const void* b_f,
     int n_layers, int n_kv_heads, int head_dim, const void* const* W_K, const void* const* W_V,
     const dflash_kv_layer* caches, const int32_t* block_table, int max_pages_per_seq,
-    int rows_per_seq, const int32_t* seq_start_pos, const int32_t* commit_lens, void* h_ctx_out,
+    int rows_per_seq, const int32_t* seq_start_pos, const int32_t* commit_lens,
+    const dflash_k_epilogue* k_epilogue, void* h_ctx_out,
     dflash_dtype dtype, void* ws, size_t ws_bytes, dflash_stream_t stream) {
   if (bad_dtype(dtype)) return DFLASH_E_ARG;
   if (T < 0 || m < 1 || d_model < 1 || n_layers < 1 || n_kv_heads < 1 || head_dim < 1)
@@ -104,6 +106,22 @@ dflash_status dflash_materialize_ctx_kv(
   a.block_table = block_table; a.max_pages = max_pages_per_seq;
   a.rows_per_seq = rows_per_seq; a.seq_start = seq_start_pos; a.commit_lens = commit_lens;
   a.h_out = h_ctx_out;
+  if (k_epilogue) {
+    const float eps = k_epilogue->k_norm_eps, theta = k_epilogue->rope_theta;
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return DFLASH_E_ARG;
+    if (!std::isfinite(theta) || !(theta == 0.f || theta > 1.f)) return DFLASH_E_ARG;
+    if (k_epilogue->k_norm_weight) {
+      for (int l = 0; l < n_layers; ++l) {
+        const void* w = k_epilogue->k_norm_weight[l];
+        if (!w) return DFLASH_E_ARG;
+        if (!al16(w)) return DFLASH_E_UNSUPPORTED;
+        a.k_norm_w[l] = w;
+      }
+      a.k_norm_on = true;
+    }
+    a.k_norm_eps = eps;
+    a.rope_theta = theta;
+  }
   const size_t need = materialize_ws_bytes(T, m, d_model, n_layers, n_kv_heads, head_dim, bf16);
   if (dflash_status s = check_ws(ws, ws_bytes, need)) return s;
   return hip_status(launch_materialize(bf16, a, ws, ws_bytes, static_cast<hipStream_t>(stream)));

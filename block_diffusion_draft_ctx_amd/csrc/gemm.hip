@@ -27,6 +27,7 @@
 //  * Tile order is XCD-aware: each XCD owns a contiguous run of tiles,
 //    walked in groups of 8 row tiles so their B columns stay in its L2.
 #include <algorithm>
+#include <cmath>
 
 #include "common.h"
 #include "launch.h"
@@ -638,6 +639,114 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmP p) {
   }
 }
 
+// K epilogue of materialisation ([SGLang DFlash], section 4.1: the K
+// projection goes through k_norm, then the rotary embedding at the row's
+// position, before the prefix-valid write), applied in place to the K rows
+// GEMM 2 has just written.  A group of D/8 consecutive lanes owns one (row,
+// layer), 8 dims of every head per lane: it evaluates its row's rotation
+// angles once for all heads, issues the loads of 8 heads together, and per
+// head takes the mean square as a shuffle sum over the group; the rotation
+// partner of dim i (i + D/2 or i - D/2) sits D/16 lanes away.  Angles are
+// reduced in double precision (revolutions = pos * theta^(-2i/D) / (2 pi),
+// fractional part kept) before the hardware sine and cosine, so they stay
+// accurate at long positions.
+struct KEpi {
+  const void* w[kML];   // per layer [D] norm weight (storage dtype), used when norm
+  float eps;
+  int norm, rope;
+  double l2theta;       // log2(rotary base)
+  int D, nl;
+};
+
+__device__ __forceinline__ void load8v(const uint16_t* p, float (&v)[8]) {
+  const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { v[2 * j] = bf16_lo(w[j]); v[2 * j + 1] = bf16_hi(w[j]); }
+}
+__device__ __forceinline__ void load8v(const float* p, float (&v)[8]) {
+  const f32x4v a = reinterpret_cast<const f32x4v*>(p)[0], b = reinterpret_cast<const f32x4v*>(p)[1];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { v[j] = a[j]; v[4 + j] = b[j]; }
+}
+__device__ __forceinline__ void store8v(uint16_t* p, const float (&v)[8]) {
+  u32x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
+  *reinterpret_cast<u32x4*>(p) = o;
+}
+__device__ __forceinline__ void store8v(float* p, const float (&v)[8]) {
+  reinterpret_cast<f32x4v*>(p)[0] = f32x4v{v[0], v[1], v[2], v[3]};
+  reinterpret_cast<f32x4v*>(p)[1] = f32x4v{v[4], v[5], v[6], v[7]};
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_k_epilogue(GemmP p, KEpi e) {
+  __shared__ double rev_rate[64];   // theta^(-2i/D) / (2 pi): revolutions per position, i < D/2
+  const int half = e.D / 2;
+  for (int i = threadIdx.x; i < half; i += 256)
+    rev_rate[i] = exp2(-(2.0 * i / e.D) * e.l2theta) * 0.15915494309189535;
+  __syncthreads();
+  const int G = e.D / 8;            // lanes per head (8 or 16: groups never straddle a wavefront)
+  const int Hkv = p.HD / e.D;
+  const int64_t items = (int64_t)p.M * e.nl;
+  const int lig = threadIdx.x % G;
+  const bool first = lig < G / 2;   // dims i < D/2: (x, y) -> (x c - y s, y c + x s)
+  const int64_t istride = (int64_t)gridDim.x * (256 / G);
+  constexpr int HB = 8;             // heads whose loads are in flight together
+  for (int64_t it = ((int64_t)blockIdx.x * 256 + threadIdx.x) / G; it < items; it += istride) {
+    // item -> (row, layer), rows fastest: the groups of a wavefront read
+    // consecutive rows, which sit in adjacent slots of one page
+    const int l = (int)(it / p.M);
+    const int row = (int)(it - (int64_t)l * p.M);
+    const int64_t slot = row_slot(p, row, l);
+    if (slot < 0) continue;         // uniform over the group
+    float cs[8], sn[8];
+    if (e.rope) {
+      const int s = row / p.rows_per_seq;
+      const int pos = p.seq_start[s] + (row - s * p.rows_per_seq);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        double rev = (double)pos * rev_rate[8 * (lig % (G / 2)) + j];
+        rev -= floor(rev);
+        // the hardware sine and cosine take their argument in revolutions
+        sn[j] = __builtin_amdgcn_sinf((float)rev);
+        cs[j] = __builtin_amdgcn_cosf((float)rev);
+      }
+    }
+    float w[8];
+    if (e.norm) load8v(static_cast<const T*>(pick(e.w, l)) + 8 * lig, w);
+    T* kp = static_cast<T*>(pick(p.ck, l)) + slot * p.HD + 8 * lig;
+    for (int h0 = 0; h0 < Hkv; h0 += HB) {
+      float v[HB][8];
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb)
+        if (h0 + hb < Hkv) load8v(kp + (h0 + hb) * e.D, v[hb]);
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        if (h0 + hb >= Hkv) break;   // uniform
+        if (e.norm) {
+          float ss = 0.f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) ss = fmaf(v[hb][j], v[hb][j], ss);
+          for (int o = G / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+          const float r = 1.f / sqrtf(ss / e.D + e.eps);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[hb][j] *= r * w[j];
+        }
+        if (e.rope) {
+          float pr[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) pr[j] = __shfl_xor(v[hb][j], G / 2, 64);
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            v[hb][j] = first ? fmaf(v[hb][j], cs[j], -pr[j] * sn[j]) : fmaf(v[hb][j], cs[j], pr[j] * sn[j]);
+        }
+        store8v(kp + (h0 + hb) * e.D, v[hb]);
+      }
+    }
+  }
+}
+
 struct Plan {
   int bm, bn;          // block tile (bf16)
   int ksplit, kchunk;
@@ -779,6 +888,20 @@ hipError_t launch_materialize(bool bf16, const MatArgs& a, void* ws, size_t ws_b
     p.seq_start = a.seq_start;
     p.commit = a.commit_lens;
     run_gemm(bf16, p, EPI_PAGED, st);
+    if (a.k_norm_on || a.rope_theta > 0.f) {
+      KEpi e{};
+      for (int l = 0; l < nl; ++l) e.w[l] = a.k_norm_w[l0 + l];
+      e.eps = a.k_norm_eps;
+      e.norm = a.k_norm_on ? 1 : 0;
+      e.rope = a.rope_theta > 0.f ? 1 : 0;
+      e.l2theta = a.rope_theta > 0.f ? std::log2((double)a.rope_theta) : 0.0;
+      e.D = a.D;
+      e.nl = nl;
+      const int64_t threads = (int64_t)a.T * nl * (a.D / 8);
+      const unsigned grid = (unsigned)std::min<int64_t>(cdiv(threads, 256), 16384);
+      if (bf16) hipLaunchKernelGGL(k_k_epilogue<uint16_t>, dim3(grid), dim3(256), 0, st, p, e);
+      else hipLaunchKernelGGL(k_k_epilogue<float>, dim3(grid), dim3(256), 0, st, p, e);
+    }
   }
   return hipGetLastError();
 }

@@ -90,6 +90,12 @@ struct MatArgs {
   const int32_t* seq_start;
   const int32_t* commit_lens;
   void* h_out;
+  // K epilogue (per-head RMSNorm, then the rotary embedding); off when both
+  // k_norm_on and rope_theta are zero
+  bool k_norm_on;
+  const void* k_norm_w[64];
+  float k_norm_eps;
+  float rope_theta;
 };
 constexpr int kMaxLayers = 64;
 size_t materialize_ws_bytes(int64_t T, int m, int d, int n_layers, int Hkv, int D, bool bf16);

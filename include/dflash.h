@@ -116,13 +116,35 @@ int dflash_version(void);
  *              r % rows_per_seq < commit_lens[s] are written (the prefix-valid
  *              write of the SGLang page)
  * h_ctx_out    [T, d_model] in the storage dtype, or NULL
+ * k_epilogue   NULL, or the K epilogue below
  * Rows whose page-table entry is outside [0, num_pages) are not written.
  * h_ctx is rounded to the storage dtype before the K/V projections; cache
  * entries are rounded to the storage dtype (bf16: round to nearest even).
+ * Rows that map to one cache slot (aliased pages) leave that slot undefined.
+ *
+ * K epilogue ([SGLang DFlash], section 4.1: kv_proj_only, then k_norm, then
+ * the rotary embedding at the token positions, then the prefix-valid write).
+ * The page names the steps without their bodies; this library computes, per
+ * row and kv-head, on the stored K projection and in fp32:
+ *   k_norm   k <- k / sqrt(mean(k^2) + eps) * w      (w: the layer's [head_dim])
+ *   rope     dims i and i + D/2 (i < D/2) rotate by a = pos * theta^(-2i/D):
+ *            (x, y) <- (x cos a - y sin a, y cos a + x sin a)
+ * with pos the row's logical position (the one that picks its cache slot),
+ * then rounds once to the storage dtype.  V is untouched.
+ *   k_norm_weight  HOST array of n_layers device pointers, each [head_dim] in
+ *                  the storage dtype and 16-byte aligned; NULL: no k_norm
+ *   k_norm_eps     >= 0 (finite)
+ *   rope_theta     rotary base > 1 (finite); 0: no rotary embedding
  * Shape limits: bf16 needs d_model % 128 == 0, (n_kv_heads*head_dim) % 128
  * == 0 and 16-byte aligned tensors; m <= 8; n_layers <= 64; head_dim in
  * {64, 128}.
  * ------------------------------------------------------------------------- */
+typedef struct {
+  const void* const* k_norm_weight;
+  float k_norm_eps;
+  float rope_theta;
+} dflash_k_epilogue;
+
 size_t dflash_materialize_workspace_size(int64_t T, int m, int d_model, int n_layers,
                                          int n_kv_heads, int head_dim, dflash_dtype dtype);
 
@@ -134,7 +156,7 @@ dflash_status dflash_materialize_ctx_kv(
     const dflash_kv_layer* caches,
     const int32_t* block_table, int max_pages_per_seq,
     int rows_per_seq, const int32_t* seq_start_pos, const int32_t* commit_lens,
-    void* h_ctx_out,
+    const dflash_k_epilogue* k_epilogue, void* h_ctx_out,
     dflash_dtype dtype, void* ws, size_t ws_bytes, dflash_stream_t stream);
 
 /* ---------------------------------------------------------------------------

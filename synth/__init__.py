@@ -163,6 +163,17 @@ def materialize_case(seed, *, dtype, m, d_model, n_layers, n_kv_heads, head_dim,
                            bt, num_pages, ck, cv)
 
 
+def k_norm_weights(seed, *, n_layers, head_dim, dtype):
+    """Per-layer norm weights [head_dim], uniform on [0.5, 1.5), stored in
+    the given dtype (a trained norm weight's scale, drawn at random)."""
+    rng = make_rng(seed)
+    out = []
+    for _ in range(n_layers):
+        x = rng.uniform(0.5, 1.5, size=head_dim).astype(np.float32)
+        out.append(bf16_bits(x) if dtype == BF16 else x)
+    return out
+
+
 # ----------------------------------------------------------------------------
 # block attention
 # ----------------------------------------------------------------------------

@@ -53,6 +53,19 @@ def rel_err(gpu, ref):
     return float(np.abs(gpu - ref).max() / rms)
 
 
+def rel_err_chained(gpu, ref, dtype):
+    """rel_err after allowing one unit in the last place of the stored value
+    (bf16: 2^-7 |ref|): for results that pass two storage roundings in a chain
+    (the K projection is stored, then the K epilogue's output), where the
+    kernel's and the oracle's values may each land on the other side of a
+    rounding boundary once."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = np.sqrt(np.mean(ref ** 2))
+    ulp = 2.0 ** -7 if dtype == "bf16" else 2.0 ** -23
+    return float(np.maximum(np.abs(gpu - ref) - ulp * np.abs(ref), 0.0).max() / rms)
+
+
 def log(msg):
     print(msg, flush=True)
     sys.stdout.flush()

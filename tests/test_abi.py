@@ -160,10 +160,16 @@ def test_attention_argument_errors(lib, kw, code):
     (dict(rps=5), dfl.E_ARG), (dict(T=-2), dfl.E_ARG), (dict(page=32), dfl.E_UNSUPPORTED),
     (dict(hid0=None), dfl.E_ARG), (dict(wf=None), dfl.E_ARG), (dict(nws=0), dfl.E_WORKSPACE),
     (dict(ck=FAKE + 2), dfl.E_UNSUPPORTED),    # bf16 caches take 16-byte stores
+    (dict(eps=-1.0), dfl.E_ARG), (dict(eps=float("nan")), dfl.E_ARG),
+    (dict(theta=0.5), dfl.E_ARG), (dict(theta=float("inf")), dfl.E_ARG),
+    (dict(theta=-2.0), dfl.E_ARG), (dict(knw=0), dfl.E_ARG), (dict(knw=FAKE + 4), dfl.E_UNSUPPORTED),
 ])
 def test_materialize_argument_errors(lib, kw, code):
-    a = dict(T=32, m=2, d=256, D=128, rps=16, page=16, hid0=FAKE, wf=FAKE, nws=1 << 26, ck=FAKE)
+    a = dict(T=32, m=2, d=256, D=128, rps=16, page=16, hid0=FAKE, wf=FAKE, nws=1 << 26, ck=FAKE,
+             eps=1e-6, theta=1e4, knw=FAKE)
     a.update(kw)
+    knw = (ctypes.c_void_p * 1)(a["knw"] or None)
+    epi = dfl.KEpilogue(ctypes.cast(knw, dfl.PP), a["eps"], a["theta"])
     m = a["m"]
     hid = (ctypes.c_void_p * max(m, 1))(*([a["hid0"]] + [FAKE] * (m - 1)))
     wk = (ctypes.c_void_p * 1)(FAKE)
@@ -171,6 +177,6 @@ def test_materialize_argument_errors(lib, kw, code):
     caches = (dfl.KVLayer * 1)(dfl.KVLayer(a["ck"], FAKE, 8, a["page"]))
     s = lib.dflash_materialize_ctx_kv(a["T"], m, a["d"], ctypes.cast(hid, dfl.PP), a["wf"], None,
                                       1, 1, a["D"], ctypes.cast(wk, dfl.PP), ctypes.cast(wv, dfl.PP),
-                                      caches, FAKE, 4, a["rps"], FAKE, None, None, dfl.BF16, WS,
-                                      a["nws"], None)
+                                      caches, FAKE, 4, a["rps"], FAKE, None, ctypes.byref(epi),
+                                      None, dfl.BF16, WS, a["nws"], None)
     assert s == code

@@ -7,12 +7,13 @@ import pytest
 import block_diffusion_draft_ctx_amd as dfl
 import oracle
 import synth
-from tests.gpu_util import TOL, bits, down, log, rel_err, up
+from tests.gpu_util import TOL, bits, down, log, rel_err, rel_err_chained, up
 
 pytestmark = pytest.mark.gpu
 
 
-def _run(c, want_h=True):
+def _run(c, want_h=True, epi=None):
+    """epi: None, or dict(w=per-layer norm weights or None, eps=..., theta=...)."""
     import torch
     kind = c.dtype
     ck = [up(x, kind) for x in c.cache_k]
@@ -21,21 +22,31 @@ def _run(c, want_h=True):
     h_out = None
     if want_h:
         h_out = torch.empty((c.T, c.d_model), dtype=hid[0].dtype, device=hid[0].device)
+    kw = {}
+    if epi is not None:
+        kw = dict(k_norm_weight=None if epi["w"] is None else [up(w, kind) for w in epi["w"]],
+                  k_norm_eps=epi["eps"], rope_theta=epi["theta"])
     dfl.materialize_ctx_kv(hid, up(c.W_f, kind), None if c.b_f is None else up(c.b_f, kind),
                            [up(w, kind) for w in c.W_K], [up(w, kind) for w in c.W_V], ck, cv,
                            up(c.block_table, "i32"), c.rows_per_seq, up(c.seq_start_pos, "i32"),
                            None if c.commit_lens is None else up(c.commit_lens, "i32"),
-                           h_ctx_out=h_out)
+                           h_ctx_out=h_out, **kw)
     return ck, cv, h_out
 
 
-def _check(c, ck, cv, h_out, rows=None):
+def _check(c, ck, cv, h_out, rows=None, epi=None):
     """Compare written slots (all rows, or the listed rows) with the oracle and
     the untouched slots with the sentinel."""
     T = c.T
     rows = np.arange(T) if rows is None else np.asarray(rows)
+    kw = {}
+    if epi is not None:
+        # the oracle's rows are the listed ones: give each its own position
+        pos = oracle.row_positions(T, c.rows_per_seq, c.seq_start_pos)[rows]
+        kw = dict(k_norm_weight=epi["w"], k_norm_eps=epi["eps"], rope_theta=epi["theta"],
+                  rows_per_seq=1, seq_start_pos=pos)
     ref = oracle.materialize([h[rows] for h in c.hiddens], c.W_f, c.b_f, c.W_K, c.W_V,
-                             c.n_kv_heads, c.head_dim, c.dtype)
+                             c.n_kv_heads, c.head_dim, c.dtype, **kw)
     if h_out is not None:
         e = rel_err(down(h_out)[rows], ref["h_ctx"])
         log(f"  h_ctx err {e:.2e}")
@@ -59,7 +70,10 @@ def _check(c, ck, cv, h_out, rows=None):
                 got.append(g[page, pos % 16])
                 want.append(rv[i])
             if got:
-                e = rel_err(np.array(got), np.array(want))
+                if epi is not None and name == "K":   # two storage points in the chain
+                    e = rel_err_chained(np.array(got), np.array(want), c.dtype)
+                else:
+                    e = rel_err(np.array(got), np.array(want))
                 assert e <= TOL[c.dtype], f"layer {l} {name}: err {e}"
             if len(rows) == T:   # every row checked: untouched slots keep the sentinel
                 untouched = gb[~written]
@@ -190,3 +204,56 @@ def test_materialize_prefill_full_size_sampled():
             e = rel_err(got, rv)
             assert e <= TOL["bf16"], (l, name, e)
     log(f"  {len(rows)} rows x {Ld} layers x K/V within {TOL['bf16']}")
+
+
+# --- K epilogue: per-head RMSNorm, then the rotary embedding at each row's position
+
+def _epi(seed, c, norm=True, theta=1e6, eps=1e-6):
+    w = synth.k_norm_weights(seed, n_layers=c.n_layers, head_dim=c.head_dim, dtype=c.dtype) \
+        if norm else None
+    return dict(w=w, eps=eps, theta=theta)
+
+
+@pytest.mark.parametrize("dtype,m,d,Ld,Hkv,D,n_seq,rps,start,commit,norm,theta,seed", [
+    ("f32", 5, 256, 1, 2, 64, 1, 64, [0], None, True, 1e4, 1501),          # tiny prefill
+    ("f32", 5, 256, 1, 2, 64, 1, 8, [64], "random", True, 1e4, 1502),      # then a decode commit
+    ("f32", 3, 96, 2, 1, 128, 3, 5, [0, 14, 30], [5, 2, 0], False, 1e6, 1503),   # rotary only
+    ("bf16", 5, 256, 2, 2, 64, 3, 16, None, "random", True, 0.0, 2501),    # norm only
+    ("bf16", 2, 384, 3, 1, 128, 2, 40, [3, 0], [40, 17], True, 1e6, 2502),
+    ("bf16", 5, 4096, 5, 8, 128, 8, 16, [8192, 100, 5000, 0, 77, 8000, 31, 4096], "random",
+     True, 1e6, 2503),                                                       # Llama-shaped decode
+    ("bf16", 2, 256, 1, 2, 128, 2, 16, [60000, 131000], None, True, 1e6, 2504),   # long positions
+])
+def test_materialize_k_epilogue_parity(dtype, m, d, Ld, Hkv, D, n_seq, rps, start, commit, norm,
+                                       theta, seed):
+    log(f"materialise + K epilogue dtype={dtype} layers={Ld} Hkv={Hkv} D={D} rows={n_seq}x{rps} "
+        f"norm={norm} theta={theta}")
+    c = synth.materialize_case(seed, dtype=dtype, m=m, d_model=d, n_layers=Ld, n_kv_heads=Hkv,
+                               head_dim=D, n_seq=n_seq, rows_per_seq=rps, start_pos=start,
+                               commit=commit)
+    epi = _epi(seed + 7, c, norm=norm, theta=theta)
+    ck, cv, h = _run(c, epi=epi)
+    _check(c, ck, cv, h, epi=epi)
+
+
+def test_materialize_k_epilogue_decode_launch_sampled():
+    """The decode launch (T = 1024, Llama-shaped, 5 layers) with the K
+    epilogue, rows at positions past 8192; sampled rows."""
+    c = synth.materialize_case(2510, dtype="bf16", m=5, d_model=4096, n_layers=5, n_kv_heads=8,
+                               head_dim=128, n_seq=64, rows_per_seq=16, start_pos=8192,
+                               commit="random")
+    epi = _epi(2511, c)
+    ck, cv, h = _run(c, epi=epi)
+    rows = np.sort(np.random.default_rng(3).choice(c.T, size=48, replace=False))
+    _check(c, ck, cv, h, rows=rows, epi=epi)
+
+
+def test_materialize_k_epilogue_prefill_sampled():
+    """Prefill shape (2 x 4096 rows, positions 0..4095, every row committed)
+    with the K epilogue; sampled rows."""
+    c = synth.materialize_case(2520, dtype="bf16", m=5, d_model=4096, n_layers=5, n_kv_heads=8,
+                               head_dim=128, n_seq=2, rows_per_seq=4096, start_pos=[0, 0])
+    epi = _epi(2521, c)
+    ck, cv, h = _run(c, want_h=False, epi=epi)
+    rows = np.sort(np.random.default_rng(4).choice(c.T, size=32, replace=False))
+    _check(c, ck, cv, None, rows=rows, epi=epi)
