@@ -83,6 +83,9 @@ def parse():
                          "ctx-KV materialisation; packed: training-style packed block mask")
     ap.add_argument("--sigma", type=float, default=1.0, help="sample-gate: draft = target + N(0, sigma)")
     ap.add_argument("--stages", type=int, default=4, help="sample-gate: DLoop stages of 8")
+    ap.add_argument("--no-gate-lse", action="store_true",
+                    help="sample-gate: the verify reduces the draft rows itself instead of reusing "
+                         "the normalisers the gates computed")
     ap.add_argument("--k-epilogue", action="store_true",
                     help="decode and prefill: K goes through the per-head RMSNorm and the rotary "
                          "embedding (base 1e6) before it is stored")
@@ -312,6 +315,35 @@ def _events_ms(fn, steps, warmup):
     return a.elapsed_time(b) / steps
 
 
+def _graph_ms(fn, steps, warmup):
+    """Average milliseconds of fn() replayed from a HIP graph: the calls are
+    captured once (all outputs and workspaces allocated beforehand, no
+    allocation or memset inside), then the graph is replayed `steps` times,
+    so no host launch overhead sits between the kernels."""
+    import torch
+    side = torch.cuda.Stream()   # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(max(1, warmup)):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
 def _base_line(args, metric, value, unit, ms, workload, higher=True, **cfg):
     return {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": higher,
@@ -350,16 +382,22 @@ def bench_sample_gate(args):
     wsg = torch.empty(max(256, dfl.lib().dflash_gate_workspace_size(B, kk, V)), dtype=torch.uint8,
                       device=dev)
     out = {}
-    gouts = [{} for _ in range(S)]
+    reuse = not args.no_gate_lse
+    # each stage's gate writes its columns of the chain's [B, L] row statistics
+    lse = torch.empty(B, L, dtype=torch.float32, device=dev)
+    rmax = torch.empty(B, L, dtype=torch.float32, device=dev)
+    gouts = [{"c": torch.empty(B, dtype=torch.float32, device=dev),
+              "go": torch.empty(B, dtype=torch.int32, device=dev),
+              "row_lse": lse[:, s_ * kk:(s_ + 1) * kk], "row_max": rmax[:, s_ * kk:(s_ + 1) * kk]}
+             for s_ in range(S)]
 
     def gates():
         for s_ in range(S):
-            gouts[s_] = dfl.gate(dstage[s_], tstage[s_], g=-0.5, row_stats=False,
-                                 out=gouts[s_] or None, workspace=wsg)
+            dfl.gate(dstage[s_], tstage[s_], g=-0.5, out=gouts[s_], workspace=wsg)
 
     def verify():
         out.update(dfl.verify_sample(tl, dl, drafts, u, u2, audit=False, out=out or None,
-                                     workspace=ws))
+                                     workspace=ws, draft_row_lse=lse if reuse else None))
 
     def step():
         gates()
@@ -368,14 +406,24 @@ def bench_sample_gate(args):
     ms = _events_ms(step, args.steps, args.warmup)
     vms = _events_ms(verify, args.steps, args.warmup)
     gms = _events_ms(gates, args.steps, args.warmup) / S
-    vbytes = B * (2 * L + 1) * V * 2
+    # the verify's algorithmic bytes: every target row, and the draft rows
+    # unless the gates already reduced them (then they count once, there)
+    vbytes = B * ((L + 1) + (0 if reuse else L)) * V * 2
     gbytes = B * kk * V * 2
+    step_bytes = B * (2 * L + 1) * V * 2    # each logit row once per step
     line = _base_line(args, "Qwen3-4B-shaped stochastic chain verify + DLoop gates, blocks/sec",
                       round(B / (ms * 1e-3), 1), "blocks/s", ms,
                       f"stochastic verify of a {S}-stage DLoop chain ({L} drafts + bonus) over vocab "
                       f"{V}, batch {B}, draft = target + N(0, {args.sigma}), T = 1, plus {S} gates "
-                      f"(c >= -0.5) on the stages' draft rows", batch=B, vocab=V, stages=S,
-                      chain=L, sigma=args.sigma)
+                      f"(c >= -0.5) on the stages' draft rows" +
+                      ("; the verify reuses the gates' draft-row normalisers" if reuse else ""),
+                      batch=B, vocab=V, stages=S, chain=L, sigma=args.sigma,
+                      gate_normalisers_reused=reuse)
+    line["step_hbm_frac"] = round(step_bytes / (ms * 1e-3) / HBM_PEAK, 4)
+    gms_step = _graph_ms(step, args.steps, args.warmup)
+    line["graph_replay"] = {"ms_per_step": round(gms_step, 4),
+                            "value": round(B / (gms_step * 1e-3), 1),
+                            "step_hbm_frac": round(step_bytes / (gms_step * 1e-3) / HBM_PEAK, 4)}
     line["roofline"] = {"kernel": "verify_sample (all its launches)", "bound": "hbm",
                         "achieved": round(vbytes / (vms * 1e-3) / 1e9, 1), "peak": HBM_PEAK / 1e9,
                         "unit": "GB/s", "frac": round(vbytes / (vms * 1e-3) / HBM_PEAK, 4),
@@ -555,6 +603,14 @@ def main():
                      "traffic": recorded_traffic(), "algorithmic_bytes": ab,
                      "avg_launch_us": round(attn_ms * 1e3, 2)},
     }
+    def whole_step():
+        st.materialize()
+        for l in range(st.Ld):
+            st.attention(l)
+        st.verify()
+
+    gms = _graph_ms(whole_step, args.steps, args.warmup)
+    out["graph_replay"] = {"ms_per_step": round(gms, 4), "value": round(st.B / (gms * 1e-3), 1)}
     if args.breakdown:
         tm = time_part(st.materialize, 10)
         tv = time_part(st.verify, 10)

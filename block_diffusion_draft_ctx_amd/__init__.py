@@ -77,11 +77,11 @@ def _declare(lib):
         I32, I32, I32, P, I64, P, I64, P, P, P, P, P, P, P, P, I32, P, SZ, P]
     lib.dflash_verify_sample.restype = I32
     lib.dflash_verify_sample.argtypes = [
-        I32, I32, I32, P, I64, P, I64, P, P, P, P, F, P, P, P, P, P, P, P, P, I32, P, SZ, P]
+        I32, I32, I32, P, I64, P, I64, P, P, P, P, F, P, P, P, P, P, P, P, P, P, I32, P, SZ, P]
     lib.dflash_gate_workspace_size.restype = SZ
     lib.dflash_gate_workspace_size.argtypes = [I32, I32, I32]
     lib.dflash_gate.restype = I32
-    lib.dflash_gate.argtypes = [I32, I32, I32, P, I64, P, P, F, F, P, P, P, P, I32, P, SZ, P]
+    lib.dflash_gate.argtypes = [I32, I32, I32, P, I64, P, P, F, F, P, P, P, P, I32, I32, P, SZ, P]
 
 
 def lib():
@@ -316,10 +316,12 @@ def verify_greedy(target_logits, draft_tokens=None, draft_logits=None, chain_len
 
 def verify_sample(target_logits, draft_logits, draft_tokens, u_accept, u_bonus, temperature=1.0,
                   chain_lens=None, prefix_lens=None, audit=True, out=None, workspace=None,
-                  stream=None):
+                  stream=None, draft_row_lse=None):
     """dflash_verify_sample.  Returns a dict with accept_len, bonus,
     commit_lens, new_seq_lens (if prefix_lens) and, with ``audit``, ratio
-    [B, L], beta [B] and cdf_gap [B]."""
+    [B, L], beta [B] and cdf_gap [B].  draft_row_lse [B, L] float32: the
+    draft rows' log-sum-exp as ``gate`` returns it (row_lse), to skip
+    reducing the draft rows again."""
     torch = _torch()
     L_ = lib()
     _logit_rows(target_logits, "target_logits")
@@ -332,7 +334,7 @@ def verify_sample(target_logits, draft_logits, draft_tokens, u_accept, u_bonus, 
     _i32(draft_tokens, "draft_tokens")
     _i32(chain_lens, "chain_lens")
     _i32(prefix_lens, "prefix_lens")
-    for n, t in (("u_accept", u_accept), ("u_bonus", u_bonus)):
+    for n, t in (("u_accept", u_accept), ("u_bonus", u_bonus), ("draft_row_lse", draft_row_lse)):
         if t is not None and t.dtype != torch.float32:
             raise TypeError(f"{n} must be float32")
         if t is not None:
@@ -351,7 +353,7 @@ def verify_sample(target_logits, draft_logits, draft_tokens, u_accept, u_bonus, 
     s = L_.dflash_verify_sample(
         B, L, V, _ptr(target_logits), _row_stride(target_logits), _ptr(draft_logits),
         _row_stride(draft_logits) if draft_logits is not None else 0, _ptr(draft_tokens),
-        _ptr(chain_lens), _ptr(u_accept), _ptr(u_bonus), float(temperature),
+        _ptr(chain_lens), _ptr(u_accept), _ptr(u_bonus), float(temperature), _ptr(draft_row_lse),
         _ptr(o["accept_len"]), _ptr(o["bonus"]), _ptr(o["commit_lens"]), _ptr(prefix_lens),
         _ptr(o.get("new_seq_lens")), _ptr(o.get("ratio")), _ptr(o.get("beta")),
         _ptr(o.get("cdf_gap")), dt, _ptr(ws), nws, _stream(stream))
@@ -377,11 +379,23 @@ def gate(draft_logits, draft_tokens, temperature=1.0, g=-0.5, valid_lens=None, r
     if row_stats:
         o.setdefault("row_max", torch.empty((B, n), dtype=torch.float32, device=dev))
         o.setdefault("row_lse", torch.empty((B, n), dtype=torch.float32, device=dev))
+    # row statistics may be column slices [B, n] of a wider [B, ld] array
+    # (a DLoop stage writing its columns of the chain's array)
+    ld = 0
+    for name in ("row_max", "row_lse"):
+        t = o.get(name)
+        if t is None:
+            continue
+        if not t.is_cuda or t.dtype != torch.float32 or tuple(t.shape) != (B, n) or t.stride(1) != 1:
+            raise ValueError(f"{name}: [B, n] float32 device tensor with unit column stride")
+        if ld and t.stride(0) != ld:
+            raise ValueError("row_max and row_lse need the same row stride")
+        ld = t.stride(0)
     need = L_.dflash_gate_workspace_size(B, n, V)
     ws, nws = _workspace(need, dev, workspace)
     s = L_.dflash_gate(B, n, V, _ptr(draft_logits), _row_stride(draft_logits), _ptr(draft_tokens),
                        _ptr(valid_lens), float(temperature), float(g), _ptr(o["c"]), _ptr(o["go"]),
-                       _ptr(o.get("row_max")), _ptr(o.get("row_lse")), dt, _ptr(ws), nws,
-                       _stream(stream))
+                       _ptr(o.get("row_max")), _ptr(o.get("row_lse")), ld if B > 1 else 0, dt,
+                       _ptr(ws), nws, _stream(stream))
     _check(s, "dflash_gate")
     return o

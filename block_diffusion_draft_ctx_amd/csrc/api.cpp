@@ -208,7 +208,8 @@ dflash_status dflash_verify_sample(int B, int L, int V, const void* target_logit
                                    int64_t t_row_stride, const void* draft_logits,
                                    int64_t d_row_stride, const int32_t* draft_tokens,
                                    const int32_t* chain_lens, const float* u_accept,
-                                   const float* u_bonus, float temperature, int32_t* accept_len,
+                                   const float* u_bonus, float temperature,
+                                   const float* draft_row_lse, int32_t* accept_len,
                                    int32_t* bonus, int32_t* commit_lens,
                                    const int32_t* prefix_lens, int32_t* new_seq_lens,
                                    float* ratio_out, float* beta_out, float* u_cdf_gap_out,
@@ -229,8 +230,8 @@ dflash_status dflash_verify_sample(int B, int L, int V, const void* target_logit
       dtype == DFLASH_BF16, B, L, V, target_logits, t_row_stride,
       draft_logits ? draft_logits : target_logits, draft_logits ? d_row_stride : t_row_stride,
       draft_tokens, chain_lens, u_accept, u_bonus, temperature, accept_len, bonus, commit_lens,
-      prefix_lens, new_seq_lens, ratio_out, beta_out, u_cdf_gap_out, ws,
-      static_cast<hipStream_t>(stream)));
+      prefix_lens, new_seq_lens, ratio_out, beta_out, u_cdf_gap_out,
+      L > 0 ? draft_row_lse : nullptr, ws, static_cast<hipStream_t>(stream)));
 }
 
 // -------------------------------------------------------------------- gate
@@ -242,18 +243,20 @@ size_t dflash_gate_workspace_size(int B, int n, int V) {
 dflash_status dflash_gate(int B, int n, int V, const void* draft_logits, int64_t row_stride,
                           const int32_t* draft_tokens, const int32_t* valid_lens,
                           float temperature, float g, float* c_out, int32_t* go_out,
-                          float* row_max_out, float* row_lse_out, dflash_dtype dtype, void* ws,
-                          size_t ws_bytes, dflash_stream_t stream) {
+                          float* row_max_out, float* row_lse_out, int stats_ld,
+                          dflash_dtype dtype, void* ws, size_t ws_bytes, dflash_stream_t stream) {
   if (bad_dtype(dtype)) return DFLASH_E_ARG;
   if (B < 0 || n < 1 || V < 1) return DFLASH_E_ARG;
   if (n > kMaxL) return DFLASH_E_UNSUPPORTED;
   if (!(temperature > 0.f) || temperature == __builtin_huge_valf() || g != g) return DFLASH_E_ARG;
+  if (stats_ld != 0 && stats_ld < n) return DFLASH_E_ARG;
   if (B == 0) return DFLASH_OK;
   if (!draft_logits || row_stride < V || !draft_tokens || !c_out || !go_out) return DFLASH_E_ARG;
   if (dflash_status s = check_ws(ws, ws_bytes, gate_ws_bytes(B, n, V))) return s;
   return hip_status(launch_gate(dtype == DFLASH_BF16, B, n, V, draft_logits, row_stride,
                                 draft_tokens, valid_lens, temperature, g, c_out, go_out,
-                                row_max_out, row_lse_out, ws, static_cast<hipStream_t>(stream)));
+                                row_max_out, row_lse_out, stats_ld ? stats_ld : n, ws,
+                                static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -41,12 +41,12 @@ hipError_t launch_verify_sample(bool bf16, int B, int L, int V, const void* tl, 
                                 const float* u_bonus, float temperature, int32_t* accept_len,
                                 int32_t* bonus, int32_t* commit_lens, const int32_t* prefix_lens,
                                 int32_t* new_seq_lens, float* ratio_out, float* beta_out,
-                                float* gap_out, void* ws, hipStream_t st);
+                                float* gap_out, const float* draft_lse, void* ws, hipStream_t st);
 
 hipError_t launch_gate(bool bf16, int B, int n, int V, const void* dl, int64_t rs,
                        const int32_t* tokens, const int32_t* valid_lens, float temperature,
                        float g, float* c_out, int32_t* go_out, float* row_max, float* row_lse,
-                       void* ws, hipStream_t st);
+                       int stats_ld, void* ws, hipStream_t st);
 
 // ----------------------------------------------------------------- attention
 struct AttnArgs {

@@ -18,6 +18,7 @@
 // rejection or the all-accepted bonus -- re-read the one chosen row pair
 // (cache-resident) to build the inverse CDF: per-chunk weight sums, then a
 // chunk-local scan inside the selected chunk.
+#include <algorithm>
 #include <climits>
 
 #include "common.h"
@@ -302,12 +303,16 @@ __device__ void reduce_lse_row(const float2* part, int row, int nc, float& m, fl
 // threads; thread t < 64 owns chain link t): merge each row's chunk partials
 // into its base-2 normalisers, form p/q at the drafted token, and find the
 // first rejected link by a ballot.  Every thread gets the request's ReqInfo.
+// With draft_lse (the draft rows' log-sum-exp at temperature T, as the gate
+// exports it) the draft rows have no chunk partials: their base-2
+// normaliser is lse * log2(e) with a unit sum.
 template <typename T>
 __device__ ReqInfo accept_scan(int b, int B, int L, int V, int nc, const float2* __restrict__ part,
                                const T* __restrict__ tl, int64_t ts, const T* __restrict__ dl,
                                int64_t ds, const int32_t* __restrict__ toks,
                                const int32_t* __restrict__ lens, const float* __restrict__ u,
-                               float a, float* __restrict__ ratio_out) {
+                               float a, float* __restrict__ ratio_out,
+                               const float* __restrict__ draft_lse) {
   const int t = threadIdx.x;
   __shared__ float Mt[65], St[65], Md[64], Sd[64], rat[64];
   __shared__ int okx[64];
@@ -316,7 +321,12 @@ __device__ ReqInfo accept_scan(int b, int B, int L, int V, int nc, const float2*
   const int nb = chain_of(lens, b, L, &bad);
   if (t <= nb) reduce_lse_row(part, b * (L + 1) + t, nc, Mt[t], St[t]);
   if (t < nb) {
-    reduce_lse_row(part, B * (L + 1) + b * L + t, nc, Md[t], Sd[t]);
+    if (draft_lse) {
+      Md[t] = draft_lse[b * L + t] * kLog2e;
+      Sd[t] = 1.f;
+    } else {
+      reduce_lse_row(part, B * (L + 1) + b * L + t, nc, Md[t], Sd[t]);
+    }
     const int x = toks[b * L + t];
     float r = __builtin_nanf("");
     okx[t] = (x >= 0 && x < V);
@@ -603,13 +613,13 @@ __global__ __launch_bounds__(kThreads) void k_bonus_partial(
     const T* __restrict__ dl, int64_t ds, float a, int row_nc, const float2* __restrict__ part,
     const int32_t* __restrict__ toks, const int32_t* __restrict__ lens,
     const float* __restrict__ u, float* __restrict__ ratio_out, ReqInfo* __restrict__ info,
-    float4* __restrict__ rpart) {
+    float4* __restrict__ rpart, const float* __restrict__ draft_lse) {
   const int c = blockIdx.x % nc;
   const int b = blockIdx.x / nc;
   // every chunk's workgroup runs the (cheap) acceptance scan itself; chunk 0
   // publishes it for the selection kernel
   const ReqInfo I = accept_scan<T>(b, B, L, V, row_nc, part, tl, ts, dl, ds, toks, lens, u, a,
-                                   c == 0 ? ratio_out : nullptr);
+                                   c == 0 ? ratio_out : nullptr, draft_lse);
   if (c == 0 && threadIdx.x == 0) info[b] = I;
   if (!I.err) bonus_chunk_sum<T, VEC>(c, chunk, V, tl, ts, dl, ds, a, b, L, I, rpart);
 }
@@ -635,7 +645,7 @@ __global__ __launch_bounds__(256) void k_gate_finalize(
     int B, int n, int V, int nc, const float2* __restrict__ part, const void* __restrict__ dl,
     int64_t rs, int bf16, const int32_t* __restrict__ toks, const int32_t* __restrict__ valid,
     int rows_all, float a, float g, float* __restrict__ c_out, int32_t* __restrict__ go_out,
-    float* __restrict__ row_max, float* __restrict__ row_lse) {
+    float* __restrict__ row_max, float* __restrict__ row_lse, int stats_ld) {
   const int b = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   __shared__ float term[64];
@@ -650,8 +660,8 @@ __global__ __launch_bounds__(256) void k_gate_finalize(
       const float S = wave_sum((M == neg_inf() || pc.x == neg_inf()) ? 0.f : pc.y * exp2f(pc.x - M));
       const float l2 = M + log2f(S);
       if (lane == 0) {
-        if (row_max) row_max[b * n + i] = M * kLn2;
-        if (row_lse) row_lse[b * n + i] = l2 * kLn2;
+        if (row_max) row_max[(int64_t)b * stats_ld + i] = M * kLn2;
+        if (row_lse) row_lse[(int64_t)b * stats_ld + i] = l2 * kLn2;
         if (i < nv) {
           const int x = toks[b * n + i];
           if (x < 0 || x >= V) {
@@ -702,23 +712,28 @@ void sample_impl(int B, int L, int V, const void* tl, int64_t ts, const void* dl
                  const int32_t* toks, const int32_t* lens, const float* u, const float* u2,
                  float temperature, int32_t* acc, int32_t* bonus, int32_t* commit,
                  const int32_t* prefix, int32_t* new_seq, float* ratio_out, float* beta_out,
-                 float* gap_out, void* ws, hipStream_t st) {
-  const int64_t rows = (int64_t)B * (2 * L + 1);
+                 float* gap_out, const float* draft_lse, void* ws, hipStream_t st) {
+  // with draft_lse only the target rows are reduced
+  const int64_t rows = (int64_t)B * (draft_lse ? L + 1 : 2 * L + 1);
   const VocabPlan pl = plan_vocab(rows, V);
   const VocabPlan pr = plan_vocab(2 * (int64_t)B, V);
   char* w = static_cast<char*>(ws);
   float2* part = reinterpret_cast<float2*>(w);
-  w += align256(sizeof(float2) * rows * pl.n_chunks);
+  {
+    const int64_t ar = (int64_t)B * (2 * L + 1), tr = (int64_t)B * (L + 1);
+    w += align256(sizeof(float2) * std::max(ar * plan_vocab(ar, V).n_chunks,
+                                            tr * plan_vocab(tr, V).n_chunks));
+  }
   ReqInfo* info = reinterpret_cast<ReqInfo*>(w);
   w += align256(sizeof(ReqInfo) * B);
   float4* rpart = reinterpret_cast<float4*>(w);
   const float a = kLog2e / temperature;
-  RowSet s0{tl, ts, L + 1, 1}, s1{dl, ds, L, 0};
+  RowSet s0{tl, ts, L + 1, 1}, s1{dl, ds, draft_lse ? 0 : L, 0};
   launch_lse<T, VEC>(s0, s1, B, L, V, lens, a, pl, rows, part, st);
   hipLaunchKernelGGL((k_bonus_partial<T, VEC>), dim3(B * pr.n_chunks), dim3(kThreads), 0, st, B,
                      L, V, pr.chunk, pr.n_chunks, static_cast<const T*>(tl), ts,
                      static_cast<const T*>(dl), ds, a, pl.n_chunks, part, toks, lens, u, ratio_out,
-                     info, rpart);
+                     info, rpart, draft_lse);
   hipLaunchKernelGGL((k_bonus_select<T>), dim3(B), dim3(kThreads), 0, st, L, V, pr.chunk,
                      pr.n_chunks, static_cast<const T*>(tl), ts, static_cast<const T*>(dl), ds, a,
                      info, rpart, u2, acc, bonus, commit, prefix, new_seq, beta_out, gap_out);
@@ -749,10 +764,12 @@ size_t greedy_ws_bytes(int B, int L, int V) {
 }
 
 size_t sample_ws_bytes(int B, int L, int V) {
-  const int64_t rows = (int64_t)B * (2 * L + 1);
-  const VocabPlan pl = plan_vocab(rows, V);
+  // partials of all 2L+1 rows, or of the L+1 target rows alone (finer chunks)
+  const int64_t rows = (int64_t)B * (2 * L + 1), trows = (int64_t)B * (L + 1);
+  const int64_t np = std::max(rows * plan_vocab(rows, V).n_chunks,
+                              trows * plan_vocab(trows, V).n_chunks);
   const VocabPlan pr = plan_vocab(2 * (int64_t)B, V);
-  return align256(sizeof(float2) * rows * pl.n_chunks) + align256(sizeof(ReqInfo) * B) +
+  return align256(sizeof(float2) * np) + align256(sizeof(ReqInfo) * B) +
          align256(sizeof(float4) * B * pr.n_chunks);
 }
 
@@ -793,23 +810,24 @@ hipError_t launch_verify_sample(bool bf16, int B, int L, int V, const void* tl, 
                                 const int32_t* lens, const float* u, const float* u2,
                                 float temperature, int32_t* acc, int32_t* bonus, int32_t* commit,
                                 const int32_t* prefix, int32_t* new_seq, float* ratio_out,
-                                float* beta_out, float* gap_out, void* ws, hipStream_t st) {
+                                float* beta_out, float* gap_out, const float* draft_lse, void* ws,
+                                hipStream_t st) {
   const int es = bf16 ? 2 : 4;
   const bool vec = aligned16(tl, ts, es) && aligned16(dl, ds, es);
   if (bf16) {
-    if (vec) sample_impl<uint16_t, true>(B, L, V, tl, ts, dl, ds, toks, lens, u, u2, temperature, acc, bonus, commit, prefix, new_seq, ratio_out, beta_out, gap_out, ws, st);
-    else sample_impl<uint16_t, false>(B, L, V, tl, ts, dl, ds, toks, lens, u, u2, temperature, acc, bonus, commit, prefix, new_seq, ratio_out, beta_out, gap_out, ws, st);
+    if (vec) sample_impl<uint16_t, true>(B, L, V, tl, ts, dl, ds, toks, lens, u, u2, temperature, acc, bonus, commit, prefix, new_seq, ratio_out, beta_out, gap_out, draft_lse, ws, st);
+    else sample_impl<uint16_t, false>(B, L, V, tl, ts, dl, ds, toks, lens, u, u2, temperature, acc, bonus, commit, prefix, new_seq, ratio_out, beta_out, gap_out, draft_lse, ws, st);
   } else {
-    if (vec) sample_impl<float, true>(B, L, V, tl, ts, dl, ds, toks, lens, u, u2, temperature, acc, bonus, commit, prefix, new_seq, ratio_out, beta_out, gap_out, ws, st);
-    else sample_impl<float, false>(B, L, V, tl, ts, dl, ds, toks, lens, u, u2, temperature, acc, bonus, commit, prefix, new_seq, ratio_out, beta_out, gap_out, ws, st);
+    if (vec) sample_impl<float, true>(B, L, V, tl, ts, dl, ds, toks, lens, u, u2, temperature, acc, bonus, commit, prefix, new_seq, ratio_out, beta_out, gap_out, draft_lse, ws, st);
+    else sample_impl<float, false>(B, L, V, tl, ts, dl, ds, toks, lens, u, u2, temperature, acc, bonus, commit, prefix, new_seq, ratio_out, beta_out, gap_out, draft_lse, ws, st);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_gate(bool bf16, int B, int n, int V, const void* dl, int64_t rs,
                        const int32_t* toks, const int32_t* valid, float temperature, float g,
-                       float* c_out, int32_t* go_out, float* row_max, float* row_lse, void* ws,
-                       hipStream_t st) {
+                       float* c_out, int32_t* go_out, float* row_max, float* row_lse,
+                       int stats_ld, void* ws, hipStream_t st) {
   const int64_t rows = (int64_t)B * n;
   const VocabPlan pl = plan_vocab(rows, V);
   float2* part = static_cast<float2*>(ws);
@@ -828,7 +846,7 @@ hipError_t launch_gate(bool bf16, int B, int n, int V, const void* dl, int64_t r
   }
   hipLaunchKernelGGL(k_gate_finalize, dim3(B), dim3(256), 0, st, B, n, V, pl.n_chunks, part, dl, rs,
                      bf16 ? 1 : 0, toks, valid, rows_all ? 1 : 0, a, g, c_out, go_out, row_max,
-                     row_lse);
+                     row_lse, stats_ld);
   return hipGetLastError();
 }
 

@@ -266,6 +266,13 @@ dflash_status dflash_verify_greedy(
  * target_logits [B, L+1, V] rows (t_row_stride apart); draft_logits [B, L, V]
  * rows (d_row_stride apart); draft_tokens [B, L]; chain_lens [B] or NULL;
  * u_accept [B, L] and u_bonus [B] in [0, 1); temperature > 0.
+ * draft_row_lse [B, L] fp32 or NULL: logsumexp(draft row / T) of every draft
+ *   row, as dflash_gate's row_lse_out gives it for the stages of a DLoop
+ *   chain ([DLoop], "机制一：置信度门控" computes these normalisers during
+ *   drafting).  When given, the draft rows are not reduced again: the verify
+ *   reads the target rows, the drafted tokens' draft logits and the one
+ *   rejected draft row.  It must come from the same draft_logits and
+ *   temperature.
  * Outputs accept_len, bonus, commit_lens [B]; new_seq_lens as for greedy.
  * Audit outputs (each may be NULL):
  *   ratio_out [B, L]  p/q of every draft within the chain (NaN past it)
@@ -281,6 +288,7 @@ dflash_status dflash_verify_sample(
     const void* draft_logits, int64_t d_row_stride,
     const int32_t* draft_tokens, const int32_t* chain_lens,
     const float* u_accept, const float* u_bonus, float temperature,
+    const float* draft_row_lse,
     int32_t* accept_len, int32_t* bonus, int32_t* commit_lens,
     const int32_t* prefix_lens, int32_t* new_seq_lens,
     float* ratio_out, float* beta_out, float* u_cdf_gap_out,
@@ -295,8 +303,11 @@ dflash_status dflash_verify_sample(
  *   go[b] = c[b] >= g
  * draft_logits [B, n, V] rows (row_stride apart); draft_tokens [B, n];
  * valid_lens [B] in [0, n] or NULL (= n); temperature > 0.
- * c_out [B] fp32, go_out [B] int32 (1/0); row_max_out, row_lse_out [B, n]
- * fp32 (max and logsumexp of row / T) or NULL.
+ * c_out [B] fp32, go_out [B] int32 (1/0); row_max_out, row_lse_out fp32
+ * (max and logsumexp of row / T) or NULL: row i of request b goes to
+ * element b * stats_ld + i (stats_ld >= n, or 0 for n), so the stages of a
+ * DLoop chain can write their columns of one [B, chain] array, the layout
+ * dflash_verify_sample's draft_row_lse reads.
  * In band: a token outside [0, V) or a valid length outside [0, n] gives
  * c = NaN and go = 0.
  * Limits: 1 <= n <= 64.
@@ -307,7 +318,7 @@ dflash_status dflash_gate(
     int B, int n, int V, const void* draft_logits, int64_t row_stride,
     const int32_t* draft_tokens, const int32_t* valid_lens,
     float temperature, float g, float* c_out, int32_t* go_out,
-    float* row_max_out, float* row_lse_out,
+    float* row_max_out, float* row_lse_out, int stats_ld,
     dflash_dtype dtype, void* ws, size_t ws_bytes, dflash_stream_t stream);
 
 #ifdef __cplusplus

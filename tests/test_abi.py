@@ -78,10 +78,10 @@ def test_zero_batch_is_a_noop(lib):
                                       None, 1, 0, None, 0.0, dfl.MASK_BIDIRECTIONAL, None, None,
                                       dfl.BF16, dfl.BF16, None, 0, None) == dfl.OK
     assert lib.dflash_gate(0, 8, 100, None, 100, None, None, 1.0, -0.5, None, None, None, None,
-                           dfl.BF16, None, 0, None) == dfl.OK
+                           0, dfl.BF16, None, 0, None) == dfl.OK
     assert lib.dflash_verify_sample(0, 8, 100, None, 100, None, 100, None, None, None, None, 1.0,
-                                    None, None, None, None, None, None, None, None, dfl.BF16,
-                                    None, 0, None) == dfl.OK
+                                    None, None, None, None, None, None, None, None, None,
+                                    dfl.BF16, None, 0, None) == dfl.OK
 
 
 def _greedy(lib, **kw):
@@ -114,7 +114,7 @@ def test_sample_argument_errors(lib, kw, code):
     a = dict(T=1.0, dl=FAKE, u=FAKE, u2=FAKE, nws=1 << 24)
     a.update(kw)
     s = lib.dflash_verify_sample(2, 3, 100, FAKE, 100, a["dl"], 100, FAKE, None, a["u"], a["u2"],
-                                 a["T"], FAKE, FAKE, FAKE, None, None, None, None, None,
+                                 a["T"], None, FAKE, FAKE, FAKE, None, None, None, None, None,
                                  dfl.BF16, WS, a["nws"], None)
     assert s == code
 
@@ -123,13 +123,13 @@ def test_sample_argument_errors(lib, kw, code):
 @pytest.mark.parametrize("kw,code", [
     (dict(n=0), dfl.E_ARG), (dict(n=65), dfl.E_UNSUPPORTED), (dict(T=-1.0), dfl.E_ARG),
     (dict(g=float("nan")), dfl.E_ARG), (dict(rs=5), dfl.E_ARG), (dict(c=None), dfl.E_ARG),
-    (dict(nws=0), dfl.E_WORKSPACE),
+    (dict(nws=0), dfl.E_WORKSPACE), (dict(ld=7), dfl.E_ARG), (dict(ld=-1), dfl.E_ARG),
 ])
 def test_gate_argument_errors(lib, kw, code):
-    a = dict(n=8, T=1.0, g=-0.5, rs=100, c=FAKE, nws=1 << 20)
+    a = dict(n=8, T=1.0, g=-0.5, rs=100, c=FAKE, nws=1 << 20, ld=32)
     a.update(kw)
     s = lib.dflash_gate(2, a["n"], 100, FAKE, a["rs"], FAKE, None, a["T"], a["g"], a["c"], FAKE,
-                        None, None, dfl.BF16, WS, a["nws"], None)
+                        None, None, a["ld"], dfl.BF16, WS, a["nws"], None)
     assert s == code
 
 

@@ -272,3 +272,34 @@ def test_gate_invalid_token_gives_nan():
     r = dfl.gate(up(c.draft_logits, "f32"), up(x, "i32"))
     cg = down(r["c"])
     assert np.isnan(cg[1]) and down(r["go"])[1] == 0 and np.isfinite(cg[[0, 2]]).all()
+
+
+# --- draft normalisers reused from the gate --------------------------------
+
+@pytest.mark.parametrize("source", ["oracle", "gpu"])
+def test_sample_reuses_gate_row_lse(source):
+    """DLoop: the gate computes every draft row's log-sum-exp while drafting;
+    the chain verify given those (draft_row_lse) reduces only the target rows
+    and must match the oracle as the full pass does (Qwen-shaped, 4 stages)."""
+    import torch
+    B, L, V, T = 16, 32, V_QWEN, 1.0
+    c = synth.sample_case(3020, dtype="bf16", B=B, L=L, V=V, sigma=1.0, temperature=T)
+    dl = up(c.draft_logits, "bf16")
+    toks = up(c.draft_tokens, "i32")
+    if source == "oracle":
+        lse = oracle.gate(c.draft_logits, c.draft_tokens, "bf16", temperature=T).row_lse
+        lse_t = torch.from_numpy(lse.astype(np.float32)).to(dl.device)
+    else:
+        # one gate per stage of 8 drafts, as the drafter runs it, each writing
+        # its columns of the chain's [B, L] statistics
+        lse_t = torch.full((B, L), float("nan"), dtype=torch.float32, device=dl.device)
+        mx = torch.empty_like(lse_t)
+        for s in range(0, L, 8):
+            dfl.gate(dl[:, s:s + 8].contiguous(), toks[:, s:s + 8].contiguous(), temperature=T,
+                     out={"row_lse": lse_t[:, s:s + 8], "row_max": mx[:, s:s + 8]})
+        assert torch.isfinite(lse_t).all()
+    r = dfl.verify_sample(up(c.target_logits, "bf16"), dl, toks, up(c.u_accept, "f32"),
+                          up(c.u_bonus, "f32"), temperature=T, draft_row_lse=lse_t.contiguous())
+    ref = oracle.verify_sample(c.target_logits, c.draft_logits, c.draft_tokens, c.u_accept,
+                               c.u_bonus, "bf16", temperature=T)
+    _sample_compare(c, r, ref, f"gate lse from {source}")
