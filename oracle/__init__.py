@@ -14,7 +14,9 @@ The pages this follows (cited by short title and section throughout):
   (10100.com/article/149138197) -- sections 3 (decode) and 4.1 (KV materialisation).
 * [Spec-decoding tutorial] "让大模型快 8 倍：从投机解码到 DDTree 的完整原理"
   (liyongzhi.xyz/posts/2026/04/speculative-decoding/) -- sections 2, 3 (the
-  acceptance rule, the residual distribution and the worked cat/dog example), 4.
+  acceptance rule, the residual distribution and the worked cat/dog example), 4,
+  and 6 (DDTree: the draft tree, its best-first growth under a node budget, the
+  ancestor-only mask and the greedy walk; followed by ``tree.py``).
 * [DLoop] "DLoop 完全拆解：让一次验证覆盖多个草稿阶段的循环投机解码"
   (pinghaoyang.com.cn/aigc/posts/dloop-looped-speculative-decoding/) --
   "机制一：置信度门控" and "验证与无损性".
@@ -33,10 +35,12 @@ from .materialize import (fuse_hiddens, project_kv, materialize, paged_write, ga
 from .attention import block_attention, block_attention_masked
 from .verify import (verify_greedy, verify_sample, gate, row_log_softmax, GreedyResult,
                      SampleResult, GateResult)
+from .tree import topk_logprobs, build_tree, ancestor_mask, walk_greedy, target_argmax, Tree, TreeWalk
 
 __all__ = [
     "widen", "round_to_bf16", "round_to_f32", "fuse_hiddens", "project_kv", "materialize",
     "paged_write", "gather_paged", "k_norm", "rope_half_split", "row_positions", "block_attention", "block_attention_masked",
     "verify_greedy", "verify_sample", "gate", "row_log_softmax", "GreedyResult",
-    "SampleResult", "GateResult",
+    "SampleResult", "GateResult", "topk_logprobs", "build_tree", "ancestor_mask", "walk_greedy",
+    "target_argmax", "Tree", "TreeWalk",
 ]

@@ -414,3 +414,43 @@ def gate_case(seed, *, dtype, B, n, V, std=3.0, temperature=1.0, g=-0.5, boost=N
     else:
         vl = np.asarray(valid, dtype=np.int32)
     return GateCase(dtype, B, n, V, float(temperature), float(g), db, toks.astype(np.int32), vl)
+
+
+# ----------------------------------------------------------------------------
+# DDTree draft trees
+# ----------------------------------------------------------------------------
+
+@dataclass
+class TreeCase:
+    dtype: str
+    B: int
+    n_pos: int
+    V: int
+    draft_logits: np.ndarray    # [B, n_pos, V]: row d is block position d + 1
+
+
+def tree_case(seed, *, dtype, B, n_pos, V, std=2.0, peaked=0.0) -> TreeCase:
+    """Draft logits ~ N(0, std) per block position; with ``peaked`` > 0 a
+    random token per row is raised by that amount (a confident drafter, so
+    that the best-first tree grows deep along likely paths)."""
+    rng = make_rng(seed)
+    x = rng.standard_normal(size=(B, n_pos, V), dtype=np.float32) * np.float32(std)
+    if peaked > 0:
+        top = rng.integers(0, V, size=(B, n_pos))
+        for b in range(B):
+            for i in range(n_pos):
+                x[b, i, top[b, i]] += np.float32(peaked)
+    return TreeCase(dtype, B, n_pos, V, bf16_bits(x) if dtype == BF16 else x)
+
+
+def tree_target_logits(seed, *, dtype, B, n_rows, V, std=3.0, follow=None, boost=30.0):
+    """Target logits [B, n_rows, V] ~ N(0, std).  ``follow``: per request a
+    list of (row, token) pairs whose token is raised by ``boost``, so the
+    target's prediction at that row is known by construction."""
+    rng = make_rng(seed)
+    x = rng.standard_normal(size=(B, n_rows, V), dtype=np.float32) * np.float32(std)
+    if follow is not None:
+        for b, pairs in enumerate(follow):
+            for r, t in pairs:
+                x[b, r, t] += np.float32(boost)
+    return bf16_bits(x) if dtype == BF16 else x

@@ -1,0 +1,148 @@
+"""Pins for the DDTree oracle: top-K against a brute-force selection and a
+library log-softmax, the best-first tree against a hand example and against
+exhaustive search for the best ancestor-closed node set, the ancestor mask
+against a path walk, and the greedy walk against the pages' example and
+against the chain verify it reduces to when the tree is one path."""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+import synth
+
+
+def test_topk_matches_brute_force_selection_and_log_softmax():
+    rng = np.random.default_rng(60)
+    x = (rng.standard_normal((2, 3, 200)) * 2).astype(np.float32)
+    x[0, 0, 7] = x[0, 0, 50] = x[0, 0, 120] = 9.0       # a three-way tie at the top
+    x[1, 2, 3] = x[1, 2, 4] = -9.0                       # ties far below: irrelevant
+    tok, lp = oracle.topk_logprobs(x, "f32", K=5, temperature=0.7)
+    ref_lp = scipy.special.log_softmax(x.astype(np.float64) / 0.7, axis=-1)
+    for b in range(2):
+        for i in range(3):
+            row = x[b, i].astype(np.float64)
+            taken, picks = np.zeros(200, dtype=bool), []
+            for _ in range(5):                           # repeated maximum, lowest index first
+                best = max(v for v, t in zip(row, taken) if not t)
+                j = next(j for j in range(200) if not taken[j] and row[j] == best)
+                taken[j] = True
+                picks.append(j)
+            assert tok[b, i].tolist() == picks
+            np.testing.assert_allclose(lp[b, i], ref_lp[b, i, picks], rtol=0, atol=1e-12)
+    assert tok[0, 0, :3].tolist() == [7, 50, 120]
+
+
+def _lists(probs):
+    """Per-position top-K as (tokens, logp) from explicit probability lists."""
+    tokens = np.array([[t for t, _ in pos] for pos in probs])
+    logp = np.log(np.array([[p for _, p in pos] for pos in probs]))
+    return tokens, logp
+
+
+def test_best_first_hand_example():
+    """Positions 1-3 offer (cat .7, dog .2), (sat .6, lay .3), (on .65, in .2);
+    K = 2, budget 5.  By hand the pops are cat .70, cat>sat .42,
+    cat>sat>on .273, cat>lay .21, dog .20 (cat>sat>in .084 and dog>sat .12 stay
+    in the heap)."""
+    CAT, DOG, SAT, LAY, ON, IN = 10, 11, 20, 21, 30, 31
+    tokens, logp = _lists([[(CAT, .7), (DOG, .2)], [(SAT, .6), (LAY, .3)], [(ON, .65), (IN, .2)]])
+    t = oracle.build_tree(tokens, logp, budget=5)
+    assert t.token.tolist() == [CAT, SAT, ON, LAY, DOG]
+    assert t.parent.tolist() == [-1, 0, 1, 0, -1]
+    assert t.depth.tolist() == [1, 2, 3, 2, 1]
+    np.testing.assert_allclose(np.exp(t.score), [.7, .42, .273, .21, .2], rtol=1e-12)
+    # one more node: dog>sat (.12) beats cat>lay>on (.1365)? no: .1365 > .12
+    t6 = oracle.build_tree(tokens, logp, budget=6)
+    assert t6.token[5] == ON and t6.parent[5] == 3
+
+
+def _all_nodes(K, n):
+    return [p for d in range(1, n + 1) for p in itertools.product(range(K), repeat=d)]
+
+
+@pytest.mark.parametrize("K,n,bmax,seed", [(2, 3, 7, 61), (3, 2, 7, 62), (2, 4, 7, 63),
+                                            (3, 3, 5, 64)])
+def test_best_first_is_optimal_among_ancestor_closed_sets(K, n, bmax, seed):
+    """The best-first tree of B nodes has the largest total node probability
+    (the expected number of accepted tokens under independent positions)
+    among all node sets of size B that contain every member's ancestors."""
+    rng = np.random.default_rng(seed)
+    logp = np.log(np.sort(rng.dirichlet(np.ones(K + 2), size=n)[:, :K], axis=1)[:, ::-1])
+    tokens = np.arange(n * K).reshape(n, K)
+    nodes = _all_nodes(K, n)
+    score = {p: sum(logp[d, r] for d, r in enumerate(p)) for p in nodes}
+    for B in range(1, min(len(nodes), bmax) + 1):
+        best = -1.0
+        for subset in itertools.combinations(nodes, B):
+            s = set(subset)
+            if all(p[:-1] in s for p in subset if len(p) > 1):
+                best = max(best, sum(math.exp(score[p]) for p in subset))
+        t = oracle.build_tree(tokens, logp, budget=B)
+        assert abs(np.exp(t.score).sum() - best) < 1e-12
+
+
+def test_tree_order_properties_on_synthetic_draft():
+    """Parents precede children, scores never increase along the pop order,
+    children scores are the parent's plus their position's log-probability,
+    and siblings carry distinct tokens."""
+    x = synth.tree_case(65, dtype="f32", B=2, n_pos=7, V=500, std=2.0).draft_logits
+    tok, lp = oracle.topk_logprobs(x, "f32", K=4)
+    for b in range(2):
+        t = oracle.build_tree(tok[b], lp[b], budget=60)
+        assert len(t.token) == 60
+        assert all(t.parent[i] < i for i in range(60))
+        assert np.all(np.diff(t.score) <= 1e-15)
+        for i in range(60):
+            base = 0.0 if t.parent[i] < 0 else t.score[t.parent[i]]
+            assert abs(t.score[i] - (base + lp[b, t.depth[i] - 1, t.rank[i]])) < 1e-12
+            if t.parent[i] >= 0:
+                assert t.depth[i] == t.depth[t.parent[i]] + 1
+        kids = {}
+        for i in range(60):
+            kids.setdefault(int(t.parent[i]), []).append(int(t.token[i]))
+        assert all(len(v) == len(set(v)) for v in kids.values())
+
+
+def test_ancestor_mask_matches_path_walk():
+    parent = np.array([-1, 0, 1, 0, -1, 4, 2, 6])
+    m = oracle.ancestor_mask(parent)
+    for i in range(len(parent)):
+        anc = {i}
+        j = parent[i]
+        while j >= 0:
+            anc.add(int(j))
+            j = parent[j]
+        assert set(np.flatnonzero(m[i]).tolist()) == anc
+        assert (m[i] == (m[parent[i]] | (np.arange(len(parent)) == i))).all() if parent[i] >= 0 \
+            else m[i].sum() == 1
+
+
+def test_walk_pages_example():
+    """[Spec-decoding tutorial, section 6.5]: root -> cat (accepted) -> sat
+    (accepted) -> on (rejected); dog is rejected at the root.  Two tokens are
+    committed and the bonus is the target's prediction after sat."""
+    CAT, DOG, SAT, LAY, ON, THE = 1, 2, 3, 4, 5, 6
+    token = np.array([CAT, DOG, SAT, LAY, ON])
+    parent = np.array([-1, -1, 0, 0, 2])
+    tp = np.array([CAT, SAT, 9, THE, 9, 9])   # after root, after node 0 (cat), 1 (dog), 2 (sat), ...
+    w = oracle.walk_greedy(token, parent, tp)
+    assert (w.accept_len, w.bonus, w.path) == (2, THE, [0, 2])
+    w = oracle.walk_greedy(token, parent, np.array([7, SAT, 9, THE, 9, 9]))
+    assert (w.accept_len, w.bonus, w.path) == (0, 7, [])
+    w = oracle.walk_greedy(token, parent, np.array([CAT, SAT, 9, ON, 9, 8]))
+    assert (w.accept_len, w.bonus, w.path) == (3, 8, [0, 2, 4])   # a leaf: bonus after it
+
+
+def test_walk_on_a_single_path_is_the_chain_verify():
+    """With K = 1 the tree is one path: the walk equals greedy chain
+    verification of those drafts."""
+    c = synth.greedy_case(66, dtype="f32", B=6, L=7, V=300, plant=True)
+    ref = oracle.verify_greedy(c.target_logits, "f32", draft_tokens=c.draft_tokens)
+    tp = oracle.target_argmax(c.target_logits, "f32")
+    for b in range(6):
+        parent = np.arange(-1, 6)
+        w = oracle.walk_greedy(c.draft_tokens[b], parent, tp[b])
+        assert w.accept_len == ref.accept_len[b] and w.bonus == ref.bonus[b]
