@@ -23,6 +23,8 @@ Readings where the pages leave a step open (also in the design doc):
 * heap order: higher score first; equal scores pop in the order of the
   parents' pops (the root first), then by sibling rank; so a parent always
   precedes its children and the result is unique;
+* a candidate of probability zero (a logit of -inf) is never a node, so a
+  tree can stop short of the budget before the full K-ary tree is spent;
 * nodes are numbered in pop order; parent -1 means the root; depth d means
   block position d (1-based), drawn from draft row d - 1;
 * greedy acceptance of a child: its token equals the target's argmax at its
@@ -70,7 +72,8 @@ def build_tree(tokens, logp, budget):
     (tokens, logp: [n, K]).  Returns a Tree with min(budget, all) nodes in pop
     order."""
     n, K = logp.shape
-    heap = [(-float(logp[0, r]), -1, r, 1) for r in range(K)]   # (-score, parent pop, rank, depth)
+    heap = [(-float(logp[0, r]), -1, r, 1) for r in range(K)   # (-score, parent pop, rank, depth)
+            if logp[0, r] > -np.inf]
     heapq.heapify(heap)
     tok, par, dep, sc, rk = [], [], [], [], []
     while heap and len(tok) < budget:
@@ -83,7 +86,8 @@ def build_tree(tokens, logp, budget):
         rk.append(r)
         if dpt < n:
             for r2 in range(K):
-                heapq.heappush(heap, (neg - float(logp[dpt, r2]), i, r2, dpt + 1))
+                if logp[dpt, r2] > -np.inf:
+                    heapq.heappush(heap, (neg - float(logp[dpt, r2]), i, r2, dpt + 1))
     return Tree(np.array(tok, dtype=np.int64), np.array(par, dtype=np.int64),
                 np.array(dep, dtype=np.int64), np.array(sc), np.array(rk, dtype=np.int64))
 

@@ -84,6 +84,22 @@ def test_best_first_is_optimal_among_ancestor_closed_sets(K, n, bmax, seed):
         assert abs(np.exp(t.score).sum() - best) < 1e-12
 
 
+def test_zero_probability_candidates_are_no_nodes():
+    """Position 2 has only two tokens of nonzero probability (the rest have
+    logit -inf): with K = 3 over two positions the whole tree is the 3 roots'
+    children plus 3 x 2 grandchildren, so a budget of 20 stops at 9 nodes, and
+    no node carries a zero-probability token."""
+    x = np.full((1, 2, 6), -np.inf)
+    x[0, 0] = [0.5, 1.0, -1.0, 2.0, 0.0, -0.5]
+    x[0, 1, [1, 4]] = [0.3, -0.2]
+    tok, lp = oracle.topk_logprobs(x, "f64", K=3)
+    assert tok[0, 1, :2].tolist() == [1, 4] and lp[0, 1, 2] == -np.inf
+    t = oracle.build_tree(tok[0], lp[0], budget=20)
+    assert len(t.token) == 9
+    assert np.all(np.isfinite(t.score))
+    assert sorted(t.token[t.depth == 2].tolist()) == [1, 1, 1, 4, 4, 4]
+
+
 def test_tree_order_properties_on_synthetic_draft():
     """Parents precede children, scores never increase along the pop order,
     children scores are the parent's plus their position's log-probability,
