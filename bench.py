@@ -77,10 +77,14 @@ def parse():
                     help="also run one 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--breakdown", action="store_true", help="per-part timings to stderr")
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "sample-gate", "prefill", "packed"],
+                    choices=["decode", "sample-gate", "prefill", "packed", "tree"],
                     help="decode: the greedy decode step (default); sample-gate: Qwen3-4B-shaped "
                          "stochastic chain verify with DLoop gates; prefill: 4 x 32768-row "
-                         "ctx-KV materialisation; packed: training-style packed block mask")
+                         "ctx-KV materialisation; packed: training-style packed block mask; "
+                         "tree: DDTree build (top-K, best-first tree, ancestor mask) + greedy "
+                         "tree verify")
+    ap.add_argument("--topk", type=int, default=8, help="tree: candidates per block position")
+    ap.add_argument("--budget", type=int, default=512, help="tree: node budget")
     ap.add_argument("--sigma", type=float, default=1.0, help="sample-gate: draft = target + N(0, sigma)")
     ap.add_argument("--stages", type=int, default=4, help="sample-gate: DLoop stages of 8")
     ap.add_argument("--no-gate-lse", action="store_true",
@@ -553,6 +557,97 @@ def bench_packed(args):
     return line
 
 
+def bench_tree(args):
+    """DDTree on a Qwen3-8B-shaped drafter: 64 requests, a block of 16 (15
+    drafted positions), vocab 151936, top-8 candidates per position, node
+    budget 512.  One step = the tree build (top-K over every draft row, the
+    best-first tree, the ancestor mask) + the greedy tree verify (argmax of
+    the target row of the root and of every node, then the walk)."""
+    import numpy as np
+    import torch
+    import block_diffusion_draft_ctx_amd as dfl
+    B, n_pos, V, K, N = args.batch, args.block - 1, 151936, args.topk, args.budget
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(4000)
+    # a confident drafter: one token per row raised well above the noise
+    dl32 = torch.randn(B, n_pos, V, generator=g, device=dev) * 2.0
+    peak = torch.randint(0, V, (B, n_pos), generator=g, device=dev)
+    dl32.scatter_add_(2, peak[..., None], torch.full((B, n_pos, 1), 14.0, device=dev))
+    dl = dl32.to(torch.bfloat16)
+    del dl32
+    tl = torch.empty(B, N + 1, V, dtype=torch.bfloat16, device=dev)
+    for b in range(B):
+        tl[b] = (torch.randn(N + 1, V, generator=g, device=dev) * 3.0).to(torch.bfloat16)
+    wsb = torch.empty(max(256, dfl.lib().dflash_tree_workspace_size(B, n_pos, V, K)),
+                      dtype=torch.uint8, device=dev)
+    wsv = torch.empty(max(256, dfl.lib().dflash_tree_verify_workspace_size(B, N, V)),
+                      dtype=torch.uint8, device=dev)
+    tb, tv = {}, {}
+
+    def build():
+        tb.update(dfl.tree_build(dl, K, N, out=tb or None, workspace=wsb))
+
+    def verify():
+        tv.update(dfl.tree_verify_greedy(tl, tb["node_token"], tb["node_parent"], tb["n_nodes"],
+                                         n_pos, out=tv or None, workspace=wsv))
+
+    def step():
+        build()
+        verify()
+
+    build()
+    ms = _events_ms(step, args.steps, args.warmup)
+    bms = _events_ms(build, args.steps, args.warmup)
+    vms = _events_ms(verify, args.steps, args.warmup)
+    gms = _graph_ms(step, args.steps, args.warmup)
+    # algorithmic bytes: the verify reads every target row it needs once (the
+    # root's and each built node's), the build every draft row once
+    n_nodes = int(tb["n_nodes"].sum().item())
+    vbytes = (B + n_nodes) * V * 2
+    bbytes = B * n_pos * V * 2
+    line = _base_line(args, "DDTree draft tree + greedy tree verify, blocks/sec",
+                      round(B / (ms * 1e-3), 1), "blocks/s", ms,
+                      f"Qwen3-8B-shaped DDTree step: batch {B}, {n_pos} drafted positions, vocab "
+                      f"{V}, top-{K} per position, node budget {N}; build (top-K, best-first tree, "
+                      f"ancestor mask) + greedy tree verify over {N + 1} target rows per request",
+                      batch=B, positions=n_pos, vocab=V, topk=K, budget=N)
+    line["roofline"] = {"kernel": "tree verify (target argmax over every node's row)",
+                        "bound": "hbm", "achieved": round(vbytes / (vms * 1e-3) / 1e9, 1),
+                        "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                        "frac": round(vbytes / (vms * 1e-3) / HBM_PEAK, 4), "traffic": None,
+                        "algorithmic_bytes": vbytes, "avg_launch_us": round(vms * 1e3, 2)}
+    line["breakdown"] = {"build_us": round(bms * 1e3, 1),
+                         "build_topk_hbm_bytes": bbytes,
+                         "verify_us": round(vms * 1e3, 1),
+                         "mean_accept_len": round(float(tv["accept_len"].float().mean().item()), 3)}
+    line["graph_replay"] = {"ms_per_step": round(gms, 4), "value": round(B / (gms * 1e-3), 1)}
+    if not args.no_cpu_baseline:
+        import time
+        import oracle
+        n_req = min(args.cpu_sample, B)
+
+        def host(t):
+            return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+        dt = 0.0
+        for b in range(n_req):
+            dh, th = host(dl[b:b + 1]), host(tl[b:b + 1])     # copies outside the timed part
+            t0 = time.perf_counter()
+            tok, lp = oracle.topk_logprobs(dh, "bf16", K)
+            tree = oracle.build_tree(tok[0], lp[0], N)
+            oracle.ancestor_mask(tree.parent)
+            pred = oracle.target_argmax(th[:, :len(tree.token) + 1], "bf16")[0]
+            oracle.walk_greedy(tree.token, tree.parent, pred)
+            dt += time.perf_counter() - t0
+        line["cpu_baseline"] = {
+            "value": round(n_req / dt, 3), "unit": "blocks/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n_req} of the {B} requests: their top-K, tree, mask, target argmax over "
+                      f"the root's and every node's row, and the walk; {dt:.1f} s of CPU work"}
+    return line
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -566,7 +661,7 @@ def main():
         sys.exit(1)
     if args.workload != "decode":
         fn = {"sample-gate": bench_sample_gate, "prefill": bench_prefill,
-              "packed": bench_packed}[args.workload]
+              "packed": bench_packed, "tree": bench_tree}[args.workload]
         print(json.dumps(fn(args)), flush=True)
         return
     st = Step(args.batch, args.ctx, args.block, args.vocab, args.layers, causal=args.causal,

@@ -24,6 +24,8 @@ EXPORTS = (
     "dflash_attention_workspace_size", "dflash_block_attention",
     "dflash_verify_workspace_size", "dflash_verify_greedy", "dflash_verify_sample",
     "dflash_gate_workspace_size", "dflash_gate",
+    "dflash_tree_workspace_size", "dflash_tree_verify_workspace_size", "dflash_tree_build",
+    "dflash_tree_verify_greedy",
 )
 
 
@@ -82,6 +84,16 @@ def _declare(lib):
     lib.dflash_gate_workspace_size.argtypes = [I32, I32, I32]
     lib.dflash_gate.restype = I32
     lib.dflash_gate.argtypes = [I32, I32, I32, P, I64, P, P, F, F, P, P, P, P, I32, I32, P, SZ, P]
+    lib.dflash_tree_workspace_size.restype = SZ
+    lib.dflash_tree_workspace_size.argtypes = [I32, I32, I32, I32]
+    lib.dflash_tree_verify_workspace_size.restype = SZ
+    lib.dflash_tree_verify_workspace_size.argtypes = [I32, I32, I32]
+    lib.dflash_tree_build.restype = I32
+    lib.dflash_tree_build.argtypes = [
+        I32, I32, I32, P, I64, F, I32, I32, P, P, P, P, P, P, P, P, I32, P, SZ, P]
+    lib.dflash_tree_verify_greedy.restype = I32
+    lib.dflash_tree_verify_greedy.argtypes = [
+        I32, I32, I32, P, I64, P, P, P, I32, P, P, P, P, P, P, I32, P, SZ, P]
 
 
 def lib():
@@ -398,4 +410,75 @@ def gate(draft_logits, draft_tokens, temperature=1.0, g=-0.5, valid_lens=None, r
                        _ptr(o.get("row_max")), _ptr(o.get("row_lse")), ld if B > 1 else 0, dt,
                        _ptr(ws), nws, _stream(stream))
     _check(s, "dflash_gate")
+    return o
+
+
+def tree_build(draft_logits, topk, budget, temperature=1.0, want_mask=True, out=None,
+               workspace=None, stream=None):
+    """dflash_tree_build.  draft_logits [B, n_pos, V] (row d: block position
+    d + 1).  Returns a dict of device tensors: topk_tokens, topk_logp
+    [B, n_pos, topk]; node_token, node_parent, node_depth, node_logp
+    [B, budget]; n_nodes [B]; ancestor_mask [B, budget, ceil(budget / 32)]
+    int32 bit rows (if wanted)."""
+    torch = _torch()
+    L_ = lib()
+    _logit_rows(draft_logits, "draft_logits")
+    B, n_pos, V = draft_logits.shape
+    dt = _dtype_code(draft_logits)
+    dev = draft_logits.device
+    o = dict(out or {})
+    o.setdefault("topk_tokens", torch.empty((B, n_pos, topk), dtype=torch.int32, device=dev))
+    o.setdefault("topk_logp", torch.empty((B, n_pos, topk), dtype=torch.float32, device=dev))
+    for name, dtp in (("node_token", torch.int32), ("node_parent", torch.int32),
+                      ("node_depth", torch.int32), ("node_logp", torch.float32)):
+        o.setdefault(name, torch.empty((B, budget), dtype=dtp, device=dev))
+    o.setdefault("n_nodes", torch.empty(B, dtype=torch.int32, device=dev))
+    if want_mask:
+        o.setdefault("ancestor_mask",
+                     torch.empty((B, budget, (budget + 31) // 32), dtype=torch.int32, device=dev))
+    need = L_.dflash_tree_workspace_size(B, n_pos, V, topk)
+    ws, nws = _workspace(need, dev, workspace)
+    s = L_.dflash_tree_build(
+        B, n_pos, V, _ptr(draft_logits), _row_stride(draft_logits), float(temperature), int(topk),
+        int(budget), _ptr(o["topk_tokens"]), _ptr(o["topk_logp"]), _ptr(o["node_token"]),
+        _ptr(o["node_parent"]), _ptr(o["node_depth"]), _ptr(o["node_logp"]), _ptr(o["n_nodes"]),
+        _ptr(o.get("ancestor_mask")), dt, _ptr(ws), nws, _stream(stream))
+    _check(s, "dflash_tree_build")
+    return o
+
+
+def tree_verify_greedy(target_logits, node_token, node_parent, n_nodes, max_depth,
+                       prefix_lens=None, out=None, workspace=None, stream=None):
+    """dflash_tree_verify_greedy.  target_logits [B, budget + 1, V] (row 0:
+    after the root, row 1 + j: after node j); node_token, node_parent
+    [B, budget] and n_nodes [B] int32.  Returns a dict with accept_len,
+    bonus, commit_lens [B], accepted_nodes [B, max_depth] and new_seq_lens
+    (if prefix_lens)."""
+    torch = _torch()
+    L_ = lib()
+    _logit_rows(target_logits, "target_logits")
+    B, R, V = target_logits.shape
+    budget = R - 1
+    dt = _dtype_code(target_logits)
+    dev = target_logits.device
+    for name, t in (("node_token", node_token), ("node_parent", node_parent)):
+        _i32(t, name)
+        if tuple(t.shape) != (B, budget):
+            raise ValueError(f"{name} must be [B, budget] = [{B}, {budget}]")
+    _i32(n_nodes, "n_nodes")
+    _i32(prefix_lens, "prefix_lens")
+    o = dict(out or {})
+    for name in ("accept_len", "bonus", "commit_lens"):
+        o.setdefault(name, torch.empty(B, dtype=torch.int32, device=dev))
+    o.setdefault("accepted_nodes", torch.empty((B, max_depth), dtype=torch.int32, device=dev))
+    if prefix_lens is not None:
+        o.setdefault("new_seq_lens", torch.empty(B, dtype=torch.int32, device=dev))
+    need = L_.dflash_tree_verify_workspace_size(B, budget, V)
+    ws, nws = _workspace(need, dev, workspace)
+    s = L_.dflash_tree_verify_greedy(
+        B, budget, V, _ptr(target_logits), _row_stride(target_logits), _ptr(node_token),
+        _ptr(node_parent), _ptr(n_nodes), int(max_depth), _ptr(o["accept_len"]), _ptr(o["bonus"]),
+        _ptr(o["accepted_nodes"]), _ptr(o["commit_lens"]), _ptr(prefix_lens),
+        _ptr(o.get("new_seq_lens")), dt, _ptr(ws), nws, _stream(stream))
+    _check(s, "dflash_tree_verify_greedy")
     return o

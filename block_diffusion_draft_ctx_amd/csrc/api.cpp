@@ -259,4 +259,60 @@ dflash_status dflash_gate(int B, int n, int V, const void* draft_logits, int64_t
                                 static_cast<hipStream_t>(stream)));
 }
 
+// ------------------------------------------------------------------ DDTree
+size_t dflash_tree_workspace_size(int B, int n_pos, int V, int topk) {
+  if (B <= 0 || n_pos <= 0 || V <= 0 || topk <= 0 || topk > kTreeTopkMax) return 0;
+  return tree_ws_bytes(B, n_pos, V, topk);
+}
+
+size_t dflash_tree_verify_workspace_size(int B, int budget, int V) {
+  if (B <= 0 || budget <= 0 || budget > kTreeBudgetMax || V <= 0) return 0;
+  return tree_verify_ws_bytes(B, budget, V);
+}
+
+dflash_status dflash_tree_build(int B, int n_pos, int V, const void* draft_logits,
+                                int64_t row_stride, float temperature, int topk, int budget,
+                                int32_t* topk_tokens, float* topk_logp, int32_t* node_token,
+                                int32_t* node_parent, int32_t* node_depth, float* node_logp,
+                                int32_t* n_nodes, uint32_t* ancestor_mask, dflash_dtype dtype,
+                                void* ws, size_t ws_bytes, dflash_stream_t stream) {
+  if (bad_dtype(dtype)) return DFLASH_E_ARG;
+  if (B < 0 || n_pos < 1 || V < 1 || topk < 1 || budget < 1) return DFLASH_E_ARG;
+  if (topk > kTreeTopkMax || topk > V || budget > kTreeBudgetMax || n_pos > kMaxL)
+    return DFLASH_E_UNSUPPORTED;
+  if (!(temperature > 0.f) || temperature == __builtin_huge_valf()) return DFLASH_E_ARG;
+  if (B == 0) return DFLASH_OK;
+  if (!draft_logits || row_stride < V || !topk_tokens || !topk_logp || !node_token ||
+      !node_parent || !node_depth || !node_logp || !n_nodes)
+    return DFLASH_E_ARG;
+  if (dflash_status s = check_ws(ws, ws_bytes, tree_ws_bytes(B, n_pos, V, topk))) return s;
+  return hip_status(launch_tree_build(dtype == DFLASH_BF16, B, n_pos, V, draft_logits, row_stride,
+                                      temperature, topk, budget, topk_tokens, topk_logp,
+                                      node_token, node_parent, node_depth, node_logp, n_nodes,
+                                      ancestor_mask, ws, static_cast<hipStream_t>(stream)));
+}
+
+dflash_status dflash_tree_verify_greedy(int B, int budget, int V, const void* target_logits,
+                                        int64_t row_stride, const int32_t* node_token,
+                                        const int32_t* node_parent, const int32_t* n_nodes,
+                                        int max_depth, int32_t* accept_len, int32_t* bonus,
+                                        int32_t* accepted_nodes, int32_t* commit_lens,
+                                        const int32_t* prefix_lens, int32_t* new_seq_lens,
+                                        dflash_dtype dtype, void* ws, size_t ws_bytes,
+                                        dflash_stream_t stream) {
+  if (bad_dtype(dtype)) return DFLASH_E_ARG;
+  if (B < 0 || budget < 1 || V < 1 || max_depth < 1) return DFLASH_E_ARG;
+  if (budget > kTreeBudgetMax) return DFLASH_E_UNSUPPORTED;
+  if (B == 0) return DFLASH_OK;
+  if (!target_logits || row_stride < V || !node_token || !node_parent || !n_nodes || !accept_len ||
+      !bonus || !accepted_nodes || !commit_lens)
+    return DFLASH_E_ARG;
+  if ((prefix_lens == nullptr) != (new_seq_lens == nullptr)) return DFLASH_E_ARG;
+  if (dflash_status s = check_ws(ws, ws_bytes, tree_verify_ws_bytes(B, budget, V))) return s;
+  return hip_status(launch_tree_verify(dtype == DFLASH_BF16, B, budget, V, target_logits,
+                                       row_stride, node_token, node_parent, n_nodes, max_depth,
+                                       accept_len, bonus, accepted_nodes, commit_lens, prefix_lens,
+                                       new_seq_lens, ws, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

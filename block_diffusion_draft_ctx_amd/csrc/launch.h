@@ -48,6 +48,23 @@ hipError_t launch_gate(bool bf16, int B, int n, int V, const void* dl, int64_t r
                        float g, float* c_out, int32_t* go_out, float* row_max, float* row_lse,
                        int stats_ld, void* ws, hipStream_t st);
 
+// ------------------------------------------------------------------- DDTree
+constexpr int kTreeTopkMax = 16;
+constexpr int kTreeBudgetMax = 1024;
+size_t tree_ws_bytes(int B, int n_pos, int V, int K);
+size_t tree_build_lds_bytes(int n_pos, int K, int budget);
+hipError_t launch_tree_build(bool bf16, int B, int n_pos, int V, const void* dl, int64_t rs,
+                             float temperature, int K, int budget, int32_t* topk_tok,
+                             float* topk_lp, int32_t* node_token, int32_t* node_parent,
+                             int32_t* node_depth, float* node_logp, int32_t* n_nodes,
+                             uint32_t* mask, void* ws, hipStream_t st);
+size_t tree_verify_ws_bytes(int B, int budget, int V);
+hipError_t launch_tree_verify(bool bf16, int B, int budget, int V, const void* tl, int64_t ts,
+                              const int32_t* node_token, const int32_t* node_parent,
+                              const int32_t* n_nodes, int max_depth, int32_t* accept_len,
+                              int32_t* bonus, int32_t* path, int32_t* commit,
+                              const int32_t* prefix, int32_t* new_seq, void* ws, hipStream_t st);
+
 // ----------------------------------------------------------------- attention
 struct AttnArgs {
   int B, k, Hq, Hkv, D;

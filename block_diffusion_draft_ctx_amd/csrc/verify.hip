@@ -637,6 +637,72 @@ __global__ __launch_bounds__(kThreads) void k_bonus_select(
                   commit, prefix, new_seq, beta_out, gap_out);
 }
 
+// ------------------------------------------------------------- tree walk
+// Greedy walk of a DDTree ([Spec tutorial], section 6.5), one wavefront per
+// request: the node tables are staged in LDS; from the root, the lanes scan
+// the nodes for the child of the current node whose token is the target's
+// argmax at that node (row 0: the root, row 1 + j: node j), a ballot picks
+// it, and the walk stops at the first node without such a child.
+__global__ __launch_bounds__(64) void k_tree_walk(
+    int budget, int max_depth, int nc, const float* __restrict__ pmax, const int* __restrict__ pidx,
+    const int32_t* __restrict__ node_token, const int32_t* __restrict__ node_parent,
+    const int32_t* __restrict__ n_nodes, int32_t* __restrict__ accept_len,
+    int32_t* __restrict__ bonus, int32_t* __restrict__ path, int32_t* __restrict__ commit,
+    const int32_t* __restrict__ prefix, int32_t* __restrict__ new_seq) {
+  extern __shared__ int tw[];
+  int* s_tok = tw;             // [budget]
+  int* s_par = tw + budget;    // [budget]
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int n = n_nodes[b];
+  const bool bad = n < 0 || n > budget;
+  const int N = bad ? 0 : n;
+  for (int j = lane; j < N; j += 64) {
+    s_tok[j] = node_token[(int64_t)b * budget + j];
+    s_par[j] = node_parent[(int64_t)b * budget + j];
+  }
+  __syncthreads();
+  // target argmax of row r: the lanes hold its chunks, ties to the lower id
+  auto predict = [&](int r) {
+    float v = neg_inf();
+    int i = INT_MAX;
+    if (lane < nc) {
+      v = pmax[((int64_t)b * (budget + 1) + r) * nc + lane];
+      i = pidx[((int64_t)b * (budget + 1) + r) * nc + lane];
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(v, o, 64);
+      const int oi = __shfl_xor(i, o, 64);
+      am_merge(v, i, ov, oi);
+    }
+    return i == INT_MAX ? 0 : i;
+  };
+  int cur = -1, len = 0, want = predict(0);
+  while (!bad && len < N) {      // a path holds at most N nodes: ends on any parent table
+    int hit = INT_MAX;
+    for (int j0 = 0; j0 < N; j0 += 64) {
+      const int j = j0 + lane;
+      const bool m = j < N && s_par[j] == cur && s_tok[j] == want;
+      const uint64_t bal = __ballot(m);
+      if (bal) { hit = j0 + (int)__ffsll((unsigned long long)bal) - 1; break; }
+    }
+    if (hit == INT_MAX) break;
+    if (lane == 0 && len < max_depth) path[(int64_t)b * max_depth + len] = hit;
+    ++len;
+    cur = hit;
+    want = predict(cur + 1);
+  }
+  if (lane == 0) {
+    for (int d = len; d < max_depth; ++d) path[(int64_t)b * max_depth + d] = -1;
+    accept_len[b] = bad ? -1 : len;
+    bonus[b] = bad ? -1 : want;
+    const int cm = bad ? 0 : len + 1;
+    commit[b] = cm;
+    if (new_seq) new_seq[b] = prefix[b] + cm;
+  }
+}
+
 // ------------------------------------------------------------------- gate
 // One workgroup per request: each wavefront merges the chunk partials of
 // one row at a time (lane c holds chunk c, at most 64 chunks) by butterfly
@@ -821,6 +887,39 @@ hipError_t launch_verify_sample(bool bf16, int B, int L, int V, const void* tl, 
     if (vec) sample_impl<float, true>(B, L, V, tl, ts, dl, ds, toks, lens, u, u2, temperature, acc, bonus, commit, prefix, new_seq, ratio_out, beta_out, gap_out, draft_lse, ws, st);
     else sample_impl<float, false>(B, L, V, tl, ts, dl, ds, toks, lens, u, u2, temperature, acc, bonus, commit, prefix, new_seq, ratio_out, beta_out, gap_out, draft_lse, ws, st);
   }
+  return hipGetLastError();
+}
+
+size_t tree_verify_ws_bytes(int B, int budget, int V) {
+  const int64_t rows = (int64_t)B * (budget + 1);
+  const VocabPlan pl = plan_vocab(rows, V);
+  return align256(sizeof(float) * rows * pl.n_chunks) + align256(sizeof(int) * rows * pl.n_chunks);
+}
+
+hipError_t launch_tree_verify(bool bf16, int B, int budget, int V, const void* tl, int64_t ts,
+                              const int32_t* node_token, const int32_t* node_parent,
+                              const int32_t* n_nodes, int max_depth, int32_t* accept_len,
+                              int32_t* bonus, int32_t* path, int32_t* commit,
+                              const int32_t* prefix, int32_t* new_seq, void* ws, hipStream_t st) {
+  // rows 0 .. n_nodes[b] of request b: the root and its nodes (the row set's
+  // chain lengths are the node counts, one extra row)
+  const int64_t rows = (int64_t)B * (budget + 1);
+  const VocabPlan pl = plan_vocab(rows, V);
+  float* pmax = static_cast<float*>(ws);
+  int* pidx = reinterpret_cast<int*>(static_cast<char*>(ws) + align256(sizeof(float) * rows * pl.n_chunks));
+  const int es = bf16 ? 2 : 4;
+  const bool vec = aligned16(tl, ts, es);
+  RowSet s0{tl, ts, budget + 1, 1}, s1{tl, ts, 0, 0};
+  if (bf16) {
+    if (vec) launch_argmax<uint16_t, true>(s0, s1, B, budget, V, n_nodes, pl, rows, pmax, pidx, st);
+    else launch_argmax<uint16_t, false>(s0, s1, B, budget, V, n_nodes, pl, rows, pmax, pidx, st);
+  } else {
+    if (vec) launch_argmax<float, true>(s0, s1, B, budget, V, n_nodes, pl, rows, pmax, pidx, st);
+    else launch_argmax<float, false>(s0, s1, B, budget, V, n_nodes, pl, rows, pmax, pidx, st);
+  }
+  hipLaunchKernelGGL(k_tree_walk, dim3(B), dim3(64), sizeof(int) * 2 * budget, st, budget,
+                     max_depth, pl.n_chunks, pmax, pidx, node_token, node_parent, n_nodes,
+                     accept_len, bonus, path, commit, prefix, new_seq);
   return hipGetLastError();
 }
 

@@ -4,6 +4,8 @@
  * Five operations, each the hot path of one part of the step:
  *   dflash_materialize_ctx_kv  target-context KV injection
  *   dflash_block_attention     non-causal block attention over [ctx; block]
+ *   dflash_tree_build          DDTree: top-K per position, best-first tree, ancestor mask
+ *   dflash_tree_verify_greedy  DDTree: target argmax per node and the greedy walk
  *   dflash_verify_greedy       greedy acceptance over the full vocabulary
  *   dflash_verify_sample       lossless rejection sampling over the full vocabulary
  *   dflash_gate                DLoop block-confidence gate
@@ -319,6 +321,68 @@ dflash_status dflash_gate(
     const int32_t* draft_tokens, const int32_t* valid_lens,
     float temperature, float g, float* c_out, int32_t* go_out,
     float* row_max_out, float* row_lse_out, int stats_ld,
+    dflash_dtype dtype, void* ws, size_t ws_bytes, dflash_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * DDTree: a draft tree under a node budget, and its greedy verification.
+ *
+ * [Spec tutorial], section 6.  6.1: the root is the last committed token and
+ * each block position offers its top-K candidates; 6.3: a path's joint
+ * probability is the product of the per-position marginals and the tree is
+ * grown best first (pop the most probable leaf, push its children) until it
+ * holds `budget` nodes; 6.4: a node sees only its ancestors; 6.5: greedy
+ * walk -- from the root step to the child whose token is the target's
+ * prediction, stop at the first node without one; the path is committed and
+ * the target's prediction there is the bonus.
+ *
+ * dflash_tree_build
+ *   draft_logits [B, n_pos, V] rows (row_stride apart): row d is block
+ *     position d + 1; temperature > 0; 1 <= topk <= 16, topk <= V;
+ *     1 <= budget <= 1024; 1 <= n_pos <= 64
+ *   topk_tokens, topk_logp  [B, n_pos, topk] outputs: each position's topk
+ *     most probable tokens (ties to the lower id) and log softmax(row / T)
+ *   node_token, node_parent, node_depth, node_logp  [B, budget] outputs, in
+ *     pop order: the token, the parent node (-1: the root), the block
+ *     position (1-based) and the joint log-probability; slots past n_nodes
+ *     hold token -1, parent -2, depth 0, logp -inf
+ *   n_nodes [B] output: nodes built (budget, or fewer if the whole tree of
+ *     topk^1 + ... + topk^n_pos nodes is smaller)
+ *   ancestor_mask [B, budget, (budget + 31) / 32] uint32 or NULL: bit j of
+ *     row i is set iff node j is node i or one of its ancestors (the target's
+ *     attention mask over the flattened tree); rows past n_nodes are zero
+ *   Order of equal joint probabilities: the parent popped earlier first
+ *   (the root's children first), then the lower sibling rank; so every
+ *   parent precedes its children and the tree is unique.
+ *
+ * dflash_tree_verify_greedy
+ *   target_logits [B, budget + 1, V] rows (row_stride apart): row 0 is the
+ *     target's output after the root, row 1 + j its output after node j
+ *     (rows past n_nodes[b] are not read); the prediction of a row is its
+ *     argmax (ties to the lower id)
+ *   node_token, node_parent, n_nodes  the tree, as dflash_tree_build gives it
+ *   accept_len, bonus, commit_lens [B] outputs; accepted_nodes [B, max_depth]
+ *     output: the accepted path's node indices, -1 past it (a path longer
+ *     than max_depth is truncated in this list only)
+ *   prefix_lens, new_seq_lens [B] or both NULL: new = prefix + commit
+ *   In band: n_nodes[b] outside [0, budget] gives accept_len = bonus = -1,
+ *   commit = 0.
+ * ------------------------------------------------------------------------- */
+size_t dflash_tree_workspace_size(int B, int n_pos, int V, int topk);
+size_t dflash_tree_verify_workspace_size(int B, int budget, int V);
+
+dflash_status dflash_tree_build(
+    int B, int n_pos, int V, const void* draft_logits, int64_t row_stride,
+    float temperature, int topk, int budget,
+    int32_t* topk_tokens, float* topk_logp,
+    int32_t* node_token, int32_t* node_parent, int32_t* node_depth, float* node_logp,
+    int32_t* n_nodes, uint32_t* ancestor_mask,
+    dflash_dtype dtype, void* ws, size_t ws_bytes, dflash_stream_t stream);
+
+dflash_status dflash_tree_verify_greedy(
+    int B, int budget, int V, const void* target_logits, int64_t row_stride,
+    const int32_t* node_token, const int32_t* node_parent, const int32_t* n_nodes,
+    int max_depth, int32_t* accept_len, int32_t* bonus, int32_t* accepted_nodes,
+    int32_t* commit_lens, const int32_t* prefix_lens, int32_t* new_seq_lens,
     dflash_dtype dtype, void* ws, size_t ws_bytes, dflash_stream_t stream);
 
 #ifdef __cplusplus

@@ -180,3 +180,55 @@ def test_materialize_argument_errors(lib, kw, code):
                                       caches, FAKE, 4, a["rps"], FAKE, None, ctypes.byref(epi),
                                       None, dfl.BF16, WS, a["nws"], None)
     assert s == code
+
+
+def test_tree_workspace_queries(lib):
+    a = lib.dflash_tree_workspace_size(8, 16, 151936, 8)
+    assert a > 0 and a % 256 == 0
+    assert lib.dflash_tree_workspace_size(8, 16, 151936, 17) == 0
+    assert lib.dflash_tree_workspace_size(0, 16, 151936, 8) == 0
+    v = lib.dflash_tree_verify_workspace_size(8, 256, 151936)
+    assert v > 0 and v % 256 == 0
+    assert lib.dflash_tree_verify_workspace_size(8, 1025, 151936) == 0
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=0), dfl.E_ARG), (dict(K=17), dfl.E_UNSUPPORTED), (dict(K=8, V=7), dfl.E_UNSUPPORTED),
+    (dict(budget=0), dfl.E_ARG), (dict(budget=1025), dfl.E_UNSUPPORTED),
+    (dict(n=0), dfl.E_ARG), (dict(n=65), dfl.E_UNSUPPORTED), (dict(T=0.0), dfl.E_ARG),
+    (dict(T=float("inf")), dfl.E_ARG), (dict(T=float("nan")), dfl.E_ARG),
+    (dict(rs=50), dfl.E_ARG), (dict(dl=None), dfl.E_ARG), (dict(nn=None), dfl.E_ARG),
+    (dict(nws=0), dfl.E_WORKSPACE), (dict(dtype=3), dfl.E_ARG),
+])
+def test_tree_build_argument_errors(lib, kw, code):
+    a = dict(B=2, n=8, V=100, dl=FAKE, rs=100, T=1.0, K=4, budget=64, nn=FAKE, nws=1 << 24,
+             dtype=dfl.BF16)
+    a.update(kw)
+    s = lib.dflash_tree_build(a["B"], a["n"], a["V"], a["dl"], a["rs"], a["T"], a["K"],
+                              a["budget"], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["nn"], None,
+                              a["dtype"], WS, a["nws"], None)
+    assert s == code
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(budget=0), dfl.E_ARG), (dict(budget=1025), dfl.E_UNSUPPORTED), (dict(md=0), dfl.E_ARG),
+    (dict(tl=None), dfl.E_ARG), (dict(rs=99), dfl.E_ARG), (dict(path=None), dfl.E_ARG),
+    (dict(pre=FAKE), dfl.E_ARG), (dict(nws=0), dfl.E_WORKSPACE), (dict(V=0), dfl.E_ARG),
+])
+def test_tree_verify_argument_errors(lib, kw, code):
+    a = dict(B=2, budget=64, V=100, tl=FAKE, rs=100, md=8, path=FAKE, pre=None, nws=1 << 24)
+    a.update(kw)
+    s = lib.dflash_tree_verify_greedy(a["B"], a["budget"], a["V"], a["tl"], a["rs"], FAKE, FAKE,
+                                      FAKE, a["md"], FAKE, FAKE, a["path"], FAKE, a["pre"], None,
+                                      dfl.BF16, WS, a["nws"], None)
+    assert s == code
+
+
+@no_gpu
+def test_tree_zero_batch_is_a_noop(lib):
+    assert lib.dflash_tree_build(0, 8, 100, None, 100, 1.0, 4, 64, None, None, None, None, None,
+                                 None, None, None, dfl.BF16, None, 0, None) == dfl.OK
+    assert lib.dflash_tree_verify_greedy(0, 64, 100, None, 100, None, None, None, 8, None, None,
+                                         None, None, None, None, dfl.BF16, None, 0, None) == dfl.OK
