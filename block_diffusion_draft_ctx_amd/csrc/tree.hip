@@ -8,20 +8,26 @@
 //
 // Design.
 //  * Top-K: one coalesced pass over every draft row, workgroups on row
-//    chunks as in the verify passes.  Each thread keeps a sorted list of its
-//    16 best (logit, token) pairs -- compared by raw logit, ties to the lower
-//    token id, so the selection is exact -- and the chunk's softmax partial
-//    (m, sum 2^(z - m)); the lists merge into the chunk's top-K by K rounds
-//    of a workgroup argmax.  A second kernel merges the chunk lists and
-//    partials of a row into its top-K tokens and natural log-probabilities.
+//    chunks as in the verify passes.  Selection is on the raw logits, ties
+//    to the lower token id, so it is exact; each wavefront filters against
+//    a threshold (its K-th best so far) and buffers the few elements that
+//    beat it, so the pass costs little more than the chunk's softmax
+//    partial (m, sum 2^(z - m)) it computes alongside.  A second kernel
+//    merges the chunk lists and partials of a row into its top-K tokens
+//    and natural log-probabilities.
 //  * Tree: one wavefront per request runs the best-first loop.  Candidates
-//    live in LDS; each lane caches the best of the slots it owns (slot s
-//    belongs to lane s % 64), so a pop is a 6-step shuffle argmax plus a
-//    rescan by the owner lane.  A pop pushes at most two candidates, the
-//    popped node's first child and its next sibling: siblings come sorted,
-//    so a sibling can never outrank the one before it and this pops exactly
-//    what pushing all K children would.  Order: higher joint log-probability
-//    first, then the parent's pop index, then the sibling rank.
+//    live in LDS as 64-bit words whose unsigned order is the pop order;
+//    each lane caches the best of the slots it owns (slot s belongs to lane
+//    s % 64), so a pop is a DPP wavefront max plus a rescan by the owner
+//    lane.  A pop pushes at most two candidates, the popped node's first
+//    child and its next sibling: siblings come sorted, so a sibling can
+//    never outrank the one before it and this pops exactly what pushing all
+//    K children would; the first child takes over the popped slot, so a
+//    request uses at most budget + 1 slots.  Order: higher joint
+//    log-probability first, then the parent's pop index, then the sibling
+//    rank.  The loop stages only the popped words in LDS and touches no
+//    global memory; the node outputs are decoded from them at the end.
+#include <algorithm>
 #include <climits>
 
 #include "common.h"
@@ -41,73 +47,245 @@ __device__ __forceinline__ bool before(float v, int i, float w, int j) {
   return v > w || (v == w && i < j);
 }
 
-// Insert (v, x) into a thread's sorted list of kTopkMax entries (best first).
-__device__ __forceinline__ void list_insert(float (&lv)[kTopkMax], int (&li)[kTopkMax], float v, int x) {
-  if (!before(v, x, lv[kTopkMax - 1], li[kTopkMax - 1])) return;
-  float cv = v;
-  int ci = x;
-#pragma unroll
-  for (int j = 0; j < kTopkMax; ++j) {
-    if (before(cv, ci, lv[j], li[j])) {
-      const float tv = lv[j];
-      const int ti = li[j];
-      lv[j] = cv; li[j] = ci;
-      cv = tv; ci = ti;
-    }
-  }
+// LDS ordering inside one wavefront: the wave's LDS operations complete in
+// issue order, so a fence at wavefront scope (it keeps the compiler from
+// moving LDS accesses across it) is all the exchange between lanes needs.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Workgroup argmax of (v, i) under before(); every thread gets the result.
-__device__ __forceinline__ void block_best(float v, int i, float* sv, int* si, float& bv, int& bi) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(v, o, 64);
-    const int oi = __shfl_xor(i, o, 64);
-    if (before(ov, oi, v, i)) { v = ov; i = oi; }
-  }
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) { sv[w] = v; si[w] = i; }
-  __syncthreads();
-  bv = sv[0];
-  bi = si[0];
-  for (int k = 1; k < kThreads / 64; ++k)
-    if (before(sv[k], si[k], bv, bi)) { bv = sv[k]; bi = si[k]; }
+// ---------------------------------------------------------------- wave reductions
+// Within a row of 16 lanes the butterfly runs on DPP lane permutations (quad
+// xor 1 and xor 2, then the half-row and row mirrors), after which every lane
+// of a row holds the row's best; the four row bests are then read into scalar
+// registers and combined there, so the result is uniform.
+template <int CTRL>
+__device__ __forceinline__ int dpp(int x) {
+  return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xf, 0xf, false);
+}
+constexpr int kQuadXor1 = 0xb1, kQuadXor2 = 0x4e, kHalfMirror = 0x141, kMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ void best_step(float& v, int& i) {
+  const float ov = __int_as_float(dpp<CTRL>(__float_as_int(v)));
+  const int oi = dpp<CTRL>(i);
+  if (before(ov, oi, v, i)) { v = ov; i = oi; }
 }
 
+// (v, i) best under before() over the wavefront, uniform in every lane.
+__device__ __forceinline__ void wave_best(float& v, int& i) {
+  best_step<kQuadXor1>(v, i);
+  best_step<kQuadXor2>(v, i);
+  best_step<kHalfMirror>(v, i);
+  best_step<kMirror>(v, i);
+  float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+  for (int r = 16; r < 64; r += 16) {
+    const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), r));
+    const int ri = __builtin_amdgcn_readlane(i, r);
+    if (before(rv, ri, bv, bi)) { bv = rv; bi = ri; }
+  }
+  v = bv;
+  i = bi;
+}
+
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int lanes_below(uint64_t b) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0));
+}
+
+#ifndef DFLASH_TOPK_NF
+#define DFLASH_TOPK_NF 4
+#endif
+#ifndef DFLASH_TOPK_WGS
+#define DFLASH_TOPK_WGS 768
+#endif
+constexpr int kTopkNF = DFLASH_TOPK_NF;   // 16-byte loads in flight per lane
+constexpr int kVecBuf = 128;       // buffered vectors of 8 per wavefront
+
+// One workgroup per (row, chunk), four wavefronts, each with its own
+// candidates.  A wavefront holds its K best so far in lanes 0..K-1 and a
+// threshold, the K-th of them: an element not before the threshold has K
+// better ones already, so dropping it is exact.  A lane whose vector of 8
+// reaches the threshold appends the whole vector to an LDS buffer (one
+// ballot for the wavefront); the buffer is folded into the K best, and the
+// threshold raised, when it fills and at the end.  The first round seeds
+// the threshold with the K-th largest lane maximum (K lanes hold an element
+// at least that large).  A vector below the threshold costs one comparison,
+// so the pass is the streaming log-sum-exp plus that test.
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_row_topk(const T* __restrict__ dl, int64_t rs, int V,
                                                        int K, float a, int chunk, int nc,
                                                        float* __restrict__ cv, int* __restrict__ ci,
                                                        float2* __restrict__ part) {
+  __shared__ float4 vb_v[kThreads / 64][kVecBuf][2];
+  __shared__ int vb_x[kThreads / 64][kVecBuf];     // token of element 0; -1 - token: a single element
+  __shared__ float sm[kThreads / 64], ss[kThreads / 64];
+  __shared__ float wv[kThreads / 64][kTopkMax];
+  __shared__ int wi[kThreads / 64][kTopkMax];
   const int c = blockIdx.x % nc;
   const int r = blockIdx.x / nc;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const T* row = dl + (int64_t)r * rs;
   const int x0 = c * chunk;
   const int x1 = min(V, x0 + chunk);
-  float lv[kTopkMax];
-  int li[kTopkMax];
-#pragma unroll
-  for (int j = 0; j < kTopkMax; ++j) { lv[j] = neg_inf(); li[j] = INT_MAX; }
+  int cnt = 0;                                      // buffered vectors (uniform)
+  float tv = neg_inf();
+  int ti = INT_MAX;                                 // threshold (uniform): nothing dropped yet
+  float kv = neg_inf();
+  int kx = INT_MAX;                                 // lane k < K: the k-th best so far
   float m = neg_inf(), s = 0.f;
-  auto take = [&](float v, int x) {
+
+  // fold the buffer into the K best: up to 64 vectors at a time, one per
+  // lane, K rounds of wave_best over each lane's best remaining entry (its
+  // vector's elements and, in lanes < K, the current k-th best)
+  auto fold = [&]() {
+    wave_sync();
+    while (cnt > 0) {
+      const int n = min(cnt, 64);
+      float e[8];
+      int ex[8];
+      const int slot = cnt - n + lane;
+      const bool have = lane < n;
+      const float4 a0 = vb_v[w][have ? slot : 0][0], a1 = vb_v[w][have ? slot : 0][1];
+      const int xb = vb_x[w][have ? slot : 0];
+      e[0] = a0.x; e[1] = a0.y; e[2] = a0.z; e[3] = a0.w;
+      e[4] = a1.x; e[5] = a1.y; e[6] = a1.z; e[7] = a1.w;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool live = have && (xb >= 0 || j == 0);
+        ex[j] = live ? (xb >= 0 ? xb + j : -1 - xb) : INT_MAX;
+        if (!live) e[j] = neg_inf();
+      }
+      cnt -= n;
+      float nv = neg_inf();
+      int ni = INT_MAX;
+      for (int k = 0; k < K; ++k) {
+        float lb = kv;
+        int lx = kx, which = 8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (before(e[j], ex[j], lb, lx)) { lb = e[j]; lx = ex[j]; which = j; }
+        float b1 = lb;
+        int b2 = lx;
+        wave_best(b1, b2);
+        if (b2 == lx && b1 == lb && lx != INT_MAX) {   // this lane holds the winner: retire it
+          if (which == 8) { kv = neg_inf(); kx = INT_MAX; }
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (j == which) { e[j] = neg_inf(); ex[j] = INT_MAX; }
+        }
+        if (lane == k) { nv = b1; ni = b2; }
+      }
+      kv = nv; kx = ni;
+    }
+    tv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(kv), K - 1));
+    ti = __builtin_amdgcn_readlane(kx, K - 1);
+    wave_sync();
+  };
+  // buffer the lanes' vectors (x: token of e[0]) that may beat the threshold
+  auto push8 = [&](const float (&e)[8], float m8, int x, bool valid) {
+    const bool maybe = valid && !(m8 < tv);
+    const uint64_t bal = __ballot(maybe);
+    if (bal == 0) return;
+    if (maybe) {
+      const int o = cnt + lanes_below(bal);
+      vb_v[w][o][0] = make_float4(e[0], e[1], e[2], e[3]);
+      vb_v[w][o][1] = make_float4(e[4], e[5], e[6], e[7]);
+      vb_x[w][o] = x;
+    }
+    cnt += __popcll(bal);
+    if (cnt > kVecBuf - 64) fold();
+  };
+  auto push1 = [&](float e, int x, bool valid) {
+    const bool maybe = valid && before(e, x, tv, ti);
+    const uint64_t bal = __ballot(maybe);
+    if (bal == 0) return;
+    if (maybe) {
+      const int o = cnt + lanes_below(bal);
+      vb_v[w][o][0] = make_float4(e, neg_inf(), neg_inf(), neg_inf());
+      vb_v[w][o][1] = make_float4(neg_inf(), neg_inf(), neg_inf(), neg_inf());
+      vb_x[w][o] = -1 - x;
+    }
+    cnt += __popcll(bal);
+    if (cnt > kVecBuf - 64) fold();
+  };
+  // threshold from the first round: the K-th largest lane maximum, ties admitted
+  auto seed = [&](float lane_max) {
+    float ev = lane_max;
+    int ei = lane;
+    float b1 = neg_inf();
+    for (int k = 0; k < K; ++k) {
+      b1 = ev;
+      int b2 = ei;
+      wave_best(b1, b2);
+      if (b2 == lane) { ev = neg_inf(); ei = INT_MAX; }
+    }
+    tv = b1;
+    ti = INT_MAX;
+  };
+  auto lse1 = [&](float v) {
     const float z = v * a;
-    if (z > m) { s *= exp2f(m - z); m = z; }
-    if (m != neg_inf()) s += exp2f(z - m);
-    list_insert(lv, li, v, x);
+    if (z > m) { s *= fexp2(m - z); m = z; }
+    if (m != neg_inf()) s += fexp2(z - m);
   };
   if (VEC) {
     const int nvec = (x1 - x0) >> 3;
-    for (int v = threadIdx.x; v < nvec; v += kThreads) {
-      float e[8];
-      load8(row + x0 + v * 8, e);
+    bool first = true;
+    for (int base = w * 64; base < nvec; base += kTopkNF * kThreads) {   // uniform per wavefront
+      float e[kTopkNF][8], mx[kTopkNF];
+      bool ok[kTopkNF];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) take(e[j], x0 + v * 8 + j);
+      for (int u = 0; u < kTopkNF; ++u) {
+        const int v = base + lane + u * kThreads;
+        ok[u] = v < nvec;
+        load8(row + x0 + (ok[u] ? v : nvec - 1) * 8, e[u]);
+      }
+      float lm = neg_inf();
+#pragma unroll
+      for (int u = 0; u < kTopkNF; ++u) {
+        float m8 = e[u][0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) m8 = fmaxf(m8, e[u][j]);
+        mx[u] = m8;
+        if (ok[u]) {
+          const float gm = m8 * a;
+          if (gm > m) { s *= fexp2(m - gm); m = gm; }
+          if (m != neg_inf()) {
+            float acc = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc += fexp2(fmaf(e[u][j], a, -m));
+            s += acc;
+          }
+          lm = fmaxf(lm, m8);
+        }
+      }
+      if (first) { seed(lm); first = false; }
+#pragma unroll
+      for (int u = 0; u < kTopkNF; ++u) push8(e[u], mx[u], x0 + (base + lane + u * kThreads) * 8, ok[u]);
     }
-    for (int x = x0 + nvec * 8 + threadIdx.x; x < x1; x += kThreads) take(load1(row + x), x);
+    // the ragged tail (fewer than 8 elements), one per lane of the first wavefront
+    if (w == 0) {
+      const int x = x0 + nvec * 8 + lane;
+      const bool ok = x < x1;
+      const float v = ok ? load1(row + x) : neg_inf();
+      if (ok) lse1(v);
+      push1(v, x, ok);
+    }
   } else {
-    for (int x = x0 + threadIdx.x; x < x1; x += kThreads) take(load1(row + x), x);
+    for (int base = x0 + w * 64; base < x1; base += kThreads) {
+      const int x = base + lane;
+      const bool ok = x < x1;
+      const float v = ok ? load1(row + x) : neg_inf();
+      if (ok) lse1(v);
+      push1(v, x, ok);
+    }
   }
+  fold();
   // softmax partial of the chunk
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -115,31 +293,28 @@ __global__ __launch_bounds__(kThreads) void k_row_topk(const T* __restrict__ dl,
     const float os = __shfl_xor(s, o, 64);
     lse2_merge(m, s, om, os);
   }
-  __shared__ float sm[kThreads / 64], ss[kThreads / 64];
-  __shared__ float sv[kThreads / 64];
-  __shared__ int si[kThreads / 64];
-  if ((threadIdx.x & 63) == 0) { sm[threadIdx.x >> 6] = m; ss[threadIdx.x >> 6] = s; }
+  if (lane == 0) { sm[w] = m; ss[w] = s; }
+  if (lane < K) { wv[w][lane] = kv; wi[w][lane] = kx; }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float mm = sm[0], s2 = ss[0];
-    for (int k = 1; k < kThreads / 64; ++k) lse2_merge(mm, s2, sm[k], ss[k]);
-    part[blockIdx.x] = make_float2(mm, s2);
-  }
-  // the chunk's top-K: K rounds, each taking the best list head
-  int head = 0;
-  for (int k = 0; k < K; ++k) {
-    float hv = neg_inf();
-    int hi = INT_MAX;
-#pragma unroll
-    for (int j = 0; j < kTopkMax; ++j)
-      if (j == head) { hv = lv[j]; hi = li[j]; }
-    float bv;
-    int bi;
-    block_best(hv, hi, sv, si, bv, bi);
-    if (bi == hi && bv == hv && hi != INT_MAX) ++head;   // tokens are distinct: one owner
-    if (threadIdx.x == 0) {
-      cv[(int64_t)blockIdx.x * K + k] = bv;
-      ci[(int64_t)blockIdx.x * K + k] = bi;
+  if (w == 0) {
+    if (lane == 0) {
+      float mm = sm[0], s2 = ss[0];
+      for (int k = 1; k < kThreads / 64; ++k) lse2_merge(mm, s2, sm[k], ss[k]);
+      part[blockIdx.x] = make_float2(mm, s2);
+    }
+    // the chunk's K best out of the wavefronts' lists: one entry per lane
+    float ev = neg_inf();
+    int ei = INT_MAX;
+    if (lane < (kThreads / 64) * K) { ev = wv[lane / K][lane % K]; ei = wi[lane / K][lane % K]; }
+    for (int k = 0; k < K; ++k) {
+      float b1 = ev;
+      int b2 = ei;
+      wave_best(b1, b2);
+      if (b2 == ei && b1 == ev && ei != INT_MAX) { ev = neg_inf(); ei = INT_MAX; }
+      if (lane == 0) {
+        cv[(int64_t)blockIdx.x * K + k] = b1;
+        ci[(int64_t)blockIdx.x * K + k] = b2;
+      }
     }
   }
 }
@@ -169,12 +344,7 @@ __global__ __launch_bounds__(64) void k_topk_finalize(int K, int nc, float a,
     }
     float bv = v;
     int bi = i;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (before(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-    }
+    wave_best(bv, bi);
     if (bi == i && bv == v && i != INT_MAX) ++head;
     if (lane == 0) {
       tok_out[(int64_t)r * K + k] = bi == INT_MAX ? -1 : bi;
@@ -196,96 +366,172 @@ struct TreeP {
   uint32_t* mask;                  // [B, budget, W] or null
 };
 
+// Candidate slots of a request: a pop's first child takes over the popped
+// slot and its next sibling a new one, so at most budget + 1 slots are ever
+// used; rounded up to whole rounds of 8 slots per lane for the rescan.
+__host__ __device__ constexpr int tree_cap(int budget) { return (budget + 1 + 511) / 512 * 512; }
+
+// A candidate is one 64-bit word whose unsigned order is the pop order:
+// bits 63..32 the joint log-probability mapped to an order-preserving
+// unsigned integer, bits 30..16 (32767 - key) with key = (parent + 1) * 16 +
+// rank (smaller key first: the parent popped earlier, then the lower rank;
+// rank < K <= 16), bits 6..0 the depth.  Keys are unique, so the depth never
+// decides; 0 is below every candidate and marks an empty slot.
+__device__ __forceinline__ uint32_t ord_of(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float float_of(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+__device__ __forceinline__ uint64_t cand(float sc, int key, int depth) {
+  return ((uint64_t)ord_of(sc) << 32) | ((uint32_t)(32767 - key) << 16) | (uint32_t)depth;
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t umax_step(uint32_t x) {
+  return max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xf, 0xf, true));
+}
+
+// Largest 32-bit value over the wavefront, uniform (scalar registers).
+__device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
+  x = umax_step<kQuadXor1>(x);
+  x = umax_step<kQuadXor2>(x);
+  x = umax_step<kHalfMirror>(x);
+  x = umax_step<kMirror>(x);
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+// Largest 64-bit value over the wavefront, uniform: the high words first,
+// then the low words of the lanes that hold the largest high word.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  const uint32_t hi = (uint32_t)(v >> 32);
+  const uint32_t H = wave_umax(hi);
+  const uint32_t L = wave_umax(hi == H ? (uint32_t)v : 0u);
+  return ((uint64_t)H << 32) | L;
+}
+
 __global__ __launch_bounds__(64) void k_tree_build(TreeP p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
-  const int NK = p.n_pos * p.K;
-  const int cap = 2 * p.budget + 2;                        // candidates ever appended
-  float* e_score = reinterpret_cast<float*>(smem);         // [cap]
-  float* e_pscore = e_score + cap;                         // [cap] parent's score
-  int* e_par = reinterpret_cast<int*>(e_pscore + cap);     // [cap] parent pop index (-1: root)
-  int* e_rd = e_par + cap;                                 // [cap] rank | depth << 8
-  float* s_lp = reinterpret_cast<float*>(e_rd + cap);      // [n_pos * K]
+  const int K = p.K, NK = p.n_pos * p.K, N = p.budget;
+  const int cap = tree_cap(N);
+  uint64_t* e_c = reinterpret_cast<uint64_t*>(smem);       // [cap] candidate slots
+  uint64_t* n_c = e_c + cap;                               // [budget] the popped words, in order
+  float* s_lp = reinterpret_cast<float*>(n_c + N);         // [n_pos * K]
   int* s_tok = reinterpret_cast<int*>(s_lp + NK);          // [n_pos * K]
-  int* s_par = s_tok + NK;                                 // [budget] node parents
+  int* n_par = s_tok + NK;                                 // [budget] parents, decoded at the end
   for (int x = lane; x < NK; x += 64) {
     s_lp[x] = p.lp[(int64_t)b * NK + x];
     s_tok[x] = p.tok[(int64_t)b * NK + x];
   }
+  for (int x = lane; x < cap; x += 64) e_c[x] = 0;
   __syncthreads();
-  const int K = p.K;
-  // candidate key: (score, (parent + 1) * K + rank), larger score first, then smaller key
-  auto key2 = [&](int e) { return (e_par[e] + 1) * K + (e_rd[e] & 0xff); };
-  // each lane caches the best of its own slots; an empty lane is (-inf, INT_MAX)
-  float best_s = neg_inf();
-  int best_k = INT_MAX, best_e = -1;
-  int n_ent = 0;
-  auto append = [&](float sc, float psc, int par, int rank, int depth) {
-    if (sc == neg_inf()) return;                  // a token of probability 0 is no candidate
-    const int e = n_ent++;                        // uniform: every lane counts
-    if ((e & 63) == lane) {
-      e_score[e] = sc; e_pscore[e] = psc; e_par[e] = par; e_rd[e] = rank | (depth << 8);
-      const int k = (par + 1) * K + rank;
-      if (before(sc, k, best_s, best_k)) { best_s = sc; best_k = k; best_e = e; }
-    }
-  };
-  // the root's first child
-  append(s_lp[0], 0.f, -1, 0, 1);
+  // lane d holds block position d's best log-probability (a first child's term)
+  const float lp_first = lane < p.n_pos ? s_lp[lane * K] : neg_inf();
+  // each lane caches the best of the slots it owns (slot s: lane s % 64)
+  uint64_t best = 0;
+  int best_e = -1;
+  int n_ent = 1;                                           // uniform: slots in use
+  if (lane == 0 && s_lp[0] != neg_inf()) {                 // the root's first child, slot 0
+    best = cand(s_lp[0], 0, 1);
+    best_e = 0;
+    e_c[0] = best;
+  }
   int i = 0;
-  for (; i < p.budget; ++i) {
-    // wavefront argmax over the lanes' cached bests
-    float v = best_s;
-    int k = best_k, e = best_e;
+  for (; i < N; ++i) {
+    const uint64_t top = wave_max_u64(best);               // uniform
+    if (top == 0) break;                                   // no candidate left: a full tree
+    const uint32_t thi = (uint32_t)(top >> 32), tlo = (uint32_t)top;
+    const float sc = float_of(thi);
+    const int key = 32767 - (int)((tlo >> 16) & 0x7fff);
+    const int depth = (int)(tlo & 0x7f);
+    const int par = (key >> 4) - 1, rank = key & 15;
+    const int slot = (depth - 1) * K + rank;
+    const uint64_t pword = n_c[max(par, 0)];
+    const float lp_sib = s_lp[min(slot + 1, NK - 1)];
+    const float lp_fc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lp_first), min(depth, 63)));
+    if (lane == 0) n_c[i] = top;
+    // the first child takes over the popped slot (an empty slot if none)
+    uint64_t c1 = 0;
+    if (depth < p.n_pos) {
+      const float s1 = sc + lp_fc;
+      if (s1 != neg_inf()) c1 = cand(s1, (i + 1) << 4, depth + 1);
+    }
+    if (best == top) {                                     // the owner refills its slot, rescans
+      e_c[best_e] = c1;
+      best = 0; best_e = -1;
+      // slots past n_ent are zero (cleared at the start, capacity padded to
+      // whole rounds of 8 per lane), so each round issues its 8 loads at once
+      for (int x = lane; x < n_ent; x += 512) {
+        uint64_t cc[8];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(v, o, 64);
-      const int ok = __shfl_xor(k, o, 64);
-      const int oe = __shfl_xor(e, o, 64);
-      if (before(ov, ok, v, k)) { v = ov; k = ok; e = oe; }   // keys are unique: a strict order
-    }
-    if (e < 0) break;                              // no candidate left: a full tree
-    __syncthreads();
-    const float sc = e_score[e], psc = e_pscore[e];
-    const int par = e_par[e], rd = e_rd[e];
-    const int rank = rd & 0xff, depth = rd >> 8;
-    if (lane == 0) {
-      const int slot = (depth - 1) * K + rank;
-      const int64_t o = (int64_t)b * p.budget + i;
-      p.node_token[o] = s_tok[slot];
-      p.node_parent[o] = par;
-      p.node_depth[o] = depth;
-      p.node_logp[o] = sc;
-      s_par[i] = par;
-    }
-    if ((e & 63) == lane) {                        // the owner drops it and rescans its slots
-      e_score[e] = neg_inf();
-      best_s = neg_inf(); best_k = INT_MAX; best_e = -1;
-      for (int x = lane; x < n_ent; x += 64) {
-        const float xs = e_score[x];
-        if (xs == neg_inf()) continue;
-        const int xk = key2(x);
-        if (before(xs, xk, best_s, best_k)) { best_s = xs; best_k = xk; best_e = x; }
+        for (int u = 0; u < 8; ++u) cc[u] = e_c[x + 64 * u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (cc[u] > best) { best = cc[u]; best_e = x + 64 * u; }
       }
     }
-    if (depth < p.n_pos) append(sc + s_lp[depth * K], sc, i, 0, depth + 1);          // first child
-    if (rank + 1 < K) append(psc + s_lp[(depth - 1) * K + rank + 1], psc, par, rank + 1, depth);   // next sibling
-    __syncthreads();
+    // the next sibling takes a new slot
+    if (rank + 1 < K) {
+      const float psc = par < 0 ? 0.f : float_of((uint32_t)(pword >> 32));
+      const float s2 = psc + lp_sib;
+      if (s2 != neg_inf()) {
+        const int e = n_ent++;
+        if ((e & 63) == lane) {
+          const uint64_t c2 = cand(s2, ((par + 1) << 4) + rank + 1, depth);
+          e_c[e] = c2;
+          if (c2 > best) { best = c2; best_e = e; }
+        }
+      }
+    }
+    wave_sync();
   }
+  __syncthreads();
   if (lane == 0) p.n_nodes[b] = i;
-  for (int x = i + lane; x < p.budget; x += 64) {  // unused node slots
-    const int64_t o = (int64_t)b * p.budget + x;
-    p.node_token[o] = -1; p.node_parent[o] = -2; p.node_depth[o] = 0; p.node_logp[o] = neg_inf();
+  for (int x = lane; x < N; x += 64) {
+    const int64_t o = (int64_t)b * N + x;
+    if (x < i) {
+      const uint64_t c = n_c[x];
+      const uint32_t lo = (uint32_t)c;
+      const int key = 32767 - (int)((lo >> 16) & 0x7fff);
+      const int depth = (int)(lo & 0x7f);
+      const int par = (key >> 4) - 1;
+      p.node_token[o] = s_tok[(depth - 1) * K + (key & 15)];
+      p.node_parent[o] = par;
+      p.node_depth[o] = depth;
+      p.node_logp[o] = float_of((uint32_t)(c >> 32));
+      n_par[x] = par;
+    } else {
+      p.node_token[o] = -1; p.node_parent[o] = -2; p.node_depth[o] = 0; p.node_logp[o] = neg_inf();
+    }
   }
   __syncthreads();
   if (p.mask) {
-    // node x sees itself and its ancestors; unused rows are all zero
-    for (int x = lane; x < p.budget; x += 64) {
-      uint32_t* row = p.mask + ((int64_t)b * p.budget + x) * p.W;
-      for (int wd = 0; wd < p.W; ++wd) row[wd] = 0u;
+    // row x: bits of x and of its ancestors.  The ancestors come in falling
+    // index order, so the row is written word by word from the top, each
+    // word once; unused rows are all zero.
+    for (int x = lane; x < N; x += 64) {
+      uint32_t* row = p.mask + ((int64_t)b * N + x) * p.W;
+      int w = p.W - 1;
       if (x < i) {
-        for (int y = x; y >= 0; y = s_par[y]) row[y >> 5] |= 1u << (y & 31);
+        const int top_w = x >> 5;
+        for (; w > top_w; --w) row[w] = 0u;
+        uint32_t acc = 0u;
+        for (int y = x; y >= 0; y = n_par[y]) {
+          const int yw = y >> 5;
+          while (w > yw) { row[w] = acc; acc = 0u; --w; }
+          acc |= 1u << (y & 31);
+        }
+        row[w] = acc;
+        --w;
       }
+      for (; w >= 0; --w) row[w] = 0u;
     }
   }
 }
@@ -296,9 +542,21 @@ struct TopkPlan {
   size_t total;
 };
 
+// Row chunks for the top-K pass: long ones (a wavefront's fixed costs, the
+// threshold seed and the folds, are then small next to its stream), split
+// only as far as needed for about DFLASH_TOPK_WGS workgroups, at most 64 per
+// row.
+VocabPlan topk_chunks(int64_t rows, int V) {
+  const int64_t want = std::max<int64_t>(1, cdiv(DFLASH_TOPK_WGS, std::max<int64_t>(rows, 1)));
+  int64_t n = std::min<int64_t>({want, cdiv(V, 32768), 64});
+  n = std::max<int64_t>(n, 1);
+  const int64_t chunk = cdiv(cdiv(V, n), 8) * 8;
+  return VocabPlan{(int)chunk, (int)cdiv(V, chunk)};
+}
+
 TopkPlan topk_plan(int64_t rows, int V, int K) {
   TopkPlan t;
-  t.pl = plan_vocab(rows, V);
+  t.pl = topk_chunks(rows, V);
   const int64_t n = rows * t.pl.n_chunks;
   t.cand_v = 0;
   t.cand_i = align256(sizeof(float) * n * K);
@@ -308,8 +566,7 @@ TopkPlan topk_plan(int64_t rows, int V, int K) {
 }
 
 size_t tree_lds_bytes(int n_pos, int K, int budget) {
-  const size_t cap = 2 * (size_t)budget + 2;
-  return cap * 16 + (size_t)n_pos * K * 8 + (size_t)budget * 4;
+  return (size_t)tree_cap(budget) * 8 + (size_t)budget * 12 + (size_t)n_pos * K * 8;
 }
 
 }  // namespace
