@@ -16,7 +16,8 @@ The pages this follows (cited by short title and section throughout):
   (liyongzhi.xyz/posts/2026/04/speculative-decoding/) -- sections 2, 3 (the
   acceptance rule, the residual distribution and the worked cat/dog example), 4,
   and 6 (DDTree: the draft tree, its best-first growth under a node budget, the
-  ancestor-only mask and the greedy walk; followed by ``tree.py``).
+  ancestor-only mask and the target's attention under it, the greedy walk, and
+  the commit of the accepted path's KV; followed by ``tree.py``).
 * [DLoop] "DLoop 完全拆解：让一次验证覆盖多个草稿阶段的循环投机解码"
   (pinghaoyang.com.cn/aigc/posts/dloop-looped-speculative-decoding/) --
   "机制一：置信度门控" and "验证与无损性".
@@ -35,12 +36,13 @@ from .materialize import (fuse_hiddens, project_kv, materialize, paged_write, ga
 from .attention import block_attention, block_attention_masked
 from .verify import (verify_greedy, verify_sample, gate, row_log_softmax, GreedyResult,
                      SampleResult, GateResult)
-from .tree import topk_logprobs, build_tree, ancestor_mask, walk_greedy, target_argmax, Tree, TreeWalk
+from .tree import (topk_logprobs, build_tree, ancestor_mask, walk_greedy, target_argmax, Tree,
+                   TreeWalk, tree_attention, commit_tree_kv)
 
 __all__ = [
     "widen", "round_to_bf16", "round_to_f32", "fuse_hiddens", "project_kv", "materialize",
     "paged_write", "gather_paged", "k_norm", "rope_half_split", "row_positions", "block_attention", "block_attention_masked",
     "verify_greedy", "verify_sample", "gate", "row_log_softmax", "GreedyResult",
     "SampleResult", "GateResult", "topk_logprobs", "build_tree", "ancestor_mask", "walk_greedy",
-    "target_argmax", "Tree", "TreeWalk",
+    "target_argmax", "Tree", "TreeWalk", "tree_attention", "commit_tree_kv",
 ]

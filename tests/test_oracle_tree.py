@@ -162,3 +162,91 @@ def test_walk_on_a_single_path_is_the_chain_verify():
         parent = np.arange(-1, 6)
         w = oracle.walk_greedy(c.draft_tokens[b], parent, tp[b])
         assert w.accept_len == ref.accept_len[b] and w.bonus == ref.bonus[b]
+
+
+# ------------------------------------------------------------ tree attention
+
+def _chain_parents(n):
+    return np.arange(n) - 1
+
+
+def test_tree_attention_of_a_chain_is_causal_block_attention():
+    """A tree that is one path (node j's parent is node j - 1) is a block of
+    n + 1 rows in which row i sees rows 0..i: the causal block mask."""
+    R = 7
+    c = synth.attention_case(71, dtype="f32", B=2, k=R, n_q_heads=4, n_kv_heads=2, head_dim=16,
+                             ctx_lens=[20, 0])
+    par = np.stack([_chain_parents(R - 1)] * 2)
+    out, lse = oracle.tree_attention(c.q, c.k_blk, c.v_blk, c.cache_k, c.cache_v, c.block_table,
+                                     c.ctx_lens, par, [R - 1, R - 1], "f32")
+    ref, rlse = oracle.block_attention(c.q, c.k_blk, c.v_blk, c.cache_k, c.cache_v, c.block_table,
+                                       c.ctx_lens, "f32", causal=True)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, rlse, rtol=0, atol=1e-12)
+
+
+def test_tree_attention_row_is_its_root_path_prefilled_alone():
+    """6.4: verifying the tree in one pass gives each node what prefilling its
+    own root path alone would: node x's row equals the last row of causal
+    block attention over [root, ancestors of x, x]."""
+    x = synth.tree_case(72, dtype="f32", B=1, n_pos=4, V=50, std=1.0).draft_logits
+    tok, lp = oracle.topk_logprobs(x, "f32", K=3)
+    t = oracle.build_tree(tok[0], lp[0], budget=20)
+    R = 21
+    c = synth.attention_case(73, dtype="f32", B=1, k=R, n_q_heads=4, n_kv_heads=1, head_dim=16,
+                             ctx_lens=[33])
+    out, _ = oracle.tree_attention(c.q, c.k_blk, c.v_blk, c.cache_k, c.cache_v, c.block_table,
+                                   c.ctx_lens, t.parent[None], [20], "f32")
+    for node in (0, 5, 11, 19):
+        path, y = [], node
+        while y >= 0:
+            path.append(1 + y)
+            y = int(t.parent[y])
+        rows = [0] + path[::-1]
+        ref, _ = oracle.block_attention(c.q[:, rows], c.k_blk[:, rows], c.v_blk[:, rows],
+                                        c.cache_k, c.cache_v, c.block_table, c.ctx_lens, "f32",
+                                        causal=True)
+        np.testing.assert_allclose(out[0, 1 + node], ref[0, -1], rtol=0, atol=1e-12)
+
+
+def test_tree_attention_star_and_rows_past_the_tree():
+    """Children of the root see the context, the root and themselves; rows
+    past n_nodes see the context and the root only."""
+    R = 6
+    c = synth.attention_case(74, dtype="f32", B=1, k=R, n_q_heads=2, n_kv_heads=2, head_dim=8,
+                             ctx_lens=[5])
+    par = np.full((1, R - 1), -1)
+    out, _ = oracle.tree_attention(c.q, c.k_blk, c.v_blk, c.cache_k, c.cache_v, c.block_table,
+                                   c.ctx_lens, par, [3], "f32")
+    for r in range(R):
+        rows = [0, r] if 1 <= r <= 3 else [0]
+        q = c.q[:, [r]]
+        # one query row against the context and the rows it sees (bidirectional block)
+        ref, _ = oracle.block_attention(np.repeat(q, len(rows), axis=1), c.k_blk[:, rows],
+                                        c.v_blk[:, rows], c.cache_k, c.cache_v, c.block_table,
+                                        c.ctx_lens, "f32")
+        np.testing.assert_allclose(out[0, r], ref[0, 0], rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------ KV recycling
+
+def test_commit_tree_kv_hand_example():
+    """Tree of 5 nodes, the walk accepted nodes 1 then 3 (accept_len 2): the
+    root and tree rows 2 and 4 land at positions prefix .. prefix + 2, in that
+    order; nothing else is written; a request with accept_len -1 commits
+    nothing; an unmapped page is skipped."""
+    Hkv, D, R = 1, 2, 6
+    kt = np.zeros((2, R, Hkv, D), dtype=np.float32)
+    for r in range(R):
+        kt[:, r] = 10 * np.arange(2)[:, None, None] + r
+    vt = -kt
+    ck = np.full((4, 16, Hkv, D), 7e3, dtype=np.float32)
+    cv = ck.copy()
+    bt = np.array([[2, 0], [1, -1]], dtype=np.int32)       # request 1's second page unmapped
+    acc_nodes = np.array([[1, 3, -1], [0, 1, 2]])
+    written = oracle.commit_tree_kv(kt, vt, acc_nodes, [2, -1], [14, 3], ck, cv, bt)
+    # request 0: positions 14, 15 on page 2, position 16 on page 0 slot 0
+    assert ck[2, 14, 0, 0] == 0 and ck[2, 15, 0, 0] == 2 and ck[0, 0, 0, 0] == 4
+    assert cv[0, 0, 0, 0] == -4
+    assert written.sum() == 3
+    assert np.all(ck[1] == 7e3) and np.all(ck[3] == 7e3)
