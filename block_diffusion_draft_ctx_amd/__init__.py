@@ -25,7 +25,8 @@ EXPORTS = (
     "dflash_verify_workspace_size", "dflash_verify_greedy", "dflash_verify_sample",
     "dflash_gate_workspace_size", "dflash_gate",
     "dflash_tree_workspace_size", "dflash_tree_verify_workspace_size", "dflash_tree_build",
-    "dflash_tree_verify_greedy",
+    "dflash_tree_verify_greedy", "dflash_tree_attention_workspace_size", "dflash_tree_attention",
+    "dflash_tree_commit_kv",
 )
 
 
@@ -94,6 +95,14 @@ def _declare(lib):
     lib.dflash_tree_verify_greedy.restype = I32
     lib.dflash_tree_verify_greedy.argtypes = [
         I32, I32, I32, P, I64, P, P, P, I32, P, P, P, P, P, P, I32, P, SZ, P]
+    lib.dflash_tree_attention_workspace_size.restype = SZ
+    lib.dflash_tree_attention_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, I32]
+    lib.dflash_tree_attention.restype = I32
+    lib.dflash_tree_attention.argtypes = [
+        I32, I32, I32, I32, I32, P, P, P, P, P, I32, I32, P, I32, P, P, F, P, P, I32, I32, P, SZ, P]
+    lib.dflash_tree_commit_kv.restype = I32
+    lib.dflash_tree_commit_kv.argtypes = [
+        I32, I32, I32, I32, I32, PP, PP, ctypes.POINTER(KVLayer), P, I32, P, I32, P, P, I32, P]
 
 
 def lib():
@@ -482,3 +491,63 @@ def tree_verify_greedy(target_logits, node_token, node_parent, n_nodes, max_dept
         _ptr(o.get("new_seq_lens")), dt, _ptr(ws), nws, _stream(stream))
     _check(s, "dflash_tree_verify_greedy")
     return o
+
+
+def tree_attention(q, k_tree, v_tree, cache_k, cache_v, block_table, ctx_lens, ancestor_mask,
+                   scale=0.0, out=None, lse=None, workspace=None, stream=None, out_dtype=None):
+    """dflash_tree_attention.  q [B, R, Hq, D], k_tree / v_tree [B, R, Hkv, D]
+    with R = 1 + budget (row 0 the root, row 1 + j node j); caches
+    [num_pages, 16, Hkv, D]; block_table [B, max_pages]; ctx_lens [B];
+    ancestor_mask [B, R - 1, ceil((R - 1) / 32)] int32 bit rows as
+    ``tree_build`` returns them.  Returns (out, lse)."""
+    torch = _torch()
+    L = lib()
+    B, R, Hq, D = q.shape
+    Hkv = k_tree.shape[2]
+    dt = _dtype_code(q)
+    for n, t in (("q", q), ("k_tree", k_tree), ("v_tree", v_tree), ("cache_k", cache_k),
+                 ("cache_v", cache_v)):
+        _dev(t, n)
+    _i32(block_table, "block_table")
+    _i32(ctx_lens, "ctx_lens")
+    if ancestor_mask is not None:
+        _i32(ancestor_mask, "ancestor_mask")
+        if tuple(ancestor_mask.shape) != (B, R - 1, (R + 30) // 32):
+            raise ValueError("ancestor_mask must be [B, R - 1, ceil((R - 1) / 32)]")
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    _dev(out, "out")
+    odt = _dtype_code(out)
+    need = L.dflash_tree_attention_workspace_size(B, R, Hq, Hkv, D, block_table.shape[1], dt)
+    ws, nws = _workspace(need, q.device, workspace)
+    s = L.dflash_tree_attention(
+        B, R, Hq, Hkv, D, _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(cache_k), _ptr(cache_v),
+        cache_k.shape[0], cache_k.shape[1], _ptr(block_table), block_table.shape[1],
+        _ptr(ctx_lens), _ptr(ancestor_mask), float(scale), _ptr(out), _ptr(lse), dt, odt,
+        _ptr(ws), nws, _stream(stream))
+    _check(s, "dflash_tree_attention")
+    return out, lse
+
+
+def tree_commit_kv(k_tree: Sequence, v_tree: Sequence, cache_k: Sequence, cache_v: Sequence,
+                   block_table, accepted_nodes, accept_len, prefix_lens, stream=None):
+    """dflash_tree_commit_kv.  Per layer l: k_tree[l] / v_tree[l]
+    [B, R, Hkv, D], cache_k[l] / cache_v[l] [num_pages, 16, Hkv, D];
+    block_table [B, max_pages]; accepted_nodes [B, max_depth], accept_len and
+    prefix_lens [B] int32 (tree_verify_greedy's outputs and its prefix)."""
+    L = lib()
+    n_layers = len(k_tree)
+    B, R, Hkv, D = k_tree[0].shape
+    dt = _dtype_code(k_tree[0])
+    for t in (accepted_nodes, accept_len, prefix_lens, block_table):
+        _i32(t, "int32 argument")
+    kp, kpa = _pp([_ptr(_dev(t, "k_tree")) for t in k_tree])
+    vp, vpa = _pp([_ptr(_dev(t, "v_tree")) for t in v_tree])
+    caches = (KVLayer * n_layers)(*[KVLayer(_ptr(_dev(k, "cache_k")), _ptr(_dev(v, "cache_v")),
+                                            k.shape[0], k.shape[1])
+                                    for k, v in zip(cache_k, cache_v)])
+    s = L.dflash_tree_commit_kv(
+        B, R, n_layers, Hkv, D, kp, vp, caches, _ptr(block_table), block_table.shape[1],
+        _ptr(accepted_nodes), accepted_nodes.shape[1], _ptr(accept_len), _ptr(prefix_lens), dt,
+        _stream(stream))
+    _check(s, "dflash_tree_commit_kv")

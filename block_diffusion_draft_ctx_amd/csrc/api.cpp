@@ -170,7 +170,52 @@ dflash_status dflash_block_attention(int B, int k, int n_q_heads, int n_kv_heads
   if (dflash_status s = check_ws(ws, ws_bytes, need)) return s;
   AttnArgs a{B, k, n_q_heads, n_kv_heads, head_dim, q, k_blk, v_blk, cache_k, cache_v, num_pages,
              block_table, max_pages_per_seq, table_rows == 1, ctx_lens, scale,
-             block_mask == DFLASH_MASK_CAUSAL, out, lse_out, out_dtype == DFLASH_F32};
+             block_mask == DFLASH_MASK_CAUSAL ? kMaskCausal : kMaskBidir, nullptr, out, lse_out,
+             out_dtype == DFLASH_F32};
+  return hip_status(launch_attention(bf16, a, ws, static_cast<hipStream_t>(stream)));
+}
+
+size_t dflash_tree_attention_workspace_size(int B, int n_rows, int n_q_heads, int n_kv_heads,
+                                            int head_dim, int max_pages_per_seq,
+                                            dflash_dtype dtype) {
+  if (B <= 0 || n_rows <= 0 || n_rows > kTreeBudgetMax + 1 || n_q_heads <= 0 || n_kv_heads <= 0 ||
+      head_dim <= 0 || max_pages_per_seq <= 0 || n_q_heads % n_kv_heads)
+    return 0;
+  if (dtype != DFLASH_BF16) return 0;
+  return attention_ws_bytes(B, n_rows, n_q_heads, n_kv_heads, head_dim, max_pages_per_seq, true);
+}
+
+dflash_status dflash_tree_attention(int B, int n_rows, int n_q_heads, int n_kv_heads, int head_dim,
+                                    const void* q, const void* k_tree, const void* v_tree,
+                                    const void* cache_k, const void* cache_v, int num_pages,
+                                    int page_size, const int32_t* block_table,
+                                    int max_pages_per_seq, const int32_t* ctx_lens,
+                                    const uint32_t* ancestor_mask, float scale, void* out,
+                                    float* lse_out, dflash_dtype dtype, dflash_dtype out_dtype,
+                                    void* ws, size_t ws_bytes, dflash_stream_t stream) {
+  if (bad_dtype(dtype) || bad_dtype(out_dtype)) return DFLASH_E_ARG;
+  if (dtype == DFLASH_F32 && out_dtype != DFLASH_F32) return DFLASH_E_UNSUPPORTED;
+  if (B < 0 || n_rows < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1) return DFLASH_E_ARG;
+  if (n_q_heads % n_kv_heads) return DFLASH_E_ARG;
+  if (head_dim != 64 && head_dim != 128) return DFLASH_E_UNSUPPORTED;
+  if (n_rows > kTreeBudgetMax + 1) return DFLASH_E_UNSUPPORTED;
+  if (page_size != 16) return DFLASH_E_UNSUPPORTED;
+  if (!(scale >= 0.f)) return DFLASH_E_ARG;
+  if (B == 0) return DFLASH_OK;
+  if (num_pages < 1 || max_pages_per_seq < 1) return DFLASH_E_ARG;
+  if (!q || !k_tree || !v_tree || !cache_k || !cache_v || !block_table || !ctx_lens || !out)
+    return DFLASH_E_ARG;
+  if (n_rows > 1 && !ancestor_mask) return DFLASH_E_ARG;
+  const bool bf16 = dtype == DFLASH_BF16;
+  if (bf16 && !(al16(q) && al16(k_tree) && al16(v_tree) && al16(cache_k) && al16(cache_v) && al16(out)))
+    return DFLASH_E_UNSUPPORTED;
+  const size_t need = bf16 ? attention_ws_bytes(B, n_rows, n_q_heads, n_kv_heads, head_dim,
+                                                max_pages_per_seq, true)
+                           : 0;
+  if (dflash_status s = check_ws(ws, ws_bytes, need)) return s;
+  AttnArgs a{B, n_rows, n_q_heads, n_kv_heads, head_dim, q, k_tree, v_tree, cache_k, cache_v,
+             num_pages, block_table, max_pages_per_seq, false, ctx_lens, scale, kMaskTree,
+             ancestor_mask, out, lse_out, out_dtype == DFLASH_F32};
   return hip_status(launch_attention(bf16, a, ws, static_cast<hipStream_t>(stream)));
 }
 
@@ -313,6 +358,40 @@ dflash_status dflash_tree_verify_greedy(int B, int budget, int V, const void* ta
                                        row_stride, node_token, node_parent, n_nodes, max_depth,
                                        accept_len, bonus, accepted_nodes, commit_lens, prefix_lens,
                                        new_seq_lens, ws, static_cast<hipStream_t>(stream)));
+}
+
+dflash_status dflash_tree_commit_kv(int B, int n_rows, int n_layers, int n_kv_heads, int head_dim,
+                                    const void* const* k_tree, const void* const* v_tree,
+                                    const dflash_kv_layer* caches, const int32_t* block_table,
+                                    int max_pages_per_seq, const int32_t* accepted_nodes,
+                                    int max_depth, const int32_t* accept_len,
+                                    const int32_t* prefix_lens, dflash_dtype dtype,
+                                    dflash_stream_t stream) {
+  if (bad_dtype(dtype)) return DFLASH_E_ARG;
+  if (B < 0 || n_rows < 1 || n_layers < 1 || n_kv_heads < 1 || head_dim < 1 || max_depth < 1)
+    return DFLASH_E_ARG;
+  if (n_layers > kCommitMaxLayers) return DFLASH_E_UNSUPPORTED;
+  if (B == 0) return DFLASH_OK;
+  if (!k_tree || !v_tree || !caches || !block_table || !accepted_nodes || !accept_len ||
+      !prefix_lens || max_pages_per_seq < 1)
+    return DFLASH_E_ARG;
+  const int es = dtype == DFLASH_BF16 ? 2 : 4;
+  if (((int64_t)n_kv_heads * head_dim * es) % 16) return DFLASH_E_UNSUPPORTED;
+  CommitArgs a{};
+  a.B = B; a.R = n_rows; a.n_layers = n_layers; a.Hkv = n_kv_heads; a.D = head_dim; a.es = es;
+  for (int l = 0; l < n_layers; ++l) {
+    if (!k_tree[l] || !v_tree[l] || !caches[l].k || !caches[l].v || caches[l].num_pages < 1)
+      return DFLASH_E_ARG;
+    if (caches[l].page_size != 16) return DFLASH_E_UNSUPPORTED;
+    if (!(al16(k_tree[l]) && al16(v_tree[l]) && al16(caches[l].k) && al16(caches[l].v)))
+      return DFLASH_E_UNSUPPORTED;
+    a.k_tree[l] = k_tree[l]; a.v_tree[l] = v_tree[l];
+    a.cache_k[l] = caches[l].k; a.cache_v[l] = caches[l].v; a.num_pages[l] = caches[l].num_pages;
+  }
+  a.block_table = block_table; a.max_pages = max_pages_per_seq;
+  a.path = accepted_nodes; a.max_depth = max_depth; a.accept_len = accept_len;
+  a.prefix = prefix_lens;
+  return hip_status(launch_tree_commit(a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -73,7 +73,9 @@ struct AttnP {
   float2* pml;  // split partials: (m, l) [B*Hkv*S*G*k]
   int S;        // ctx splits
   int RC;       // query-row chunks per (request, kv-head): more rows than one workgroup holds
-  int causal;   // block position i sees block keys 0..i only
+  int mode;     // kMaskBidir, kMaskCausal or kMaskTree
+  const uint32_t* tm;   // kMaskTree: ancestor bit rows [B, k - 1, tmw]
+  int tmw;
 };
 
 // Transposing LDS read (gfx950): within each 16-lane group, output lane j
@@ -293,6 +295,43 @@ void k_attn_bf16(AttnP p) {
   // P.V accumulation for this wave's query slice and key half.
   auto compute = [&](const uint16_t* Ks, int tile) __attribute__((always_inline)) {
     const uint16_t* Vs = Ks + kKT * KS;
+    // no masked key in the tile (uniform): all context, or -- with the
+    // bidirectional mask -- all keys of a single request's list
+    const bool dense = tile * kKT + kKT <= (NB == 1 && p.mode == kMaskBidir ? total : Cmin);
+    // visibility of this lane's 16 keys; key j of the lane is key
+    // 32wk + 8*(j/4) + 4*hh + j%4 of the tile (the S^T accumulator order)
+    uint32_t vis = 0xffffu;
+    if (!dense) {
+      uint64_t win = 0;       // tree: ancestor bits of this row for nodes [ybase, ybase + 64)
+      int ybase = 0;
+      if (p.mode == kMaskTree) {
+        const int y0 = tile * kKT + 32 * wk - C - 1;   // node of the wave half's first key
+        ybase = y0 >= 0 ? (y0 & ~31) : -32;
+        if (qvalid && pos >= 1) {
+          const uint32_t* mrow = p.tm + ((int64_t)b * (k - 1) + (pos - 1)) * p.tmw;
+          const int w0 = ybase >> 5;
+          const uint32_t lo = (w0 >= 0 && w0 < p.tmw) ? mrow[w0] : 0u;
+          const uint32_t hi = (w0 + 1 >= 0 && w0 + 1 < p.tmw) ? mrow[w0 + 1] : 0u;
+          win = ((uint64_t)hi << 32) | lo;
+        }
+      }
+      vis = 0u;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int kk = tile * kKT + 32 * wk + 8 * (j >> 2) + 4 * hh + (j & 3);
+        bool v = kk < total;
+        if (NB > 1) v = kk < C ? kk < Crow : (v && (kk - C) / k == jb);
+        if (p.mode == kMaskCausal && kk >= C) v = v && (kk - C) % k <= pos;
+        if (p.mode == kMaskTree && kk >= C) {
+          const int y = kk - C - 1;                     // -1: the root
+          v = v && (y < 0 || ((win >> (y - ybase)) & 1));
+        }
+        vis |= (v ? 1u : 0u) << j;
+      }
+      // a wave half with no visible key in the tile skips it (the sparse
+      // blocks of a tree mask); its softmax state is unchanged
+      if (p.mode == kMaskTree && !__any(vis != 0u)) return;
+    }
     // S^T[32 keys x 32 q] for this wave's key half
     f32x16 sacc;
 #pragma unroll
@@ -306,9 +345,7 @@ void k_attn_bf16(AttnP p) {
     // sacc[j]: key 32wk + 8*(j/4) + 4*hh + j%4 of the tile, query l32
     float sv[16];
     float tmax = neg_inf();
-    // no masked key in the tile (uniform): all context, or -- without the
-    // causal mask -- all keys of a single request's list
-    if (tile * kKT + kKT <= (NB == 1 && !p.causal ? total : Cmin)) {
+    if (dense) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         sv[j] = sacc[j] * p.sl2;
@@ -317,11 +354,7 @@ void k_attn_bf16(AttnP p) {
     } else {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int kk = tile * kKT + 32 * wk + 8 * (j >> 2) + 4 * hh + (j & 3);
-        bool vis = kk < total;
-        if (NB > 1) vis = kk < C ? kk < Crow : (vis && (kk - C) / k == jb);
-        if (p.causal && kk >= C) vis = vis && (kk - C) % k <= pos;
-        sv[j] = vis ? sacc[j] * p.sl2 : neg_inf();
+        sv[j] = ((vis >> j) & 1u) ? sacc[j] * p.sl2 : neg_inf();
         tmax = fmaxf(tmax, sv[j]);
       }
     }
@@ -515,7 +548,8 @@ __global__ __launch_bounds__(64) void k_attn_f32(int B, int k, int Hq, int Hkv, 
                                                  const float* kb, const float* vb,
                                                  const float* ck, const float* cv, int num_pages,
                                                  const int32_t* bt, int max_pages, int bt_stride,
-                                                 const int32_t* ctx, float sl2, int causal,
+                                                 const int32_t* ctx, float sl2, int mode,
+                                                 const uint32_t* tm, int tmw,
                                                  float* out, float* lse, int S, float* po,
                                                  float2* pml) {
   const int i = blockIdx.x % k;
@@ -530,7 +564,8 @@ __global__ __launch_bounds__(64) void k_attn_f32(int B, int k, int Hq, int Hkv, 
   int C = ctx[b];
   bool poison = (C < 0 || C > max_pages * 16);
   if (poison) C = 0;
-  const int total = C + (causal ? i + 1 : k);   // causal: block keys 0..i
+  const int total = C + (mode == kMaskCausal ? i + 1 : k);   // causal: block keys 0..i
+  const uint32_t* mrow = (mode == kMaskTree && i >= 1) ? tm + ((int64_t)b * (k - 1) + (i - 1)) * tmw : nullptr;
   float m = neg_inf(), l = 0.f, o[D];
   for (int d = 0; d < D; ++d) o[d] = 0.f;
   for (int j = t; j < total; j += 64) {
@@ -542,6 +577,10 @@ __global__ __launch_bounds__(64) void k_attn_f32(int B, int k, int Hq, int Hkv, 
       const int64_t off = (((int64_t)page * 16 + (j & 15)) * Hkv + g) * D;
       kr = ck + off; vr = cv + off;
     } else {
+      if (mode == kMaskTree && j > C) {           // node y = j - C - 1: an ancestor (or itself)?
+        const int y = j - C - 1;
+        if (!mrow || !((mrow[y >> 5] >> (y & 31)) & 1u)) continue;
+      }
       const int64_t off = (((int64_t)b * k + (j - C)) * Hkv + g) * D;
       kr = kb + off; vr = vb + off;
     }
@@ -582,6 +621,8 @@ __global__ __launch_bounds__(64) void k_attn_f32(int B, int k, int Hq, int Hkv, 
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+// 32-bit words of a tree mask row for a block of k rows (k - 1 nodes)
+inline int tree_words(int k) { return k > 1 ? (k - 1 + 31) / 32 : 1; }
 
 template <int D, int NQ, int NB>
 void launch_bf16(const AttnArgs& a, AttnP p, hipStream_t st) {
@@ -595,7 +636,7 @@ void dispatch_nw(const AttnArgs& a, AttnP p, hipStream_t st) {
   const int rows = a.Hq / a.Hkv * a.k;            // query rows per request and kv-head
   // Requests on one shared table row go two to a workgroup when the pair's
   // rows fit four 32-row slices: the shared context is then read once per pair.
-  if (DFLASH_ATTN_PAIR && a.shared_table && a.B > 1 && 2 * rows <= 128) {
+  if (DFLASH_ATTN_PAIR && a.shared_table && a.mode != kMaskTree && a.B > 1 && 2 * rows <= 128) {
     if (2 * rows <= 64) launch_bf16<D, 2, 2>(a, p, st);
     else launch_bf16<D, 4, 2>(a, p, st);
     return;
@@ -606,18 +647,26 @@ void dispatch_nw(const AttnArgs& a, AttnP p, hipStream_t st) {
   if (nq <= 1) launch_bf16<D, 1, 1>(a, p, st);
   else if (nq <= 2) launch_bf16<D, 2, 1>(a, p, st);
   else {
-    p.RC = (nq + 3) / 4;
+    p.RC = attention_row_chunks(a.Hq / a.Hkv, a.k);
     launch_bf16<D, 4, 1>(a, p, st);
   }
 }
 
 }  // namespace
 
-int attention_splits(int B, int Hkv, int k, int max_pages) {
+int attention_row_chunks(int G, int k) {
+  // query-row chunks of one (request, kv-head): one workgroup up to 64 rows,
+  // otherwise chunks of 128 rows (four 32-row slices)
+  const int nq = (G * k + 31) / 32;
+  return nq <= 2 ? 1 : (nq + 3) / 4;
+}
+
+int attention_splits(int B, int Hkv, int G, int k, int max_pages) {
   // About two workgroups per CU so every CU keeps several tiles in flight,
   // but no split shorter than 4 key tiles; a split never spans more pages
-  // than its LDS page list holds.
-  const int64_t groups = (int64_t)B * Hkv;
+  // than its LDS page list holds.  Row chunks already multiply the
+  // workgroups.
+  const int64_t groups = (int64_t)B * Hkv * attention_row_chunks(G, k);
   // (sized for the longest key list of either workgroup shape: a pair of
   // requests on one shared table row adds 2k block keys)
   const int64_t tiles = ((int64_t)max_pages * 16 + 2 * k + kKT - 1) / kKT;
@@ -631,7 +680,7 @@ int attention_splits(int B, int Hkv, int k, int max_pages) {
 
 size_t attention_ws_bytes(int B, int k, int Hq, int Hkv, int D, int max_pages, bool bf16) {
   (void)bf16;
-  const int S = attention_splits(B, Hkv, k, max_pages);
+  const int S = attention_splits(B, Hkv, Hq / Hkv, k, max_pages);
   if (S == 1) return 0;
   const int64_t rows = (int64_t)B * Hkv * S * (Hq / Hkv) * k;
   return align256(sizeof(float) * rows * D) + align256(sizeof(float2) * rows);
@@ -639,7 +688,7 @@ size_t attention_ws_bytes(int B, int k, int Hq, int Hkv, int D, int max_pages, b
 
 hipError_t launch_attention(bool bf16, const AttnArgs& a, void* ws, hipStream_t st) {
   const float scale = a.scale == 0.f ? 1.f / std::sqrt((float)a.D) : a.scale;
-  const int S = attention_splits(a.B, a.Hkv, a.k, a.max_pages);
+  const int S = bf16 ? attention_splits(a.B, a.Hkv, a.Hq / a.Hkv, a.k, a.max_pages) : 1;
   const int64_t rows = (int64_t)a.B * a.Hkv * S * (a.Hq / a.Hkv) * a.k;
   float* po = static_cast<float*>(ws);
   float2* pml = reinterpret_cast<float2*>(static_cast<char*>(ws) + align256(sizeof(float) * rows * a.D));
@@ -649,7 +698,7 @@ hipError_t launch_attention(bool bf16, const AttnArgs& a, void* ws, hipStream_t 
             static_cast<const uint16_t*>(a.v_blk), static_cast<const uint16_t*>(a.cache_k),
             static_cast<const uint16_t*>(a.cache_v), a.num_pages, a.block_table, a.max_pages,
             a.shared_table ? 0 : a.max_pages, a.ctx_lens, scale * kLog2e, a.out,
-            a.out_f32 ? 1 : 0, a.lse, po, pml, S, 1, a.causal ? 1 : 0};
+            a.out_f32 ? 1 : 0, a.lse, po, pml, S, 1, a.mode, a.tree_mask, tree_words(a.k)};
     if (a.D == 64) dispatch_nw<64>(a, p, st);
     else dispatch_nw<128>(a, p, st);
     if (S > 1) {
@@ -670,16 +719,16 @@ hipError_t launch_attention(bool bf16, const AttnArgs& a, void* ws, hipStream_t 
                          static_cast<const float*>(a.v_blk), static_cast<const float*>(a.cache_k),
                          static_cast<const float*>(a.cache_v), a.num_pages, a.block_table,
                          a.max_pages, a.shared_table ? 0 : a.max_pages, a.ctx_lens,
-                         scale * kLog2e, a.causal ? 1 : 0, static_cast<float*>(a.out), a.lse, 1,
-                         nullptr, nullptr);
+                         scale * kLog2e, a.mode, a.tree_mask, tree_words(a.k),
+                         static_cast<float*>(a.out), a.lse, 1, nullptr, nullptr);
     else
       hipLaunchKernelGGL((k_attn_f32<128>), dim3(grid), dim3(64), 0, st, a.B, a.k, a.Hq, a.Hkv,
                          static_cast<const float*>(a.q), static_cast<const float*>(a.k_blk),
                          static_cast<const float*>(a.v_blk), static_cast<const float*>(a.cache_k),
                          static_cast<const float*>(a.cache_v), a.num_pages, a.block_table,
                          a.max_pages, a.shared_table ? 0 : a.max_pages, a.ctx_lens,
-                         scale * kLog2e, a.causal ? 1 : 0, static_cast<float*>(a.out), a.lse, 1,
-                         nullptr, nullptr);
+                         scale * kLog2e, a.mode, a.tree_mask, tree_words(a.k),
+                         static_cast<float*>(a.out), a.lse, 1, nullptr, nullptr);
   }
   return hipGetLastError();
 }

@@ -59,6 +59,24 @@ hipError_t launch_tree_build(bool bf16, int B, int n_pos, int V, const void* dl,
                              int32_t* node_depth, float* node_logp, int32_t* n_nodes,
                              uint32_t* mask, void* ws, hipStream_t st);
 size_t tree_verify_ws_bytes(int B, int budget, int V);
+// KV commit of the accepted path: per layer, the tree pass's K/V rows and the
+// paged cache they join
+constexpr int kCommitMaxLayers = 64;
+struct CommitArgs {
+  int B, R, n_layers, Hkv, D, es;          // es: bytes per element
+  const void* k_tree[kCommitMaxLayers];    // [B, R, Hkv, D]
+  const void* v_tree[kCommitMaxLayers];
+  void* cache_k[kCommitMaxLayers];         // [num_pages, 16, Hkv, D]
+  void* cache_v[kCommitMaxLayers];
+  int num_pages[kCommitMaxLayers];
+  const int32_t* block_table;              // [B, max_pages]
+  int max_pages;
+  const int32_t* path;                     // [B, max_depth] accepted node indices
+  int max_depth;
+  const int32_t* accept_len;               // [B]
+  const int32_t* prefix;                   // [B]
+};
+hipError_t launch_tree_commit(const CommitArgs& a, hipStream_t st);
 hipError_t launch_tree_verify(bool bf16, int B, int budget, int V, const void* tl, int64_t ts,
                               const int32_t* node_token, const int32_t* node_parent,
                               const int32_t* n_nodes, int max_depth, int32_t* accept_len,
@@ -79,12 +97,19 @@ struct AttnArgs {
   bool shared_table;  // every request reads block-table row 0
   const int32_t* ctx_lens;
   float scale;
-  bool causal;        // block position i sees block keys 0..i only
+  int mode;           // what a block row sees of the block: kMaskBidir, kMaskCausal, kMaskTree
+  const uint32_t* tree_mask;  // kMaskTree: [B, k - 1, (k + 30) / 32] ancestor bit rows of the nodes
   void* out;
   float* lse;
   bool out_f32;  // bf16 inputs with an fp32 output
 };
-int attention_splits(int B, int Hkv, int k, int max_pages);
+// Block masks: every block row sees all k block rows; row i sees rows 0..i;
+// or (a flattened draft tree, row 0 the root, row 1 + j node j) row 0 sees
+// itself and row 1 + j sees row 0 and the rows 1 + y of the nodes y whose bit
+// is set in node j's ancestor row.
+constexpr int kMaskBidir = 0, kMaskCausal = 1, kMaskTree = 2;
+int attention_row_chunks(int G, int k);
+int attention_splits(int B, int Hkv, int G, int k, int max_pages);
 size_t attention_ws_bytes(int B, int k, int Hq, int Hkv, int D, int max_pages, bool bf16);
 hipError_t launch_attention(bool bf16, const AttnArgs& a, void* ws, hipStream_t st);
 

@@ -536,6 +536,35 @@ __global__ __launch_bounds__(64) void k_tree_build(TreeP p) {
   }
 }
 
+// KV recycling ([Spec tutorial] 6.6): one workgroup per (layer, request,
+// committed row t): row t is the root (t = 0) or the t-th accepted node, and
+// it is copied, K and V, to the slot of logical position prefix + t, 16 bytes
+// per lane.  Rows past the accepted length, past the path list, or on an
+// unmapped or out-of-range page are not written.
+__global__ __launch_bounds__(256) void k_tree_commit(CommitArgs a) {
+  const int T = a.max_depth + 1;
+  const int t = blockIdx.x % T;
+  const int b = (blockIdx.x / T) % a.B;
+  const int l = blockIdx.x / (T * a.B);
+  const int acc = a.accept_len[b];
+  if (acc < 0 || t > acc) return;
+  const int src = t == 0 ? 0 : 1 + a.path[(int64_t)b * a.max_depth + t - 1];
+  if (src < 0 || src >= a.R) return;
+  const int pos = a.prefix[b] + t;
+  if (pos < 0 || (pos >> 4) >= a.max_pages) return;
+  const int page = a.block_table[(int64_t)b * a.max_pages + (pos >> 4)];
+  if (page < 0 || page >= a.num_pages[l]) return;
+  const int64_t row_bytes = (int64_t)a.Hkv * a.D * a.es;
+  const char* ks = static_cast<const char*>(a.k_tree[l]) + ((int64_t)b * a.R + src) * row_bytes;
+  const char* vs = static_cast<const char*>(a.v_tree[l]) + ((int64_t)b * a.R + src) * row_bytes;
+  char* kd = static_cast<char*>(a.cache_k[l]) + ((int64_t)page * 16 + (pos & 15)) * row_bytes;
+  char* vd = static_cast<char*>(a.cache_v[l]) + ((int64_t)page * 16 + (pos & 15)) * row_bytes;
+  for (int64_t c = threadIdx.x; c < row_bytes / 16; c += 256) {
+    *reinterpret_cast<uint4*>(kd + 16 * c) = *reinterpret_cast<const uint4*>(ks + 16 * c);
+    *reinterpret_cast<uint4*>(vd + 16 * c) = *reinterpret_cast<const uint4*>(vs + 16 * c);
+  }
+}
+
 struct TopkPlan {
   VocabPlan pl;
   size_t cand_v, cand_i, part;   // byte offsets in the workspace
@@ -604,6 +633,12 @@ hipError_t launch_tree_build(bool bf16, int B, int n_pos, int V, const void* dl,
   TreeP p{n_pos, K, budget, (budget + 31) / 32, topk_tok, topk_lp, node_token, node_parent,
           node_depth, node_logp, n_nodes, mask};
   hipLaunchKernelGGL(k_tree_build, dim3(B), dim3(64), tree_lds_bytes(n_pos, K, budget), st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_commit(const CommitArgs& a, hipStream_t st) {
+  const int64_t grid = (int64_t)a.n_layers * a.B * (a.max_depth + 1);
+  hipLaunchKernelGGL(k_tree_commit, dim3((unsigned)grid), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

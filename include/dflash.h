@@ -6,6 +6,8 @@
  *   dflash_block_attention     non-causal block attention over [ctx; block]
  *   dflash_tree_build          DDTree: top-K per position, best-first tree, ancestor mask
  *   dflash_tree_verify_greedy  DDTree: target argmax per node and the greedy walk
+ *   dflash_tree_attention      DDTree: the target's attention under the ancestor-only mask
+ *   dflash_tree_commit_kv      DDTree: the accepted path's KV into the paged cache
  *   dflash_verify_greedy       greedy acceptance over the full vocabulary
  *   dflash_verify_sample       lossless rejection sampling over the full vocabulary
  *   dflash_gate                DLoop block-confidence gate
@@ -384,6 +386,70 @@ dflash_status dflash_tree_verify_greedy(
     int max_depth, int32_t* accept_len, int32_t* bonus, int32_t* accepted_nodes,
     int32_t* commit_lens, const int32_t* prefix_lens, int32_t* new_seq_lens,
     dflash_dtype dtype, void* ws, size_t ws_bytes, dflash_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * DDTree: the target's attention over the flattened tree, and the KV commit
+ * of the accepted path.
+ *
+ * dflash_tree_attention -- [Spec tutorial], section 6.4: the target verifies
+ * the whole tree in one pass.  The rows of request b are the root (row 0, the
+ * last committed token, not yet in the cache) and the nodes (row 1 + j, node j
+ * of dflash_tree_build).  Every row attends to the committed context (cache
+ * positions [0, ctx_lens[b])) and to the tree rows on its own root path: row 0
+ * sees itself; row 1 + j sees row 0 and the rows 1 + y of every node y whose
+ * bit is set in node j's ancestor row (node j itself and its ancestors) --
+ * never siblings or cousins, as if each path were prefilled alone.  A node
+ * row whose ancestor row is all zero (past the tree) sees the context and the
+ * root.  Key tiles with no visible key are skipped (the sparse blocks of the
+ * mask).
+ *
+ * q            [B, n_rows, Hq, D]     k_tree, v_tree  [B, n_rows, Hkv, D]
+ *              (position-encoded by the caller: a node's position is the
+ *              context length plus its depth)
+ * cache_k/v, num_pages, page_size, block_table [B, max_pages_per_seq],
+ *   ctx_lens   as dflash_block_attention (one table row per request)
+ * ancestor_mask [B, n_rows - 1, (n_rows + 30) / 32] uint32, as
+ *              dflash_tree_build writes it for budget = n_rows - 1
+ *              (NULL allowed only when n_rows = 1)
+ * 1 <= n_rows <= 1025; head_dim 64 or 128; bf16 pointers 16-byte aligned
+ * out, lse_out, scale, dtype, out_dtype, ws: as dflash_block_attention, with
+ *   the workspace sized by dflash_tree_attention_workspace_size
+ * In band: a page-table entry outside [0, num_pages) or ctx_len outside
+ *   [0, 16 * max_pages_per_seq] makes that request's outputs NaN.
+ *
+ * dflash_tree_commit_kv -- [Spec tutorial], section 6.6: after the walk only
+ * the accepted path's KV joins the cache; rejected rows are never stored.
+ * For every layer l and request b with accept_len[b] >= 0, the rows
+ *   t = 0 (the root) and t = 1 .. min(accept_len[b], max_depth) (tree row
+ *   1 + accepted_nodes[b, t - 1])
+ * of k_tree[l] / v_tree[l] ([B, n_rows, Hkv, D]) are copied to the cache slot
+ * of logical position prefix_lens[b] + t (block_table [B, max_pages_per_seq],
+ * 16-token pages of caches[l]).  A row on an unmapped or out-of-range page,
+ * or whose node index is outside [0, n_rows - 1), is skipped.  accepted_nodes,
+ * accept_len and the prefix are dflash_tree_verify_greedy's accepted_nodes,
+ * accept_len and prefix_lens (the commit length is accept_len + 1).
+ * n_layers <= 64; Hkv * D * element size a multiple of 16; every pointer
+ * 16-byte aligned.  No workspace.
+ * ------------------------------------------------------------------------- */
+size_t dflash_tree_attention_workspace_size(int B, int n_rows, int n_q_heads, int n_kv_heads,
+                                            int head_dim, int max_pages_per_seq,
+                                            dflash_dtype dtype);
+
+dflash_status dflash_tree_attention(
+    int B, int n_rows, int n_q_heads, int n_kv_heads, int head_dim,
+    const void* q, const void* k_tree, const void* v_tree,
+    const void* cache_k, const void* cache_v, int num_pages, int page_size,
+    const int32_t* block_table, int max_pages_per_seq, const int32_t* ctx_lens,
+    const uint32_t* ancestor_mask, float scale, void* out, float* lse_out,
+    dflash_dtype dtype, dflash_dtype out_dtype, void* ws, size_t ws_bytes,
+    dflash_stream_t stream);
+
+dflash_status dflash_tree_commit_kv(
+    int B, int n_rows, int n_layers, int n_kv_heads, int head_dim,
+    const void* const* k_tree, const void* const* v_tree, const dflash_kv_layer* caches,
+    const int32_t* block_table, int max_pages_per_seq,
+    const int32_t* accepted_nodes, int max_depth, const int32_t* accept_len,
+    const int32_t* prefix_lens, dflash_dtype dtype, dflash_stream_t stream);
 
 #ifdef __cplusplus
 }

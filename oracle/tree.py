@@ -157,7 +157,7 @@ def _root_path(parent, x):
 
 
 def tree_attention(q, k_tree, v_tree, cache_k, cache_v, block_table, ctx_lens, node_parent,
-                   n_nodes, dtype, scale=None):
+                   n_nodes, dtype, scale=None, rows=None):
     """The target's attention over the flattened tree ([Spec-decoding tutorial] 6.4).
 
     Rows of a request: row 0 is the root (the last committed token, not yet in
@@ -169,7 +169,8 @@ def tree_attention(q, k_tree, v_tree, cache_k, cache_v, block_table, ctx_lens, n
 
     q [B, R, Hq, D], k_tree / v_tree [B, R, Hkv, D] with R = 1 + budget;
     node_parent [B, budget] (-1: a child of the root).  Returns
-    (out [B, R, Hq, D], lse [B, Hq, R])."""
+    (out [B, R, Hq, D], lse [B, Hq, R]); with ``rows`` (a list of row
+    indices) only those rows are computed, the others are left zero."""
     q, kt, vt = widen(q, dtype), widen(k_tree, dtype), widen(v_tree, dtype)
     ck, cv = widen(cache_k, dtype), widen(cache_v, dtype)
     B, R, Hq, D = q.shape
@@ -185,10 +186,10 @@ def tree_attention(q, k_tree, v_tree, cache_k, cache_v, block_table, ctx_lens, n
         pages = block_table[b, pos // 16]
         ctx_k, ctx_v = ck[pages, pos % 16], cv[pages, pos % 16]
         n = int(n_nodes[b])
-        for r in range(R):
-            rows = [0] if r == 0 or r - 1 >= n else [0] + [1 + y for y in _root_path(node_parent[b], r - 1)]
-            keys = np.concatenate([ctx_k, kt[b, rows]], axis=0)
-            vals = np.concatenate([ctx_v, vt[b, rows]], axis=0)
+        for r in (range(R) if rows is None else rows):
+            seen = [0] if r == 0 or r - 1 >= n else [0] + [1 + y for y in _root_path(node_parent[b], r - 1)]
+            keys = np.concatenate([ctx_k, kt[b, seen]], axis=0)
+            vals = np.concatenate([ctx_v, vt[b, seen]], axis=0)
             for h in range(Hq):
                 s = scale * (keys[:, h // G, :] @ q[b, r, h])
                 m = s.max()

@@ -232,3 +232,40 @@ def test_tree_zero_batch_is_a_noop(lib):
                                  None, None, None, dfl.BF16, None, 0, None) == dfl.OK
     assert lib.dflash_tree_verify_greedy(0, 64, 100, None, 100, None, None, None, 8, None, None,
                                          None, None, None, None, dfl.BF16, None, 0, None) == dfl.OK
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(R=0), dfl.E_ARG), (dict(R=1026), dfl.E_UNSUPPORTED), (dict(D=96), dfl.E_UNSUPPORTED),
+    (dict(Hq=30), dfl.E_ARG), (dict(mask=None), dfl.E_ARG), (dict(q=None), dfl.E_ARG),
+    (dict(q=FAKE + 2), dfl.E_UNSUPPORTED), (dict(ps=32), dfl.E_UNSUPPORTED),
+    (dict(nws=0, B=1), dfl.E_WORKSPACE), (dict(dt=dfl.F32, odt=dfl.BF16), dfl.E_UNSUPPORTED),
+    (dict(scale=-1.0), dfl.E_ARG),
+])
+def test_tree_attention_argument_errors(lib, kw, code):
+    a = dict(B=4, R=513, Hq=32, Hkv=8, D=128, q=FAKE, ps=16, scale=0.0, nws=1 << 28,
+             dt=dfl.BF16, odt=dfl.BF16, mask=FAKE)
+    a.update(kw)
+    s = lib.dflash_tree_attention(a["B"], a["R"], a["Hq"], a["Hkv"], a["D"], a["q"], FAKE, FAKE,
+                                  FAKE, FAKE, 10, a["ps"], FAKE, 64, FAKE, a["mask"], a["scale"],
+                                  FAKE, None, a["dt"], a["odt"], WS, a["nws"], None)
+    assert s == code
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(L=0), dfl.E_ARG), (dict(L=65), dfl.E_UNSUPPORTED), (dict(md=0), dfl.E_ARG),
+    (dict(acc=None), dfl.E_ARG), (dict(ps=32), dfl.E_UNSUPPORTED), (dict(kt=FAKE + 4), dfl.E_UNSUPPORTED),
+    (dict(kt=0), dfl.E_ARG), (dict(D=3, Hkv=1), dfl.E_UNSUPPORTED),
+])
+def test_tree_commit_argument_errors(lib, kw, code):
+    a = dict(L=1, md=8, acc=FAKE, ps=16, kt=FAKE, D=128, Hkv=8)
+    a.update(kw)
+    n = max(a["L"], 1)
+    kt = (ctypes.c_void_p * n)(*([a["kt"] or None] * n))
+    vt = (ctypes.c_void_p * n)(*([FAKE] * n))
+    caches = (dfl.KVLayer * n)(*([dfl.KVLayer(FAKE, FAKE, 8, a["ps"])] * n))
+    s = lib.dflash_tree_commit_kv(2, 9, a["L"], a["Hkv"], a["D"], ctypes.cast(kt, dfl.PP),
+                                  ctypes.cast(vt, dfl.PP), caches, FAKE, 4, FAKE, a["md"], a["acc"],
+                                  FAKE, dfl.BF16, None)
+    assert s == code

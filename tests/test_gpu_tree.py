@@ -317,3 +317,167 @@ def test_build_then_verify_on_device():
     assert keep, "no request's tree came out exact"
     sub = {k: v[keep] for k, v in rv.items()}
     _walk_check(sub, [trees[b] for b in keep], tl[keep], dtype, n_pos)
+
+
+# ------------------------------------------------------------ tree attention
+
+def _pack_mask(m, budget):
+    """bool [n, n] ancestor matrix of an n-node tree -> int32 bit rows
+    [budget, ceil(budget / 32)] (bit j of row i: node j is i or an ancestor),
+    rows past n all zero: the layout dflash_tree_build writes."""
+    W = (budget + 31) // 32
+    out = np.zeros((budget, W), dtype=np.uint32)
+    n = m.shape[0]
+    for i in range(n):
+        for j in np.flatnonzero(m[i]):
+            out[i, j >> 5] |= np.uint32(1) << np.uint32(j & 31)
+    return out.view(np.int32)
+
+
+def _oracle_trees(seed, B, n_pos, K, budget, V=64, peaked=3.0):
+    c = synth.tree_case(seed, dtype="f32", B=B, n_pos=n_pos, V=V, peaked=peaked)
+    tok, lp = oracle.topk_logprobs(c.draft_logits, "f32", K)
+    trees = [oracle.build_tree(tok[b], lp[b], budget) for b in range(B)]
+    par = np.full((B, budget), -2, dtype=np.int64)
+    nn = np.zeros(B, dtype=np.int64)
+    masks = np.zeros((B, budget, (budget + 31) // 32), dtype=np.int32)
+    for b, t in enumerate(trees):
+        n = len(t.token)
+        nn[b] = n
+        par[b, :n] = t.parent
+        masks[b] = _pack_mask(oracle.ancestor_mask(t.parent), budget)
+    return trees, par, nn, masks
+
+
+def _tree_attn_check(c, par, nn, masks, out, lse, sel=None, rows=None):
+    import torch
+    from tests.test_gpu_attention import _subset
+    if sel is not None:
+        c = _subset(c, sel)
+        out, lse = out[sel], lse[sel]
+        par, nn = par[sel], nn[sel]
+    o_ref, l_ref = oracle.tree_attention(c.q, c.k_blk, c.v_blk, c.cache_k, c.cache_v,
+                                         c.block_table, c.ctx_lens, par, nn, c.dtype, rows=rows)
+    o_k, l_k = down(out), down(lse)
+    if rows is not None:
+        o_ref, o_k = o_ref[:, rows], o_k[:, rows]
+        l_ref, l_k = l_ref[:, :, rows], l_k[:, :, rows]
+    rms = np.sqrt(np.mean(o_ref ** 2))
+    diff = np.abs(o_k - o_ref)
+    if out.dtype == torch.bfloat16:
+        diff = np.maximum(diff - 2.0 ** -8 * np.abs(o_ref), 0.0)   # storage rounding
+    e = float(diff.max() / rms)
+    el = float(np.abs(l_k - l_ref).max() / np.sqrt(np.mean(l_ref ** 2)))
+    log(f"  tree attention out({out.dtype}) err {e:.2e}, lse err {el:.2e}")
+    tol = {"bf16": 2e-2, "f32": 1e-4}[c.dtype]
+    assert e <= tol and el <= tol
+
+
+def _tree_attn_run(c, masks, out_dtype=None):
+    import torch
+    kind = c.dtype
+    q = up(c.q, kind)
+    lse = torch.empty((c.B, c.n_q_heads, c.k), dtype=torch.float32, device=q.device)
+    od = {"f32": torch.float32, "bf16": torch.bfloat16, None: None}[out_dtype]
+    return dfl.tree_attention(q, up(c.k_blk, kind), up(c.v_blk, kind), up(c.cache_k, kind),
+                              up(c.cache_v, kind), up(c.block_table, "i32"), up(c.ctx_lens, "i32"),
+                              up(masks, "i32"), lse=lse, out_dtype=od)
+
+
+@pytest.mark.parametrize("dtype,B,n_pos,K,budget,Hq,Hkv,D,ctx,out_dtype,seed", [
+    ("f32", 2, 5, 3, 20, 4, 2, 64, [37, 0], None, 3301),          # tiny fp32
+    ("bf16", 2, 6, 4, 63, 32, 8, 128, [100, 1000], "f32", 3302),  # 64 tree rows
+    ("bf16", 2, 6, 4, 63, 32, 8, 128, [100, 1000], "bf16", 3302),
+    ("bf16", 1, 15, 8, 512, 32, 8, 128, [2048], "f32", 3303),     # the page's budget
+    ("bf16", 2, 2, 3, 100, 16, 4, 64, [333, 17], "f32", 3304),    # 12-node trees in 100 rows
+    ("bf16", 1, 64, 2, 1024, 8, 8, 64, [64], "f32", 3305),        # largest budget, deepest block
+])
+def test_tree_attention_parity(dtype, B, n_pos, K, budget, Hq, Hkv, D, ctx, out_dtype, seed):
+    log(f"tree_attention dtype={dtype} B={B} budget={budget} heads={Hq}/{Hkv}x{D} ctx={ctx}")
+    trees, par, nn, masks = _oracle_trees(seed, B, n_pos, K, budget)
+    c = synth.attention_case(seed + 1, dtype=dtype, B=B, k=budget + 1, n_q_heads=Hq,
+                             n_kv_heads=Hkv, head_dim=D, ctx_lens=ctx)
+    out, lse = _tree_attn_run(c, masks, out_dtype)
+    _tree_attn_check(c, par, nn, masks, out, lse)
+
+
+def test_tree_attention_full_size_sampled():
+    """64 requests, ctx 8192, 32 Q / 8 KV heads x 128, budget 512 (the
+    bench's launch): sampled rows of sampled requests against the oracle,
+    every output finite."""
+    B, C, budget = 64, 8192, 512
+    log(f"tree_attention full B={B} ctx={C} budget={budget}")
+    trees, par, nn, masks = _oracle_trees(3311, B, 15, 8, budget)
+    c = synth.attention_case(3312, dtype="bf16", B=B, k=budget + 1, n_q_heads=32, n_kv_heads=8,
+                             head_dim=128, ctx_lens=[C] * B)
+    out, lse = _tree_attn_run(c, masks, "bf16")
+    assert np.isfinite(down(out)).all()
+    rows = [0, 1, 2, 3, 64, 200, 389, 511, 512]
+    _tree_attn_check(c, par, nn, masks, out, lse, sel=[0, 37, 63], rows=rows)
+
+
+def test_tree_attention_of_a_chain_equals_causal_block_attention_on_device():
+    """The kernel's two mask modes agree where the page's definitions do: a
+    one-path tree of 31 nodes is the causal block of 32 rows."""
+    import torch
+    R = 32
+    c = synth.attention_case(3321, dtype="bf16", B=3, k=R, n_q_heads=32, n_kv_heads=8,
+                             head_dim=128, ctx_lens=[500, 0, 77])
+    par = np.arange(R - 1) - 1
+    m = _pack_mask(oracle.ancestor_mask(par), R - 1)
+    masks = np.stack([m] * 3)
+    out_t, _ = _tree_attn_run(c, masks, "f32")
+    out_c, _ = dfl.block_attention(up(c.q, "bf16"), up(c.k_blk, "bf16"), up(c.v_blk, "bf16"),
+                                   up(c.cache_k, "bf16"), up(c.cache_v, "bf16"),
+                                   up(c.block_table, "i32"), up(c.ctx_lens, "i32"),
+                                   out_dtype=torch.float32, causal=True)
+    np.testing.assert_array_equal(down(out_t), down(out_c))
+
+
+# ------------------------------------------------------------ KV recycling
+
+@pytest.mark.parametrize("dtype,seed", [("bf16", 3401), ("f32", 3402)])
+def test_tree_commit_kv_parity(dtype, seed):
+    """The accepted paths of oracle walks (lengths 0 .. depth, one in-band
+    error) committed into three layers' caches: every slot bit-exact against
+    the oracle's commit, including the untouched sentinel slots and a request
+    whose next page is unmapped."""
+    import torch
+    B, n_pos, K, budget, Hkv, D, Ld = 5, 6, 3, 40, 2, 64, 3
+    trees, tl = _walk_case(seed, "f32", B, n_pos, 500, K, budget, stop_at=[0, 1, 3, 6, 6])
+    walks = [oracle.walk_greedy(t.token, t.parent, _LazyPredict(tl[b], "f32"))
+             for b, t in enumerate(trees)]
+    md = n_pos
+    acc = np.array([w.accept_len for w in walks])
+    acc[4] = -1                                            # the walk's in-band error
+    path = np.full((B, md), -1, dtype=np.int64)
+    for b, w in enumerate(walks):
+        path[b, :len(w.path)] = w.path[:md]
+    rng = np.random.default_rng(seed)
+    prefix = np.array([0, 14, 31, 60, 5])
+    max_pages = 8
+    n_pages = 40
+    bt = rng.permutation(n_pages)[:B * max_pages].reshape(B, max_pages).astype(np.int32)
+    bt[3, 4] = -1                                          # positions 64.. of request 3 unmapped
+    kts, vts, cks, cvs, refs = [], [], [], [], []
+    for l in range(Ld):
+        ktree = synth.attention_case(seed + 10 + l, dtype=dtype, B=B, k=budget + 1, n_q_heads=Hkv,
+                                     n_kv_heads=Hkv, head_dim=D, ctx_lens=[0] * B)
+        sent = np.full((n_pages, 16, Hkv, D), 0x7FA1 if dtype == "bf16" else np.nan,
+                       dtype=np.uint16 if dtype == "bf16" else np.float32)
+        rk, rv = sent.copy(), sent.copy()
+        oracle.commit_tree_kv(ktree.k_blk, ktree.v_blk, path, acc, prefix, rk, rv, bt)
+        refs.append((rk, rv))
+        kts.append(up(ktree.k_blk, dtype))
+        vts.append(up(ktree.v_blk, dtype))
+        cks.append(up(sent, dtype))
+        cvs.append(up(sent, dtype))
+    dfl.tree_commit_kv(kts, vts, cks, cvs, up(bt, "i32"), up(path, "i32"), up(acc, "i32"),
+                       up(prefix, "i32"))
+    from tests.gpu_util import bits
+    for l in range(Ld):
+        want_k = refs[l][0].view(np.uint16 if dtype == "bf16" else np.uint32)
+        want_v = refs[l][1].view(np.uint16 if dtype == "bf16" else np.uint32)
+        np.testing.assert_array_equal(bits(cks[l]), want_k)
+        np.testing.assert_array_equal(bits(cvs[l]), want_v)
+    log(f"  committed rows per request: {[int(a) + 1 if a >= 0 else 0 for a in acc]}")
