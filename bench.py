@@ -77,12 +77,13 @@ def parse():
                     help="also run one 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--breakdown", action="store_true", help="per-part timings to stderr")
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "sample-gate", "prefill", "packed", "tree"],
+                    choices=["decode", "sample-gate", "prefill", "packed", "tree", "tree-attn"],
                     help="decode: the greedy decode step (default); sample-gate: Qwen3-4B-shaped "
                          "stochastic chain verify with DLoop gates; prefill: 4 x 32768-row "
                          "ctx-KV materialisation; packed: training-style packed block mask; "
                          "tree: DDTree build (top-K, best-first tree, ancestor mask) + greedy "
-                         "tree verify")
+                         "tree verify; tree-attn: the target's attention over the flattened tree "
+                         "(ancestor-only mask), one layer")
     ap.add_argument("--topk", type=int, default=8, help="tree: candidates per block position")
     ap.add_argument("--budget", type=int, default=512, help="tree: node budget")
     ap.add_argument("--sigma", type=float, default=1.0, help="sample-gate: draft = target + N(0, sigma)")
@@ -648,6 +649,87 @@ def bench_tree(args):
     return line
 
 
+def bench_tree_attn(args):
+    """The target's attention over the flattened DDTree, one layer
+    (Llama-3.1-8B-shaped target: 32 Q / 8 KV heads x 128): 64 requests, ctx
+    8192, node budget 512 (513 rows: the root and the nodes), the ancestor-only
+    mask of trees built by dflash_tree_build from a confident drafter's rows
+    (15 positions, top-8)."""
+    import numpy as np
+    import torch
+    import block_diffusion_draft_ctx_amd as dfl
+    B, C, N, Hq, Hkv, D = args.batch, args.ctx, args.budget, 32, 8, 128
+    R = N + 1
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(6000)
+    bf = torch.bfloat16
+    # tree shapes from a confident drafter (the vocabulary only sets the shape)
+    dl = torch.randn(B, args.block - 1, 4096, generator=g, device=dev) * 2.0
+    peak = torch.randint(0, 4096, (B, args.block - 1), generator=g, device=dev)
+    dl.scatter_add_(2, peak[..., None], torch.full((B, args.block - 1, 1), 8.0, device=dev))
+    tb = dfl.tree_build(dl.to(bf), args.topk, N)
+    mask = tb["ancestor_mask"]
+    npg = B * C // 16
+    bt = torch.randperm(npg, generator=g, device=dev).to(torch.int32).view(B, C // 16).contiguous()
+    ck = torch.randn(npg, 16, Hkv, D, generator=g, device=dev).to(bf)
+    cv = torch.randn(npg, 16, Hkv, D, generator=g, device=dev).to(bf)
+    q = torch.randn(B, R, Hq, D, generator=g, device=dev).to(bf)
+    kt = torch.randn(B, R, Hkv, D, generator=g, device=dev).to(bf)
+    vt = torch.randn(B, R, Hkv, D, generator=g, device=dev).to(bf)
+    ctx = torch.full((B,), C, dtype=torch.int32, device=dev)
+    out = torch.empty(B, R, Hq, D, dtype=bf, device=dev)
+    ws = torch.empty(max(256, dfl.lib().dflash_tree_attention_workspace_size(B, R, Hq, Hkv, D,
+                                                                             C // 16, dfl.BF16)),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        dfl.tree_attention(q, kt, vt, ck, cv, bt, ctx, mask, out=out, workspace=ws)
+
+    ms = _events_ms(step, args.steps, args.warmup)
+    # keys each row sees: the context, the root, and (node rows) its ancestors
+    # and itself -- the bits of its mask row
+    m = mask.cpu().numpy().view(np.uint32)
+    node_bits = int(np.unpackbits(m.view(np.uint8)).sum())
+    row_keys = B * R * (C + 1) + node_bits
+    flops = 4.0 * Hq * D * row_keys
+    line = _base_line(args, "DDTree tree attention (one target layer), blocks/sec",
+                      round(B / (ms * 1e-3), 1), "blocks/s", ms,
+                      f"the target's attention over the flattened DDTree, one layer: batch {B}, ctx "
+                      f"{C}, node budget {N} ({R} rows: root + nodes), ancestor-only mask of trees "
+                      f"built from 15 drafted positions (top-{args.topk}), 32 Q / 8 KV heads x 128",
+                      batch=B, ctx=C, budget=N, topk=args.topk)
+    line["roofline"] = {"kernel": "tree_attention (k_attn_bf16, tree mask)", "bound": "mfma",
+                        "achieved": round(flops / (ms * 1e-3) / 1e12, 1), "peak": BF16_PEAK / 1e12,
+                        "unit": "TFLOP/s", "frac": round(flops / (ms * 1e-3) / BF16_PEAK, 4),
+                        "traffic": None, "algorithmic_flops": flops,
+                        "avg_launch_us": round(ms * 1e3, 2),
+                        "mean_tree_keys_per_node_row": round(node_bits / (B * N), 2)}
+    if not args.no_cpu_baseline:
+        import time
+        import oracle
+
+        def host(t):
+            t = t.detach().cpu().contiguous()
+            return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == bf else t.numpy()
+
+        # one request, all its rows, its own pages compacted
+        pages = bt[0].long()
+        par = host(tb["node_parent"][:1]).astype(np.int64)
+        nn = host(tb["n_nodes"][:1])
+        args_h = (host(q[:1]), host(kt[:1]), host(vt[:1]), host(ck[pages]), host(cv[pages]),
+                  np.arange(C // 16, dtype=np.int32)[None], np.array([C], dtype=np.int32))
+        rows = list(range(0, R, 2))
+        t0 = time.perf_counter()
+        oracle.tree_attention(*args_h, par, nn, "bf16", rows=rows)
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {
+            "value": round(len(rows) / R / dt, 5), "unit": "blocks/s", "cores": 1, "kind": "oracle",
+            "sample": f"every 2nd row ({len(rows)} of {R}) of 1 of the {B} requests, all {Hq} "
+                      f"heads at ctx {C}, scaled to a whole request; {dt:.1f} s of CPU work"}
+    return line
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -661,7 +743,8 @@ def main():
         sys.exit(1)
     if args.workload != "decode":
         fn = {"sample-gate": bench_sample_gate, "prefill": bench_prefill,
-              "packed": bench_packed, "tree": bench_tree}[args.workload]
+              "packed": bench_packed, "tree": bench_tree,
+              "tree-attn": bench_tree_attn}[args.workload]
         print(json.dumps(fn(args)), flush=True)
         return
     st = Step(args.batch, args.ctx, args.block, args.vocab, args.layers, causal=args.causal,
