@@ -9,7 +9,8 @@ The pages this follows (cited by short title and section throughout):
 
 * [DFlash overview] "DFlash 块扩散解码：以并行扩散替代自回归草稿，实现无损 6 倍推理加速"
   (pinghaoyang.com.cn/aigc/posts/dflash/) -- sections "块扩散", "KV 注入",
-  "训练策略 / 随机锚点采样", "验证流程", "关键伪代码".
+  "训练策略 / 随机锚点采样", "验证流程", "关键伪代码", and "草稿模型架构" (the
+  drafter's decoder layers and shared head, followed by ``draft.py``).
 * [SGLang DFlash] "详解SGlang 最新DFlash投机解码算法的工程实现、overlap策略和改进点"
   (10100.com/article/149138197) -- sections 3 (decode) and 4.1 (KV materialisation).
 * [Spec-decoding tutorial] "让大模型快 8 倍：从投机解码到 DDTree 的完整原理"
@@ -38,11 +39,13 @@ from .verify import (verify_greedy, verify_sample, gate, row_log_softmax, Greedy
                      SampleResult, GateResult)
 from .tree import (topk_logprobs, build_tree, ancestor_mask, walk_greedy, target_argmax, Tree,
                    TreeWalk, tree_attention, commit_tree_kv)
+from .draft import rms_norm, silu, embed, draft_layer, draft_head
 
 __all__ = [
     "widen", "round_to_bf16", "round_to_f32", "fuse_hiddens", "project_kv", "materialize",
     "paged_write", "gather_paged", "k_norm", "rope_half_split", "row_positions", "block_attention", "block_attention_masked",
     "verify_greedy", "verify_sample", "gate", "row_log_softmax", "GreedyResult",
     "SampleResult", "GateResult", "topk_logprobs", "build_tree", "ancestor_mask", "walk_greedy",
-    "target_argmax", "Tree", "TreeWalk", "tree_attention", "commit_tree_kv",
+    "target_argmax", "Tree", "TreeWalk", "tree_attention", "commit_tree_kv", "rms_norm", "silu",
+    "embed", "draft_layer", "draft_head",
 ]
