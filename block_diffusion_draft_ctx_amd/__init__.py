@@ -26,7 +26,8 @@ EXPORTS = (
     "dflash_gate_workspace_size", "dflash_gate",
     "dflash_tree_workspace_size", "dflash_tree_verify_workspace_size", "dflash_tree_build",
     "dflash_tree_verify_greedy", "dflash_tree_attention_workspace_size", "dflash_tree_attention",
-    "dflash_tree_commit_kv",
+    "dflash_tree_commit_kv", "dflash_draft_layer_workspace_size", "dflash_draft_layer",
+    "dflash_draft_head_workspace_size", "dflash_draft_head", "dflash_embed",
 )
 
 
@@ -38,6 +39,11 @@ class KVLayer(ctypes.Structure):
 class KEpilogue(ctypes.Structure):
     _fields_ = [("k_norm_weight", ctypes.POINTER(ctypes.c_void_p)), ("k_norm_eps", ctypes.c_float),
                 ("rope_theta", ctypes.c_float)]
+
+
+class DraftLayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("ln1", "qkv", "q_norm", "k_norm", "o", "ln2",
+                                                "gate_up", "down")]
 
 
 class DFlashError(RuntimeError):
@@ -100,6 +106,18 @@ def _declare(lib):
     lib.dflash_tree_attention.restype = I32
     lib.dflash_tree_attention.argtypes = [
         I32, I32, I32, I32, I32, P, P, P, P, P, I32, I32, P, I32, P, P, F, P, P, I32, I32, P, SZ, P]
+    lib.dflash_draft_layer_workspace_size.restype = SZ
+    lib.dflash_draft_layer_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32, I32]
+    lib.dflash_draft_layer.restype = I32
+    lib.dflash_draft_layer.argtypes = [
+        I32, I32, I32, I32, I32, I32, I32, P, ctypes.POINTER(DraftLayerWeights), F, F, P, P, I32, I32,
+        P, I32, P, I32, I32, P, SZ, P]
+    lib.dflash_draft_head_workspace_size.restype = SZ
+    lib.dflash_draft_head_workspace_size.argtypes = [I32, I32, I32, I32]
+    lib.dflash_draft_head.restype = I32
+    lib.dflash_draft_head.argtypes = [I32, I32, I32, P, P, P, F, P, I32, P, SZ, P]
+    lib.dflash_embed.restype = I32
+    lib.dflash_embed.argtypes = [I32, I32, I32, P, P, P, I32, P]
     lib.dflash_tree_commit_kv.restype = I32
     lib.dflash_tree_commit_kv.argtypes = [
         I32, I32, I32, I32, I32, PP, PP, ctypes.POINTER(KVLayer), P, I32, P, I32, P, P, I32, P]
@@ -551,3 +569,75 @@ def tree_commit_kv(k_tree: Sequence, v_tree: Sequence, cache_k: Sequence, cache_
         _ptr(accepted_nodes), accepted_nodes.shape[1], _ptr(accept_len), _ptr(prefix_lens), dt,
         _stream(stream))
     _check(s, "dflash_tree_commit_kv")
+
+
+_DRAFT_KEYS = ("ln1", "qkv", "q_norm", "k_norm", "o", "ln2", "gate_up", "down")
+
+
+def draft_layer(x, weights, cache_k, cache_v, block_table, ctx_lens, k, n_q_heads, eps=1e-6,
+                rope_theta=1e6, causal=False, workspace=None, stream=None):
+    """dflash_draft_layer: one drafter layer on x [B*k, d] (updated in place).
+    weights: dict of device tensors ln1 [d], qkv [(Hq + 2 Hkv) D, d], q_norm /
+    k_norm [D] or None, o [d, Hq D], ln2 [d], gate_up [2 I, d], down [d, I].
+    cache_k / cache_v [num_pages, 16, Hkv, D] (this layer's context),
+    block_table [B, max_pages], ctx_lens [B].  Returns x."""
+    L = lib()
+    M, d = x.shape
+    B = M // k
+    Hkv, D = cache_k.shape[2], cache_k.shape[3]
+    I = weights["down"].shape[1]
+    dt = _dtype_code(x)
+    _dev(x, "x")
+    for n in _DRAFT_KEYS:
+        if weights.get(n) is not None:
+            _dev(weights[n], n)
+    _i32(block_table, "block_table")
+    _i32(ctx_lens, "ctx_lens")
+    wst = DraftLayerWeights(*[_ptr(weights.get(n)) for n in _DRAFT_KEYS])
+    need = L.dflash_draft_layer_workspace_size(B, k, d, n_q_heads, Hkv, D, I, block_table.shape[1], dt)
+    ws, nws = _workspace(need, x.device, workspace)
+    s = L.dflash_draft_layer(B, k, d, n_q_heads, Hkv, D, I, _ptr(x), ctypes.byref(wst), float(eps),
+                             float(rope_theta), _ptr(_dev(cache_k, "cache_k")),
+                             _ptr(_dev(cache_v, "cache_v")), cache_k.shape[0], cache_k.shape[1],
+                             _ptr(block_table), block_table.shape[1], _ptr(ctx_lens),
+                             MASK_CAUSAL if causal else MASK_BIDIRECTIONAL, dt, _ptr(ws), nws,
+                             _stream(stream))
+    _check(s, "dflash_draft_layer")
+    return x
+
+
+def draft_head(x, norm_weight, lm_head, eps=1e-6, out=None, workspace=None, stream=None):
+    """dflash_draft_head: logits [M, V] = rmsnorm(x) * norm_weight . lm_head^T."""
+    torch = _torch()
+    L = lib()
+    M, d = x.shape
+    V = lm_head.shape[0]
+    dt = _dtype_code(x)
+    for n, t in (("x", x), ("norm_weight", norm_weight), ("lm_head", lm_head)):
+        _dev(t, n)
+    if out is None:
+        out = torch.empty((M, V), dtype=x.dtype, device=x.device)
+    _dev(out, "out")
+    need = L.dflash_draft_head_workspace_size(M, d, V, dt)
+    ws, nws = _workspace(need, x.device, workspace)
+    s = L.dflash_draft_head(M, d, V, _ptr(x), _ptr(norm_weight), _ptr(lm_head), float(eps),
+                            _ptr(out), dt, _ptr(ws), nws, _stream(stream))
+    _check(s, "dflash_draft_head")
+    return out
+
+
+def embed(table, tokens, out=None, stream=None):
+    """dflash_embed: rows of table [V, d] for tokens [M] (or [B, k]) -> [M, d]."""
+    torch = _torch()
+    L = lib()
+    V, d = table.shape
+    _dev(table, "table")
+    _i32(tokens, "tokens")
+    M = tokens.numel()
+    if out is None:
+        out = torch.empty((M, d), dtype=table.dtype, device=table.device)
+    _dev(out, "out")
+    s = L.dflash_embed(M, d, V, _ptr(table), _ptr(tokens), _ptr(out), _dtype_code(table),
+                       _stream(stream))
+    _check(s, "dflash_embed")
+    return out

@@ -394,4 +394,97 @@ dflash_status dflash_tree_commit_kv(int B, int n_rows, int n_layers, int n_kv_he
   return hip_status(launch_tree_commit(a, static_cast<hipStream_t>(stream)));
 }
 
+// ------------------------------------------------------------------ drafter
+static dflash_status draft_shape_check(int B, int k, int d, int Hq, int Hkv, int D, int I,
+                                       dflash_dtype dtype) {
+  if (bad_dtype(dtype)) return DFLASH_E_ARG;
+  if (B < 0 || k < 1 || d < 8 || Hq < 1 || Hkv < 1 || D < 1 || I < 8) return DFLASH_E_ARG;
+  if (Hq % Hkv) return DFLASH_E_ARG;
+  if (D != 64 && D != 128) return DFLASH_E_UNSUPPORTED;
+  if (k > 64 || (Hq / Hkv) * k > 256) return DFLASH_E_UNSUPPORTED;
+  if (d % 128 || ((Hq + 2 * Hkv) * D) % 128 || (Hq * D) % 128 || I % 128) return DFLASH_E_UNSUPPORTED;
+  return DFLASH_OK;
+}
+
+size_t dflash_draft_layer_workspace_size(int B, int k, int d_model, int n_q_heads, int n_kv_heads,
+                                         int head_dim, int d_ff, int max_pages_per_seq,
+                                         dflash_dtype dtype) {
+  if (B <= 0 || max_pages_per_seq < 1 ||
+      draft_shape_check(B, k, d_model, n_q_heads, n_kv_heads, head_dim, d_ff, dtype))
+    return 0;
+  DraftArgs a{};
+  a.B = B; a.k = k; a.d = d_model; a.Hq = n_q_heads; a.Hkv = n_kv_heads; a.D = head_dim;
+  a.I = d_ff; a.bf16 = dtype == DFLASH_BF16; a.max_pages = max_pages_per_seq;
+  return draft_layer_ws_bytes(a);
+}
+
+dflash_status dflash_draft_layer(int B, int k, int d_model, int n_q_heads, int n_kv_heads,
+                                 int head_dim, int d_ff, void* x,
+                                 const dflash_draft_layer_weights* w, float eps, float rope_theta,
+                                 const void* cache_k, const void* cache_v, int num_pages,
+                                 int page_size, const int32_t* block_table, int max_pages_per_seq,
+                                 const int32_t* ctx_lens, dflash_block_mask block_mask,
+                                 dflash_dtype dtype, void* ws, size_t ws_bytes,
+                                 dflash_stream_t stream) {
+  if (dflash_status s = draft_shape_check(B, k, d_model, n_q_heads, n_kv_heads, head_dim, d_ff, dtype))
+    return s;
+  if (!(eps >= 0.f) || eps == __builtin_huge_valf()) return DFLASH_E_ARG;
+  if (!(rope_theta == 0.f || (rope_theta > 1.f && rope_theta < __builtin_huge_valf())))
+    return DFLASH_E_ARG;
+  if (block_mask != DFLASH_MASK_BIDIRECTIONAL && block_mask != DFLASH_MASK_CAUSAL) return DFLASH_E_ARG;
+  if (page_size != 16) return DFLASH_E_UNSUPPORTED;
+  if (B == 0) return DFLASH_OK;
+  if (!x || !w || !w->ln1 || !w->qkv || !w->o || !w->ln2 || !w->gate_up || !w->down || !cache_k ||
+      !cache_v || !block_table || !ctx_lens || num_pages < 1 || max_pages_per_seq < 1)
+    return DFLASH_E_ARG;
+  const void* ptrs[] = {x, w->ln1, w->qkv, w->q_norm, w->k_norm, w->o, w->ln2, w->gate_up,
+                        w->down, cache_k, cache_v};
+  for (const void* q : ptrs)
+    if (q && !al16(q)) return DFLASH_E_UNSUPPORTED;
+  DraftArgs a{};
+  a.B = B; a.k = k; a.d = d_model; a.Hq = n_q_heads; a.Hkv = n_kv_heads; a.D = head_dim;
+  a.I = d_ff; a.bf16 = dtype == DFLASH_BF16;
+  a.x = x; a.ln1 = w->ln1; a.w_qkv = w->qkv; a.q_norm = w->q_norm; a.k_norm = w->k_norm;
+  a.w_o = w->o; a.ln2 = w->ln2; a.w_gate_up = w->gate_up; a.w_down = w->down;
+  a.eps = eps; a.rope_theta = rope_theta;
+  a.cache_k = cache_k; a.cache_v = cache_v; a.num_pages = num_pages;
+  a.block_table = block_table; a.max_pages = max_pages_per_seq; a.ctx_lens = ctx_lens;
+  a.causal = block_mask == DFLASH_MASK_CAUSAL;
+  if (dflash_status s = check_ws(ws, ws_bytes, draft_layer_ws_bytes(a))) return s;
+  return hip_status(launch_draft_layer(a, ws, static_cast<hipStream_t>(stream)));
+}
+
+size_t dflash_draft_head_workspace_size(int M, int d_model, int V, dflash_dtype dtype) {
+  if (M <= 0 || d_model < 8 || V < 1 || bad_dtype(dtype)) return 0;
+  return draft_head_ws_bytes(M, d_model, V, dtype == DFLASH_BF16);
+}
+
+dflash_status dflash_draft_head(int M, int d_model, int V, const void* x, const void* norm_weight,
+                                const void* lm_head, float eps, void* logits, dflash_dtype dtype,
+                                void* ws, size_t ws_bytes, dflash_stream_t stream) {
+  if (bad_dtype(dtype)) return DFLASH_E_ARG;
+  if (M < 0 || d_model < 8 || V < 1) return DFLASH_E_ARG;
+  if (d_model % 128 || V % 128) return DFLASH_E_UNSUPPORTED;
+  if (!(eps >= 0.f) || eps == __builtin_huge_valf()) return DFLASH_E_ARG;
+  if (M == 0) return DFLASH_OK;
+  if (!x || !norm_weight || !lm_head || !logits) return DFLASH_E_ARG;
+  if (!(al16(x) && al16(norm_weight) && al16(lm_head) && al16(logits))) return DFLASH_E_UNSUPPORTED;
+  if (dflash_status s = check_ws(ws, ws_bytes, draft_head_ws_bytes(M, d_model, V, dtype == DFLASH_BF16)))
+    return s;
+  return hip_status(launch_draft_head(dtype == DFLASH_BF16, M, d_model, V, x, norm_weight, lm_head,
+                                      eps, logits, ws, static_cast<hipStream_t>(stream)));
+}
+
+dflash_status dflash_embed(int M, int d_model, int V, const void* table, const int32_t* tokens,
+                           void* out, dflash_dtype dtype, dflash_stream_t stream) {
+  if (bad_dtype(dtype)) return DFLASH_E_ARG;
+  if (M < 0 || d_model < 8 || V < 1) return DFLASH_E_ARG;
+  if (d_model % 8) return DFLASH_E_UNSUPPORTED;
+  if (M == 0) return DFLASH_OK;
+  if (!table || !tokens || !out) return DFLASH_E_ARG;
+  if (!(al16(table) && al16(out))) return DFLASH_E_UNSUPPORTED;
+  return hip_status(launch_embed(dtype == DFLASH_BF16, M, d_model, V, table, tokens, out,
+                                 static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -48,6 +48,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #ifndef DFLASH_ATTN_NT
 #define DFLASH_ATTN_NT 1
 #endif
+#ifndef DFLASH_ATTN_WIDE
+#define DFLASH_ATTN_WIDE 0     // 256-row workgroups (16 wavefronts: they spill at 128 VGPRs)
+#endif
 constexpr int kKT = DFLASH_ATTN_KT;  // keys per tile
 constexpr int kMaxSplitPages = 1024; // pages one split may span (16384 keys)
 
@@ -125,10 +128,26 @@ void k_attn_bf16(AttnP p) {
   __shared__ __align__(16) uint16_t smem[2 * STAGE];   // two stages
   __shared__ int pages[kMaxSplitPages];
 
-  const int split = blockIdx.x % p.S;
-  const int rc = (blockIdx.x / p.S) % p.RC;           // 32*NQ-row chunk of the query rows
-  const int g = (blockIdx.x / (p.S * p.RC)) % p.Hkv;
-  const int b0 = (blockIdx.x / (p.S * p.RC * p.Hkv)) * NB;   // first request of the workgroup
+  // Workgroups that read the same context -- the row chunks of a (request,
+  // kv-head), and with a shared table every request's workgroups of one
+  // kv-head -- are numbered contiguously, and each XCD takes a contiguous
+  // run of numbers (the hardware deals workgroups to the 8 XCDs round
+  // robin), so a context streams into one XCD's L2 once instead of eight.
+  int id = blockIdx.x;
+  const int nwg = (int)gridDim.x;
+  const bool shares = p.RC > 1 || p.bt_stride == 0;
+  if (shares && (nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
+  const int split = id % p.S;
+  const int rc = (id / p.S) % p.RC;                   // 32*NQ-row chunk of the query rows
+  int g, b0;
+  if (p.bt_stride == 0) {                             // shared table: kv-head major
+    const int nbg = (p.B + NB - 1) / NB;
+    b0 = ((id / (p.S * p.RC)) % nbg) * NB;
+    g = id / (p.S * p.RC * nbg);
+  } else {
+    g = (id / (p.S * p.RC)) % p.Hkv;
+    b0 = (id / (p.S * p.RC * p.Hkv)) * NB;            // first request of the workgroup
+  }
   const int nbv = min(NB, p.B - b0);                   // requests it owns
   const int G = p.Hq / p.Hkv;
   const int k = p.k;
@@ -236,16 +255,23 @@ void k_attn_bf16(AttnP p) {
   auto fetch = [&](int tile, u32x4 (&kr_)[CPT], u32x4 (&vr_)[CPT]) __attribute__((always_inline)) {
     const int pbase = (tile - t0) * (kKT / 16);
     if (tile * kKT + kKT <= C) {     // the whole tile is context (uniform)
+      // a context read by one workgroup streams past the caches; the layouts
+      // whose contexts other workgroups read too (row chunks, shared tables)
+      // keep it in L2
+      if (DFLASH_ATTN_NT && NQ <= 2 && NB == 1) {
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        const int64_t off = (int64_t)pages[pbase + (kc[c] >> 4)] * page_elems + coff[c];
-#if DFLASH_ATTN_NT
-        kr_[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.ck + off));
-        vr_[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.cv + off));
-#else
-        kr_[c] = *reinterpret_cast<const u32x4*>(p.ck + off);
-        vr_[c] = *reinterpret_cast<const u32x4*>(p.cv + off);
-#endif
+        for (int c = 0; c < CPT; ++c) {
+          const int64_t off = (int64_t)pages[pbase + (kc[c] >> 4)] * page_elems + coff[c];
+          kr_[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.ck + off));
+          vr_[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.cv + off));
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+          const int64_t off = (int64_t)pages[pbase + (kc[c] >> 4)] * page_elems + coff[c];
+          kr_[c] = *reinterpret_cast<const u32x4*>(p.ck + off);
+          vr_[c] = *reinterpret_cast<const u32x4*>(p.cv + off);
+        }
       }
     } else {
 #pragma unroll
@@ -634,21 +660,26 @@ void launch_bf16(const AttnArgs& a, AttnP p, hipStream_t st) {
 template <int D>
 void dispatch_nw(const AttnArgs& a, AttnP p, hipStream_t st) {
   const int rows = a.Hq / a.Hkv * a.k;            // query rows per request and kv-head
-  // Requests on one shared table row go two to a workgroup when the pair's
-  // rows fit four 32-row slices: the shared context is then read once per pair.
+  // Requests on one shared table row go two (or four) to a workgroup when
+  // their rows fit its 32-row slices: the shared context is then read once
+  // per group.  Where the work is MFMA-bound the context comes from L2 and
+  // the infinity cache, and rows per workgroup is what divides that traffic.
   if (DFLASH_ATTN_PAIR && a.shared_table && a.mode != kMaskTree && a.B > 1 && 2 * rows <= 128) {
-    if (2 * rows <= 64) launch_bf16<D, 2, 2>(a, p, st);
+    if (DFLASH_ATTN_WIDE && a.B > 2 && 4 * rows <= 256 && 2 * rows > 64) launch_bf16<D, 8, 4>(a, p, st);
+    else if (2 * rows <= 64) launch_bf16<D, 2, 2>(a, p, st);
     else launch_bf16<D, 4, 2>(a, p, st);
     return;
   }
-  // Otherwise one request per workgroup, at most 128 query rows each (more
-  // rows take several workgroups, each reading the context from L2).
+  // Otherwise one request per workgroup, at most 128 query rows each, or 256
+  // for long row lists (more rows take several workgroups, each streaming
+  // the context from L2).
   const int nq = (rows + 31) / 32;                 // 32-row query slices
   if (nq <= 1) launch_bf16<D, 1, 1>(a, p, st);
   else if (nq <= 2) launch_bf16<D, 2, 1>(a, p, st);
   else {
     p.RC = attention_row_chunks(a.Hq / a.Hkv, a.k);
-    launch_bf16<D, 4, 1>(a, p, st);
+    if (DFLASH_ATTN_WIDE && nq > 8) launch_bf16<D, 8, 1>(a, p, st);
+    else launch_bf16<D, 4, 1>(a, p, st);
   }
 }
 
@@ -656,9 +687,11 @@ void dispatch_nw(const AttnArgs& a, AttnP p, hipStream_t st) {
 
 int attention_row_chunks(int G, int k) {
   // query-row chunks of one (request, kv-head): one workgroup up to 64 rows,
-  // otherwise chunks of 128 rows (four 32-row slices)
+  // chunks of 128 rows (four 32-row slices) up to 256, of 256 rows beyond
   const int nq = (G * k + 31) / 32;
-  return nq <= 2 ? 1 : (nq + 3) / 4;
+  if (nq <= 2) return 1;
+  if (DFLASH_ATTN_WIDE && nq > 8) return (nq + 7) / 8;
+  return (nq + 3) / 4;
 }
 
 int attention_splits(int B, int Hkv, int G, int k, int max_pages) {

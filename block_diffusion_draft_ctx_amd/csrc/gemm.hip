@@ -110,7 +110,8 @@ struct GemmP {
   int ksplit, kchunk;
   float* part;       // [ksplit, M, N]
   const void* bias;  // [N] or null (dense epilogue)
-  void* out;         // dense epilogue output [M, N]
+  const void* resid; // [M, N] or null (dense epilogue): out = resid + (product rounded to storage)
+  void* out;         // dense epilogue output [M, N] (may be resid itself)
   void* ck[kML];
   void* cv[kML];
   int np[kML];
@@ -157,7 +158,13 @@ template <typename T, int EPI>
 __device__ __forceinline__ void emit(const GemmP& p, int row, int col, float v, int64_t slot) {
   if (EPI == EPI_DENSE) {
     if (p.bias) v += static_cast<float>(load1(static_cast<const T*>(p.bias) + col));
-    store_val<T>(static_cast<T*>(p.out), (int64_t)row * p.N + col, v);
+    const int64_t i = (int64_t)row * p.N + col;
+    if (p.resid) {
+      // the product is stored (rounded), then added to the residual
+      if (sizeof(T) == 2) v = bf16_to_f32(f32_to_bf16(v));
+      v += static_cast<float>(load1(static_cast<const T*>(p.resid) + i));
+    }
+    store_val<T>(static_cast<T*>(p.out), i, v);
   } else {
     if (slot < 0) return;
     const int l = col / (2 * p.HD);
@@ -505,8 +512,15 @@ __global__ __launch_bounds__(64 * WM_ * WN_) void k_gemm_bf16(GemmP p) {
       if (slot < 0) continue;
       dst = slot * row_stride;
     }
-    *reinterpret_cast<u32x4*>(dst_base + dst + 8 * c) =
-        *reinterpret_cast<const u32x4*>(ot + rl * OS + 8 * c);
+    u32x4 o = *reinterpret_cast<const u32x4*>(ot + rl * OS + 8 * c);
+    if (EPI == EPI_DENSE && p.resid) {   // residual add on the rounded product
+      const u32x4 r = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.resid) + n0 +
+                                                      dst + 8 * c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        o[j] = pack_bf16x2(bf16_lo(o[j]) + bf16_lo(r[j]), bf16_hi(o[j]) + bf16_hi(r[j]));
+    }
+    *reinterpret_cast<u32x4*>(dst_base + dst + 8 * c) = o;
   }
 }
 
@@ -624,6 +638,12 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmP p) {
       u32x4 o;
 #pragma unroll
       for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
+      if (EPI == EPI_DENSE && p.resid) {   // residual add on the rounded product
+        const u32x4 r = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.resid) + base);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          o[j] = pack_bf16x2(bf16_lo(o[j]) + bf16_lo(r[j]), bf16_hi(o[j]) + bf16_hi(r[j]));
+      }
       *reinterpret_cast<u32x4*>(dst) = o;
     }
     return;
@@ -834,6 +854,27 @@ size_t partial_bytes(int64_t M, int64_t N, int64_t K, bool bf16) {
 }
 
 }  // namespace
+
+size_t dense_gemm_ws_bytes(int64_t M, int64_t N, int64_t K, bool bf16) {
+  return partial_bytes(M, N, K, bf16);
+}
+
+hipError_t launch_dense_gemm(bool bf16, int M, int N, int K, const void* A, const void* B,
+                             const void* bias, const void* resid, void* out, void* ws,
+                             hipStream_t st) {
+  GemmP p{};
+  p.M = M; p.N = N; p.K = K;
+  p.a[0] = A;
+  p.a_seg = K;
+  p.b = B; p.ldb = K;
+  p.b_layered = 0;
+  p.part = static_cast<float*>(ws);
+  p.bias = bias;
+  p.resid = resid;
+  p.out = out;
+  run_gemm(bf16, p, EPI_DENSE, st);
+  return hipGetLastError();
+}
 
 size_t materialize_ws_bytes(int64_t T, int m, int d, int n_layers, int Hkv, int D, bool bf16) {
   const int64_t es = bf16 ? 2 : 4;

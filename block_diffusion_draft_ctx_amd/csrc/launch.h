@@ -113,6 +113,44 @@ int attention_splits(int B, int Hkv, int G, int k, int max_pages);
 size_t attention_ws_bytes(int B, int k, int Hq, int Hkv, int D, int max_pages, bool bf16);
 hipError_t launch_attention(bool bf16, const AttnArgs& a, void* ws, hipStream_t st);
 
+// ------------------------------------------------------------- dense GEMM
+// out[M, N] = A[M, K] . B[N, K]^T (+ bias[N]) (+ resid[M, N], added to the
+// product rounded to storage); bf16 needs N % 128 == 0 and K % 128 == 0.
+size_t dense_gemm_ws_bytes(int64_t M, int64_t N, int64_t K, bool bf16);
+hipError_t launch_dense_gemm(bool bf16, int M, int N, int K, const void* A, const void* B,
+                             const void* bias, const void* resid, void* out, void* ws,
+                             hipStream_t st);
+
+// ------------------------------------------------------------ drafter layer
+struct DraftArgs {
+  int B, k, d, Hq, Hkv, D, I;
+  bool bf16;
+  void* x;                       // [B*k, d] residual stream, updated in place
+  const void* ln1;               // [d]
+  const void* w_qkv;             // [(Hq + 2 Hkv) D, d]
+  const void* q_norm;            // [D] or null
+  const void* k_norm;            // [D] or null
+  const void* w_o;               // [d, Hq D]
+  const void* ln2;               // [d]
+  const void* w_gate_up;         // [2 I, d]: gate rows, then up rows
+  const void* w_down;            // [d, I]
+  float eps, rope_theta;         // rope_theta 0: no rotary embedding
+  const void* cache_k;           // this layer's injected context [num_pages, 16, Hkv, D]
+  const void* cache_v;
+  int num_pages;
+  const int32_t* block_table;    // [B, max_pages]
+  int max_pages;
+  const int32_t* ctx_lens;       // [B]
+  bool causal;
+};
+size_t draft_layer_ws_bytes(const DraftArgs& a);
+hipError_t launch_draft_layer(const DraftArgs& a, void* ws, hipStream_t st);
+size_t draft_head_ws_bytes(int M, int d, int V, bool bf16);
+hipError_t launch_draft_head(bool bf16, int M, int d, int V, const void* x, const void* norm_w,
+                             const void* lm_head, float eps, void* logits, void* ws, hipStream_t st);
+hipError_t launch_embed(bool bf16, int M, int d, int V, const void* table, const int32_t* tokens,
+                        void* out, hipStream_t st);
+
 // ----------------------------------------------------------- materialisation
 struct MatArgs {
   int64_t T;

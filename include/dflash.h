@@ -8,6 +8,9 @@
  *   dflash_tree_verify_greedy  DDTree: target argmax per node and the greedy walk
  *   dflash_tree_attention      DDTree: the target's attention under the ancestor-only mask
  *   dflash_tree_commit_kv      DDTree: the accepted path's KV into the paged cache
+ *   dflash_draft_layer         the drafter's decoder layer around block attention
+ *   dflash_draft_head          the drafter's final norm and shared lm_head
+ *   dflash_embed               the shared embedding gather
  *   dflash_verify_greedy       greedy acceptance over the full vocabulary
  *   dflash_verify_sample       lossless rejection sampling over the full vocabulary
  *   dflash_gate                DLoop block-confidence gate
@@ -450,6 +453,69 @@ dflash_status dflash_tree_commit_kv(
     const int32_t* block_table, int max_pages_per_seq,
     const int32_t* accepted_nodes, int max_depth, const int32_t* accept_len,
     const int32_t* prefix_lens, dflash_dtype dtype, dflash_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * The drafter around block attention.
+ *
+ * [DFlash overview], section "草稿模型架构": the drafter is a small
+ * Qwen3-style decoder that shares the target's embedding table and lm_head;
+ * its block is the anchor followed by mask tokens (section "块扩散"), and
+ * every layer's attention sees that layer's injected context ("KV 注入",
+ * written by dflash_materialize_ctx_kv) and the whole block.
+ *
+ * dflash_draft_layer: one decoder layer on the block rows x [B*k, d_model]
+ * (request-major, updated in place):
+ *   n1 = rmsnorm(x) * ln1;  [q | k | v] = n1 . qkv^T  (Hq, Hkv, Hkv heads of D)
+ *   q = rope(rmsnorm_head(q) * q_norm), k = rope(rmsnorm_head(k) * k_norm)
+ *       (a NULL norm weight skips that norm; rope_theta 0 skips the rotary
+ *       embedding; half-split rotation; block position i of request b sits
+ *       at ctx_lens[b] + i)
+ *   a  = dflash_block_attention(q, k, v, the layer's cache, block_mask)
+ *   x += a . o^T;  n2 = rmsnorm(x) * ln2
+ *   [g | u] = n2 . gate_up^T;  x += (silu(g) * u) . down^T
+ * rmsnorm(x) = x / sqrt(mean(x^2) + eps).  Weights are row-major [out, in];
+ * no biases.  Every intermediate is stored (rounded) in the workspace; each
+ * projection's product is rounded before its residual add.
+ * bf16: d_model, (Hq + 2 Hkv) * D, Hq * D and d_ff multiples of 128, every
+ * pointer 16-byte aligned; head_dim 64 or 128; k <= 64 and (Hq/Hkv) * k <=
+ * 256 (dflash_block_attention's limits).  The cache arguments are those of
+ * dflash_block_attention (one table row per request).
+ *
+ * dflash_draft_head: logits [M, V] = (rmsnorm(x) * norm_w) . lm_head^T.
+ * dflash_embed: out [M, d_model] = table[tokens] (the shared embedding
+ *   table [V, d_model]); a token outside [0, V) gives a NaN row (in band).
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  const void* ln1;        /* [d_model] */
+  const void* qkv;        /* [(Hq + 2 Hkv) * D, d_model] */
+  const void* q_norm;     /* [D] or NULL */
+  const void* k_norm;     /* [D] or NULL */
+  const void* o;          /* [d_model, Hq * D] */
+  const void* ln2;        /* [d_model] */
+  const void* gate_up;    /* [2 * d_ff, d_model]: gate rows, then up rows */
+  const void* down;       /* [d_model, d_ff] */
+} dflash_draft_layer_weights;
+
+size_t dflash_draft_layer_workspace_size(int B, int k, int d_model, int n_q_heads, int n_kv_heads,
+                                         int head_dim, int d_ff, int max_pages_per_seq,
+                                         dflash_dtype dtype);
+
+dflash_status dflash_draft_layer(
+    int B, int k, int d_model, int n_q_heads, int n_kv_heads, int head_dim, int d_ff,
+    void* x, const dflash_draft_layer_weights* weights, float eps, float rope_theta,
+    const void* cache_k, const void* cache_v, int num_pages, int page_size,
+    const int32_t* block_table, int max_pages_per_seq, const int32_t* ctx_lens,
+    dflash_block_mask block_mask, dflash_dtype dtype, void* ws, size_t ws_bytes,
+    dflash_stream_t stream);
+
+size_t dflash_draft_head_workspace_size(int M, int d_model, int V, dflash_dtype dtype);
+
+dflash_status dflash_draft_head(int M, int d_model, int V, const void* x, const void* norm_weight,
+                                const void* lm_head, float eps, void* logits, dflash_dtype dtype,
+                                void* ws, size_t ws_bytes, dflash_stream_t stream);
+
+dflash_status dflash_embed(int M, int d_model, int V, const void* table, const int32_t* tokens,
+                           void* out, dflash_dtype dtype, dflash_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -454,3 +454,24 @@ def tree_target_logits(seed, *, dtype, B, n_rows, V, std=3.0, follow=None, boost
             for r, t in pairs:
                 x[b, r, t] += np.float32(boost)
     return bf16_bits(x) if dtype == BF16 else x
+
+
+def draft_layer_weights(seed, *, dtype, d_model, n_q_heads, n_kv_heads, head_dim, d_ff,
+                        qk_norm=True, std=0.02):
+    """One drafter layer's weights (row-major [out, in]): projections ~N(0,
+    std), norm weights 1 + N(0, 0.1).  Draw order: ln1, qkv, q_norm, k_norm,
+    o, ln2, gate_up, down."""
+    rng = make_rng(seed)
+    D = head_dim
+    w = {"ln1": 1.0 + rng.standard_normal(d_model, dtype=np.float32) * np.float32(0.1),
+         "qkv": rng.standard_normal(((n_q_heads + 2 * n_kv_heads) * D, d_model), dtype=np.float32) * np.float32(std),
+         "q_norm": 1.0 + rng.standard_normal(D, dtype=np.float32) * np.float32(0.1),
+         "k_norm": 1.0 + rng.standard_normal(D, dtype=np.float32) * np.float32(0.1),
+         "o": rng.standard_normal((d_model, n_q_heads * D), dtype=np.float32) * np.float32(std),
+         "ln2": 1.0 + rng.standard_normal(d_model, dtype=np.float32) * np.float32(0.1),
+         "gate_up": rng.standard_normal((2 * d_ff, d_model), dtype=np.float32) * np.float32(std),
+         "down": rng.standard_normal((d_model, d_ff), dtype=np.float32) * np.float32(std)}
+    if not qk_norm:
+        w["q_norm"] = w["k_norm"] = None
+    return {k: (None if v is None else (bf16_bits(v.astype(np.float32)) if dtype == BF16
+                                        else v.astype(np.float32))) for k, v in w.items()}

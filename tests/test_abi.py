@@ -269,3 +269,35 @@ def test_tree_commit_argument_errors(lib, kw, code):
                                   ctypes.cast(vt, dfl.PP), caches, FAKE, 4, FAKE, a["md"], a["acc"],
                                   FAKE, dfl.BF16, None)
     assert s == code
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=96), dfl.E_UNSUPPORTED), (dict(k=65), dfl.E_UNSUPPORTED), (dict(d=200), dfl.E_UNSUPPORTED),
+    (dict(I=100), dfl.E_UNSUPPORTED), (dict(Hq=30), dfl.E_ARG), (dict(eps=-1.0), dfl.E_ARG),
+    (dict(theta=0.5), dfl.E_ARG), (dict(mask=3), dfl.E_ARG), (dict(ps=32), dfl.E_UNSUPPORTED),
+    (dict(x=None), dfl.E_ARG), (dict(x=FAKE + 2), dfl.E_UNSUPPORTED), (dict(nws=0), dfl.E_WORKSPACE),
+    (dict(ln1=None), dfl.E_ARG),
+])
+def test_draft_layer_argument_errors(lib, kw, code):
+    a = dict(D=128, k=16, d=4096, I=12288, Hq=32, eps=1e-6, theta=1e6, mask=0, ps=16, x=FAKE,
+             nws=1 << 30, ln1=FAKE)
+    a.update(kw)
+    w = dfl.DraftLayerWeights(a["ln1"], FAKE, None, None, FAKE, FAKE, FAKE, FAKE)
+    s = lib.dflash_draft_layer(4, a["k"], a["d"], a["Hq"], 8, a["D"], a["I"], a["x"], ctypes.byref(w),
+                               a["eps"], a["theta"], FAKE, FAKE, 100, a["ps"], FAKE, 64, FAKE,
+                               a["mask"], dfl.BF16, WS, a["nws"], None)
+    assert s == code
+
+
+@no_gpu
+def test_draft_head_and_embed_argument_errors(lib):
+    assert lib.dflash_draft_head(16, 4096, 1000, FAKE, FAKE, FAKE, 1e-6, FAKE, dfl.BF16, WS, 1 << 30,
+                                 None) == dfl.E_UNSUPPORTED            # V % 128
+    assert lib.dflash_draft_head(16, 4096, 1024, FAKE, FAKE, None, 1e-6, FAKE, dfl.BF16, WS, 1 << 30,
+                                 None) == dfl.E_ARG
+    assert lib.dflash_draft_head(16, 4096, 1024, FAKE, FAKE, FAKE, 1e-6, FAKE, dfl.BF16, WS, 0,
+                                 None) == dfl.E_WORKSPACE
+    assert lib.dflash_embed(4, 100, 10, FAKE, FAKE, FAKE, dfl.BF16, None) == dfl.E_UNSUPPORTED
+    assert lib.dflash_embed(4, 128, 10, None, FAKE, FAKE, dfl.BF16, None) == dfl.E_ARG
+    assert lib.dflash_embed(0, 128, 10, None, None, None, dfl.BF16, None) == dfl.OK
