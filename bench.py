@@ -77,13 +77,15 @@ def parse():
                     help="also run one 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--breakdown", action="store_true", help="per-part timings to stderr")
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "sample-gate", "prefill", "packed", "tree", "tree-attn"],
+                    choices=["decode", "sample-gate", "prefill", "packed", "tree", "tree-attn",
+                             "draft"],
                     help="decode: the greedy decode step (default); sample-gate: Qwen3-4B-shaped "
                          "stochastic chain verify with DLoop gates; prefill: 4 x 32768-row "
                          "ctx-KV materialisation; packed: training-style packed block mask; "
                          "tree: DDTree build (top-K, best-first tree, ancestor mask) + greedy "
                          "tree verify; tree-attn: the target's attention over the flattened tree "
-                         "(ancestor-only mask), one layer")
+                         "(ancestor-only mask), one layer; draft: the drafter's forward (embedding, "
+                         "5 Qwen3-8B-shaped layers over injected context, head)")
     ap.add_argument("--topk", type=int, default=8, help="tree: candidates per block position")
     ap.add_argument("--budget", type=int, default=512, help="tree: node budget")
     ap.add_argument("--sigma", type=float, default=1.0, help="sample-gate: draft = target + N(0, sigma)")
@@ -730,6 +732,115 @@ def bench_tree_attn(args):
     return line
 
 
+def bench_draft(args):
+    """The drafter's forward for one block per request, Qwen3-8B-shaped:
+    embedding gather of [anchor, mask x 15], five decoder layers (d 4096, 32 Q
+    / 8 KV heads x 128, d_ff 12288, q/k head norms, rotary base 1e6) each
+    attending to its injected context (ctx 8192) and the block, then the
+    final norm and the shared lm_head over vocab 151936 -> the draft logits."""
+    import numpy as np
+    import torch
+    import block_diffusion_draft_ctx_amd as dfl
+    B, k, C, Ld = args.batch, args.block, args.ctx, args.layers
+    d, Hq, Hkv, D, I, V = 4096, 32, 8, 128, 12288, 151936
+    M = B * k
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(7000)
+    bf = torch.bfloat16
+
+    def rnd(*shape, std=1.0, mean=0.0):
+        return (torch.randn(*shape, generator=g, device=dev) * std + mean).to(bf)
+
+    layers = []
+    npg = B * C // 16
+    for _ in range(Ld):
+        w = {"ln1": rnd(d, std=0.1, mean=1.0), "qkv": rnd((Hq + 2 * Hkv) * D, d, std=0.02),
+             "q_norm": rnd(D, std=0.1, mean=1.0), "k_norm": rnd(D, std=0.1, mean=1.0),
+             "o": rnd(d, Hq * D, std=0.02), "ln2": rnd(d, std=0.1, mean=1.0),
+             "gate_up": rnd(2 * I, d, std=0.02), "down": rnd(d, I, std=0.02)}
+        layers.append((w, rnd(npg, 16, Hkv, D), rnd(npg, 16, Hkv, D)))
+    bt = torch.randperm(npg, generator=g, device=dev).to(torch.int32).view(B, C // 16).contiguous()
+    ctx = torch.full((B,), C, dtype=torch.int32, device=dev)
+    table = rnd(V, d, std=0.02)
+    lm = rnd(V, d, std=0.02)
+    fnorm = rnd(d, std=0.1, mean=1.0)
+    toks = torch.randint(0, V, (B, k), generator=g, device=dev).to(torch.int32)
+    toks[:, 1:] = V - 1                                   # the mask token after each anchor
+    x = torch.empty(M, d, dtype=bf, device=dev)
+    logits = torch.empty(M, V, dtype=bf, device=dev)
+    wsl = torch.empty(dfl.lib().dflash_draft_layer_workspace_size(B, k, d, Hq, Hkv, D, I, C // 16,
+                                                                  dfl.BF16), dtype=torch.uint8, device=dev)
+    wsh = torch.empty(dfl.lib().dflash_draft_head_workspace_size(M, d, V, dfl.BF16), dtype=torch.uint8,
+                      device=dev)
+
+    def step():
+        dfl.embed(table, toks, out=x)
+        for w, ck, cv in layers:
+            dfl.draft_layer(x, w, ck, cv, bt, ctx, k, Hq, workspace=wsl)
+        dfl.draft_head(x, fnorm, lm, out=logits, workspace=wsh)
+
+    ms = _events_ms(step, args.steps, args.warmup)
+    hms = _events_ms(lambda: dfl.draft_head(x, fnorm, lm, out=logits, workspace=wsh), args.steps,
+                     args.warmup)
+    lms = _events_ms(lambda: dfl.draft_layer(x, layers[0][0], layers[0][1], layers[0][2], bt, ctx, k,
+                                             Hq, workspace=wsl), args.steps, args.warmup)
+    gms = _graph_ms(step, args.steps, args.warmup)
+    layer_params = (Hq + 2 * Hkv) * D * d + d * Hq * D + 2 * I * d + d * I
+    gemm_flops = 2.0 * M * (Ld * layer_params + V * d)
+    attn_flops = Ld * 4.0 * M * Hq * D * (C + k)
+    head_flops = 2.0 * M * V * d
+    line = _base_line(args, "drafter forward (embedding + layers + head), blocks/sec",
+                      round(B / (ms * 1e-3), 1), "blocks/s", ms,
+                      f"Qwen3-8B-shaped DFlash drafter forward: batch {B}, block {k}, {Ld} layers "
+                      f"(d 4096, 32 Q / 8 KV heads x 128, d_ff 12288, q/k head norms, rotary 1e6) over "
+                      f"injected context {C}, final norm and shared lm_head over vocab {V}",
+                      batch=B, block=k, ctx=C, layers=Ld, d_model=d, d_ff=I, vocab=V)
+    line["roofline"] = {"kernel": "lm_head GEMM (draft head)", "bound": "mfma",
+                        "achieved": round(head_flops / (hms * 1e-3) / 1e12, 1),
+                        "peak": BF16_PEAK / 1e12, "unit": "TFLOP/s",
+                        "frac": round(head_flops / (hms * 1e-3) / BF16_PEAK, 4), "traffic": None,
+                        "algorithmic_flops": head_flops, "avg_launch_us": round(hms * 1e3, 2)}
+    line["breakdown"] = {"layer_us": round(lms * 1e3, 1), "head_us": round(hms * 1e3, 1),
+                         "step_gemm_tflop": round(gemm_flops / 1e12, 3),
+                         "step_attention_tflop": round(attn_flops / 1e12, 3),
+                         "step_mfma_frac": round((gemm_flops + attn_flops) / (ms * 1e-3) / BF16_PEAK, 4)}
+    line["graph_replay"] = {"ms_per_step": round(gms, 4), "value": round(B / (gms * 1e-3), 1)}
+    if not args.no_cpu_baseline:
+        import time
+        import oracle
+
+        def host(t):
+            return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+        # one request: its 16 rows through every layer and the head
+        pages = bt[0].long()
+        hw = [({n: host(v) for n, v in w.items()}, host(ck[pages]), host(cv[pages])) for w, ck, cv in layers]
+        th, tk = host(table), toks[:1].cpu().numpy()
+        bth = np.arange(C // 16, dtype=np.int32)[None]
+        ch = np.array([C], dtype=np.int32)
+        fh, lh = host(fnorm), host(lm)
+        t0 = time.perf_counter()
+        xb = oracle.embed(th, tk, "bf16")          # float64 values on the bf16 grid
+        for w, ck, cv in hw:
+            xb = oracle.draft_layer(_f64_to_bf16_bits(xb), w, ck, cv, bth, ch, k=k, n_q_heads=Hq,
+                                    n_kv_heads=Hkv, head_dim=D, dtype="bf16")
+        oracle.draft_head(_f64_to_bf16_bits(xb), fh, lh, "bf16")
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {
+            "value": round(1 / dt, 4), "unit": "blocks/s", "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle",
+            "sample": f"1 of the {B} requests: its {k} rows through the embedding, {Ld} layers "
+                      f"(ctx {C}) and the head; {dt:.1f} s of CPU work"}
+    return line
+
+
+def _f64_to_bf16_bits(x):
+    """float64 values already on the bf16 grid -> their bf16 bit patterns."""
+    import numpy as np
+    return (np.asarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -744,7 +855,7 @@ def main():
     if args.workload != "decode":
         fn = {"sample-gate": bench_sample_gate, "prefill": bench_prefill,
               "packed": bench_packed, "tree": bench_tree,
-              "tree-attn": bench_tree_attn}[args.workload]
+              "tree-attn": bench_tree_attn, "draft": bench_draft}[args.workload]
         print(json.dumps(fn(args)), flush=True)
         return
     st = Step(args.batch, args.ctx, args.block, args.vocab, args.layers, causal=args.causal,

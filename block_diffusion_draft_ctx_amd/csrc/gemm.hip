@@ -112,6 +112,7 @@ struct GemmP {
   const void* bias;  // [N] or null (dense epilogue)
   const void* resid; // [M, N] or null (dense epilogue): out = resid + (product rounded to storage)
   void* out;         // dense epilogue output [M, N] (may be resid itself)
+  int64_t ldc;       // row stride of out and resid (dense epilogue)
   void* ck[kML];
   void* cv[kML];
   int np[kML];
@@ -158,7 +159,7 @@ template <typename T, int EPI>
 __device__ __forceinline__ void emit(const GemmP& p, int row, int col, float v, int64_t slot) {
   if (EPI == EPI_DENSE) {
     if (p.bias) v += static_cast<float>(load1(static_cast<const T*>(p.bias) + col));
-    const int64_t i = (int64_t)row * p.N + col;
+    const int64_t i = (int64_t)row * p.ldc + col;
     if (p.resid) {
       // the product is stored (rounded), then added to the residual
       if (sizeof(T) == 2) v = bf16_to_f32(f32_to_bf16(v));
@@ -491,7 +492,7 @@ __global__ __launch_bounds__(64 * WM_ * WN_) void k_gemm_bf16(GemmP p) {
   int hd0 = 0, layer = 0;
   if (EPI == EPI_DENSE) {
     dst_base = static_cast<uint16_t*>(p.out) + n0;
-    row_stride = p.N;
+    row_stride = p.ldc;
   } else {
     layer = n0 / (2 * p.HD);
     const int kv = (n0 / p.HD) & 1;
@@ -626,7 +627,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmP p) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) v[j] += bf16_to_f32(static_cast<const uint16_t*>(p.bias)[col + j]);
         }
-        dst = static_cast<uint16_t*>(p.out) + base;
+        dst = static_cast<uint16_t*>(p.out) + (int64_t)row * p.ldc + col;
       } else {
         const int l = col / (2 * p.HD);
         const int64_t slot = row_slot(p, row, l);
@@ -639,7 +640,8 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmP p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
       if (EPI == EPI_DENSE && p.resid) {   // residual add on the rounded product
-        const u32x4 r = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.resid) + base);
+        const u32x4 r = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.resid) +
+                                                        (int64_t)row * p.ldc + col);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           o[j] = pack_bf16x2(bf16_lo(o[j]) + bf16_lo(r[j]), bf16_hi(o[j]) + bf16_hi(r[j]));
@@ -856,23 +858,34 @@ size_t partial_bytes(int64_t M, int64_t N, int64_t K, bool bf16) {
 }  // namespace
 
 size_t dense_gemm_ws_bytes(int64_t M, int64_t N, int64_t K, bool bf16) {
+  if (bf16 && N > 256 && N % 256 == 128)
+    return std::max(partial_bytes(M, N - 128, K, bf16), partial_bytes(M, 128, K, bf16));
   return partial_bytes(M, N, K, bf16);
 }
 
 hipError_t launch_dense_gemm(bool bf16, int M, int N, int K, const void* A, const void* B,
                              const void* bias, const void* resid, void* out, void* ws,
                              hipStream_t st) {
-  GemmP p{};
-  p.M = M; p.N = N; p.K = K;
-  p.a[0] = A;
-  p.a_seg = K;
-  p.b = B; p.ldb = K;
-  p.b_layered = 0;
-  p.part = static_cast<float*>(ws);
-  p.bias = bias;
-  p.resid = resid;
-  p.out = out;
-  run_gemm(bf16, p, EPI_DENSE, st);
+  // 256-column tiles need N % 256 == 0: a width of 256j + 128 runs as the
+  // first 256j columns plus one 128-column strip (same output rows).
+  const int tail = (bf16 && N > 256 && N % 256 == 128) ? 128 : 0;
+  for (int part = 0; part < (tail ? 2 : 1); ++part) {
+    const int c0 = part == 0 ? 0 : N - tail;
+    const int n = tail ? (part == 0 ? N - tail : tail) : N;
+    const int64_t es = bf16 ? 2 : 4;
+    GemmP p{};
+    p.M = M; p.N = n; p.K = K;
+    p.a[0] = A;
+    p.a_seg = K;
+    p.b = static_cast<const char*>(B) + (int64_t)c0 * K * es; p.ldb = K;
+    p.b_layered = 0;
+    p.part = static_cast<float*>(ws);
+    p.bias = bias ? static_cast<const char*>(bias) + c0 * es : nullptr;
+    p.resid = resid ? static_cast<const char*>(resid) + c0 * es : nullptr;
+    p.out = static_cast<char*>(out) + c0 * es;
+    p.ldc = N;
+    run_gemm(bf16, p, EPI_DENSE, st);
+  }
   return hipGetLastError();
 }
 
@@ -903,6 +916,7 @@ hipError_t launch_materialize(bool bf16, const MatArgs& a, void* ws, size_t ws_b
     p.part = part;
     p.bias = a.b_f;
     p.out = h;
+    p.ldc = a.d;
     run_gemm(bf16, p, EPI_DENSE, st);
   }
   // GEMM 2: every layer's K and V in one product, scattered into the caches.
