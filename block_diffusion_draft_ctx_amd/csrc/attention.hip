@@ -48,6 +48,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #ifndef DFLASH_ATTN_NT
 #define DFLASH_ATTN_NT 1
 #endif
+#ifndef DFLASH_ATTN_MIN_SPLIT_TILES
+#define DFLASH_ATTN_MIN_SPLIT_TILES 4   // shortest context split, in 64-key tiles
+#endif
 #ifndef DFLASH_ATTN_WIDE
 #define DFLASH_ATTN_WIDE 0     // 256-row workgroups (16 wavefronts: they spill at 128 VGPRs)
 #endif
@@ -696,15 +699,15 @@ int attention_row_chunks(int G, int k) {
 
 int attention_splits(int B, int Hkv, int G, int k, int max_pages) {
   // About two workgroups per CU so every CU keeps several tiles in flight,
-  // but no split shorter than 4 key tiles; a split never spans more pages
-  // than its LDS page list holds.  Row chunks already multiply the
+  // but no split shorter than DFLASH_ATTN_MIN_SPLIT_TILES key tiles; a split
+  // never spans more pages than its LDS page list holds.  Row chunks already multiply the
   // workgroups.
   const int64_t groups = (int64_t)B * Hkv * attention_row_chunks(G, k);
   // (sized for the longest key list of either workgroup shape: a pair of
   // requests on one shared table row adds 2k block keys)
   const int64_t tiles = ((int64_t)max_pages * 16 + 2 * k + kKT - 1) / kKT;
   int64_t s = (DFLASH_ATTN_TARGET_WGS + groups - 1) / std::max<int64_t>(groups, 1);
-  s = std::min<int64_t>(s, std::max<int64_t>(1, tiles / 4));
+  s = std::min<int64_t>(s, std::max<int64_t>(1, tiles / DFLASH_ATTN_MIN_SPLIT_TILES));
   s = std::min<int64_t>(s, 64);
   const int64_t tiles_cap = kMaxSplitPages * 16 / kKT;
   s = std::max<int64_t>(s, (tiles + tiles_cap - 1) / tiles_cap);

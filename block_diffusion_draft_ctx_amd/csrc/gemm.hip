@@ -46,6 +46,9 @@ constexpr int BK = 64;   // granularity of split-K chunks (a multiple of the pip
 #ifndef DFLASH_GEMM_SMALL_BM
 #define DFLASH_GEMM_SMALL_BM 128
 #endif
+#ifndef DFLASH_GEMM_SPLIT_MIN_K
+#define DFLASH_GEMM_SPLIT_MIN_K 4096   // shortest contraction split of the 256 x 256 plan
+#endif
 #ifndef DFLASH_GEMM_WGS
 #define DFLASH_GEMM_WGS 512
 #endif
@@ -615,6 +618,9 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmP p) {
       const int col = (int)(e - (int64_t)row * n8) * 8;
       const int64_t base = (int64_t)row * p.N + col;
       float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      // in split order (deterministic); unrolled so several splits' loads are
+      // in flight at once
+#pragma unroll 8
       for (int s = 0; s < p.ksplit; ++s) {
         const f32x4v* src = reinterpret_cast<const f32x4v*>(p.part + (int64_t)s * total + base);
         const f32x4v lo = src[0], hi = src[1];
@@ -793,7 +799,7 @@ Plan plan_gemm(int64_t M, int64_t N, int64_t K, bool bf16) {
   //    DFLASH_GEMM_WGS workgroups exist.
   constexpr int64_t kCUs = DFLASH_GEMM_BIG_MIN_TILES;
   const int64_t t256 = N % 256 == 0 ? cdiv(M, 256) * (N / 256) : 0;
-  const bool split_ok = t256 > 0 && K / cdiv(kCUs, t256) >= 4096;
+  const bool split_ok = t256 > 0 && K / cdiv(kCUs, t256) >= DFLASH_GEMM_SPLIT_MIN_K;
   if (split_ok || t256 >= DFLASH_GEMM_BIG_UNSPLIT_MIN) {
     const int64_t ks0 = split_ok ? cdiv(kCUs, t256) : 1;
     const int64_t kchunk = cdiv(cdiv(K, ks0), BK) * BK;
