@@ -155,7 +155,23 @@ __global__ __launch_bounds__(kThreads) void k_row_argmax(RowSet s0, RowSet s1, i
 __device__ int reduce_argmax_row(const float* pmax, const int* pidx, int row, int nc) {
   float best = neg_inf();
   int bi = INT_MAX;
-  for (int c = 0; c < nc; ++c) am_merge(best, bi, pmax[row * nc + c], pidx[row * nc + c]);
+  // the chunk partials load 16 at a time (clamped indices, the repeats
+  // skipped) before they merge, so the loads are in flight together; the
+  // merge is a total order (value, then lower index), so the winner does
+  // not depend on the grouping
+  for (int c0 = 0; c0 < nc; c0 += 16) {
+    float v[16];
+    int ix[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int c = min(c0 + j, nc - 1);
+      v[j] = pmax[row * nc + c];
+      ix[j] = pidx[row * nc + c];
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (c0 + j < nc) am_merge(best, bi, v[j], ix[j]);
+  }
   return bi == INT_MAX ? 0 : bi;  // an all -inf row: every entry ties, the first wins
 }
 
