@@ -140,8 +140,8 @@ class Step:
         perm = torch.randperm(num_pages, generator=g, device=dev).to(torch.int32)
         self.block_table = perm.view(B, self.max_pages).contiguous()
         self.num_pages = num_pages
-        self.cache_k = [randn(num_pages, 16, Hkv, D) for _ in range(Ld)]
-        self.cache_v = [randn(num_pages, 16, Hkv, D) for _ in range(Ld)]
+        self.cache_k = [randn(num_pages, Hkv, 16, D) for _ in range(Ld)]
+        self.cache_v = [randn(num_pages, Hkv, 16, D) for _ in range(Ld)]
         self.q = [randn(B, k, Hq, D) for _ in range(Ld)]
         self.k_blk = [randn(B, k, Hkv, D) for _ in range(Ld)]
         self.v_blk = [randn(B, k, Hkv, D) for _ in range(Ld)]
@@ -466,8 +466,8 @@ def bench_prefill(args):
     maxp = rps // 16
     npg = n_seq * maxp
     bt = torch.randperm(npg, generator=g, device=dev).to(torch.int32).view(n_seq, maxp).contiguous()
-    ck = [torch.empty(npg, 16, Hkv, D, dtype=bf, device=dev) for _ in range(Ld)]
-    cv = [torch.empty(npg, 16, Hkv, D, dtype=bf, device=dev) for _ in range(Ld)]
+    ck = [torch.empty(npg, Hkv, 16, D, dtype=bf, device=dev) for _ in range(Ld)]
+    cv = [torch.empty(npg, Hkv, 16, D, dtype=bf, device=dev) for _ in range(Ld)]
     start = torch.zeros(n_seq, dtype=torch.int32, device=dev)
     ws = torch.empty(dfl.lib().dflash_materialize_workspace_size(T, m, d, Ld, Hkv, D, dfl.BF16),
                      dtype=torch.uint8, device=dev)
@@ -524,8 +524,8 @@ def bench_packed(args):
     npg = seq // 16
     perm = torch.randperm(npg, generator=g, device=dev).to(torch.int32)
     bt = perm.view(1, npg).contiguous()   # one shared row: every block reads the sequence
-    ck = torch.randn(npg, 16, Hkv, D, generator=g, device=dev).to(bf)
-    cv = torch.randn(npg, 16, Hkv, D, generator=g, device=dev).to(bf)
+    ck = torch.randn(npg, Hkv, 16, D, generator=g, device=dev).to(bf)
+    cv = torch.randn(npg, Hkv, 16, D, generator=g, device=dev).to(bf)
     q = torch.randn(nb, kk, Hq, D, generator=g, device=dev).to(bf)
     kb = torch.randn(nb, kk, Hkv, D, generator=g, device=dev).to(bf)
     vb = torch.randn(nb, kk, Hkv, D, generator=g, device=dev).to(bf)
@@ -674,8 +674,8 @@ def bench_tree_attn(args):
     mask = tb["ancestor_mask"]
     npg = B * C // 16
     bt = torch.randperm(npg, generator=g, device=dev).to(torch.int32).view(B, C // 16).contiguous()
-    ck = torch.randn(npg, 16, Hkv, D, generator=g, device=dev).to(bf)
-    cv = torch.randn(npg, 16, Hkv, D, generator=g, device=dev).to(bf)
+    ck = torch.randn(npg, Hkv, 16, D, generator=g, device=dev).to(bf)
+    cv = torch.randn(npg, Hkv, 16, D, generator=g, device=dev).to(bf)
     q = torch.randn(B, R, Hq, D, generator=g, device=dev).to(bf)
     kt = torch.randn(B, R, Hkv, D, generator=g, device=dev).to(bf)
     vt = torch.randn(B, R, Hkv, D, generator=g, device=dev).to(bf)
@@ -759,7 +759,7 @@ def bench_draft(args):
              "q_norm": rnd(D, std=0.1, mean=1.0), "k_norm": rnd(D, std=0.1, mean=1.0),
              "o": rnd(d, Hq * D, std=0.02), "ln2": rnd(d, std=0.1, mean=1.0),
              "gate_up": rnd(2 * I, d, std=0.02), "down": rnd(d, I, std=0.02)}
-        layers.append((w, rnd(npg, 16, Hkv, D), rnd(npg, 16, Hkv, D)))
+        layers.append((w, rnd(npg, Hkv, 16, D), rnd(npg, Hkv, 16, D)))
     bt = torch.randperm(npg, generator=g, device=dev).to(torch.int32).view(B, C // 16).contiguous()
     ctx = torch.full((B,), C, dtype=torch.int32, device=dev)
     table = rnd(V, d, std=0.02)

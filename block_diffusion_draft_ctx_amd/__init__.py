@@ -175,6 +175,20 @@ def _dev(t, name):
     return t
 
 
+def _cache_pair(ck, cv, Hkv, D):
+    """One layer's K and V caches, each [num_pages, Hkv, page_size, D]
+    (head-major) on the device with the same shape; returns (num_pages,
+    page_size)."""
+    for name, t in (("cache_k", ck), ("cache_v", cv)):
+        _dev(t, name)
+        if t.dim() != 4 or t.shape[1] != Hkv or t.shape[3] != D:
+            raise ValueError(f"{name} must be [num_pages, {Hkv}, page_size, {D}] (head-major), "
+                             f"got {tuple(t.shape)}")
+    if ck.shape != cv.shape:
+        raise ValueError(f"cache_k {tuple(ck.shape)} and cache_v {tuple(cv.shape)} differ")
+    return ck.shape[0], ck.shape[2]
+
+
 def _i32(t, name):
     torch = _torch()
     if t is None:
@@ -217,7 +231,7 @@ def materialize_ctx_kv(hiddens: Sequence, W_f, b_f, W_K: Sequence, W_V: Sequence
                        k_norm_eps: float = 1e-6, rope_theta: float = 0.0):
     """dflash_materialize_ctx_kv.  hiddens: m tensors [T, d]; W_f [d, m*d];
     b_f [d] or None; W_K/W_V: per-layer [Hkv*D, d]; cache_k/cache_v: per-layer
-    [num_pages, 16, Hkv, D]; block_table [n_seq, max_pages] int32.  K
+    [num_pages, Hkv, 16, D]; block_table [n_seq, max_pages] int32.  K
     epilogue: k_norm_weight (per-layer [D] tensors, or None) and rope_theta
     (0: none)."""
     L = lib()
@@ -227,12 +241,11 @@ def materialize_ctx_kv(hiddens: Sequence, W_f, b_f, W_K: Sequence, W_V: Sequence
         _dev(h, f"hiddens[{i}]")
     dt = _dtype_code(hiddens[0])
     n_layers = len(W_K)
-    _, _, Hkv, D = cache_k[0].shape
+    _, Hkv, _, D = cache_k[0].shape
     _i32(block_table, "block_table")
     _i32(seq_start_pos, "seq_start_pos")
     _i32(commit_lens, "commit_lens")
-    caches = (KVLayer * n_layers)(*[KVLayer(_ptr(_dev(k, "cache_k")), _ptr(_dev(v, "cache_v")),
-                                            k.shape[0], k.shape[1])
+    caches = (KVLayer * n_layers)(*[KVLayer(_ptr(k), _ptr(v), *_cache_pair(k, v, Hkv, D))
                                     for k, v in zip(cache_k, cache_v)])
     need = L.dflash_materialize_workspace_size(T, m, d, n_layers, Hkv, D, dt)
     ws, nws = _workspace(need, hiddens[0].device, workspace)
@@ -275,9 +288,9 @@ def block_attention(q, k_blk, v_blk, cache_k, cache_v, block_table, ctx_lens, sc
     B, k, Hq, D = q.shape
     Hkv = k_blk.shape[2]
     dt = _dtype_code(q)
-    for n, t in (("q", q), ("k_blk", k_blk), ("v_blk", v_blk), ("cache_k", cache_k),
-                 ("cache_v", cache_v)):
+    for n, t in (("q", q), ("k_blk", k_blk), ("v_blk", v_blk)):
         _dev(t, n)
+    npg, psz = _cache_pair(cache_k, cache_v, Hkv, D)
     _i32(block_table, "block_table")
     _i32(ctx_lens, "ctx_lens")
     if out is None:
@@ -288,7 +301,7 @@ def block_attention(q, k_blk, v_blk, cache_k, cache_v, block_table, ctx_lens, sc
     ws, nws = _workspace(need, q.device, workspace)
     s = L.dflash_block_attention(
         B, k, Hq, Hkv, D, _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(cache_k), _ptr(cache_v),
-        cache_k.shape[0], cache_k.shape[1], _ptr(block_table), block_table.shape[1],
+        npg, psz, _ptr(block_table), block_table.shape[1],
         block_table.shape[0], _ptr(ctx_lens), float(scale), MASK_CAUSAL if causal else MASK_BIDIRECTIONAL,
         _ptr(out), _ptr(lse), dt, odt,
         _ptr(ws), nws,
@@ -515,7 +528,7 @@ def tree_attention(q, k_tree, v_tree, cache_k, cache_v, block_table, ctx_lens, a
                    scale=0.0, out=None, lse=None, workspace=None, stream=None, out_dtype=None):
     """dflash_tree_attention.  q [B, R, Hq, D], k_tree / v_tree [B, R, Hkv, D]
     with R = 1 + budget (row 0 the root, row 1 + j node j); caches
-    [num_pages, 16, Hkv, D]; block_table [B, max_pages]; ctx_lens [B];
+    [num_pages, Hkv, 16, D]; block_table [B, max_pages]; ctx_lens [B];
     ancestor_mask [B, R - 1, ceil((R - 1) / 32)] int32 bit rows as
     ``tree_build`` returns them.  Returns (out, lse)."""
     torch = _torch()
@@ -523,9 +536,9 @@ def tree_attention(q, k_tree, v_tree, cache_k, cache_v, block_table, ctx_lens, a
     B, R, Hq, D = q.shape
     Hkv = k_tree.shape[2]
     dt = _dtype_code(q)
-    for n, t in (("q", q), ("k_tree", k_tree), ("v_tree", v_tree), ("cache_k", cache_k),
-                 ("cache_v", cache_v)):
+    for n, t in (("q", q), ("k_tree", k_tree), ("v_tree", v_tree)):
         _dev(t, n)
+    npg, psz = _cache_pair(cache_k, cache_v, Hkv, D)
     _i32(block_table, "block_table")
     _i32(ctx_lens, "ctx_lens")
     if ancestor_mask is not None:
@@ -540,7 +553,7 @@ def tree_attention(q, k_tree, v_tree, cache_k, cache_v, block_table, ctx_lens, a
     ws, nws = _workspace(need, q.device, workspace)
     s = L.dflash_tree_attention(
         B, R, Hq, Hkv, D, _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(cache_k), _ptr(cache_v),
-        cache_k.shape[0], cache_k.shape[1], _ptr(block_table), block_table.shape[1],
+        npg, psz, _ptr(block_table), block_table.shape[1],
         _ptr(ctx_lens), _ptr(ancestor_mask), float(scale), _ptr(out), _ptr(lse), dt, odt,
         _ptr(ws), nws, _stream(stream))
     _check(s, "dflash_tree_attention")
@@ -550,7 +563,7 @@ def tree_attention(q, k_tree, v_tree, cache_k, cache_v, block_table, ctx_lens, a
 def tree_commit_kv(k_tree: Sequence, v_tree: Sequence, cache_k: Sequence, cache_v: Sequence,
                    block_table, accepted_nodes, accept_len, prefix_lens, stream=None):
     """dflash_tree_commit_kv.  Per layer l: k_tree[l] / v_tree[l]
-    [B, R, Hkv, D], cache_k[l] / cache_v[l] [num_pages, 16, Hkv, D];
+    [B, R, Hkv, D], cache_k[l] / cache_v[l] [num_pages, Hkv, 16, D];
     block_table [B, max_pages]; accepted_nodes [B, max_depth], accept_len and
     prefix_lens [B] int32 (tree_verify_greedy's outputs and its prefix)."""
     L = lib()
@@ -561,8 +574,7 @@ def tree_commit_kv(k_tree: Sequence, v_tree: Sequence, cache_k: Sequence, cache_
         _i32(t, "int32 argument")
     kp, kpa = _pp([_ptr(_dev(t, "k_tree")) for t in k_tree])
     vp, vpa = _pp([_ptr(_dev(t, "v_tree")) for t in v_tree])
-    caches = (KVLayer * n_layers)(*[KVLayer(_ptr(_dev(k, "cache_k")), _ptr(_dev(v, "cache_v")),
-                                            k.shape[0], k.shape[1])
+    caches = (KVLayer * n_layers)(*[KVLayer(_ptr(k), _ptr(v), *_cache_pair(k, v, Hkv, D))
                                     for k, v in zip(cache_k, cache_v)])
     s = L.dflash_tree_commit_kv(
         B, R, n_layers, Hkv, D, kp, vp, caches, _ptr(block_table), block_table.shape[1],
@@ -579,12 +591,13 @@ def draft_layer(x, weights, cache_k, cache_v, block_table, ctx_lens, k, n_q_head
     """dflash_draft_layer: one drafter layer on x [B*k, d] (updated in place).
     weights: dict of device tensors ln1 [d], qkv [(Hq + 2 Hkv) D, d], q_norm /
     k_norm [D] or None, o [d, Hq D], ln2 [d], gate_up [2 I, d], down [d, I].
-    cache_k / cache_v [num_pages, 16, Hkv, D] (this layer's context),
+    cache_k / cache_v [num_pages, Hkv, 16, D] (this layer's context),
     block_table [B, max_pages], ctx_lens [B].  Returns x."""
     L = lib()
     M, d = x.shape
     B = M // k
-    Hkv, D = cache_k.shape[2], cache_k.shape[3]
+    Hkv, D = cache_k.shape[1], cache_k.shape[3]
+    npg, psz = _cache_pair(cache_k, cache_v, Hkv, D)
     I = weights["down"].shape[1]
     dt = _dtype_code(x)
     _dev(x, "x")
@@ -597,8 +610,7 @@ def draft_layer(x, weights, cache_k, cache_v, block_table, ctx_lens, k, n_q_head
     need = L.dflash_draft_layer_workspace_size(B, k, d, n_q_heads, Hkv, D, I, block_table.shape[1], dt)
     ws, nws = _workspace(need, x.device, workspace)
     s = L.dflash_draft_layer(B, k, d, n_q_heads, Hkv, D, I, _ptr(x), ctypes.byref(wst), float(eps),
-                             float(rope_theta), _ptr(_dev(cache_k, "cache_k")),
-                             _ptr(_dev(cache_v, "cache_v")), cache_k.shape[0], cache_k.shape[1],
+                             float(rope_theta), _ptr(cache_k), _ptr(cache_v), npg, psz,
                              _ptr(block_table), block_table.shape[1], _ptr(ctx_lens),
                              MASK_CAUSAL if causal else MASK_BIDIRECTIONAL, dt, _ptr(ws), nws,
                              _stream(stream))

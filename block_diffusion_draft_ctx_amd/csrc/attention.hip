@@ -22,6 +22,10 @@
 // factor; the two key halves merge through LDS at the end.  Small batches
 // split the context across workgroups and a second kernel merges the splits
 // by their log-sum-exp.
+//
+// The paged context cache is head-major, [num_pages, Hkv, 16, D]: a page's
+// 16 keys of one kv-head are one contiguous run (4 KB at D = 128), so a
+// 64-key tile is four such runs rather than 64 rows at a stride of Hkv*D.
 #include <climits>
 #include <cmath>
 
@@ -236,14 +240,14 @@ void k_attn_bf16(AttnP p) {
   // Per-thread chunk geometry is fixed for the whole loop: chunk c of every
   // tile is key kc[c] of the tile, 16-byte column dcc[c].
   int kc[CPT];
-  int64_t coff[CPT];   // offset of (slot kc%16, head g, column) inside a page
+  int64_t coff[CPT];   // offset of (head g, slot kc%16, column) inside a head-major page
   int64_t boff[CPT];   // offset of (head g, column) inside a block row
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int e = min((int)threadIdx.x + c * NT, NCH - 1);
     kc[c] = e / CPR;
     const int dc = e - kc[c] * CPR;
-    coff[c] = ((int64_t)(kc[c] & 15) * p.Hkv + g) * D + dc * 8;
+    coff[c] = ((int64_t)g * 16 + (kc[c] & 15)) * D + dc * 8;
     boff[c] = (int64_t)g * D + dc * 8;
   }
   const int64_t page_elems = (int64_t)16 * p.Hkv * D;
@@ -603,7 +607,7 @@ __global__ __launch_bounds__(64) void k_attn_f32(int B, int k, int Hq, int Hkv, 
     if (j < C) {
       const int page = bt[(int64_t)b * bt_stride + (j >> 4)];
       if (page < 0 || page >= num_pages) { poison = true; continue; }
-      const int64_t off = (((int64_t)page * 16 + (j & 15)) * Hkv + g) * D;
+      const int64_t off = (((int64_t)page * Hkv + g) * 16 + (j & 15)) * D;
       kr = ck + off; vr = cv + off;
     } else {
       if (mode == kMaskTree && j > C) {           // node y = j - C - 1: an ancestor (or itself)?

@@ -110,6 +110,7 @@ struct GemmP {
   const void* wk[kML];
   const void* wv[kML];
   int HD;            // Hkv * D
+  int D;             // head dim (paged cache offsets)
   int ksplit, kchunk;
   float* part;       // [ksplit, M, N]
   const void* bias;  // [N] or null (dense epilogue)
@@ -135,6 +136,14 @@ __device__ __forceinline__ T pick(const T (&arr)[N], int i) {
   for (int j = 1; j < N; ++j)
     if (i == j) r = arr[j];
   return r;
+}
+
+// Element offset of (slot, column hd of the Hkv*D row) in a head-major paged
+// cache [num_pages, Hkv, 16, D]: a page's 16 positions of one kv-head are
+// contiguous.  8 consecutive columns never straddle a head (D % 8 == 0).
+__device__ __forceinline__ int64_t kv_off(const GemmP& p, int64_t slot, int hd) {
+  const int h = hd / p.D;
+  return (slot >> 4) * 16 * (int64_t)p.HD + ((int64_t)h * 16 + (slot & 15)) * p.D + (hd - h * p.D);
 }
 
 // Physical slot of output row r in layer l's cache, or -1 when the row is not
@@ -175,7 +184,7 @@ __device__ __forceinline__ void emit(const GemmP& p, int row, int col, float v, 
     const int kv = (col / p.HD) & 1;
     const int hd = col - (col / p.HD) * p.HD;
     T* cache = static_cast<T*>(kv ? pick(p.cv, l) : pick(p.ck, l));
-    store_val<T>(cache, slot * p.HD + hd, v);
+    store_val<T>(cache, kv_off(p, slot, hd), v);
   }
 }
 
@@ -491,40 +500,36 @@ __global__ __launch_bounds__(64 * WM_ * WN_) void k_gemm_bf16(GemmP p) {
   }
   __syncthreads();
   uint16_t* dst_base;
-  int64_t row_stride;
   int hd0 = 0, layer = 0;
   if (EPI == EPI_DENSE) {
     dst_base = static_cast<uint16_t*>(p.out) + n0;
-    row_stride = p.ldc;
   } else {
     layer = n0 / (2 * p.HD);
     const int kv = (n0 / p.HD) & 1;
     hd0 = n0 - (n0 / p.HD) * p.HD;
-    dst_base = static_cast<uint16_t*>(kv ? pick(p.cv, layer) : pick(p.ck, layer)) + hd0;
-    row_stride = p.HD;
+    dst_base = static_cast<uint16_t*>(kv ? pick(p.cv, layer) : pick(p.ck, layer));
   }
   constexpr int CPRW = BN_ / 8;            // 16-byte chunks per output row
   for (int e = tid; e < BM_ * CPRW; e += NT) {
     const int rl = e / CPRW, c = e - rl * CPRW;
     const int row = m0 + rl;
     if (row >= p.M) continue;
-    int64_t dst;
+    int64_t dst;                           // element offset of the chunk from dst_base
     if (EPI == EPI_DENSE) {
-      dst = (int64_t)row * row_stride;
+      dst = (int64_t)row * p.ldc + 8 * c;
     } else {
       const int64_t slot = row_slot(p, row, layer);
       if (slot < 0) continue;
-      dst = slot * row_stride;
+      dst = kv_off(p, slot, hd0 + 8 * c);
     }
     u32x4 o = *reinterpret_cast<const u32x4*>(ot + rl * OS + 8 * c);
     if (EPI == EPI_DENSE && p.resid) {   // residual add on the rounded product
-      const u32x4 r = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.resid) + n0 +
-                                                      dst + 8 * c);
+      const u32x4 r = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.resid) + n0 + dst);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         o[j] = pack_bf16x2(bf16_lo(o[j]) + bf16_lo(r[j]), bf16_hi(o[j]) + bf16_hi(r[j]));
     }
-    *reinterpret_cast<u32x4*>(dst_base + dst + 8 * c) = o;
+    *reinterpret_cast<u32x4*>(dst_base + dst) = o;
   }
 }
 
@@ -640,7 +645,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmP p) {
         if (slot < 0) continue;
         const int kv = (col / p.HD) & 1;
         const int hd = col - (col / p.HD) * p.HD;
-        dst = static_cast<uint16_t*>(kv ? pick(p.cv, l) : pick(p.ck, l)) + slot * p.HD + hd;
+        dst = static_cast<uint16_t*>(kv ? pick(p.cv, l) : pick(p.ck, l)) + kv_off(p, slot, hd);
       }
       u32x4 o;
 #pragma unroll
@@ -743,12 +748,13 @@ __global__ __launch_bounds__(256) void k_k_epilogue(GemmP p, KEpi e) {
     }
     float w[8];
     if (e.norm) load8v(static_cast<const T*>(pick(e.w, l)) + 8 * lig, w);
-    T* kp = static_cast<T*>(pick(p.ck, l)) + slot * p.HD + 8 * lig;
+    // head h of this slot sits at kp + h * 16 * D (head-major pages)
+    T* kp = static_cast<T*>(pick(p.ck, l)) + kv_off(p, slot, 8 * lig);
     for (int h0 = 0; h0 < Hkv; h0 += HB) {
       float v[HB][8];
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb)
-        if (h0 + hb < Hkv) load8v(kp + (h0 + hb) * e.D, v[hb]);
+        if (h0 + hb < Hkv) load8v(kp + (int64_t)(h0 + hb) * 16 * e.D, v[hb]);
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
         if (h0 + hb >= Hkv) break;   // uniform
@@ -769,7 +775,7 @@ __global__ __launch_bounds__(256) void k_k_epilogue(GemmP p, KEpi e) {
           for (int j = 0; j < 8; ++j)
             v[hb][j] = first ? fmaf(v[hb][j], cs[j], -pr[j] * sn[j]) : fmaf(v[hb][j], cs[j], pr[j] * sn[j]);
         }
-        store8v(kp + (h0 + hb) * e.D, v[hb]);
+        store8v(kp + (int64_t)(h0 + hb) * 16 * e.D, v[hb]);
       }
     }
   }
@@ -942,6 +948,7 @@ hipError_t launch_materialize(bool bf16, const MatArgs& a, void* ws, size_t ws_b
       p.np[l] = a.num_pages[l0 + l];
     }
     p.HD = HD;
+    p.D = a.D;
     p.part = part;
     p.bt = a.block_table;
     p.max_pages = a.max_pages;

@@ -66,7 +66,7 @@ struct CommitArgs {
   int B, R, n_layers, Hkv, D, es;          // es: bytes per element
   const void* k_tree[kCommitMaxLayers];    // [B, R, Hkv, D]
   const void* v_tree[kCommitMaxLayers];
-  void* cache_k[kCommitMaxLayers];         // [num_pages, 16, Hkv, D]
+  void* cache_k[kCommitMaxLayers];         // [num_pages, Hkv, 16, D]
   void* cache_v[kCommitMaxLayers];
   int num_pages[kCommitMaxLayers];
   const int32_t* block_table;              // [B, max_pages]
@@ -135,7 +135,7 @@ struct DraftArgs {
   const void* w_gate_up;         // [2 I, d]: gate rows, then up rows
   const void* w_down;            // [d, I]
   float eps, rope_theta;         // rope_theta 0: no rotary embedding
-  const void* cache_k;           // this layer's injected context [num_pages, 16, Hkv, D]
+  const void* cache_k;           // this layer's injected context [num_pages, Hkv, 16, D]
   const void* cache_v;
   int num_pages;
   const int32_t* block_table;    // [B, max_pages]

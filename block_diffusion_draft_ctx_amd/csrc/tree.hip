@@ -554,14 +554,19 @@ __global__ __launch_bounds__(256) void k_tree_commit(CommitArgs a) {
   if (pos < 0 || (pos >> 4) >= a.max_pages) return;
   const int page = a.block_table[(int64_t)b * a.max_pages + (pos >> 4)];
   if (page < 0 || page >= a.num_pages[l]) return;
-  const int64_t row_bytes = (int64_t)a.Hkv * a.D * a.es;
+  const int64_t head_bytes = (int64_t)a.D * a.es;
+  const int64_t row_bytes = a.Hkv * head_bytes;
   const char* ks = static_cast<const char*>(a.k_tree[l]) + ((int64_t)b * a.R + src) * row_bytes;
   const char* vs = static_cast<const char*>(a.v_tree[l]) + ((int64_t)b * a.R + src) * row_bytes;
-  char* kd = static_cast<char*>(a.cache_k[l]) + ((int64_t)page * 16 + (pos & 15)) * row_bytes;
-  char* vd = static_cast<char*>(a.cache_v[l]) + ((int64_t)page * 16 + (pos & 15)) * row_bytes;
+  // head-major pages [Hkv, 16, D]: head h of position pos at (h*16 + pos%16) * D
+  const int64_t dst0 = (int64_t)page * 16 * row_bytes + (pos & 15) * head_bytes;
+  char* kd = static_cast<char*>(a.cache_k[l]) + dst0;
+  char* vd = static_cast<char*>(a.cache_v[l]) + dst0;
   for (int64_t c = threadIdx.x; c < row_bytes / 16; c += 256) {
-    *reinterpret_cast<uint4*>(kd + 16 * c) = *reinterpret_cast<const uint4*>(ks + 16 * c);
-    *reinterpret_cast<uint4*>(vd + 16 * c) = *reinterpret_cast<const uint4*>(vs + 16 * c);
+    const int64_t h = 16 * c / head_bytes;
+    const int64_t o = h * 16 * head_bytes + (16 * c - h * head_bytes);
+    *reinterpret_cast<uint4*>(kd + o) = *reinterpret_cast<const uint4*>(ks + 16 * c);
+    *reinterpret_cast<uint4*>(vd + o) = *reinterpret_cast<const uint4*>(vs + 16 * c);
   }
 }
 

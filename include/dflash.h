@@ -43,8 +43,9 @@
  * Dtypes      DFLASH_BF16: bf16 storage for hiddens, weights, logits, Q/K/V
  *             and caches; all accumulation, softmax, ratio and CDF arithmetic
  *             is fp32.  DFLASH_F32: fp32 storage and arithmetic throughout.
- * Paged cache One tensor each for K and V, shape [num_pages, page_size,
- *             n_kv_heads, head_dim]; page_size must be 16.  A block table
+ * Paged cache One tensor each for K and V, shape [num_pages, n_kv_heads,
+ *             page_size, head_dim] (head-major: a page's positions of one
+ *             kv-head are contiguous); page_size must be 16.  A block table
  *             [n_seq, max_pages_per_seq] of int32 maps a request's logical
  *             page (position / 16) to a physical page; -1 = unmapped.
  * Errors      A call returns DFLASH_OK or an error code.  Every argument error
@@ -83,7 +84,7 @@ typedef enum { DFLASH_MASK_BIDIRECTIONAL = 0, DFLASH_MASK_CAUSAL = 1 } dflash_bl
 
 /* One draft layer's paged KV cache (device pointers). */
 typedef struct {
-  void* k;           /* [num_pages, page_size, n_kv_heads, head_dim] */
+  void* k;           /* [num_pages, n_kv_heads, page_size, head_dim] */
   void* v;           /* same shape as k */
   int32_t num_pages;
   int32_t page_size; /* must be 16 */
@@ -191,7 +192,7 @@ dflash_status dflash_materialize_ctx_kv(
  * blocks.  Any other value is DFLASH_E_ARG.
  *
  * q            [B, k, Hq, D]      k_blk, v_blk  [B, k, Hkv, D]
- * cache_k/v    [num_pages, 16, Hkv, D]
+ * cache_k/v    [num_pages, Hkv, 16, D]
  * block_table  [table_rows, max_pages_per_seq] int32;  ctx_lens [B] int32 (0 allowed)
  * table_rows   B (request b reads row b) or 1 (every request reads row 0:
  *              the blocks of one packed sequence)

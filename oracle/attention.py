@@ -31,6 +31,7 @@ not written to the cache.
 """
 import numpy as np
 
+from .materialize import slots
 from .numerics import widen
 
 PAGE = 16
@@ -61,8 +62,8 @@ def block_attention(q, k_blk, v_blk, cache_k, cache_v, block_table, ctx_lens, dt
         C = int(ctx_lens[b])
         pos = np.arange(C)
         pages = block_table[b, pos // PAGE]
-        keys = np.concatenate([ck[pages, pos % PAGE], kb[b]], axis=0)   # [C+k, Hkv, D]
-        vals = np.concatenate([cv[pages, pos % PAGE], vb[b]], axis=0)
+        keys = np.concatenate([slots(ck)[pages, pos % PAGE], kb[b]], axis=0)   # [C+k, Hkv, D]
+        vals = np.concatenate([slots(cv)[pages, pos % PAGE], vb[b]], axis=0)
         for h in range(Hq):
             g = h // G
             s = scale * (q[b, :, h, :] @ keys[:, g, :].T)               # [k, C+k]
@@ -84,7 +85,7 @@ def block_attention_masked(q, k_blk, v_blk, cache_k, cache_v, block_table, ctx_l
     are dropped explicitly.  Same outputs as ``block_attention``; used to pin
     it."""
     q, kb, vb = widen(q, dtype), widen(k_blk, dtype), widen(v_blk, dtype)
-    ck, cv = widen(cache_k, dtype), widen(cache_v, dtype)
+    ck, cv = slots(widen(cache_k, dtype)), slots(widen(cache_v, dtype))   # [P, PAGE, Hkv, D]
     B, k, Hq, D = q.shape
     P, _, Hkv, _ = ck.shape
     G = Hq // Hkv

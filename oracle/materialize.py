@@ -42,6 +42,14 @@ from .numerics import widen, round_to
 PAGE = 16
 
 
+def slots(cache):
+    """The paged cache is stored head-major, [num_pages, Hkv, PAGE, D] (a
+    page's positions of one kv-head lie together).  This returns the
+    [num_pages, PAGE, Hkv, D] view of it by page position; it is a view, so
+    writes through it land in ``cache``."""
+    return np.swapaxes(cache, 1, 2)
+
+
 def fuse_hiddens(hiddens, W_f, b_f=None):
     """h_ctx = [h_1; ...; h_m] W_f^T + b_f in float64 (no rounding)."""
     X = np.concatenate(list(hiddens), axis=1)
@@ -108,14 +116,15 @@ def materialize(hiddens, W_f, b_f, W_K, W_V, n_kv_heads, head_dim, dtype, k_norm
 
 
 def paged_write(cache, rows, block_table, rows_per_seq, seq_start_pos, commit_lens=None):
-    """Write ``rows`` [T, Hkv, D] into ``cache`` [num_pages, 16, Hkv, D] in place.
+    """Write ``rows`` [T, Hkv, D] into ``cache`` [num_pages, Hkv, 16, D] in place.
 
     Row r belongs to request s = r // rows_per_seq at logical position
     seq_start_pos[s] + (r mod rows_per_seq).  It is written only if its index
     within the request is below commit_lens[s] (when given) and its logical
     page is mapped (block_table entry >= 0).  Returns a bool [num_pages, 16]
     marking the slots written."""
-    written = np.zeros(cache.shape[:2], dtype=bool)
+    sv = slots(cache)
+    written = np.zeros(sv.shape[:2], dtype=bool)
     T = rows.shape[0]
     for r in range(T):
         s, i = divmod(r, rows_per_seq)
@@ -125,7 +134,7 @@ def paged_write(cache, rows, block_table, rows_per_seq, seq_start_pos, commit_le
         page = int(block_table[s, pos // PAGE])
         if page < 0:
             continue
-        cache[page, pos % PAGE] = rows[r]
+        sv[page, pos % PAGE] = rows[r]
         written[page, pos % PAGE] = True
     return written
 
@@ -134,4 +143,4 @@ def gather_paged(cache, block_table_row, n):
     """Logical positions [0, n) of one request -> [n, Hkv, D]."""
     pos = np.arange(n)
     pages = block_table_row[pos // PAGE]
-    return cache[pages, pos % PAGE]
+    return slots(cache)[pages, pos % PAGE]

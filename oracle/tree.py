@@ -47,6 +47,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
+from .materialize import slots
 from .numerics import widen
 
 
@@ -184,7 +185,7 @@ def tree_attention(q, k_tree, v_tree, cache_k, cache_v, block_table, ctx_lens, n
         C = int(ctx_lens[b])
         pos = np.arange(C)
         pages = block_table[b, pos // 16]
-        ctx_k, ctx_v = ck[pages, pos % 16], cv[pages, pos % 16]
+        ctx_k, ctx_v = slots(ck)[pages, pos % 16], slots(cv)[pages, pos % 16]
         n = int(n_nodes[b])
         for r in (range(R) if rows is None else rows):
             seen = [0] if r == 0 or r - 1 >= n else [0] + [1 + y for y in _root_path(node_parent[b], r - 1)]

@@ -17,7 +17,7 @@ Conventions
 * Uniforms are ``int * 2**-24`` with ``int`` in ``[0, 2**24)``, so every value
   is exactly representable in float32 and lies in ``[0, 1)``.
 * Paged KV caches use pages of 16 token slots, shape
-  ``[num_pages, 16, n_kv_heads, head_dim]``; the physical page order is a
+  ``[num_pages, n_kv_heads, 16, head_dim]`` (head-major); the physical page order is a
   seeded random permutation, and ``block_table[seq, logical_page]`` maps a
   sequence's logical page to a physical page (``-1`` = unmapped).
 """
@@ -93,7 +93,7 @@ def page_table(rng, n_positions: Sequence[int], max_pages: Optional[int] = None,
 
 
 def empty_cache(num_pages, n_kv_heads, head_dim, dtype):
-    shape = (num_pages, PAGE, n_kv_heads, head_dim)
+    shape = (num_pages, n_kv_heads, PAGE, head_dim)
     if dtype == BF16:
         return np.full(shape, CACHE_SENTINEL_BF16, dtype=np.uint16)
     return np.full(shape, CACHE_SENTINEL_F32_BITS, dtype=np.uint32).view(np.float32)
@@ -189,7 +189,7 @@ class AttentionCase:
     q: np.ndarray            # [B, k, Hq, D]
     k_blk: np.ndarray        # [B, k, Hkv, D]
     v_blk: np.ndarray
-    cache_k: np.ndarray      # [num_pages, 16, Hkv, D]
+    cache_k: np.ndarray      # [num_pages, Hkv, 16, D]
     cache_v: np.ndarray
     block_table: np.ndarray  # [B, max_pages] int32
     ctx_lens: np.ndarray     # [B] int32
@@ -206,8 +206,8 @@ def attention_case(seed, *, dtype, B, k, n_q_heads, n_kv_heads, head_dim, ctx_le
     vb = _draw(rng, (B, k, n_kv_heads, head_dim), kv_std, dtype)
     bt, num_pages = page_table(rng, [int(c) for c in ctx_lens], max_pages=max_pages,
                                shuffle=shuffle)
-    ck = _draw(rng, (num_pages, PAGE, n_kv_heads, head_dim), kv_std, dtype)
-    cv = _draw(rng, (num_pages, PAGE, n_kv_heads, head_dim), kv_std, dtype)
+    ck = _draw(rng, (num_pages, n_kv_heads, PAGE, head_dim), kv_std, dtype)
+    cv = _draw(rng, (num_pages, n_kv_heads, PAGE, head_dim), kv_std, dtype)
     return AttentionCase(dtype, B, k, n_q_heads, n_kv_heads, head_dim, q, kb, vb, ck, cv,
                          bt, ctx_lens)
 
@@ -249,8 +249,8 @@ def packed_attention_case(seed, *, dtype=BF16, seq_len=8192, k=16, n_q_heads=32,
     vb = _draw(rng, (nb, k, n_kv_heads, head_dim), kv_std, dtype)
     bt1, num_pages = page_table(rng, [seq_len])
     bt = np.repeat(bt1, nb, axis=0)
-    ck = _draw(rng, (num_pages, PAGE, n_kv_heads, head_dim), kv_std, dtype)
-    cv = _draw(rng, (num_pages, PAGE, n_kv_heads, head_dim), kv_std, dtype)
+    ck = _draw(rng, (num_pages, n_kv_heads, PAGE, head_dim), kv_std, dtype)
+    cv = _draw(rng, (num_pages, n_kv_heads, PAGE, head_dim), kv_std, dtype)
     case = AttentionCase(dtype, nb, k, n_q_heads, n_kv_heads, head_dim, q, kb, vb, ck, cv,
                          np.ascontiguousarray(bt), anchors.copy())
     return case, P

@@ -54,9 +54,9 @@ def _check(c, ck, cv, h_out, rows=None, epi=None):
     sentinel = c.cache_k[0].reshape(-1).view(np.uint16 if c.dtype == "bf16" else np.uint32)[0]
     for l in range(c.n_layers):
         for name, gpu, rv in (("K", ck[l], ref["K"][l]), ("V", cv[l], ref["V"][l])):
-            g = down(gpu)
-            gb = bits(gpu)
-            written = np.zeros(gpu.shape[:2], dtype=bool)
+            g = oracle.slots(down(gpu))       # [num_pages, 16, Hkv, D] by page position
+            gb = oracle.slots(bits(gpu))
+            written = np.zeros(g.shape[:2], dtype=bool)
             got, want = [], []
             for i, r in enumerate(rows):
                 s, j = divmod(int(r), c.rows_per_seq)
@@ -146,7 +146,7 @@ def test_materialize_unmapped_and_out_of_range_pages_are_skipped():
     gb = bits(ck[0])
     sentinel = c.cache_k[0].reshape(-1)[0]
     written = 32  # 16 rows of seq 0 + 16 rows of seq 1
-    assert (gb != sentinel).reshape(gb.shape[0], 16, -1).any(-1).sum() == written
+    assert oracle.slots(gb != sentinel).any(axis=(2, 3)).sum() == written
 
 
 def test_materialize_is_deterministic():
@@ -183,8 +183,8 @@ def test_materialize_prefill_full_size_sampled():
     WV = [randn(Hkv * D, d, std=0.02) for _ in range(Ld)]
     maxp = rps // 16
     bt = torch.randperm(n_seq * maxp, generator=g, device=dev).to(torch.int32).view(n_seq, maxp)
-    ck = [torch.zeros(n_seq * maxp, 16, Hkv, D, dtype=bf, device=dev) for _ in range(Ld)]
-    cv = [torch.zeros(n_seq * maxp, 16, Hkv, D, dtype=bf, device=dev) for _ in range(Ld)]
+    ck = [torch.zeros(n_seq * maxp, Hkv, 16, D, dtype=bf, device=dev) for _ in range(Ld)]
+    cv = [torch.zeros(n_seq * maxp, Hkv, 16, D, dtype=bf, device=dev) for _ in range(Ld)]
     start = torch.zeros(n_seq, dtype=torch.int32, device=dev)
     dfl.materialize_ctx_kv(hid, Wf, bfv, WK, WV, ck, cv, bt.contiguous(), rps, start, None)
     torch.cuda.synchronize()
@@ -196,11 +196,12 @@ def test_materialize_prefill_full_size_sampled():
     ref = oracle.materialize([bits(h.index_select(0, ridx)) for h in hid], bits(Wf), bits(bfv),
                              [bits(w) for w in WK], [bits(w) for w in WV], Hkv, D, "bf16")
     btn = bt.cpu().numpy()
-    slots = torch.tensor([int(btn[r // rps, (r % rps) // 16]) * 16 + r % 16 for r in rows],
-                         dtype=torch.int64, device=dev)
+    sidx = torch.tensor([int(btn[r // rps, (r % rps) // 16]) * 16 + r % 16 for r in rows],
+                        dtype=torch.int64, device=dev)
     for l in range(Ld):
         for name, cache, rv in (("K", ck[l], ref["K"][l]), ("V", cv[l], ref["V"][l])):
-            got = down(cache.view(-1, Hkv, D).index_select(0, slots))
+            by_slot = cache.transpose(1, 2).reshape(-1, Hkv, D)   # head-major -> slot order
+            got = down(by_slot.index_select(0, sidx))
             e = rel_err(got, rv)
             assert e <= TOL["bf16"], (l, name, e)
     log(f"  {len(rows)} rows x {Ld} layers x K/V within {TOL['bf16']}")

@@ -463,7 +463,7 @@ def test_tree_commit_kv_parity(dtype, seed):
     for l in range(Ld):
         ktree = synth.attention_case(seed + 10 + l, dtype=dtype, B=B, k=budget + 1, n_q_heads=Hkv,
                                      n_kv_heads=Hkv, head_dim=D, ctx_lens=[0] * B)
-        sent = np.full((n_pages, 16, Hkv, D), 0x7FA1 if dtype == "bf16" else np.nan,
+        sent = np.full((n_pages, Hkv, 16, D), 0x7FA1 if dtype == "bf16" else np.nan,
                        dtype=np.uint16 if dtype == "bf16" else np.float32)
         rk, rv = sent.copy(), sent.copy()
         oracle.commit_tree_kv(ktree.k_blk, ktree.v_blk, path, acc, prefix, rk, rv, bt)

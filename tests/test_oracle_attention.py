@@ -87,8 +87,9 @@ def test_closed_form_zero_query_is_mean_of_values():
 
 def test_identical_keys_give_mean_of_values():
     c = _case(8, ctx=(5, 12, 2))
-    c.cache_k[:] = c.cache_k[0, 0, :, :][None, None]
-    c.k_blk[:] = c.cache_k[0, 0][None, None]
+    key = oracle.slots(c.cache_k)[0, 0].copy()        # [Hkv, D]: page 0, position 0
+    c.cache_k[:] = key[None, :, None, :]               # every position of every page
+    c.k_blk[:] = key[None, None]
     out, _ = _run(c)
     v = oracle.widen(c.v_blk, "f32"); cv = oracle.widen(c.cache_v, "f32")
     G = c.n_q_heads // c.n_kv_heads

@@ -89,7 +89,7 @@ def test_paged_commit_masked_write_and_gather():
                                commit=[5, 2, 0])
     res = oracle.materialize(c.hiddens, c.W_f, c.b_f, c.W_K, c.W_V, 2, 4, "f32")
     cache = oracle.widen(c.cache_k[0], "f32")
-    before = c.cache_k[0].view(np.uint32).copy()
+    before = oracle.slots(c.cache_k[0].view(np.uint32).copy())
     written = oracle.paged_write(cache, res["K"][0], c.block_table, 5, c.seq_start_pos,
                                  c.commit_lens)
     assert written.sum() == 5 + 2 + 0
@@ -99,7 +99,7 @@ def test_paged_commit_masked_write_and_gather():
         got = oracle.gather_paged(cache, c.block_table[s], start + n)[start:]
         np.testing.assert_array_equal(got, res["K"][0][s * 5: s * 5 + n])
     # untouched slots keep the sentinel bits
-    after = cache.astype(np.float32).view(np.uint32)
+    after = oracle.slots(cache.astype(np.float32).view(np.uint32))
     np.testing.assert_array_equal(after[~written], before[~written])
 
 

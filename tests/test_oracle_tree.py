@@ -240,13 +240,13 @@ def test_commit_tree_kv_hand_example():
     for r in range(R):
         kt[:, r] = 10 * np.arange(2)[:, None, None] + r
     vt = -kt
-    ck = np.full((4, 16, Hkv, D), 7e3, dtype=np.float32)
+    ck = np.full((4, Hkv, 16, D), 7e3, dtype=np.float32)     # head-major pages
     cv = ck.copy()
     bt = np.array([[2, 0], [1, -1]], dtype=np.int32)       # request 1's second page unmapped
     acc_nodes = np.array([[1, 3, -1], [0, 1, 2]])
     written = oracle.commit_tree_kv(kt, vt, acc_nodes, [2, -1], [14, 3], ck, cv, bt)
     # request 0: positions 14, 15 on page 2, position 16 on page 0 slot 0
-    assert ck[2, 14, 0, 0] == 0 and ck[2, 15, 0, 0] == 2 and ck[0, 0, 0, 0] == 4
+    assert ck[2, 0, 14, 0] == 0 and ck[2, 0, 15, 0] == 2 and ck[0, 0, 0, 0] == 4
     assert cv[0, 0, 0, 0] == -4
     assert written.sum() == 3
     assert np.all(ck[1] == 7e3) and np.all(ck[3] == 7e3)
