@@ -180,12 +180,13 @@ def _cache_pair(ck, cv, Hkv, D):
     (head-major) on the device with the same shape; returns (num_pages,
     page_size)."""
     for name, t in (("cache_k", ck), ("cache_v", cv)):
-        _dev(t, name)
         if t.dim() != 4 or t.shape[1] != Hkv or t.shape[3] != D:
             raise ValueError(f"{name} must be [num_pages, {Hkv}, page_size, {D}] (head-major), "
                              f"got {tuple(t.shape)}")
     if ck.shape != cv.shape:
         raise ValueError(f"cache_k {tuple(ck.shape)} and cache_v {tuple(cv.shape)} differ")
+    _dev(ck, "cache_k")
+    _dev(cv, "cache_v")
     return ck.shape[0], ck.shape[2]
 
 

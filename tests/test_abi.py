@@ -301,3 +301,19 @@ def test_draft_head_and_embed_argument_errors(lib):
     assert lib.dflash_embed(4, 100, 10, FAKE, FAKE, FAKE, dfl.BF16, None) == dfl.E_UNSUPPORTED
     assert lib.dflash_embed(4, 128, 10, None, FAKE, FAKE, dfl.BF16, None) == dfl.E_ARG
     assert lib.dflash_embed(0, 128, 10, None, None, None, dfl.BF16, None) == dfl.OK
+
+
+def test_binding_rejects_caches_not_in_head_major_layout():
+    """The paged cache is [num_pages, Hkv, 16, D]; the binding checks each
+    cache against the call's Hkv and D (and K against V) before any pointer
+    crosses the ABI.  Shape checks come first, so CPU tensors reach them."""
+    import torch
+    Hkv, D = 8, 128
+    good = torch.empty(4, Hkv, 16, D, dtype=torch.bfloat16)
+    pos_major = torch.empty(4, 16, Hkv, D, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="head-major"):
+        dfl._cache_pair(pos_major, pos_major, Hkv, D)
+    with pytest.raises(ValueError, match="differ"):
+        dfl._cache_pair(good, torch.empty(5, Hkv, 16, D, dtype=torch.bfloat16), Hkv, D)
+    with pytest.raises(ValueError, match="device tensor"):
+        dfl._cache_pair(good, good, Hkv, D)   # right shape, but host memory
