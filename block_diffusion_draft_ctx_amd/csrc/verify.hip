@@ -152,29 +152,44 @@ __global__ __launch_bounds__(kThreads) void k_row_argmax(RowSet s0, RowSet s1, i
   }
 }
 
-__device__ int reduce_argmax_row(const float* pmax, const int* pidx, int row, int nc) {
+// Argmax of one row from its chunk partials, by a group of G lanes (G = 1, 2
+// or 4, aligned within the wavefront, nc <= 16 G): lane `sub` of the group
+// loads chunks sub, sub + G, ... together, merges them, and the group merges
+// its lanes by shuffles.  The merge is a total order (value, then lower
+// index; a NaN never wins), so the winner does not depend on the grouping.
+// Every lane of the wavefront must call this (the shuffles); lanes with
+// valid == false contribute nothing.  An all -inf row: every entry ties and
+// the first wins; no entry at all gives 0.
+__device__ int group_argmax_row(const float* pmax, const int* pidx, int row, int nc, int G,
+                                int sub, bool valid) {
   float best = neg_inf();
   int bi = INT_MAX;
-  // the chunk partials load 16 at a time (clamped indices, the repeats
-  // skipped) before they merge, so the loads are in flight together; the
-  // merge is a total order (value, then lower index), so the winner does
-  // not depend on the grouping
-  for (int c0 = 0; c0 < nc; c0 += 16) {
+  if (valid) {
     float v[16];
     int ix[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int c = min(c0 + j, nc - 1);
+      const int c = min(sub + G * j, nc - 1);
       v[j] = pmax[row * nc + c];
       ix[j] = pidx[row * nc + c];
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-      if (c0 + j < nc) am_merge(best, bi, v[j], ix[j]);
+      if (sub + G * j < nc) am_merge(best, bi, v[j], ix[j]);
   }
-  return bi == INT_MAX ? 0 : bi;  // an all -inf row: every entry ties, the first wins
+  for (int o = 1; o < G; o <<= 1) {
+    const float ob = __shfl_xor(best, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    am_merge(best, bi, ob, oi);
+  }
+  return bi == INT_MAX ? 0 : bi;
 }
 
+// Greedy acceptance of request b: the argmax of every target row of the
+// chain (and, with fused draft logits, of every draft row) from the chunk
+// partials, then matches -> cumulative product -> accept_len and the bonus.
+// The rows' merges run on groups of lanes, so a request whose rows have many
+// chunk partials (small batches) reads them in one round of loads.
 __global__ __launch_bounds__(128) void k_greedy_finalize(
     int B, int L, int V, int nc, const float* __restrict__ pmax, const int* __restrict__ pidx,
     int have_dl, int32_t* __restrict__ draft_tokens, const int32_t* __restrict__ lens,
@@ -187,25 +202,26 @@ __global__ __launch_bounds__(128) void k_greedy_finalize(
   __shared__ int dt[64];
   bool bad;
   const int nb = chain_of(lens, b, L, &bad);
-  if (t <= L) {
-    int v = -1;
-    if (t <= nb) v = reduce_argmax_row(pmax, pidx, b * (L + 1) + t, nc);
-    tp[t] = v;
-    if (target_predict) target_predict[b * (L + 1) + t] = v;
-  }
-  if (t < L) {
-    int v = -1;
-    if (have_dl) {
-      if (t < nb) {
-        v = reduce_argmax_row(pmax, pidx, B * (L + 1) + b * L + t, nc);
-        draft_tokens[b * L + t] = v;
-      }
-    } else {
-      v = draft_tokens[b * L + t];
+  if (t <= L) tp[t] = -1;
+  if (t < L) dt[t] = have_dl ? -1 : draft_tokens[b * L + t];
+  __syncthreads();
+  // rows r <= nb: target row r; rows nb < r <= 2 nb (with draft logits):
+  // draft row r - nb - 1
+  const int G = nc > 32 ? 4 : (nc > 16 ? 2 : 1);
+  const int R = nb + 1 + (have_dl ? nb : 0);
+  for (int r0 = 0; r0 < R; r0 += 128 / G) {
+    const int r = r0 + t / G;
+    const bool valid = r < R;
+    const int row = r <= nb ? b * (L + 1) + r : B * (L + 1) + b * L + (r - nb - 1);
+    const int v = group_argmax_row(pmax, pidx, valid ? row : 0, nc, G, t % G, valid);
+    if (valid && t % G == 0) {
+      if (r <= nb) tp[r] = v;
+      else dt[r - nb - 1] = v;
     }
-    dt[t] = v;
   }
   __syncthreads();
+  if (t <= L && target_predict) target_predict[b * (L + 1) + t] = tp[t];
+  if (have_dl && t < nb) draft_tokens[b * L + t] = dt[t];
   if (t == 0) {
     bool err = bad;
     for (int i = 0; i < nb; ++i) err |= (dt[i] < 0 || dt[i] >= V);
