@@ -552,17 +552,37 @@ __global__ __launch_bounds__(128) void k_attn_combine(int B, int k, int Hq, int 
   const int bg = blockIdx.x / Mq;
   const int b = bg / Hkv, g = bg - b * Hkv;
   const int64_t base = (int64_t)bg * S * Mq + qrow;
+  // the splits' partials load 8 at a time at clamped (valid) indices, so each
+  // group's loads are in flight together; they merge in split order
+  constexpr int SB = 8;
   float M = neg_inf();
-  for (int s = 0; s < S; ++s) M = fmaxf(M, pml[base + (int64_t)s * Mq].x);
+  for (int s0 = 0; s0 < S; s0 += SB) {
+    float mx[SB];
+#pragma unroll
+    for (int j = 0; j < SB; ++j) mx[j] = pml[base + (int64_t)min(s0 + j, S - 1) * Mq].x;
+#pragma unroll
+    for (int j = 0; j < SB; ++j)
+      if (s0 + j < S) M = fmaxf(M, mx[j]);
+  }
   const int hg = qrow / k, pos = qrow - hg * k, h = g * G + hg;
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
     float Ls = 0.f, O = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float2 ml = pml[base + (int64_t)s * Mq];
-      if (ml.x == neg_inf() && ml.y == 0.f) continue;  // an empty split
-      const float wgt = exp2f(ml.x - M);
-      Ls += ml.y * wgt;
-      O += po[(base + (int64_t)s * Mq) * D + d] * wgt;
+    for (int s0 = 0; s0 < S; s0 += SB) {
+      float2 ml[SB];
+      float ov[SB];
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        const int64_t r = base + (int64_t)min(s0 + j, S - 1) * Mq;
+        ml[j] = pml[r];
+        ov[j] = po[r * D + d];
+      }
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        if (s0 + j >= S || (ml[j].x == neg_inf() && ml[j].y == 0.f)) continue;  // past S, or an empty split
+        const float wgt = exp2f(ml[j].x - M);
+        Ls += ml[j].y * wgt;
+        O += ov[j] * wgt;
+      }
     }
     const float v = O / Ls;
     const int64_t oi = (((int64_t)b * k + pos) * Hq + h) * D + d;
