@@ -692,8 +692,12 @@ void dispatch_nw(const AttnArgs& a, AttnP p, hipStream_t st) {
   // per group.  Where the work is MFMA-bound the context comes from L2 and
   // the infinity cache, and rows per workgroup is what divides that traffic.
   if (DFLASH_ATTN_PAIR && a.shared_table && a.mode != kMaskTree && a.B > 1 && 2 * rows <= 128) {
-    if (DFLASH_ATTN_WIDE && a.B > 2 && 4 * rows <= 256 && 2 * rows > 64) launch_bf16<D, 8, 4>(a, p, st);
-    else if (2 * rows <= 64) launch_bf16<D, 2, 2>(a, p, st);
+    // (the sixteen-wavefront variants are compiled only when enabled: at
+    // the 128 VGPRs they allow they spill)
+    if constexpr (DFLASH_ATTN_WIDE != 0) {
+      if (a.B > 2 && 4 * rows <= 256 && 2 * rows > 64) { launch_bf16<D, 8, 4>(a, p, st); return; }
+    }
+    if (2 * rows <= 64) launch_bf16<D, 2, 2>(a, p, st);
     else launch_bf16<D, 4, 2>(a, p, st);
     return;
   }
@@ -705,8 +709,10 @@ void dispatch_nw(const AttnArgs& a, AttnP p, hipStream_t st) {
   else if (nq <= 2) launch_bf16<D, 2, 1>(a, p, st);
   else {
     p.RC = attention_row_chunks(a.Hq / a.Hkv, a.k);
-    if (DFLASH_ATTN_WIDE && nq > 8) launch_bf16<D, 8, 1>(a, p, st);
-    else launch_bf16<D, 4, 1>(a, p, st);
+    if constexpr (DFLASH_ATTN_WIDE != 0) {
+      if (nq > 8) { launch_bf16<D, 8, 1>(a, p, st); return; }
+    }
+    launch_bf16<D, 4, 1>(a, p, st);
   }
 }
 
