@@ -52,6 +52,16 @@ constexpr int BK = 64;   // granularity of split-K chunks (a multiple of the pip
 #ifndef DFLASH_GEMM_WGS
 #define DFLASH_GEMM_WGS 512
 #endif
+// Few-row products (at most DFLASH_GEMM_SKINNY_M rows: a decode batch of one
+// or two blocks, the drafter at batch 1) stream their weights: 32 x 256 tiles
+// with four stages keep about three times the bytes in flight of a 128 x 128
+// tile, split over the contraction toward DFLASH_GEMM_SKINNY_WGS workgroups.
+#ifndef DFLASH_GEMM_SKINNY_M
+#define DFLASH_GEMM_SKINNY_M 32
+#endif
+#ifndef DFLASH_GEMM_SKINNY_WGS
+#define DFLASH_GEMM_SKINNY_WGS 256
+#endif
 // Pipeline shape (contraction columns per step, stages) for the 256 x 256
 // tile and for the smaller tiles.
 #ifndef DFLASH_GEMM_KB_BIG
@@ -400,8 +410,7 @@ __global__ __launch_bounds__(64 * WM_ * WN_) void k_gemm_bf16(GemmP p) {
   // the first ones (with two stages the loads need the rest of the step to
   // land)
   constexpr int SPREAD = NSTG_ == 2 ? (SS - 1 < DFLASH_GEMM_SPREAD2 ? SS - 1 : DFLASH_GEMM_SPREAD2) : SS - 1;
-  constexpr int SLOTS = SPREAD * MF;
-  static_assert(DMA_PER_STEP <= SLOTS, "DMA issue slots");
+  constexpr int SLOTS = SPREAD * MF;   // (with more DMA instructions than slots, several share one)
 
   for (int s = 0; s < NSTG_ - 1 && s < nk; ++s) issue(s);
   if (nk > 0) {
@@ -803,6 +812,12 @@ Plan plan_gemm(int64_t M, int64_t N, int64_t K, bool bf16) {
   //  * unsplit when at least DFLASH_GEMM_BIG_UNSPLIT_MIN tiles exist;
   //  * else 128-row tiles, the contraction split until about
   //    DFLASH_GEMM_WGS workgroups exist.
+  if (M <= DFLASH_GEMM_SKINNY_M && N % 256 == 0) {
+    const int64_t tiles = N / 256;
+    int64_t ks = std::min<int64_t>(cdiv(DFLASH_GEMM_SKINNY_WGS, tiles), std::max<int64_t>(1, K / (4 * BK)));
+    const int64_t kchunk = cdiv(cdiv(K, std::max<int64_t>(ks, 1)), BK) * BK;
+    return Plan{32, 256, (int)cdiv(K, kchunk), (int)kchunk};
+  }
   constexpr int64_t kCUs = DFLASH_GEMM_BIG_MIN_TILES;
   const int64_t t256 = N % 256 == 0 ? cdiv(M, 256) * (N / 256) : 0;
   const bool split_ok = t256 > 0 && K / cdiv(kCUs, t256) >= DFLASH_GEMM_SPLIT_MIN_K;
@@ -839,6 +854,8 @@ void run_gemm(bool bf16, GemmP p, int epi_final, hipStream_t st) {
     const dim3 grid((unsigned)(cdiv(p.M, pl.bm) * (p.N / pl.bn)), (unsigned)pl.ksplit);
     if (pl.bm == 256 && pl.bn == 256)
       launch_bf16_gemm<256, 256, DFLASH_GEMM_BIG_WM, DFLASH_GEMM_BIG_WN, DFLASH_GEMM_KB_BIG, DFLASH_GEMM_NSTG_BIG>(p, epi, grid, st);
+    else if (pl.bm == 32)
+      launch_bf16_gemm<32, 256, 1, 4, 64, 4>(p, epi, grid, st);
     else if (pl.bm == 256)
       launch_bf16_gemm<256, 128, 2, 2, DFLASH_GEMM_KB_SMALL, DFLASH_GEMM_NSTG_SMALL>(p, epi, grid, st);
     else

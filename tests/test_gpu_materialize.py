@@ -88,6 +88,8 @@ def _check(c, ck, cv, h_out, rows=None, epi=None):
     ("bf16", 5, 256, 2, 2, 64, 3, 16, None, "random", 2401),
     ("bf16", 2, 384, 3, 1, 128, 2, 40, [3, 0], [40, 17], 2402),  # rows straddle pages
     ("bf16", 5, 4096, 5, 8, 128, 8, 16, None, "random", 2403),   # Llama-shaped decode, B = 8
+    ("bf16", 5, 4096, 5, 8, 128, 1, 16, [8192], "random", 2404),  # B = 1: the 32-row tile plan
+    ("bf16", 5, 4096, 5, 8, 128, 2, 16, [1000, 77], [16, 3], 2405),  # B = 2: 32 rows, split-K
 ])
 def test_materialize_parity(dtype, m, d, Ld, Hkv, D, n_seq, rps, start, commit, seed):
     log(f"materialise dtype={dtype} m={m} d={d} layers={Ld} Hkv={Hkv} D={D} rows={n_seq}x{rps}")
