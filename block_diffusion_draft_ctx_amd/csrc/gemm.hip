@@ -57,7 +57,7 @@ constexpr int BK = 64;   // granularity of split-K chunks (a multiple of the pip
 // with four stages keep about three times the bytes in flight of a 128 x 128
 // tile, split over the contraction toward DFLASH_GEMM_SKINNY_WGS workgroups.
 #ifndef DFLASH_GEMM_SKINNY_M
-#define DFLASH_GEMM_SKINNY_M 32
+#define DFLASH_GEMM_SKINNY_M 128
 #endif
 #ifndef DFLASH_GEMM_SKINNY_WGS
 #define DFLASH_GEMM_SKINNY_WGS 256
@@ -795,7 +795,11 @@ struct Plan {
   int ksplit, kchunk;
 };
 
-Plan plan_gemm(int64_t M, int64_t N, int64_t K, bool bf16) {
+// col_block: the width of the column blocks no tile may straddle (the K/V
+// GEMM's Hkv*D-wide blocks, one per layer and K or V, each with its own
+// weight matrix and cache), or 0 for a dense product.  256-wide tiles need
+// it to be a multiple of 256; 128 always divides it.
+Plan plan_gemm(int64_t M, int64_t N, int64_t K, bool bf16, int64_t col_block) {
   if (!bf16) {
     const int64_t tiles = cdiv(M, 64) * cdiv(N, 64);
     int64_t ks = 1;
@@ -812,14 +816,16 @@ Plan plan_gemm(int64_t M, int64_t N, int64_t K, bool bf16) {
   //  * unsplit when at least DFLASH_GEMM_BIG_UNSPLIT_MIN tiles exist;
   //  * else 128-row tiles, the contraction split until about
   //    DFLASH_GEMM_WGS workgroups exist.
-  if (M <= DFLASH_GEMM_SKINNY_M && N % 256 == 0) {
-    const int64_t tiles = N / 256;
+  const bool w256 = N % 256 == 0 && col_block % 256 == 0;
+  if (M <= DFLASH_GEMM_SKINNY_M && w256) {
+    const int bm = M <= 32 ? 32 : (M <= 64 ? 64 : 128);
+    const int64_t tiles = cdiv(M, bm) * (N / 256);
     int64_t ks = std::min<int64_t>(cdiv(DFLASH_GEMM_SKINNY_WGS, tiles), std::max<int64_t>(1, K / (4 * BK)));
     const int64_t kchunk = cdiv(cdiv(K, std::max<int64_t>(ks, 1)), BK) * BK;
-    return Plan{32, 256, (int)cdiv(K, kchunk), (int)kchunk};
+    return Plan{bm, 256, (int)cdiv(K, kchunk), (int)kchunk};
   }
   constexpr int64_t kCUs = DFLASH_GEMM_BIG_MIN_TILES;
-  const int64_t t256 = N % 256 == 0 ? cdiv(M, 256) * (N / 256) : 0;
+  const int64_t t256 = w256 ? cdiv(M, 256) * (N / 256) : 0;
   const bool split_ok = t256 > 0 && K / cdiv(kCUs, t256) >= DFLASH_GEMM_SPLIT_MIN_K;
   if (split_ok || t256 >= DFLASH_GEMM_BIG_UNSPLIT_MIN) {
     const int64_t ks0 = split_ok ? cdiv(kCUs, t256) : 1;
@@ -846,7 +852,7 @@ void launch_bf16_gemm(GemmP p, int epi, dim3 grid, hipStream_t st) {
 }
 
 void run_gemm(bool bf16, GemmP p, int epi_final, hipStream_t st) {
-  const Plan pl = plan_gemm(p.M, p.N, p.K, bf16);
+  const Plan pl = plan_gemm(p.M, p.N, p.K, bf16, p.b_layered ? p.HD : 0);
   p.ksplit = pl.ksplit;
   p.kchunk = pl.kchunk;
   const int epi = pl.ksplit > 1 ? EPI_PARTIAL : epi_final;
@@ -856,6 +862,10 @@ void run_gemm(bool bf16, GemmP p, int epi_final, hipStream_t st) {
       launch_bf16_gemm<256, 256, DFLASH_GEMM_BIG_WM, DFLASH_GEMM_BIG_WN, DFLASH_GEMM_KB_BIG, DFLASH_GEMM_NSTG_BIG>(p, epi, grid, st);
     else if (pl.bm == 32)
       launch_bf16_gemm<32, 256, 1, 4, 64, 4>(p, epi, grid, st);
+    else if (pl.bm == 64)
+      launch_bf16_gemm<64, 256, 1, 4, 64, 3>(p, epi, grid, st);
+    else if (pl.bm == 128 && pl.bn == 256)
+      launch_bf16_gemm<128, 256, 2, 2, 64, 3>(p, epi, grid, st);
     else if (pl.bm == 256)
       launch_bf16_gemm<256, 128, 2, 2, DFLASH_GEMM_KB_SMALL, DFLASH_GEMM_NSTG_SMALL>(p, epi, grid, st);
     else
@@ -879,8 +889,8 @@ void run_gemm(bool bf16, GemmP p, int epi_final, hipStream_t st) {
   }
 }
 
-size_t partial_bytes(int64_t M, int64_t N, int64_t K, bool bf16) {
-  const Plan pl = plan_gemm(M, N, K, bf16);
+size_t partial_bytes(int64_t M, int64_t N, int64_t K, bool bf16, int64_t col_block = 0) {
+  const Plan pl = plan_gemm(M, N, K, bf16, col_block);
   return pl.ksplit > 1 ? align256(sizeof(float) * pl.ksplit * M * N) : 0;
 }
 
@@ -922,7 +932,12 @@ size_t materialize_ws_bytes(int64_t T, int m, int d, int n_layers, int Hkv, int 
   const int64_t es = bf16 ? 2 : 4;
   const size_t h = align256((size_t)(T * d * es));
   const size_t p1 = partial_bytes(T, d, (int64_t)m * d, bf16);
-  const size_t p2 = partial_bytes(T, 2LL * std::min(n_layers, kML) * Hkv * D, d, bf16);
+  // the K/V GEMM runs in groups of up to kML layers: size for every group
+  // width that occurs (a narrower last group may plan more splits)
+  const int64_t HD = (int64_t)Hkv * D;
+  size_t p2 = partial_bytes(T, 2LL * std::min(n_layers, kML) * HD, d, bf16, HD);
+  if (n_layers > kML && n_layers % kML)
+    p2 = std::max(p2, partial_bytes(T, 2LL * (n_layers % kML) * HD, d, bf16, HD));
   return h + std::max(p1, p2);
 }
 

@@ -90,6 +90,9 @@ def _check(c, ck, cv, h_out, rows=None, epi=None):
     ("bf16", 5, 4096, 5, 8, 128, 8, 16, None, "random", 2403),   # Llama-shaped decode, B = 8
     ("bf16", 5, 4096, 5, 8, 128, 1, 16, [8192], "random", 2404),  # B = 1: the 32-row tile plan
     ("bf16", 5, 4096, 5, 8, 128, 2, 16, [1000, 77], [16, 3], 2405),  # B = 2: 32 rows, split-K
+    # Hkv*D = 128: no tile may straddle a layer's K and V blocks (256-wide tiles are not allowed)
+    ("bf16", 5, 256, 5, 2, 64, 4, 2048, None, None, 2406),       # prefill-sized T = 8192
+    ("bf16", 2, 128, 17, 2, 64, 2, 16, [0, 40], "random", 2407),  # 17 layers: two layer groups
 ])
 def test_materialize_parity(dtype, m, d, Ld, Hkv, D, n_seq, rps, start, commit, seed):
     log(f"materialise dtype={dtype} m={m} d={d} layers={Ld} Hkv={Hkv} D={D} rows={n_seq}x{rps}")
