@@ -55,6 +55,9 @@ def _oracle_layer(c, w, x, k, Hq, rope_theta, causal, rows=None):
     ("bf16", 3, 16, 256, 4, 2, 64, 384, [100, 0, 33], 1e6, False, True, 5103),
     ("bf16", 2, 16, 256, 4, 2, 64, 384, [500, 17], 1e6, True, True, 5104),
     ("bf16", 2, 16, 4096, 32, 8, 128, 12288, [300, 1000], 1e6, False, True, 5105),  # Qwen3-8B-shaped
+    # 64 and 128 block rows: the few-row GEMM tiles with the residual epilogue
+    ("bf16", 4, 16, 512, 8, 4, 64, 1536, [64, 0, 200, 31], 1e6, False, True, 5106),
+    ("bf16", 8, 16, 512, 8, 4, 64, 1536, [16 * i + 5 for i in range(8)], 1e6, True, True, 5107),
 ])
 def test_draft_layer_parity(dtype, B, k, d, Hq, Hkv, D, I, ctx, theta, causal, qkn, seed):
     log(f"draft_layer dtype={dtype} B={B} k={k} d={d} heads={Hq}/{Hkv}x{D} I={I} ctx={ctx} "
