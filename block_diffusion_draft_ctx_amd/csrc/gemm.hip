@@ -52,10 +52,11 @@ constexpr int BK = 64;   // granularity of split-K chunks (a multiple of the pip
 #ifndef DFLASH_GEMM_WGS
 #define DFLASH_GEMM_WGS 512
 #endif
-// Few-row products (at most DFLASH_GEMM_SKINNY_M rows: a decode batch of one
-// or two blocks, the drafter at batch 1) stream their weights: 32 x 256 tiles
-// with four stages keep about three times the bytes in flight of a 128 x 128
-// tile, split over the contraction toward DFLASH_GEMM_SKINNY_WGS workgroups.
+// Few-row products (at most DFLASH_GEMM_SKINNY_M rows: decode and the
+// drafter at up to eight blocks of 16) stream their weights: BM x 256 tiles
+// (BM = 32, 64 or 128, four wavefronts) keep more weight bytes in flight per
+// CU than 128 x 128 tiles, split over the contraction toward
+// DFLASH_GEMM_SKINNY_WGS workgroups.
 #ifndef DFLASH_GEMM_SKINNY_M
 #define DFLASH_GEMM_SKINNY_M 128
 #endif
