@@ -821,8 +821,22 @@ Plan plan_gemm(int64_t M, int64_t N, int64_t K, bool bf16, int64_t col_block) {
   if (M <= DFLASH_GEMM_SKINNY_M && w256) {
     const int bm = M <= 32 ? 32 : (M <= 64 ? 64 : 128);
     const int64_t tiles = cdiv(M, bm) * (N / 256);
-    int64_t ks = std::min<int64_t>(cdiv(DFLASH_GEMM_SKINNY_WGS, tiles), std::max<int64_t>(1, K / (4 * BK)));
-    const int64_t kchunk = cdiv(cdiv(K, std::max<int64_t>(ks, 1)), BK) * BK;
+    // These tiles run one workgroup per CU, in rounds of
+    // DFLASH_GEMM_SKINNY_WGS.  Cost of k splits, in bytes per CU: each round
+    // streams one tile's weights over K / k columns (512 K / k bytes), and
+    // the fp32 partials are written and read back (8 k M N bytes over the
+    // CUs).  The cheapest count wins, the fewest splits on a tie; no split is
+    // shorter than 4 steps.
+    const int64_t ks_max = std::max<int64_t>(1, K / (4 * BK));
+    const int64_t W = DFLASH_GEMM_SKINNY_WGS;
+    int64_t ks = 1;
+    double best = (double)cdiv(tiles, W) * 512.0 * (double)K;
+    for (int64_t k = 2; k <= ks_max; ++k) {
+      const double cost = (double)cdiv(tiles * k, W) * 512.0 * (double)K / (double)k +
+                          8.0 * (double)k * (double)M * (double)N / (double)W;
+      if (cost < best) { best = cost; ks = k; }
+    }
+    const int64_t kchunk = cdiv(cdiv(K, ks), BK) * BK;
     return Plan{bm, 256, (int)cdiv(K, kchunk), (int)kchunk};
   }
   constexpr int64_t kCUs = DFLASH_GEMM_BIG_MIN_TILES;
