@@ -60,6 +60,11 @@ constexpr int BK = 64;   // granularity of split-K chunks (a multiple of the pip
 #ifndef DFLASH_GEMM_SKINNY_M
 #define DFLASH_GEMM_SKINNY_M 128
 #endif
+// The 128 x 128 plan picks its split count with the same cost model (1) or
+// aims at DFLASH_GEMM_WGS workgroups (0).
+#ifndef DFLASH_GEMM_SMALL_COST
+#define DFLASH_GEMM_SMALL_COST 1
+#endif
 #ifndef DFLASH_GEMM_SKINNY_WGS
 #define DFLASH_GEMM_SKINNY_WGS 256
 #endif
@@ -800,6 +805,24 @@ struct Plan {
 // GEMM's Hkv*D-wide blocks, one per layer and K or V, each with its own
 // weight matrix and cache), or 0 for a dense product.  256-wide tiles need
 // it to be a multiple of 256; 128 always divides it.
+// Split count for tiles that run one workgroup per CU, in rounds of W.
+// Cost of k splits, in bytes per CU: each round streams one tile's operands
+// over K / k columns (512 K / k bytes for 256 operand rows), and the fp32
+// partials are written and read back (8 k M N bytes over the CUs).  The
+// cheapest count wins, the fewest splits on a tie; no split is shorter than
+// 4 steps.
+int64_t pick_splits(int64_t tiles, int64_t M, int64_t N, int64_t K, int64_t W) {
+  const int64_t ks_max = std::max<int64_t>(1, K / (4 * BK));
+  int64_t ks = 1;
+  double best = (double)cdiv(tiles, W) * 512.0 * (double)K;
+  for (int64_t k = 2; k <= ks_max; ++k) {
+    const double cost = (double)cdiv(tiles * k, W) * 512.0 * (double)K / (double)k +
+                        8.0 * (double)k * (double)M * (double)N / (double)W;
+    if (cost < best) { best = cost; ks = k; }
+  }
+  return ks;
+}
+
 Plan plan_gemm(int64_t M, int64_t N, int64_t K, bool bf16, int64_t col_block) {
   if (!bf16) {
     const int64_t tiles = cdiv(M, 64) * cdiv(N, 64);
@@ -821,21 +844,7 @@ Plan plan_gemm(int64_t M, int64_t N, int64_t K, bool bf16, int64_t col_block) {
   if (M <= DFLASH_GEMM_SKINNY_M && w256) {
     const int bm = M <= 32 ? 32 : (M <= 64 ? 64 : 128);
     const int64_t tiles = cdiv(M, bm) * (N / 256);
-    // These tiles run one workgroup per CU, in rounds of
-    // DFLASH_GEMM_SKINNY_WGS.  Cost of k splits, in bytes per CU: each round
-    // streams one tile's weights over K / k columns (512 K / k bytes), and
-    // the fp32 partials are written and read back (8 k M N bytes over the
-    // CUs).  The cheapest count wins, the fewest splits on a tie; no split is
-    // shorter than 4 steps.
-    const int64_t ks_max = std::max<int64_t>(1, K / (4 * BK));
-    const int64_t W = DFLASH_GEMM_SKINNY_WGS;
-    int64_t ks = 1;
-    double best = (double)cdiv(tiles, W) * 512.0 * (double)K;
-    for (int64_t k = 2; k <= ks_max; ++k) {
-      const double cost = (double)cdiv(tiles * k, W) * 512.0 * (double)K / (double)k +
-                          8.0 * (double)k * (double)M * (double)N / (double)W;
-      if (cost < best) { best = cost; ks = k; }
-    }
+    const int64_t ks = pick_splits(tiles, M, N, K, DFLASH_GEMM_SKINNY_WGS);
     const int64_t kchunk = cdiv(cdiv(K, ks), BK) * BK;
     return Plan{bm, 256, (int)cdiv(K, kchunk), (int)kchunk};
   }
@@ -850,7 +859,9 @@ Plan plan_gemm(int64_t M, int64_t N, int64_t K, bool bf16, int64_t col_block) {
   const int bm = DFLASH_GEMM_SMALL_BM, bn = 128;
   const int64_t tiles = cdiv(M, bm) * (N / bn);
   int64_t ks = 1;
-  if (tiles < DFLASH_GEMM_WGS)
+  if (DFLASH_GEMM_SMALL_COST)   // one workgroup per CU: the same cost model
+    ks = pick_splits(tiles, M, N, K, DFLASH_GEMM_SKINNY_WGS);
+  else if (tiles < DFLASH_GEMM_WGS)
     ks = std::min<int64_t>(cdiv(DFLASH_GEMM_WGS, tiles), std::max<int64_t>(1, K / (4 * BK)));
   const int64_t kchunk = cdiv(cdiv(K, ks), BK) * BK;
   ks = cdiv(K, kchunk);
