@@ -62,6 +62,12 @@ constexpr int BK = 64;   // granularity of split-K chunks (a multiple of the pip
 #endif
 // The 128 x 128 plan picks its split count with the same cost model (1) or
 // aims at DFLASH_GEMM_WGS workgroups (0).
+// Bytes charged per fp32 partial element in that cost: 16, twice its write
+// and read, since the reduce pass streams them less efficiently than the
+// GEMM streams weights (measured better than 8 at batch 1 to 32).
+#ifndef DFLASH_GEMM_PART_W
+#define DFLASH_GEMM_PART_W 16.0
+#endif
 #ifndef DFLASH_GEMM_SMALL_COST
 #define DFLASH_GEMM_SMALL_COST 1
 #endif
@@ -808,7 +814,8 @@ struct Plan {
 // Split count for tiles that run one workgroup per CU, in rounds of W.
 // Cost of k splits, in bytes per CU: each round streams one tile's operands
 // over K / k columns (512 K / k bytes for 256 operand rows), and the fp32
-// partials are written and read back (8 k M N bytes over the CUs).  The
+// partials are written and read back (DFLASH_GEMM_PART_W k M N bytes over
+// the CUs).  The
 // cheapest count wins, the fewest splits on a tie; no split is shorter than
 // 4 steps.
 int64_t pick_splits(int64_t tiles, int64_t M, int64_t N, int64_t K, int64_t W) {
@@ -817,7 +824,7 @@ int64_t pick_splits(int64_t tiles, int64_t M, int64_t N, int64_t K, int64_t W) {
   double best = (double)cdiv(tiles, W) * 512.0 * (double)K;
   for (int64_t k = 2; k <= ks_max; ++k) {
     const double cost = (double)cdiv(tiles * k, W) * 512.0 * (double)K / (double)k +
-                        8.0 * (double)k * (double)M * (double)N / (double)W;
+                        DFLASH_GEMM_PART_W * (double)k * (double)M * (double)N / (double)W;
     if (cost < best) { best = cost; ks = k; }
   }
   return ks;
