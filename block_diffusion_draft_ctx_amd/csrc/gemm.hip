@@ -58,7 +58,7 @@ constexpr int BK = 64;   // granularity of split-K chunks (a multiple of the pip
 // CU than 128 x 128 tiles, split over the contraction toward
 // DFLASH_GEMM_SKINNY_WGS workgroups.
 #ifndef DFLASH_GEMM_SKINNY_M
-#define DFLASH_GEMM_SKINNY_M 128
+#define DFLASH_GEMM_SKINNY_M 256
 #endif
 // The 128 x 128 plan picks its split count with the same cost model (1) or
 // aims at DFLASH_GEMM_WGS workgroups (0).

@@ -58,6 +58,7 @@ def _oracle_layer(c, w, x, k, Hq, rope_theta, causal, rows=None):
     # 64 and 128 block rows: the few-row GEMM tiles with the residual epilogue
     ("bf16", 4, 16, 512, 8, 4, 64, 1536, [64, 0, 200, 31], 1e6, False, True, 5106),
     ("bf16", 8, 16, 512, 8, 4, 64, 1536, [16 * i + 5 for i in range(8)], 1e6, True, True, 5107),
+    ("bf16", 12, 16, 512, 8, 4, 64, 1536, [40 * i for i in range(12)], 1e6, False, True, 5108),  # 192 rows
 ])
 def test_draft_layer_parity(dtype, B, k, d, Hq, Hkv, D, I, ctx, theta, causal, qkn, seed):
     log(f"draft_layer dtype={dtype} B={B} k={k} d={d} heads={Hq}/{Hkv}x{D} I={I} ctx={ctx} "

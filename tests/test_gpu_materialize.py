@@ -93,6 +93,7 @@ def _check(c, ck, cv, h_out, rows=None, epi=None):
     # Hkv*D = 128: no tile may straddle a layer's K and V blocks (256-wide tiles are not allowed)
     ("bf16", 5, 256, 5, 2, 64, 4, 2048, None, None, 2406),       # prefill-sized T = 8192
     ("bf16", 2, 128, 17, 2, 64, 2, 16, [0, 40], "random", 2407),  # 17 layers: two layer groups
+    ("bf16", 5, 512, 2, 8, 128, 16, 16, None, "random", 2408),    # T = 256: two 128-row tiles
 ])
 def test_materialize_parity(dtype, m, d, Ld, Hkv, D, n_seq, rps, start, commit, seed):
     log(f"materialise dtype={dtype} m={m} d={d} layers={Ld} Hkv={Hkv} D={D} rows={n_seq}x{rps}")
