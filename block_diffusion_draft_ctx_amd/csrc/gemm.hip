@@ -53,10 +53,10 @@ constexpr int BK = 64;   // granularity of split-K chunks (a multiple of the pip
 #define DFLASH_GEMM_WGS 512
 #endif
 // Few-row products (at most DFLASH_GEMM_SKINNY_M rows: decode and the
-// drafter at up to eight blocks of 16) stream their weights: BM x 256 tiles
-// (BM = 32, 64 or 128, four wavefronts) keep more weight bytes in flight per
-// CU than 128 x 128 tiles, split over the contraction toward
-// DFLASH_GEMM_SKINNY_WGS workgroups.
+// drafter at up to sixteen blocks of 16) stream their weights: BM x 256
+// tiles (BM = 32, 64 or 128, four wavefronts) keep more weight bytes in
+// flight per CU than 128 x 128 tiles; the split count comes from the cost
+// model of pick_splits, with rounds of DFLASH_GEMM_SKINNY_WGS workgroups.
 #ifndef DFLASH_GEMM_SKINNY_M
 #define DFLASH_GEMM_SKINNY_M 256
 #endif
