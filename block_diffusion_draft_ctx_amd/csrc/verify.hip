@@ -365,8 +365,14 @@ __device__ ReqInfo accept_scan(int b, int B, int L, int V, int nc, const float2*
     if (okx[t]) {
       const float tx = load1(tl + (int64_t)(b * (L + 1) + t) * ts + x);
       const float dx = load1(dl + (int64_t)(b * L + t) * ds + x);
-      const float e = fmaf(tx, a, -Mt[t]) - fmaf(dx, a, -Md[t]);
-      r = exp2f(e) * (Sd[t] / St[t]);
+      if (dx == neg_inf()) {
+        // q(x) = 0: the ratio is taken as +inf, so the token is accepted
+        // whatever p(x) is (0/0 included)
+        r = __builtin_inff();
+      } else {
+        const float e = fmaf(tx, a, -Mt[t]) - fmaf(dx, a, -Md[t]);
+        r = exp2f(e) * (Sd[t] / St[t]);
+      }
     }
     rat[t] = r;
     if (ratio_out) ratio_out[b * L + t] = r;
@@ -711,7 +717,9 @@ __global__ __launch_bounds__(64) void k_tree_walk(
     return i == INT_MAX ? 0 : i;
   };
   int cur = -1, len = 0, want = predict(0);
-  while (!bad && len < N) {      // a path holds at most N nodes: ends on any parent table
+  // a path holds at most N nodes (this ends the loop on any parent table);
+  // the walk also stops once max_depth nodes are accepted
+  while (!bad && len < N && len < max_depth) {
     int hit = INT_MAX;
     for (int j0 = 0; j0 < N; j0 += 64) {
       const int j = j0 + lane;
@@ -720,7 +728,7 @@ __global__ __launch_bounds__(64) void k_tree_walk(
       if (bal) { hit = j0 + (int)__ffsll((unsigned long long)bal) - 1; break; }
     }
     if (hit == INT_MAX) break;
-    if (lane == 0 && len < max_depth) path[(int64_t)b * max_depth + len] = hit;
+    if (lane == 0) path[(int64_t)b * max_depth + len] = hit;
     ++len;
     cur = hit;
     want = predict(cur + 1);

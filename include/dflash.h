@@ -1,9 +1,13 @@
 /*
  * dflash.h -- C ABI of the DFlash draft-and-verify step on AMD MI355X (gfx950).
  *
- * Five operations, each the hot path of one part of the step:
+ * Twelve operations.  The five of the draft-and-verify step:
  *   dflash_materialize_ctx_kv  target-context KV injection
  *   dflash_block_attention     non-causal block attention over [ctx; block]
+ *   dflash_verify_greedy       greedy acceptance over the full vocabulary
+ *   dflash_verify_sample       lossless rejection sampling over the full vocabulary
+ *   dflash_gate                DLoop block-confidence gate
+ * and seven around them:
  *   dflash_tree_build          DDTree: top-K per position, best-first tree, ancestor mask
  *   dflash_tree_verify_greedy  DDTree: target argmax per node and the greedy walk
  *   dflash_tree_attention      DDTree: the target's attention under the ancestor-only mask
@@ -11,9 +15,8 @@
  *   dflash_draft_layer         the drafter's decoder layer around block attention
  *   dflash_draft_head          the drafter's final norm and shared lm_head
  *   dflash_embed               the shared embedding gather
- *   dflash_verify_greedy       greedy acceptance over the full vocabulary
- *   dflash_verify_sample       lossless rejection sampling over the full vocabulary
- *   dflash_gate                DLoop block-confidence gate
+ * plus one workspace-size query per operation that needs scratch memory,
+ * dflash_status_string and dflash_version.
  *
  * Pages these follow (cited by short title):
  *   [DFlash overview]  "DFlash 块扩散解码：以并行扩散替代自回归草稿，实现无损 6 倍推理加速"
@@ -367,8 +370,11 @@ dflash_status dflash_gate(
  *     argmax (ties to the lower id)
  *   node_token, node_parent, n_nodes  the tree, as dflash_tree_build gives it
  *   accept_len, bonus, commit_lens [B] outputs; accepted_nodes [B, max_depth]
- *     output: the accepted path's node indices, -1 past it (a path longer
- *     than max_depth is truncated in this list only)
+ *     output: the accepted path's node indices, -1 past it.  The walk stops
+ *     after max_depth accepted nodes: accept_len <= max_depth, the bonus is
+ *     the target's prediction at the last node kept, and every committed row
+ *     (commit = accept_len + 1) is the root or a listed node, so
+ *     dflash_tree_commit_kv writes exactly commit_lens rows
  *   prefix_lens, new_seq_lens [B] or both NULL: new = prefix + commit
  *   In band: n_nodes[b] outside [0, budget] gives accept_len = bonus = -1,
  *   commit = 0.

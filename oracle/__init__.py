@@ -35,7 +35,7 @@ from .numerics import widen, round_to_bf16, round_to_f32
 from .materialize import (fuse_hiddens, project_kv, materialize, paged_write, gather_paged, slots,
                           k_norm, rope_half_split, row_positions)
 from .attention import block_attention, block_attention_masked
-from .verify import (verify_greedy, verify_sample, gate, row_log_softmax, GreedyResult,
+from .verify import (verify_greedy, verify_sample, gate, row_log_softmax, residual, GreedyResult,
                      SampleResult, GateResult)
 from .tree import (topk_logprobs, build_tree, ancestor_mask, walk_greedy, target_argmax, Tree,
                    TreeWalk, tree_attention, commit_tree_kv)
@@ -44,7 +44,7 @@ from .draft import rms_norm, silu, embed, draft_layer, draft_head
 __all__ = [
     "widen", "round_to_bf16", "round_to_f32", "fuse_hiddens", "project_kv", "materialize",
     "paged_write", "gather_paged", "slots", "k_norm", "rope_half_split", "row_positions", "block_attention", "block_attention_masked",
-    "verify_greedy", "verify_sample", "gate", "row_log_softmax", "GreedyResult",
+    "verify_greedy", "verify_sample", "gate", "row_log_softmax", "residual", "GreedyResult",
     "SampleResult", "GateResult", "topk_logprobs", "build_tree", "ancestor_mask", "walk_greedy",
     "target_argmax", "Tree", "TreeWalk", "tree_attention", "commit_tree_kv", "rms_norm", "silu",
     "embed", "draft_layer", "draft_head",

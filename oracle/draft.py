@@ -56,18 +56,25 @@ def embed(table, tokens, dtype):
 
 
 def draft_layer(x, w, cache_k, cache_v, block_table, ctx_lens, *, k, n_q_heads, n_kv_heads,
-                head_dim, dtype, eps=1e-6, rope_theta=1e6, causal=False):
+                head_dim, dtype, eps=1e-6, rope_theta=1e6, causal=False, storage_rounding=True):
     """One drafter layer on the stored block rows x [B*k, d].  ``w`` holds the
     stored weights: ln1 [d], qkv [(Hq + 2 Hkv) D, d], q_norm / k_norm [D] or
     None, o [d, Hq D], ln2 [d], gate_up [2 I, d], down [d, I].  cache_k/v are
-    this layer's injected context.  Returns x2 [B*k, d] on the storage grid."""
+    this layer's injected context.  Returns x2 [B*k, d], on the storage grid
+    when ``storage_rounding`` (the default); with it off, every step after
+    widening the inputs stays in float64 (the layer's exact value for the
+    stored inputs, which the rounded form approximates)."""
+    if storage_rounding:
+        round_to_storage = lambda v: round_to(v, dtype)
+    else:
+        round_to_storage = lambda v: v
     X = widen(x, dtype)
     M, d = X.shape
     B = M // k
     Hq, Hkv, D = n_q_heads, n_kv_heads, head_dim
     W = {name: (None if v is None else widen(v, dtype)) for name, v in w.items()}
-    n1 = round_to(rms_norm(X, W["ln1"], eps), dtype)
-    qkv = round_to(n1 @ W["qkv"].T, dtype)
+    n1 = round_to_storage(rms_norm(X, W["ln1"], eps))
+    qkv = round_to_storage(n1 @ W["qkv"].T)
     q = qkv[:, :Hq * D].reshape(M, Hq, D)
     kb = qkv[:, Hq * D:(Hq + Hkv) * D].reshape(M, Hkv, D)
     vb = qkv[:, (Hq + Hkv) * D:].reshape(M, Hkv, D)
@@ -79,19 +86,19 @@ def draft_layer(x, w, cache_k, cache_v, block_table, ctx_lens, *, k, n_q_heads, 
     if rope_theta > 0:
         q = rope_half_split(q, pos, rope_theta)
         kb = rope_half_split(kb, pos, rope_theta)
-    q, kb = round_to(q, dtype), round_to(kb, dtype)
-    # block_attention widens its inputs from storage: hand it float64 values
-    # that already lie on the storage grid, declared as float64
+    q, kb = round_to_storage(q), round_to_storage(kb)
+    # block_attention widens its inputs from storage: hand it the float64
+    # values (on the storage grid when rounding), declared as float64
     a, _ = block_attention(q.reshape(B, k, Hq, D), kb.reshape(B, k, Hkv, D), vb.reshape(B, k, Hkv, D),
                            widen(cache_k, dtype), widen(cache_v, dtype), block_table, ctx_lens,
                            "f64", causal=causal)
-    a = round_to(a.reshape(M, Hq * D), dtype)
-    x1 = round_to(X + round_to(a @ W["o"].T, dtype), dtype)
-    n2 = round_to(rms_norm(x1, W["ln2"], eps), dtype)
-    gu = round_to(n2 @ W["gate_up"].T, dtype)
+    a = round_to_storage(a.reshape(M, Hq * D))
+    x1 = round_to_storage(X + round_to_storage(a @ W["o"].T))
+    n2 = round_to_storage(rms_norm(x1, W["ln2"], eps))
+    gu = round_to_storage(n2 @ W["gate_up"].T)
     I = gu.shape[1] // 2
-    h = round_to(silu(gu[:, :I]) * gu[:, I:], dtype)
-    return round_to(x1 + round_to(h @ W["down"].T, dtype), dtype)
+    h = round_to_storage(silu(gu[:, :I]) * gu[:, I:])
+    return round_to_storage(x1 + round_to_storage(h @ W["down"].T))
 
 
 def draft_head(x, w_norm, w_lm, dtype, eps=1e-6):

@@ -123,12 +123,19 @@ class TreeWalk:
     path: list          # accepted node indices, root side first
 
 
-def walk_greedy(tree_token, tree_parent, target_predict):
+def walk_greedy(tree_token, tree_parent, target_predict, max_depth=None):
     """Greedy walk of one request's tree.  target_predict[0] is the target's
-    argmax after the root, target_predict[1 + j] after node j."""
+    argmax after the root, target_predict[1 + j] after node j.
+
+    With ``max_depth`` the walk stops after that many accepted nodes (the
+    caller keeps room for only that many); the bonus is then the target's
+    argmax at the last node kept, so the commit (accepted + 1) never exceeds
+    max_depth + 1 and every committed row has a tree row behind it."""
     cur, path = -1, []
     while True:
         want = int(target_predict[cur + 1])
+        if max_depth is not None and len(path) >= max_depth:
+            return TreeWalk(len(path), want, path)
         nxt = [j for j in range(len(tree_token)) if tree_parent[j] == cur and tree_token[j] == want]
         if not nxt:
             return TreeWalk(len(path), want, path)

@@ -143,6 +143,15 @@ def _inverse_cdf(w, u):
     return x, gap
 
 
+def residual(target_row, draft_row):
+    """One row pair's acceptance quantities ([Spec-decoding tutorial], section 3):
+    p = softmax(target_row), q = softmax(draft_row) (both already divided by the
+    temperature), the overlap min(p, q) whose sum is beta, and the residual
+    max(0, p - q) whose sum R equals 1 - beta in exact arithmetic."""
+    p, q = _softmax(target_row), _softmax(draft_row)
+    return p, q, np.minimum(p, q), np.maximum(0.0, p - q)
+
+
 def verify_sample(target_logits, draft_logits, draft_tokens, u_accept, u_bonus, dtype,
                   temperature=1.0, chain_lens=None, prefix_lens=None) -> SampleResult:
     t = widen(target_logits, dtype) / temperature
@@ -178,9 +187,8 @@ def verify_sample(target_logits, draft_logits, draft_tokens, u_accept, u_bonus, 
         acc[b] = a
         brow[b] = a
         if rej[b]:
-            p, q = _softmax(t[b, a]), _softmax(d[b, a])
-            res = np.maximum(0.0, p - q)
-            beta[b] = np.minimum(p, q).sum()
+            p, _, overlap, res = residual(t[b, a], d[b, a])
+            beta[b] = overlap.sum()
             w = res if res.sum() > 0 else p
         else:
             w = _softmax(t[b, nb])

@@ -20,3 +20,15 @@ def worked_pq_example():
             elif len(parts) == 2:
                 scal[parts[0]] = float(parts[1])
     return toks, cols, scal
+
+
+def block_causal_mask():
+    """The 9 x 9 visibility matrix of block_causal_3x3.txt as a list of rows
+    of 0/1 ints (row = query position, column = key position)."""
+    rows = []
+    with open(os.path.join(HERE, "block_causal_3x3.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                rows.append([int(v) for v in line.split()])
+    return rows

@@ -307,3 +307,28 @@ def test_attention_causal_first_position_and_last_row():
     ob, lb = _run(c, out_dtype="f32")
     e = float(np.abs(down(oc)[:, -1] - down(ob)[:, -1]).max())
     assert e <= 1e-5 * float(np.abs(down(ob)[:, -1]).max()), e
+
+
+@pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 128)])
+def test_block_causal_figure_through_the_kernel(dtype, D):
+    """[Spec tutorial] 5.3, the BD3-LM block-causal figure (three blocks of
+    three positions): block j is one request of the bidirectional kernel with
+    the earlier blocks as its context (one shared page table).  Compared with
+    torch CPU float64 SDPA under the figure's 9 x 9 boolean mask."""
+    import torch
+    from tests.golden.load import block_causal_mask
+    from tests.test_oracle_attention import block_causal_case
+    log(f"block-causal figure dtype={dtype} D={D}")
+    mask = torch.tensor(block_causal_mask(), dtype=torch.bool)
+    c, (q, kk, vv) = block_causal_case(52, dtype, Hq=8, Hkv=2, D=D)
+    out, lse = _run(c, out_dtype="f32")
+    got = down(out).reshape(9, c.n_q_heads, D)
+    G = c.n_q_heads // c.n_kv_heads
+    ref = np.stack([torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q[:, h])[None, None], torch.from_numpy(kk[:, h // G])[None, None],
+        torch.from_numpy(vv[:, h // G])[None, None], attn_mask=mask[None, None])[0, 0].numpy()
+        for h in range(c.n_q_heads)], axis=1)
+    e = rel_err(got, ref)
+    log(f"  err {e:.2e}")
+    assert e <= TOL[dtype]
+    _check(c, out, lse)

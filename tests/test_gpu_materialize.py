@@ -71,7 +71,8 @@ def _check(c, ck, cv, h_out, rows=None, epi=None):
                 want.append(rv[i])
             if got:
                 if epi is not None and name == "K":   # two storage points in the chain
-                    e = rel_err_chained(np.array(got), np.array(want), c.dtype)
+                    e = rel_err_chained(np.array(got), np.array(want), c.dtype,
+                                        what=f"K epilogue, layer {l}, {len(got)} rows")
                 else:
                     e = rel_err(np.array(got), np.array(want))
                 assert e <= TOL[c.dtype], f"layer {l} {name}: err {e}"

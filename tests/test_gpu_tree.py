@@ -249,7 +249,8 @@ def _walk_check(r, trees, tl, dtype, max_depth, n_nodes=None, prefix=None):
         if n < 0 or n > tl.shape[1] - 1:
             assert (acc[b], bon[b], com[b]) == (-1, -1, 0)
             continue
-        w = oracle.walk_greedy(t.token[:n], t.parent[:n], _LazyPredict(tl[b], dtype))
+        w = oracle.walk_greedy(t.token[:n], t.parent[:n], _LazyPredict(tl[b], dtype),
+                               max_depth=max_depth)
         assert acc[b] == w.accept_len and bon[b] == w.bonus and com[b] == w.accept_len + 1, b
         want = (w.path + [-1] * max_depth)[:max_depth]
         np.testing.assert_array_equal(path[b], want)
@@ -280,8 +281,9 @@ def test_tree_verify_parity(dtype, B, n_pos, V, K, budget, seed):
 
 def test_tree_verify_edge_cases():
     """An empty tree (bonus only), node counts out of range (in-band error),
-    and an accepted path longer than max_depth (the list is cut, the length
-    is not)."""
+    and a tree whose accepted path is longer than max_depth (the walk stops
+    after max_depth nodes; the bonus is the prediction at the last node
+    kept)."""
     B, n_pos, V, K, budget = 4, 6, 2000, 3, 40
     trees, tl = _walk_case(3211, "bf16", B, n_pos, V, K, budget)
     toks = np.stack([_padded(t, budget)[0] for t in trees])
@@ -292,7 +294,8 @@ def test_tree_verify_edge_cases():
     r = dfl.tree_verify_greedy(up(tl, "bf16"), up(toks, "i32"), up(pars, "i32"), up(nn, "i32"),
                                max_depth)
     _walk_check(r, trees, tl, "bf16", max_depth, n_nodes=nn)
-    assert down(r["accept_len"])[3] == max_depth + 1
+    assert down(r["accept_len"])[3] == max_depth
+    assert (down(r["accepted_nodes"])[3] >= 0).all()
 
 
 def test_build_then_verify_on_device():

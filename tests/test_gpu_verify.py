@@ -16,7 +16,7 @@ import block_diffusion_draft_ctx_amd as dfl
 import oracle
 import synth
 from tests.golden.load import worked_pq_example
-from tests.gpu_util import down, log, rel_err, up
+from tests.gpu_util import down, log, rel_err, report, up
 
 pytestmark = pytest.mark.gpu
 
@@ -146,8 +146,9 @@ def _sample_compare(c, r, ref, what):
     assert np.isnan(bg[~ref.rejected & (acc == ref.accept_len)]).all()
     ties_ratio = int((ref.ratio_gap < 1e-5).sum())
     ties_cdf = int((ref.cdf_gap < 1e-5).sum())
-    log(f"{what}: {len(near)} near-tie mismatches; near-ties in the inputs: ratio {ties_ratio}, "
-        f"cdf {ties_cdf}; accept_len histogram {np.bincount(ref.accept_len[ref.accept_len >= 0])}")
+    report(f"{what}: {len(near)} near-tie mismatches; near-ties in the inputs "
+           f"(|u - p/q| < 1e-5): ratio {ties_ratio}, cdf {ties_cdf}; accept_len histogram "
+           f"{np.bincount(ref.accept_len[ref.accept_len >= 0]).tolist()}")
     return len(near)
 
 
@@ -262,7 +263,7 @@ def test_gate_parity(dtype, B, n, V, T, valid, seed):
     go = down(r["go"])
     decided = np.abs(ref.c - (-0.5)) >= 1e-4
     np.testing.assert_array_equal(go[decided], ref.go[decided].astype(np.int64))
-    log(f"gate c: {np.round(ref.c, 3)}; near-ties {int((~decided).sum())}")
+    report(f"gate seed {seed}: near-ties |c - g| < 1e-4: {int((~decided).sum())} of {B}")
 
 
 def test_gate_invalid_token_gives_nan():
@@ -303,3 +304,31 @@ def test_sample_reuses_gate_row_lse(source):
     ref = oracle.verify_sample(c.target_logits, c.draft_logits, c.draft_tokens, c.u_accept,
                                c.u_bonus, "bf16", temperature=T)
     _sample_compare(c, r, ref, f"gate lse from {source}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_sample_zero_draft_probability_accepts(dtype):
+    """A drafted token with draft logit -inf (q(x) = 0) is accepted, as the
+    oracle reads it (ratio +inf), both with a finite target logit and with the
+    target logit -inf too (0/0); u is the largest uniform, so nothing else
+    would accept.  Other requests and rows keep the ordinary rule."""
+    B, L, V = 5, 4, 3001
+    c = synth.sample_case(3040, dtype=dtype, B=B, L=L, V=V, sigma=1.0)
+    t, d, x = c.target_logits.copy(), c.draft_logits.copy(), c.draft_tokens.copy()
+    u = c.u_accept.copy()
+    ninf = np.uint16(0xFF80) if dtype == "bf16" else np.float32(-np.inf)
+    top = np.float32(1 - 2.0 ** -24)
+    d[0, 0, x[0, 0]] = ninf; u[0, 0] = top                            # target finite
+    d[1, 0, x[1, 0]] = ninf; t[1, 0, x[1, 0]] = ninf; u[1, 0] = top   # both -inf
+    for i in range(L):                                                 # a whole chain at q = 0
+        d[2, i, x[2, i]] = ninf; u[2, i] = top
+    d[3, 2, x[3, 2]] = ninf; t[3, 2, x[3, 2]] = ninf; u[3, :3] = 0.0   # accepted up to it
+    r = dfl.verify_sample(up(t, dtype), up(d, dtype), up(x, "i32"), up(u, "f32"),
+                          up(c.u_bonus, "f32"))
+    ref = oracle.verify_sample(t, d, x, u, c.u_bonus, dtype)
+    assert ref.accept_len[0] >= 1 and ref.accept_len[1] >= 1 and ref.accept_len[2] == L
+    assert ref.accept_len[3] >= 3
+    rg = down(r["ratio"])
+    assert np.isinf(rg[[0, 1, 2, 3], [0, 0, 0, 2]]).all() and (rg[[0, 1, 2, 3], [0, 0, 0, 2]] > 0).all()
+    c2 = synth.SampleCase(**{**c.__dict__, "u_accept": u})
+    _sample_compare(c2, r, ref, f"q(x) = 0 drafts ({dtype})")

@@ -222,3 +222,105 @@ def test_causal_closed_forms():
     np.testing.assert_allclose(lc[:, :, -1], lb[:, :, -1], rtol=0, atol=1e-12)
     c = _case(27, B=2, k=1, Hq=2, Hkv=1, D=8, ctx=(3, 9))
     np.testing.assert_allclose(_run_causal(c)[0], _run(c)[0], rtol=0, atol=1e-12)
+
+
+# --- split-context merge and logical-position permutation -------------------
+
+def test_split_context_lse_merge_equals_unsplit():
+    """Splitting the keys into parts and merging the parts' outputs by their
+    log-sum-exp reproduces the unsplit attention: with S(A) = exp(lse_A) and
+    N(A) = O_A * S(A), S and N are additive over disjoint key sets.  The
+    three runs below see A = ctx[0, 16) + block, B = ctx[16, C) + block and
+    the block alone, so S(all) = S(A) + S(B) - S(block) and likewise N.  This
+    checks the exported lse as well as the output."""
+    c = _case(31, B=2, k=4, Hq=4, Hkv=2, D=8, ctx=(40, 37))
+    full_o, full_l = _run(c)
+
+    def with_ctx(lens, table):
+        return oracle.block_attention(c.q, c.k_blk, c.v_blk, c.cache_k, c.cache_v, table,
+                                      np.asarray(lens), c.dtype)
+
+    oA, lA = with_ctx([16, 16], c.block_table)
+    shifted = np.full_like(c.block_table, -1)
+    shifted[:, :-1] = c.block_table[:, 1:]                 # logical page p+1 becomes page p
+    oB, lB = with_ctx(c.ctx_lens - 16, shifted)
+    o0, l0 = with_ctx([0, 0], c.block_table)
+    sA, sB, s0 = (np.exp(l)[..., None] for l in (lA, lB, l0))          # [B, Hq, k, 1]
+    to_bhk = lambda o: np.transpose(o, (0, 2, 1, 3))                  # [B, Hq, k, D]
+    S = sA + sB - s0
+    N = to_bhk(oA) * sA + to_bhk(oB) * sB - to_bhk(o0) * s0
+    np.testing.assert_allclose(np.log(S[..., 0]), full_l, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(N / S, to_bhk(full_o), rtol=0, atol=1e-12)
+
+
+def test_invariant_to_permutation_of_context_positions():
+    """Attention without positions inside is a set function of the visible
+    (key, value) pairs: permuting which logical context position holds which
+    pair leaves every output unchanged (only the summation order moves)."""
+    c = _case(32, B=3, k=4, Hq=4, Hkv=2, D=8, ctx=(40, 17, 33))
+    o1, l1 = _run(c)
+    rng = np.random.default_rng(33)
+    ck, cv = oracle.slots(c.cache_k.copy()), oracle.slots(c.cache_v.copy())
+    new_k, new_v = c.cache_k.copy(), c.cache_v.copy()
+    nk, nv = oracle.slots(new_k), oracle.slots(new_v)
+    for b in range(c.B):
+        C = int(c.ctx_lens[b])
+        perm = rng.permutation(C)
+        for dst, src in enumerate(perm):
+            pd, ps = c.block_table[b, dst // 16], c.block_table[b, src // 16]
+            nk[pd, dst % 16] = ck[ps, src % 16]
+            nv[pd, dst % 16] = cv[ps, src % 16]
+    o2, l2 = oracle.block_attention(c.q, c.k_blk, c.v_blk, new_k, new_v, c.block_table,
+                                    c.ctx_lens, c.dtype)
+    assert not np.array_equal(new_k, c.cache_k)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l2, l1, rtol=0, atol=1e-13)
+
+
+# --- BD3-LM block-causal mask ([Spec tutorial] 5.3) --------------------------
+
+def block_causal_case(seed, dtype="f32", n_blocks=3, k=3, Hq=4, Hkv=2, D=8):
+    """The page's block-causal figure as block attention: block j is one
+    request whose context is the K/V of blocks 0..j-1, stored in a paged cache
+    at logical positions 0..3j-1 (one page table shared by all blocks), and
+    whose own k rows are its block.  Returns (case, dense q/k/v [n*k, H, D] in
+    float64 for the explicit-mask reference)."""
+    rng = synth.make_rng(seed)
+    n = n_blocks * k
+    q = synth._draw(rng, (n_blocks, k, Hq, D), 1.0, dtype)
+    kk = synth._draw(rng, (n_blocks, k, Hkv, D), 1.0, dtype)
+    vv = synth._draw(rng, (n_blocks, k, Hkv, D), 1.0, dtype)
+    num_pages = 3
+    perm = rng.permutation(num_pages).astype(np.int32)
+    table = np.tile(perm, (n_blocks, 1))
+    ck = synth.empty_cache(num_pages, Hkv, D, dtype)
+    cv = synth.empty_cache(num_pages, Hkv, D, dtype)
+    sk, sv = oracle.slots(ck), oracle.slots(cv)
+    for pos in range(n):
+        sk[perm[pos // 16], pos % 16] = kk.reshape(n, Hkv, D)[pos]
+        sv[perm[pos // 16], pos % 16] = vv.reshape(n, Hkv, D)[pos]
+    ctx = (np.arange(n_blocks) * k).astype(np.int32)
+    c = synth.AttentionCase(dtype, n_blocks, k, Hq, Hkv, D, q, kk, vv, ck, cv, table, ctx)
+    dense = [oracle.widen(a, dtype).reshape(n, -1, D) for a in (q, kk, vv)]
+    return c, dense
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_block_causal_figure_equals_context_plus_bidirectional_block(dtype):
+    """Each row of the page's 3-block figure, evaluated by torch CPU float64
+    SDPA with the figure's boolean mask over the nine positions, equals the
+    bidirectional block attention of that row's block over a context holding
+    the earlier blocks."""
+    from tests.golden.load import block_causal_mask
+    mask = torch.tensor(block_causal_mask(), dtype=torch.bool)
+    assert mask.shape == (9, 9)
+    c, (q, kk, vv) = block_causal_case(51, dtype)
+    out, _ = _run(c)
+    G = c.n_q_heads // c.n_kv_heads
+    for h in range(c.n_q_heads):
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[:, h])[None, None], torch.from_numpy(kk[:, h // G])[None, None],
+            torch.from_numpy(vv[:, h // G])[None, None], attn_mask=mask[None, None])[0, 0]
+        np.testing.assert_allclose(out[:, :, h].reshape(9, -1), ref.numpy(), rtol=0, atol=1e-12)
+    # the mask is the figure's: not causal inside a block, causal across blocks
+    assert mask[0, 2] and not mask[2, 3] and mask[8, 0] and not mask[5, 6]

@@ -186,3 +186,40 @@ def test_k_epilogue_in_the_chain():
     want = oracle.round_to_f32(oracle.rope_half_split(
         oracle.k_norm(plain["K"][0], w[0].astype(np.float64), 1e-6), pos, 1e4))
     np.testing.assert_array_equal(epi["K"][0], want)
+
+
+def test_brute_force_exact_sums_on_a_tiny_case():
+    """A second path for the whole chain on a tiny bf16 case: every h_ctx,
+    K and V element is an explicit sum over the concatenated features,
+    accumulated exactly by math.fsum and rounded once, with the
+    concatenation indexed by hand (feature j of X is feature j mod d of hidden
+    j // d).  No matrix product is involved; the oracle must agree to the last
+    bit except where the two sums straddle a bf16 rounding boundary, which an
+    exact sum and a float64 matmul may do on a near-halfway value."""
+    import math
+    c = synth.materialize_case(61, dtype="bf16", m=3, d_model=8, n_layers=2, n_kv_heads=2,
+                               head_dim=4, n_seq=1, rows_per_seq=5, commit=[5])
+    res = oracle.materialize(c.hiddens, c.W_f, c.b_f, c.W_K, c.W_V, 2, 4, "bf16")
+    H = [oracle.widen(h, "bf16") for h in c.hiddens]
+    Wf, bf = oracle.widen(c.W_f, "bf16"), oracle.widen(c.b_f, "bf16")
+    T, d, m = 5, 8, 3
+    h = np.zeros((T, d))
+    for r in range(T):
+        for o in range(d):
+            h[r, o] = math.fsum([H[j // d][r, j % d] * Wf[o, j] for j in range(m * d)] + [bf[o]])
+    h = oracle.round_to_bf16(h)
+    off = 0
+    for name, Ws in (("K", c.W_K), ("V", c.W_V)):
+        for l, W in enumerate(Ws):
+            W = oracle.widen(W, "bf16")
+            want = np.array([[math.fsum(h[r, j] * W[o, j] for j in range(d)) for o in range(8)]
+                             for r in range(T)])
+            want = oracle.round_to_bf16(want).reshape(T, 2, 4)
+            got = res[name][l]
+            ulp = 2.0 ** (np.floor(np.log2(np.abs(want) + 1e-300)) - 7)
+            assert (np.abs(got - want) <= ulp).all()
+            off += int((got != want).sum())
+    off += int((res["h_ctx"] != h).sum())
+    hulp = 2.0 ** (np.floor(np.log2(np.abs(h) + 1e-300)) - 7)
+    assert (np.abs(res["h_ctx"] - h) <= hulp).all()
+    assert off <= 2     # at most a rare near-halfway disagreement

@@ -152,6 +152,21 @@ def test_walk_pages_example():
     assert (w.accept_len, w.bonus, w.path) == (3, 8, [0, 2, 4])   # a leaf: bonus after it
 
 
+def test_walk_stops_at_max_depth():
+    """A caller with room for max_depth accepted nodes: the walk of the page's
+    example (cat, sat, on all accepted) stops after max_depth nodes and the
+    bonus is the target's prediction at the last node kept, so commit =
+    accepted + 1 rows all have a tree row behind them."""
+    CAT, DOG, SAT, LAY, ON = 1, 2, 3, 4, 5
+    token = np.array([CAT, DOG, SAT, LAY, ON])
+    parent = np.array([-1, -1, 0, 0, 2])
+    tp = np.array([CAT, SAT, 9, ON, 9, 8])
+    for md, want in [(1, (1, SAT, [0])), (2, (2, ON, [0, 2])), (3, (3, 8, [0, 2, 4])),
+                     (9, (3, 8, [0, 2, 4]))]:
+        w = oracle.walk_greedy(token, parent, tp, max_depth=md)
+        assert (w.accept_len, w.bonus, w.path) == want
+
+
 def test_walk_on_a_single_path_is_the_chain_verify():
     """With K = 1 the tree is one path: the walk equals greedy chain
     verification of those drafts."""

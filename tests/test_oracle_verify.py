@@ -407,3 +407,90 @@ def test_gate_valid_lens():
     for b, vl in enumerate([6, 0, 3, 1]):
         per = [ls[b, i, c.draft_tokens[b, i]] - full.row_lse[b, i] for i in range(vl)]
         assert part.c[b] == pytest.approx(sum(per), abs=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# the residual identity and the acceptance probability
+# ----------------------------------------------------------------------------
+
+
+def _identity_rows():
+    """The worked example's (p, q) as logits, then random rows at two
+    temperatures and a row pair with disjoint and -inf entries."""
+    _, cols, _ = worked_pq_example()
+    rows = [(np.log(cols["p"]), np.log(cols["q"]))]
+    rng = np.random.default_rng(41)
+    for T in (1.0, 0.6):
+        t = rng.normal(0, 3, 1024)
+        rows.append((t / T, (t + rng.normal(0, 1, 1024)) / T))
+    t = np.full(8, -np.inf); t[:5] = rng.normal(0, 1, 5)
+    d = np.full(8, -np.inf); d[3:] = rng.normal(0, 1, 5)
+    rows.append((t, d))
+    return rows
+
+
+def test_overlap_plus_residual_is_p_elementwise():
+    """[Spec-decoding tutorial] section 3: min(p, q) + max(0, p - q) = p for
+    every token (accepted mass plus resampled mass), sum min = beta and the
+    residual sums to 1 - beta.  A residual with the operands swapped
+    (max(0, q - p)) or an overlap of max(p, q) fails it (checked below)."""
+    for t, d in _identity_rows():
+        p, q, overlap, res = oracle.residual(t, d)
+        np.testing.assert_allclose(overlap + res, p, rtol=0, atol=1e-15)
+        assert np.all(res >= 0) and np.all(overlap <= q + 1e-300)
+        assert abs(res.sum() - (1.0 - overlap.sum())) <= 1e-12
+        np.testing.assert_allclose(p.sum(), 1.0, atol=1e-12)
+        np.testing.assert_allclose(q.sum(), 1.0, atol=1e-12)
+    # the identity is not vacuous: the swapped residual breaks it
+    t, d = _identity_rows()[0]
+    p, q, overlap, _ = oracle.residual(t, d)
+    assert np.abs(overlap + np.maximum(0.0, q - p) - p).max() > 0.1
+    assert np.abs(np.maximum(p, q) + np.maximum(0.0, p - q) - p).max() > 0.1
+
+
+def test_verify_sample_beta_is_the_overlap_of_the_rejected_row():
+    """The beta that verify_sample reports equals sum min(p, q) of the rejected
+    row, and on the worked example that is the printed 0.80."""
+    _, cols, scal = worked_pq_example()
+    t, d, x, u, u2 = _worked_inputs(0.9, 0.3)
+    r = oracle.verify_sample(t, d, x, u, u2, "f64")
+    _, _, overlap, res = oracle.residual(t[0, 0], d[0, 0])
+    assert r.beta[0] == overlap.sum() == pytest.approx(scal["beta"], abs=1e-12)
+    np.testing.assert_allclose(res / res.sum(), cols["res"], atol=1e-12)
+
+
+def test_binomial_acceptance_rate_equals_beta():
+    """Monte Carlo: draft x ~ q and u ~ U[0, 1) fresh per trial, run the
+    oracle's acceptance test; the number of accepts is Binomial(n, beta)
+    ([Spec-decoding tutorial] section 3: P(accept) = sum min(p, q)).  A
+    two-sided exact binomial test must not reject (p-value > 1e-3)."""
+    _, cols, scal = worked_pq_example()
+    p, q = np.array(cols["p"]), np.array(cols["q"])
+    rng = np.random.default_rng(43)
+    n, chunk = 100_000, 5000
+    t = np.broadcast_to(np.stack([np.log(p), np.log(np.full(5, 0.2))]), (chunk, 2, 5))
+    d = np.broadcast_to(np.log(q), (chunk, 1, 5))
+    accepts = 0
+    for _ in range(n // chunk):
+        xs = np.minimum(np.searchsorted(np.cumsum(q), rng.random(chunk) * q.sum(), side="right"), 4)
+        u = synth.uniforms(rng, (chunk, 1))
+        r = oracle.verify_sample(t, d, xs[:, None].astype(np.int32), u, synth.uniforms(rng, (chunk,)),
+                                 "f64")
+        accepts += int((r.accept_len == 1).sum())
+    pv = scipy.stats.binomtest(accepts, n, scal["beta"]).pvalue
+    assert pv > 1e-3, (accepts / n, pv)
+    # the test has power: a rate of 0.79 would be rejected at this n
+    assert scipy.stats.binomtest(int(0.79 * n), n, scal["beta"]).pvalue < 1e-6
+
+
+def test_zero_draft_probability_accepts():
+    """A drafted token the drafter gave probability zero (logit -inf) is
+    accepted whatever its target probability (ratio taken as +inf), also when
+    the target gives it probability zero too."""
+    V = 6
+    t = np.zeros((2, 2, V)); t[1, 0, 2] = -np.inf
+    d = np.zeros((2, 1, V)); d[:, 0, 2] = -np.inf
+    x = np.array([[2], [2]], dtype=np.int32)
+    r = oracle.verify_sample(t, d, x, np.full((2, 1), 1 - 2.0 ** -24), np.array([0.5, 0.5]), "f64")
+    assert r.accept_len.tolist() == [1, 1]
+    assert np.isinf(r.ratio).all()
