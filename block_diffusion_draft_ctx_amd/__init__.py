@@ -14,7 +14,7 @@ from typing import Optional, Sequence
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdflash.so")
 
-OK, E_ARG, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, 1, 2, 3, 4
+OK, E_ARG, E_UNSUPPORTED, E_WORKSPACE, E_HIP, E_TOO_LARGE = 0, 1, 2, 3, 4, 5
 F32, BF16 = 0, 1
 MASK_BIDIRECTIONAL, MASK_CAUSAL = 0, 1
 
@@ -22,6 +22,7 @@ EXPORTS = (
     "dflash_status_string", "dflash_version",
     "dflash_materialize_workspace_size", "dflash_materialize_ctx_kv",
     "dflash_attention_workspace_size", "dflash_block_attention",
+    "dflash_verify_greedy_noalloc", "dflash_noalloc_scratch_bytes",
     "dflash_verify_workspace_size", "dflash_verify_greedy", "dflash_verify_sample",
     "dflash_gate_workspace_size", "dflash_gate",
     "dflash_tree_workspace_size", "dflash_tree_verify_workspace_size", "dflash_tree_build",
@@ -84,6 +85,11 @@ def _declare(lib):
     lib.dflash_verify_greedy.restype = I32
     lib.dflash_verify_greedy.argtypes = [
         I32, I32, I32, P, I64, P, I64, P, P, P, P, P, P, P, P, I32, P, SZ, P]
+    lib.dflash_verify_greedy_noalloc.restype = I32
+    lib.dflash_verify_greedy_noalloc.argtypes = [
+        I32, I32, I32, P, I64, P, I64, P, P, P, P, P, P, P, P, I32, P]
+    lib.dflash_noalloc_scratch_bytes.restype = SZ
+    lib.dflash_noalloc_scratch_bytes.argtypes = []
     lib.dflash_verify_sample.restype = I32
     lib.dflash_verify_sample.argtypes = [
         I32, I32, I32, P, I64, P, I64, P, P, P, P, F, P, P, P, P, P, P, P, P, P, I32, P, SZ, P]
@@ -363,6 +369,44 @@ def verify_greedy(target_logits, draft_tokens=None, draft_logits=None, chain_len
         _ptr(o["commit_lens"]), _ptr(prefix_lens), _ptr(o.get("new_seq_lens")), dt, _ptr(ws),
         nws, _stream(stream))
     _check(s, "dflash_verify_greedy")
+    o["draft_tokens"] = draft_tokens
+    return o
+
+
+def verify_greedy_noalloc(target_logits, draft_tokens=None, draft_logits=None, chain_lens=None,
+                          prefix_lens=None, want_target_predict=True, out=None, stream=None):
+    """dflash_verify_greedy_noalloc: verify_greedy without a workspace (the
+    library's static per-GPU scratch holds the partials).  Same arguments and
+    results as verify_greedy; the caller still provides the outputs (``out``)
+    or lets this allocate them here, outside the library call."""
+    torch = _torch()
+    L_ = lib()
+    _logit_rows(target_logits, "target_logits")
+    B, Lp1, V = target_logits.shape
+    L = Lp1 - 1
+    dt = _dtype_code(target_logits)
+    dev = target_logits.device
+    o = dict(out or {})
+    if draft_logits is not None:
+        _logit_rows(draft_logits, "draft_logits")
+        if draft_tokens is None:
+            draft_tokens = torch.empty((B, L), dtype=torch.int32, device=dev)
+    _i32(draft_tokens, "draft_tokens")
+    _i32(chain_lens, "chain_lens")
+    _i32(prefix_lens, "prefix_lens")
+    for name in ("accept_len", "bonus", "commit_lens"):
+        o.setdefault(name, torch.empty(B, dtype=torch.int32, device=dev))
+    if prefix_lens is not None:
+        o.setdefault("new_seq_lens", torch.empty(B, dtype=torch.int32, device=dev))
+    if want_target_predict:
+        o.setdefault("target_predict", torch.empty((B, L + 1), dtype=torch.int32, device=dev))
+    s = L_.dflash_verify_greedy_noalloc(
+        B, L, V, _ptr(target_logits), _row_stride(target_logits), _ptr(draft_logits),
+        _row_stride(draft_logits) if draft_logits is not None else 0, _ptr(draft_tokens),
+        _ptr(chain_lens), _ptr(o.get("target_predict")), _ptr(o["accept_len"]), _ptr(o["bonus"]),
+        _ptr(o["commit_lens"]), _ptr(prefix_lens), _ptr(o.get("new_seq_lens")), dt,
+        _stream(stream))
+    _check(s, "dflash_verify_greedy_noalloc")
     o["draft_tokens"] = draft_tokens
     return o
 

@@ -49,6 +49,9 @@ const char* dflash_status_string(dflash_status s) {
     case DFLASH_E_UNSUPPORTED: return "DFLASH_E_UNSUPPORTED: shape or dtype not implemented";
     case DFLASH_E_WORKSPACE: return "DFLASH_E_WORKSPACE: workspace missing, too small or misaligned";
     case DFLASH_E_HIP: return "DFLASH_E_HIP: kernel launch failed";
+    case DFLASH_E_TOO_LARGE:
+      return "DFLASH_E_TOO_LARGE: the problem needs more scratch than the allocation-free "
+             "entry point's static buffer holds";
   }
   return "DFLASH_E_UNKNOWN";
 }
@@ -248,6 +251,34 @@ dflash_status dflash_verify_greedy(int B, int L, int V, const void* target_logit
                                          commit_lens, prefix_lens, new_seq_lens, ws,
                                          static_cast<hipStream_t>(stream)));
 }
+
+dflash_status dflash_verify_greedy_noalloc(int B, int L, int V, const void* target_logits,
+                                           int64_t t_row_stride, const void* draft_logits,
+                                           int64_t d_row_stride, int32_t* draft_tokens,
+                                           const int32_t* chain_lens, int32_t* target_predict,
+                                           int32_t* accept_len, int32_t* bonus,
+                                           int32_t* commit_lens, const int32_t* prefix_lens,
+                                           int32_t* new_seq_lens, dflash_dtype dtype,
+                                           dflash_stream_t stream) {
+  if (bad_dtype(dtype)) return DFLASH_E_ARG;
+  if (dflash_status s = check_verify_common(B, L, V, target_logits, t_row_stride, draft_logits,
+                                            d_row_stride, false))
+    return s;
+  if (B == 0) return DFLASH_OK;
+  if ((L > 0 && !draft_tokens) || !accept_len || !bonus || !commit_lens) return DFLASH_E_ARG;
+  if ((prefix_lens == nullptr) != (new_seq_lens == nullptr)) return DFLASH_E_ARG;
+  if (greedy_ws_bytes(B, L, V) > kNoallocScratchBytes) return DFLASH_E_TOO_LARGE;
+  void* scr = nullptr;
+  if (noalloc_scratch(&scr) != hipSuccess) return DFLASH_E_HIP;
+  // the kernels write every scratch word they read: nothing needs clearing
+  return hip_status(launch_verify_greedy(dtype == DFLASH_BF16, B, L, V, target_logits,
+                                         t_row_stride, draft_logits, d_row_stride, draft_tokens,
+                                         chain_lens, target_predict, accept_len, bonus,
+                                         commit_lens, prefix_lens, new_seq_lens, scr,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+size_t dflash_noalloc_scratch_bytes(void) { return kNoallocScratchBytes; }
 
 dflash_status dflash_verify_sample(int B, int L, int V, const void* target_logits,
                                    int64_t t_row_stride, const void* draft_logits,

@@ -35,6 +35,11 @@ hipError_t launch_verify_greedy(bool bf16, int B, int L, int V, const void* tl, 
                                 const int32_t* prefix_lens, int32_t* new_seq_lens, void* ws,
                                 hipStream_t st);
 
+// Static per-device scratch of the allocation-free greedy verify: its size,
+// and its device address on the current device (looked up once per device).
+constexpr size_t kNoallocScratchBytes = size_t(1) << 20;
+hipError_t noalloc_scratch(void** out);
+
 hipError_t launch_verify_sample(bool bf16, int B, int L, int V, const void* tl, int64_t ts,
                                 const void* dl, int64_t ds, const int32_t* draft_tokens,
                                 const int32_t* chain_lens, const float* u_accept,

@@ -20,6 +20,7 @@
 // chunk-local scan inside the selected chunk.
 #include <algorithm>
 #include <climits>
+#include <mutex>
 
 #include "common.h"
 #include "launch.h"
@@ -909,6 +910,38 @@ hipError_t launch_verify_greedy(bool bf16, int B, int L, int V, const void* tl, 
                      pidx, dl ? 1 : 0, draft_tokens, lens, target_predict, accept_len, bonus,
                      commit, prefix, new_seq);
   return hipGetLastError();
+}
+
+// ---------------------------------------------- static scratch (no allocation)
+// The greedy pass's chunk partials for dflash_verify_greedy_noalloc, in place
+// of a caller workspace.  Each GPU the library runs on holds its own copy
+// until the process ends, and every call on that GPU shares it.  In host code
+// `scratch` names a host-side stand-in, never the device memory: its device
+// address comes from hipGetSymbolAddress, taken once per device with that
+// device current and kept in scratch_ptr below; only that address is ever
+// handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_verify_sample(bool bf16, int B, int L, int V, const void* tl, int64_t ts,

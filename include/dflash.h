@@ -59,8 +59,9 @@
  *             outside [0, num_pages)) are reported in band, as described at
  *             each entry point.  No exception crosses the ABI; the library
  *             never prints.
- * Threads     The library holds no mutable global state; calls from several
- *             host threads are safe.
+ * Threads     Calls from several host threads are safe.  The only global
+ *             state is the static scratch of dflash_verify_greedy_noalloc
+ *             (one buffer per GPU) and the per-device lookup of its address.
  */
 #ifndef DFLASH_H_
 #define DFLASH_H_
@@ -77,7 +78,9 @@ typedef enum {
   DFLASH_E_ARG = 1,          /* a NULL pointer, a negative or inconsistent size */
   DFLASH_E_UNSUPPORTED = 2,  /* a valid request outside what is implemented (e.g. head_dim) */
   DFLASH_E_WORKSPACE = 3,    /* ws too small or misaligned */
-  DFLASH_E_HIP = 4           /* a HIP launch failed */
+  DFLASH_E_HIP = 4,          /* a HIP launch failed */
+  DFLASH_E_TOO_LARGE = 5     /* more scratch than the allocation-free entry point's static
+                                buffer holds (dflash_verify_greedy_noalloc) */
 } dflash_status;
 
 typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
@@ -256,6 +259,41 @@ dflash_status dflash_verify_greedy(
     int32_t* target_predict, int32_t* accept_len, int32_t* bonus, int32_t* commit_lens,
     const int32_t* prefix_lens, int32_t* new_seq_lens,
     dflash_dtype dtype, void* ws, size_t ws_bytes, dflash_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * dflash_verify_greedy_noalloc -- for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): dflash_verify_greedy without a workspace.  Arguments,
+ * results, layouts and in-band errors are those of dflash_verify_greedy, and
+ * the results are bit-identical to it.
+ *
+ * Scratch   The chunk partials live in a static device buffer of
+ *           DFLASH_NOALLOC_SCRATCH_BYTES (1 MiB) that each GPU holds from the
+ *           first call on it until the process ends.  That holds every call
+ *           with B * (2L + 1) <= 131072 rows; a larger call returns
+ *           DFLASH_E_TOO_LARGE before anything is enqueued.  The call
+ *           allocates nothing (no hipMalloc, hipFree or allocating library
+ *           routine); its first call on a device looks up the buffer's
+ *           address there (hipGetSymbolAddress).
+ * Sharing   Every call on one GPU uses the same buffer, and every word a call
+ *           reads it wrote first, so no state carries between calls.  Calls
+ *           that can overlap on one GPU (concurrent streams, or several host
+ *           threads on one device) race on it: serialise them, or use
+ *           dflash_verify_greedy with a workspace each.
+ * ------------------------------------------------------------------------- */
+#define DFLASH_NOALLOC_SCRATCH_BYTES ((size_t)1 << 20)
+
+dflash_status dflash_verify_greedy_noalloc(
+    int B, int L, int V,
+    const void* target_logits, int64_t t_row_stride,
+    const void* draft_logits, int64_t d_row_stride,
+    int32_t* draft_tokens, const int32_t* chain_lens,
+    int32_t* target_predict, int32_t* accept_len, int32_t* bonus, int32_t* commit_lens,
+    const int32_t* prefix_lens, int32_t* new_seq_lens,
+    dflash_dtype dtype, dflash_stream_t stream);
+
+/* The static scratch size the library was built with (bytes). */
+size_t dflash_noalloc_scratch_bytes(void);
 
 /* ---------------------------------------------------------------------------
  * Lossless rejection-sampling verification.

@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    for s in range(5):
+    for s in range(6):
         assert dfl.status_string(s).startswith("DFLASH_")
     assert "UNKNOWN" in dfl.status_string(99)
     assert lib.dflash_version() >= 100
@@ -317,3 +317,24 @@ def test_binding_rejects_caches_not_in_head_major_layout():
         dfl._cache_pair(good, torch.empty(5, Hkv, 16, D, dtype=torch.bfloat16), Hkv, D)
     with pytest.raises(ValueError, match="device tensor"):
         dfl._cache_pair(good, good, Hkv, D)   # right shape, but host memory
+
+
+@no_gpu
+def test_noalloc_rejects_more_than_its_static_scratch(lib):
+    """dflash_verify_greedy_noalloc: the chunk partials of B*(2L+1) rows fit
+    the 1 MiB static scratch up to 131072 rows; one more row is rejected with
+    DFLASH_E_TOO_LARGE before anything touches the device; argument errors
+    come first, as in dflash_verify_greedy."""
+    assert lib.dflash_noalloc_scratch_bytes() == 1 << 20
+
+    def call(B, L, V=128256, **kw):
+        a = dict(tl=FAKE, acc=FAKE, dtype=dfl.BF16)
+        a.update(kw)
+        return lib.dflash_verify_greedy_noalloc(B, L, V, a["tl"], V, None, 0, FAKE, None, None,
+                                                a["acc"], FAKE, FAKE, None, None, a["dtype"], None)
+    assert call(131073, 0) == dfl.E_TOO_LARGE            # 131073 rows of one target row each
+    assert call(4033, 16) == dfl.E_TOO_LARGE             # 4033 * 33 = 133089 rows
+    assert call(2, 65) == dfl.E_UNSUPPORTED
+    assert call(131073, 0, acc=None) == dfl.E_ARG
+    assert call(131073, 0, dtype=9) == dfl.E_ARG
+    assert call(0, 15) == dfl.OK
