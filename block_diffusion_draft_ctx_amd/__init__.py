@@ -12,7 +12,9 @@ import os
 from typing import Optional, Sequence
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libdflash.so")
+# DFLASH_LIBRARY names another build of the same library (the AddressSanitizer
+# build of the ABI tests); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("DFLASH_LIBRARY") or os.path.join(HERE, "libdflash.so")
 
 OK, E_ARG, E_UNSUPPORTED, E_WORKSPACE, E_HIP, E_TOO_LARGE = 0, 1, 2, 3, 4, 5
 F32, BF16 = 0, 1
