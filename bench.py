@@ -12,8 +12,14 @@ random weights ~N(0, 0.02), logits ~N(0, 3), caches ~N(0, 1), all bf16 and
 resident in HBM before timing starts.
 
 Prints one JSON line (rank 0) with blocks/s, the roofline of the dominant
-kernel (block attention) measured live with HIP events, and the CPU oracle
-timed on a bounded sample of the same step.
+kernel (block attention) measured live with HIP events, every part of the
+step against its roofline (median of 50 launches after 10 warm-ups) with the
+step-level fraction, and the CPU oracle timed on a bounded sample of the same
+step.  Unless --headline-only, the line also carries one object per other
+workload of the measurement plan -- the Qwen3-4B-shaped sampled chain verify
+with DLoop gates (with the oracle's near-tie counts and its parity on the
+bench's own inputs), the 4 x 32768-row prefill materialisation, and the
+packed training mask -- each with its own roofline and oracle baseline.
 """
 import argparse
 import json
@@ -73,6 +79,12 @@ def parse():
     ap.add_argument("--layers", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=32, help="requests in the oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=8192,
+                    help="prefill: rows in the oracle sample")
+    ap.add_argument("--cpu-blocks", type=int, default=96,
+                    help="packed: blocks in the oracle sample")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="decode: skip the sub-objects of the other workloads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--breakdown", action="store_true", help="per-part timings to stderr")
@@ -322,6 +334,42 @@ def _events_ms(fn, steps, warmup):
     return a.elapsed_time(b) / steps
 
 
+def _median_us(fn, n=50, warmup=10):
+    """Median microseconds of fn() over n calls after `warmup` calls, each call
+    bracketed by HIP events on the stream the library launches on (the timing
+    protocol of the measurement plan: 10 warm-ups, then the median of 50)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    return t[n // 2] if n % 2 else 0.5 * (t[n // 2 - 1] + t[n // 2])
+
+
+def _host(t):
+    """Device tensor -> numpy in storage form (bf16 as uint16 bits)."""
+    import numpy as np
+    import torch
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def _cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count()
+
+
 def _graph_ms(fn, steps, warmup):
     """Average milliseconds of fn() replayed from a HIP graph: the calls are
     captured once (all outputs and workspaces allocated beforehand, no
@@ -440,6 +488,32 @@ def bench_sample_gate(args):
                     "hbm_frac": round(gbytes / (gms * 1e-3) / HBM_PEAK, 4),
                     "go_fraction": round(float(torch.cat([o["go"] for o in gouts]).float().mean()), 4)}
     line["accept_len_mean"] = round(float(out["accept_len"].float().mean()), 3)
+    vmed = _median_us(verify)
+    gmed = _median_us(lambda: dfl.gate(dstage[0], tstage[0], g=-0.5, out=gouts[0], workspace=wsg))
+    line["roofline"]["median_us"] = round(vmed, 2)
+    line["roofline"]["frac_at_median"] = round(vbytes / (vmed * 1e-6) / HBM_PEAK, 4)
+    line["gate"]["median_us"] = round(gmed, 2)
+    if not getattr(args, "no_cpu_baseline", False):
+        import numpy as np
+        import oracle
+        tlh, dlh, xh = _host(tl), _host(dl), _host(drafts)
+        uh, u2h = _host(u), _host(u2)
+        t0 = time.perf_counter()
+        ref = oracle.verify_sample(tlh, dlh, xh, uh, u2h, "bf16")
+        for s_ in range(S):
+            oracle.gate(dlh[:, s_ * kk:(s_ + 1) * kk], xh[:, s_ * kk:(s_ + 1) * kk], "bf16", g=-0.5)
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {
+            "value": round(B / dt, 3), "unit": "blocks/s", "cores": _cores(), "kind": "oracle",
+            "sample": f"all {B} requests of the same step: the {S} gates and the sampled chain "
+                      f"verify; {dt:.1f} s of CPU work"}
+        acc, bon = _host(out["accept_len"]).astype(np.int64), _host(out["bonus"]).astype(np.int64)
+        mism = np.flatnonzero((acc != ref.accept_len) | (bon != ref.bonus))
+        near = [b for b in mism if ref.ratio_gap[b] < 1e-5 or ref.cdf_gap[b] < 1e-5]
+        line["near_ties"] = {"ratio_lt_1e-5": int((ref.ratio_gap < 1e-5).sum()),
+                             "cdf_lt_1e-5": int((ref.cdf_gap < 1e-5).sum()), "requests": B}
+        line["oracle_parity"] = {"accept_len_or_bonus_mismatches": int(len(mism)),
+                                 "of_which_near_ties": int(len(near))}
     return line
 
 
@@ -493,6 +567,35 @@ def bench_prefill(args):
                         "unit": "TFLOP/s", "frac": round(flops / (ms * 1e-3) / BF16_PEAK, 4),
                         "traffic": None, "algorithmic_flops": flops,
                         "avg_launch_us": round(ms * 1e3, 2)}
+    med = _median_us(step)
+    line["roofline"]["median_us"] = round(med, 1)
+    line["roofline"]["frac_at_median"] = round(flops / (med * 1e-6) / BF16_PEAK, 4)
+    if not getattr(args, "no_cpu_baseline", False):
+        import numpy as np
+        import oracle
+        n = min(args.cpu_rows, rps)
+        hh = [_host(h[:n]) for h in hid]
+        Wfh, bfh = _host(Wf), _host(bfv)
+        WKh, WVh = [_host(w) for w in WK], [_host(w) for w in WV]
+        pages = _host(bt[0, :(n + 15) // 16]).astype(np.int64)
+        table = np.arange(len(pages), dtype=np.int32)[None, :]   # the rows' pages, compacted
+        epi_h = {}
+        if args.k_epilogue:
+            epi_h = dict(k_norm_weight=[_host(w) for w in epi["k_norm_weight"]], k_norm_eps=1e-6,
+                         rope_theta=1e6, rows_per_seq=n, seq_start_pos=np.zeros(1, np.int64))
+        t0 = time.perf_counter()
+        res = oracle.materialize(hh, Wfh, bfh, WKh, WVh, Hkv, D, "bf16", **epi_h)
+        for l in range(Ld):
+            for rows in (res["K"][l], res["V"][l]):
+                cache = np.zeros((len(pages), Hkv, 16, D))
+                oracle.paged_write(cache, rows, table, n, np.zeros(1, np.int64))
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {
+            "value": round(n / dt, 1), "unit": "rows/s", "cores": _cores(), "kind": "oracle",
+            "sample": f"the first {n} of the {T} rows (sequence 0, positions 0..{n - 1}): fused, "
+                      f"projected for all {Ld} layers and written to a compact copy of their "
+                      f"pages; {dt:.1f} s of CPU work, scaled to rows/s (rows are independent, "
+                      f"so the rate extrapolates linearly in T)"}
     return line
 
 
@@ -557,6 +660,24 @@ def bench_packed(args):
                         "traffic": None, "algorithmic_flops": flops,
                         "avg_launch_us": round(ms * 1e3, 2),
                         "ctx_stream_GBps": round(stream / (ms * 1e-3) / 1e9, 1)}
+    med = _median_us(step)
+    line["roofline"]["median_us"] = round(med, 1)
+    line["roofline"]["frac_at_median"] = round(flops / (med * 1e-6) / BF16_PEAK, 4)
+    if not getattr(args, "no_cpu_baseline", False):
+        import oracle
+        sel = np.linspace(0, nb - 1, min(args.cpu_blocks, nb)).round().astype(np.int64)
+        qh, kbh, vbh = _host(q)[sel], _host(kb)[sel], _host(vb)[sel]
+        ckh, cvh = _host(ck), _host(cv)
+        bth = np.repeat(_host(bt), len(sel), axis=0)
+        t0 = time.perf_counter()
+        oracle.block_attention(qh, kbh, vbh, ckh, cvh, bth, anchors[sel], "bf16",
+                               causal=args.causal)
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {
+            "value": round(len(sel) / dt, 3), "unit": "blocks/s", "cores": _cores(),
+            "kind": "oracle",
+            "sample": f"{len(sel)} of the {nb} blocks, evenly spaced in anchor order (mean anchor "
+                      f"{float(anchors[sel].mean()):.0f}), all 32 heads; {dt:.1f} s of CPU work"}
     return line
 
 
@@ -900,6 +1021,24 @@ def main():
 
     gms = _graph_ms(whole_step, args.steps, args.warmup)
     out["graph_replay"] = {"ms_per_step": round(gms, 4), "value": round(st.B / (gms * 1e-3), 1)}
+    # every part of the step: median of 50 launches after 10 warm-ups, against
+    # its roofline time max(bytes / 8 TB/s, flops / 2.5 PF)
+    parts = {}
+    for name, fn, nbytes, flops, count in (
+            ("inject", st.materialize, st.mat_bytes(), st.mat_flops(), 1),
+            ("attention", lambda: st.attention(0), st.attn_bytes(), st.attn_flops(), st.Ld),
+            ("verify", st.verify, st.verify_bytes(), 0.0, 1)):
+        med = _median_us(fn)
+        roof = max(nbytes / HBM_PEAK, flops / BF16_PEAK) * 1e6
+        parts[name] = {"median_us": round(med, 2), "launches_per_step": count,
+                       "roofline_us": round(roof, 2),
+                       "bound": "hbm" if nbytes / HBM_PEAK >= flops / BF16_PEAK else "mfma",
+                       "frac": round(roof / med, 4)}
+    out["parts"] = parts
+    out["step_roofline_frac"] = round(
+        sum(p["roofline_us"] * p["launches_per_step"] for p in parts.values()) /
+        sum(p["median_us"] * p["launches_per_step"] for p in parts.values()), 4)
+    print(f"[bench] parts {json.dumps(parts)}", file=sys.stderr, flush=True)
     if args.breakdown:
         tm = time_part(st.materialize, 10)
         tv = time_part(st.verify, 10)
@@ -919,6 +1058,27 @@ def main():
                        f"{args.cpu_sample * st.k} committed rows materialised, their block "
                        f"attention for all {st.Ld} layers at ctx {st.C}, their greedy verify "
                        f"({st.k} target + {st.k - 1} draft rows each); {dt:.1f} s of CPU work")}
+    if not args.headline_only:
+        # the other workloads of the measurement plan, each with its own
+        # roofline and oracle baseline (defaults: 4 DLoop stages, sigma 1,
+        # bidirectional block, no K epilogue)
+        del st
+        torch.cuda.empty_cache()
+        sub = argparse.Namespace(**vars(args))
+        sub.stages, sub.sigma, sub.no_gate_lse = 4, 1.0, False
+        sub.causal, sub.k_epilogue = False, False
+        out["configs"] = {}
+        for key, fn in (("qwen3_4b_sampled_verify_dloop", bench_sample_gate),
+                        ("prefill_materialize_t131072", bench_prefill),
+                        ("packed_training_mask", bench_packed)):
+            line = fn(sub)
+            for k in ("n_gpus", "steps", "warmup", "higher_is_better", "scaling", "vs_baseline",
+                      "dtype", "data"):
+                line.pop(k, None)
+            out["configs"][key] = line
+            torch.cuda.empty_cache()
+            print(f"[bench] {key}: {line['value']} {line['unit']}, roofline frac "
+                  f"{line['roofline']['frac']}", file=sys.stderr, flush=True)
     print(json.dumps(out), flush=True)
 
 
