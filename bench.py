@@ -822,7 +822,7 @@ def bench_tree_attn(args):
                       f"{C}, node budget {N} ({R} rows: root + nodes), ancestor-only mask of trees "
                       f"built from 15 drafted positions (top-{args.topk}), 32 Q / 8 KV heads x 128",
                       batch=B, ctx=C, budget=N, topk=args.topk)
-    line["roofline"] = {"kernel": "tree_attention (k_attn_bf16, tree mask)", "bound": "mfma",
+    line["roofline"] = {"kernel": "tree_attention (k_attn_wide, tree mask)", "bound": "mfma",
                         "achieved": round(flops / (ms * 1e-3) / 1e12, 1), "peak": BF16_PEAK / 1e12,
                         "unit": "TFLOP/s", "frac": round(flops / (ms * 1e-3) / BF16_PEAK, 4),
                         "traffic": None, "algorithmic_flops": flops,

@@ -58,8 +58,21 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #ifndef DFLASH_ATTN_WIDE
 #define DFLASH_ATTN_WIDE 0     // 256-row workgroups (16 wavefronts: they spill at 128 VGPRs)
 #endif
+#ifndef DFLASH_ATTN_WIDE_LAYOUT
+#define DFLASH_ATTN_WIDE_LAYOUT 1   // compute-shaped layouts go to k_attn_wide (head_dim 128)
+#endif
+#ifndef DFLASH_ATTN_WIDE_NW
+#define DFLASH_ATTN_WIDE_NW 8       // k_attn_wide: 8 wavefronts x 32 rows, or 4 x 64
+#endif
+#ifndef DFLASH_ATTN_KPF
+#define DFLASH_ATTN_KPF 4           // k_attn_wide: K fragments read ahead of their MFMA
+#endif
+#ifndef DFLASH_ATTN_PINGPONG
+#define DFLASH_ATTN_PINGPONG 0      // k_attn_wide: the two wavefronts of a SIMD in opposite orders
+#endif
 constexpr int kKT = DFLASH_ATTN_KT;  // keys per tile
 constexpr int kMaxSplitPages = 1024; // pages one split may span (16384 keys)
+constexpr int kWideNW = DFLASH_ATTN_WIDE_NW;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -540,6 +553,507 @@ void k_attn_bf16(AttnP p) {
   }
 }
 
+// Compute-shaped layout (D = 128): many query rows share one context -- the
+// packed training mask (consecutive blocks on one shared block-table row)
+// and long row lists of one request (tree attention, large blocks).  Here the
+// work is MFMA-bound, and per score the softmax costs about as many cycles on
+// the vector ALU as the two products cost on the matrix cores, so the kernel
+// is laid out to keep both pipes busy at once:
+//  * one workgroup = 4 wavefronts (one per SIMD) x 64 query rows = up to 256
+//    rows on one kv-head; every wavefront covers whole 64-key tiles, so each
+//    K and V fragment read from LDS feeds two MFMAs;
+//  * iteration t issues the P.V products of tile t-1 and the scores of tile
+//    t+1 on the matrix cores while the vector ALU runs the softmax of tile t
+//    (the three are independent), so the two pipes overlap inside one
+//    wavefront; the reference max moves lazily (by more than 2^8), and the
+//    rare accumulator rescale runs at the end of the iteration, after the
+//    products that used the old reference;
+//  * three LDS stages of K and V: tile t's V, tile t+1's K and tile t+2
+//    (being stored from registers, fetched one iteration earlier) are
+//    resident together; one barrier per tile.
+// nbw > 0: nbw consecutive requests on a shared table row per workgroup;
+// nbw == 0: chunks of rows_wg rows of one request (p.RC chunks).
+template <int D, int NWV, int JQ, bool TREE>
+__global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(NWV / 4, NWV / 4)))
+void k_attn_wide(AttnP p, int nbw, int rows_wg) {
+  static_assert(D == 128, "the wide layout is built for head_dim 128");
+  static_assert(NWV * JQ == 8 && NWV % 4 == 0, "256 query rows per workgroup");
+  constexpr int NT = 64 * NWV;
+  constexpr int CPR = D / 8;
+  constexpr int NCH = kKT * CPR;
+  constexpr int CPT = NCH / NT;
+  constexpr int KS = D + 8;
+  constexpr int VS = D + 32;
+  constexpr int NMB = D / 32;
+  constexpr int NSTG = 4;
+  static_assert(kKT == 64 && NCH % NT == 0, "tile geometry");
+  constexpr int STAGE = kKT * KS + kKT * VS;
+  __shared__ __align__(16) uint16_t smem[NSTG * STAGE];
+  __shared__ int pages[kMaxSplitPages];
+  __shared__ int first_bad;
+
+  const int G = p.Hq / p.Hkv;
+  const int k = p.k;
+  const int GK = G * k;
+  const int id = blockIdx.x;
+  const int split = id % p.S;
+  const int rest = id / p.S;
+  int g, b0, nb, r0, Mq;
+  if (nbw > 0) {
+    // kv-head fastest: with 8 kv-heads each XCD streams one head's context;
+    // groups are taken from the end (later anchors, longer contexts, first)
+    const int ngrp = (p.B + nbw - 1) / nbw;
+    g = rest % p.Hkv;
+    const int grp = ngrp - 1 - rest / p.Hkv;
+    b0 = grp * nbw;
+    nb = min(nbw, p.B - b0);
+    r0 = 0;
+    Mq = nb * GK;
+  } else {
+    // the chunks of one (request, kv-head) are numbered so that they land on
+    // one XCD back to back (workgroups are dealt to the 8 XCDs round robin)
+    const int npair = p.B * p.Hkv;
+    int pair, c;
+    if ((npair & 7) == 0) {
+      const int x = rest & 7, r2 = rest >> 3;
+      c = r2 % p.RC;
+      pair = (r2 / p.RC) * 8 + x;
+    } else {
+      c = rest % p.RC;
+      pair = rest / p.RC;
+    }
+    b0 = pair / p.Hkv;
+    g = pair - b0 * p.Hkv;
+    nb = 1;
+    r0 = c * rows_wg;
+    Mq = min(GK - r0, rows_wg);
+  }
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  // the lane's two query rows (q-blocks jq = 0, 1 of its wavefront)
+  bool qv[JQ];
+  int bq[JQ], pos[JQ], hq[JQ], jr[JQ], rr_[JQ];
+#pragma unroll
+  for (int jq = 0; jq < JQ; ++jq) {
+    const int r = 32 * JQ * w + 32 * jq + l32;
+    qv[jq] = r < Mq;
+    const int rg = r0 + (qv[jq] ? r : 0);
+    jr[jq] = rg / GK;
+    rr_[jq] = rg - jr[jq] * GK;
+    const int hg = rr_[jq] / k;
+    pos[jq] = rr_[jq] - hg * k;
+    bq[jq] = b0 + jr[jq];
+    hq[jq] = g * G + hg;
+  }
+  bf16x8 qf[JQ][D / 16];
+#pragma unroll
+  for (int jq = 0; jq < JQ; ++jq) {
+    const uint16_t* qp = p.q + (((int64_t)bq[jq] * k + pos[jq]) * p.Hq + hq[jq]) * D + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      uint4 v = qv[jq] ? *reinterpret_cast<const uint4*>(qp + 16 * s) : make_uint4(0, 0, 0, 0);
+      qf[jq][s] = as_bf16x8(v);
+    }
+  }
+
+  // context lengths: each row's own (Crow), the longest and shortest of the
+  // workgroup's requests (C, Cmin); the key list is the context up to C,
+  // then the nb requests' own keys
+  bool poison[JQ];
+  int Crow[JQ];
+#pragma unroll
+  for (int jq = 0; jq < JQ; ++jq) {
+    Crow[jq] = p.ctx[bq[jq]];
+    poison[jq] = Crow[jq] < 0 || Crow[jq] > p.max_pages * 16;
+    if (poison[jq]) Crow[jq] = 0;
+  }
+  int C = 0, Cmin = INT_MAX;
+  for (int j = 0; j < nb; ++j) {
+    int cj = p.ctx[b0 + j];
+    if (cj < 0 || cj > p.max_pages * 16) cj = 0;
+    C = max(C, cj);
+    Cmin = min(Cmin, cj);
+  }
+  const int total = C + k * nb;
+  const int nt = (total + kKT - 1) / kKT;
+  const int tps = (nt + p.S - 1) / p.S;
+  const int t0 = split * tps;
+  const int t1 = min(nt, t0 + tps);
+
+  // the split's physical pages, staged once; a bad entry poisons only the
+  // rows whose context reaches it
+  const int pg0 = t0 * (kKT / 16);
+  const int pg1 = min((t1 * kKT + 15) >> 4, (C + 15) >> 4);
+  if (threadIdx.x == 0) first_bad = INT_MAX;
+  __syncthreads();
+  {
+    const int32_t* btr = p.bt + (int64_t)b0 * p.bt_stride;
+    for (int i = pg0 + (int)threadIdx.x; i < pg1; i += NT) {
+      int pg = btr[i];
+      if (pg < 0 || pg >= p.num_pages) { atomicMin(&first_bad, i); pg = 0; }
+      pages[i - pg0] = pg;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int jq = 0; jq < JQ; ++jq) poison[jq] |= (first_bad != INT_MAX && Crow[jq] > first_bad * 16);
+
+  // tile fetch geometry (as in k_attn_bf16): chunk c of every tile is key
+  // kc[c], 16-byte column dcc
+  int kc[CPT], coff[CPT], boff[CPT];   // (offsets inside one page / one key row fit 32 bits)
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int e = (int)threadIdx.x + c * NT;
+    kc[c] = e / CPR;
+    const int dc = e - kc[c] * CPR;
+    coff[c] = (g * 16 + (kc[c] & 15)) * D + dc * 8;
+    boff[c] = g * D + dc * 8;
+  }
+  const int64_t page_elems = (int64_t)16 * p.Hkv * D;
+  const uint16_t* kblk = p.kb + (int64_t)b0 * k * p.Hkv * D;
+  const uint16_t* vblk = p.vb + (int64_t)b0 * k * p.Hkv * D;
+  u32x4 kr[CPT], vr[CPT];
+  // tiles past the split's end are fetched as its last tile (their products
+  // are never used); the fetch is branch-free (each chunk selects a context
+  // slot or a block key), so it shares a basic block with the products
+  auto fetch = [&](int tile) __attribute__((always_inline)) {
+    tile = min(tile, t1 - 1);
+    const int pbase = (tile - t0) * (kKT / 16);
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int kp = tile * kKT + kc[c];
+      const bool in_ctx = kp < C;
+      const int pi = min(pbase + (kc[c] >> 4), kMaxSplitPages - 1);
+      const int pg = pages[pi];
+      const int64_t off_c = (int64_t)(in_ctx ? pg : 0) * page_elems + coff[c];
+      const int64_t off_b = (int64_t)min(max(kp - C, 0), k * nb - 1) * p.Hkv * D + boff[c];
+      const uint16_t* pk = in_ctx ? p.ck + off_c : kblk + off_b;
+      const uint16_t* pv = in_ctx ? p.cv + off_c : vblk + off_b;
+      kr[c] = *reinterpret_cast<const u32x4*>(pk);
+      vr[c] = *reinterpret_cast<const u32x4*>(pv);
+    }
+  };
+  auto stage = [&](int st) __attribute__((always_inline)) {
+    uint16_t* Kd = smem + st * STAGE;
+    uint16_t* Vd = Kd + kKT * KS;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int e = threadIdx.x + c * NT;
+      const int dc = e - kc[c] * CPR;
+      *reinterpret_cast<u32x4*>(Kd + kc[c] * KS + dc * 8) = kr[c];
+      *reinterpret_cast<u32x4*>(Vd + kc[c] * VS + dc * 8) = vr[c];
+    }
+  };
+
+  constexpr float kLazy = 8.f;
+  float m[JQ], l[JQ];
+  f32x16 acc[JQ][NMB];
+#pragma unroll
+  for (int jq = 0; jq < JQ; ++jq) {
+    m[jq] = neg_inf();
+    l[jq] = 0.f;
+  }
+#pragma unroll
+  for (int jq = 0; jq < JQ; ++jq)
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[jq][mb][j] = 0.f;
+  const int tr_r = (lane & 15) >> 2, tr_q = lane & 3;
+  const int grp16 = lane >> 4;
+
+  // S^T[64 keys x 64 q] of the tile in stage st: sc[kb][jq][j] is the score
+  // of key 32kb + 8(j/4) + 4hh + j%4 against query row 32jq + l32
+  auto scores = [&](int st, f32x16 (&sc)[2][JQ]) __attribute__((always_inline)) {
+    const uint16_t* Ks = smem + st * STAGE;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int jq = 0; jq < JQ; ++jq)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sc[kb][jq][j] = 0.f;
+    // K fragments f = 2s + kb go through a ring of KPF registers: fragment
+    // f + KPF is read while the MFMAs of fragment f run, so an LDS read is
+    // never consumed by the instruction right after it
+    constexpr int NF = 2 * (D / 16);
+    constexpr int KPF = DFLASH_ATTN_KPF;
+    auto kaddr = [&](int f) __attribute__((always_inline)) {
+      return reinterpret_cast<const uint4*>(Ks + (32 * (f & 1) + l32) * KS + 16 * (f >> 1) + 8 * hh);
+    };
+    uint4 ring[KPF];
+#pragma unroll
+    for (int f = 0; f < KPF; ++f) ring[f] = *kaddr(f);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const uint4 a = ring[f % KPF];
+      if (f + KPF < NF) ring[f % KPF] = *kaddr(f + KPF);
+      const int kb = f & 1, s = f >> 1;
+#pragma unroll
+      for (int jq = 0; jq < JQ; ++jq)
+        sc[kb][jq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[jq][s], sc[kb][jq], 0, 0, 0);
+    }
+  };
+  // masked scores of tile `tile` set to -inf (tiles not wholly visible to
+  // every row only); kept apart from the softmax so that the softmax stays in
+  // one basic block with the products it overlaps
+  auto mask = [&](f32x16 (&sc)[2][JQ], int tile) __attribute__((always_inline)) {
+    const bool dense = tile * kKT + kKT <= (nb == 1 && !TREE && p.mode == kMaskBidir ? total : Cmin);
+    if (dense) return;
+    // a row sees the context keys [0, Crow) and, of the keys after the
+    // context, its own block's [lo, hi) -- or, with the tree mask, the root
+    // (key C) and the rows of its ancestors (bits of its mask row)
+    const int kbase = tile * kKT + 4 * hh;
+#pragma unroll
+    for (int jq = 0; jq < JQ; ++jq) {
+      if constexpr (!TREE) {
+        const int lo = C + (nbw > 0 ? jr[jq] * k : 0);
+        const int hi = lo + (p.mode == kMaskCausal ? pos[jq] + 1 : k);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int kk = kbase + 32 * kb + 8 * (j >> 2) + (j & 3);
+            const bool v = kk < Crow[jq] || (kk >= lo && kk < hi);
+            sc[kb][jq][j] = v ? sc[kb][jq][j] : neg_inf();
+          }
+      } else {
+        // Branch-free on purpose: the mask words load at clamped (valid)
+        // indices and are zeroed by selects, the shift is clamped, and the
+        // visibility is bitwise arithmetic, so the scores never pass through
+        // divergent branches.  (With short-circuit tests and a guarded shift
+        // the compiler split every element into branches, and the code it
+        // made overwrote kept scores.)  The launcher sends k > 1 only, so
+        // the mask array has rows.
+        const bool has_row = qv[jq] && pos[jq] >= 1;
+        const uint32_t* mrow = p.tm + ((int64_t)bq[jq] * (k - 1) + max(pos[jq] - 1, 0)) * p.tmw;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          // ancestor bits of this row for nodes [ybase, ybase + 64)
+          const int y0 = tile * kKT + 32 * kb - C - 1;
+          const int ybase = y0 >= 0 ? (y0 & ~31) : -32;
+          const int w0 = ybase >> 5;
+          const uint32_t wlo = mrow[min(max(w0, 0), p.tmw - 1)];
+          const uint32_t whi = mrow[min(max(w0 + 1, 0), p.tmw - 1)];
+          const bool okl = has_row && w0 >= 0 && w0 < p.tmw;
+          const bool okh = has_row && w0 + 1 >= 0 && w0 + 1 < p.tmw;
+          const uint64_t win = ((uint64_t)(okh ? whi : 0u) << 32) | (okl ? wlo : 0u);
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int kk = kbase + 32 * kb + 8 * (j >> 2) + (j & 3);
+            const int y = kk - C - 1;                       // -1: the root
+            const unsigned bit = (unsigned)(win >> min(max(y - ybase, 0), 63)) & 1u;
+            const unsigned v = (unsigned)(kk < Crow[jq]) |
+                               ((unsigned)(kk >= C) & (unsigned)(kk < total) & ((unsigned)(y < 0) | bit));
+            sc[kb][jq][j] = v ? sc[kb][jq][j] : neg_inf();
+          }
+        }
+      }
+    }
+  };
+  // softmax of a (masked) tile: the exponentials relative to the lazily
+  // moved reference, in place (pack turns them into P, bf16, in the P^T
+  // operand order: contraction index 8hh + e of k-step (kb, kk2) is key
+  // 32kb + 16kk2 + 8(e/4) + 4hh + e%4), the row sums, and the factor alpha
+  // by which the accumulators must be rescaled once the previous tile's
+  // products are in
+  auto softmax = [&](f32x16 (&sc)[2][JQ], float (&alpha)[JQ]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int jq = 0; jq < JQ; ++jq) {
+      float tmax = neg_inf();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) tmax = fmaxf(tmax, sc[kb][jq][j]);
+      tmax *= p.sl2;
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float mn = (tmax > m[jq] + kLazy) ? tmax : m[jq];
+      alpha[jq] = (mn == m[jq]) ? 1.f : __builtin_amdgcn_exp2f(m[jq] - mn);
+      m[jq] = mn;
+      const float mref = (mn == neg_inf()) ? 0.f : mn;
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(sc[kb][jq][j], p.sl2, -mref));
+          sc[kb][jq][j] = e;
+          rs += e;
+        }
+      rs += __shfl_xor(rs, 32, 64);
+      l[jq] = l[jq] * alpha[jq] + rs;
+    }
+  };
+  // the exponentials, in place in the score registers, to P (bf16)
+  auto pack = [&](const f32x16 (&sc)[2][JQ], uint4 (&pb)[2][2][JQ]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int jq = 0; jq < JQ; ++jq)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int kk2 = 0; kk2 < 2; ++kk2) {
+          const int o = 8 * kk2;
+          pb[kb][kk2][jq] = make_uint4(pack_bf16x2(sc[kb][jq][o], sc[kb][jq][o + 1]),
+                                       pack_bf16x2(sc[kb][jq][o + 2], sc[kb][jq][o + 3]),
+                                       pack_bf16x2(sc[kb][jq][o + 4], sc[kb][jq][o + 5]),
+                                       pack_bf16x2(sc[kb][jq][o + 6], sc[kb][jq][o + 7]));
+        }
+  };
+  // O^T[d x 64 q] += V^T . P^T over the tile in stage st
+  auto pv = [&](int st, const uint4 (&pb)[2][2][JQ]) __attribute__((always_inline)) {
+    const uint16_t* Vs = smem + st * STAGE + kKT * KS;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int kk2 = 0; kk2 < 2; ++kk2) {
+        const uint16_t* v0 = Vs + (32 * kb + 16 * kk2 + 4 * (grp16 >> 1) + tr_r) * VS +
+                             16 * (grp16 & 1) + 4 * tr_q;
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          const uint2 lo = lds_read_tr16(v0 + 32 * mb);
+          const uint2 hi = lds_read_tr16(v0 + 8 * VS + 32 * mb);
+          const bf16x8 a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+          for (int jq = 0; jq < JQ; ++jq)
+            acc[jq][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(pb[kb][kk2][jq]),
+                                                                   acc[jq][mb], 0, 0, 0);
+        }
+      }
+  };
+  auto rescale = [&](const float (&alpha)[JQ]) __attribute__((always_inline)) {
+    bool move = false;
+#pragma unroll
+    for (int jq = 0; jq < JQ; ++jq) move = move || alpha[jq] != 1.f;
+    if (__any(move)) {
+#pragma unroll
+      for (int jq = 0; jq < JQ; ++jq)
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) acc[jq][mb] *= alpha[jq];
+    }
+  };
+
+  if (t0 < t1) {
+    f32x16 sa[2][JQ], sb[2][JQ];
+    uint4 pa[2][2][JQ];   // P of the tile whose products come next
+    float al[JQ];
+    // tile x lives in LDS stage (x - t0) mod 4
+    auto sg = [&](int x) __attribute__((always_inline)) { return (x - t0) & (NSTG - 1); };
+    // The products, the scores and the softmax of an iteration are
+    // independent.  The two wavefronts that share a SIMD (w and w + NWV/2)
+    // take them in opposite orders -- matrix work first, or the softmax
+    // first -- so that while one keeps the matrix core busy the other runs
+    // on the vector ALU, instead of both meeting at every tile's barrier
+    // in the same phase.
+    const bool mfma_first = !DFLASH_ATTN_PINGPONG || w < NWV / 2;
+    // prologue: tiles t0, t0+1 in LDS, t0+2 in registers, scores of t0
+    fetch(t0);
+    stage(0);
+    fetch(t0 + 1);
+    stage(1);
+    fetch(t0 + 2);
+    __syncthreads();
+    scores(0, sa);
+    // iteration t0: softmax of t0, scores of t0+1 (no product yet)
+    mask(sa, t0);
+    scores(1, sb);
+    softmax(sa, al);
+    pack(sa, pa);
+    stage(2);
+    fetch(t0 + 3);
+    __syncthreads();
+    // iteration t (t0 < t < t1): products of t-1 (their P is read before the
+    // softmax of t overwrites it), scores of t+1, softmax of t, tile t+2 into
+    // the stage tile t-2 left; live stages hold V(t-1), V(t), K and V(t+1)
+    // and tile t+2.  The roles of the two score sets alternate, two tiles per
+    // trip.
+    int t = t0 + 1;
+    for (; t + 1 < t1; t += 2) {
+      mask(sb, t);
+      if (mfma_first) {
+        pv(sg(t - 1), pa);
+        scores(sg(t + 1), sa);
+        softmax(sb, al);
+      } else {
+        softmax(sb, al);
+        pv(sg(t - 1), pa);
+        scores(sg(t + 1), sa);
+      }
+      pack(sb, pa);          // after the products of t-1 have read pa
+      stage(sg(t + 2));
+      fetch(t + 3);
+      rescale(al);
+      __syncthreads();
+      mask(sa, t + 1);
+      if (mfma_first) {
+        pv(sg(t), pa);
+        scores(sg(t + 2), sb);
+        softmax(sa, al);
+      } else {
+        softmax(sa, al);
+        pv(sg(t), pa);
+        scores(sg(t + 2), sb);
+      }
+      pack(sa, pa);
+      stage(sg(t + 3));
+      fetch(t + 4);
+      rescale(al);
+      __syncthreads();
+    }
+    if (t < t1) {            // one tile left: t = t1 - 1 (its scores are in sb)
+      mask(sb, t);
+      pv(sg(t - 1), pa);
+      softmax(sb, al);
+      pack(sb, pa);
+      rescale(al);
+      pv(sg(t), pa);
+    } else {                 // the last tile (t1 - 1) has its P in pa
+      pv(sg(t - 1), pa);
+    }
+  }
+
+  // lane (q, hh) holds O^T[d][q] of q-block jq for d = 32mb + 8(j/4) + 4hh + j%4
+#pragma unroll
+  for (int jq = 0; jq < JQ; ++jq) {
+    if (!qv[jq]) continue;
+    const int b = bq[jq], h = hq[jq];
+    if (p.S == 1) {
+      const float inv = poison[jq] ? __builtin_nanf("") : 1.f / l[jq];
+      const int64_t o0 = (((int64_t)b * k + pos[jq]) * p.Hq + h) * D + 4 * hh;
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int d0 = 32 * mb + 8 * jj;
+          if (p.out_f32) {
+            *reinterpret_cast<float4*>(static_cast<float*>(p.out) + o0 + d0) =
+                make_float4(acc[jq][mb][4 * jj] * inv, acc[jq][mb][4 * jj + 1] * inv,
+                            acc[jq][mb][4 * jj + 2] * inv, acc[jq][mb][4 * jj + 3] * inv);
+          } else {
+            uint2 o;
+            o.x = pack_bf16x2(acc[jq][mb][4 * jj] * inv, acc[jq][mb][4 * jj + 1] * inv);
+            o.y = pack_bf16x2(acc[jq][mb][4 * jj + 2] * inv, acc[jq][mb][4 * jj + 3] * inv);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o0 + d0) = o;
+          }
+        }
+      if (p.lse && hh == 0)
+        p.lse[((int64_t)b * p.Hq + h) * k + pos[jq]] =
+            poison[jq] ? __builtin_nanf("") : (m[jq] + log2f(l[jq])) * kLn2;
+    } else {
+      const int64_t rowi = (((int64_t)b * p.Hkv + g) * p.S + split) * GK + rr_[jq];
+      float* op = p.po + rowi * D + 4 * hh;
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          *reinterpret_cast<float4*>(op + 32 * mb + 8 * jj) =
+              make_float4(acc[jq][mb][4 * jj], acc[jq][mb][4 * jj + 1], acc[jq][mb][4 * jj + 2],
+                          acc[jq][mb][4 * jj + 3]);
+      if (hh == 0) p.pml[rowi] = make_float2(m[jq], poison[jq] ? __builtin_nanf("") : l[jq]);
+    }
+  }
+}
+
 template <typename OutT>
 __global__ __launch_bounds__(128) void k_attn_combine(int B, int k, int Hq, int Hkv, int D, int S,
                                                      const float* __restrict__ po,
@@ -684,8 +1198,42 @@ void launch_bf16(const AttnArgs& a, AttnP p, hipStream_t st) {
                      dim3(NQ * 128), 0, st, p);
 }
 
+// Compute-shaped layouts (head_dim 128): several requests on one shared
+// table row (nbw of them per workgroup, up to 256 rows), or the rows of one
+// request cut into chunks of at most 256.
+template <int D>
+bool launch_wide(const AttnArgs& a, AttnP p, hipStream_t st) {
+  if constexpr (D != 128) {
+    return false;
+  } else {
+    if (!DFLASH_ATTN_WIDE_LAYOUT) return false;
+    const int rows = a.Hq / a.Hkv * a.k;
+    if (a.shared_table && a.mode != kMaskTree && a.B > 1 && rows <= 128) {
+      const int nbw = 256 / rows;
+      const int groups = (a.B + nbw - 1) / nbw;
+      hipLaunchKernelGGL((k_attn_wide<D, kWideNW, 8 / kWideNW, false>),
+                         dim3((unsigned)(groups * a.Hkv * p.S)), dim3(64 * kWideNW), 0, st, p, nbw, 0);
+      return true;
+    }
+    if (rows > 128 && (a.mode != kMaskTree || a.k > 1)) {
+      p.RC = (rows + 255) / 256;
+      const int rows_wg = (rows + p.RC - 1) / p.RC;
+      const dim3 grid((unsigned)(a.B * a.Hkv * p.RC * p.S));
+      if (a.mode == kMaskTree)
+        hipLaunchKernelGGL((k_attn_wide<D, kWideNW, 8 / kWideNW, true>), grid, dim3(64 * kWideNW), 0,
+                           st, p, 0, rows_wg);
+      else
+        hipLaunchKernelGGL((k_attn_wide<D, kWideNW, 8 / kWideNW, false>), grid, dim3(64 * kWideNW),
+                           0, st, p, 0, rows_wg);
+      return true;
+    }
+    return false;
+  }
+}
+
 template <int D>
 void dispatch_nw(const AttnArgs& a, AttnP p, hipStream_t st) {
+  if (launch_wide<D>(a, p, st)) return;
   const int rows = a.Hq / a.Hkv * a.k;            // query rows per request and kv-head
   // Requests on one shared table row go two (or four) to a workgroup when
   // their rows fit its 32-row slices: the shared context is then read once

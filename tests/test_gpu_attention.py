@@ -77,6 +77,7 @@ def _subset(c, sel):
     ("bf16", 1, 64, 16, 4, 64, [95], 1.0, 2306),            # k = 64: two 128-row chunks
     ("bf16", 2, 16, 40, 4, 128, [70, 300], 1.0, 2308),      # 160 rows: a partial second chunk
     ("bf16", 2, 5, 12, 3, 128, [31, 32], 2.0, 2307),        # rows not a multiple of 16
+    ("bf16", 2, 64, 32, 8, 128, [100, 1000], 1.0, 2309),    # 256 rows, splits of one tile
 ])
 def test_attention_parity(dtype, B, k, Hq, Hkv, D, ctx, qs, seed):
     log(f"attention dtype={dtype} B={B} k={k} Hq={Hq} Hkv={Hkv} D={D} ctx={ctx} seed={seed}")
@@ -254,6 +255,8 @@ def test_attention_shared_table_bad_page_poisons_only_its_readers():
     ("bf16", 1, 64, 16, 4, 64, [95], 2403),               # k = 64: block spans two key tiles
     ("bf16", 2, 5, 12, 3, 128, [31, 32], 2404),           # rows not a multiple of 16
     ("bf16", 2, 16, 64, 8, 128, [100, 513], 2405),        # G = 8
+    ("bf16", 2, 64, 32, 8, 128, [100, 1000], 2406),       # 256 rows, splits of one tile
+    ("bf16", 2, 16, 40, 4, 128, [70, 300], 2407),         # 160 rows: a partial chunk
 ])
 def test_attention_causal_parity(dtype, B, k, Hq, Hkv, D, ctx, seed):
     log(f"attention causal dtype={dtype} B={B} k={k} Hq={Hq} Hkv={Hkv} D={D} ctx={ctx}")
