@@ -573,7 +573,7 @@ void k_attn_bf16(AttnP p) {
 //    resident together; one barrier per tile.
 // nbw > 0: nbw consecutive requests on a shared table row per workgroup;
 // nbw == 0: chunks of rows_wg rows of one request (p.RC chunks).
-template <int D, int NWV, int JQ, bool TREE>
+template <int D, int NWV, int JQ, bool TREE, bool OFF32>
 __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(NWV / 4, NWV / 4)))
 void k_attn_wide(AttnP p, int nbw, int rows_wg) {
   static_assert(D == 128, "the wide layout is built for head_dim 128");
@@ -676,7 +676,12 @@ void k_attn_wide(AttnP p, int nbw, int rows_wg) {
     C = max(C, cj);
     Cmin = min(Cmin, cj);
   }
-  const int total = C + k * nb;
+  // The block keys start at the first tile boundary at or after the
+  // context (Cb), so that a tile holds context keys only (and past C, pad
+  // keys nobody sees) or block keys only: the tile's kind is uniform, and so
+  // are the base pointers of its loads.
+  const int Cb = (C + kKT - 1) / kKT * kKT;
+  const int total = Cb + k * nb;
   const int nt = (total + kKT - 1) / kKT;
   const int tps = (nt + p.S - 1) / p.S;
   const int t0 = split * tps;
@@ -690,7 +695,7 @@ void k_attn_wide(AttnP p, int nbw, int rows_wg) {
   __syncthreads();
   {
     const int32_t* btr = p.bt + (int64_t)b0 * p.bt_stride;
-    for (int i = pg0 + (int)threadIdx.x; i < pg1; i += NT) {
+    for (int i = pg0 + (int)threadIdx.x; i < min(pg1, pg0 + kMaxSplitPages); i += NT) {
       int pg = btr[i];
       if (pg < 0 || pg >= p.num_pages) { atomicMin(&first_bad, i); pg = 0; }
       pages[i - pg0] = pg;
@@ -702,37 +707,54 @@ void k_attn_wide(AttnP p, int nbw, int rows_wg) {
 
   // tile fetch geometry (as in k_attn_bf16): chunk c of every tile is key
   // kc[c], 16-byte column dcc
-  int kc[CPT], coff[CPT], boff[CPT];   // (offsets inside one page / one key row fit 32 bits)
+  // byte offsets: of chunk c inside its page (slot kc & 15, and slot 0 for
+  // pad keys), and inside one block key row
+  int kc[CPT], coff[CPT], coff0[CPT], boff[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int e = (int)threadIdx.x + c * NT;
     kc[c] = e / CPR;
     const int dc = e - kc[c] * CPR;
-    coff[c] = (g * 16 + (kc[c] & 15)) * D + dc * 8;
-    boff[c] = g * D + dc * 8;
+    coff[c] = 2 * ((g * 16 + (kc[c] & 15)) * D + dc * 8);
+    coff0[c] = 2 * (g * 16 * D + dc * 8);
+    boff[c] = 2 * (g * D + dc * 8);
   }
-  const int64_t page_elems = (int64_t)16 * p.Hkv * D;
-  const uint16_t* kblk = p.kb + (int64_t)b0 * k * p.Hkv * D;
-  const uint16_t* vblk = p.vb + (int64_t)b0 * k * p.Hkv * D;
+  const int64_t page_bytes = (int64_t)32 * p.Hkv * D;
+  const int row_bytes = 2 * p.Hkv * D;
+  const char* kblk = reinterpret_cast<const char*>(p.kb + (int64_t)b0 * k * p.Hkv * D);
+  const char* vblk = reinterpret_cast<const char*>(p.vb + (int64_t)b0 * k * p.Hkv * D);
   u32x4 kr[CPT], vr[CPT];
-  // tiles past the split's end are fetched as its last tile (their products
-  // are never used); the fetch is branch-free (each chunk selects a context
-  // slot or a block key), so it shares a basic block with the products
+  // Tiles past the split's end are fetched as its last tile (their products
+  // are never used).  The fetch is branch-free, so it shares a basic block
+  // with the products.  A pad key (a context tile's key at or past C) reads
+  // the tile's first key: a context key, so finite (its score is masked, and
+  // P = 0 times a finite V adds nothing).  With OFF32 every byte offset from
+  // the uniform base fits 32 bits (checked by the launcher), which gives
+  // loads with a scalar base and a 32-bit lane offset.
   auto fetch = [&](int tile) __attribute__((always_inline)) {
     tile = min(tile, t1 - 1);
+    const int t0k = tile * kKT;
+    const bool ctx_tile = t0k < C;
     const int pbase = (tile - t0) * (kKT / 16);
+    const char* bk = ctx_tile ? reinterpret_cast<const char*>(p.ck) : kblk;
+    const char* bv = ctx_tile ? reinterpret_cast<const char*>(p.cv) : vblk;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int kp = tile * kKT + kc[c];
-      const bool in_ctx = kp < C;
-      const int pi = min(pbase + (kc[c] >> 4), kMaxSplitPages - 1);
-      const int pg = pages[pi];
-      const int64_t off_c = (int64_t)(in_ctx ? pg : 0) * page_elems + coff[c];
-      const int64_t off_b = (int64_t)min(max(kp - C, 0), k * nb - 1) * p.Hkv * D + boff[c];
-      const uint16_t* pk = in_ctx ? p.ck + off_c : kblk + off_b;
-      const uint16_t* pv = in_ctx ? p.cv + off_c : vblk + off_b;
-      kr[c] = *reinterpret_cast<const u32x4*>(pk);
-      vr[c] = *reinterpret_cast<const u32x4*>(pv);
+      const bool pad = t0k + kc[c] >= C;
+      const int pi = min(pbase + (pad ? 0 : kc[c] >> 4), kMaxSplitPages - 1);
+      const int co = pad ? coff0[c] : coff[c];
+      const int bo = min(t0k - Cb + kc[c], k * nb - 1) * row_bytes + boff[c];
+      if constexpr (OFF32) {
+        const uint32_t oc = (uint32_t)pages[pi] * (uint32_t)page_bytes + (uint32_t)co;
+        const uint32_t off = ctx_tile ? oc : (uint32_t)bo;
+        kr[c] = *reinterpret_cast<const u32x4*>(bk + off);
+        vr[c] = *reinterpret_cast<const u32x4*>(bv + off);
+      } else {
+        const int64_t oc = (int64_t)pages[pi] * page_bytes + co;
+        const int64_t off = ctx_tile ? oc : (int64_t)bo;
+        kr[c] = *reinterpret_cast<const u32x4*>(bk + off);
+        vr[c] = *reinterpret_cast<const u32x4*>(bv + off);
+      }
     }
   };
   auto stage = [&](int st) __attribute__((always_inline)) {
@@ -799,23 +821,27 @@ void k_attn_wide(AttnP p, int nbw, int rows_wg) {
   // every row only); kept apart from the softmax so that the softmax stays in
   // one basic block with the products it overlaps
   auto mask = [&](f32x16 (&sc)[2][JQ], int tile) __attribute__((always_inline)) {
-    const bool dense = tile * kKT + kKT <= (nb == 1 && !TREE && p.mode == kMaskBidir ? total : Cmin);
+    const int tk = tile * kKT;
+    const bool dense = tk + kKT <= Cmin ||
+                       (nb == 1 && !TREE && p.mode == kMaskBidir && tk >= Cb && tk + kKT <= total);
     if (dense) return;
-    // a row sees the context keys [0, Crow) and, of the keys after the
-    // context, its own block's [lo, hi) -- or, with the tree mask, the root
-    // (key C) and the rows of its ancestors (bits of its mask row)
-    const int kbase = tile * kKT + 4 * hh;
+    // A row sees the context keys [0, Crow) and, of the block keys (from
+    // Cb), its own block's [lo, hi) -- or, with the tree mask, the root (key
+    // Cb) and the rows of its ancestors (bits of its mask row).  The tests
+    // are bitwise, without short-circuit branches, so the scores never pass
+    // through divergent code.
+    const int kbase = tk + 4 * hh;
 #pragma unroll
     for (int jq = 0; jq < JQ; ++jq) {
       if constexpr (!TREE) {
-        const int lo = C + (nbw > 0 ? jr[jq] * k : 0);
+        const int lo = Cb + (nbw > 0 ? jr[jq] * k : 0);
         const int hi = lo + (p.mode == kMaskCausal ? pos[jq] + 1 : k);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const int kk = kbase + 32 * kb + 8 * (j >> 2) + (j & 3);
-            const bool v = kk < Crow[jq] || (kk >= lo && kk < hi);
+            const unsigned v = (unsigned)(kk < Crow[jq]) | ((unsigned)(kk >= lo) & (unsigned)(kk < hi));
             sc[kb][jq][j] = v ? sc[kb][jq][j] : neg_inf();
           }
       } else {
@@ -831,7 +857,7 @@ void k_attn_wide(AttnP p, int nbw, int rows_wg) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           // ancestor bits of this row for nodes [ybase, ybase + 64)
-          const int y0 = tile * kKT + 32 * kb - C - 1;
+          const int y0 = tk + 32 * kb - Cb - 1;
           const int ybase = y0 >= 0 ? (y0 & ~31) : -32;
           const int w0 = ybase >> 5;
           const uint32_t wlo = mrow[min(max(w0, 0), p.tmw - 1)];
@@ -842,10 +868,10 @@ void k_attn_wide(AttnP p, int nbw, int rows_wg) {
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const int kk = kbase + 32 * kb + 8 * (j >> 2) + (j & 3);
-            const int y = kk - C - 1;                       // -1: the root
+            const int y = kk - Cb - 1;                      // -1: the root
             const unsigned bit = (unsigned)(win >> min(max(y - ybase, 0), 63)) & 1u;
             const unsigned v = (unsigned)(kk < Crow[jq]) |
-                               ((unsigned)(kk >= C) & (unsigned)(kk < total) & ((unsigned)(y < 0) | bit));
+                               ((unsigned)(kk >= Cb) & (unsigned)(kk < total) & ((unsigned)(y < 0) | bit));
             sc[kb][jq][j] = v ? sc[kb][jq][j] : neg_inf();
           }
         }
@@ -855,9 +881,8 @@ void k_attn_wide(AttnP p, int nbw, int rows_wg) {
   // softmax of a (masked) tile: the exponentials relative to the lazily
   // moved reference, in place (pack turns them into P, bf16, in the P^T
   // operand order: contraction index 8hh + e of k-step (kb, kk2) is key
-  // 32kb + 16kk2 + 8(e/4) + 4hh + e%4), the row sums, and the factor alpha
-  // by which the accumulators must be rescaled once the previous tile's
-  // products are in
+  // 32kb + 16kk2 + 8(e/4) + 4hh + e%4), and the factor alpha by which the
+  // accumulators and the row sum must be rescaled
   auto softmax = [&](f32x16 (&sc)[2][JQ], float (&alpha)[JQ]) __attribute__((always_inline)) {
 #pragma unroll
     for (int jq = 0; jq < JQ; ++jq) {
@@ -872,23 +897,23 @@ void k_attn_wide(AttnP p, int nbw, int rows_wg) {
       alpha[jq] = (mn == m[jq]) ? 1.f : __builtin_amdgcn_exp2f(m[jq] - mn);
       m[jq] = mn;
       const float mref = (mn == neg_inf()) ? 0.f : mn;
-      float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(sc[kb][jq][j], p.sl2, -mref));
-          sc[kb][jq][j] = e;
-          rs += e;
-        }
-      rs += __shfl_xor(rs, 32, 64);
-      l[jq] = l[jq] * alpha[jq] + rs;
+        for (int j = 0; j < 16; ++j)
+          sc[kb][jq][j] = __builtin_amdgcn_exp2f(fmaf(sc[kb][jq][j], p.sl2, -mref));
     }
   };
-  // the exponentials, in place in the score registers, to P (bf16)
-  auto pack = [&](const f32x16 (&sc)[2][JQ], uint4 (&pb)[2][2][JQ]) __attribute__((always_inline)) {
+  // The exponentials, in place in the score registers, to P (bf16), and the
+  // row sum of P as the products use it (the bf16 values, summed in fp32 two
+  // at a time by dot products with (1, 1)): the normaliser then matches the
+  // weights exactly.
+  auto pack = [&](const f32x16 (&sc)[2][JQ], uint4 (&pb)[2][2][JQ], const float (&alpha)[JQ])
+      __attribute__((always_inline)) {
+    const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
-    for (int jq = 0; jq < JQ; ++jq)
+    for (int jq = 0; jq < JQ; ++jq) {
+      float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -898,7 +923,16 @@ void k_attn_wide(AttnP p, int nbw, int rows_wg) {
                                        pack_bf16x2(sc[kb][jq][o + 2], sc[kb][jq][o + 3]),
                                        pack_bf16x2(sc[kb][jq][o + 4], sc[kb][jq][o + 5]),
                                        pack_bf16x2(sc[kb][jq][o + 6], sc[kb][jq][o + 7]));
+          const uint4 w = pb[kb][kk2][jq];
+          rs0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), ones, rs0, false);
+          rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y), ones, rs1, false);
+          rs0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z), ones, rs0, false);
+          rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), ones, rs1, false);
         }
+      float rs = rs0 + rs1;
+      rs += __shfl_xor(rs, 32, 64);
+      l[jq] = l[jq] * alpha[jq] + rs;
+    }
   };
   // O^T[d x 64 q] += V^T . P^T over the tile in stage st
   auto pv = [&](int st, const uint4 (&pb)[2][2][JQ]) __attribute__((always_inline)) {
@@ -958,7 +992,7 @@ void k_attn_wide(AttnP p, int nbw, int rows_wg) {
     mask(sa, t0);
     scores(1, sb);
     softmax(sa, al);
-    pack(sa, pa);
+    pack(sa, pa, al);
     stage(2);
     fetch(t0 + 3);
     __syncthreads();
@@ -979,7 +1013,7 @@ void k_attn_wide(AttnP p, int nbw, int rows_wg) {
         pv(sg(t - 1), pa);
         scores(sg(t + 1), sa);
       }
-      pack(sb, pa);          // after the products of t-1 have read pa
+      pack(sb, pa, al);          // after the products of t-1 have read pa
       stage(sg(t + 2));
       fetch(t + 3);
       rescale(al);
@@ -994,7 +1028,7 @@ void k_attn_wide(AttnP p, int nbw, int rows_wg) {
         pv(sg(t), pa);
         scores(sg(t + 2), sb);
       }
-      pack(sa, pa);
+      pack(sa, pa, al);
       stage(sg(t + 3));
       fetch(t + 4);
       rescale(al);
@@ -1004,7 +1038,7 @@ void k_attn_wide(AttnP p, int nbw, int rows_wg) {
       mask(sb, t);
       pv(sg(t - 1), pa);
       softmax(sb, al);
-      pack(sb, pa);
+      pack(sb, pa, al);
       rescale(al);
       pv(sg(t), pa);
     } else {                 // the last tile (t1 - 1) has its P in pa
@@ -1201,6 +1235,23 @@ void launch_bf16(const AttnArgs& a, AttnP p, hipStream_t st) {
 // Compute-shaped layouts (head_dim 128): several requests on one shared
 // table row (nbw of them per workgroup, up to 256 rows), or the rows of one
 // request cut into chunks of at most 256.
+template <int D, bool TREE>
+void launch_wide_k(const AttnArgs& a, AttnP p, dim3 grid, int nbw, int rows_wg, hipStream_t st) {
+  // every byte offset from a load's base fits 32 bits: the context cache, and
+  // the nbw requests' block rows
+  const bool off32 = (int64_t)a.num_pages * 32 * a.Hkv * D <= (int64_t)UINT32_MAX &&
+                     (int64_t)a.k * std::max(nbw, 1) * 2 * a.Hkv * D <= (int64_t)UINT32_MAX;
+  if (off32)
+    hipLaunchKernelGGL((k_attn_wide<D, kWideNW, 8 / kWideNW, TREE, true>), grid, dim3(64 * kWideNW), 0,
+                       st, p, nbw, rows_wg);
+  else
+    hipLaunchKernelGGL((k_attn_wide<D, kWideNW, 8 / kWideNW, TREE, false>), grid, dim3(64 * kWideNW), 0,
+                       st, p, nbw, rows_wg);
+}
+
+// Compute-shaped layouts (head_dim 128): several requests on one shared
+// table row (nbw of them per workgroup, up to 256 rows), or the rows of one
+// request cut into chunks of at most 256.
 template <int D>
 bool launch_wide(const AttnArgs& a, AttnP p, hipStream_t st) {
   if constexpr (D != 128) {
@@ -1208,23 +1259,25 @@ bool launch_wide(const AttnArgs& a, AttnP p, hipStream_t st) {
   } else {
     if (!DFLASH_ATTN_WIDE_LAYOUT) return false;
     const int rows = a.Hq / a.Hkv * a.k;
+    // a split's context pages must fit the kernel's page list: at most
+    // kMaxSplitPages / 4 tiles per split, for the longest key list (the
+    // context rounded up to a tile, then up to 256 block keys or one
+    // request's k)
+    const int64_t nt_max = ((int64_t)a.max_pages * 16 + kKT - 1) / kKT +
+                           (std::max<int64_t>(256, a.k) + kKT - 1) / kKT;
+    if ((nt_max + p.S - 1) / p.S * (kKT / 16) > kMaxSplitPages) return false;
     if (a.shared_table && a.mode != kMaskTree && a.B > 1 && rows <= 128) {
       const int nbw = 256 / rows;
       const int groups = (a.B + nbw - 1) / nbw;
-      hipLaunchKernelGGL((k_attn_wide<D, kWideNW, 8 / kWideNW, false>),
-                         dim3((unsigned)(groups * a.Hkv * p.S)), dim3(64 * kWideNW), 0, st, p, nbw, 0);
+      launch_wide_k<D, false>(a, p, dim3((unsigned)(groups * a.Hkv * p.S)), nbw, 0, st);
       return true;
     }
     if (rows > 128 && (a.mode != kMaskTree || a.k > 1)) {
       p.RC = (rows + 255) / 256;
       const int rows_wg = (rows + p.RC - 1) / p.RC;
       const dim3 grid((unsigned)(a.B * a.Hkv * p.RC * p.S));
-      if (a.mode == kMaskTree)
-        hipLaunchKernelGGL((k_attn_wide<D, kWideNW, 8 / kWideNW, true>), grid, dim3(64 * kWideNW), 0,
-                           st, p, 0, rows_wg);
-      else
-        hipLaunchKernelGGL((k_attn_wide<D, kWideNW, 8 / kWideNW, false>), grid, dim3(64 * kWideNW),
-                           0, st, p, 0, rows_wg);
+      if (a.mode == kMaskTree) launch_wide_k<D, true>(a, p, grid, 0, rows_wg, st);
+      else launch_wide_k<D, false>(a, p, grid, 0, rows_wg, st);
       return true;
     }
     return false;
