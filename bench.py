@@ -493,6 +493,30 @@ def bench_sample_gate(args):
     line["roofline"]["median_us"] = round(vmed, 2)
     line["roofline"]["frac_at_median"] = round(vbytes / (vmed * 1e-6) / HBM_PEAK, 4)
     line["gate"]["median_us"] = round(gmed, 2)
+    # What bounds the call: its row pass streams the target rows once (a
+    # library reduction over the same rows is the reference for the rate a
+    # pass of this size reaches), then two dependent per-request launches
+    # follow (acceptance scan + residual sums, bonus selection), each at
+    # least one dependent launch of a trivial kernel.
+    # (with the gates' normalisers reused the pass reads the target rows
+    # alone; otherwise the draft rows too)
+    rows2d = tl.view(-1, V) if reuse else torch.cat([tl.view(-1, V), dl.view(-1, V)])
+    ref_us = _median_us(lambda: torch.sum(rows2d, dim=1, dtype=torch.float32))
+    tiny = torch.zeros(16, device=dev)
+
+    def ten_launches():
+        for _ in range(10):
+            tiny.add_(1.0)
+    launch_us = _median_us(ten_launches) / 10
+    line["bounds"] = {
+        "row_pass_reference": {"what": f"torch.sum (fp32 accumulation) over the same "
+                                       f"{rows2d.shape[0]} x {V} bf16 logit rows",
+                               "median_us": round(ref_us, 2),
+                               "hbm_frac": round(vbytes / (ref_us * 1e-6) / HBM_PEAK, 4)},
+        "dependent_launch_us": round(launch_us, 2),
+        "tail_launches": 2,
+        "floor_us": round(ref_us + 2 * launch_us, 2),
+        "frac_at_floor": round(vbytes / ((ref_us + 2 * launch_us) * 1e-6) / HBM_PEAK, 4)}
     if not getattr(args, "no_cpu_baseline", False):
         import numpy as np
         import oracle
