@@ -33,6 +33,12 @@
 #include "common.h"
 #include "launch.h"
 
+// 1: the tree is built by the parallel kernel (the serial loop as its
+// fallback); 0: by the serial loop, one wavefront per request
+#ifndef DFLASH_TREE_PARALLEL
+#define DFLASH_TREE_PARALLEL 1
+#endif
+
 namespace dflash {
 namespace {
 
@@ -415,10 +421,10 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return ((uint64_t)H << 32) | L;
 }
 
-__global__ __launch_bounds__(64) void k_tree_build(TreeP p) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int b = blockIdx.x;
-  const int lane = threadIdx.x;
+// The best-first loop of one request by one wavefront (lane = its lane): the
+// serial form, used by the parallel build when a request's candidates exceed
+// its buffers.  Only wavefront-level synchronisation inside.
+__device__ void tree_build_serial(const TreeP& p, unsigned char* smem, int b, int lane) {
   const int K = p.K, NK = p.n_pos * p.K, N = p.budget;
   const int cap = tree_cap(N);
   uint64_t* e_c = reinterpret_cast<uint64_t*>(smem);       // [cap] candidate slots
@@ -431,7 +437,7 @@ __global__ __launch_bounds__(64) void k_tree_build(TreeP p) {
     s_tok[x] = p.tok[(int64_t)b * NK + x];
   }
   for (int x = lane; x < cap; x += 64) e_c[x] = 0;
-  __syncthreads();
+  wave_sync();
   // lane d holds block position d's best log-probability (a first child's term)
   const float lp_first = lane < p.n_pos ? s_lp[lane * K] : neg_inf();
   // each lane caches the best of the slots it owns (slot s: lane s % 64)
@@ -492,7 +498,7 @@ __global__ __launch_bounds__(64) void k_tree_build(TreeP p) {
     }
     wave_sync();
   }
-  __syncthreads();
+  wave_sync();
   if (lane == 0) p.n_nodes[b] = i;
   for (int x = lane; x < N; x += 64) {
     const int64_t o = (int64_t)b * N + x;
@@ -511,7 +517,7 @@ __global__ __launch_bounds__(64) void k_tree_build(TreeP p) {
       p.node_token[o] = -1; p.node_parent[o] = -2; p.node_depth[o] = 0; p.node_logp[o] = neg_inf();
     }
   }
-  __syncthreads();
+  wave_sync();
   if (p.mask) {
     // row x: bits of x and of its ancestors.  The ancestors come in falling
     // index order, so the row is written word by word from the top, each
@@ -532,6 +538,395 @@ __global__ __launch_bounds__(64) void k_tree_build(TreeP p) {
         --w;
       }
       for (; w >= 0; --w) row[w] = 0u;
+    }
+  }
+}
+
+__global__ __launch_bounds__(64) void k_tree_build(TreeP p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  tree_build_serial(p, smem, blockIdx.x, threadIdx.x);
+}
+
+// ------------------------------------------------------------ parallel build
+// The serial loop pops in the order "higher score first; equal scores by the
+// parents' pop order, then by sibling rank".  That order is a fixed total
+// order on all nodes in which a parent precedes its children (a child's score
+// is its parent's plus a log-probability <= 0), so the tree is its first
+// `budget` nodes.  The parallel build finds them without popping one at a
+// time:
+//  * grow: every frontier candidate is popped at once (a pop pushes its first
+//    child and its next sibling, as in the serial loop) until at least
+//    `budget` nodes are popped;
+//  * finish: while a frontier candidate scores at least the budget-th best
+//    popped score, such candidates are popped too.  Every node never pushed
+//    is a descendant or a later sibling of a frontier candidate and so comes
+//    after it; hence the popped set then holds the first `budget` nodes;
+//  * order: the popped nodes scoring at least that score are sorted by the
+//    total order (bitonic sort; on equal scores the comparison walks up to
+//    the first pair of differing ancestors) and the first `budget` kept.
+// A request whose buffers would overflow (huge groups of exactly equal
+// scores) is built by the serial loop instead, by its first wavefront.
+constexpr int kBT = 256;          // threads of the parallel build
+constexpr int kBI = 17;           // frontier items per thread held in registers
+
+__host__ __device__ constexpr int par_cap(int budget) { return 4 * budget + 64; }
+__host__ __device__ constexpr int pow2_at_least(int x) {
+  int v = 1;
+  while (v < x) v <<= 1;
+  return v;
+}
+
+__device__ __forceinline__ uint32_t node_meta(int par, int rank, int depth) {
+  return ((uint32_t)(par + 1) << 16) | ((uint32_t)rank << 8) | (uint32_t)depth;
+}
+__device__ __forceinline__ int meta_par(uint32_t m) { return (int)(m >> 16) - 1; }
+__device__ __forceinline__ int meta_rank(uint32_t m) { return (int)((m >> 8) & 255u); }
+__device__ __forceinline__ int meta_depth(uint32_t m) { return (int)(m & 255u); }
+
+// exclusive prefix sum of v over the workgroup's 256 threads, and the total
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* sh, uint32_t& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh[w] = x;
+  __syncthreads();
+  uint32_t base = 0;
+  total = 0;
+#pragma unroll
+  for (int i = 0; i < kBT / 64; ++i) {
+    const uint32_t t = sh[i];
+    if (i < w) base += t;
+    total += t;
+  }
+  __syncthreads();
+  return base + x - v;
+}
+
+// Does popped node x come before popped node y in the pop order?
+__device__ bool pop_before(int x, int y, const float* Ss, const uint32_t* Sm) {
+  while (x != y) {
+    const float sx = Ss[x], sy = Ss[y];
+    if (sx != sy) return sx > sy;
+    const int px = meta_par(Sm[x]), py = meta_par(Sm[y]);
+    if (px == py) return meta_rank(Sm[x]) < meta_rank(Sm[y]);
+    if (px < 0) return true;       // the root's children first
+    if (py < 0) return false;
+    x = px;
+    y = py;
+  }
+  return false;
+}
+
+__global__ __launch_bounds__(kBT) void k_tree_build_par(TreeP p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int K = p.K, NK = p.n_pos * K, N = p.budget;
+  const int CS = par_cap(N), CF = CS + 1, M = pow2_at_least(CS);
+  float* s_lp = reinterpret_cast<float*>(smem);                    // [NK]
+  int* s_tok = reinterpret_cast<int*>(s_lp + NK);                  // [NK]
+  float* Ss = reinterpret_cast<float*>(s_tok + NK);                // [CS] popped scores
+  uint32_t* Sm = reinterpret_cast<uint32_t*>(Ss + CS);             // [CS] popped (parent, rank, depth)
+  float* Fs = reinterpret_cast<float*>(Sm + CS);                   // [CF] frontier
+  uint32_t* Fm = reinterpret_cast<uint32_t*>(Fs + CF);
+  uint32_t* okey = Fm + CF;                                        // [M] sort keys
+  uint16_t* ord = reinterpret_cast<uint16_t*>(okey + M);           // [M] sort slots
+  int16_t* fin = reinterpret_cast<int16_t*>(ord + M);              // [CS] popped -> final index
+  int16_t* n_par = fin + CS;                                       // [N] final parents
+  __shared__ uint32_t sh_scan[kBT / 64];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sel_prefix, sel_k, max_f;
+  __shared__ int long_run;
+
+  for (int x = tid; x < NK; x += kBT) {
+    s_lp[x] = p.lp[(int64_t)b * NK + x];
+    s_tok[x] = p.tok[(int64_t)b * NK + x];
+  }
+  __syncthreads();
+  int nS = 0, nF = 0;
+  if (s_lp[0] != neg_inf()) {                                      // the root's first child
+    if (tid == 0) { Fs[0] = s_lp[0]; Fm[0] = node_meta(-1, 0, 1); }
+    nF = 1;
+  }
+  __syncthreads();
+
+  // Pops every frontier candidate whose order key is at least th (0: all)
+  // and pushes their first children and next siblings.  Returns false on
+  // overflow (uniform).
+  auto pop_round = [&](uint32_t th) -> bool {
+    const int ipt = (nF + kBT - 1) / kBT;
+    if (ipt > kBI) return false;
+    const int i0 = tid * ipt;
+    float fs[kBI];
+    uint32_t fm[kBI];
+    uint32_t npop = 0, npush = 0;
+#pragma unroll
+    for (int j = 0; j < kBI; ++j) {
+      const int i = i0 + j;
+      const bool have = j < ipt && i < nF;
+      fs[j] = have ? Fs[i] : neg_inf();
+      fm[j] = have ? Fm[i] : 0u;
+      if (have && ord_of(fs[j]) >= th) {
+        ++npop;
+        const int d = meta_depth(fm[j]), r = meta_rank(fm[j]);
+        if (d < p.n_pos && s_lp[d * K] != neg_inf()) ++npush;
+        if (r + 1 < K && s_lp[(d - 1) * K + r + 1] != neg_inf()) ++npush;
+      }
+    }
+    uint32_t tot;
+    const uint32_t base = block_scan(npop | (npush << 16), sh_scan, tot);
+    const int cpop = (int)(tot & 0xffffu), cpush = (int)(tot >> 16);
+    const int nrem = nF - cpop;
+    if (nS + cpop > CS || nrem + cpush > CF) return false;
+    // every thread's items are in registers: the frontier may be rewritten
+    uint32_t pp = base & 0xffffu, pu = base >> 16;
+    int rp = min(i0, nF) - (int)pp;            // remaining items before this thread's
+#pragma unroll
+    for (int j = 0; j < kBI; ++j) {
+      const int i = i0 + j;
+      if (!(j < ipt && i < nF)) continue;
+      if (ord_of(fs[j]) >= th) {
+        const int g = nS + (int)pp++;
+        Ss[g] = fs[j];
+        Sm[g] = fm[j];
+        const int d = meta_depth(fm[j]), r = meta_rank(fm[j]), par = meta_par(fm[j]);
+        if (d < p.n_pos && s_lp[d * K] != neg_inf()) {
+          const int o = nrem + (int)pu++;
+          Fs[o] = fs[j] + s_lp[d * K];
+          Fm[o] = node_meta(g, 0, d + 1);
+        }
+        if (r + 1 < K && s_lp[(d - 1) * K + r + 1] != neg_inf()) {
+          const float ps = par < 0 ? 0.f : Ss[par];
+          const int o = nrem + (int)pu++;
+          Fs[o] = ps + s_lp[(d - 1) * K + r + 1];
+          Fm[o] = node_meta(par, r + 1, d);
+        }
+      } else {
+        Fs[rp] = fs[j];
+        Fm[rp] = fm[j];
+        ++rp;
+      }
+    }
+    __syncthreads();
+    nS += cpop;
+    nF = nrem + cpush;
+    return true;
+  };
+
+  // the kth largest order key of the popped nodes (radix select, 8 bits a pass)
+  auto kth_popped_key = [&](int kth) -> uint32_t {
+    uint32_t prefix = 0, pmask = 0;
+    uint32_t krem = (uint32_t)kth;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int sh = 24 - 8 * pass;
+      hist[tid] = 0;
+      __syncthreads();
+      // the keys mostly share their high bytes: the lanes of a wavefront
+      // whose bin is its first active lane's add together, in one atomic
+      for (int g = tid; g < nS; g += kBT) {
+        const uint32_t key = ord_of(Ss[g]);
+        const bool act = (key & pmask) == prefix;
+        const uint32_t bin = (key >> sh) & 255u;
+        const uint64_t am = __ballot(act);
+        if (am) {
+          const int first = __ffsll((unsigned long long)am) - 1;
+          const uint32_t b0 = (uint32_t)__shfl((int)bin, first, 64);
+          const uint64_t same = __ballot(act && bin == b0);
+          if (lane == first) atomicAdd(&hist[b0], (uint32_t)__popcll(same));
+          if (act && bin != b0) atomicAdd(&hist[bin], 1u);
+        }
+      }
+      __syncthreads();
+      if (w == 0) {
+        // lane l holds bins 4l..4l+3; suffix sums from the top bin down
+        uint32_t c[4], s4 = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) { c[q] = hist[4 * lane + q]; s4 += c[q]; }
+        uint32_t suf = s4;                        // inclusive suffix over lanes >= lane
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t y = __shfl_down(suf, o, 64);
+          if (lane + o < 64) suf += y;
+        }
+        const uint32_t above = suf - s4;          // keys in bins of higher lanes
+        const bool mine = above < krem && krem <= suf;
+        if (mine) {
+          uint32_t acc = above;
+          int bin = 4 * lane;
+#pragma unroll
+          for (int q = 3; q >= 0; --q) {
+            if (acc + c[q] >= krem) { bin = 4 * lane + q; break; }
+            acc += c[q];
+          }
+          sel_prefix = prefix | ((uint32_t)bin << sh);
+          sel_k = krem - acc;
+        }
+      }
+      __syncthreads();
+      prefix = sel_prefix;
+      krem = sel_k;
+      pmask |= 255u << sh;
+      __syncthreads();
+    }
+    return prefix;
+  };
+
+  bool ok = true;
+  while (ok && nF > 0 && nS < N) ok = pop_round(0u);
+  // finish: th is the budget-th best key of the popped nodes when last
+  // computed; it only rises as nodes are popped, so an older value is a
+  // lower bound and the test below stays valid with it (it may pop a few
+  // nodes more).  It is recomputed after every budget / 4 new pops.
+  uint32_t th = 0;
+  int at = -N;
+  while (ok && nF > 0) {
+    if (nS - at > N / 4) {
+      th = kth_popped_key(N);
+      at = nS;
+    }
+    if (tid == 0) max_f = 0;
+    __syncthreads();
+    uint32_t mf = 0;
+    for (int i = tid; i < nF; i += kBT) mf = max(mf, ord_of(Fs[i]));
+    mf = wave_umax(mf);
+    if (lane == 0) atomicMax(&max_f, mf);
+    __syncthreads();
+    const uint32_t mfv = max_f;
+    __syncthreads();
+    if (mfv < th) break;
+    ok = pop_round(th);
+  }
+  if (!ok) {
+    // overflow: the serial loop, from scratch, in the same memory
+    if (w == 0) tree_build_serial(p, smem, b, lane);
+    return;
+  }
+  // the candidates for the first N: popped nodes at or above the budget-th
+  // best key (all popped nodes if fewer than N exist)
+  if (nS < N) th = 0;
+  else th = kth_popped_key(N);
+  uint32_t tot;
+  {
+    // slots in popped order: each thread takes a contiguous range
+    const int ipt = (nS + kBT - 1) / kBT;
+    const int g0 = tid * ipt, g1 = min(nS, g0 + ipt);
+    uint32_t c = 0;
+    for (int g = g0; g < g1; ++g) c += ord_of(Ss[g]) >= th;
+    uint32_t o = block_scan(c, sh_scan, tot);
+    for (int g = g0; g < g1; ++g) {
+      const uint32_t key = ord_of(Ss[g]);
+      if (key >= th) { okey[o] = key; ord[o++] = (uint16_t)g; }
+    }
+  }
+  const int nc = (int)tot;
+  const int Msort = pow2_at_least(max(nc, 2));
+  for (int x = nc + tid; x < Msort; x += kBT) { okey[x] = 0u; ord[x] = 0xffffu; }   // sort last
+  __syncthreads();
+  // bitonic sort of the slots by key descending, then popped index
+  // ascending (the pop order wherever the scores differ)
+  for (int size = 2; size <= Msort; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int x = tid; x < Msort / 2; x += kBT) {
+        const int lo = 2 * x - (x & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const uint32_t ka = okey[lo], kb = okey[hi];
+        const int a = ord[lo], bb = ord[hi];
+        const bool a_after = ka < kb || (ka == kb && a > bb);
+        if (a_after == up) {
+          okey[lo] = kb; okey[hi] = ka;
+          ord[lo] = (uint16_t)bb; ord[hi] = (uint16_t)a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // runs of equal scores: put each run in the pop order (its parents' pop
+  // order, then rank), by the thread that holds the run's first slot; a run
+  // longer than 32 slots sends the whole list through the exact comparison
+  if (tid == 0) long_run = 0;
+  __syncthreads();
+  for (int x = tid; x < nc; x += kBT) {
+    if ((x > 0 && okey[x - 1] == okey[x]) || x + 1 >= nc || okey[x + 1] != okey[x]) continue;
+    int e = x + 1;
+    while (e < nc && okey[e] == okey[x]) ++e;
+    if (e - x > 32) {
+      long_run = 1;
+      continue;
+    }
+    for (int i = x + 1; i < e; ++i) {            // insertion sort of ord[x, e)
+      const int v = ord[i];
+      int j = i - 1;
+      while (j >= x && pop_before(v, ord[j], Ss, Sm)) {
+        ord[j + 1] = ord[j];
+        --j;
+      }
+      ord[j + 1] = (uint16_t)v;
+    }
+  }
+  __syncthreads();
+  if (long_run) {
+    for (int size = 2; size <= Msort; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int x = tid; x < Msort / 2; x += kBT) {
+          const int lo = 2 * x - (x & (stride - 1));
+          const int hi = lo + stride;
+          const bool up = (lo & size) == 0;
+          const int a = ord[lo], bb = ord[hi];
+          const bool a_after = a == 0xffff ? bb != 0xffff
+                                           : (bb != 0xffff && pop_before(bb, a, Ss, Sm));
+          if (a_after == up) { ord[lo] = (uint16_t)bb; ord[hi] = (uint16_t)a; }
+        }
+        __syncthreads();
+      }
+    }
+  }
+  const int n = min(N, nc);
+  for (int g = tid; g < nS; g += kBT) fin[g] = -1;
+  __syncthreads();
+  for (int i = tid; i < n; i += kBT) fin[ord[i]] = (int16_t)i;
+  __syncthreads();
+  if (tid == 0) p.n_nodes[b] = n;
+  for (int x = tid; x < N; x += kBT) {
+    const int64_t o = (int64_t)b * N + x;
+    if (x < n) {
+      const int g = ord[x];
+      const uint32_t m = Sm[g];
+      const int d = meta_depth(m), par = meta_par(m);
+      const int fp = par < 0 ? -1 : fin[par];
+      p.node_token[o] = s_tok[(d - 1) * K + meta_rank(m)];
+      p.node_parent[o] = fp;
+      p.node_depth[o] = d;
+      p.node_logp[o] = Ss[g];
+      n_par[x] = (int16_t)fp;
+    } else {
+      p.node_token[o] = -1; p.node_parent[o] = -2; p.node_depth[o] = 0; p.node_logp[o] = neg_inf();
+    }
+  }
+  __syncthreads();
+  if (p.mask) {
+    // row x: bits of x and of its ancestors, written word by word from the
+    // top (the ancestors come in falling index order); unused rows are zero
+    for (int x = tid; x < N; x += kBT) {
+      uint32_t* row = p.mask + ((int64_t)b * N + x) * p.W;
+      int wd = p.W - 1;
+      if (x < n) {
+        const int top_w = x >> 5;
+        for (; wd > top_w; --wd) row[wd] = 0u;
+        uint32_t acc = 0u;
+        for (int y = x; y >= 0; y = n_par[y]) {
+          const int yw = y >> 5;
+          while (wd > yw) { row[wd] = acc; acc = 0u; --wd; }
+          acc |= 1u << (y & 31);
+        }
+        row[wd] = acc;
+        --wd;
+      }
+      for (; wd >= 0; --wd) row[wd] = 0u;
     }
   }
 }
@@ -609,7 +1004,18 @@ size_t tree_ws_bytes(int B, int n_pos, int V, int K) {
   return topk_plan((int64_t)B * n_pos, V, K).total;
 }
 
-size_t tree_build_lds_bytes(int n_pos, int K, int budget) { return tree_lds_bytes(n_pos, K, budget); }
+// the parallel build's buffers (or the serial loop's, if larger: its fallback
+// runs in the same memory)
+size_t par_lds_bytes(int n_pos, int K, int budget) {
+  const size_t CS = par_cap(budget), CF = CS + 1, M = pow2_at_least(par_cap(budget));
+  const size_t NK = (size_t)n_pos * K;
+  const size_t need = NK * 8 + CS * 8 + CF * 8 + M * 6 + CS * 2 + (size_t)budget * 2;
+  return std::max(need, tree_lds_bytes(n_pos, K, budget));
+}
+
+size_t tree_build_lds_bytes(int n_pos, int K, int budget) {
+  return DFLASH_TREE_PARALLEL ? par_lds_bytes(n_pos, K, budget) : tree_lds_bytes(n_pos, K, budget);
+}
 
 hipError_t launch_tree_build(bool bf16, int B, int n_pos, int V, const void* dl, int64_t rs,
                              float temperature, int K, int budget, int32_t* topk_tok,
@@ -637,7 +1043,10 @@ hipError_t launch_tree_build(bool bf16, int B, int n_pos, int V, const void* dl,
                      ci, part, topk_tok, topk_lp);
   TreeP p{n_pos, K, budget, (budget + 31) / 32, topk_tok, topk_lp, node_token, node_parent,
           node_depth, node_logp, n_nodes, mask};
-  hipLaunchKernelGGL(k_tree_build, dim3(B), dim3(64), tree_lds_bytes(n_pos, K, budget), st, p);
+  if (DFLASH_TREE_PARALLEL)
+    hipLaunchKernelGGL(k_tree_build_par, dim3(B), dim3(kBT), par_lds_bytes(n_pos, K, budget), st, p);
+  else
+    hipLaunchKernelGGL(k_tree_build, dim3(B), dim3(64), tree_lds_bytes(n_pos, K, budget), st, p);
   return hipGetLastError();
 }
 
