@@ -169,6 +169,33 @@ def test_tree_build_ties_and_zero_probability():
         _check_request(b, r, tok_o[b], lp_o[b], tree_o, 200, 3, 6)
 
 
+@pytest.mark.parametrize("K,n_pos,budget,flat", [
+    (2, 8, 64, 2),       # every path of a depth ties; the budget cuts a tie group
+    (16, 4, 1024, 16),   # 16 equal candidates per position: the frontier outgrows the
+                         # parallel build's buffers and the serial loop builds the tree
+])
+def test_tree_build_exact_ties(K, n_pos, budget, flat):
+    """Rows whose top `flat` logits are equal (the rest of the top-K a half
+    apart, everything else -inf): whole depths of the tree tie exactly, in
+    fp32 as in fp64, and the pops must follow the page's order for equal
+    scores (the parents' pop order, then rank) exactly as the oracle does."""
+    x = np.full((2, n_pos, 64), -np.inf, dtype=np.float32)
+    x[:, :, :K] = -0.5 * np.arange(K, dtype=np.float32)
+    x[:, :, :flat] = 0.0
+    log(f"tree_build exact ties K={K} n_pos={n_pos} budget={budget}")
+    r = dfl.tree_build(up(x, "f32"), K, budget)
+    tok_o, lp_o = oracle.topk_logprobs(x, "f32", K)
+    for b in range(2):
+        tree_o = oracle.build_tree(tok_o[b], lp_o[b], budget)
+        n = int(down(r["n_nodes"])[b])
+        assert n == len(tree_o.token)
+        np.testing.assert_array_equal(down(r["node_parent"])[b, :n], tree_o.parent)
+        np.testing.assert_array_equal(down(r["node_token"])[b, :n], tree_o.token)
+        np.testing.assert_array_equal(down(r["node_depth"])[b, :n], tree_o.depth)
+        np.testing.assert_allclose(down(r["node_logp"])[b, :n], tree_o.score, rtol=0, atol=TOL_SCORE)
+        _check_request(b, r, tok_o[b], lp_o[b], tree_o, budget, n_pos, K)
+
+
 def test_tree_build_full_size_sampled():
     """The bench's launch configuration: 64 requests, 15 block positions,
     the Qwen3 vocabulary, K = 8, budget 512; requests checked one by one on a
