@@ -568,6 +568,7 @@ __global__ __launch_bounds__(64) void k_tree_build(TreeP p) {
 // scores) is built by the serial loop instead, by its first wavefront.
 constexpr int kBT = 256;          // threads of the parallel build
 constexpr int kBI = 17;           // frontier items per thread held in registers
+constexpr int kSortE = 8;         // sort slots per thread held in registers (up to 2048 slots)
 
 __host__ __device__ constexpr int par_cap(int budget) { return 4 * budget + 64; }
 __host__ __device__ constexpr int pow2_at_least(int x) {
@@ -621,6 +622,71 @@ __device__ bool pop_before(int x, int y, const float* Ss, const uint32_t* Sm) {
   return false;
 }
 
+// Bitonic sort of MS slots (key descending, then index ascending) held in
+// registers: a slot is one 64-bit word (key, 0xffff - index) sorted
+// descending, thread t holds slots E t + e.  Exchanges inside a thread need
+// nothing, inside a wavefront a shuffle, and only the strides that span
+// wavefronts go through LDS (xch, MS words).  Every stride is a constant.
+template <int MS>
+__device__ __forceinline__ void sort_slots(uint32_t* okey, uint16_t* ord, uint64_t* xch) {
+  constexpr int E = MS / kBT;
+  static_assert(E >= 1 && E <= kSortE && E * kBT == MS, "slots per thread");
+  const int tid = threadIdx.x;
+  uint64_t v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = E * tid + e;
+    v[e] = ((uint64_t)okey[i] << 32) | (uint32_t)(0xffffu - ord[i]);
+  }
+#pragma unroll
+  for (int size = 2; size <= MS; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride < E) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if (e & stride) continue;
+          const int ep = e | stride;
+          const bool up = ((E * tid + e) & size) == 0;
+          const bool swap = up ? v[e] < v[ep] : v[e] > v[ep];
+          if (swap) { const uint64_t tmp = v[e]; v[e] = v[ep]; v[ep] = tmp; }
+        }
+      } else {
+        const int ts = stride / E;             // partner thread: tid ^ ts
+        if (ts >= 64) {
+          __syncthreads();
+#pragma unroll
+          for (int e = 0; e < E; ++e) xch[E * tid + e] = v[e];
+          __syncthreads();
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int i = E * tid + e;
+          uint64_t o;
+          if (ts >= 64) {
+            o = xch[i ^ stride];
+          } else {
+            const uint32_t lo = __shfl_xor((uint32_t)v[e], ts, 64);
+            const uint32_t hi = __shfl_xor((uint32_t)(v[e] >> 32), ts, 64);
+            o = ((uint64_t)hi << 32) | lo;
+          }
+          const bool up = (i & size) == 0;
+          const bool low = (i & stride) == 0;  // the pair's lower slot
+          // descending when up: the lower slot keeps the larger word
+          v[e] = (up == low) ? (v[e] > o ? v[e] : o) : (v[e] < o ? v[e] : o);
+        }
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    okey[E * tid + e] = (uint32_t)(v[e] >> 32);
+    ord[E * tid + e] = (uint16_t)(0xffffu - (uint32_t)v[e]);
+  }
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(kBT) void k_tree_build_par(TreeP p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int b = blockIdx.x;
@@ -655,11 +721,12 @@ __global__ __launch_bounds__(kBT) void k_tree_build_par(TreeP p) {
   __syncthreads();
 
   // Pops every frontier candidate whose order key is at least th (0: all)
-  // and pushes their first children and next siblings.  Returns false on
-  // overflow (uniform).
+  // and pushes their first children and next siblings; max_f gets the new
+  // frontier's largest key.  Returns false on overflow (uniform).
   auto pop_round = [&](uint32_t th) -> bool {
     const int ipt = (nF + kBT - 1) / kBT;
     if (ipt > kBI) return false;
+    if (tid == 0) max_f = 0;                   // ordered by the scan's barriers
     const int i0 = tid * ipt;
     float fs[kBI];
     uint32_t fm[kBI];
@@ -685,6 +752,7 @@ __global__ __launch_bounds__(kBT) void k_tree_build_par(TreeP p) {
     // every thread's items are in registers: the frontier may be rewritten
     uint32_t pp = base & 0xffffu, pu = base >> 16;
     int rp = min(i0, nF) - (int)pp;            // remaining items before this thread's
+    uint32_t mk = 0;                           // largest key left in or pushed to the frontier
 #pragma unroll
     for (int j = 0; j < kBI; ++j) {
       const int i = i0 + j;
@@ -696,32 +764,41 @@ __global__ __launch_bounds__(kBT) void k_tree_build_par(TreeP p) {
         const int d = meta_depth(fm[j]), r = meta_rank(fm[j]), par = meta_par(fm[j]);
         if (d < p.n_pos && s_lp[d * K] != neg_inf()) {
           const int o = nrem + (int)pu++;
-          Fs[o] = fs[j] + s_lp[d * K];
+          const float sc = fs[j] + s_lp[d * K];
+          Fs[o] = sc;
           Fm[o] = node_meta(g, 0, d + 1);
+          mk = max(mk, ord_of(sc));
         }
         if (r + 1 < K && s_lp[(d - 1) * K + r + 1] != neg_inf()) {
           const float ps = par < 0 ? 0.f : Ss[par];
           const int o = nrem + (int)pu++;
-          Fs[o] = ps + s_lp[(d - 1) * K + r + 1];
+          const float sc = ps + s_lp[(d - 1) * K + r + 1];
+          Fs[o] = sc;
           Fm[o] = node_meta(par, r + 1, d);
+          mk = max(mk, ord_of(sc));
         }
       } else {
         Fs[rp] = fs[j];
         Fm[rp] = fm[j];
         ++rp;
+        mk = max(mk, ord_of(fs[j]));
       }
     }
+    mk = wave_umax(mk);
+    if (lane == 0) atomicMax(&max_f, mk);
     __syncthreads();
     nS += cpop;
     nF = nrem + cpush;
     return true;
   };
 
-  // the kth largest order key of the popped nodes (radix select, 8 bits a pass)
-  auto kth_popped_key = [&](int kth) -> uint32_t {
+  // the kth largest order key of the popped nodes (radix select, 8 bits a
+  // pass); with fewer than 4 passes, the smallest key with the kth's high
+  // bytes: a lower bound of it
+  auto kth_popped_key = [&](int kth, int passes) -> uint32_t {
     uint32_t prefix = 0, pmask = 0;
     uint32_t krem = (uint32_t)kth;
-    for (int pass = 0; pass < 4; ++pass) {
+    for (int pass = 0; pass < passes; ++pass) {
       const int sh = 24 - 8 * pass;
       hist[tid] = 0;
       __syncthreads();
@@ -777,26 +854,19 @@ __global__ __launch_bounds__(kBT) void k_tree_build_par(TreeP p) {
 
   bool ok = true;
   while (ok && nF > 0 && nS < N) ok = pop_round(0u);
-  // finish: th is the budget-th best key of the popped nodes when last
-  // computed; it only rises as nodes are popped, so an older value is a
-  // lower bound and the test below stays valid with it (it may pop a few
-  // nodes more).  It is recomputed after every budget / 4 new pops.
+  // finish: th is a lower bound of the budget-th best key of the popped
+  // nodes (its high 16 bits, from when it was last computed; the key only
+  // rises as nodes are popped), which keeps the test below valid (it may pop
+  // a few nodes more).  It is recomputed after every budget / 4 new pops.
   uint32_t th = 0;
   int at = -N;
   while (ok && nF > 0) {
     if (nS - at > N / 4) {
-      th = kth_popped_key(N);
+      th = kth_popped_key(N, 2);
       at = nS;
     }
-    if (tid == 0) max_f = 0;
-    __syncthreads();
-    uint32_t mf = 0;
-    for (int i = tid; i < nF; i += kBT) mf = max(mf, ord_of(Fs[i]));
-    mf = wave_umax(mf);
-    if (lane == 0) atomicMax(&max_f, mf);
-    __syncthreads();
-    const uint32_t mfv = max_f;
-    __syncthreads();
+    const uint32_t mfv = max_f;                // from the last pop round
+    __syncthreads();                           // read by all before the next round resets it
     if (mfv < th) break;
     ok = pop_round(th);
   }
@@ -808,7 +878,7 @@ __global__ __launch_bounds__(kBT) void k_tree_build_par(TreeP p) {
   // the candidates for the first N: popped nodes at or above the budget-th
   // best key (all popped nodes if fewer than N exist)
   if (nS < N) th = 0;
-  else th = kth_popped_key(N);
+  else th = kth_popped_key(N, 4);
   uint32_t tot;
   {
     // slots in popped order: each thread takes a contiguous range
@@ -828,21 +898,29 @@ __global__ __launch_bounds__(kBT) void k_tree_build_par(TreeP p) {
   __syncthreads();
   // bitonic sort of the slots by key descending, then popped index
   // ascending (the pop order wherever the scores differ)
-  for (int size = 2; size <= Msort; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int x = tid; x < Msort / 2; x += kBT) {
-        const int lo = 2 * x - (x & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const uint32_t ka = okey[lo], kb = okey[hi];
-        const int a = ord[lo], bb = ord[hi];
-        const bool a_after = ka < kb || (ka == kb && a > bb);
-        if (a_after == up) {
-          okey[lo] = kb; okey[hi] = ka;
-          ord[lo] = (uint16_t)bb; ord[hi] = (uint16_t)a;
+  if (Msort >= kBT && Msort <= kBT * kSortE) {
+    uint64_t* xch = reinterpret_cast<uint64_t*>(Fs);    // the frontier's memory, no longer needed
+    if (Msort == kBT) sort_slots<kBT>(okey, ord, xch);
+    else if (Msort == 2 * kBT) sort_slots<2 * kBT>(okey, ord, xch);
+    else if (Msort == 4 * kBT) sort_slots<4 * kBT>(okey, ord, xch);
+    else sort_slots<8 * kBT>(okey, ord, xch);
+  } else {
+    for (int size = 2; size <= Msort; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int x = tid; x < Msort / 2; x += kBT) {
+          const int lo = 2 * x - (x & (stride - 1));
+          const int hi = lo + stride;
+          const bool up = (lo & size) == 0;
+          const uint32_t ka = okey[lo], kb = okey[hi];
+          const int a = ord[lo], bb = ord[hi];
+          const bool a_after = ka < kb || (ka == kb && a > bb);
+          if (a_after == up) {
+            okey[lo] = kb; okey[hi] = ka;
+            ord[lo] = (uint16_t)bb; ord[hi] = (uint16_t)a;
+          }
         }
+        __syncthreads();
       }
-      __syncthreads();
     }
   }
   // runs of equal scores: put each run in the pop order (its parents' pop
