@@ -28,6 +28,7 @@
 //    walked in groups of 8 row tiles so their B columns stay in its L2.
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -116,8 +117,21 @@ constexpr int BK = 64;   // granularity of split-K chunks (a multiple of the pip
 #ifndef DFLASH_GEMM_SPREAD2
 #define DFLASH_GEMM_SPREAD2 1
 #endif
+// 1: the DMA of step k + NSTG goes out during the last sub-step of step k,
+// right behind the barrier that frees its stage (every stage is loaded
+// before the first step); 0: the DMA of step k + NSTG - 1 goes out during
+// the sub-steps of step k before its last.
+#ifndef DFLASH_GEMM_EARLY
+#define DFLASH_GEMM_EARLY 1
+#endif
+
+// MFMA shape of the 256 x 256 tiles (32: 32x32x16, 16: 16x16x32)
+#ifndef DFLASH_GEMM_MT_BIG
+#define DFLASH_GEMM_MT_BIG 16
+#endif
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 enum { EPI_DENSE = 0, EPI_PAGED = 1, EPI_PARTIAL = 2 };
@@ -148,6 +162,15 @@ struct GemmP {
   const int32_t* seq_start;
   const int32_t* commit;
 };
+
+// Whether every operand byte offset of a BN-column tile fits the 32-bit
+// offsets of the buffer-resource loads: A rows of all M rows of a source,
+// B rows of one tile plus the contraction.
+inline bool buf_offsets_fit(const GemmP& p, int bn) {
+  const uint64_t lim = 0xFFFFFFFFull;
+  const uint64_t ldb = p.b_layered ? (uint64_t)p.K : (uint64_t)p.ldb;
+  return (uint64_t)p.M * p.a_seg * 2 <= lim && ((uint64_t)bn * ldb + p.K) * 2 <= lim;
+}
 
 // Uniform selection from a kernel-argument array without dynamic indexing
 // (which would copy the array to scratch memory).
@@ -242,15 +265,53 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
                :: "v"(gptr), "s"(lds_addr) : "memory", "m0");
 }
 
+// The same load through a buffer resource: lane L reads 16 bytes at byte
+// offset voff + soff of the resource (voff per lane, soff uniform), so a step
+// advance is one scalar add instead of a 64-bit address update per lane.
+__device__ __forceinline__ void dma16_buf(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_addr) : "memory", "m0");
+}
+
+// Raw buffer resource over [base, base + bytes) (untyped, range checked).
+__device__ __forceinline__ u32x4 buf_rsrc(const void* base, uint64_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  u32x4 r;
+  r[0] = (uint32_t)a;
+  r[1] = (uint32_t)(a >> 32) & 0xFFFFu;
+  r[2] = (uint32_t)min(bytes, (uint64_t)0xFFFFFFFFu);
+  r[3] = 0x00020000u;
+  return r;
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int BM_, int BN_, int WM_, int WN_, int KB_, int NSTG_, int EPI>
+// Operand fragments of one sub-step (A blocks 0..MI-1, then B blocks as
+// MI..MI+NJ-1) in the order the sub-step's MFMAs (A block t / NJ, B block
+// t % NJ) first use them.  Reads issued in this order, one per MFMA of the
+// sub-step before, give every fragment about one sub-step of lead.
+template <int MI, int NJ>
+struct FragOrder {
+  int f[MI + NJ];
+  constexpr FragOrder() : f() {
+    bool a[MI] = {}, b[NJ] = {};
+    int n = 0;
+    for (int t = 0; t < MI * NJ; ++t) {
+      if (!a[t / NJ]) { a[t / NJ] = true; f[n++] = t / NJ; }
+      if (!b[t % NJ]) { b[t % NJ] = true; f[n++] = MI + t % NJ; }
+    }
+  }
+};
+
+template <int BM_, int BN_, int WM_, int WN_, int KB_, int NSTG_, int EPI, int MT_ = 32, bool BUF = false>
 __global__ __launch_bounds__(64 * WM_ * WN_) void k_gemm_bf16(GemmP p) {
   constexpr int NW = WM_ * WN_, NT = 64 * NW;     // wavefronts (WM x WN grid), threads
-  constexpr int MI = BM_ / (32 * WM_), NJ = BN_ / (32 * WN_);   // 32x32 blocks per wave
+  // MFMA shape: 32x32x16 (MT 32) or 16x16x32 (MT 16); MI x NJ blocks per wave
+  static_assert(MT_ == 32 || MT_ == 16, "MFMA shape");
+  constexpr int MI = BM_ / (MT_ * WM_), NJ = BN_ / (MT_ * WN_);
   constexpr int ROWB = KB_ * 2;                   // bytes per operand row per stage
   constexpr int CH = KB_ / 8;                     // 16-byte chunks per row
   constexpr int RP256 = 256 / ROWB;               // rows per 256 bytes of LDS
@@ -259,7 +320,7 @@ __global__ __launch_bounds__(64 * WM_ * WN_) void k_gemm_bf16(GemmP p) {
   constexpr int AI = BM_ / RPI / NW, BI = BN_ / RPI / NW;   // DMA instructions per wave per step
   static_assert(AI * RPI * NW == BM_ && BI * RPI * NW == BN_, "DMA rows per wave");
   constexpr int DMA_PER_STEP = AI + BI;
-  static_assert(NSTG_ >= 2 && NSTG_ <= 4 && (NSTG_ - 2) * DMA_PER_STEP <= 63, "vmcnt range");
+  static_assert(NSTG_ >= 2 && NSTG_ <= 4 && (NSTG_ - 1) * DMA_PER_STEP <= 63, "vmcnt range");
   static_assert(BK % KB_ == 0 && (KB_ == 32 || KB_ == 64), "pipeline step");
   extern __shared__ __align__(16) uint16_t lds[];
   uint8_t* lb = reinterpret_cast<uint8_t*>(lds);
@@ -285,16 +346,18 @@ __global__ __launch_bounds__(64 * WM_ * WN_) void k_gemm_bf16(GemmP p) {
   const int nk = (kend - kbeg) / KB_;
 
   const uint16_t* bbase;
-  int64_t ldb;
+  int64_t ldb, brows;
   if (p.b_layered) {
     const int l = n0 / (2 * p.HD);
     const int kv = (n0 / p.HD) & 1;
     const int hd0 = n0 - (n0 / p.HD) * p.HD;
     bbase = static_cast<const uint16_t*>(kv ? pick(p.wv, l) : pick(p.wk, l)) + (int64_t)hd0 * p.K;
     ldb = p.K;
+    brows = p.HD - hd0;
   } else {
     bbase = static_cast<const uint16_t*>(p.b) + (int64_t)n0 * p.ldb;
     ldb = p.ldb;
+    brows = p.N - n0;
   }
 
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w / WN_, wn = w % WN_;
@@ -336,11 +399,27 @@ __global__ __launch_bounds__(64 * WM_ * WN_) void k_gemm_bf16(GemmP p) {
   };
   set_pos(kbeg + rot);
   const uint32_t lds0 = (uint32_t)(uintptr_t)LPTR(lb);
+  uint32_t avo[AI], bvo[BI];
+  u32x4 arsrc, brsrc;
+  const uint64_t a_bytes = (uint64_t)p.M * p.a_seg * 2;
+  if (BUF) {
+#pragma unroll
+    for (int q = 0; q < AI; ++q) avo[q] = (uint32_t)((aoff[q] + achk[q]) * 2);
+#pragma unroll
+    for (int i = 0; i < BI; ++i) bvo[i] = (uint32_t)((boff[i] + bchk[i]) * 2);
+    arsrc = buf_rsrc(pick(p.a, is_src), a_bytes);
+    brsrc = buf_rsrc(bbase, (uint64_t)brows * ldb * 2);
+  }
   // DMA instruction q (< AI + BI) of the step at the issue position into
   // stage st; the last one moves the position to the next step.
   auto dma_one = [&](int st, int q) __attribute__((always_inline)) {
     const uint32_t base = lds0 + st * STG;
-    if (q < AI) {
+    if (BUF) {
+      if (q < AI)
+        dma16_buf(arsrc, avo[q], (uint32_t)is_off * 2, base + (w * AI + q) * 1024);
+      else
+        dma16_buf(brsrc, bvo[q - AI], (uint32_t)is_k * 2, base + BM_ * ROWB + (w * BI + q - AI) * 1024);
+    } else if (q < AI) {
       dma16(acur + aoff[q] + achk[q], base + (w * AI + q) * 1024);
     } else {
       const int i = q - AI;
@@ -352,11 +431,13 @@ __global__ __launch_bounds__(64 * WM_ * WN_) void k_gemm_bf16(GemmP p) {
       acur += KB_;
       if (DFLASH_GEMM_ROT > 0 && is_k == kend) {
         set_pos(kbeg);
+        if (BUF) arsrc = buf_rsrc(pick(p.a, is_src), a_bytes);
         lgkm_drain();   // the pointer may come from a scalar load
       } else if (is_off == p.a_seg) {
         is_off = 0;
         ++is_src;
         acur = static_cast<const uint16_t*>(pick(p.a, is_src));
+        if (BUF) arsrc = buf_rsrc(acur, a_bytes);
         lgkm_drain();   // the pointer may come from a scalar load
       }
     }
@@ -366,30 +447,42 @@ __global__ __launch_bounds__(64 * WM_ * WN_) void k_gemm_bf16(GemmP p) {
     for (int q = 0; q < AI + BI; ++q) dma_one(st, q);
   };
 
-  const int r32 = lane & 31, hh = lane >> 5;
-  f32x16 acc[MI][NJ];
+  // Operand layout of both MFMA shapes: lane L holds 8 contraction values
+  // (16 bytes) of block row L % MT, chunk L / MT of the sub-step's columns.
+  // Result layout: lane L holds block column L % MT; accumulator q holds
+  // block row crow(q).
+  const int rb = lane % MT_, kq = lane / MT_;
+  using AccT = std::conditional_t<MT_ == 32, f32x16, f32x4v>;
+  constexpr int NACC = MT_ == 32 ? 16 : 4;
+  auto crow = [&](int q) __attribute__((always_inline)) {
+    return MT_ == 32 ? 8 * (q >> 2) + 4 * kq + (q & 3) : 4 * kq + q;
+  };
+  auto mfma = [](bf16x8 a, bf16x8 b, AccT c) __attribute__((always_inline)) {
+    if constexpr (MT_ == 32) return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    else return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  };
+  AccT acc[MI][NJ];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+      for (int q = 0; q < NACC; ++q) acc[i][j][q] = 0.f;
 
   // operand read offsets within a stage (row, swizzled chunk), per sub-step
-  constexpr int SS = KB_ / 16;
-  int aro[MI][SS], bro[NJ][SS];
+  constexpr int SS = KB_ / (MT_ == 32 ? 16 : 32);
+  constexpr int CPS = 64 / MT_;   // 16-byte chunks per row per sub-step
+  // the fragment register sets alternate by sub-step parity across steps
+  static_assert(SS % 2 == 0, "an even number of sub-steps per step");
+  // Block rows differ by multiples of MT (and the wave offsets by multiples
+  // of 64), which the swizzle ignores: one base per operand and sub-step,
+  // plus a constant per block (an instruction offset).
+  static_assert((MT_ / RP256) % CH == 0 && (64 / RP256) % CH == 0, "swizzle period");
+  int aro0[SS], bro0[SS];
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
-    const int row = BM_ / WM_ * wm + 32 * i + r32;
-#pragma unroll
-    for (int ss = 0; ss < SS; ++ss) aro[i][ss] = row * ROWB + 16 * ((2 * ss + hh) ^ swz(row));
-  }
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int row = BN_ / WN_ * wn + 32 * j + r32;
-#pragma unroll
-    for (int ss = 0; ss < SS; ++ss)
-      bro[j][ss] = BM_ * ROWB + row * ROWB + 16 * ((2 * ss + hh) ^ swz(row));
+  for (int ss = 0; ss < SS; ++ss) {
+    aro0[ss] = (BM_ / WM_ * wm + rb) * ROWB + 16 * ((CPS * ss + kq) ^ swz(rb));
+    bro0[ss] = (BM_ + BN_ / WN_ * wn + rb) * ROWB + 16 * ((CPS * ss + kq) ^ swz(rb));
   }
 
   // Software pipeline over steps of KB contraction columns, SS sub-steps of
@@ -406,9 +499,9 @@ __global__ __launch_bounds__(64 * WM_ * WN_) void k_gemm_bf16(GemmP p) {
   // fragment f of sub-step ss: A blocks first (f < MI), then B blocks
   auto read_one = [&](int set, const uint8_t* sb, int ss, int f) __attribute__((always_inline)) {
     if (f < MI)
-      fa[set][f] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sb + aro[f][ss]));
+      fa[set][f] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sb + aro0[ss] + MT_ * f * ROWB));
     else
-      fb[set][f - MI] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sb + bro[f - MI][ss]));
+      fb[set][f - MI] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sb + bro0[ss] + MT_ * (f - MI) * ROWB));
   };
   // wait until at most `ahead` steps of DMA are outstanding (ahead < NSTG - 1)
   auto wait_steps = [&](int ahead) __attribute__((always_inline)) {
@@ -424,80 +517,94 @@ __global__ __launch_bounds__(64 * WM_ * WN_) void k_gemm_bf16(GemmP p) {
   constexpr int SPREAD = NSTG_ == 2 ? (SS - 1 < DFLASH_GEMM_SPREAD2 ? SS - 1 : DFLASH_GEMM_SPREAD2) : SS - 1;
   constexpr int SLOTS = SPREAD * MF;   // (with more DMA instructions than slots, several share one)
 
-  for (int s = 0; s < NSTG_ - 1 && s < nk; ++s) issue(s);
-  if (nk > 0) {
-    wait_steps(min(NSTG_ - 2, nk - 1));
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int f = 0; f < NF; ++f) read_one(0, lb, 0, f);
-  }
-  lgkm_drain();
-  // mode 0: issue the DMA of step kt+NSTG-1; 1: nothing left to issue;
-  // 2: the final step (no hand-over to a next step)
-  auto step = [&](int kt, int mode) __attribute__((always_inline)) {
-    const uint8_t* sb = lb + (kt % NSTG_) * STG;
-    const int dst = (kt + NSTG_ - 1) % NSTG_;
-#pragma unroll
-    for (int ss = 0; ss < SS; ++ss) {
-      const int c = ss & 1;
-      // fragments for the next sub-step: this stage, or the next stage once
-      // every wave has its DMA and is done with this stage
-      const uint8_t* rsb = sb;
-      int rss = ss + 1;
-      const bool rd = ss + 1 < SS || mode != 2;
-      if (ss + 1 == SS && mode != 2) {
-        wait_steps(min(NSTG_ - 2, nk - 2 - kt));
-        lgkm_drain();   // own reads of this stage are done
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        rsb = lb + ((kt + 1) % NSTG_) * STG;
-        rss = 0;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int t = 0; t < MF; ++t) {
-        const int i = t / NJ, j = t % NJ;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][i], fb[c][j], acc[i][j], 0, 0, 0);
-        // fragment t rides on MFMA t; any beyond the last MFMA follow it
-        if (rd) {
-#pragma unroll
-          for (int f = 0; f < NF; ++f)
-            if (f == t || (t == MF - 1 && f > t)) read_one(c ^ 1, rsb, rss, f);
-        }
-        if (mode == 0 && ss < SPREAD) {
-          const int slot = ss * MF + t;
-#pragma unroll
-          for (int q = 0; q < DMA_PER_STEP; ++q)
-            if (q * SLOTS / DMA_PER_STEP == slot) {
-              __builtin_amdgcn_sched_barrier(0);
-              dma_one(dst, q);
-            }
+  {
+    constexpr bool EARLY = DFLASH_GEMM_EARLY;
+    for (int s = 0; s < NSTG_ - (EARLY ? 0 : 1) && s < nk; ++s) issue(s);
+    if (nk > 0) {
+      if (EARLY && nk >= NSTG_) wait_vmcnt<(NSTG_ - 1) * DMA_PER_STEP>();   // step 0 of NSTG
+      else wait_steps(min(NSTG_ - 2, nk - 1));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+  #pragma unroll
+      for (int f = 0; f < NF; ++f) read_one(0, lb, 0, f);
+    }
+    lgkm_drain();
+    // mode 0: issue the DMA of step kt+NSTG-1; 1: nothing left to issue;
+    // 2: the final step (no hand-over to a next step)
+    auto step = [&](int kt, int mode) __attribute__((always_inline)) {
+      const uint8_t* sb = lb + (kt % NSTG_) * STG;
+      const int dst = (kt + NSTG_ - 1) % NSTG_;
+  #pragma unroll
+      for (int ss = 0; ss < SS; ++ss) {
+        const int c = ss & 1;
+        // fragments for the next sub-step: this stage, or the next stage once
+        // every wave has its DMA and is done with this stage
+        const uint8_t* rsb = sb;
+        int rss = ss + 1;
+        const bool rd = ss + 1 < SS || mode != 2;
+        if (ss + 1 == SS && mode != 2) {
+          wait_steps(min(NSTG_ - 2, nk - 2 - kt));
+          lgkm_drain();   // own reads of this stage are done
+          __builtin_amdgcn_s_barrier();
+          asm volatile("" ::: "memory");
+          rsb = lb + ((kt + 1) % NSTG_) * STG;
+          rss = 0;
         }
         __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+        for (int t = 0; t < MF; ++t) {
+          const int i = t / NJ, j = t % NJ;
+          acc[i][j] = mfma(fa[c][i], fb[c][j], acc[i][j]);
+          // the t-th fragment in first-use order rides on MFMA t; any beyond
+          // the last MFMA follow it
+          if (rd) {
+            constexpr FragOrder<MI, NJ> fo;
+            if (t < NF) read_one(c ^ 1, rsb, rss, fo.f[t]);
+            if (t == MF - 1) {
+  #pragma unroll
+              for (int u = MF; u < NF; ++u) read_one(c ^ 1, rsb, rss, fo.f[u]);
+            }
+          }
+          if (EARLY && mode == 0 && ss + 1 == SS) {
+            // DMA instructions q with q * MF / DMA_PER_STEP == t
+  #pragma unroll
+            for (int q = (t * DMA_PER_STEP + MF - 1) / MF; q < ((t + 1) * DMA_PER_STEP + MF - 1) / MF; ++q) {
+              __builtin_amdgcn_sched_barrier(0);
+              dma_one(kt % NSTG_, q);
+            }
+          }
+          if (!EARLY && mode == 0 && ss < SPREAD) {
+            const int slot = ss * MF + t;
+  #pragma unroll
+            for (int q = 0; q < DMA_PER_STEP; ++q)
+              if (q * SLOTS / DMA_PER_STEP == slot) {
+                __builtin_amdgcn_sched_barrier(0);
+                dma_one(dst, q);
+              }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-    }
-  };
-  const int n_issue = max(0, nk - (NSTG_ - 1));   // steps that still issue a DMA
-  int kt = 0;
-  for (; kt < n_issue; ++kt) step(kt, 0);
-  for (; kt < nk - 1; ++kt) step(kt, 1);
-  if (nk > 0) step(nk - 1, 2);
+    };
+    const int n_issue = max(0, nk - (NSTG_ - (EARLY ? 0 : 1)));   // steps that still issue a DMA
+    int kt = 0;
+    for (; kt < n_issue; ++kt) step(kt, 0);
+    for (; kt < nk - 1; ++kt) step(kt, 1);
+    if (nk > 0) step(nk - 1, 2);
+  }
   wait_vmcnt<0>();
   __syncthreads();   // every wave is done with the stages before they are reused
 
-  // C layout of the 32x32 MFMA: lane holds column (lane % 32); accumulator q
-  // holds row 8*(q/4) + 4*(lane/32) + q%4.
   if (EPI == EPI_PARTIAL) {
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int row = m0 + BM_ / WM_ * wm + 32 * i + 8 * (q >> 2) + 4 * hh + (q & 3);
+      for (int q = 0; q < NACC; ++q) {
+        const int row = m0 + BM_ / WM_ * wm + MT_ * i + crow(q);
         if (row >= p.M) continue;
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-          p.part[((int64_t)split * p.M + row) * p.N + n0 + BN_ / WN_ * wn + 32 * j + r32] = acc[i][j][q];
+          p.part[((int64_t)split * p.M + row) * p.N + n0 + BN_ / WN_ * wn + MT_ * j + rb] = acc[i][j][q];
       }
     return;
   }
@@ -508,14 +615,14 @@ __global__ __launch_bounds__(64 * WM_ * WN_) void k_gemm_bf16(GemmP p) {
   uint16_t* ot = lds;           // [BM][OS] bf16 (reuses the operand stages)
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int cl = BN_ / WN_ * wn + 32 * j + r32;
+    const int cl = BN_ / WN_ * wn + MT_ * j + rb;
     const float bias = (EPI == EPI_DENSE && p.bias)
                            ? bf16_to_f32(static_cast<const uint16_t*>(p.bias)[n0 + cl]) : 0.f;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int rl = BM_ / WM_ * wm + 32 * i + 8 * (q >> 2) + 4 * hh + (q & 3);
+      for (int q = 0; q < NACC; ++q) {
+        const int rl = BM_ / WM_ * wm + MT_ * i + crow(q);
         ot[rl * OS + cl] = f32_to_bf16(acc[i][j][q] + bias);
       }
   }
@@ -875,13 +982,16 @@ Plan plan_gemm(int64_t M, int64_t N, int64_t K, bool bf16, int64_t col_block) {
   return Plan{bm, bn, (int)ks, (int)kchunk};
 }
 
-template <int BM_, int BN_, int WM_, int WN_, int KB_, int NSTG_>
+template <int BM_, int BN_, int WM_, int WN_, int KB_, int NSTG_, int MT_ = 32, bool BUF = false>
 void launch_bf16_gemm(GemmP p, int epi, dim3 grid, hipStream_t st) {
   const size_t lds = gemm_lds_bytes<BM_, BN_, KB_, NSTG_>();
   const dim3 block(64 * WM_ * WN_);
-  if (epi == EPI_DENSE) hipLaunchKernelGGL((k_gemm_bf16<BM_, BN_, WM_, WN_, KB_, NSTG_, EPI_DENSE>), grid, block, lds, st, p);
-  else if (epi == EPI_PAGED) hipLaunchKernelGGL((k_gemm_bf16<BM_, BN_, WM_, WN_, KB_, NSTG_, EPI_PAGED>), grid, block, lds, st, p);
-  else hipLaunchKernelGGL((k_gemm_bf16<BM_, BN_, WM_, WN_, KB_, NSTG_, EPI_PARTIAL>), grid, block, lds, st, p);
+  if (epi == EPI_DENSE)
+    hipLaunchKernelGGL((k_gemm_bf16<BM_, BN_, WM_, WN_, KB_, NSTG_, EPI_DENSE, MT_, BUF>), grid, block, lds, st, p);
+  else if (epi == EPI_PAGED)
+    hipLaunchKernelGGL((k_gemm_bf16<BM_, BN_, WM_, WN_, KB_, NSTG_, EPI_PAGED, MT_, BUF>), grid, block, lds, st, p);
+  else
+    hipLaunchKernelGGL((k_gemm_bf16<BM_, BN_, WM_, WN_, KB_, NSTG_, EPI_PARTIAL, MT_, BUF>), grid, block, lds, st, p);
 }
 
 void run_gemm(bool bf16, GemmP p, int epi_final, hipStream_t st) {
@@ -891,8 +1001,14 @@ void run_gemm(bool bf16, GemmP p, int epi_final, hipStream_t st) {
   const int epi = pl.ksplit > 1 ? EPI_PARTIAL : epi_final;
   if (bf16) {
     const dim3 grid((unsigned)(cdiv(p.M, pl.bm) * (p.N / pl.bn)), (unsigned)pl.ksplit);
-    if (pl.bm == 256 && pl.bn == 256)
-      launch_bf16_gemm<256, 256, DFLASH_GEMM_BIG_WM, DFLASH_GEMM_BIG_WN, DFLASH_GEMM_KB_BIG, DFLASH_GEMM_NSTG_BIG>(p, epi, grid, st);
+    if (pl.bm == 256 && pl.bn == 256) {
+      if (buf_offsets_fit(p, 256))
+        launch_bf16_gemm<256, 256, DFLASH_GEMM_BIG_WM, DFLASH_GEMM_BIG_WN, DFLASH_GEMM_KB_BIG, DFLASH_GEMM_NSTG_BIG,
+                         DFLASH_GEMM_MT_BIG, true>(p, epi, grid, st);
+      else
+        launch_bf16_gemm<256, 256, DFLASH_GEMM_BIG_WM, DFLASH_GEMM_BIG_WN, DFLASH_GEMM_KB_BIG, DFLASH_GEMM_NSTG_BIG,
+                         DFLASH_GEMM_MT_BIG>(p, epi, grid, st);
+    }
     else if (pl.bm == 32)
       launch_bf16_gemm<32, 256, 1, 4, 64, 4>(p, epi, grid, st);
     else if (pl.bm == 64)
