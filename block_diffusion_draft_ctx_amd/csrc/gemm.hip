@@ -129,6 +129,10 @@ constexpr int BK = 64;   // granularity of split-K chunks (a multiple of the pip
 #ifndef DFLASH_GEMM_MT_BIG
 #define DFLASH_GEMM_MT_BIG 16
 #endif
+// MFMA shape of the smaller tiles
+#ifndef DFLASH_GEMM_MT_SMALL
+#define DFLASH_GEMM_MT_SMALL 32
+#endif
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -1010,15 +1014,16 @@ void run_gemm(bool bf16, GemmP p, int epi_final, hipStream_t st) {
                          DFLASH_GEMM_MT_BIG>(p, epi, grid, st);
     }
     else if (pl.bm == 32)
-      launch_bf16_gemm<32, 256, 1, 4, 64, 4>(p, epi, grid, st);
+      launch_bf16_gemm<32, 256, 1, 4, 64, 4, DFLASH_GEMM_MT_SMALL>(p, epi, grid, st);
     else if (pl.bm == 64)
-      launch_bf16_gemm<64, 256, 1, 4, 64, 3>(p, epi, grid, st);
+      launch_bf16_gemm<64, 256, 1, 4, 64, 3, DFLASH_GEMM_MT_SMALL>(p, epi, grid, st);
     else if (pl.bm == 128 && pl.bn == 256)
-      launch_bf16_gemm<128, 256, 2, 2, 64, 3>(p, epi, grid, st);
+      launch_bf16_gemm<128, 256, 2, 2, 64, 3, DFLASH_GEMM_MT_SMALL>(p, epi, grid, st);
     else if (pl.bm == 256)
-      launch_bf16_gemm<256, 128, 2, 2, DFLASH_GEMM_KB_SMALL, DFLASH_GEMM_NSTG_SMALL>(p, epi, grid, st);
+      launch_bf16_gemm<256, 128, 2, 2, DFLASH_GEMM_KB_SMALL, DFLASH_GEMM_NSTG_SMALL, DFLASH_GEMM_MT_SMALL>(p, epi, grid, st);
     else
-      launch_bf16_gemm<128, 128, 2, DFLASH_GEMM_SMALL_WN, DFLASH_GEMM_KB_SMALL, DFLASH_GEMM_NSTG_SMALL>(p, epi, grid, st);
+      launch_bf16_gemm<128, 128, 2, DFLASH_GEMM_SMALL_WN, DFLASH_GEMM_KB_SMALL, DFLASH_GEMM_NSTG_SMALL,
+                       DFLASH_GEMM_MT_SMALL>(p, epi, grid, st);
   } else {
     const dim3 grid((unsigned)(cdiv(p.M, 64) * cdiv(p.N, 64)), (unsigned)pl.ksplit);
     if (epi == EPI_DENSE) hipLaunchKernelGGL(k_gemm_f32<EPI_DENSE>, grid, dim3(256), 0, st, p);
