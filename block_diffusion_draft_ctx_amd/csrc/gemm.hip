@@ -479,9 +479,10 @@ __global__ __launch_bounds__(64 * WM_ * WN_) void k_gemm_bf16(GemmP p) {
   // the fragment register sets alternate by sub-step parity across steps
   static_assert(SS % 2 == 0, "an even number of sub-steps per step");
   // Block rows differ by multiples of MT (and the wave offsets by multiples
-  // of 64), which the swizzle ignores: one base per operand and sub-step,
+  // of the wave tile), which the swizzle ignores: one base per operand and sub-step,
   // plus a constant per block (an instruction offset).
-  static_assert((MT_ / RP256) % CH == 0 && (64 / RP256) % CH == 0, "swizzle period");
+  static_assert((MT_ / RP256) % CH == 0 && (BM_ / WM_ / RP256) % CH == 0 && (BN_ / WN_ / RP256) % CH == 0,
+                "swizzle period");
   int aro0[SS], bro0[SS];
 #pragma unroll
   for (int ss = 0; ss < SS; ++ss) {
@@ -972,6 +973,12 @@ Plan plan_gemm(int64_t M, int64_t N, int64_t K, bool bf16, int64_t col_block) {
   if (split_ok || t256 >= DFLASH_GEMM_BIG_UNSPLIT_MIN) {
     const int64_t ks0 = split_ok ? cdiv(kCUs, t256) : 1;
     const int64_t kchunk = cdiv(cdiv(K, ks0), BK) * BK;
+    // Unsplit, 192-row tiles when their rounds of workgroups take clearly
+    // less time (rounds x tile rows): 160 256-row tiles of a 1024-row product
+    // leave 96 CUs idle, 240 192-row ones fill them.
+    const int64_t t192 = cdiv(M, 192) * (N / 256);
+    if (ks0 == 1 && 10 * cdiv(t192, kCUs) * 192 < 9 * cdiv(t256, kCUs) * 256)
+      return Plan{192, 256, 1, (int)cdiv(K, BK) * BK};
     return Plan{256, 256, (int)cdiv(K, kchunk), (int)kchunk};
   }
   const int bm = DFLASH_GEMM_SMALL_BM, bn = 128;
@@ -1012,6 +1019,12 @@ void run_gemm(bool bf16, GemmP p, int epi_final, hipStream_t st) {
       else
         launch_bf16_gemm<256, 256, DFLASH_GEMM_BIG_WM, DFLASH_GEMM_BIG_WN, DFLASH_GEMM_KB_BIG, DFLASH_GEMM_NSTG_BIG,
                          DFLASH_GEMM_MT_BIG>(p, epi, grid, st);
+    }
+    else if (pl.bm == 192) {
+      if (buf_offsets_fit(p, 256))
+        launch_bf16_gemm<192, 256, 2, 4, 64, 2, DFLASH_GEMM_MT_BIG, true>(p, epi, grid, st);
+      else
+        launch_bf16_gemm<192, 256, 2, 4, 64, 2, DFLASH_GEMM_MT_BIG>(p, epi, grid, st);
     }
     else if (pl.bm == 32)
       launch_bf16_gemm<32, 256, 1, 4, 64, 4, DFLASH_GEMM_MT_SMALL>(p, epi, grid, st);

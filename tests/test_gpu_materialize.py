@@ -118,17 +118,18 @@ def test_materialize_decode_launch_config_sampled():
 
 @pytest.mark.parametrize("n_seq,rps,seed", [(125, 8, 2415), (65, 16, 2416)])
 def test_materialize_ragged_rows_on_large_tiles(n_seq, rps, seed):
-    """Row counts that are not a multiple of the 256-row tile (T = 1000 and
-    1040) at full width: the fusion GEMM splits its contraction over 256 x 256
-    tiles and the K/V GEMM runs 256 x 256 tiles whole, both with a partial
-    last row tile; rows in and around that tile are checked."""
+    """Row counts that are not a multiple of the row tile (T = 1000 and 1040)
+    at full width: the fusion GEMM splits its contraction over 256 x 256 tiles
+    and the K/V GEMM runs 192 x 256 tiles whole (240 tiles fill the CUs where
+    256-row ones would leave some idle), both with a partial last row tile;
+    rows at the tile edges of both tilings are checked."""
     c = synth.materialize_case(seed, dtype="bf16", m=5, d_model=4096, n_layers=5, n_kv_heads=8,
                                head_dim=128, n_seq=n_seq, rows_per_seq=rps, commit="random")
     T = c.T
     log(f"materialise ragged T={T}")
     ck, cv, h = _run(c)
     rng = np.random.default_rng(seed)
-    rows = sorted({0, 255, 256, 767, 768, T - 2, T - 1, *rng.choice(T, size=16, replace=False).tolist()})
+    rows = sorted({0, 191, 192, 255, 256, 767, 768, 959, 960, T - 2, T - 1, *rng.choice(T, size=16, replace=False).tolist()})
     _check(c, ck, cv, h, rows=np.asarray(rows))
 
 
