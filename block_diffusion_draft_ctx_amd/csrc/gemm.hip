@@ -6,12 +6,15 @@
 // request go into its paged draft KV cache.
 //
 // Design.  Both products are "NT" GEMMs (every operand row is contiguous
-// along the contraction), run on the gfx950 MFMA 32x32x16 bf16 instruction.
-//  * Tiles: 256 x 256 with eight wavefronts (2 x 4, two per SIMD, each
-//    128 x 64) when there are enough of them to fill the chip, else
-//    128 x 128 with four; operands stream straight from global memory into
+// along the contraction), run on the gfx950 bf16 MFMAs: 16x16x32 on the
+// large tiles, 32x32x16 on the smaller ones.
+//  * Tiles: 256 x 256 (or 192 x 256 when one round of those fills more CUs)
+//    with eight wavefronts (2 x 4, two per SIMD) when there are enough of
+//    them to fill the chip, else 128 x 128 with four, or BM x 256 for
+//    products of few rows; operands stream straight from global memory into
 //    LDS (no staging registers) through a software pipeline of 64-column
-//    steps, 2 or 3 stages deep.
+//    steps, 2 or 3 stages deep, each step's loads issued right behind the
+//    barrier that frees their stage.
 //  * GEMM 1 reads A as a virtual concatenation: the contraction index picks
 //    one of the m hidden-state buffers, so the [T, m*d] matrix never exists.
 //  * GEMM 2 fuses all layers' K and V projections horizontally: output column
@@ -491,15 +494,17 @@ __global__ __launch_bounds__(64 * WM_ * WN_) void k_gemm_bf16(GemmP p) {
   }
 
   // Software pipeline over steps of KB contraction columns, SS sub-steps of
-  // 16 each.
+  // one MFMA's contraction (16 or 32 columns) each.
   //  * Operand fragments of sub-step s+1 are read from LDS while the MFMAs of
   //    sub-step s run.
   //  * At the start of the last sub-step of step k every wave waits for its
   //    DMA of step k+1, finishes its reads of stage k and meets the others
   //    at a barrier; it then reads the first fragments of step k+1.
-  //  * The DMA of step k+NSTG-1 goes into the stage of step k-1 (free since
-  //    that barrier), one instruction every few MFMAs of the sub-steps before
-  //    the last, so the matrix pipe keeps running while the loads issue.
+  //  * Default (EARLY): the DMA of step k+NSTG goes into stage k right behind
+  //    that barrier, one instruction every few MFMAs of the last sub-step, so
+  //    every step's loads have NSTG-1 whole steps to land.  Otherwise the DMA
+  //    of step k+NSTG-1 goes into the stage of step k-1 during the sub-steps
+  //    before the last.
   bf16x8 fa[2][MI], fb[2][NJ];
   // fragment f of sub-step ss: A blocks first (f < MI), then B blocks
   auto read_one = [&](int set, const uint8_t* sb, int ss, int f) __attribute__((always_inline)) {
