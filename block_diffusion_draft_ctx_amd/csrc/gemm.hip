@@ -539,8 +539,9 @@ __global__ __launch_bounds__(64 * WM_ * WN_) void k_gemm_bf16(GemmP p) {
       for (int f = 0; f < NF; ++f) read_one(0, lb, 0, f);
     }
     lgkm_drain();
-    // mode 0: issue the DMA of step kt+NSTG-1; 1: nothing left to issue;
-    // 2: the final step (no hand-over to a next step)
+    // mode 0: issue the DMA of a later step (kt+NSTG, or kt+NSTG-1 without
+    // EARLY); 1: nothing left to issue; 2: the final step (no hand-over to a
+    // next step)
     auto step = [&](int kt, int mode) __attribute__((always_inline)) {
       const uint8_t* sb = lb + (kt % NSTG_) * STG;
       const int dst = (kt + NSTG_ - 1) % NSTG_;
