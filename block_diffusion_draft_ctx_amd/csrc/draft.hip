@@ -73,6 +73,50 @@ __global__ __launch_bounds__(256) void k_rmsnorm(int M, int d, const T* __restri
   }
 }
 
+// The same with one workgroup per row, for rows of at most 2048 * NC
+// elements: each lane keeps its NC vectors of 8 in registers between the sum
+// of squares (wavefront sums, then the four combined through LDS) and the
+// scaling, so the row is read once and every row's loads are in flight at
+// once.  Few rows (a small batch) then take one load round, not d / 512.
+template <typename T, int NC>
+__global__ __launch_bounds__(256) void k_rmsnorm_row(int M, int d, const T* __restrict__ x,
+                                                     const T* __restrict__ w, float eps,
+                                                     T* __restrict__ y) {
+  __shared__ float part[4];
+  const int row = blockIdx.x;
+  const T* xr = x + (int64_t)row * d;
+  float v[NC][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int i = (threadIdx.x + 256 * c) * 8;
+    if (i < d) {
+      ld8(xr + i, v[c]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[c][j] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss = fmaf(v[c][j], v[c][j], ss);
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  ss = (part[0] + part[1]) + (part[2] + part[3]);
+  const float r = 1.f / sqrtf(ss / d + eps);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int i = (threadIdx.x + 256 * c) * 8;
+    if (i < d) {
+      float g[8];
+      ld8(w + i, g);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[c][j] = v[c][j] * r * g[j];
+      st8(y + (int64_t)row * d + i, v[c]);
+    }
+  }
+}
+
 // q / k / v out of the fused projection [M, (Hq + 2 Hkv) D]: per-head RMSNorm
 // of q and k (when a weight is given), then the half-split rotary embedding
 // at the row's position ctx_lens[row / k] + row % k; v is copied.  A group of
@@ -193,8 +237,18 @@ unsigned grid_for(int64_t threads) {
 
 template <typename T>
 void rmsnorm(int M, int d, const void* x, const void* w, float eps, void* y, hipStream_t st) {
-  hipLaunchKernelGGL(k_rmsnorm<T>, dim3((unsigned)cdiv(M, 4)), dim3(256), 0, st, M, d,
-                     static_cast<const T*>(x), static_cast<const T*>(w), eps, static_cast<T*>(y));
+  const T* xt = static_cast<const T*>(x);
+  const T* wt = static_cast<const T*>(w);
+  T* yt = static_cast<T*>(y);
+  if (M <= 0) return;
+  if (d <= 2048)
+    hipLaunchKernelGGL((k_rmsnorm_row<T, 1>), dim3((unsigned)M), dim3(256), 0, st, M, d, xt, wt, eps, yt);
+  else if (d <= 4096)
+    hipLaunchKernelGGL((k_rmsnorm_row<T, 2>), dim3((unsigned)M), dim3(256), 0, st, M, d, xt, wt, eps, yt);
+  else if (d <= 8192)
+    hipLaunchKernelGGL((k_rmsnorm_row<T, 4>), dim3((unsigned)M), dim3(256), 0, st, M, d, xt, wt, eps, yt);
+  else
+    hipLaunchKernelGGL(k_rmsnorm<T>, dim3((unsigned)cdiv(M, 4)), dim3(256), 0, st, M, d, xt, wt, eps, yt);
 }
 
 struct LayerWs {
