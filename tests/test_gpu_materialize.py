@@ -215,6 +215,57 @@ def test_materialize_prefill_full_size_sampled():
     log(f"  {len(rows)} rows x {Ld} layers x K/V within {TOL['bf16']}")
 
 
+
+def test_materialize_past_32bit_operand_offsets_sampled():
+    """Rows enough that a hidden-state buffer exceeds 4 GiB (T = 528384 rows of
+    4096 bf16 per hidden, two hiddens, one draft layer): both GEMMs then load
+    their operands with 64-bit addresses instead of 32-bit buffer offsets.
+    Device-drawn seeded normals as in the full-size prefill test; sampled rows
+    (including rows whose operand bytes lie past 4 GiB) are compared."""
+    import torch
+    n_seq, rps, d, m, Ld, Hkv, D = 1, 528384, 4096, 2, 1, 8, 128
+    T = n_seq * rps
+    assert T * d * 2 > 2 ** 32
+    log(f"materialise past 32-bit offsets T={T}")
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(2460)
+    bf = torch.bfloat16
+
+    def randn(*shape, std=1.0):
+        return (torch.randn(*shape, generator=g, device=dev) * std).to(bf)
+
+    hid = [randn(T, d) for _ in range(m)]
+    Wf, bfv = randn(d, m * d, std=0.02), randn(d, std=0.02)
+    WK = [randn(Hkv * D, d, std=0.02) for _ in range(Ld)]
+    WV = [randn(Hkv * D, d, std=0.02) for _ in range(Ld)]
+    maxp = rps // 16
+    bt = torch.randperm(n_seq * maxp, generator=g, device=dev).to(torch.int32).view(n_seq, maxp)
+    ck = [torch.zeros(n_seq * maxp, Hkv, 16, D, dtype=bf, device=dev) for _ in range(Ld)]
+    cv = [torch.zeros(n_seq * maxp, Hkv, 16, D, dtype=bf, device=dev) for _ in range(Ld)]
+    start = torch.zeros(n_seq, dtype=torch.int32, device=dev)
+    dfl.materialize_ctx_kv(hid, Wf, bfv, WK, WV, ck, cv, bt.contiguous(), rps, start, None)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2460)
+    past = 2 ** 32 // (d * 2)   # first row whose bytes start past 4 GiB
+    rows = sorted({0, 255, past - 1, past, past + 255, T - 256, T - 1,
+                   *rng.choice(T, size=12, replace=False).tolist()})
+    ridx = torch.tensor(rows, dtype=torch.int64, device=dev)
+    ref = oracle.materialize([bits(h.index_select(0, ridx)) for h in hid], bits(Wf), bits(bfv),
+                             [bits(w) for w in WK], [bits(w) for w in WV], Hkv, D, "bf16")
+    btn = bt.cpu().numpy()
+    sidx = torch.tensor([int(btn[r // rps, (r % rps) // 16]) * 16 + r % 16 for r in rows],
+                        dtype=torch.int64, device=dev)
+    for l in range(Ld):
+        for name, cache, rv in (("K", ck[l], ref["K"][l]), ("V", cv[l], ref["V"][l])):
+            by_slot = cache.transpose(1, 2).reshape(-1, Hkv, D)
+            got = down(by_slot.index_select(0, sidx))
+            e = rel_err(got, rv)
+            assert e <= TOL["bf16"], (l, name, e)
+    log(f"  {len(rows)} rows x {Ld} layer x K/V within {TOL['bf16']}")
+    del hid, ck, cv
+    torch.cuda.empty_cache()
+
 # --- K epilogue: per-head RMSNorm, then the rotary embedding at each row's position
 
 def _epi(seed, c, norm=True, theta=1e6, eps=1e-6):
