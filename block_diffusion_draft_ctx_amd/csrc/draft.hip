@@ -3,8 +3,9 @@
 // embedding table and lm_head; its block is the anchor followed by mask
 // tokens, and each layer's attention sees the injected target context.
 //
-// One layer is nine launches on the caller's stream, every intermediate in
-// the caller's workspace:
+// One layer is nine launches on the caller's stream (eight when the gate/up
+// product splits its contraction: SiLU then rides on its reduction), every
+// intermediate in the caller's workspace:
 //   RMSNorm -> QKV GEMM -> q/k head norm + rotary embedding (v copied out)
 //   -> block attention over [context; block] -> O GEMM + residual (in place)
 //   -> RMSNorm -> gate/up GEMM -> SiLU(gate) * up -> down GEMM + residual.
@@ -309,9 +310,13 @@ hipError_t layer_impl(const DraftArgs& a, void* ws, hipStream_t st) {
   if ((e = launch_attention(a.bf16, aa, w + L.attn_ws, st))) return e;
   if ((e = launch_dense_gemm(a.bf16, M, a.d, a.Hq * a.D, attn, a.w_o, nullptr, a.x, a.x, gw, st))) return e;
   rmsnorm<T>(M, a.d, a.x, a.ln2, a.eps, xn, st);
-  if ((e = launch_dense_gemm(a.bf16, M, 2 * a.I, a.d, xn, a.w_gate_up, nullptr, nullptr, gu, gw, st))) return e;
-  hipLaunchKernelGGL(k_silu_mul<T>, dim3(grid_for((int64_t)M * a.I / 8)), dim3(256), 0, st, M, a.I,
-                     static_cast<const T*>(gu), static_cast<T*>(h));
+  if (dense_gemm_splits(M, 2 * a.I, a.d, a.bf16)) {   // few rows: SiLU in the split reduction
+    if ((e = launch_dense_gemm_silu(a.bf16, M, a.I, a.d, xn, a.w_gate_up, h, gw, st))) return e;
+  } else {
+    if ((e = launch_dense_gemm(a.bf16, M, 2 * a.I, a.d, xn, a.w_gate_up, nullptr, nullptr, gu, gw, st))) return e;
+    hipLaunchKernelGGL(k_silu_mul<T>, dim3(grid_for((int64_t)M * a.I / 8)), dim3(256), 0, st, M, a.I,
+                       static_cast<const T*>(gu), static_cast<T*>(h));
+  }
   if ((e = launch_dense_gemm(a.bf16, M, a.d, a.I, h, a.w_down, nullptr, a.x, a.x, gw, st))) return e;
   return hipGetLastError();
 }

@@ -811,6 +811,49 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmP p) {
   }
 }
 
+// The drafter's gate/up product [M, 2I] split over the contraction, reduced
+// straight into h[M, I] = silu(gate) * up: per 8 columns c of h, the partials
+// of gate column c and up column I + c are summed in split order, each sum
+// rounded to storage (as the stored product would be), then combined.
+// Element-wise identical to the stored product followed by the SiLU kernel.
+template <typename T>
+__global__ __launch_bounds__(256) void k_splitk_reduce_silu(GemmP p, int I) {
+  const int64_t total = (int64_t)p.M * p.N;   // N = 2 I
+  const int i8 = I / 8;
+  const int64_t n = (int64_t)p.M * i8;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+    const int row = (int)(e / i8);
+    const int col = (int)(e - (int64_t)row * i8) * 8;
+    const int64_t gb = (int64_t)row * p.N + col;
+    float g[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, u[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int s = 0; s < p.ksplit; ++s) {
+      const f32x4v* sg = reinterpret_cast<const f32x4v*>(p.part + (int64_t)s * total + gb);
+      const f32x4v* su = reinterpret_cast<const f32x4v*>(p.part + (int64_t)s * total + gb + I);
+      const f32x4v g0 = sg[0], g1 = sg[1], u0 = su[0], u1 = su[1];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { g[j] += g0[j]; g[4 + j] += g1[j]; u[j] += u0[j]; u[4 + j] += u1[j]; }
+    }
+    float h[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float gr = sizeof(T) == 2 ? bf16_to_f32(f32_to_bf16(g[j])) : g[j];
+      const float ur = sizeof(T) == 2 ? bf16_to_f32(f32_to_bf16(u[j])) : u[j];
+      h[j] = gr / (1.f + __expf(-gr)) * ur;
+    }
+    T* dst = static_cast<T*>(p.out) + (int64_t)row * p.ldc + col;
+    if constexpr (sizeof(T) == 2) {
+      u32x4 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(h[2 * j], h[2 * j + 1]);
+      *reinterpret_cast<u32x4*>(dst) = o;
+    } else {
+      reinterpret_cast<f32x4v*>(dst)[0] = f32x4v{h[0], h[1], h[2], h[3]};
+      reinterpret_cast<f32x4v*>(dst)[1] = f32x4v{h[4], h[5], h[6], h[7]};
+    }
+  }
+}
+
 // K epilogue of materialisation ([SGLang DFlash], section 4.1: the K
 // projection goes through k_norm, then the rotary embedding at the row's
 // position, before the prefix-valid write), applied in place to the K rows
@@ -1011,6 +1054,35 @@ void launch_bf16_gemm(GemmP p, int epi, dim3 grid, hipStream_t st) {
     hipLaunchKernelGGL((k_gemm_bf16<BM_, BN_, WM_, WN_, KB_, NSTG_, EPI_PARTIAL, MT_, BUF>), grid, block, lds, st, p);
 }
 
+// The bf16 tile kernel of plan pl (tile shape, MFMA shape, operand loads).
+void launch_plan_bf16(GemmP p, const Plan& pl, int epi, dim3 grid, hipStream_t st) {
+  if (pl.bm == 256 && pl.bn == 256) {
+    if (buf_offsets_fit(p, 256))
+      launch_bf16_gemm<256, 256, DFLASH_GEMM_BIG_WM, DFLASH_GEMM_BIG_WN, DFLASH_GEMM_KB_BIG, DFLASH_GEMM_NSTG_BIG,
+                       DFLASH_GEMM_MT_BIG, true>(p, epi, grid, st);
+    else
+      launch_bf16_gemm<256, 256, DFLASH_GEMM_BIG_WM, DFLASH_GEMM_BIG_WN, DFLASH_GEMM_KB_BIG, DFLASH_GEMM_NSTG_BIG,
+                       DFLASH_GEMM_MT_BIG>(p, epi, grid, st);
+  }
+  else if (pl.bm == 192) {
+    if (buf_offsets_fit(p, 256))
+      launch_bf16_gemm<192, 256, 2, 4, 64, 2, DFLASH_GEMM_MT_BIG, true>(p, epi, grid, st);
+    else
+      launch_bf16_gemm<192, 256, 2, 4, 64, 2, DFLASH_GEMM_MT_BIG>(p, epi, grid, st);
+  }
+  else if (pl.bm == 32)
+    launch_bf16_gemm<32, 256, 1, 4, 64, 4, DFLASH_GEMM_MT_SMALL>(p, epi, grid, st);
+  else if (pl.bm == 64)
+    launch_bf16_gemm<64, 256, 1, 4, 64, 3, DFLASH_GEMM_MT_SMALL>(p, epi, grid, st);
+  else if (pl.bm == 128 && pl.bn == 256)
+    launch_bf16_gemm<128, 256, 2, 2, 64, 3, DFLASH_GEMM_MT_SMALL>(p, epi, grid, st);
+  else if (pl.bm == 256)
+    launch_bf16_gemm<256, 128, 2, 2, DFLASH_GEMM_KB_SMALL, DFLASH_GEMM_NSTG_SMALL, DFLASH_GEMM_MT_SMALL>(p, epi, grid, st);
+  else
+    launch_bf16_gemm<128, 128, 2, DFLASH_GEMM_SMALL_WN, DFLASH_GEMM_KB_SMALL, DFLASH_GEMM_NSTG_SMALL,
+                     DFLASH_GEMM_MT_SMALL>(p, epi, grid, st);
+}
+
 void run_gemm(bool bf16, GemmP p, int epi_final, hipStream_t st) {
   const Plan pl = plan_gemm(p.M, p.N, p.K, bf16, p.b_layered ? p.HD : 0);
   p.ksplit = pl.ksplit;
@@ -1018,31 +1090,7 @@ void run_gemm(bool bf16, GemmP p, int epi_final, hipStream_t st) {
   const int epi = pl.ksplit > 1 ? EPI_PARTIAL : epi_final;
   if (bf16) {
     const dim3 grid((unsigned)(cdiv(p.M, pl.bm) * (p.N / pl.bn)), (unsigned)pl.ksplit);
-    if (pl.bm == 256 && pl.bn == 256) {
-      if (buf_offsets_fit(p, 256))
-        launch_bf16_gemm<256, 256, DFLASH_GEMM_BIG_WM, DFLASH_GEMM_BIG_WN, DFLASH_GEMM_KB_BIG, DFLASH_GEMM_NSTG_BIG,
-                         DFLASH_GEMM_MT_BIG, true>(p, epi, grid, st);
-      else
-        launch_bf16_gemm<256, 256, DFLASH_GEMM_BIG_WM, DFLASH_GEMM_BIG_WN, DFLASH_GEMM_KB_BIG, DFLASH_GEMM_NSTG_BIG,
-                         DFLASH_GEMM_MT_BIG>(p, epi, grid, st);
-    }
-    else if (pl.bm == 192) {
-      if (buf_offsets_fit(p, 256))
-        launch_bf16_gemm<192, 256, 2, 4, 64, 2, DFLASH_GEMM_MT_BIG, true>(p, epi, grid, st);
-      else
-        launch_bf16_gemm<192, 256, 2, 4, 64, 2, DFLASH_GEMM_MT_BIG>(p, epi, grid, st);
-    }
-    else if (pl.bm == 32)
-      launch_bf16_gemm<32, 256, 1, 4, 64, 4, DFLASH_GEMM_MT_SMALL>(p, epi, grid, st);
-    else if (pl.bm == 64)
-      launch_bf16_gemm<64, 256, 1, 4, 64, 3, DFLASH_GEMM_MT_SMALL>(p, epi, grid, st);
-    else if (pl.bm == 128 && pl.bn == 256)
-      launch_bf16_gemm<128, 256, 2, 2, 64, 3, DFLASH_GEMM_MT_SMALL>(p, epi, grid, st);
-    else if (pl.bm == 256)
-      launch_bf16_gemm<256, 128, 2, 2, DFLASH_GEMM_KB_SMALL, DFLASH_GEMM_NSTG_SMALL, DFLASH_GEMM_MT_SMALL>(p, epi, grid, st);
-    else
-      launch_bf16_gemm<128, 128, 2, DFLASH_GEMM_SMALL_WN, DFLASH_GEMM_KB_SMALL, DFLASH_GEMM_NSTG_SMALL,
-                       DFLASH_GEMM_MT_SMALL>(p, epi, grid, st);
+    launch_plan_bf16(p, pl, epi, grid, st);
   } else {
     const dim3 grid((unsigned)(cdiv(p.M, 64) * cdiv(p.N, 64)), (unsigned)pl.ksplit);
     if (epi == EPI_DENSE) hipLaunchKernelGGL(k_gemm_f32<EPI_DENSE>, grid, dim3(256), 0, st, p);
@@ -1098,6 +1146,39 @@ hipError_t launch_dense_gemm(bool bf16, int M, int N, int K, const void* A, cons
     p.ldc = N;
     run_gemm(bf16, p, EPI_DENSE, st);
   }
+  return hipGetLastError();
+}
+
+bool dense_gemm_splits(int M, int N, int K, bool bf16) {
+  if (bf16 && N > 256 && N % 256 == 128) return false;
+  return plan_gemm(M, N, K, bf16, 0).ksplit > 1;
+}
+
+hipError_t launch_dense_gemm_silu(bool bf16, int M, int I, int K, const void* A, const void* B, void* h,
+                                  void* ws, hipStream_t st) {
+  if (!dense_gemm_splits(M, 2 * I, K, bf16) || I % 8) return hipErrorInvalidValue;
+  const Plan pl = plan_gemm(M, 2 * I, K, bf16, 0);
+  GemmP p{};
+  p.M = M; p.N = 2 * I; p.K = K;
+  p.a[0] = A;
+  p.a_seg = K;
+  p.b = B; p.ldb = K;
+  p.b_layered = 0;
+  p.part = static_cast<float*>(ws);
+  p.out = h;
+  p.ldc = I;
+  p.ksplit = pl.ksplit;
+  p.kchunk = pl.kchunk;
+  if (bf16) {
+    const dim3 grid((unsigned)(cdiv(p.M, pl.bm) * (p.N / pl.bn)), (unsigned)pl.ksplit);
+    launch_plan_bf16(p, pl, EPI_PARTIAL, grid, st);
+  } else {
+    const dim3 grid((unsigned)(cdiv(p.M, 64) * cdiv(p.N, 64)), (unsigned)pl.ksplit);
+    hipLaunchKernelGGL(k_gemm_f32<EPI_PARTIAL>, grid, dim3(256), 0, st, p);
+  }
+  const unsigned blocks = (unsigned)std::min<int64_t>(cdiv((int64_t)M * I / 8, 256), 8192);
+  if (bf16) hipLaunchKernelGGL(k_splitk_reduce_silu<uint16_t>, dim3(blocks), dim3(256), 0, st, p, I);
+  else hipLaunchKernelGGL(k_splitk_reduce_silu<float>, dim3(blocks), dim3(256), 0, st, p, I);
   return hipGetLastError();
 }
 

@@ -125,6 +125,14 @@ size_t dense_gemm_ws_bytes(int64_t M, int64_t N, int64_t K, bool bf16);
 hipError_t launch_dense_gemm(bool bf16, int M, int N, int K, const void* A, const void* B,
                              const void* bias, const void* resid, void* out, void* ws,
                              hipStream_t st);
+// Whether that product splits its contraction (fp32 partials in ws, then a
+// reduction pass).
+bool dense_gemm_splits(int M, int N, int K, bool bf16);
+// The drafter's gate/up product [M, 2I] (gate columns first) when it splits:
+// its reduction writes h[M, I] = silu(gate) * up directly, element-wise as the
+// stored product followed by the SiLU kernel would.  Only for split shapes.
+hipError_t launch_dense_gemm_silu(bool bf16, int M, int I, int K, const void* A, const void* B, void* h,
+                                  void* ws, hipStream_t st);
 
 // ------------------------------------------------------------ drafter layer
 struct DraftArgs {
