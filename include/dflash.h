@@ -16,7 +16,9 @@
  *   dflash_draft_head          the drafter's final norm and shared lm_head
  *   dflash_embed               the shared embedding gather
  * plus one workspace-size query per operation that needs scratch memory,
- * dflash_status_string and dflash_version.
+ * dflash_status_string and dflash_version, and dflash_verify_greedy_noalloc
+ * (the greedy verify on a static scratch buffer, for callers that cannot
+ * allocate) with its dflash_noalloc_scratch_bytes.
  *
  * Pages these follow (cited by short title):
  *   [DFlash overview]  "DFlash 块扩散解码：以并行扩散替代自回归草稿，实现无损 6 倍推理加速"
