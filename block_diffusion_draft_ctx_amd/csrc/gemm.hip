@@ -138,7 +138,6 @@ constexpr int BK = 64;   // granularity of split-K chunks (a multiple of the pip
 #endif
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 enum { EPI_DENSE = 0, EPI_PAGED = 1, EPI_PARTIAL = 2 };
@@ -527,82 +526,80 @@ __global__ __launch_bounds__(64 * WM_ * WN_) void k_gemm_bf16(GemmP p) {
   constexpr int SPREAD = NSTG_ == 2 ? (SS - 1 < DFLASH_GEMM_SPREAD2 ? SS - 1 : DFLASH_GEMM_SPREAD2) : SS - 1;
   constexpr int SLOTS = SPREAD * MF;   // (with more DMA instructions than slots, several share one)
 
-  {
-    constexpr bool EARLY = DFLASH_GEMM_EARLY;
-    for (int s = 0; s < NSTG_ - (EARLY ? 0 : 1) && s < nk; ++s) issue(s);
-    if (nk > 0) {
-      if (EARLY && nk >= NSTG_) wait_vmcnt<(NSTG_ - 1) * DMA_PER_STEP>();   // step 0 of NSTG
-      else wait_steps(min(NSTG_ - 2, nk - 1));
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-  #pragma unroll
-      for (int f = 0; f < NF; ++f) read_one(0, lb, 0, f);
-    }
-    lgkm_drain();
-    // mode 0: issue the DMA of a later step (kt+NSTG, or kt+NSTG-1 without
-    // EARLY); 1: nothing left to issue; 2: the final step (no hand-over to a
-    // next step)
-    auto step = [&](int kt, int mode) __attribute__((always_inline)) {
-      const uint8_t* sb = lb + (kt % NSTG_) * STG;
-      const int dst = (kt + NSTG_ - 1) % NSTG_;
-  #pragma unroll
-      for (int ss = 0; ss < SS; ++ss) {
-        const int c = ss & 1;
-        // fragments for the next sub-step: this stage, or the next stage once
-        // every wave has its DMA and is done with this stage
-        const uint8_t* rsb = sb;
-        int rss = ss + 1;
-        const bool rd = ss + 1 < SS || mode != 2;
-        if (ss + 1 == SS && mode != 2) {
-          wait_steps(min(NSTG_ - 2, nk - 2 - kt));
-          lgkm_drain();   // own reads of this stage are done
-          __builtin_amdgcn_s_barrier();
-          asm volatile("" ::: "memory");
-          rsb = lb + ((kt + 1) % NSTG_) * STG;
-          rss = 0;
+  constexpr bool EARLY = DFLASH_GEMM_EARLY;
+  for (int s = 0; s < NSTG_ - (EARLY ? 0 : 1) && s < nk; ++s) issue(s);
+  if (nk > 0) {
+    if (EARLY && nk >= NSTG_) wait_vmcnt<(NSTG_ - 1) * DMA_PER_STEP>();   // step 0 of NSTG
+    else wait_steps(min(NSTG_ - 2, nk - 1));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int f = 0; f < NF; ++f) read_one(0, lb, 0, f);
+  }
+  lgkm_drain();
+  // mode 0: issue the DMA of a later step (kt+NSTG, or kt+NSTG-1 without
+  // EARLY); 1: nothing left to issue; 2: the final step (no hand-over to a
+  // next step)
+  auto step = [&](int kt, int mode) __attribute__((always_inline)) {
+    const uint8_t* sb = lb + (kt % NSTG_) * STG;
+    const int dst = (kt + NSTG_ - 1) % NSTG_;
+#pragma unroll
+    for (int ss = 0; ss < SS; ++ss) {
+      const int c = ss & 1;
+      // fragments for the next sub-step: this stage, or the next stage once
+      // every wave has its DMA and is done with this stage
+      const uint8_t* rsb = sb;
+      int rss = ss + 1;
+      const bool rd = ss + 1 < SS || mode != 2;
+      if (ss + 1 == SS && mode != 2) {
+        wait_steps(min(NSTG_ - 2, nk - 2 - kt));
+        lgkm_drain();   // own reads of this stage are done
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        rsb = lb + ((kt + 1) % NSTG_) * STG;
+        rss = 0;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < MF; ++t) {
+        const int i = t / NJ, j = t % NJ;
+        acc[i][j] = mfma(fa[c][i], fb[c][j], acc[i][j]);
+        // the t-th fragment in first-use order rides on MFMA t; any beyond
+        // the last MFMA follow it
+        if (rd) {
+          constexpr FragOrder<MI, NJ> fo;
+          if (t < NF) read_one(c ^ 1, rsb, rss, fo.f[t]);
+          if (t == MF - 1) {
+#pragma unroll
+            for (int u = MF; u < NF; ++u) read_one(c ^ 1, rsb, rss, fo.f[u]);
+          }
+        }
+        if (EARLY && mode == 0 && ss + 1 == SS) {
+          // DMA instructions q with q * MF / DMA_PER_STEP == t
+#pragma unroll
+          for (int q = (t * DMA_PER_STEP + MF - 1) / MF; q < ((t + 1) * DMA_PER_STEP + MF - 1) / MF; ++q) {
+            __builtin_amdgcn_sched_barrier(0);
+            dma_one(kt % NSTG_, q);
+          }
+        }
+        if (!EARLY && mode == 0 && ss < SPREAD) {
+          const int slot = ss * MF + t;
+#pragma unroll
+          for (int q = 0; q < DMA_PER_STEP; ++q)
+            if (q * SLOTS / DMA_PER_STEP == slot) {
+              __builtin_amdgcn_sched_barrier(0);
+              dma_one(dst, q);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
-  #pragma unroll
-        for (int t = 0; t < MF; ++t) {
-          const int i = t / NJ, j = t % NJ;
-          acc[i][j] = mfma(fa[c][i], fb[c][j], acc[i][j]);
-          // the t-th fragment in first-use order rides on MFMA t; any beyond
-          // the last MFMA follow it
-          if (rd) {
-            constexpr FragOrder<MI, NJ> fo;
-            if (t < NF) read_one(c ^ 1, rsb, rss, fo.f[t]);
-            if (t == MF - 1) {
-  #pragma unroll
-              for (int u = MF; u < NF; ++u) read_one(c ^ 1, rsb, rss, fo.f[u]);
-            }
-          }
-          if (EARLY && mode == 0 && ss + 1 == SS) {
-            // DMA instructions q with q * MF / DMA_PER_STEP == t
-  #pragma unroll
-            for (int q = (t * DMA_PER_STEP + MF - 1) / MF; q < ((t + 1) * DMA_PER_STEP + MF - 1) / MF; ++q) {
-              __builtin_amdgcn_sched_barrier(0);
-              dma_one(kt % NSTG_, q);
-            }
-          }
-          if (!EARLY && mode == 0 && ss < SPREAD) {
-            const int slot = ss * MF + t;
-  #pragma unroll
-            for (int q = 0; q < DMA_PER_STEP; ++q)
-              if (q * SLOTS / DMA_PER_STEP == slot) {
-                __builtin_amdgcn_sched_barrier(0);
-                dma_one(dst, q);
-              }
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
       }
-    };
-    const int n_issue = max(0, nk - (NSTG_ - (EARLY ? 0 : 1)));   // steps that still issue a DMA
-    int kt = 0;
-    for (; kt < n_issue; ++kt) step(kt, 0);
-    for (; kt < nk - 1; ++kt) step(kt, 1);
-    if (nk > 0) step(nk - 1, 2);
-  }
+    }
+  };
+  const int n_issue = max(0, nk - (NSTG_ - (EARLY ? 0 : 1)));   // steps that still issue a DMA
+  int kt = 0;
+  for (; kt < n_issue; ++kt) step(kt, 0);
+  for (; kt < nk - 1; ++kt) step(kt, 1);
+  if (nk > 0) step(nk - 1, 2);
   wait_vmcnt<0>();
   __syncthreads();   // every wave is done with the stages before they are reused
 
