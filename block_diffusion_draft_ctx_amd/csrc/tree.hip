@@ -107,6 +107,9 @@ __device__ __forceinline__ int lanes_below(uint64_t b) {
 #ifndef DFLASH_TOPK_NF
 #define DFLASH_TOPK_NF 4
 #endif
+#ifndef DFLASH_TOPK_PREFETCH
+#define DFLASH_TOPK_PREFETCH 1   // top-K pass: next round's loads issued before this round's arithmetic
+#endif
 #ifndef DFLASH_TOPK_WGS
 #define DFLASH_TOPK_WGS 768
 #endif
@@ -241,15 +244,50 @@ __global__ __launch_bounds__(kThreads) void k_row_topk(const T* __restrict__ dl,
   };
   if (VEC) {
     const int nvec = (x1 - x0) >> 3;
+    constexpr int kStep = kTopkNF * kThreads;
+    constexpr int NW = sizeof(T) / 2;   // 16-byte pieces per vector of 8
+    // The loads of round base + kStep go out before round base is
+    // converted and tested, so they land while this one computes.  They go
+    // out unconditionally (past the end they re-read the last vector) so
+    // that the registers they fill are never a merge of old and new values,
+    // which would make the compiler wait for them at the top of the loop.
+    uint4 nx[kTopkNF][NW];
+    auto fetch = [&](int base) {
+#pragma unroll
+      for (int u = 0; u < kTopkNF; ++u) {
+        const int v = min(base + lane + u * kThreads, nvec - 1);
+        const uint4* q = reinterpret_cast<const uint4*>(row + x0 + (int64_t)v * 8);
+#pragma unroll
+        for (int i = 0; i < NW; ++i) nx[u][i] = ld_stream16(q + i);
+      }
+    };
     bool first = true;
-    for (int base = w * 64; base < nvec; base += kTopkNF * kThreads) {   // uniform per wavefront
+    int base = w * 64;
+    if (base < nvec) fetch(base);
+    for (; base < nvec; base += kStep) {   // uniform per wavefront
+      uint4 cur[kTopkNF][NW];
+#pragma unroll
+      for (int u = 0; u < kTopkNF; ++u)
+#pragma unroll
+        for (int i = 0; i < NW; ++i) cur[u][i] = nx[u][i];
+      if (DFLASH_TOPK_PREFETCH) fetch(base + kStep);
       float e[kTopkNF][8], mx[kTopkNF];
       bool ok[kTopkNF];
 #pragma unroll
       for (int u = 0; u < kTopkNF; ++u) {
-        const int v = base + lane + u * kThreads;
-        ok[u] = v < nvec;
-        load8(row + x0 + (ok[u] ? v : nvec - 1) * 8, e[u]);
+        ok[u] = base + lane + u * kThreads < nvec;
+        if constexpr (NW == 1) {
+          const uint4 q = cur[u][0];
+          e[u][0] = bf16_lo(q.x); e[u][1] = bf16_hi(q.x);
+          e[u][2] = bf16_lo(q.y); e[u][3] = bf16_hi(q.y);
+          e[u][4] = bf16_lo(q.z); e[u][5] = bf16_hi(q.z);
+          e[u][6] = bf16_lo(q.w); e[u][7] = bf16_hi(q.w);
+        } else {
+          e[u][0] = __uint_as_float(cur[u][0].x); e[u][1] = __uint_as_float(cur[u][0].y);
+          e[u][2] = __uint_as_float(cur[u][0].z); e[u][3] = __uint_as_float(cur[u][0].w);
+          e[u][4] = __uint_as_float(cur[u][1].x); e[u][5] = __uint_as_float(cur[u][1].y);
+          e[u][6] = __uint_as_float(cur[u][1].z); e[u][7] = __uint_as_float(cur[u][1].w);
+        }
       }
       float lm = neg_inf();
 #pragma unroll
@@ -273,6 +311,7 @@ __global__ __launch_bounds__(kThreads) void k_row_topk(const T* __restrict__ dl,
       if (first) { seed(lm); first = false; }
 #pragma unroll
       for (int u = 0; u < kTopkNF; ++u) push8(e[u], mx[u], x0 + (base + lane + u * kThreads) * 8, ok[u]);
+      if (!DFLASH_TOPK_PREFETCH) fetch(base + kStep);
     }
     // the ragged tail (fewer than 8 elements), one per lane of the first wavefront
     if (w == 0) {
