@@ -67,6 +67,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #ifndef DFLASH_ATTN_KPF
 #define DFLASH_ATTN_KPF 4           // k_attn_wide: K fragments read ahead of their MFMA
 #endif
+#ifndef DFLASH_ATTN_VPF
+#define DFLASH_ATTN_VPF 2           // k_attn_wide: V fragments read ahead of their MFMA
+#endif
 #ifndef DFLASH_ATTN_PINGPONG
 #define DFLASH_ATTN_PINGPONG 0      // k_attn_wide: the two wavefronts of a SIMD in opposite orders
 #endif
@@ -935,25 +938,39 @@ void k_attn_wide(AttnP p, int nbw, int rows_wg) {
     }
   };
   // O^T[d x 64 q] += V^T . P^T over the tile in stage st
+  // V fragments f = 4(2kb + kk2) + mb go through a ring of VPF register
+  // pairs like the K fragments: fragment f + VPF is read while the MFMAs of
+  // fragment f run (read just before its MFMA, each fragment's latency would
+  // stall the matrix pipe once per MFMA)
   auto pv = [&](int st, const uint4 (&pb)[2][2][JQ]) __attribute__((always_inline)) {
     const uint16_t* Vs = smem + st * STAGE + kKT * KS;
+    const uint16_t* vbase = Vs + (4 * (grp16 >> 1) + tr_r) * VS + 16 * (grp16 & 1) + 4 * tr_q;
+    constexpr int NF = 4 * NMB;
+    constexpr int VPF = DFLASH_ATTN_VPF;
+    auto vaddr = [&](int f) __attribute__((always_inline)) {
+      const int kb = f / (2 * NMB), kk2 = (f / NMB) & 1, mb = f % NMB;
+      return vbase + (32 * kb + 16 * kk2) * VS + 32 * mb;
+    };
+    uint2 rlo[VPF], rhi[VPF];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int f = 0; f < VPF; ++f) {
+      rlo[f] = lds_read_tr16(vaddr(f));
+      rhi[f] = lds_read_tr16(vaddr(f) + 8 * VS);
+    }
 #pragma unroll
-      for (int kk2 = 0; kk2 < 2; ++kk2) {
-        const uint16_t* v0 = Vs + (32 * kb + 16 * kk2 + 4 * (grp16 >> 1) + tr_r) * VS +
-                             16 * (grp16 & 1) + 4 * tr_q;
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
-          const uint2 lo = lds_read_tr16(v0 + 32 * mb);
-          const uint2 hi = lds_read_tr16(v0 + 8 * VS + 32 * mb);
-          const bf16x8 a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-#pragma unroll
-          for (int jq = 0; jq < JQ; ++jq)
-            acc[jq][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(pb[kb][kk2][jq]),
-                                                                   acc[jq][mb], 0, 0, 0);
-        }
+    for (int f = 0; f < NF; ++f) {
+      const uint2 lo = rlo[f % VPF], hi = rhi[f % VPF];
+      if (f + VPF < NF) {
+        rlo[f % VPF] = lds_read_tr16(vaddr(f + VPF));
+        rhi[f % VPF] = lds_read_tr16(vaddr(f + VPF) + 8 * VS);
       }
+      const bf16x8 a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+      const int kb = f / (2 * NMB), kk2 = (f / NMB) & 1, mb = f % NMB;
+#pragma unroll
+      for (int jq = 0; jq < JQ; ++jq)
+        acc[jq][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(pb[kb][kk2][jq]),
+                                                               acc[jq][mb], 0, 0, 0);
+    }
   };
   auto rescale = [&](const float (&alpha)[JQ]) __attribute__((always_inline)) {
     bool move = false;
