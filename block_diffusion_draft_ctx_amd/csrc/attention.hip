@@ -559,20 +559,19 @@ void k_attn_bf16(AttnP p) {
 // Compute-shaped layout (D = 128): many query rows share one context -- the
 // packed training mask (consecutive blocks on one shared block-table row)
 // and long row lists of one request (tree attention, large blocks).  Here the
-// work is MFMA-bound, and per score the softmax costs about as many cycles on
-// the vector ALU as the two products cost on the matrix cores, so the kernel
-// is laid out to keep both pipes busy at once:
-//  * one workgroup = 4 wavefronts (one per SIMD) x 64 query rows = up to 256
-//    rows on one kv-head; every wavefront covers whole 64-key tiles, so each
-//    K and V fragment read from LDS feeds two MFMAs;
+// work is MFMA-bound, so each context tile is read from L2 once for 256 query
+// rows:
+//  * one workgroup = NWV wavefronts x 32 JQ query rows = up to 256 rows on
+//    one kv-head (8 x 32 by default: two wavefronts per SIMD; 4 x 64 lets
+//    each K and V fragment feed two MFMAs but does not fit the registers);
+//    every wavefront covers whole 64-key tiles;
 //  * iteration t issues the P.V products of tile t-1 and the scores of tile
-//    t+1 on the matrix cores while the vector ALU runs the softmax of tile t
-//    (the three are independent), so the two pipes overlap inside one
-//    wavefront; the reference max moves lazily (by more than 2^8), and the
-//    rare accumulator rescale runs at the end of the iteration, after the
-//    products that used the old reference;
-//  * three LDS stages of K and V: tile t's V, tile t+1's K and tile t+2
-//    (being stored from registers, fetched one iteration earlier) are
+//    t+1 on the matrix cores and runs the softmax of tile t on the vector
+//    ALU (the three are independent); the reference max moves lazily (by
+//    more than 2^8), and the rare accumulator rescale runs at the end of the
+//    iteration, after the products that used the old reference;
+//  * four LDS stages of K and V: tile t-1's V, tile t's V, tile t+1's K and V
+//    and tile t+2 (stored from registers, fetched one iteration earlier) are
 //    resident together; one barrier per tile.
 // nbw > 0: nbw consecutive requests on a shared table row per workgroup;
 // nbw == 0: chunks of rows_wg rows of one request (p.RC chunks).
