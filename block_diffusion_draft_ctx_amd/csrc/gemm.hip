@@ -50,6 +50,20 @@ constexpr int BK = 64;   // granularity of split-K chunks (a multiple of the pip
 #ifndef DFLASH_GEMM_SMALL_BM
 #define DFLASH_GEMM_SMALL_BM 128
 #endif
+// Non-temporal stores for the products' outputs: split partials (read once by
+// the reduction), paged K/V rows (read by attention much later) and dense
+// outputs.  Written back lazily, tens of MB of dirty lines cost the next
+// streaming kernel (block attention after the K/V materialisation) far more
+// than their size in HBM time; written non-temporally they do not linger.
+#ifndef DFLASH_GEMM_NT_PARTIAL
+#define DFLASH_GEMM_NT_PARTIAL 1
+#endif
+#ifndef DFLASH_GEMM_NT_CACHE
+#define DFLASH_GEMM_NT_CACHE 1
+#endif
+#ifndef DFLASH_GEMM_NT_DENSE
+#define DFLASH_GEMM_NT_DENSE 1
+#endif
 #ifndef DFLASH_GEMM_SPLIT_MIN_K
 #define DFLASH_GEMM_SPLIT_MIN_K 4096   // shortest contraction split of the 256 x 256 plan
 #endif
@@ -611,8 +625,11 @@ __global__ __launch_bounds__(64 * WM_ * WN_) void k_gemm_bf16(GemmP p) {
         const int row = m0 + BM_ / WM_ * wm + MT_ * i + crow(q);
         if (row >= p.M) continue;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          p.part[((int64_t)split * p.M + row) * p.N + n0 + BN_ / WN_ * wn + MT_ * j + rb] = acc[i][j][q];
+        for (int j = 0; j < NJ; ++j) {
+          float* dst = p.part + ((int64_t)split * p.M + row) * p.N + n0 + BN_ / WN_ * wn + MT_ * j + rb;
+          if (DFLASH_GEMM_NT_PARTIAL) __builtin_nontemporal_store(acc[i][j][q], dst);
+          else *dst = acc[i][j][q];
+        }
       }
     return;
   }
@@ -665,7 +682,11 @@ __global__ __launch_bounds__(64 * WM_ * WN_) void k_gemm_bf16(GemmP p) {
       for (int j = 0; j < 4; ++j)
         o[j] = pack_bf16x2(bf16_lo(o[j]) + bf16_lo(r[j]), bf16_hi(o[j]) + bf16_hi(r[j]));
     }
-    *reinterpret_cast<u32x4*>(dst_base + dst) = o;
+    u32x4* d = reinterpret_cast<u32x4*>(dst_base + dst);
+    if ((EPI == EPI_PAGED && DFLASH_GEMM_NT_CACHE) || (EPI == EPI_DENSE && DFLASH_GEMM_NT_DENSE))
+      __builtin_nontemporal_store(o, d);
+    else
+      *d = o;
   }
 }
 
@@ -793,7 +814,10 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmP p) {
         for (int j = 0; j < 4; ++j)
           o[j] = pack_bf16x2(bf16_lo(o[j]) + bf16_lo(r[j]), bf16_hi(o[j]) + bf16_hi(r[j]));
       }
-      *reinterpret_cast<u32x4*>(dst) = o;
+      if ((EPI == EPI_PAGED && DFLASH_GEMM_NT_CACHE) || (EPI == EPI_DENSE && DFLASH_GEMM_NT_DENSE))
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(dst));
+      else
+        *reinterpret_cast<u32x4*>(dst) = o;
     }
     return;
   }
