@@ -73,11 +73,25 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #ifndef DFLASH_ATTN_PINGPONG
 #define DFLASH_ATTN_PINGPONG 0      // k_attn_wide: the two wavefronts of a SIMD in opposite orders
 #endif
+#ifndef DFLASH_ATTN_STEPS
+#define DFLASH_ATTN_STEPS 1         // k_attn_wide: steady-state iteration as 32 fenced MFMA steps
+#endif
 constexpr int kKT = DFLASH_ATTN_KT;  // keys per tile
 constexpr int kMaxSplitPages = 1024; // pages one split may span (16384 keys)
 constexpr int kWideNW = DFLASH_ATTN_WIDE_NW;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Max and sum of a value and its copy 32 lanes away, by the gfx950 lane swap
+// (a VALU instruction: no LDS round trip as with a bpermute).
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 struct AttnP {
   int B, k, Hq, Hkv;
@@ -894,7 +908,7 @@ void k_attn_wide(AttnP p, int nbw, int rows_wg) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) tmax = fmaxf(tmax, sc[kb][jq][j]);
       tmax *= p.sl2;
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      tmax = xor32_max(tmax);
       const float mn = (tmax > m[jq] + kLazy) ? tmax : m[jq];
       alpha[jq] = (mn == m[jq]) ? 1.f : __builtin_amdgcn_exp2f(m[jq] - mn);
       m[jq] = mn;
@@ -932,7 +946,7 @@ void k_attn_wide(AttnP p, int nbw, int rows_wg) {
           rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), ones, rs1, false);
         }
       float rs = rs0 + rs1;
-      rs += __shfl_xor(rs, 32, 64);
+      rs = xor32_sum(rs);
       l[jq] = l[jq] * alpha[jq] + rs;
     }
   };
@@ -983,6 +997,135 @@ void k_attn_wide(AttnP p, int nbw, int rows_wg) {
     }
   };
 
+  // The steady-state iteration as 32 steps, each one MFMA -- the 16
+  // products of the tile in stage spv (P = pb), then the 16 scores of the
+  // tile in stage ssc (into so) -- with a slice of the softmax of si on the
+  // vector ALU, and a scheduling barrier closing every step, so that the
+  // vector instructions of a step can issue while its MFMA runs.  (Left to
+  // itself the compiler issues the 32 MFMAs back to back and the softmax
+  // after them.)  Slices: row max (steps 0-3), the reference (4), the
+  // exponentials, two per step (5-20), P packed to bf16 with its row sum
+  // (21-28), the normaliser (29); the tile in registers goes to stage sst
+  // at step 8 and the loads of tile tf go out at step 10.  The products read
+  // P of the previous tile before step 21 packs the new one into pb.
+  auto steps = [&](int spv, int ssc, f32x16 (&si)[2][JQ], f32x16 (&so)[2][JQ], uint4 (&pb)[2][2][JQ],
+                   float (&alpha)[JQ], int sst, int tf) __attribute__((always_inline)) {
+    const uint16_t* Vs = smem + spv * STAGE + kKT * KS;
+    const uint16_t* vbase = Vs + (4 * (grp16 >> 1) + tr_r) * VS + 16 * (grp16 & 1) + 4 * tr_q;
+    const uint16_t* Ks = smem + ssc * STAGE;
+    constexpr int NFV = 4 * NMB;
+    constexpr int NFK = 2 * (D / 16);
+    constexpr int VPF = DFLASH_ATTN_VPF;
+    constexpr int KPF = DFLASH_ATTN_KPF;
+    static_assert(NFV == 16 && NFK == 16, "step slices assume 16 + 16 MFMA steps");
+    auto vaddr = [&](int f) __attribute__((always_inline)) {
+      const int kb = f / (2 * NMB), kk2 = (f / NMB) & 1, mb = f % NMB;
+      return vbase + (32 * kb + 16 * kk2) * VS + 32 * mb;
+    };
+    auto kaddr = [&](int f) __attribute__((always_inline)) {
+      return reinterpret_cast<const uint4*>(Ks + (32 * (f & 1) + l32) * KS + 16 * (f >> 1) + 8 * hh);
+    };
+    uint2 rlo[VPF], rhi[VPF];
+    uint4 kring[KPF];
+#pragma unroll
+    for (int f = 0; f < VPF; ++f) {
+      rlo[f] = lds_read_tr16(vaddr(f));
+      rhi[f] = lds_read_tr16(vaddr(f) + 8 * VS);
+    }
+    float tmax[JQ], mref[JQ], rs0[JQ], rs1[JQ];
+#pragma unroll
+    for (int jq = 0; jq < JQ; ++jq) {
+      tmax[jq] = neg_inf();
+      mref[jq] = 0.f;
+      rs0[jq] = 0.f;
+      rs1[jq] = 0.f;
+    }
+    const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+    for (int s = 0; s < NFV + NFK; ++s) {
+      if (s < NFV) {
+        const int f = s;
+        const uint2 lo = rlo[f % VPF], hi = rhi[f % VPF];
+        if (f + VPF < NFV) {
+          rlo[f % VPF] = lds_read_tr16(vaddr(f + VPF));
+          rhi[f % VPF] = lds_read_tr16(vaddr(f + VPF) + 8 * VS);
+        }
+        const bf16x8 a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+        const int kb = f / (2 * NMB), kk2 = (f / NMB) & 1, mb = f % NMB;
+#pragma unroll
+        for (int jq = 0; jq < JQ; ++jq)
+          acc[jq][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(pb[kb][kk2][jq]), acc[jq][mb], 0, 0, 0);
+        // the K ring fills during the last products
+        if (s >= NFV - KPF) kring[s - (NFV - KPF)] = *kaddr(s - (NFV - KPF));
+      } else {
+        const int f = s - NFV;
+        if (f == 0) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int jq = 0; jq < JQ; ++jq)
+#pragma unroll
+              for (int j = 0; j < 16; ++j) so[kb][jq][j] = 0.f;
+        }
+        const uint4 a = kring[f % KPF];
+        if (f + KPF < NFK) kring[f % KPF] = *kaddr(f + KPF);
+        const int kb = f & 1, ks = f >> 1;
+#pragma unroll
+        for (int jq = 0; jq < JQ; ++jq)
+          so[kb][jq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[jq][ks], so[kb][jq], 0, 0, 0);
+      }
+      // softmax slices (as softmax() and pack(), spread over the steps)
+      if (s < 4) {
+#pragma unroll
+        for (int jq = 0; jq < JQ; ++jq)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int e = 8 * s + i;
+            tmax[jq] = fmaxf(tmax[jq], si[e >> 4][jq][e & 15]);
+          }
+      } else if (s == 4) {
+#pragma unroll
+        for (int jq = 0; jq < JQ; ++jq) {
+          const float tm = xor32_max(tmax[jq] * p.sl2);
+          const float mn = (tm > m[jq] + kLazy) ? tm : m[jq];
+          alpha[jq] = (mn == m[jq]) ? 1.f : __builtin_amdgcn_exp2f(m[jq] - mn);
+          m[jq] = mn;
+          mref[jq] = (mn == neg_inf()) ? 0.f : mn;
+        }
+      } else if (s < 21) {
+#pragma unroll
+        for (int jq = 0; jq < JQ; ++jq)
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int e = 2 * (s - 5) + i;
+            si[e >> 4][jq][e & 15] = __builtin_amdgcn_exp2f(fmaf(si[e >> 4][jq][e & 15], p.sl2, -mref[jq]));
+          }
+      } else if (s < 29) {
+        const int q = s - 21, kb = q >> 2, kk2 = (q >> 1) & 1, half = q & 1;
+        const int o = 8 * kk2 + 4 * half;
+#pragma unroll
+        for (int jq = 0; jq < JQ; ++jq) {
+          const uint32_t w0 = pack_bf16x2(si[kb][jq][o], si[kb][jq][o + 1]);
+          const uint32_t w1 = pack_bf16x2(si[kb][jq][o + 2], si[kb][jq][o + 3]);
+          if (half == 0) {
+            pb[kb][kk2][jq].x = w0;
+            pb[kb][kk2][jq].y = w1;
+          } else {
+            pb[kb][kk2][jq].z = w0;
+            pb[kb][kk2][jq].w = w1;
+          }
+          rs0[jq] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w0), ones, rs0[jq], false);
+          rs1[jq] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w1), ones, rs1[jq], false);
+        }
+      } else if (s == 29) {
+#pragma unroll
+        for (int jq = 0; jq < JQ; ++jq) l[jq] = l[jq] * alpha[jq] + xor32_sum(rs0[jq] + rs1[jq]);
+      }
+      if (s == 8) stage(sst);
+      if (s == 10) fetch(tf);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   if (t0 < t1) {
     f32x16 sa[2][JQ], sb[2][JQ];
     uint4 pa[2][2][JQ];   // P of the tile whose products come next
@@ -1020,33 +1163,41 @@ void k_attn_wide(AttnP p, int nbw, int rows_wg) {
     int t = t0 + 1;
     for (; t + 1 < t1; t += 2) {
       mask(sb, t);
-      if (mfma_first) {
-        pv(sg(t - 1), pa);
-        scores(sg(t + 1), sa);
-        softmax(sb, al);
+      if constexpr (DFLASH_ATTN_STEPS) {
+        steps(sg(t - 1), sg(t + 1), sb, sa, pa, al, sg(t + 2), t + 3);
       } else {
-        softmax(sb, al);
-        pv(sg(t - 1), pa);
-        scores(sg(t + 1), sa);
+        if (mfma_first) {
+          pv(sg(t - 1), pa);
+          scores(sg(t + 1), sa);
+          softmax(sb, al);
+        } else {
+          softmax(sb, al);
+          pv(sg(t - 1), pa);
+          scores(sg(t + 1), sa);
+        }
+        pack(sb, pa, al);          // after the products of t-1 have read pa
+        stage(sg(t + 2));
+        fetch(t + 3);
       }
-      pack(sb, pa, al);          // after the products of t-1 have read pa
-      stage(sg(t + 2));
-      fetch(t + 3);
       rescale(al);
       __syncthreads();
       mask(sa, t + 1);
-      if (mfma_first) {
-        pv(sg(t), pa);
-        scores(sg(t + 2), sb);
-        softmax(sa, al);
+      if constexpr (DFLASH_ATTN_STEPS) {
+        steps(sg(t), sg(t + 2), sa, sb, pa, al, sg(t + 3), t + 4);
       } else {
-        softmax(sa, al);
-        pv(sg(t), pa);
-        scores(sg(t + 2), sb);
+        if (mfma_first) {
+          pv(sg(t), pa);
+          scores(sg(t + 2), sb);
+          softmax(sa, al);
+        } else {
+          softmax(sa, al);
+          pv(sg(t), pa);
+          scores(sg(t + 2), sb);
+        }
+        pack(sa, pa, al);
+        stage(sg(t + 3));
+        fetch(t + 4);
       }
-      pack(sa, pa, al);
-      stage(sg(t + 3));
-      fetch(t + 4);
       rescale(al);
       __syncthreads();
     }
