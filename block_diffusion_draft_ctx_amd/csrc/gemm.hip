@@ -47,6 +47,9 @@ constexpr int BK = 64;   // granularity of split-K chunks (a multiple of the pip
 
 // Tuning knobs: the block-tile height used below 256 x 256 (128 or 256, with
 // 128 columns), and the workgroup count split-K aims for.
+#ifndef DFLASH_GEMM_GM
+#define DFLASH_GEMM_GM 2     // row tiles per group in the XCD-local tile walk (more than 8 row tiles)
+#endif
 #ifndef DFLASH_GEMM_SMALL_BM
 #define DFLASH_GEMM_SMALL_BM 128
 #endif
@@ -352,8 +355,13 @@ __global__ __launch_bounds__(64 * WM_ * WN_) void k_gemm_bf16(GemmP p) {
   // owns a contiguous run of tiles, then walk the tiles in groups of GM
   // row-tiles so that the B columns of a group stay in that XCD's L2.
   if ((tiles & 7) == 0) id = (id & 7) * (tiles >> 3) + (id >> 3);
-  constexpr int GM = 8;
+  // With many row tiles (prefill) the groups are 2 row tiles wide: the 32
+  // CUs of an XCD then share each A tile 16 ways in their L2 and stream the
+  // B columns (which stay in the MALL).  8-wide groups (A 4 ways, B 8 ways)
+  // measured 1.6% slower at T = 131072; with at most 8 row tiles (decode)
+  // one group holds them all.
   const int n_mt = (p.M + BM_ - 1) / BM_;
+  const int GM = n_mt > 8 ? DFLASH_GEMM_GM : 8;
   const int group = id / (GM * n_nt);
   const int first_m = group * GM;
   const int gsz = min(GM, n_mt - first_m);
