@@ -355,13 +355,14 @@ __global__ __launch_bounds__(64 * WM_ * WN_) void k_gemm_bf16(GemmP p) {
   // owns a contiguous run of tiles, then walk the tiles in groups of GM
   // row-tiles so that the B columns of a group stay in that XCD's L2.
   if ((tiles & 7) == 0) id = (id & 7) * (tiles >> 3) + (id >> 3);
-  // With many row tiles (prefill) the groups are 2 row tiles wide: the 32
-  // CUs of an XCD then share each A tile 16 ways in their L2 and stream the
-  // B columns (which stay in the MALL).  8-wide groups (A 4 ways, B 8 ways)
-  // measured 1.6% slower at T = 131072; with at most 8 row tiles (decode)
-  // one group holds them all.
+  // With many row tiles (prefill) and at most 32 column tiles, the groups
+  // are 2 row tiles wide: the 32 CUs of an XCD then share each A tile 16
+  // ways in their L2 and stream the B columns (which stay in the MALL).
+  // Measured at T = 131072: the fusion GEMM (16 column tiles) 3% faster than
+  // with 8-wide groups; the K/V GEMM (40 column tiles) 1% slower, so it keeps
+  // 8.  With at most 8 row tiles (decode) one group holds them all.
   const int n_mt = (p.M + BM_ - 1) / BM_;
-  const int GM = n_mt > 8 ? DFLASH_GEMM_GM : 8;
+  const int GM = (n_mt > 8 && n_nt <= 32) ? DFLASH_GEMM_GM : 8;
   const int group = id / (GM * n_nt);
   const int first_m = group * GM;
   const int gsz = min(GM, n_mt - first_m);
