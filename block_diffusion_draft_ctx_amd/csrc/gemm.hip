@@ -45,11 +45,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kML = 16;  // layers a single launch can address
 constexpr int BK = 64;   // granularity of split-K chunks (a multiple of the pipeline step)
 
-// Tuning knobs: the block-tile height used below 256 x 256 (128 or 256, with
-// 128 columns), and the workgroup count split-K aims for.
 #ifndef DFLASH_GEMM_GM
 #define DFLASH_GEMM_GM 2     // row tiles per group in the XCD-local tile walk (more than 8 row tiles)
 #endif
+
+// Tuning knobs: the block-tile height used below 256 x 256 (128 or 256, with
+// 128 columns), and the workgroup count split-K aims for.
 #ifndef DFLASH_GEMM_SMALL_BM
 #define DFLASH_GEMM_SMALL_BM 128
 #endif
